@@ -1,0 +1,9 @@
+"""MI355X (gfx950) forward pass of the fine-grained gated delta rule (FG2-GDN) and
+its KDA, GDN, DeltaProduct and GDN2/RWKV-7-style variants.
+
+The computation lives in libgdn.so (hand-written HIP kernels behind the C ABI of
+include/gdn.h); this package is its ctypes binding.
+"""
+from ._lib import (GdnArgs, GdnError, VARIANTS, gdn_abi_version, gdn_chunk_fwd,  # noqa: F401
+                   gdn_final_state, gdn_recurrent_step, gdn_status_str, gdn_workspace_bytes,
+                   load_library, make_args)

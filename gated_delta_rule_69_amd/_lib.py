@@ -1,0 +1,210 @@
+"""ctypes binding of libgdn.so: the C ABI of include/gdn.h under the same names.
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every step of the computation runs in the library's kernels. There
+is no fallback: if libgdn.so is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgdn.so")
+
+VARIANTS = {"fg2": 0, "kda": 1, "gdn": 2, "deltaproduct": 3, "asym": 4}
+DTYPE_F32, DTYPE_BF16 = 0, 1
+STATUS = {0: "GDN_OK", -1: "GDN_ERR_ARG", -2: "GDN_ERR_UNSUPPORTED", -3: "GDN_ERR_WORKSPACE",
+          -4: "GDN_ERR_HIP"}
+
+
+class GdnArgs(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("dk", ctypes.c_int64), ("dv", ctypes.c_int64),
+                ("chunk", ctypes.c_int32), ("n_h", ctypes.c_int32),
+                ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("alpha", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+                ("beta_v", ctypes.c_void_p), ("j", ctypes.c_void_p), ("eta", ctypes.c_void_p),
+                ("s0", ctypes.c_void_p), ("s_final", ctypes.c_void_p), ("o", ctypes.c_void_p)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({gdn_status_str(status)})")
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it first "
+                               "(python -m gated_delta_rule_69_amd.build)")
+        lib = ctypes.CDLL(path)
+        P = ctypes.POINTER(GdnArgs)
+        lib.gdn_workspace_bytes.argtypes = [P]
+        lib.gdn_workspace_bytes.restype = ctypes.c_size_t
+        lib.gdn_chunk_fwd.argtypes = [P, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        lib.gdn_chunk_fwd.restype = ctypes.c_int
+        lib.gdn_final_state.argtypes = [P, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        lib.gdn_final_state.restype = ctypes.c_int
+        lib.gdn_recurrent_step.argtypes = [P, ctypes.c_void_p, ctypes.c_void_p]
+        lib.gdn_recurrent_step.restype = ctypes.c_int
+        lib.gdn_status_str.argtypes = [ctypes.c_int]
+        lib.gdn_status_str.restype = ctypes.c_char_p
+        lib.gdn_abi_version.argtypes = []
+        lib.gdn_abi_version.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def gdn_status_str(status: int) -> str:
+    return load_library().gdn_status_str(int(status)).decode()
+
+
+def gdn_abi_version() -> int:
+    return int(load_library().gdn_abi_version())
+
+
+# ---- tensor marshalling -----------------------------------------------------------
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, device, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a device tensor on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def make_args(variant, q, k, v, alpha, beta=None, *, chunk=64, n_h=None, beta_v=None, j=None,
+              eta=None, s0=None, s_final=None, o=None) -> GdnArgs:
+    import torch
+    if variant not in VARIANTS:
+        raise ValueError(f"unknown variant {variant!r}")
+    dev = k.device
+    io = k.dtype
+    if io not in (torch.float32, torch.bfloat16):
+        raise ValueError("inputs must be float32 or bfloat16")
+    for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta),
+                    ("beta_v", beta_v), ("j", j), ("eta", eta), ("o", o)):
+        _check(t, name, dev, io)
+    for name, t in (("s0", s0), ("s_final", s_final)):
+        _check(t, name, dev, torch.float32)
+    dp = variant == "deltaproduct"
+    B, T, H = k.shape[0], k.shape[1], k.shape[2]
+    if dp:
+        nh = k.shape[3]
+        if n_h is not None and n_h != nh:
+            raise ValueError("n_h does not match k.shape[3]")
+    else:
+        nh = 1
+    a = GdnArgs()
+    a.variant = VARIANTS[variant]
+    a.dtype = DTYPE_BF16 if io == torch.bfloat16 else DTYPE_F32
+    a.B, a.T, a.H = B, T, H
+    a.dk, a.dv = k.shape[-1], v.shape[-1]
+    a.chunk, a.n_h = int(chunk), int(nh)
+    a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
+    a.alpha, a.beta, a.beta_v = _ptr(alpha), _ptr(beta), _ptr(beta_v)
+    a.j, a.eta = _ptr(j), _ptr(eta)
+    a.s0, a.s_final, a.o = _ptr(s0), _ptr(s_final), _ptr(o)
+    a._keep = (q, k, v, alpha, beta, beta_v, j, eta, s0, s_final, o)  # lifetimes
+    return a
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def gdn_workspace_bytes(args: GdnArgs) -> int:
+    return int(load_library().gdn_workspace_bytes(ctypes.byref(args)))
+
+
+def _workspace(args, ws, device):
+    import torch
+    need = gdn_workspace_bytes(args)
+    if need == 0:
+        raise GdnError(-1, "gdn_workspace_bytes")
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    if ws.numel() < need:
+        raise GdnError(-3, "workspace")
+    return ws
+
+
+def gdn_chunk_fwd(variant, q, k, v, alpha, beta=None, *, chunk=64, beta_v=None, j=None,
+                  eta=None, s0=None, s_final=None, o=None, workspace=None, stream=None,
+                  want_state=True):
+    """Chunkwise forward. Returns (o, s_final); allocates o / s_final / workspace
+    when not given (torch device memory). s_final may be s0 (updated in place)."""
+    import torch
+    dev = k.device
+    B, T, H = k.shape[:3]
+    dk, dv = k.shape[-1], v.shape[-1]
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=k.dtype, device=dev)
+    if s_final is None and want_state:
+        s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    a = make_args(variant, q, k, v, alpha, beta, chunk=chunk, beta_v=beta_v, j=j, eta=eta,
+                  s0=s0, s_final=s_final, o=o)
+    ws = _workspace(a, workspace, dev)
+    st = load_library().gdn_chunk_fwd(ctypes.byref(a), ctypes.c_void_p(ws.data_ptr()),
+                                      ctypes.c_size_t(ws.numel()), _stream(stream))
+    if st != 0:
+        raise GdnError(st, "gdn_chunk_fwd")
+    return o, s_final
+
+
+def gdn_final_state(variant, k, v, alpha, beta=None, *, chunk=64, beta_v=None, j=None,
+                    eta=None, s0=None, s_final=None, workspace=None, stream=None):
+    """State-only chunkwise forward. Returns s_final."""
+    import torch
+    dev = k.device
+    B, T, H = k.shape[:3]
+    dk, dv = k.shape[-1], v.shape[-1]
+    if s_final is None:
+        s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    a = make_args(variant, None, k, v, alpha, beta, chunk=chunk, beta_v=beta_v, j=j, eta=eta,
+                  s0=s0, s_final=s_final, o=None)
+    ws = _workspace(a, workspace, dev)
+    st = load_library().gdn_final_state(ctypes.byref(a), ctypes.c_void_p(ws.data_ptr()),
+                                        ctypes.c_size_t(ws.numel()), _stream(stream))
+    if st != 0:
+        raise GdnError(st, "gdn_final_state")
+    return s_final
+
+
+def gdn_recurrent_step(variant, q, k, v, alpha, beta=None, *, state, beta_v=None, j=None,
+                       eta=None, o=None, stream=None):
+    """Token-sequential update of ``state`` (in place) over k.shape[1] tokens; returns o."""
+    import torch
+    B, T, H = k.shape[:3]
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=k.dtype, device=k.device)
+    _check(state, "state", k.device, torch.float32)
+    a = make_args(variant, q, k, v, alpha, beta, chunk=16, beta_v=beta_v, j=j, eta=eta,
+                  s0=None, s_final=None, o=o)
+    st = load_library().gdn_recurrent_step(ctypes.byref(a), ctypes.c_void_p(state.data_ptr()),
+                                           _stream(stream))
+    if st != 0:
+        raise GdnError(st, "gdn_recurrent_step")
+    return o

@@ -1,0 +1,183 @@
+// C ABI entry points: argument validation, workspace sizing and dispatch.
+// This translation unit makes no HIP call itself; launches live in the .hip files.
+#include <cstdint>
+#include <cstring>
+
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+bool head_dim_ok(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool ptr_ok(const void* p) { return p != nullptr && aligned16(p); }
+bool opt_ptr_ok(const void* p) { return p == nullptr || aligned16(p); }
+
+size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
+
+}  // namespace
+
+int validate(const gdn_args* a, Entry e, Problem* out) {
+  if (a == nullptr) return GDN_ERR_ARG;
+  if (a->variant < GDN_VARIANT_FG2 || a->variant > GDN_VARIANT_ASYM) return GDN_ERR_ARG;
+  if (a->dtype != GDN_DTYPE_F32 && a->dtype != GDN_DTYPE_BF16) return GDN_ERR_ARG;
+  if (a->B < 1 || a->H < 1 || a->T < 0) return GDN_ERR_ARG;
+  // Keep every element offset far inside int64 and every grid dimension valid.
+  if (a->B > (1 << 20) || a->H > (1 << 16) || a->B * a->H > (1 << 24) ||
+      a->T > (int64_t(1) << 31))
+    return GDN_ERR_UNSUPPORTED;
+  if (!head_dim_ok(a->dk) || !head_dim_ok(a->dv)) return GDN_ERR_UNSUPPORTED;
+  const bool dp = a->variant == GDN_VARIANT_DELTAPRODUCT;
+  if (dp) {
+    if (a->n_h < 1) return GDN_ERR_ARG;
+    if (a->n_h > 8) return GDN_ERR_UNSUPPORTED;
+  } else if (a->n_h != 1) {
+    return GDN_ERR_ARG;
+  }
+  if (e != Entry::Recurrent) {
+    if (a->chunk != 16 && a->chunk != 32 && a->chunk != 64) return GDN_ERR_UNSUPPORTED;
+    if (a->chunk % a->n_h != 0) return GDN_ERR_UNSUPPORTED;
+    if (a->chunk / a->n_h < 16) return GDN_ERR_UNSUPPORTED;  // one 16-row output tile at least
+  }
+  if (a->variant == GDN_VARIANT_FG2 && a->beta_v == nullptr && a->dk != a->dv)
+    return GDN_ERR_ARG;  // one beta vector scales both key and value channels
+  if (a->variant != GDN_VARIANT_FG2 && a->beta_v != nullptr) return GDN_ERR_ARG;
+
+  if (e != Entry::Shapes) {
+    if (!ptr_ok(a->k) || !ptr_ok(a->v) || !ptr_ok(a->alpha)) return GDN_ERR_ARG;
+    if (a->variant == GDN_VARIANT_ASYM) {
+      if (!ptr_ok(a->j) || !ptr_ok(a->eta)) return GDN_ERR_ARG;
+      if (!opt_ptr_ok(a->beta)) return GDN_ERR_ARG;
+    } else {
+      if (!ptr_ok(a->beta)) return GDN_ERR_ARG;
+      if (a->j != nullptr || a->eta != nullptr) return GDN_ERR_ARG;
+    }
+    if (!opt_ptr_ok(a->beta_v)) return GDN_ERR_ARG;
+    if (e != Entry::FinalState) {
+      if (!ptr_ok(a->q) || !ptr_ok(a->o)) return GDN_ERR_ARG;
+    } else {
+      if (!opt_ptr_ok(a->q) || !opt_ptr_ok(a->o)) return GDN_ERR_ARG;
+      if (a->s_final == nullptr) return GDN_ERR_ARG;
+    }
+    if (!opt_ptr_ok(a->s0) || !opt_ptr_ok(a->s_final)) return GDN_ERR_ARG;
+  }
+
+  if (out) {
+    Problem& p = *out;
+    p.variant = a->variant;
+    p.dtype = a->dtype;
+    p.B = a->B;
+    p.T = a->T;
+    p.H = a->H;
+    p.dk = a->dk;
+    p.dv = a->dv;
+    p.chunk = a->chunk;
+    p.n_h = a->n_h;
+    p.q = a->q;
+    p.k = a->k;
+    p.v = a->v;
+    p.alpha = a->alpha;
+    p.beta = a->beta;
+    p.beta_v = a->beta_v;
+    p.j = a->j;
+    p.eta = a->eta;
+    p.s0 = a->s0;
+    p.s_final = a->s_final;
+    p.o = a->o;
+    p.steps = a->T * a->n_h;
+    if (e != Entry::Recurrent) {
+      p.nchunks = (p.steps + a->chunk - 1) / a->chunk;
+      p.rows_out = a->chunk / a->n_h;
+    } else {
+      p.nchunks = 0;
+      p.rows_out = 0;
+    }
+  }
+  return GDN_OK;
+}
+
+ChunkLayout chunk_layout(const Problem& p) {
+  ChunkLayout L{};
+  L.elem = p.dtype == GDN_DTYPE_BF16 ? 2 : 4;
+  const size_t C = size_t(p.chunk), R = size_t(p.rows_out);
+  const size_t dk = size_t(p.dk), dv = size_t(p.dv);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = round_up(off + bytes, 256);
+    return at;
+  };
+  L.off_W = take(C * dk * L.elem);
+  L.off_UT = take(dv * C * L.elem);
+  L.off_AT = take(dk * C * L.elem);
+  L.off_Q = take(R * dk * L.elem);
+  L.off_P = take(R * C * L.elem);
+  L.off_gamma = take(dk * sizeof(float));
+  L.off_qinv = take(R * sizeof(float));
+  L.off_winv = take(4 * sizeof(float));
+  L.bytes = off;
+  return L;
+}
+
+}  // namespace gdn
+
+using gdn::Entry;
+using gdn::Problem;
+
+extern "C" {
+
+size_t gdn_workspace_bytes(const gdn_args* args) {
+  Problem p;
+  if (gdn::validate(args, Entry::Shapes, &p) != GDN_OK) return 0;
+  if (p.nchunks == 0) return 256;
+  const gdn::ChunkLayout L = gdn::chunk_layout(p);
+  return size_t(p.B) * size_t(p.H) * size_t(p.nchunks) * L.bytes;
+}
+
+static int run_chunked(const gdn_args* args, void* ws, size_t ws_bytes, void* stream,
+                       Entry e) {
+  Problem p;
+  int st = gdn::validate(args, e, &p);
+  if (st != GDN_OK) return st;
+  if (p.T == 0) {
+    if (p.s_final == nullptr) return GDN_OK;
+    return gdn::launch_state_copy(p, stream) == 0 ? GDN_OK : GDN_ERR_HIP;
+  }
+  const size_t need = gdn_workspace_bytes(args);
+  if (ws == nullptr || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return GDN_ERR_WORKSPACE;
+  return gdn::launch_chunk(p, ws, e == Entry::ChunkFwd, stream) == 0 ? GDN_OK : GDN_ERR_HIP;
+}
+
+int gdn_chunk_fwd(const gdn_args* args, void* ws, size_t ws_bytes, void* stream) {
+  return run_chunked(args, ws, ws_bytes, stream, Entry::ChunkFwd);
+}
+
+int gdn_final_state(const gdn_args* args, void* ws, size_t ws_bytes, void* stream) {
+  return run_chunked(args, ws, ws_bytes, stream, Entry::FinalState);
+}
+
+int gdn_recurrent_step(const gdn_args* args, float* state_inout, void* stream) {
+  Problem p;
+  int st = gdn::validate(args, Entry::Recurrent, &p);
+  if (st != GDN_OK) return st;
+  if (state_inout == nullptr || (reinterpret_cast<uintptr_t>(state_inout) & 15u) != 0)
+    return GDN_ERR_ARG;
+  if (p.T == 0) return GDN_OK;
+  return gdn::launch_recurrent(p, state_inout, stream) == 0 ? GDN_OK : GDN_ERR_HIP;
+}
+
+const char* gdn_status_str(int status) {
+  switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_ARG: return "invalid argument (null or misaligned pointer, or bad shape)";
+    case GDN_ERR_UNSUPPORTED: return "unsupported size, chunk length or step count";
+    case GDN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case GDN_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+}  // extern "C"

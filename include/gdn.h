@@ -1,0 +1,136 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) gated-delta-rule forward library.
+ *
+ * One recurrence covers every model served here. With S in R^{dk x dv} (rows are
+ * key channels) and per token (or per Householder sub-step) vectors a, b in R^dk,
+ * w in R^dv and a forget vector alpha in (0,1]^dk:
+ *
+ *     S_t = (I - a_t b_t^T) Diag(alpha_t) S_{t-1} + a_t w_t^T,     o_t = S_t^T q_t
+ *
+ *   FG2-GDN   a = b = sqrt(beta) . k,  w = sqrt(beta) . v,  alpha per channel
+ *             (FG2-GDN, "Enhancing Long-Context Gated Delta Networks with Doubly
+ *             Fine-Grained Control": summary section 2, reading notes section 2.2,
+ *             eq. (11)). With beta_v given: w = sqrt(beta_v) . v (FG2-GDN+, eq. (13)).
+ *   KDA       a = b = sqrt(beta) k, w = sqrt(beta) v, beta scalar, alpha per channel
+ *   GDN       as KDA with a scalar alpha (GDN2-stability page, "Problem Description")
+ *   DELTAPRODUCT  n_h steps per token; step i: a = k_i, b = beta_i k_i, w = beta_i v_i;
+ *             the scalar gate alpha acts once per token before step 1; q is read after
+ *             step n_h (DeltaProduct summary, "Approach")
+ *   ASYM      GDN2 / RWKV-7-style  S' = S' D (I - eta j k^T) + eta v k^T, o = S' q
+ *             (GDN2-stability page, eq. (1)); the library state is S = S'^T, so
+ *             a = k, b = eta j, w = eta v, alpha = D.
+ *
+ * Layouts: every array is row-major and contiguous; every pointer is a device
+ * pointer aligned to 16 bytes.
+ *   q, o                      [B, T, H, dk] / [B, T, H, dv]
+ *   k, v (all but DP)         [B, T, H, dk] / [B, T, H, dv]
+ *   k, v (DELTAPRODUCT)       [B, T, H, n_h, dk] / [B, T, H, n_h, dv]
+ *   FG2   alpha, beta         [B, T, H, dk];  beta_v [B, T, H, dv] (optional)
+ *   KDA   alpha [B, T, H, dk];  beta [B, T, H]
+ *   GDN   alpha, beta         [B, T, H]
+ *   DELTAPRODUCT  alpha (gate) [B, T, H];  beta [B, T, H, n_h]
+ *   ASYM  alpha (= D) [B, T, H, dk];  j [B, T, H, dk];  eta [B, T, H]
+ *   s0, s_final, state        [B, H, dk, dv] float32
+ * dtype covers q, k, v, alpha, beta, beta_v, j, eta and o. The state is float32.
+ *
+ * Ownership: the caller owns every buffer, the workspace included. The library
+ * allocates nothing on the device, keeps no state between calls and may be called
+ * from several host threads at once.
+ *
+ * Semantics: calls are asynchronous and stream-ordered (stream is a hipStream_t;
+ * NULL means the default stream); they return after enqueueing and never
+ * synchronise the host. Results are bitwise deterministic for equal inputs and
+ * launch parameters.
+ *
+ * Errors: 0 is success; negative codes below. Arguments are validated before
+ * anything is enqueued: on an error nothing is launched and no output is touched.
+ * Out-of-domain values (beta < 0, alpha outside (0, 1]) are not checked on the
+ * device; they give NaN or Inf. The chunked path factors the decay through one
+ * reference point in the middle of each chunk: it is exact in float32 range when
+ * every channel's summed log-decay over half a chunk stays above -80 (for
+ * chunk = 64 that is a geometric-mean alpha above 0.08 over 32 steps); use a
+ * smaller chunk for stronger decay.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+enum gdn_variant {
+  GDN_VARIANT_FG2 = 0,
+  GDN_VARIANT_KDA = 1,
+  GDN_VARIANT_GDN = 2,
+  GDN_VARIANT_DELTAPRODUCT = 3,
+  GDN_VARIANT_ASYM = 4
+};
+
+enum gdn_dtype { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1 };
+
+enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_ARG = -1,         /* null pointer, bad shape, misaligned pointer     */
+  GDN_ERR_UNSUPPORTED = -2, /* valid but not implemented (size, chunk, n_h)   */
+  GDN_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required     */
+  GDN_ERR_HIP = -4          /* a HIP launch reported an error                 */
+};
+
+typedef struct gdn_args {
+  int32_t variant;  /* enum gdn_variant */
+  int32_t dtype;    /* enum gdn_dtype   */
+  int64_t B, T, H;  /* batch, tokens (T >= 0), heads                          */
+  int64_t dk, dv;   /* key and value head dims, each in {16, 32, 64, 128}     */
+  int32_t chunk;    /* chunk length C in {16, 32, 64} (chunked entry points) */
+  int32_t n_h;      /* Householder steps per token (DELTAPRODUCT), else 1     */
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* alpha;
+  const void* beta;   /* unused by ASYM */
+  const void* beta_v; /* FG2 only, optional (NULL: the value uses beta)       */
+  const void* j;      /* ASYM only */
+  const void* eta;    /* ASYM only */
+  const float* s0;    /* initial state, NULL means zero                        */
+  float* s_final;     /* final state, NULL means not written; may alias s0     */
+  void* o;            /* outputs; ignored by gdn_final_state                   */
+} gdn_args;
+
+/* Bytes of device workspace gdn_chunk_fwd / gdn_final_state need for *args
+ * (0 for an invalid argument set). */
+size_t gdn_workspace_bytes(const gdn_args* args);
+
+/* Chunkwise-parallel forward pass: writes o for all T tokens and, when
+ * s_final != NULL, the state after token T. The sequence is cut into chunks of
+ * `chunk` steps (tokens, or Householder sub-steps for DELTAPRODUCT, whose chunk
+ * must then be a multiple of n_h); inside a chunk the work is parallel (the
+ * WY/UT form of the FG2-GDN reading notes, section 2.4), between chunks the state
+ * is carried. T = 0 copies s0 (or zeros) to s_final. ws must hold
+ * gdn_workspace_bytes(args) bytes and be 256-byte aligned. */
+int gdn_chunk_fwd(const gdn_args* args, void* ws, size_t ws_bytes, void* stream);
+
+/* Same pass computing the final state only (o is not read or written;
+ * s_final must be non-NULL). */
+int gdn_final_state(const gdn_args* args, void* ws, size_t ws_bytes, void* stream);
+
+/* Token-sequential recurrence: advances state_inout ([B, H, dk, dv] float32,
+ * updated in place) by args->T tokens, writing o for each (T = 1 is one decode
+ * step). args->s0, args->s_final and args->chunk are ignored. No workspace. */
+int gdn_recurrent_step(const gdn_args* args, float* state_inout, void* stream);
+
+/* Static text for a status code. */
+const char* gdn_status_str(int status);
+
+/* GDN_ABI_VERSION of the loaded library. */
+int gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

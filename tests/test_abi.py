@@ -1,0 +1,123 @@
+"""The C ABI library loads, exports every function include/gdn.h declares, and its
+host-side argument checks return the documented status before any launch.
+No GPU is touched: every call here fails validation (or the workspace check),
+which happens before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from gated_delta_rule_69_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from gated_delta_rule_69_amd import build
+        build.build()
+    return _lib.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) >= {"gdn_chunk_fwd", "gdn_final_state", "gdn_recurrent_step",
+                          "gdn_workspace_bytes", "gdn_status_str", "gdn_abi_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.gdn_abi_version() == 1
+
+
+def test_status_strings(lib):
+    from gated_delta_rule_69_amd import _lib
+    for code in (0, -1, -2, -3, -4):
+        assert _lib.gdn_status_str(code) != "unknown status"
+    assert _lib.gdn_status_str(7) == "unknown status"
+
+
+FAKE = 1 << 20  # an aligned, never-dereferenced address
+
+
+def good_args(**over):
+    from gated_delta_rule_69_amd._lib import GdnArgs
+    a = GdnArgs()
+    a.variant, a.dtype = 0, 1
+    a.B, a.T, a.H, a.dk, a.dv = 2, 100, 4, 64, 64
+    a.chunk, a.n_h = 64, 1
+    for f in ("q", "k", "v", "alpha", "beta", "o"):
+        setattr(a, f, FAKE)
+    for key, val in over.items():
+        setattr(a, key, val)
+    return a
+
+
+def call_chunk(lib, a, ws=None, nbytes=0):
+    return lib.gdn_chunk_fwd(ctypes.byref(a), ws, nbytes, None)
+
+
+def test_valid_args_reach_the_workspace_check(lib):
+    a = good_args()
+    need = lib.gdn_workspace_bytes(ctypes.byref(a))
+    assert need > 0
+    # 2*4 heads * 2 chunks * record; the record holds at least W, U~, A^, Q+ in fp16
+    assert need >= 2 * 4 * 2 * (4 * 64 * 64 * 2)
+    assert call_chunk(lib, a) == -3
+    assert call_chunk(lib, a, FAKE, need - 1) == -3
+    assert call_chunk(lib, a, FAKE + 16, need) == -3      # not 256-byte aligned
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("variant", 9, -1), ("dtype", 5, -1), ("B", 0, -1), ("H", 0, -1), ("T", -1, -1),
+    ("dk", 48, -2), ("dv", 256, -2), ("chunk", 128, -2), ("chunk", 8, -2), ("n_h", 2, -1),
+    ("k", 0, -1), ("v", FAKE + 4, -1), ("alpha", 0, -1), ("beta", 0, -1), ("q", 0, -1),
+    ("o", 0, -1), ("j", FAKE, -1), ("s0", FAKE + 8, -1), ("beta_v", FAKE + 2, -1),
+])
+def test_rejections(lib, field, value, status):
+    a = good_args(**{field: value})
+    assert call_chunk(lib, a, FAKE, 1 << 40) == status
+
+
+def test_variant_specific_rules(lib):
+    # FG2 with one beta vector needs dk == dv
+    assert call_chunk(lib, good_args(dv=32), FAKE, 1 << 40) == -1
+    # ... but FG2-GDN+ (beta_v) lifts it: reaches the launch, so only check sizing
+    assert lib.gdn_workspace_bytes(ctypes.byref(good_args(dv=32, beta_v=FAKE))) > 0
+    # KDA may not pass beta_v
+    assert call_chunk(lib, good_args(variant=1, beta_v=FAKE), FAKE, 1 << 40) == -1
+    # ASYM needs j and eta
+    assert call_chunk(lib, good_args(variant=4), FAKE, 1 << 40) == -1
+    # DeltaProduct: chunk must be a multiple of n_h with >= 16 output rows
+    dp = dict(variant=3, n_h=3)
+    assert call_chunk(lib, good_args(**dp), FAKE, 1 << 40) == -2
+    assert call_chunk(lib, good_args(variant=3, n_h=8), FAKE, 1 << 40) == -2
+    assert call_chunk(lib, good_args(variant=3, n_h=9), FAKE, 1 << 40) == -2
+    assert call_chunk(lib, good_args(variant=3, n_h=0), FAKE, 1 << 40) == -1
+    assert call_chunk(lib, good_args(variant=3, n_h=2), FAKE, 0) == -3
+
+
+def test_final_state_and_recurrent_checks(lib):
+    a = good_args(q=0, o=0)
+    assert lib.gdn_final_state(ctypes.byref(a), FAKE, 1 << 40, None) == -1  # s_final required
+    a = good_args(q=0, o=0, s_final=FAKE)
+    assert lib.gdn_final_state(ctypes.byref(a), None, 0, None) == -3
+    a = good_args()
+    assert lib.gdn_recurrent_step(ctypes.byref(a), None, None) == -1
+    assert lib.gdn_recurrent_step(ctypes.byref(a), FAKE + 4, None) == -1
+    assert lib.gdn_recurrent_step(ctypes.byref(good_args(variant=3, n_h=9)), FAKE, None) == -2
+    assert lib.gdn_recurrent_step(None, FAKE, None) == -1
+
+
+def test_workspace_bytes_grows_with_tokens(lib):
+    small = lib.gdn_workspace_bytes(ctypes.byref(good_args(T=64)))
+    big = lib.gdn_workspace_bytes(ctypes.byref(good_args(T=6400)))
+    assert big == 100 * small
+    assert lib.gdn_workspace_bytes(ctypes.byref(good_args(dk=48))) == 0
+    assert lib.gdn_workspace_bytes(None) == 0
