@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Throughput of the FG2-GDN chunkwise forward pass on one MI355X.
+
+Workload: the long-context prefill B=2, H=16, T=32768, dk=dv=128, chunk 64, bf16
+inputs, fp32 state, final states returned. One step = one gdn_chunk_fwd call (its
+two stages, gdn_chunk_prepare and gdn_chunk_scan, launched back to back) over
+inputs already resident in HBM.
+
+Prints one JSON line on stdout: tokens/s (B*T per step time), the roofline of the
+dominant kernel from HIP events around each stage inside the timed region, the
+whole path's HBM roofline, a parity check of sampled heads against the float64
+oracle, and the oracle's own throughput on the host cores (a reported baseline).
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import multiprocessing as mp
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gdn_inputs  # noqa: E402
+
+METRIC = "FG²-GDN chunked prefill tokens/s at 32K (H=16,d=128); % of MFMA/HBM roofline"
+WORKLOAD = gdn_inputs.CONFIGS[2]
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "chunk_traffic_fg2_32k.json")
+KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_69_amd", "csrc", "gdn_chunk.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---- algorithmic work per token-head (dk = dv = d, chunk C, bf16 I/O) ----------------
+# prepare: reads q, k, v, alpha, beta (5 d elements); chunk-local products
+#          M, P (C d each, triangular halves), W = T B+, U~ = T Wv (C d each).
+# scan:    W S, A^T U, Q+ S (2 d^2 each) and P U (C d, triangular); writes o (d).
+def prep_bytes_per_th(d, es=2):
+    return 5 * d * es
+
+
+def prep_flops_per_th(d, C):
+    return 4 * C * d
+
+
+def scan_flops_per_th(d, C):
+    return 6 * d * d + C * d
+
+
+def scan_bytes_per_th(d, es=2):
+    return d * es
+
+
+# ---- CPU baseline: the float64 oracle on a bounded sample ---------------------------
+_CPU_INP = None
+
+
+def _oracle_one(args):
+    b, h, T = args
+    from threadpoolctl import threadpool_limits
+    import oracle
+    with threadpool_limits(1):
+        sub = {k: (v[b:b + 1, :T, h:h + 1] if isinstance(v, np.ndarray) else v)
+               for k, v in _CPU_INP.items()}
+        sub["B"], sub["H"], sub["T"] = 1, 1, T
+        t0 = time.perf_counter()
+        o, _ = oracle.forward(sub)
+        return b, h, o[0, :, 0].astype(np.float32), time.perf_counter() - t0
+
+
+def cpu_baseline(inp, T_sample):
+    global _CPU_INP
+    _CPU_INP = inp
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 1
+    workers = max(1, min(16, ncpu))
+    pairs = [(b, h) for b in range(inp["B"]) for h in range(inp["H"])][:workers]
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(workers) as pool:
+        res = pool.map(_oracle_one, [(b, h, T_sample) for b, h in pairs])
+    wall = time.perf_counter() - t0
+    tokens = len(pairs) * T_sample / inp["H"]     # metric tokens carry all H heads
+    return dict(value=tokens / wall, unit="tokens/s", cores=workers, kind="oracle",
+                sample=f"{len(pairs)} of {inp['B'] * inp['H']} (batch, head) sequences, "
+                       f"first {T_sample} tokens each, float64 token loop, one process per core; "
+                       f"wall {wall:.1f} s"), res
+
+
+def read_traffic(launch_units):
+    """HBM bytes per launch from a committed rocprofv3 PMC summary, if it was taken on
+    the current kernel source."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            rec = json.load(f)
+        sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+        if rec.get("source_sha256") != sha:
+            return None
+        return rec.get("traffic_bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=16384)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    W = WORKLOAD
+    B, H, T, d, C = W["B"], W["H"], W["T"], W["dk"], W["chunk"]
+    log(f"bench: generating inputs {W['name']} (seed {W['index']})")
+    inp = gdn_inputs.config_inputs(W["index"])
+
+    cpu = None
+    cpu_res = []
+    if not args.no_cpu_baseline:
+        log("bench: oracle CPU baseline")
+        cpu, cpu_res = cpu_baseline(inp, min(args.cpu_tokens, T))
+        log(f"bench: cpu {cpu['value']:.1f} tokens/s on {cpu['cores']} cores")
+
+    import torch
+    import gated_delta_rule_69_amd as gdn
+    dev = torch.device("cuda:0")
+    tens = {k: torch.from_numpy(inp[k]).to(dev).to(torch.bfloat16).contiguous()
+            for k in ("q", "k", "v", "alpha", "beta")}
+    o = torch.empty((B, T, H, d), dtype=torch.bfloat16, device=dev)
+    s_final = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    a = gdn.make_args("fg2", tens["q"], tens["k"], tens["v"], tens["alpha"], tens["beta"],
+                      chunk=C, s_final=s_final, o=o)
+    ws = torch.empty(gdn.gdn_workspace_bytes(a), dtype=torch.uint8, device=dev)
+    log(f"bench: workspace {ws.numel() / 2**30:.2f} GiB")
+
+    def step(evs=None):
+        if evs:
+            evs[0].record()
+        gdn.gdn_chunk_prepare(a, ws)
+        if evs:
+            evs[1].record()
+        gdn.gdn_chunk_scan(a, ws)
+        if evs:
+            evs[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    log(f"bench: {ms_step:.3f} ms/step (prepare {prep_ms:.3f} ms, scan {scan_ms:.3f} ms)")
+
+    units = B * T * H                                   # token-heads per launch
+    if scan_ms >= prep_ms:
+        flops = scan_flops_per_th(d, C) * units
+        ach = flops / (scan_ms * 1e-3) / 1e12
+        roof = dict(kernel="chunk_scan_kernel", bound="mfma", achieved=ach, peak=MFMA_PEAK_TFLOPS,
+                    unit="TFLOP/s", frac=ach / MFMA_PEAK_TFLOPS, algorithmic=flops)
+    else:
+        nbytes = prep_bytes_per_th(d) * units
+        ach = nbytes / (prep_ms * 1e-3) / 1e9
+        roof = dict(kernel="chunk_prep_kernel", bound="hbm", achieved=ach, peak=HBM_PEAK_GBS,
+                    unit="GB/s", frac=ach / HBM_PEAK_GBS, algorithmic=nbytes)
+    roof["traffic"] = read_traffic(units)
+    path_bytes = (prep_bytes_per_th(d) + scan_bytes_per_th(d)) * units + B * H * d * d * 4
+    path_gbs = path_bytes / (ms_step * 1e-3) / 1e9
+    path = dict(bound="hbm", achieved=path_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=path_gbs / HBM_PEAK_GBS, algorithmic=path_bytes,
+                prepare_ms=prep_ms, scan_ms=scan_ms)
+
+    parity = None
+    if cpu_res:
+        o_host = o.float().cpu().numpy()
+        errs = []
+        for b, h, o_ref, _ in cpu_res:
+            got = o_host[b, :o_ref.shape[0], h]
+            errs.append(float(np.linalg.norm(got - o_ref) / np.linalg.norm(o_ref)))
+        parity = dict(o_rel_l2_max=max(errs), heads=len(errs), tokens=int(cpu_res[0][2].shape[0]),
+                      tolerance=5e-3)
+        log(f"bench: parity vs oracle, max rel-L2 {max(errs):.2e} over {len(errs)} heads")
+
+    out = {
+        "metric": METRIC,
+        "value": B * T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": W["name"], "variant": "fg2", "B": B, "T": T, "H": H, "dk": d,
+                   "dv": d, "chunk": C, "io_dtype": "bf16", "state_dtype": "f32",
+                   "mfma": "fp16 (Gram: bf16 hi/lo split), fp32 accumulate"},
+        "roofline": roof,
+        "path_roofline": path,
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -56,6 +56,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.gdn_chunk_fwd.restype = ctypes.c_int
         lib.gdn_final_state.argtypes = [P, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         lib.gdn_final_state.restype = ctypes.c_int
+        for name in ("gdn_chunk_prepare", "gdn_chunk_scan"):
+            fn = getattr(lib, name)
+            fn.argtypes = [P, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+            fn.restype = ctypes.c_int
         lib.gdn_recurrent_step.argtypes = [P, ctypes.c_void_p, ctypes.c_void_p]
         lib.gdn_recurrent_step.restype = ctypes.c_int
         lib.gdn_status_str.argtypes = [ctypes.c_int]
@@ -208,3 +212,27 @@ def gdn_recurrent_step(variant, q, k, v, alpha, beta=None, *, state, beta_v=None
     if st != 0:
         raise GdnError(st, "gdn_recurrent_step")
     return o
+
+
+def _staged(name, args: GdnArgs, workspace, stream):
+    fn = getattr(load_library(), name)
+    st = fn(ctypes.byref(args), ctypes.c_void_p(workspace.data_ptr()),
+            ctypes.c_size_t(workspace.numel()), _stream(stream))
+    if st != 0:
+        raise GdnError(st, name)
+
+
+def gdn_chunk_prepare(args: GdnArgs, workspace, stream=None):
+    """First stage of gdn_chunk_fwd on prebuilt args (see make_args) and a workspace
+    tensor of at least gdn_workspace_bytes(args) bytes."""
+    _staged("gdn_chunk_prepare", args, workspace, stream)
+
+
+def gdn_chunk_scan(args: GdnArgs, workspace, stream=None):
+    """Second stage of gdn_chunk_fwd (same args and workspace as the prepare call)."""
+    _staged("gdn_chunk_scan", args, workspace, stream)
+
+
+def gdn_chunk_fwd_args(args: GdnArgs, workspace, stream=None):
+    """gdn_chunk_fwd on prebuilt args (no per-call marshalling)."""
+    _staged("gdn_chunk_fwd", args, workspace, stream)

@@ -38,28 +38,37 @@ int validate(const gdn_args* a, Entry e, Problem* out) {
     if (a->chunk != 16 && a->chunk != 32 && a->chunk != 64) return GDN_ERR_UNSUPPORTED;
     if (a->chunk % a->n_h != 0) return GDN_ERR_UNSUPPORTED;
     if (a->chunk / a->n_h < 16) return GDN_ERR_UNSUPPORTED;  // one 16-row output tile at least
+    // fp32 tiles of a 64-step chunk with 128 key channels exceed the 160 KB LDS
+    if (a->dtype == GDN_DTYPE_F32 && a->dk == 128 && a->chunk == 64) return GDN_ERR_UNSUPPORTED;
   }
   if (a->variant == GDN_VARIANT_FG2 && a->beta_v == nullptr && a->dk != a->dv)
     return GDN_ERR_ARG;  // one beta vector scales both key and value channels
   if (a->variant != GDN_VARIANT_FG2 && a->beta_v != nullptr) return GDN_ERR_ARG;
 
   if (e != Entry::Shapes) {
-    if (!ptr_ok(a->k) || !ptr_ok(a->v) || !ptr_ok(a->alpha)) return GDN_ERR_ARG;
+    // With T == 0 the per-token arrays are empty and may be NULL.
+    auto need = [&](const void* p) { return a->T == 0 ? opt_ptr_ok(p) : ptr_ok(p); };
+    if (!need(a->k) || !need(a->v) || !need(a->alpha)) return GDN_ERR_ARG;
     if (a->variant == GDN_VARIANT_ASYM) {
-      if (!ptr_ok(a->j) || !ptr_ok(a->eta)) return GDN_ERR_ARG;
+      if (!need(a->j) || !need(a->eta)) return GDN_ERR_ARG;
       if (!opt_ptr_ok(a->beta)) return GDN_ERR_ARG;
     } else {
-      if (!ptr_ok(a->beta)) return GDN_ERR_ARG;
+      if (!need(a->beta)) return GDN_ERR_ARG;
       if (a->j != nullptr || a->eta != nullptr) return GDN_ERR_ARG;
     }
     if (!opt_ptr_ok(a->beta_v)) return GDN_ERR_ARG;
     if (e != Entry::FinalState) {
-      if (!ptr_ok(a->q) || !ptr_ok(a->o)) return GDN_ERR_ARG;
+      if (!need(a->q) || !need(a->o)) return GDN_ERR_ARG;
     } else {
       if (!opt_ptr_ok(a->q) || !opt_ptr_ok(a->o)) return GDN_ERR_ARG;
       if (a->s_final == nullptr) return GDN_ERR_ARG;
     }
     if (!opt_ptr_ok(a->s0) || !opt_ptr_ok(a->s_final)) return GDN_ERR_ARG;
+  }
+
+  if (e != Entry::Recurrent) {
+    const int64_t nchunks = (a->T * a->n_h + a->chunk - 1) / a->chunk;
+    if (nchunks * a->B * a->H >= (int64_t(1) << 31)) return GDN_ERR_UNSUPPORTED;  // grid size
   }
 
   if (out) {
@@ -134,27 +143,48 @@ size_t gdn_workspace_bytes(const gdn_args* args) {
   return size_t(p.B) * size_t(p.H) * size_t(p.nchunks) * L.bytes;
 }
 
+enum class Stage { Both, Prepare, Scan };
+
 static int run_chunked(const gdn_args* args, void* ws, size_t ws_bytes, void* stream,
-                       Entry e) {
+                       Entry e, Stage stage) {
   Problem p;
   int st = gdn::validate(args, e, &p);
   if (st != GDN_OK) return st;
   if (p.T == 0) {
-    if (p.s_final == nullptr) return GDN_OK;
+    if (p.s_final == nullptr || stage == Stage::Prepare) return GDN_OK;
     return gdn::launch_state_copy(p, stream) == 0 ? GDN_OK : GDN_ERR_HIP;
   }
   const size_t need = gdn_workspace_bytes(args);
   if (ws == nullptr || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
     return GDN_ERR_WORKSPACE;
-  return gdn::launch_chunk(p, ws, e == Entry::ChunkFwd, stream) == 0 ? GDN_OK : GDN_ERR_HIP;
+  const bool want_out = e == Entry::ChunkFwd;
+  int rc = 0;
+  switch (stage) {
+    case Stage::Both: rc = gdn::launch_chunk(p, ws, want_out, stream); break;
+    case Stage::Prepare: rc = gdn::launch_prep(p, ws, want_out, stream); break;
+    case Stage::Scan: rc = gdn::launch_scan(p, ws, want_out, stream); break;
+  }
+  return rc == 0 ? GDN_OK : GDN_ERR_HIP;
 }
 
 int gdn_chunk_fwd(const gdn_args* args, void* ws, size_t ws_bytes, void* stream) {
-  return run_chunked(args, ws, ws_bytes, stream, Entry::ChunkFwd);
+  return run_chunked(args, ws, ws_bytes, stream, Entry::ChunkFwd, Stage::Both);
 }
 
 int gdn_final_state(const gdn_args* args, void* ws, size_t ws_bytes, void* stream) {
-  return run_chunked(args, ws, ws_bytes, stream, Entry::FinalState);
+  return run_chunked(args, ws, ws_bytes, stream, Entry::FinalState, Stage::Both);
+}
+
+static Entry stage_entry(const gdn_args* args) {
+  return (args != nullptr && args->o == nullptr) ? Entry::FinalState : Entry::ChunkFwd;
+}
+
+int gdn_chunk_prepare(const gdn_args* args, void* ws, size_t ws_bytes, void* stream) {
+  return run_chunked(args, ws, ws_bytes, stream, stage_entry(args), Stage::Prepare);
+}
+
+int gdn_chunk_scan(const gdn_args* args, void* ws, size_t ws_bytes, void* stream) {
+  return run_chunked(args, ws, ws_bytes, stream, stage_entry(args), Stage::Scan);
 }
 
 int gdn_recurrent_step(const gdn_args* args, float* state_inout, void* stream) {

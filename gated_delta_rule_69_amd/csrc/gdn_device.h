@@ -111,13 +111,14 @@ __device__ __forceinline__ half8 pack_f16(const float lo[4], const float hi[4]) 
   return r;
 }
 
-// Exact power of two 2^-floor(log2(m)) (1 for m == 0 or non-finite m): multiplying
-// by it maps m into [1, 2) without rounding.
-__device__ __forceinline__ float pow2_scale_for(float m) {
+// Exact power of two that maps m into [2^target, 2^(target+1)) (1 for m == 0 or a
+// non-finite m). Multiplying by it never rounds.
+__device__ __forceinline__ float pow2_scale_for(float m, int target = 0) {
   if (!(m > 0.0f) || !(m < 3.0e38f)) return 1.0f;
   int e;
   frexpf(m, &e);  // m = f * 2^e, f in [0.5, 1)
-  return ldexpf(1.0f, 1 - e);
+  const int x = min(max(target + 1 - e, -100), 100);
+  return ldexpf(1.0f, x);
 }
 
 }  // namespace gdn

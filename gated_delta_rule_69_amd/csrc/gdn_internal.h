@@ -56,6 +56,8 @@ ChunkLayout chunk_layout(const Problem& p);
 // Kernel launchers (defined in the .hip translation units). Return hipError_t as int.
 int launch_recurrent(const Problem& p, float* state, void* stream);
 int launch_chunk(const Problem& p, void* ws, bool want_output, void* stream);
+int launch_prep(const Problem& p, void* ws, bool want_output, void* stream);
+int launch_scan(const Problem& p, void* ws, bool want_output, void* stream);
 int launch_state_copy(const Problem& p, void* stream);
 
 }  // namespace gdn

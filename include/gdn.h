@@ -118,6 +118,17 @@ int gdn_chunk_fwd(const gdn_args* args, void* ws, size_t ws_bytes, void* stream)
  * s_final must be non-NULL). */
 int gdn_final_state(const gdn_args* args, void* ws, size_t ws_bytes, void* stream);
 
+/* The two stages of gdn_chunk_fwd, for callers that schedule them separately
+ * (gdn_chunk_fwd is exactly prepare followed by scan on one stream).
+ * gdn_chunk_prepare runs the chunk-local work (decay cumsum, masked Grams, the
+ * UT inverse T = (I + M)^{-1}, W = T B+, U~ = T Wv; FG2-GDN reading notes,
+ * section 2.4) into ws; gdn_chunk_scan carries the state across chunks and writes
+ * o and s_final. Both take the same args, ws and ws_bytes; with args->o == NULL
+ * the pair computes the final state only (as gdn_final_state). ws must not be
+ * modified between the two calls. */
+int gdn_chunk_prepare(const gdn_args* args, void* ws, size_t ws_bytes, void* stream);
+int gdn_chunk_scan(const gdn_args* args, void* ws, size_t ws_bytes, void* stream);
+
 /* Token-sequential recurrence: advances state_inout ([B, H, dk, dv] float32,
  * updated in place) by args->T tokens, writing o for each (T = 1 is one decode
  * step). args->s0, args->s_final and args->chunk are ignored. No workspace. */
