@@ -13,8 +13,6 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool ptr_ok(const void* p) { return p != nullptr && aligned16(p); }
 bool opt_ptr_ok(const void* p) { return p == nullptr || aligned16(p); }
 
-size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
-
 }  // namespace
 
 int validate(const gdn_args* a, Entry e, Problem* out) {
@@ -106,26 +104,8 @@ int validate(const gdn_args* a, Entry e, Problem* out) {
 }
 
 ChunkLayout chunk_layout(const Problem& p) {
-  ChunkLayout L{};
-  L.elem = p.dtype == GDN_DTYPE_BF16 ? 2 : 4;
-  const size_t C = size_t(p.chunk), R = size_t(p.rows_out);
-  const size_t dk = size_t(p.dk), dv = size_t(p.dv);
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    size_t at = off;
-    off = round_up(off + bytes, 256);
-    return at;
-  };
-  L.off_W = take(C * dk * L.elem);
-  L.off_UT = take(dv * C * L.elem);
-  L.off_AT = take(dk * C * L.elem);
-  L.off_Q = take(R * dk * L.elem);
-  L.off_P = take(R * C * L.elem);
-  L.off_gamma = take(dk * sizeof(float));
-  L.off_qinv = take(R * sizeof(float));
-  L.off_winv = take(4 * sizeof(float));
-  L.bytes = off;
-  return L;
+  return make_chunk_layout(p.dtype == GDN_DTYPE_BF16 ? 2 : 4, size_t(p.dk), size_t(p.dv),
+                           size_t(p.chunk));
 }
 
 }  // namespace gdn

@@ -70,10 +70,14 @@ __device__ __forceinline__ float sum_over_groups(float x) {
   x += __shfl_xor(x, 32, 64);
   return x;
 }
+// Max over the same four lanes with the gfx950 lane-swap instructions (no LDS):
+// v_permlane32_swap pairs lane l with l^32 and v_permlane16_swap pairs l with l^16;
+// the maximum of the two swapped registers is the pair's maximum in every lane.
 __device__ __forceinline__ float max_over_groups(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16, 64));
-  x = fmaxf(x, __shfl_xor(x, 32, 64));
-  return x;
+  const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+  const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
 }
 
 // ---- MFMA wrappers -------------------------------------------------------------

@@ -38,19 +38,40 @@ enum class Entry { ChunkFwd, FinalState, Recurrent, Shapes };
 // Pure argument checks; no HIP call. Returns GDN_OK or a negative status.
 int validate(const gdn_args* a, Entry e, Problem* out);
 
-// Per-chunk workspace record (bytes) and the offsets of its parts.
+// Per-chunk workspace record. Its first part is byte-for-byte the LDS image the
+// scan kernel stages (padded rows), so staging is a flat copy:
+//   W     [C][dk+4]   A^^T [dk][C+4]   gamma [dk] f32   1/ws [4] f32     (state image)
+//   Q+    [C][dk+4]   P    [C][C+4]    1/qs  [C] f32                      (output part)
+// followed by U~^T [dv][C] (read straight into registers). Elements are fp16
+// (bf16 inputs) or fp32 (fp32 inputs).
 struct ChunkLayout {
-  size_t elem;        // 2 (fp16 operands) or 4 (fp32 operands)
-  size_t off_W;       // W      [C][dk]
-  size_t off_UT;      // U~^T   [dv][C]
-  size_t off_AT;      // A^^T   [dk][C]
-  size_t off_Q;       // Q+     [R][dk]
-  size_t off_P;       // P      [R][C]
-  size_t off_gamma;   // gamma  [dk] float
-  size_t off_qinv;    // per-output-row inverse q scale [R] float
-  size_t off_winv;    // per-chunk inverse w scale      [4] float
-  size_t bytes;       // record size (multiple of 256)
+  size_t elem, ldk, ldc;
+  size_t off_W, off_AT, off_gamma, off_winv, state_bytes;
+  size_t off_Q, off_P, off_qinv, image_bytes;
+  size_t off_UT, bytes;
 };
+
+constexpr size_t round_up_c(size_t x, size_t m) { return (x + m - 1) / m * m; }
+
+constexpr ChunkLayout make_chunk_layout(size_t es, size_t dk, size_t dv, size_t C) {
+  ChunkLayout L{};
+  L.elem = es;
+  L.ldk = dk + 4;
+  L.ldc = C + 4;
+  L.off_W = 0;
+  L.off_AT = L.off_W + C * L.ldk * es;
+  L.off_gamma = L.off_AT + dk * L.ldc * es;
+  L.off_winv = L.off_gamma + dk * 4;
+  L.state_bytes = L.off_winv + 16;
+  L.off_Q = L.state_bytes;
+  L.off_P = L.off_Q + C * L.ldk * es;
+  L.off_qinv = L.off_P + C * L.ldc * es;
+  L.image_bytes = L.off_qinv + C * 4;
+  L.off_UT = round_up_c(L.image_bytes, 256);
+  L.bytes = round_up_c(L.off_UT + dv * C * es, 256);
+  return L;
+}
+
 ChunkLayout chunk_layout(const Problem& p);
 
 // Kernel launchers (defined in the .hip translation units). Return hipError_t as int.
