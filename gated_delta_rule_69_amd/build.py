@@ -20,7 +20,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 INCLUDE = os.path.join(ROOT, "include")
 
-SOURCES = ["gdn_api.cpp", "gdn_recurrent.hip", "gdn_chunk.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_recurrent.hip", "gdn_chunk.hip", "gdn_prep_fg2.hip", "gdn_prep_kda.hip",
+           "gdn_prep_gdn.hip", "gdn_prep_dp.hip", "gdn_prep_asym.hip"]
 ARCH = "gfx950"
 # Packed fp32 instructions are disabled for every device compile.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",

@@ -1,0 +1,988 @@
+// Chunkwise-parallel forward pass (WY / UT form): device code shared by the
+// per-variant preparation units (gdn_prep_*.hip) and the scan unit (gdn_chunk.hip).
+//
+// Unified step (gdn.h): S_t = (I - a_t b_t^T) Diag(alpha_t) S_{t-1} + a_t w_t^T,
+// o_t = S_t^T q_t. Take a chunk of C steps with start state S and inclusive
+// cumulative log-decay G_r = sum_{s<=r} log alpha_s (per key channel). Writing
+// u_r for the correction of step r (S_r = Diag(alpha_r) S_{r-1} + a_r u_r^T),
+//   u_r = w_r - S^T (b_r . e^{G_r}) - sum_{s<r} <b_r . e^{G_r}, a_s . e^{-G_s}> u_s,
+// so with B+ = B . e^G, A- = A . e^{-G}, M = strict_tril(B+ A-^T) and
+// T = (I + M)^{-1} (unit lower triangular):
+//   U = U~ - W S,   U~ = T Wv,   W = T B+
+//   S' = Diag(e^{G_C}) S + A^^T U,          A^ = A . e^{G_C - G}
+//   O  = Q+ S + P U,  Q+ = Q . e^{G},  P = tril_incl(Q+ A-^T)
+// This is the diagonal-plus-rank-1 chunk recursion that the FG2-GDN reading
+// notes (section 2.4) inherit from KDA's WY/UT algorithm, written out for the
+// unified step. The Gram factors use a reference point in the middle of the
+// chunk (e^{G - G_mid}, e^{G_mid - G}) so that no factor exceeds the decay
+// accumulated over half a chunk.
+//
+// Kernel 1 (chunk_prep): persistent; each workgroup walks chunks. Wave w owns
+// rows 16w..16w+15 of the chunk: it loads them straight into registers (16-byte
+// fragments, the next chunk's rows in flight while the current one is processed),
+// scans the log decay over its rows with DPP row shifts, and forms the decayed
+// operands. LDS carries only what crosses waves (per-channel decay constants, A-
+// for the Grams, B+ and Wv transposed, then M and T). It writes one record per
+// chunk (gdn_internal.h). The variant is a template parameter: one translation
+// unit per variant.
+// Kernel 2 (chunk_scan): one workgroup per (batch*head, 64 value columns); each
+// wave owns 16 value columns and carries its dk x 16 fp32 state slice in MFMA
+// accumulator registers across all chunks. The next chunk's record is copied
+// into LDS (a flat image) while the current one is processed.
+//
+// Precision (bf16 inputs): the Gram products run as bf16 hi/lo splits (three
+// bf16 MFMAs, about 16 mantissa bits, full fp32 range); every other product runs
+// on fp16 MFMA with fp32 accumulation. Quantities whose scale follows the
+// caller's values (v, q, the state, U) are multiplied by exact powers of two
+// before the fp16 conversion and divided back after the product, so fp16's
+// range never clips them. fp32 inputs use fp32 MFMA throughout.
+#pragma once
+
+#include <algorithm>
+#include <type_traits>
+
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+// The state and U enter fp16 MFMAs with their per-column maximum scaled into
+// [2^12, 2^13): far below fp16's 65504 and well above its subnormal range.
+constexpr int kStateScaleExp = 12;
+
+union H8 {
+  half8 h;
+  bhalf8 b;
+  uint2 u[2];
+  uint4 q;
+};
+
+// ---- lane channel maps -------------------------------------------------------------
+// A lane (i = lane % 16, g = lane / 16) of the wave that owns a 16-row tile holds
+// NX = D / 4 channels of its row, in 16-byte groups:
+//   bf16 rows:  UW = min(8, D/4) consecutive channels per group, channel of value x
+//               = (x / UW) * 4 UW + UW g + x % UW  (the natural k order of the
+//               16x16x32 MFMA: slot s of k-block u is channel 32 u + 8 g + s)
+//   fp32 rows:  4 consecutive channels per group, channel = (x / 4) 16 + 4 g + x % 4
+//               (slot g of the e-th 16x16x4 MFMA of slice t is channel 16 t + 4 g + e)
+template <bool F16, int D>
+struct ChanMap {
+  static constexpr int NX = D / 4;
+  static constexpr int UW = F16 ? (NX < 8 ? NX : 8) : 4;
+  static constexpr int NU = NX / UW;
+  __device__ static constexpr int chan(int g, int x) {
+    return (x / UW) * 4 * UW + UW * g + (x % UW);
+  }
+};
+
+// Load group u (UW consecutive channels) of the lane's channels of a row (fp32 out).
+template <bool F16, int D, typename In>
+__device__ __forceinline__ void load_unit(const In* row, int g, int u, float* out) {
+  using M = ChanMap<F16, D>;
+  const In* p = row + u * 4 * M::UW + M::UW * g;
+  if constexpr (std::is_same<In, float>::value) {
+    const float4 x = *reinterpret_cast<const float4*>(p);
+    out[0] = x.x;
+    out[1] = x.y;
+    out[2] = x.z;
+    out[3] = x.w;
+  } else if constexpr (M::UW == 8) {
+    const uint4 x = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      out[2 * e] = __uint_as_float(w[e] << 16);
+      out[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+  } else {
+    const uint2 x = *reinterpret_cast<const uint2*>(p);
+    out[0] = __uint_as_float(x.x << 16);
+    out[1] = __uint_as_float(x.x & 0xffff0000u);
+    out[2] = __uint_as_float(x.y << 16);
+    out[3] = __uint_as_float(x.y & 0xffff0000u);
+  }
+}
+
+// All NX channels of the lane's row.
+template <bool F16, int D, typename In>
+__device__ __forceinline__ void load_row(const In* row, int g, float* out) {
+  using M = ChanMap<F16, D>;
+#pragma unroll
+  for (int u = 0; u < M::NU; ++u) load_unit<F16, D>(row, g, u, out + u * M::UW);
+}
+
+// Written values w of one row (the lane's DV/4 value channels), vector loads.
+// Returns max |w| (pass 0) or stores fp16/fp32 w * scale transposed into wvt
+// (pass 1).
+template <bool F16, int DVT, typename In, typename Op, int LDC>
+__device__ __forceinline__ float row_values(int variant, const In* vrow, const In* brow, int bstride_dk,
+                                            const In* bvrow, float wscal, bool valid, int g, int r,
+                                            float scale, Op (*wvt)[LDC], bool store) {
+  using M = ChanMap<F16, DVT>;
+  float w[M::NX];
+#pragma unroll
+  for (int x = 0; x < M::NX; ++x) w[x] = 0.0f;
+  if (valid) {
+    load_row<F16, DVT>(vrow, g, w);
+    if (variant == GDN_VARIANT_FG2) {
+      float bq[M::NX];
+      load_row<F16, DVT>(bvrow ? bvrow : brow, g, bq);
+#pragma unroll
+      for (int x = 0; x < M::NX; ++x) w[x] *= sqrtf(bq[x]);
+    } else {
+#pragma unroll
+      for (int x = 0; x < M::NX; ++x) w[x] *= wscal;
+    }
+  }
+  (void)bstride_dk;
+  float mx = 0.0f;
+#pragma unroll
+  for (int x = 0; x < M::NX; ++x) {
+    mx = fmaxf(mx, fabsf(w[x]));
+    if (store) wvt[M::chan(g, x)][r] = (Op)(w[x] * scale);
+  }
+  return mx;
+}
+
+__device__ __forceinline__ void quad(const float* p, float out[4]) {
+  const float4 x = *reinterpret_cast<const float4*>(p);
+  out[0] = x.x;
+  out[1] = x.y;
+  out[2] = x.z;
+  out[3] = x.w;
+}
+
+// Eight 16-bit operand values: 4 at p0 and 4 at p1 (or zeros).
+__device__ __forceinline__ H8 pair4(const void* p0, const void* p1) {
+  H8 r;
+  r.u[0] = *reinterpret_cast<const uint2*>(p0);
+  r.u[1] = p1 ? *reinterpret_cast<const uint2*>(p1) : make_uint2(0u, 0u);
+  return r;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+  return x;
+}
+
+// Inclusive prefix sum over the 16 lanes of each DPP row (lanes 16 g .. 16 g + 15,
+// the rows of a tile): four row-shift adds; lanes shifted in from outside the row
+// read zero (bound control).
+__device__ __forceinline__ float scan16(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, true));
+  return x;
+}
+
+inline int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 256;
+  return cus;
+}
+
+// ---- kernel 1: chunk-local preparation -----------------------------------------------
+
+// The log decay is kept in base 2 on the bf16 path (hardware log2 / exp2 / rcp /
+// sqrt: one instruction each, about 1 ulp) and in base e with the accurate library
+// calls on the fp32 path.
+template <bool F16>
+__device__ __forceinline__ float path_log(float x) {
+  if constexpr (F16) return __builtin_amdgcn_logf(x);
+  else return logf(x);
+}
+template <bool F16>
+__device__ __forceinline__ float path_exp(float x) {
+  if constexpr (F16) return __builtin_amdgcn_exp2f(x);
+  else return expf(x);
+}
+template <bool F16>
+__device__ __forceinline__ float path_sqrt(float x) {
+  if constexpr (F16) return __builtin_amdgcn_sqrtf(x);
+  else return sqrtf(x);
+}
+
+// Value x (compile-time after unrolling) of bf16 groups held as uint4 (8 per group).
+__device__ __forceinline__ float bf16_at(const uint4* v, int x) {
+  const uint4 w = v[x / 8];
+  const uint32_t word = (x % 8) / 2 == 0 ? w.x : (x % 8) / 2 == 1 ? w.y : (x % 8) / 2 == 2 ? w.z : w.w;
+  return __uint_as_float((x & 1) ? (word & 0xffff0000u) : (word << 16));
+}
+
+// Raw bf16 inputs of one step row, loaded one chunk ahead of use.
+template <int DK>
+struct RawRow {
+  using KM = ChanMap<true, DK>;
+  static constexpr int KU = KM::UW == 8 ? KM::NU : 1;  // uint4 groups per key row
+  uint4 k[KU], a[KU], bj[KU], q[KU];
+  uint4 v[4], bv[4];
+  float s_alpha, s_beta, s_eta;
+};
+
+template <bool F16, int DK, int C, bool DPV>
+struct alignas(16) PrepLds {
+  using Op = std::conditional_t<F16, _Float16, float>;
+  using Am = std::conditional_t<F16, __bf16, float>;
+  static constexpr int NT = C / 16;
+  static constexpr int LDA = F16 ? DK + 8 : DK + 4;  // rows of A- (16-byte aligned)
+  static constexpr int LDC = C + 4;
+  static constexpr int QR = DPV ? C / 2 : 1;         // output rows kept in LDS (n_h >= 2)
+  union RA {
+    struct {
+      Am hi[C][LDA];
+      Am lo[F16 ? C : 1][LDA];
+    } am;                      // A- (mid reference), Gram phase
+    struct {
+      float m[C][LDC];         // strictly lower Gram M; T in fp16 after the inverse
+      float t[C][LDC];         // T = (I + M)^{-1}
+    } mt;
+  } ra;
+  Op bt[DK][LDC];              // B+ (chunk-start reference), transposed
+  Op wvt[128][LDC];            // written values (scaled), transposed
+  Op at[DK][LDC];              // A^ transposed, staged for a coalesced copy to the record
+  Am qmh[QR][LDA];             // Q+ (mid reference) of output rows, DeltaProduct only
+  Am qml[(DPV && F16) ? QR : 1][LDA];
+  float tot[NT][DK];           // per-tile totals of the log decay
+  float gmid_loc[DK];          // in-tile prefix at the middle row
+  // per-channel decay constants. bf16 path (base 2): [t] = G_mid - (prefix before
+  // tile t), [NT] = 2^G_mid, [NT+1] = 2^(G_C - G_mid). fp32 path (base e): [t] =
+  // prefix before tile t, [NT] = G_mid, [NT+1] = G_C.
+  float chv[NT + 2][DK];
+  float qs[C];                 // per output row q scale
+  float red[kWaves];
+};
+
+// V: the variant (gdn_variant); DPV: DeltaProduct with n_h >= 2 (output rows are
+// every n_h-th step row).
+template <typename In, int DK, int C, int V, bool DPV>
+__global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigned char* __restrict__ ws,
+                                                              ChunkLayout L, int want_out) {
+  constexpr bool F16 = std::is_same<In, uint16_t>::value;
+  constexpr bool DP = V == GDN_VARIANT_DELTAPRODUCT;
+  static_assert(!DPV || DP, "multi-step rows are DeltaProduct only");
+  constexpr bool CH_ALPHA = V == GDN_VARIANT_FG2 || V == GDN_VARIANT_KDA || V == GDN_VARIANT_ASYM;
+  constexpr bool CH_BJ = V == GDN_VARIANT_FG2 || V == GDN_VARIANT_ASYM;  // per-channel beta / j
+  using Sm = PrepLds<F16, DK, C, DPV>;
+  using Op = typename Sm::Op;
+  using KM = ChanMap<F16, DK>;
+  using Raw = RawRow<DK>;
+  constexpr int NX = KM::NX;
+  constexpr int UW = KM::UW;
+  constexpr int NT = C / 16;
+  constexpr int KB = F16 ? (DK + 31) / 32 : DK / 16;  // k-blocks (F16) or slices (F32) of a key row
+  static_assert(sizeof(Sm) <= 160 * 1024, "LDS budget");
+  static_assert(NT <= kWaves, "one wave per 16-row tile");
+  static_assert(DK <= kThreads, "one thread per channel for the decay constants");
+  __shared__ Sm sm;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int n_h = DPV ? p.n_h : 1;
+  const int R = p.rows_out, RT = R / 16;
+  const int dv = int(p.dv);
+  const int NC = int(p.nchunks);
+  const int H = int(p.H);
+  const int total = NC * int(p.B) * H;  // < 2^31 (checked on the host)
+  const int mid = C / 2 - 1, tile_mid = mid / 16, row_mid = mid % 16;
+  const In* qg = static_cast<const In*>(p.q);
+  const In* kg = static_cast<const In*>(p.k);
+  const In* vg = static_cast<const In*>(p.v);
+  const In* alg = static_cast<const In*>(p.alpha);
+  const In* beg = static_cast<const In*>(p.beta);
+  const In* bvg = static_cast<const In*>(p.beta_v);
+  const In* jg = static_cast<const In*>(p.j);
+  const In* etg = static_cast<const In*>(p.eta);
+  const bool owner = wave < NT;
+  const int r = 16 * wave + li;  // virtual row (step) in the chunk owned by this lane
+  // FG2 with its own value-side beta; otherwise (dk == dv) the key-side sqrt(beta)
+  // of the same channel scales the value
+  const bool bv_sep = V == GDN_VARIANT_FG2 && bvg != nullptr;
+  // value-row groups: 8 bf16 channels (32 u + 8 g + s) per uint4, or 4 (4 g + s) when dv == 16
+  const int vuw = (F16 && dv == 16) ? 4 : 8;
+  const int vnu = F16 ? (dv == 16 ? 1 : dv / 32) : 0;
+  auto ld = [](const In* x) { return IO<In>::ld(x); };
+
+  struct Where {
+    bool valid, out_row;
+    int64_t th, vrow;
+    int sub, ro;
+  };
+  auto where = [&](int item) __attribute__((always_inline)) -> Where {
+    Where w;
+    const int bh = item / NC, n = item - bh * NC;
+    const int b = bh / H, h = bh - b * H;
+    const int64_t vs = int64_t(n) * C + r;
+    w.valid = owner && vs < p.steps;
+    int64_t tok = vs;
+    w.sub = 0;
+    if constexpr (DPV) {
+      tok = vs / n_h;
+      w.sub = int(vs - tok * n_h);
+    }
+    w.th = (int64_t(b) * p.T + tok) * H + h;
+    w.vrow = DP ? w.th * p.n_h + w.sub : w.th;
+    w.out_row = want_out && owner && w.sub == n_h - 1;
+    w.ro = DPV ? r / n_h : r;
+    return w;
+  };
+  // Issue every load of this lane's row of `item` (bf16 rows only; fp32 rows are
+  // read where they are used).
+  auto prefetch = [&](int item, Raw& raw) __attribute__((always_inline)) {
+    if constexpr (F16) {
+      const Where w = where(item);
+      if (!w.valid) return;
+      auto ld_row = [&](const In* row, uint4* dst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < Raw::KU; ++u) {
+          if constexpr (UW == 8) {
+            dst[u] = *reinterpret_cast<const uint4*>(row + u * 32 + 8 * lg);
+          } else {
+            const uint2 x = *reinterpret_cast<const uint2*>(row + 4 * lg);
+            dst[u] = make_uint4(x.x, x.y, 0u, 0u);
+          }
+        }
+      };
+      ld_row(kg + w.vrow * DK, raw.k);
+      if constexpr (CH_ALPHA) ld_row(alg + w.th * DK, raw.a);
+      else raw.s_alpha = ld(alg + w.th);
+      if constexpr (V == GDN_VARIANT_FG2) ld_row(beg + w.th * DK, raw.bj);
+      if constexpr (V == GDN_VARIANT_ASYM) {
+        ld_row(jg + w.th * DK, raw.bj);
+        raw.s_eta = ld(etg + w.th);
+      }
+      if constexpr (V == GDN_VARIANT_KDA || V == GDN_VARIANT_GDN) raw.s_beta = ld(beg + w.th);
+      if constexpr (DP) raw.s_beta = ld(beg + w.vrow);
+      if (w.out_row) ld_row(qg + w.th * DK, raw.q);
+      const In* vrow = vg + w.vrow * dv;
+      const In* bvrow = bvg + w.th * dv;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (u < vnu) {
+          if (vuw == 8) {
+            raw.v[u] = *reinterpret_cast<const uint4*>(vrow + u * 32 + 8 * lg);
+            if (bv_sep) raw.bv[u] = *reinterpret_cast<const uint4*>(bvrow + u * 32 + 8 * lg);
+          } else {
+            const uint2 x = *reinterpret_cast<const uint2*>(vrow + 4 * lg);
+            raw.v[u] = make_uint4(x.x, x.y, 0u, 0u);
+            if (bv_sep) {
+              const uint2 y = *reinterpret_cast<const uint2*>(bvrow + 4 * lg);
+              raw.bv[u] = make_uint4(y.x, y.y, 0u, 0u);
+            }
+          }
+        }
+      }
+    }
+  };
+
+  Raw raw;
+  if (int(blockIdx.x) < total) prefetch(blockIdx.x, raw);
+
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    const Where w = where(item);
+    unsigned char* rec = ws + size_t(item) * L.bytes;
+    Op* W_g = reinterpret_cast<Op*>(rec + L.off_W);
+    Op* AT_g = reinterpret_cast<Op*>(rec + L.off_AT);
+    Op* Q_g = reinterpret_cast<Op*>(rec + L.off_Q);
+    Op* P_g = reinterpret_cast<Op*>(rec + L.off_P);
+    Op* UT_g = reinterpret_cast<Op*>(rec + L.off_UT);
+    float* gam_g = reinterpret_cast<float*>(rec + L.off_gamma);
+    float* winv_g = reinterpret_cast<float*>(rec + L.off_winv);
+    float* qinv_g = reinterpret_cast<float*>(rec + L.off_qinv);
+
+    // ---- this lane's row: write key a, erase key bb, log decay G, query, values ----
+    float a[NX], bb[NX], G[NX], qv[NX];
+    float wv[32];  // written values (bf16 path; the fp32 path reads them later)
+#pragma unroll
+    for (int x = 0; x < NX; ++x) a[x] = bb[x] = G[x] = qv[x] = 0.0f;
+#pragma unroll
+    for (int x = 0; x < 32; ++x) wv[x] = 0.0f;
+    float wscal = 0.0f;
+    if (w.valid) {
+      float kf[NX], af[NX], bf[NX];
+      float sa = 0.0f, sbt = 0.0f, seta = 0.0f;
+      if constexpr (F16) {
+#pragma unroll
+        for (int x = 0; x < NX; ++x) {
+          kf[x] = bf16_at(raw.k, x);
+          af[x] = CH_ALPHA ? bf16_at(raw.a, x) : 0.0f;
+          bf[x] = CH_BJ ? bf16_at(raw.bj, x) : 0.0f;
+        }
+        sa = raw.s_alpha;
+        sbt = raw.s_beta;
+        seta = raw.s_eta;
+        if (w.out_row) {
+#pragma unroll
+          for (int x = 0; x < NX; ++x) qv[x] = bf16_at(raw.q, x);
+        }
+      } else {
+        load_row<F16, DK>(kg + w.vrow * DK, lg, kf);
+        if constexpr (CH_ALPHA) load_row<F16, DK>(alg + w.th * DK, lg, af);
+        else sa = ld(alg + w.th);
+        if constexpr (V == GDN_VARIANT_FG2) load_row<F16, DK>(beg + w.th * DK, lg, bf);
+        if constexpr (V == GDN_VARIANT_ASYM) {
+          load_row<F16, DK>(jg + w.th * DK, lg, bf);
+          seta = ld(etg + w.th);
+        }
+        if constexpr (V == GDN_VARIANT_KDA || V == GDN_VARIANT_GDN) sbt = ld(beg + w.th);
+        if constexpr (DP) sbt = ld(beg + w.vrow);
+        if (w.out_row) load_row<F16, DK>(qg + w.th * DK, lg, qv);
+      }
+      float sbk[NX];  // FG2: sqrt(beta) per key channel
+#pragma unroll
+      for (int x = 0; x < NX; ++x) {
+        if constexpr (V == GDN_VARIANT_FG2) {
+          sbk[x] = path_sqrt<F16>(bf[x]);
+          a[x] = sbk[x] * kf[x];
+          bb[x] = a[x];
+          G[x] = path_log<F16>(af[x]);
+        } else if constexpr (V == GDN_VARIANT_KDA || V == GDN_VARIANT_GDN) {
+          a[x] = kf[x];  // scaled by sqrt(beta) below
+          G[x] = V == GDN_VARIANT_KDA ? path_log<F16>(af[x]) : 0.0f;
+        } else if constexpr (DP) {
+          a[x] = kf[x];
+          bb[x] = sbt * kf[x];
+        } else {  // ASYM
+          a[x] = kf[x];
+          bb[x] = seta * bf[x];
+          G[x] = path_log<F16>(af[x]);
+        }
+      }
+      if constexpr (V == GDN_VARIANT_KDA || V == GDN_VARIANT_GDN) {
+        const float sb = path_sqrt<F16>(sbt);
+        const float lga = V == GDN_VARIANT_GDN ? path_log<F16>(sa) : 0.0f;
+#pragma unroll
+        for (int x = 0; x < NX; ++x) {
+          a[x] *= sb;
+          bb[x] = a[x];
+          if constexpr (V == GDN_VARIANT_GDN) G[x] = lga;
+        }
+        wscal = sb;
+      } else if constexpr (DP) {
+        const float lgate = w.sub == 0 ? path_log<F16>(sa) : 0.0f;
+#pragma unroll
+        for (int x = 0; x < NX; ++x) G[x] = lgate;
+        wscal = sbt;
+      } else if constexpr (V == GDN_VARIANT_ASYM) {
+        wscal = seta;
+      }
+      if constexpr (F16) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (u < vnu) {
+#pragma unroll
+            for (int s2 = 0; s2 < 8; ++s2) {
+              const int y = 8 * u + s2;
+              float f = wscal;
+              if constexpr (V == GDN_VARIANT_FG2)
+                f = bv_sep ? path_sqrt<F16>(bf16_at(raw.bv, y)) : sbk[y < NX ? y : 0];
+              wv[y] = (vuw == 8 || s2 < 4) ? bf16_at(raw.v, y) * f : 0.0f;
+            }
+          }
+        }
+      }
+    }
+
+    // inclusive scan of the log decay over the tile's 16 rows, then tile totals
+#pragma unroll
+    for (int x = 0; x < NX; ++x) G[x] = scan16(G[x]);
+    if (owner && li == 15) {
+#pragma unroll
+      for (int x = 0; x < NX; ++x) sm.tot[wave][KM::chan(lg, x)] = G[x];
+    }
+    if (owner && wave == tile_mid && li == row_mid) {
+#pragma unroll
+      for (int x = 0; x < NX; ++x) sm.gmid_loc[KM::chan(lg, x)] = G[x];
+    }
+    // power-of-two scales: per output row for q, per chunk for the written values
+    float qsc = 1.0f;
+    float wmax = 0.0f;
+    if constexpr (F16) {
+      if (owner && want_out) {
+        float mx = 0.0f;
+#pragma unroll
+        for (int x = 0; x < NX; ++x) mx = fmaxf(mx, fabsf(qv[x]));
+        qsc = pow2_scale_for(max_over_groups(mx));
+      }
+#pragma unroll
+      for (int x = 0; x < 32; ++x) wmax = fmaxf(wmax, fabsf(wv[x]));
+      wmax = wave_max(wmax);
+      if (lane == 0) sm.red[wave] = wmax;
+    }
+    __syncthreads();
+
+    // ---- per-channel decay constants (one thread per key channel) ----
+    if (tid < DK) {
+      const int c = tid;
+      float pre = 0.0f, gm = sm.gmid_loc[c];
+      float pres[NT];
+#pragma unroll
+      for (int I = 0; I < NT; ++I) {
+        pres[I] = pre;
+        if (I < tile_mid) gm += sm.tot[I][c];
+        pre += sm.tot[I][c];
+      }
+      const float ge = pre;
+      if constexpr (F16) {
+#pragma unroll
+        for (int I = 0; I < NT; ++I) sm.chv[I][c] = gm - pres[I];
+        sm.chv[NT][c] = path_exp<F16>(gm);
+        sm.chv[NT + 1][c] = path_exp<F16>(ge - gm);
+      } else {
+#pragma unroll
+        for (int I = 0; I < NT; ++I) sm.chv[I][c] = pres[I];
+        sm.chv[NT][c] = gm;
+        sm.chv[NT + 1][c] = ge;
+      }
+      gam_g[c] = path_exp<F16>(ge);
+    }
+    float wsc = 1.0f;
+    if constexpr (F16) {
+      float m = sm.red[0];
+#pragma unroll
+      for (int w2 = 1; w2 < kWaves; ++w2) m = fmaxf(m, sm.red[w2]);
+      wsc = pow2_scale_for(m);
+    }
+    if (tid == 0) winv_g[0] = 1.0f / wsc;
+    __syncthreads();
+
+    // ---- decayed operands of this wave's rows ----
+    float bm[NX];  // B+ with the mid reference: B-side of M
+    float qm[NX];  // Q+ with the mid reference: B-side of P
+#pragma unroll
+    for (int x = 0; x < NX; ++x) bm[x] = qm[x] = 0.0f;
+    if (owner) {
+#pragma unroll
+      for (int u = 0; u < NX / UW; ++u) {
+        const int c0 = KM::chan(lg, u * UW);  // UW consecutive channels
+        float cof[UW], cp[UW], cq[UW];
+#pragma unroll
+        for (int e = 0; e < UW; e += 4) {
+          const float4 x0 = *reinterpret_cast<const float4*>(&sm.chv[wave][c0 + e]);
+          const float4 x1 = *reinterpret_cast<const float4*>(&sm.chv[NT][c0 + e]);
+          const float4 x2 = *reinterpret_cast<const float4*>(&sm.chv[NT + 1][c0 + e]);
+          cof[e] = x0.x, cof[e + 1] = x0.y, cof[e + 2] = x0.z, cof[e + 3] = x0.w;
+          cp[e] = x1.x, cp[e + 1] = x1.y, cp[e + 2] = x1.z, cp[e + 3] = x1.w;
+          cq[e] = x2.x, cq[e + 1] = x2.y, cq[e + 2] = x2.z, cq[e + 3] = x2.w;
+        }
+        float amv[UW];
+#pragma unroll
+        for (int e = 0; e < UW; ++e) {
+          const int x = u * UW + e, c = c0 + e;
+          float fup, eg, eat, eam;
+          if constexpr (F16) {
+            fup = path_exp<F16>(G[x] - cof[e]);  // e^{G - G_mid}
+            eam = __builtin_amdgcn_rcpf(fup);    // e^{G_mid - G}
+            eg = cp[e] * fup;                    // e^{G}
+            eat = cq[e] * eam;                   // e^{G_C - G}
+          } else {
+            const float g = G[x] + cof[e];
+            fup = expf(g - cp[e]);
+            eg = expf(g);
+            eat = expf(cq[e] - g);
+            eam = expf(cp[e] - g);
+          }
+          bm[x] = bb[x] * fup;
+          sm.bt[c][r] = (Op)(bb[x] * eg);
+          sm.at[c][r] = (Op)(a[x] * eat);
+          amv[e] = a[x] * eam;
+          qm[x] = qv[x] * fup;
+          qv[x] = qv[x] * eg * qsc;  // Q+ (chunk-start reference), scaled
+        }
+        // A- row group: bf16 hi / lo (or fp32), one vector store each
+        if constexpr (F16) {
+          H8 hi, lo;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float v = e < UW ? amv[e < UW ? e : 0] : 0.0f;
+            hi.b[e] = (__bf16)v;
+            lo.b[e] = (__bf16)(v - (float)hi.b[e]);
+          }
+          if constexpr (UW == 8) {
+            *reinterpret_cast<uint4*>(&sm.ra.am.hi[r][c0]) = hi.q;
+            *reinterpret_cast<uint4*>(&sm.ra.am.lo[r][c0]) = lo.q;
+          } else {
+            *reinterpret_cast<uint2*>(&sm.ra.am.hi[r][c0]) = hi.u[0];
+            *reinterpret_cast<uint2*>(&sm.ra.am.lo[r][c0]) = lo.u[0];
+          }
+        } else {
+          *reinterpret_cast<float4*>(&sm.ra.am.hi[r][c0]) = make_float4(amv[0], amv[1], amv[2], amv[3]);
+        }
+        if constexpr (DPV) {
+          if (w.out_row) {
+#pragma unroll
+            for (int e = 0; e < UW; ++e) {
+              const float v = qm[u * UW + e];
+              if constexpr (F16) {
+                const __bf16 hi = (__bf16)v;
+                sm.qmh[w.ro][c0 + e] = hi;
+                sm.qml[w.ro][c0 + e] = (__bf16)(v - (float)hi);
+              } else {
+                sm.qmh[w.ro][c0 + e] = v;
+              }
+            }
+          }
+        }
+      }
+      if (w.out_row) {
+        Op* qrow = Q_g + size_t(w.ro) * L.ldk;
+        if constexpr (F16) {
+#pragma unroll
+          for (int u = 0; u < NX / UW; ++u) {
+            H8 h8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h8.h[e] = (_Float16)(e < UW ? qv[u * UW + (e < UW ? e : 0)] : 0.0f);
+            // the row pitch (dk + 4 halves) keeps rows 8-byte aligned
+            uint2* q2 = reinterpret_cast<uint2*>(qrow + KM::chan(lg, u * UW));
+            q2[0] = h8.u[0];
+            if constexpr (UW == 8) q2[1] = h8.u[1];
+          }
+        } else {
+#pragma unroll
+          for (int x = 0; x < NX; x += 4)
+            *reinterpret_cast<float4*>(qrow + KM::chan(lg, x)) = make_float4(qv[x], qv[x + 1], qv[x + 2], qv[x + 3]);
+        }
+        if (lg == 0) {
+          sm.qs[w.ro] = qsc;
+          qinv_g[w.ro] = 1.0f / qsc;
+        }
+      }
+      // written values, scaled, transposed into LDS
+      if constexpr (F16) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (u < vnu) {
+#pragma unroll
+            for (int s2 = 0; s2 < 8; ++s2) {
+              if (vuw == 8 || s2 < 4) {
+                const int c = vuw == 8 ? 32 * u + 8 * lg + s2 : 4 * lg + s2;
+                sm.wvt[c][r] = (Op)(wv[8 * u + s2] * wsc);
+              }
+            }
+          }
+        }
+      } else {
+        const In* vrow = vg + w.vrow * dv;
+        const In* brow_v = beg + w.th * DK;
+        const In* bvrow = bvg ? bvg + w.th * dv : nullptr;
+        switch (dv) {
+          case 16: row_values<F16, 16>(V, vrow, brow_v, DK, bvrow, wscal, w.valid, lg, r, wsc, sm.wvt, true); break;
+          case 32: row_values<F16, 32>(V, vrow, brow_v, DK, bvrow, wscal, w.valid, lg, r, wsc, sm.wvt, true); break;
+          case 64: row_values<F16, 64>(V, vrow, brow_v, DK, bvrow, wscal, w.valid, lg, r, wsc, sm.wvt, true); break;
+          default: row_values<F16, 128>(V, vrow, brow_v, DK, bvrow, wscal, w.valid, lg, r, wsc, sm.wvt, true); break;
+        }
+      }
+    }
+    __syncthreads();
+
+    // A^ transposed: the LDS tile has the record's row pitch (C + 4), so the copy
+    // is flat and coalesced (the pad columns are never read as operands).
+    {
+      constexpr int UNITS = DK * Sm::LDC * int(sizeof(Op)) / 16;
+      static_assert(DK * Sm::LDC * sizeof(Op) % 16 == 0, "flat copy in 16-byte units");
+      const uint4* src = reinterpret_cast<const uint4*>(&sm.at[0][0]);
+      uint4* dst = reinterpret_cast<uint4*>(AT_g);
+      for (int u = tid; u < UNITS; u += kThreads) dst[u] = src[u];
+    }
+
+    // ---- Gram tiles: M^T(J, I) = A-(J) B+(I)^T and P^T(J, Io) = A-(J) Q+(Io)^T ----
+    // The B side (own rows) is split into bf16 hi/lo once per item.
+    H8 bmh[F16 ? KB : 1], bml[F16 ? KB : 1], qmh8[F16 ? KB : 1], qml8[F16 ? KB : 1];
+    if constexpr (F16) {
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2) {
+          const float v0 = s2 < UW ? bm[u * UW + (s2 < UW ? s2 : 0)] : 0.0f;
+          const float v1 = s2 < UW ? qm[u * UW + (s2 < UW ? s2 : 0)] : 0.0f;
+          const __bf16 h0 = (__bf16)v0, h1 = (__bf16)v1;
+          bmh[u].b[s2] = h0;
+          bml[u].b[s2] = (__bf16)(v0 - (float)h0);
+          qmh8[u].b[s2] = h1;
+          qml8[u].b[s2] = (__bf16)(v1 - (float)h1);
+        }
+      }
+    }
+    // A side from LDS rows of tile J; B side from registers (own rows) or LDS.
+    auto gram = [&](int J, const H8* xh, const H8* xl, const float* xb, int qrow_lds)
+        __attribute__((always_inline)) -> float4v {
+      float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (F16) {
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+          const int c0 = u * 4 * UW + UW * lg;
+          H8 ah, al, bh, bl;
+          if constexpr (UW == 8) {
+            ah.q = *reinterpret_cast<const uint4*>(&sm.ra.am.hi[16 * J + li][c0]);
+            al.q = *reinterpret_cast<const uint4*>(&sm.ra.am.lo[16 * J + li][c0]);
+          } else {
+            ah = pair4(&sm.ra.am.hi[16 * J + li][c0], nullptr);
+            al = pair4(&sm.ra.am.lo[16 * J + li][c0], nullptr);
+          }
+          if (qrow_lds >= 0) {
+            if constexpr (DPV) {
+              if constexpr (UW == 8) {
+                bh.q = *reinterpret_cast<const uint4*>(&sm.qmh[qrow_lds][c0]);
+                bl.q = *reinterpret_cast<const uint4*>(&sm.qml[qrow_lds][c0]);
+              } else {
+                bh = pair4(&sm.qmh[qrow_lds][c0], nullptr);
+                bl = pair4(&sm.qml[qrow_lds][c0], nullptr);
+              }
+            }
+          } else {
+            bh = xh[u];
+            bl = xl[u];
+          }
+          acc = mma_pair_bf16(ah.b, bh.b, acc);
+          acc = mma_pair_bf16(ah.b, bl.b, acc);
+          acc = mma_pair_bf16(al.b, bh.b, acc);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < KB; ++t) {
+          float a4[4], b4[4];
+          quad(&sm.ra.am.hi[16 * J + li][16 * t + 4 * lg], a4);
+          if (qrow_lds >= 0) {
+            if constexpr (DPV) quad(&sm.qmh[qrow_lds][16 * t + 4 * lg], b4);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) b4[e] = xb[4 * t + e];
+          }
+          acc = mma_slice_f32(a4, b4, acc);
+        }
+      }
+      return acc;
+    };
+
+    float4v mreg[NT];
+#pragma unroll
+    for (int J = 0; J < NT; ++J) mreg[J] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+    if (owner) {
+#pragma unroll
+      for (int J = 0; J < NT; ++J) {
+        if (J <= wave) mreg[J] = gram(J, bmh, bml, bm, -1);
+      }
+    }
+    if (want_out) {
+      if constexpr (!DPV) {
+        if (owner) {  // output rows are this wave's own rows
+          const int ro = 16 * wave + li;
+          const float qsl = sm.qs[ro];
+#pragma unroll
+          for (int J = 0; J < NT; ++J) {
+            float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (J <= wave) acc = gram(J, qmh8, qml8, qm, -1);
+            const int s0 = 16 * J + 4 * lg;
+            Op* dst = P_g + size_t(ro) * L.ldc + s0;
+            if constexpr (F16) {
+              H8 h8;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) h8.h[e] = (_Float16)((s0 + e <= ro) ? acc[e] * qsl : 0.0f);
+              *reinterpret_cast<uint2*>(dst) = h8.u[0];
+            } else {
+              *reinterpret_cast<float4*>(dst) = make_float4((s0 + 0 <= ro) ? acc[0] : 0.0f, (s0 + 1 <= ro) ? acc[1] : 0.0f,
+                                                            (s0 + 2 <= ro) ? acc[2] : 0.0f, (s0 + 3 <= ro) ? acc[3] : 0.0f);
+            }
+          }
+        }
+      } else {
+        if (wave < RT) {
+          const int ro = 16 * wave + li;
+          const int tau = ro * n_h + n_h - 1;
+          const int jmax = min(NT - 1, ((16 * wave + 15) * n_h + n_h - 1) / 16);
+          const float qsl = sm.qs[ro];
+          for (int J = 0; J < NT; ++J) {
+            float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (J <= jmax) acc = gram(J, qmh8, qml8, qm, ro);
+            const int s0 = 16 * J + 4 * lg;
+            Op* dst = P_g + size_t(ro) * L.ldc + s0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[e] = (Op)((s0 + e <= tau) ? acc[e] * qsl : 0.0f);
+          }
+        }
+      }
+    }
+    // Every raw value of this item is consumed: load the next item's rows now so
+    // they arrive while the inverse and W / U~ are computed.
+    if (item + int(gridDim.x) < total) prefetch(item + gridDim.x, raw);
+    __syncthreads();  // A- is dead: its space now holds M and T
+    if (owner) {
+#pragma unroll
+      for (int J = 0; J < NT; ++J) {
+        if (J <= wave) {
+          const int s0 = 16 * J + 4 * lg;
+          float4 m4;
+          m4.x = (s0 + 0 < r) ? mreg[J][0] : 0.0f;
+          m4.y = (s0 + 1 < r) ? mreg[J][1] : 0.0f;
+          m4.z = (s0 + 2 < r) ? mreg[J][2] : 0.0f;
+          m4.w = (s0 + 3 < r) ? mreg[J][3] : 0.0f;
+          *reinterpret_cast<float4*>(&sm.ra.mt.m[r][s0]) = m4;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- T = (I + M)^{-1}: diagonal 16x16 blocks by forward substitution ----
+    if (wave == 0) {
+      const int bI = lane >> 4, c = lane & 15;
+      if (bI < NT) {
+        float xcol[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          float sacc = (rr == c) ? 1.0f : 0.0f;
+#pragma unroll
+          for (int s2 = 0; s2 < rr; ++s2) sacc -= sm.ra.mt.m[16 * bI + rr][16 * bI + s2] * xcol[s2];
+          xcol[rr] = sacc;
+        }
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) sm.ra.mt.t[16 * bI + rr][16 * bI + c] = xcol[rr];
+      }
+    }
+    // off-diagonal blocks: T_IJ = -T_II sum_{K=J}^{I-1} M_IK T_KJ, one level per I
+#pragma unroll
+    for (int I = 1; I < NT; ++I) {
+      __syncthreads();
+      if (wave < I) {
+        const int J = wave;
+        float4v xa = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int K = J; K < I; ++K) {
+          float a4[4], b4[4];
+          quad(&sm.ra.mt.m[16 * I + li][16 * K + 4 * lg], a4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) b4[e] = sm.ra.mt.t[16 * K + 4 * lg + e][16 * J + li];
+          xa = mma_slice_f32(a4, b4, xa);
+        }
+        float a4[4], xb[4] = {xa[0], xa[1], xa[2], xa[3]};
+        quad(&sm.ra.mt.t[16 * I + li][16 * I + 4 * lg], a4);
+        const float4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        const float4v y = mma_slice_f32(a4, xb, zero);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.ra.mt.t[16 * I + 4 * lg + e][16 * J + li] = -y[e];
+      }
+    }
+    __syncthreads();
+    // operand copy of T with a zero upper triangle (fp16 over the dead M; fp32 in place)
+    Op* top = F16 ? reinterpret_cast<Op*>(&sm.ra.mt.m[0][0]) : reinterpret_cast<Op*>(&sm.ra.mt.t[0][0]);
+    constexpr int LDT = F16 ? 2 * Sm::LDC : Sm::LDC;  // fp16 rows over fp32 rows: twice the elements
+    for (int u = tid; u < C * C; u += kThreads) {
+      const int rr = u / C, s2 = u % C;
+      const float tv = sm.ra.mt.t[rr][s2];
+      if constexpr (F16) top[rr * LDT + s2] = (s2 <= rr) ? (Op)tv : (Op)0.0f;
+      else if (s2 > rr) sm.ra.mt.t[rr][s2] = 0.0f;
+    }
+    __syncthreads();
+
+    // ---- W^T = B+^T T^T (stored as W rows) and U~ = T Wv (stored transposed) ----
+    auto tprod = [&](const Op* arow, const Op* brow, int I) __attribute__((always_inline)) -> float4v {
+      float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (F16) {
+        for (int u = 0; 2 * u <= I; ++u) {
+          const bool two = 2 * u + 1 < NT;
+          const H8 a8 = pair4(arow + 32 * u + 4 * lg, two ? arow + 32 * u + 16 + 4 * lg : nullptr);
+          const H8 b8 = pair4(brow + 32 * u + 4 * lg, two ? brow + 32 * u + 16 + 4 * lg : nullptr);
+          acc = mma_pair_f16(a8.h, b8.h, acc);
+        }
+      } else {
+        for (int t = 0; t <= I; ++t) {
+          float a4[4], b4[4];
+          quad(arow + 16 * t + 4 * lg, a4);
+          quad(brow + 16 * t + 4 * lg, b4);
+          acc = mma_slice_f32(a4, b4, acc);
+        }
+      }
+      return acc;
+    };
+    constexpr int NWT = (DK / 16) * NT;
+    for (int x = wave; x < NWT; x += kWaves) {
+      const int ct = x / NT, I = x % NT;
+      const float4v acc = tprod(&sm.bt[16 * ct + li][0], top + (16 * I + li) * LDT, I);
+      Op* dst = W_g + size_t(16 * I + li) * L.ldk + 16 * ct + 4 * lg;
+      if constexpr (F16) {
+        H8 h8;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h8.h[e] = (_Float16)acc[e];
+        *reinterpret_cast<uint2*>(dst) = h8.u[0];
+      } else {
+        *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      }
+    }
+    const int VT = dv / 16;
+    for (int x = wave; x < NT * VT; x += kWaves) {
+      const int I = x / VT, ct = x % VT;
+      const float4v acc = tprod(top + (16 * I + li) * LDT, &sm.wvt[16 * ct + li][0], I);
+      Op* dst = UT_g + size_t(16 * ct + li) * C + 16 * I + 4 * lg;
+      if constexpr (F16) {
+        H8 h8;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h8.h[e] = (_Float16)acc[e];
+        *reinterpret_cast<uint2*>(dst) = h8.u[0];
+      } else {
+        *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      }
+    }
+    __syncthreads();  // LDS is reused by the next chunk
+  }
+}
+
+template <typename In, int DK, int C, int V, bool DPV>
+int launch_prep_t(const Problem& p, void* ws, bool want_out, hipStream_t s) {
+  const ChunkLayout L = chunk_layout(p);
+  const int64_t items = p.nchunks * p.B * p.H;
+  constexpr size_t lds = sizeof(PrepLds<std::is_same<In, uint16_t>::value, DK, C, DPV>);
+  const int per_cu = lds <= 40 * 1024 ? 4 : lds <= 80 * 1024 ? 2 : 1;
+  const int64_t grid = std::min<int64_t>(items, int64_t(device_cus()) * per_cu);
+  chunk_prep_kernel<In, DK, C, V, DPV><<<dim3(unsigned(grid)), kThreads, 0, s>>>(
+      p, static_cast<unsigned char*>(ws), L, want_out ? 1 : 0);
+  return int(hipGetLastError());
+}
+
+template <typename In, int DK, int V>
+int launch_prep_dk(const Problem& p, void* ws, bool want_out, hipStream_t s) {
+  constexpr bool DPAIR = V == GDN_VARIANT_DELTAPRODUCT;
+  switch (p.chunk) {
+    case 16:
+      if constexpr (DPAIR)
+        if (p.n_h > 1) return launch_prep_t<In, DK, 16, V, DPAIR>(p, ws, want_out, s);
+      return launch_prep_t<In, DK, 16, V, false>(p, ws, want_out, s);
+    case 32:
+      if constexpr (DPAIR)
+        if (p.n_h > 1) return launch_prep_t<In, DK, 32, V, DPAIR>(p, ws, want_out, s);
+      return launch_prep_t<In, DK, 32, V, false>(p, ws, want_out, s);
+    case 64:
+      if constexpr (std::is_same<In, float>::value && DK == 128) {
+        return int(hipErrorInvalidValue);
+      } else {
+        if constexpr (DPAIR)
+          if (p.n_h > 1) return launch_prep_t<In, DK, 64, V, DPAIR>(p, ws, want_out, s);
+        return launch_prep_t<In, DK, 64, V, false>(p, ws, want_out, s);
+      }
+    default: return int(hipErrorInvalidValue);
+  }
+}
+
+template <typename In, int V>
+int launch_prep_in(const Problem& p, void* ws, bool want_out, hipStream_t s) {
+  switch (p.dk) {
+    case 16: return launch_prep_dk<In, 16, V>(p, ws, want_out, s);
+    case 32: return launch_prep_dk<In, 32, V>(p, ws, want_out, s);
+    case 64: return launch_prep_dk<In, 64, V>(p, ws, want_out, s);
+    case 128: return launch_prep_dk<In, 128, V>(p, ws, want_out, s);
+    default: return int(hipErrorInvalidValue);
+  }
+}
+
+template <int V>
+int launch_prep_variant(const Problem& p, void* ws, bool want_out, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return p.dtype == GDN_DTYPE_BF16 ? launch_prep_in<uint16_t, V>(p, ws, want_out, s)
+                                   : launch_prep_in<float, V>(p, ws, want_out, s);
+}
+
+}  // namespace
+}  // namespace gdn

@@ -79,6 +79,12 @@ int launch_recurrent(const Problem& p, float* state, void* stream);
 int launch_chunk(const Problem& p, void* ws, bool want_output, void* stream);
 int launch_prep(const Problem& p, void* ws, bool want_output, void* stream);
 int launch_scan(const Problem& p, void* ws, bool want_output, void* stream);
+// Preparation launchers, one translation unit per variant (gdn_prep_*.hip).
+int launch_prep_fg2(const Problem& p, void* ws, bool want_output, void* stream);
+int launch_prep_kda(const Problem& p, void* ws, bool want_output, void* stream);
+int launch_prep_gdn(const Problem& p, void* ws, bool want_output, void* stream);
+int launch_prep_dp(const Problem& p, void* ws, bool want_output, void* stream);
+int launch_prep_asym(const Problem& p, void* ws, bool want_output, void* stream);
 int launch_state_copy(const Problem& p, void* stream);
 
 }  // namespace gdn

@@ -1,0 +1,11 @@
+// Chunk preparation kernels of the FG2 variant (one translation unit per variant keeps
+// the per-variant kernels compiling in parallel).
+#include "gdn_chunk.h"
+
+namespace gdn {
+
+int launch_prep_fg2(const Problem& p, void* ws, bool want_out, void* stream) {
+  return launch_prep_variant<GDN_VARIANT_FG2>(p, ws, want_out, stream);
+}
+
+}  // namespace gdn

@@ -1,0 +1,11 @@
+// Chunk preparation kernels of the KDA variant (one translation unit per variant keeps
+// the per-variant kernels compiling in parallel).
+#include "gdn_chunk.h"
+
+namespace gdn {
+
+int launch_prep_kda(const Problem& p, void* ws, bool want_out, void* stream) {
+  return launch_prep_variant<GDN_VARIANT_KDA>(p, ws, want_out, stream);
+}
+
+}  // namespace gdn
