@@ -24,8 +24,10 @@ SOURCES = ["gdn_api.cpp", "gdn_recurrent.hip", "gdn_chunk.hip", "gdn_prep_fg2.hi
            "gdn_prep_gdn.hip", "gdn_prep_dp.hip", "gdn_prep_asym.hip"]
 ARCH = "gfx950"
 # Packed fp32 instructions are disabled for every device compile.
+# MFMA accumulators are kept in VGPRs (VALU reads them without AGPR copies).
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I", INCLUDE, "-I", CSRC]
 
 

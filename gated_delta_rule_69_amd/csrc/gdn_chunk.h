@@ -280,6 +280,9 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
   static_assert(sizeof(Sm) <= 160 * 1024, "LDS budget");
   static_assert(NT <= kWaves, "one wave per 16-row tile");
   static_assert(DK <= kThreads, "one thread per channel for the decay constants");
+  // fragment-ordered record (the row-split scan's operand order)
+  constexpr bool FRAG = frag_layout(sizeof(Op), DK, C);
+  constexpr int CK = C / 32;  // k-blocks of 32 steps (fragment format)
   __shared__ Sm sm;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -380,6 +383,17 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
       }
     }
   };
+
+  // fragment-format offsets (elements) of this lane's 4 consecutive values of an
+  // accumulator tile: P row ro, steps 16 J + 4 lg ..; W row 16 I + li, channels
+  // 16 ct + 4 lg ..; U~ steps 16 I + 4 lg .., value column 16 ct + li.
+  auto p_frag = [&](int ro, int J) -> size_t {
+    return size_t((((ro >> 4) * CK + (J >> 1)) * 64 + (ro & 15) + 16 * (2 * (J & 1) + (lg >> 1))) * 8 + 4 * (lg & 1));
+  };
+  auto w_frag = [&](int I, int ct) -> size_t {
+    return size_t(((I * KB + (ct >> 1)) * 64 + li + 16 * (2 * (ct & 1) + (lg >> 1))) * 8 + 4 * (lg & 1));
+  };
+  auto u_frag = [&](int I, int ct) -> size_t { return size_t(((I * (dv / 16) + ct) * 64 + lane) * 4); };
 
   Raw raw;
   if (int(blockIdx.x) < total) prefetch(blockIdx.x, raw);
@@ -632,7 +646,15 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
       }
       if (w.out_row) {
         Op* qrow = Q_g + size_t(w.ro) * L.ldk;
-        if constexpr (F16) {
+        if constexpr (FRAG) {
+#pragma unroll
+          for (int u = 0; u < KB; ++u) {
+            H8 h8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h8.h[e] = (_Float16)qv[u * 8 + e];
+            *reinterpret_cast<uint4*>(Q_g + ((((w.ro >> 4) * KB + u) * 64 + (w.ro & 15) + 16 * lg) * 8)) = h8.q;
+          }
+        } else if constexpr (F16) {
 #pragma unroll
           for (int u = 0; u < NX / UW; ++u) {
             H8 h8;
@@ -682,8 +704,18 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
     __syncthreads();
 
     // A^ transposed: the LDS tile has the record's row pitch (C + 4), so the copy
-    // is flat and coalesced (the pad columns are never read as operands).
-    {
+    // is flat and coalesced (the pad columns are never read as operands); the
+    // fragment format gathers 16-byte pieces in its lane order instead.
+    if constexpr (FRAG) {
+      constexpr int UNITS = DK * C / 8;
+      uint4* dst = reinterpret_cast<uint4*>(AT_g);
+      for (int d = tid; d < UNITS; d += kThreads) {
+        const int l = d & 63, u = (d >> 6) % CK, tile = d / (64 * CK);
+        const uint2* s2 = reinterpret_cast<const uint2*>(&sm.at[16 * tile + (l & 15)][32 * u + 8 * (l >> 4)]);
+        const uint2 x0 = s2[0], x1 = s2[1];
+        dst[d] = make_uint4(x0.x, x0.y, x1.x, x1.y);
+      }
+    } else {
       constexpr int UNITS = DK * Sm::LDC * int(sizeof(Op)) / 16;
       static_assert(DK * Sm::LDC * sizeof(Op) % 16 == 0, "flat copy in 16-byte units");
       const uint4* src = reinterpret_cast<const uint4*>(&sm.at[0][0]);
@@ -779,7 +811,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
             float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
             if (J <= wave) acc = gram(J, qmh8, qml8, qm, -1);
             const int s0 = 16 * J + 4 * lg;
-            Op* dst = P_g + size_t(ro) * L.ldc + s0;
+            Op* dst = FRAG ? P_g + p_frag(ro, J) : P_g + size_t(ro) * L.ldc + s0;
             if constexpr (F16) {
               H8 h8;
 #pragma unroll
@@ -801,7 +833,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
             float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
             if (J <= jmax) acc = gram(J, qmh8, qml8, qm, ro);
             const int s0 = 16 * J + 4 * lg;
-            Op* dst = P_g + size_t(ro) * L.ldc + s0;
+            Op* dst = FRAG ? P_g + p_frag(ro, J) : P_g + size_t(ro) * L.ldc + s0;
 #pragma unroll
             for (int e = 0; e < 4; ++e) dst[e] = (Op)((s0 + e <= tau) ? acc[e] * qsl : 0.0f);
           }
@@ -902,7 +934,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
     for (int x = wave; x < NWT; x += kWaves) {
       const int ct = x / NT, I = x % NT;
       const float4v acc = tprod(&sm.bt[16 * ct + li][0], top + (16 * I + li) * LDT, I);
-      Op* dst = W_g + size_t(16 * I + li) * L.ldk + 16 * ct + 4 * lg;
+      Op* dst = FRAG ? W_g + w_frag(I, ct) : W_g + size_t(16 * I + li) * L.ldk + 16 * ct + 4 * lg;
       if constexpr (F16) {
         H8 h8;
 #pragma unroll
@@ -916,7 +948,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
     for (int x = wave; x < NT * VT; x += kWaves) {
       const int I = x / VT, ct = x % VT;
       const float4v acc = tprod(top + (16 * I + li) * LDT, &sm.wvt[16 * ct + li][0], I);
-      Op* dst = UT_g + size_t(16 * ct + li) * C + 16 * I + 4 * lg;
+      Op* dst = FRAG ? UT_g + u_frag(I, ct) : UT_g + size_t(16 * ct + li) * C + 16 * I + 4 * lg;
       if constexpr (F16) {
         H8 h8;
 #pragma unroll

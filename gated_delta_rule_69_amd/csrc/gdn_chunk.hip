@@ -320,16 +320,309 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(Problem p, const u
   }
 }
 
+// ---- kernel 2b: sequential scan, row-split waves (fragment-format records) ---------
+//
+// bf16 inputs, dk = 128, chunk 64. One workgroup per (batch*head, NB value
+// columns). Wave w owns rows 16w..16w+15 of U and O and rows 32w..32w+31 of the
+// workgroup's dk x NB state slice (fp32, MFMA accumulator layout). Its A operands
+// (its rows of W, Q+, A^^T and P, and its U~ tile) are read straight from the
+// record into registers one chunk ahead. The B operands, the state and U in fp16,
+// cross waves through LDS, transposed, with one power-of-two scale per column taken
+// from the workgroup's column maximum (LDS atomic max between two barriers).
+template <int NCT>
+__global__ __launch_bounds__(kThreads) void chunk_scan_rows_kernel(Problem p, const unsigned char* __restrict__ ws,
+                                                                   ChunkLayout L, int want_out) {
+  constexpr int DK = 128, C = 64;
+  constexpr int NB = 16 * NCT;
+  constexpr int KU = DK / 32;             // k-blocks over dk (one per wave block of state rows)
+  constexpr int CU = C / 32;              // k-blocks over the chunk (two wave blocks of U rows each)
+  constexpr int SRT = DK / 16 / kWaves;   // state row tiles per wave
+  static_assert(SRT * 16 * kWaves == DK && KU == kWaves, "one k-block of state rows per wave");
+  __shared__ __align__(16) _Float16 st[NB][DK + 8];   // state^T, fp16, column-scaled
+  __shared__ __align__(16) _Float16 ut[NB][C + 8];    // U^T, fp16, column-scaled
+  __shared__ float ssc[NB], usc[NB];                  // column scales (powers of two)
+  __shared__ uint32_t smax[NB], umax[NB];             // column maxima (float bits, >= 0)
+  __shared__ __align__(16) uint16_t ost[C][NB + 8];   // output rows of the chunk (bf16)
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar branches)
+  const int li = lane & 15, lg = lane >> 4;
+  const int dv = int(p.dv), dvt = dv / 16;
+  const int cblocks = dv / NB;
+  int bh, cb;
+  {
+    // column blocks of one (batch, head) read the same records: place them 8
+    // workgroups apart (same XCD, shared L2) whenever the grid allows
+    const int x = blockIdx.x, nbh = int(p.B * p.H);
+    const int full = (nbh / 8) * 8 * cblocks;
+    if (cblocks > 1 && x < full) {
+      const int grp = x / (8 * cblocks), rem = x % (8 * cblocks);
+      bh = grp * 8 + rem % 8;
+      cb = rem / 8;
+    } else {
+      bh = x / cblocks;
+      cb = x % cblocks;
+    }
+  }
+  const int H = int(p.H);
+  const int b = bh / H, h = bh - b * H;
+  const int NC = int(p.nchunks);
+  const int R = p.rows_out;
+  const bool orows = want_out && wave < R / 16;
+  uint16_t* o = static_cast<uint16_t*>(p.o);
+  const int col_base = cb * NB;
+
+  // A operands of one chunk, in two halves refilled for the next chunk as soon as
+  // the current chunk's half is consumed (mid-step), so that one register set
+  // suffices: FA for U and the state part of O, FB for the state update and P U.
+  struct FragsA {
+    uint4 w[KU], q[KU];
+    uint2 u[NCT];
+    float winv;
+  };
+  struct FragsB {
+    uint4 at[SRT][CU], pp[CU];
+    float4 gam[SRT];
+    float4 qi;
+  };
+  auto rec_of = [&](int n) -> const unsigned char* { return ws + (size_t(bh) * size_t(NC) + size_t(n)) * L.bytes; };
+  auto load_a = [&](int n, FragsA& f) __attribute__((always_inline)) {
+    const unsigned char* rec = rec_of(n);
+    const uint4* Wf = reinterpret_cast<const uint4*>(rec + L.off_W);
+    const uint4* Qf = reinterpret_cast<const uint4*>(rec + L.off_Q);
+    const uint2* Uf = reinterpret_cast<const uint2*>(rec + L.off_UT);
+#pragma unroll
+    for (int u = 0; u < KU; ++u) f.w[u] = Wf[(wave * KU + u) * 64 + lane];
+    // output operands are loaded by every wave (the record holds C rows of them),
+    // so that the number of loads in flight is the same on every path
+#pragma unroll
+    for (int u = 0; u < KU; ++u) f.q[u] = Qf[(wave * KU + u) * 64 + lane];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) f.u[ct] = Uf[(wave * dvt + cb * NCT + ct) * 64 + lane];
+    f.winv = *reinterpret_cast<const float*>(rec + L.off_winv);
+  };
+  auto load_b = [&](int n, FragsB& f) __attribute__((always_inline)) {
+    const unsigned char* rec = rec_of(n);
+    const uint4* Af = reinterpret_cast<const uint4*>(rec + L.off_AT);
+    const uint4* Pf = reinterpret_cast<const uint4*>(rec + L.off_P);
+    const float* gam = reinterpret_cast<const float*>(rec + L.off_gamma);
+    const float* qinv = reinterpret_cast<const float*>(rec + L.off_qinv);
+#pragma unroll
+    for (int rt = 0; rt < SRT; ++rt)
+#pragma unroll
+      for (int u = 0; u < CU; ++u) f.at[rt][u] = Af[((wave * SRT + rt) * CU + u) * 64 + lane];
+#pragma unroll
+    for (int u = 0; u < CU; ++u) f.pp[u] = Pf[(wave * CU + u) * 64 + lane];
+#pragma unroll
+    for (int rt = 0; rt < SRT; ++rt) f.gam[rt] = *reinterpret_cast<const float4*>(gam + 32 * wave + 16 * rt + 4 * lg);
+    f.qi = *reinterpret_cast<const float4*>(qinv + 16 * wave + 4 * lg);
+  };
+
+  // state: S[rt][ct][e] = S[32 w + 16 rt + 4 lg + e][col_base + 16 ct + li]
+  float S[SRT][NCT][4];
+  const size_t sbase = size_t(bh) * DK * size_t(dv);
+#pragma unroll
+  for (int rt = 0; rt < SRT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        S[rt][ct][e] = p.s0 ? p.s0[sbase + size_t(32 * wave + 16 * rt + 4 * lg + e) * dv + col_base + 16 * ct + li]
+                            : 0.0f;
+  // 1 / x for a power of two x in [2^-126, 2^126] (exact, one integer op)
+  auto inv_pow2 = [](float x) { return __uint_as_float(0x7f000000u - __float_as_uint(x)); };
+  // Column maximum of |x| over the workgroup: the wave's four lane groups, then an
+  // LDS atomic max over the waves (non-negative floats order as their bits).
+  auto col_max = [&](float m, uint32_t* dst, int ct) __attribute__((always_inline)) {
+    m = max_over_groups(m);
+    if (lg == 0) atomicMax(&dst[16 * ct + li], __float_as_uint(m));
+  };
+  // Column scale from the workgroup maximum: maps it into [2^12, 2^13); all-zero
+  // columns take 1.
+  auto col_scale = [&](const uint32_t* src, int ct) __attribute__((always_inline)) -> float {
+    return pow2_scale_for(__uint_as_float(src[16 * ct + li]), kStateScaleExp);
+  };
+  // publish the state image with the common column scales (after smax is complete)
+  auto publish_state = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const float sc = col_scale(smax, ct);
+#pragma unroll
+      for (int rt = 0; rt < SRT; ++rt) {
+        H8 hv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hv.h[e] = (_Float16)(S[rt][ct][e] * sc);
+        *reinterpret_cast<uint2*>(&st[16 * ct + li][32 * wave + 16 * rt + 4 * lg]) = hv.u[0];
+      }
+      if (wave == 0 && lg == 0) ssc[16 * ct + li] = sc;
+    }
+  };
+  auto state_max = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      float m = 0.0f;
+#pragma unroll
+      for (int rt = 0; rt < SRT; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(S[rt][ct][e]));
+      col_max(m, smax, ct);
+    }
+  };
+
+  auto step = [&](int n, FragsA& fa, FragsB& fb) __attribute__((always_inline)) {
+    const int nn = min(n + 1, NC - 1);  // next chunk (the last one is read again at the end)
+    // ---- U = U~ / ws - W S and the state part of O (B = state, scale cs) ----
+    if (tid < NB) smax[tid] = 0u;  // last read before the previous barrier
+    float cs[NCT], ics[NCT];
+    float4v ua[NCT], oa[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      cs[ct] = ssc[16 * ct + li];
+      ics[ct] = inv_pow2(cs[ct]);
+      ua[ct] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+      oa[ct] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int u = 0; u < KU; ++u) {
+        const half8 bv = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&st[16 * ct + li][32 * u + 8 * lg]));
+        ua[ct] = mma_pair_f16(__builtin_bit_cast(half8, fa.w[u]), bv, ua[ct]);
+        oa[ct] = mma_pair_f16(__builtin_bit_cast(half8, fa.q[u]), bv, oa[ct]);  // (unused without output rows)
+      }
+    }
+    // U * cs, rows 16 w + 4 lg + e, column 16 ct + li
+    float U[NCT][4];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const half4 t4 = __builtin_bit_cast(half4, fa.u[ct]);
+      const float wc = fa.winv * cs[ct];
+      float m = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        U[ct][e] = (float)t4[e] * wc - ua[ct][e];
+        m = fmaxf(m, fabsf(U[ct][e]));
+      }
+      col_max(m, umax, ct);
+    }
+    load_a(nn, fa);
+    __syncthreads();
+    // fp16 U^T with scale cu = cs * ku (the workgroup's column maximum of U * cs)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const float ku = col_scale(umax, ct);
+      H8 hv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hv.h[e] = (_Float16)(U[ct][e] * ku);
+      *reinterpret_cast<uint2*>(&ut[16 * ct + li][16 * wave + 4 * lg]) = hv.u[0];
+      if (wave == 0 && lg == 0) usc[16 * ct + li] = cs[ct] * ku;
+    }
+    __syncthreads();
+
+    // ---- S' = Diag(gamma) S + A^^T U and O = (Q+ S + P U) / qs (B = U, scale cu) ----
+    if (tid < NB) umax[tid] = 0u;  // read before the previous barrier
+    float4v sa[SRT][NCT], pa[NCT];
+    float icu[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      icu[ct] = inv_pow2(usc[16 * ct + li]);
+#pragma unroll
+      for (int rt = 0; rt < SRT; ++rt) sa[rt][ct] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+      pa[ct] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int u = 0; u < CU; ++u) {
+        const half8 bv = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&ut[16 * ct + li][32 * u + 8 * lg]));
+#pragma unroll
+        for (int rt = 0; rt < SRT; ++rt) sa[rt][ct] = mma_pair_f16(__builtin_bit_cast(half8, fb.at[rt][u]), bv, sa[rt][ct]);
+        pa[ct] = mma_pair_f16(__builtin_bit_cast(half8, fb.pp[u]), bv, pa[ct]);
+      }
+    }
+    if (orows) {
+      const float qi[4] = {fb.qi.x, fb.qi.y, fb.qi.z, fb.qi.w};
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float ov = (oa[ct][e] * ics[ct] + pa[ct][e] * icu[ct]) * qi[e];
+          ost[16 * wave + 4 * lg + e][16 * ct + li] = __builtin_bit_cast(uint16_t, (__bf16)ov);
+        }
+    }
+    const float gm[SRT][4] = {{fb.gam[0].x, fb.gam[0].y, fb.gam[0].z, fb.gam[0].w},
+                              {fb.gam[SRT - 1].x, fb.gam[SRT - 1].y, fb.gam[SRT - 1].z, fb.gam[SRT - 1].w}};
+#pragma unroll
+    for (int rt = 0; rt < SRT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[rt][ct][e] = gm[rt][e] * S[rt][ct][e] + sa[rt][ct][e] * icu[ct];
+    load_b(nn, fb);
+    state_max();
+    __syncthreads();
+    publish_state();
+    __syncthreads();
+    // ---- coalesced copy of the chunk's output rows ----
+    if (want_out) {
+      constexpr int RU = NB / 8;  // 16-byte units per output row
+      constexpr int PER = (C * RU + kThreads - 1) / kThreads;
+#pragma unroll
+      for (int it = 0; it < PER; ++it) {  // fixed trip count: static store count per step
+        const int x = tid + it * kThreads;
+        const int ro = x / RU, c8 = x % RU;
+        const int64_t t = int64_t(n) * R + ro;
+        if (ro < R && t < p.T)
+          *reinterpret_cast<uint4*>(o + ((int64_t(b) * p.T + t) * H + h) * dv + col_base + 8 * c8) =
+              *reinterpret_cast<const uint4*>(&ost[ro][8 * c8]);
+      }
+    }
+  };
+
+  if (tid < NB) smax[tid] = umax[tid] = 0u;
+  __syncthreads();
+  state_max();
+  __syncthreads();
+  publish_state();
+  __syncthreads();
+  if (NC > 0) {
+    FragsA fa;
+    FragsB fb;
+    load_a(0, fa);
+    load_b(0, fb);
+    for (int n = 0; n < NC; ++n) step(n, fa, fb);
+  }
+
+  if (p.s_final) {
+#pragma unroll
+    for (int rt = 0; rt < SRT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          p.s_final[sbase + size_t(32 * wave + 16 * rt + 4 * lg + e) * dv + col_base + 16 * ct + li] = S[rt][ct][e];
+  }
+}
+
 // ---- launch ----------------------------------------------------------------------------
 
 template <typename In, int DK, int C>
 int launch_scan_t(const Problem& p, void* ws, bool want_out, hipStream_t s) {
   const ChunkLayout L = chunk_layout(p);
-  const unsigned cblocks = unsigned((p.dv + 63) / 64);
-  const dim3 g2(unsigned(p.B * p.H) * cblocks);
-  chunk_scan_kernel<In, DK, C><<<g2, kThreads, 0, s>>>(p, static_cast<const unsigned char*>(ws), L,
-                                                       want_out ? 1 : 0);
-  return int(hipGetLastError());
+  if constexpr (std::is_same<In, uint16_t>::value && DK == 128 && C == 64) {
+    // fragment-format records: row-split scan, 64 value columns per workgroup
+    // (all of dv when dv < 64)
+    const unsigned nb = unsigned(std::min<int64_t>(64, p.dv));
+    const dim3 g(unsigned(p.B * p.H) * unsigned(p.dv / nb));
+    const unsigned char* w = static_cast<const unsigned char*>(ws);
+    const int wo = want_out ? 1 : 0;
+    switch (nb) {
+      case 16: chunk_scan_rows_kernel<1><<<g, kThreads, 0, s>>>(p, w, L, wo); break;
+      case 32: chunk_scan_rows_kernel<2><<<g, kThreads, 0, s>>>(p, w, L, wo); break;
+      default: chunk_scan_rows_kernel<4><<<g, kThreads, 0, s>>>(p, w, L, wo); break;
+    }
+    return int(hipGetLastError());
+  } else {
+    const unsigned cblocks = unsigned((p.dv + 63) / 64);
+    const dim3 g2(unsigned(p.B * p.H) * cblocks);
+    chunk_scan_kernel<In, DK, C><<<g2, kThreads, 0, s>>>(p, static_cast<const unsigned char*>(ws), L,
+                                                         want_out ? 1 : 0);
+    return int(hipGetLastError());
+  }
 }
 
 template <typename In, int DK>

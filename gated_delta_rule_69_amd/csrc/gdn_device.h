@@ -9,6 +9,7 @@
 namespace gdn {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bhalf8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
@@ -123,6 +124,13 @@ __device__ __forceinline__ float pow2_scale_for(float m, int target = 0) {
   frexpf(m, &e);  // m = f * 2^e, f in [0.5, 1)
   const int x = min(max(target + 1 - e, -100), 100);
   return ldexpf(1.0f, x);
+}
+
+// Scale of one block of a column whose blocks are scaled separately and later
+// brought to the column's common (smallest) scale: an all-zero block takes the
+// largest scale so that it never sets the common one.
+__device__ __forceinline__ float block_scale(float m, int target) {
+  return m > 0.0f ? pow2_scale_for(m, target) : 0x1p100f;
 }
 
 }  // namespace gdn

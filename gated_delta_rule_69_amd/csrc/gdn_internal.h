@@ -38,24 +38,57 @@ enum class Entry { ChunkFwd, FinalState, Recurrent, Shapes };
 // Pure argument checks; no HIP call. Returns GDN_OK or a negative status.
 int validate(const gdn_args* a, Entry e, Problem* out);
 
-// Per-chunk workspace record. Its first part is byte-for-byte the LDS image the
-// scan kernel stages (padded rows), so staging is a flat copy:
+// Per-chunk workspace record. Elements are fp16 (bf16 inputs) or fp32 (fp32
+// inputs). Two formats:
+//
+// Image format (every configuration except the one below): the first part is
+// byte-for-byte the LDS image the image scan stages (padded rows), so staging is
+// a flat copy:
 //   W     [C][dk+4]   A^^T [dk][C+4]   gamma [dk] f32   1/ws [4] f32     (state image)
 //   Q+    [C][dk+4]   P    [C][C+4]    1/qs  [C] f32                      (output part)
-// followed by U~^T [dv][C] (read straight into registers). Elements are fp16
-// (bf16 inputs) or fp32 (fp32 inputs).
+// followed by U~^T [dv][C] (read straight into registers).
+//
+// Fragment format (fp16 operands, dk = 128, C = 64): every operand is stored in
+// the order the row-split scan's lanes read it, 16 bytes per lane per MFMA
+// fragment, so one wave-wide load moves 1 KB of contiguous memory:
+//   W, Q+  [row tile][k-block of 32 channels][lane][8]   lane = row % 16 + 16 * (k % 32 / 8)
+//   A^^T   [channel tile][k-block of 32 steps][lane][8]
+//   P      [row tile][k-block of 32 steps][lane][8]
+//   U~     [step tile][value-column tile][lane][4]        lane = column % 16 + 16 * (step % 16 / 4)
+//   gamma [dk] f32, 1/qs [C] f32, 1/ws [4] f32.
 struct ChunkLayout {
   size_t elem, ldk, ldc;
   size_t off_W, off_AT, off_gamma, off_winv, state_bytes;
   size_t off_Q, off_P, off_qinv, image_bytes;
   size_t off_UT, bytes;
+  bool frag;
 };
 
 constexpr size_t round_up_c(size_t x, size_t m) { return (x + m - 1) / m * m; }
 
+// The fragment format (and the row-split scan) covers fp16 operands with dk = 128
+// and chunk 64.
+constexpr bool frag_layout(size_t es, size_t dk, size_t C) { return es == 2 && dk == 128 && C == 64; }
+
 constexpr ChunkLayout make_chunk_layout(size_t es, size_t dk, size_t dv, size_t C) {
   ChunkLayout L{};
   L.elem = es;
+  L.frag = frag_layout(es, dk, C);
+  if (L.frag) {
+    L.ldk = dk;
+    L.ldc = C;
+    L.off_W = 0;
+    L.off_Q = L.off_W + C * dk * es;
+    L.off_AT = L.off_Q + C * dk * es;
+    L.off_P = L.off_AT + dk * C * es;
+    L.off_UT = L.off_P + C * C * es;
+    L.off_gamma = L.off_UT + dv * C * es;
+    L.off_qinv = L.off_gamma + dk * 4;
+    L.off_winv = L.off_qinv + C * 4;
+    L.state_bytes = L.image_bytes = 0;
+    L.bytes = round_up_c(L.off_winv + 16, 256);
+    return L;
+  }
   L.ldk = dk + 4;
   L.ldc = C + 4;
   L.off_W = 0;
