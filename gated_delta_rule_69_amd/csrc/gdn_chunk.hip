@@ -327,10 +327,14 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(Problem p, const u
 // workgroup's dk x NB state slice (fp32, MFMA accumulator layout). Its A operands
 // (its rows of W, Q+, A^^T and P, and its U~ tile) are read straight from the
 // record into registers one chunk ahead. The B operands, the state and U in fp16,
-// cross waves through LDS, transposed, with one power-of-two scale per column taken
-// from the workgroup's column maximum (LDS atomic max between two barriers).
+// cross waves through LDS, transposed, each wave block with its own power-of-two
+// scale per column; a fragment is brought to the column's common (smallest) scale
+// by an exact power-of-two product before its MFMA. Two barriers per chunk.
+// chunks of look-ahead of the scan's L2 prefetch wave
+constexpr int kAhead = 4;
+
 template <int NCT>
-__global__ __launch_bounds__(kThreads) void chunk_scan_rows_kernel(Problem p, const unsigned char* __restrict__ ws,
+__global__ __launch_bounds__(kThreads + 64) void chunk_scan_rows_kernel(Problem p, const unsigned char* __restrict__ ws,
                                                                    ChunkLayout L, int want_out) {
   constexpr int DK = 128, C = 64;
   constexpr int NB = 16 * NCT;
@@ -338,10 +342,10 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_rows_kernel(Problem p, co
   constexpr int CU = C / 32;              // k-blocks over the chunk (two wave blocks of U rows each)
   constexpr int SRT = DK / 16 / kWaves;   // state row tiles per wave
   static_assert(SRT * 16 * kWaves == DK && KU == kWaves, "one k-block of state rows per wave");
-  __shared__ __align__(16) _Float16 st[NB][DK + 8];   // state^T, fp16, column-scaled
-  __shared__ __align__(16) _Float16 ut[NB][C + 8];    // U^T, fp16, column-scaled
-  __shared__ float ssc[NB], usc[NB];                  // column scales (powers of two)
-  __shared__ uint32_t smax[NB], umax[NB];             // column maxima (float bits, >= 0)
+  __shared__ __align__(16) _Float16 st[NB][DK + 8];   // state^T, fp16, block-scaled
+  __shared__ __align__(16) _Float16 ut[NB][C + 8];    // U^T, fp16, block-scaled
+  __shared__ __align__(16) float ssc[NB][kWaves];     // state scale of (column, wave block)
+  __shared__ __align__(16) float usc[NB][kWaves];     // U scale of (column, wave block)
   __shared__ __align__(16) uint16_t ost[C][NB + 8];   // output rows of the chunk (bf16)
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -418,6 +422,46 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_rows_kernel(Problem p, co
     f.qi = *reinterpret_cast<const float4*>(qinv + 16 * wave + 4 * lg);
   };
 
+  // ---- prefetch wave: pulls the records of chunk n + kAhead into L2 while the
+  // compute waves process chunk n (one dword of every 128-byte line this
+  // workgroup will read, moved to a scratch LDS word: nothing waits on it). It
+  // joins every barrier of the compute waves without a memory fence.
+  if (wave == kWaves) {
+    __shared__ uint32_t sink[64];
+    auto touch = [&](int n) __attribute__((always_inline)) {
+      const unsigned char* rec = rec_of(n);
+      auto line = [&](const unsigned char* a) __attribute__((always_inline)) {
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(a),
+                                         reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                             reinterpret_cast<uintptr_t>(&sink[0]) & 0xffffffffu),
+                                         4, 0, 0);
+      };
+      // W, Q+, A^^T, P: contiguous [0, off_UT), shared by the head's column
+      // blocks (same XCD, same L2): each block touches its share of the lines
+      const int main_lines = int(L.off_UT / 128);
+      const int share = (main_lines + cblocks - 1) / cblocks;
+      const int x0 = cb * share, x1 = min(main_lines, x0 + share);
+      for (int x = x0 + lane; x < x1; x += 64) line(rec + size_t(x) * 128);
+      // this workgroup's U~ tiles (NCT * 512 bytes per row block), then gamma, 1/qs, 1/ws
+      constexpr int UL = 4 * NCT;  // lines per row block
+      for (int x = lane; x < kWaves * UL + 7; x += 64) {
+        if (x < kWaves * UL)
+          line(rec + L.off_UT + size_t((x / UL) * dvt + cb * NCT) * 512 + size_t(x % UL) * 128);
+        else
+          line(rec + L.off_gamma + size_t(x - kWaves * UL) * 128);
+      }
+    };
+    for (int n = 1; n < min(NC, kAhead); ++n) touch(n);
+    __builtin_amdgcn_s_barrier();
+    for (int n = 0; n < NC; ++n) {
+      if (n + kAhead < NC) touch(n + kAhead);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_s_barrier();
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // no LDS write may outlive the workgroup
+    return;
+  }
+
   // state: S[rt][ct][e] = S[32 w + 16 rt + 4 lg + e][col_base + 16 ct + li]
   float S[SRT][NCT][4];
   const size_t sbase = size_t(bh) * DK * size_t(dv);
@@ -431,33 +475,8 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_rows_kernel(Problem p, co
                             : 0.0f;
   // 1 / x for a power of two x in [2^-126, 2^126] (exact, one integer op)
   auto inv_pow2 = [](float x) { return __uint_as_float(0x7f000000u - __float_as_uint(x)); };
-  // Column maximum of |x| over the workgroup: the wave's four lane groups, then an
-  // LDS atomic max over the waves (non-negative floats order as their bits).
-  auto col_max = [&](float m, uint32_t* dst, int ct) __attribute__((always_inline)) {
-    m = max_over_groups(m);
-    if (lg == 0) atomicMax(&dst[16 * ct + li], __float_as_uint(m));
-  };
-  // Column scale from the workgroup maximum: maps it into [2^12, 2^13); all-zero
-  // columns take 1.
-  auto col_scale = [&](const uint32_t* src, int ct) __attribute__((always_inline)) -> float {
-    return pow2_scale_for(__uint_as_float(src[16 * ct + li]), kStateScaleExp);
-  };
-  // publish the state image with the common column scales (after smax is complete)
+  // publish this wave's state rows: fp16 image and the block's column scales
   auto publish_state = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const float sc = col_scale(smax, ct);
-#pragma unroll
-      for (int rt = 0; rt < SRT; ++rt) {
-        H8 hv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) hv.h[e] = (_Float16)(S[rt][ct][e] * sc);
-        *reinterpret_cast<uint2*>(&st[16 * ct + li][32 * wave + 16 * rt + 4 * lg]) = hv.u[0];
-      }
-      if (wave == 0 && lg == 0) ssc[16 * ct + li] = sc;
-    }
-  };
-  auto state_max = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       float m = 0.0f;
@@ -465,73 +484,99 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_rows_kernel(Problem p, co
       for (int rt = 0; rt < SRT; ++rt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(S[rt][ct][e]));
-      col_max(m, smax, ct);
+      const float sc = block_scale(max_over_groups(m), kStateScaleExp);
+#pragma unroll
+      for (int rt = 0; rt < SRT; ++rt) {
+        H8 hv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hv.h[e] = (_Float16)(S[rt][ct][e] * sc);
+        *reinterpret_cast<uint2*>(&st[16 * ct + li][32 * wave + 16 * rt + 4 * lg]) = hv.u[0];
+      }
+      if (lg == 0) ssc[16 * ct + li][wave] = sc;
     }
   };
 
   auto step = [&](int n, FragsA& fa, FragsB& fb) __attribute__((always_inline)) {
     const int nn = min(n + 1, NC - 1);  // next chunk (the last one is read again at the end)
-    // ---- U = U~ / ws - W S and the state part of O (B = state, scale cs) ----
-    if (tid < NB) smax[tid] = 0u;  // last read before the previous barrier
-    float cs[NCT], ics[NCT];
+    // ---- U = U~ / ws - W S and the state part of O (B = state at scale cs) ----
+    // k-block u of the state is wave block u: its fragment is brought from the
+    // block's scale to the column's common (smallest) one by an exact power of two
+    // (k-block outer, column tile inner: 2 NCT independent accumulator chains
+    // interleave, which hides the MFMA latency)
+    float ics[NCT], facs[NCT][KU];
     float4v ua[NCT], oa[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      cs[ct] = ssc[16 * ct + li];
-      ics[ct] = inv_pow2(cs[ct]);
+      const float4 s4 = *reinterpret_cast<const float4*>(&ssc[16 * ct + li][0]);
+      const float cs = fminf(fminf(s4.x, s4.y), fminf(s4.z, s4.w));
+      facs[ct][0] = cs * inv_pow2(s4.x);
+      facs[ct][1] = cs * inv_pow2(s4.y);
+      facs[ct][2] = cs * inv_pow2(s4.z);
+      facs[ct][3] = cs * inv_pow2(s4.w);
+      ics[ct] = inv_pow2(cs);
       ua[ct] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
       oa[ct] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+    }
 #pragma unroll
-      for (int u = 0; u < KU; ++u) {
-        const half8 bv = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&st[16 * ct + li][32 * u + 8 * lg]));
-        ua[ct] = mma_pair_f16(__builtin_bit_cast(half8, fa.w[u]), bv, ua[ct]);
-        oa[ct] = mma_pair_f16(__builtin_bit_cast(half8, fa.q[u]), bv, oa[ct]);  // (unused without output rows)
+    for (int u = 0; u < KU; ++u) {
+      half8 bv[NCT];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+        bv[ct] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&st[16 * ct + li][32 * u + 8 * lg])) *
+                 (_Float16)facs[ct][u];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        ua[ct] = mma_pair_f16(__builtin_bit_cast(half8, fa.w[u]), bv[ct], ua[ct]);
+        oa[ct] = mma_pair_f16(__builtin_bit_cast(half8, fa.q[u]), bv[ct], oa[ct]);  // (unused without output rows)
       }
     }
-    // U * cs, rows 16 w + 4 lg + e, column 16 ct + li
-    float U[NCT][4];
+    // U rows 16 w + 4 lg + e, column 16 ct + li; fp16 U^T with this block's scale
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       const half4 t4 = __builtin_bit_cast(half4, fa.u[ct]);
-      const float wc = fa.winv * cs[ct];
-      float m = 0.0f;
+      float uv[4], m = 0.0f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        U[ct][e] = (float)t4[e] * wc - ua[ct][e];
-        m = fmaxf(m, fabsf(U[ct][e]));
+        uv[e] = (float)t4[e] * fa.winv - ua[ct][e] * ics[ct];
+        m = fmaxf(m, fabsf(uv[e]));
       }
-      col_max(m, umax, ct);
+      const float su = block_scale(max_over_groups(m), kStateScaleExp);
+      H8 hv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hv.h[e] = (_Float16)(uv[e] * su);
+      *reinterpret_cast<uint2*>(&ut[16 * ct + li][16 * wave + 4 * lg]) = hv.u[0];
+      if (lg == 0) usc[16 * ct + li][wave] = su;
     }
     load_a(nn, fa);
     __syncthreads();
-    // fp16 U^T with scale cu = cs * ku (the workgroup's column maximum of U * cs)
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const float ku = col_scale(umax, ct);
-      H8 hv;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) hv.h[e] = (_Float16)(U[ct][e] * ku);
-      *reinterpret_cast<uint2*>(&ut[16 * ct + li][16 * wave + 4 * lg]) = hv.u[0];
-      if (wave == 0 && lg == 0) usc[16 * ct + li] = cs[ct] * ku;
-    }
-    __syncthreads();
 
-    // ---- S' = Diag(gamma) S + A^^T U and O = (Q+ S + P U) / qs (B = U, scale cu) ----
-    if (tid < NB) umax[tid] = 0u;  // read before the previous barrier
+    // ---- S' = Diag(gamma) S + A^^T U and O = (Q+ S + P U) / qs (B = U at scale cu) ----
+    // fragment u of a column holds U rows 32 u + 8 lg .. +7: wave block 2 u + lg / 2
     float4v sa[SRT][NCT], pa[NCT];
-    float icu[NCT];
+    float icu[NCT], facu[NCT][CU];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      icu[ct] = inv_pow2(usc[16 * ct + li]);
+      const float4 s4 = *reinterpret_cast<const float4*>(&usc[16 * ct + li][0]);
+      const float cu = fminf(fminf(s4.x, s4.y), fminf(s4.z, s4.w));
+      icu[ct] = inv_pow2(cu);
+      facu[ct][0] = cu * inv_pow2((lg >> 1) ? s4.y : s4.x);
+      facu[ct][1] = cu * inv_pow2((lg >> 1) ? s4.w : s4.z);
 #pragma unroll
       for (int rt = 0; rt < SRT; ++rt) sa[rt][ct] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
       pa[ct] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+    }
 #pragma unroll
-      for (int u = 0; u < CU; ++u) {
-        const half8 bv = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&ut[16 * ct + li][32 * u + 8 * lg]));
+    for (int u = 0; u < CU; ++u) {
+      half8 bv[NCT];
 #pragma unroll
-        for (int rt = 0; rt < SRT; ++rt) sa[rt][ct] = mma_pair_f16(__builtin_bit_cast(half8, fb.at[rt][u]), bv, sa[rt][ct]);
-        pa[ct] = mma_pair_f16(__builtin_bit_cast(half8, fb.pp[u]), bv, pa[ct]);
+      for (int ct = 0; ct < NCT; ++ct)
+        bv[ct] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&ut[16 * ct + li][32 * u + 8 * lg])) *
+                 (_Float16)facu[ct][u];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+        for (int rt = 0; rt < SRT; ++rt) sa[rt][ct] = mma_pair_f16(__builtin_bit_cast(half8, fb.at[rt][u]), bv[ct], sa[rt][ct]);
+        pa[ct] = mma_pair_f16(__builtin_bit_cast(half8, fb.pp[u]), bv[ct], pa[ct]);
       }
     }
     if (orows) {
@@ -553,8 +598,6 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_rows_kernel(Problem p, co
 #pragma unroll
         for (int e = 0; e < 4; ++e) S[rt][ct][e] = gm[rt][e] * S[rt][ct][e] + sa[rt][ct][e] * icu[ct];
     load_b(nn, fb);
-    state_max();
-    __syncthreads();
     publish_state();
     __syncthreads();
     // ---- coalesced copy of the chunk's output rows ----
@@ -573,10 +616,6 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_rows_kernel(Problem p, co
     }
   };
 
-  if (tid < NB) smax[tid] = umax[tid] = 0u;
-  __syncthreads();
-  state_max();
-  __syncthreads();
   publish_state();
   __syncthreads();
   if (NC > 0) {
@@ -604,16 +643,17 @@ template <typename In, int DK, int C>
 int launch_scan_t(const Problem& p, void* ws, bool want_out, hipStream_t s) {
   const ChunkLayout L = chunk_layout(p);
   if constexpr (std::is_same<In, uint16_t>::value && DK == 128 && C == 64) {
-    // fragment-format records: row-split scan, 64 value columns per workgroup
-    // (all of dv when dv < 64)
-    const unsigned nb = unsigned(std::min<int64_t>(64, p.dv));
+    // fragment-format records: row-split scan, 16 value columns per workgroup
+    // (one workgroup per 16 columns keeps the step latency short: the scan is a
+    // chain of dependent MFMA / LDS / barrier phases, 512 steps long at 32K)
+    const unsigned nb = 16;
     const dim3 g(unsigned(p.B * p.H) * unsigned(p.dv / nb));
     const unsigned char* w = static_cast<const unsigned char*>(ws);
     const int wo = want_out ? 1 : 0;
     switch (nb) {
-      case 16: chunk_scan_rows_kernel<1><<<g, kThreads, 0, s>>>(p, w, L, wo); break;
-      case 32: chunk_scan_rows_kernel<2><<<g, kThreads, 0, s>>>(p, w, L, wo); break;
-      default: chunk_scan_rows_kernel<4><<<g, kThreads, 0, s>>>(p, w, L, wo); break;
+      case 16: chunk_scan_rows_kernel<1><<<g, kThreads + 64, 0, s>>>(p, w, L, wo); break;
+      case 32: chunk_scan_rows_kernel<2><<<g, kThreads + 64, 0, s>>>(p, w, L, wo); break;
+      default: chunk_scan_rows_kernel<4><<<g, kThreads + 64, 0, s>>>(p, w, L, wo); break;
     }
     return int(hipGetLastError());
   } else {
