@@ -246,7 +246,7 @@ struct alignas(16) PrepLds {
   } ra;
   Op bt[DK][LDC];              // B+ (chunk-start reference), transposed
   Op wvt[128][LDC];            // written values (scaled), transposed
-  Op at[DK][LDC];              // A^ transposed, staged for a coalesced copy to the record
+  Op at[F16 ? 1 : DK][LDC];    // A^ transposed, staged for a coalesced copy (fp32 path)
   Am qmh[QR][LDA];             // Q+ (mid reference) of output rows, DeltaProduct only
   Am qml[(DPV && F16) ? QR : 1][LDA];
   float tot[NT][DK];           // per-tile totals of the log decay
@@ -292,7 +292,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
   const int dv = int(p.dv);
   const int NC = int(p.nchunks);
   const int H = int(p.H);
-  const int total = NC * int(p.B) * H;  // < 2^31 (checked on the host)
+  const int BH = int(p.B) * H;
+  const int total = NC * BH;  // < 2^31 (checked on the host)
   const int mid = C / 2 - 1, tile_mid = mid / 16, row_mid = mid % 16;
   const In* qg = static_cast<const In*>(p.q);
   const In* kg = static_cast<const In*>(p.k);
@@ -319,7 +320,9 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
   };
   auto where = [&](int item) __attribute__((always_inline)) -> Where {
     Where w;
-    const int bh = item / NC, n = item - bh * NC;
+    // chunk-major order: the workgroups in flight read the same tokens of every
+    // head, i.e. contiguous memory ([B, T, H, d] rows of one token are adjacent)
+    const int n = item / BH, bh = item - n * BH;
     const int b = bh / H, h = bh - b * H;
     const int64_t vs = int64_t(n) * C + r;
     w.valid = owner && vs < p.steps;
@@ -395,12 +398,25 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
   };
   auto u_frag = [&](int I, int ct) -> size_t { return size_t(((I * (dv / 16) + ct) * 64 + lane) * 4); };
 
+  // 0/1 selection fragments (B operand of a 16x16x32 MFMA) that move the k-slot of
+  // relative channel 16 h + n to column n: with an A operand holding one row group
+  // (lane (i, g): channels of slots 8 g + s), the product is that group transposed.
+  half8 sel[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) {
+      const bool hit = UW == 8 ? (8 * lg + s2 == li + 16 * hh) : (s2 < UW && UW * lg + s2 == li + 16 * hh);
+      sel[hh][s2] = hit ? (_Float16)1.0f : (_Float16)0.0f;
+    }
+
   Raw raw;
   if (int(blockIdx.x) < total) prefetch(blockIdx.x, raw);
 
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     const Where w = where(item);
-    unsigned char* rec = ws + size_t(item) * L.bytes;
+    const int item_n = item / BH;
+    unsigned char* rec = ws + (size_t(item - item_n * BH) * size_t(NC) + size_t(item_n)) * L.bytes;
     Op* W_g = reinterpret_cast<Op*>(rec + L.off_W);
     Op* AT_g = reinterpret_cast<Op*>(rec + L.off_AT);
     Op* Q_g = reinterpret_cast<Op*>(rec + L.off_Q);
@@ -586,6 +602,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
           cq[e] = x2.x, cq[e + 1] = x2.y, cq[e + 2] = x2.z, cq[e + 3] = x2.w;
         }
         float amv[UW];
+        half8 xbt = {}, xat = {};  // fp16 B+ and A^ of the group (bf16 path)
 #pragma unroll
         for (int e = 0; e < UW; ++e) {
           const int x = u * UW + e, c = c0 + e;
@@ -603,11 +620,40 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
             eam = expf(cp[e] - g);
           }
           bm[x] = bb[x] * fup;
-          sm.bt[c][r] = (Op)(bb[x] * eg);
-          sm.at[c][r] = (Op)(a[x] * eat);
+          if constexpr (F16) {
+            xbt[e] = (_Float16)(bb[x] * eg);
+            xat[e] = (_Float16)(a[x] * eat);
+          } else {
+            sm.bt[c][r] = (Op)(bb[x] * eg);
+            sm.at[c][r] = (Op)(a[x] * eat);
+          }
           amv[e] = a[x] * eam;
           qm[x] = qv[x] * fup;
           qv[x] = qv[x] * eg * qsc;  // Q+ (chunk-start reference), scaled
+        }
+        if constexpr (F16) {
+          // B+ and A^ of this row group transposed by MFMA (product with a 0/1
+          // selection matrix: exact): lane (li, lg) then holds 4 consecutive steps
+          // 16 w + 4 lg .. of channel ch0 + 16 h + li
+          const int ch0 = u * 4 * UW;
+#pragma unroll
+          for (int hh = 0; hh < UW / 4; ++hh) {
+            const float4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
+            const float4v tb = mma_pair_f16(xbt, sel[hh], zero);
+            const float4v ta = mma_pair_f16(xat, sel[hh], zero);
+            const int c = ch0 + 16 * hh + li;
+            H8 pb, pa;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              pb.h[e] = (_Float16)tb[e];
+              pa.h[e] = (_Float16)ta[e];
+            }
+            *reinterpret_cast<uint2*>(&sm.bt[c][16 * wave + 4 * lg]) = pb.u[0];
+            Op* adst = FRAG ? AT_g + size_t((((c >> 4) * CK + (wave >> 1)) * 64 + li + 16 * (2 * (wave & 1) + (lg >> 1))) * 8 +
+                                            4 * (lg & 1))
+                            : AT_g + size_t(c) * L.ldc + 16 * wave + 4 * lg;
+            *reinterpret_cast<uint2*>(adst) = pa.u[0];
+          }
         }
         // A- row group: bf16 hi / lo (or fp32), one vector store each
         if constexpr (F16) {
@@ -675,16 +721,29 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
           qinv_g[w.ro] = 1.0f / qsc;
         }
       }
-      // written values, scaled, transposed into LDS
+      // written values, scaled, transposed into LDS (bf16 path: by MFMA, as above)
       if constexpr (F16) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           if (u < vnu) {
+            half8 xv;
 #pragma unroll
-            for (int s2 = 0; s2 < 8; ++s2) {
-              if (vuw == 8 || s2 < 4) {
-                const int c = vuw == 8 ? 32 * u + 8 * lg + s2 : 4 * lg + s2;
-                sm.wvt[c][r] = (Op)(wv[8 * u + s2] * wsc);
+            for (int s2 = 0; s2 < 8; ++s2) xv[s2] = (vuw == 8 || s2 < 4) ? (_Float16)(wv[8 * u + s2] * wsc) : (_Float16)0.0f;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              if (vuw == 8 || hh == 0) {
+                half8 sv;
+#pragma unroll
+                for (int s2 = 0; s2 < 8; ++s2) {
+                  const bool hit = vuw == 8 ? (8 * lg + s2 == li + 16 * hh) : (s2 < 4 && 4 * lg + s2 == li);
+                  sv[s2] = hit ? (_Float16)1.0f : (_Float16)0.0f;
+                }
+                const float4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                const float4v tv = mma_pair_f16(xv, sv, zero);
+                H8 pv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pv.h[e] = (_Float16)tv[e];
+                *reinterpret_cast<uint2*>(&sm.wvt[32 * u + 16 * hh + li][16 * wave + 4 * lg]) = pv.u[0];
               }
             }
           }
@@ -703,19 +762,10 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
     }
     __syncthreads();
 
-    // A^ transposed: the LDS tile has the record's row pitch (C + 4), so the copy
-    // is flat and coalesced (the pad columns are never read as operands); the
-    // fragment format gathers 16-byte pieces in its lane order instead.
-    if constexpr (FRAG) {
-      constexpr int UNITS = DK * C / 8;
-      uint4* dst = reinterpret_cast<uint4*>(AT_g);
-      for (int d = tid; d < UNITS; d += kThreads) {
-        const int l = d & 63, u = (d >> 6) % CK, tile = d / (64 * CK);
-        const uint2* s2 = reinterpret_cast<const uint2*>(&sm.at[16 * tile + (l & 15)][32 * u + 8 * (l >> 4)]);
-        const uint2 x0 = s2[0], x1 = s2[1];
-        dst[d] = make_uint4(x0.x, x0.y, x1.x, x1.y);
-      }
-    } else {
+    // A^ transposed (fp32 path): the LDS tile has the record's row pitch (C + 4),
+    // so the copy is flat and coalesced (the pad columns are never read as
+    // operands). The bf16 path stored it from the MFMA transposes above.
+    if constexpr (!F16) {
       constexpr int UNITS = DK * Sm::LDC * int(sizeof(Op)) / 16;
       static_assert(DK * Sm::LDC * sizeof(Op) % 16 == 0, "flat copy in 16-byte units");
       const uint4* src = reinterpret_cast<const uint4*>(&sm.at[0][0]);
@@ -795,6 +845,56 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
     float4v mreg[NT];
 #pragma unroll
     for (int J = 0; J < NT; ++J) mreg[J] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (F16 && !DPV) {
+      // M and P tiles of every J together, k-block outer: 2 NT independent
+      // accumulator chains interleave (tiles above the diagonal are computed and
+      // masked, which costs no time: the last wave computes all of them anyway).
+      float4v preg[NT];
+#pragma unroll
+      for (int J = 0; J < NT; ++J) preg[J] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+      if (owner) {
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+          const int c0 = u * 4 * UW + UW * lg;
+          H8 ah[NT], al[NT];
+#pragma unroll
+          for (int J = 0; J < NT; ++J) {
+            if constexpr (UW == 8) {
+              ah[J].q = *reinterpret_cast<const uint4*>(&sm.ra.am.hi[16 * J + li][c0]);
+              al[J].q = *reinterpret_cast<const uint4*>(&sm.ra.am.lo[16 * J + li][c0]);
+            } else {
+              ah[J] = pair4(&sm.ra.am.hi[16 * J + li][c0], nullptr);
+              al[J] = pair4(&sm.ra.am.lo[16 * J + li][c0], nullptr);
+            }
+          }
+#pragma unroll
+          for (int J = 0; J < NT; ++J) mreg[J] = mma_pair_bf16(ah[J].b, bmh[u].b, mreg[J]);
+#pragma unroll
+          for (int J = 0; J < NT; ++J) preg[J] = mma_pair_bf16(ah[J].b, qmh8[u].b, preg[J]);
+#pragma unroll
+          for (int J = 0; J < NT; ++J) mreg[J] = mma_pair_bf16(ah[J].b, bml[u].b, mreg[J]);
+#pragma unroll
+          for (int J = 0; J < NT; ++J) preg[J] = mma_pair_bf16(ah[J].b, qml8[u].b, preg[J]);
+#pragma unroll
+          for (int J = 0; J < NT; ++J) mreg[J] = mma_pair_bf16(al[J].b, bmh[u].b, mreg[J]);
+#pragma unroll
+          for (int J = 0; J < NT; ++J) preg[J] = mma_pair_bf16(al[J].b, qmh8[u].b, preg[J]);
+        }
+        if (want_out) {  // output rows are this wave's own rows
+          const int ro = 16 * wave + li;
+          const float qsl = sm.qs[ro];
+#pragma unroll
+          for (int J = 0; J < NT; ++J) {
+            const int s0 = 16 * J + 4 * lg;
+            Op* dst = FRAG ? P_g + p_frag(ro, J) : P_g + size_t(ro) * L.ldc + s0;
+            H8 h8;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h8.h[e] = (_Float16)((s0 + e <= ro) ? preg[J][e] * qsl : 0.0f);
+            *reinterpret_cast<uint2*>(dst) = h8.u[0];
+          }
+        }
+      }
+    } else {
     if (owner) {
 #pragma unroll
       for (int J = 0; J < NT; ++J) {
@@ -840,6 +940,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
         }
       }
     }
+    }  // generic Gram path
     // Every raw value of this item is consumed: load the next item's rows now so
     // they arrive while the inverse and W / U~ are computed.
     if (item + int(gridDim.x) < total) prefetch(item + gridDim.x, raw);
@@ -930,6 +1031,64 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
       }
       return acc;
     };
+    const int VT = dv / 16;
+    if constexpr (F16 && NT == kWaves) {
+      // chunk 64: wave w computes the W and U~ tiles of step rows 16 w .. 16 w + 15,
+      // every k-block (T's upper triangle is zero), independent chains interleaved
+      H8 ta[2];  // T rows 16 w + li (A of U~; B of W^T), steps 32 u + 4 lg .. (+16)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const Op* trow = top + (16 * wave + li) * LDT + 32 * u + 4 * lg;
+        ta[u] = pair4(trow, trow + 16);
+      }
+      constexpr int CT = DK / 16;
+      float4v wacc[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) wacc[ct] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const Op* brow = &sm.bt[16 * ct + li][32 * u + 4 * lg];
+          const H8 b8 = pair4(brow, brow + 16);
+          wacc[ct] = mma_pair_f16(b8.h, ta[u].h, wacc[ct]);
+        }
+      }
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        Op* dst = FRAG ? W_g + w_frag(wave, ct) : W_g + size_t(16 * wave + li) * L.ldk + 16 * ct + 4 * lg;
+        H8 h8;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h8.h[e] = (_Float16)wacc[ct][e];
+        *reinterpret_cast<uint2*>(dst) = h8.u[0];
+      }
+      for (int c0 = 0; c0 < VT; c0 += 4) {
+        float4v uacc[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) uacc[j] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int ct = min(c0 + j, VT - 1);  // tail tiles repeat the last one (not stored)
+            const Op* brow = &sm.wvt[16 * ct + li][32 * u + 4 * lg];
+            const H8 b8 = pair4(brow, brow + 16);
+            uacc[j] = mma_pair_f16(ta[u].h, b8.h, uacc[j]);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (c0 + j < VT) {
+            const int ct = c0 + j;
+            Op* dst = FRAG ? UT_g + u_frag(wave, ct) : UT_g + size_t(16 * ct + li) * C + 16 * wave + 4 * lg;
+            H8 h8;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h8.h[e] = (_Float16)uacc[j][e];
+            *reinterpret_cast<uint2*>(dst) = h8.u[0];
+          }
+        }
+      }
+    } else {
     constexpr int NWT = (DK / 16) * NT;
     for (int x = wave; x < NWT; x += kWaves) {
       const int ct = x / NT, I = x % NT;
@@ -944,7 +1103,6 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
         *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
       }
     }
-    const int VT = dv / 16;
     for (int x = wave; x < NT * VT; x += kWaves) {
       const int I = x / VT, ct = x % VT;
       const float4v acc = tprod(top + (16 * I + li) * LDT, &sm.wvt[16 * ct + li][0], I);
@@ -958,6 +1116,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
         *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
       }
     }
+    }  // generic W / U~ path
     __syncthreads();  // LDS is reused by the next chunk
   }
 }
