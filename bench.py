@@ -35,7 +35,7 @@ WORKLOAD = gdn_inputs.CONFIGS[2]
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "chunk_traffic_fg2_32k.json")
-KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_69_amd", "csrc", "gdn_chunk.hip")
+CSRC = os.path.join(ROOT, "gated_delta_rule_69_amd", "csrc")
 
 
 def log(*a):
@@ -87,7 +87,7 @@ def cpu_baseline(inp, T_sample):
     except AttributeError:
         ncpu = os.cpu_count() or 1
     workers = max(1, min(16, ncpu))
-    pairs = [(b, h) for b in range(inp["B"]) for h in range(inp["H"])][:workers]
+    pairs = [(b, h) for b in range(inp["B"]) for h in range(inp["H"])]
     ctx = mp.get_context("fork")
     t0 = time.perf_counter()
     with ctx.Pool(workers) as pool:
@@ -95,23 +95,60 @@ def cpu_baseline(inp, T_sample):
     wall = time.perf_counter() - t0
     tokens = len(pairs) * T_sample / inp["H"]     # metric tokens carry all H heads
     return dict(value=tokens / wall, unit="tokens/s", cores=workers, kind="oracle",
-                sample=f"{len(pairs)} of {inp['B'] * inp['H']} (batch, head) sequences, "
-                       f"first {T_sample} tokens each, float64 token loop, one process per core; "
-                       f"wall {wall:.1f} s"), res
+                sample=f"all {len(pairs)} (batch, head) sequences of the workload, first {T_sample} "
+                       f"of {inp['T']} tokens each (B*{T_sample} metric tokens); float64 token "
+                       f"loop, {workers} worker processes, one thread each; wall {wall:.1f} s"), res
 
 
-def read_traffic(launch_units):
-    """HBM bytes per launch from a committed rocprofv3 PMC summary, if it was taken on
-    the current kernel source."""
+def source_sha256():
+    """Hash of every kernel source file (the PMC traffic figures are only valid for
+    the sources they were measured on)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def read_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 PMC summary,
+    if it was taken on the current kernel sources; else None."""
     try:
         with open(PROFILE_TRAFFIC) as f:
             rec = json.load(f)
-        sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-        if rec.get("source_sha256") != sha:
+        if rec.get("source_sha256") != source_sha256():
             return None
-        return rec.get("traffic_bytes_per_launch")
-    except (OSError, ValueError):
+        return rec["kernels"][kernel]["traffic_bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
         return None
+
+
+def profile_driver(args):
+    """Workload for the rocprofv3 counter runs: a few prepare + scan steps and a
+    device-to-device copy of exactly 1 GiB (the calibration of FETCH_SIZE and
+    WRITE_SIZE)."""
+    import torch
+    import gated_delta_rule_69_amd as gdn
+    W = WORKLOAD
+    inp = gdn_inputs.config_inputs(W["index"])
+    dev = torch.device("cuda:0")
+    t = {k: torch.from_numpy(inp[k]).to(dev).to(torch.bfloat16).contiguous()
+         for k in ("q", "k", "v", "alpha", "beta")}
+    o = torch.empty_like(t["q"])
+    s_final = torch.empty((W["B"], W["H"], W["dk"], W["dv"]), dtype=torch.float32, device=dev)
+    a = gdn.make_args("fg2", t["q"], t["k"], t["v"], t["alpha"], t["beta"], chunk=W["chunk"],
+                      s_final=s_final, o=o)
+    ws = torch.empty(gdn.gdn_workspace_bytes(a), dtype=torch.uint8, device=dev)
+    for _ in range(args.steps):
+        gdn.gdn_chunk_prepare(a, ws)
+        gdn.gdn_chunk_scan(a, ws)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"profile driver: {args.steps} steps and a 1 GiB copy done")
 
 
 def main():
@@ -121,12 +158,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=16384)
+    ap.add_argument("--profile-driver", action="store_true",
+                    help="only run the workload for rocprofv3 counter collection")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
+
+    if args.profile_driver:
+        profile_driver(args)
+        return
 
     W = WORKLOAD
     B, H, T, d, C = W["B"], W["H"], W["T"], W["dk"], W["chunk"]
@@ -178,17 +221,20 @@ def main():
     log(f"bench: {ms_step:.3f} ms/step (prepare {prep_ms:.3f} ms, scan {scan_ms:.3f} ms)")
 
     units = B * T * H                                   # token-heads per launch
-    if scan_ms >= prep_ms:
-        flops = scan_flops_per_th(d, C) * units
-        ach = flops / (scan_ms * 1e-3) / 1e12
-        roof = dict(kernel="chunk_scan_kernel", bound="mfma", achieved=ach, peak=MFMA_PEAK_TFLOPS,
-                    unit="TFLOP/s", frac=ach / MFMA_PEAK_TFLOPS, algorithmic=flops)
-    else:
-        nbytes = prep_bytes_per_th(d) * units
-        ach = nbytes / (prep_ms * 1e-3) / 1e9
-        roof = dict(kernel="chunk_prep_kernel", bound="hbm", achieved=ach, peak=HBM_PEAK_GBS,
-                    unit="GB/s", frac=ach / HBM_PEAK_GBS, algorithmic=nbytes)
-    roof["traffic"] = read_traffic(units)
+    # per-kernel rooflines (algorithmic work per launch / mean launch time from the
+    # HIP events above); `roofline` reports the longer of the two kernels
+    prep_bytes = prep_bytes_per_th(d) * units
+    prep_gbs = prep_bytes / (prep_ms * 1e-3) / 1e9
+    prep_roof = dict(kernel="chunk_prep_kernel", bound="hbm", achieved=prep_gbs, peak=HBM_PEAK_GBS,
+                     unit="GB/s", frac=prep_gbs / HBM_PEAK_GBS, algorithmic=prep_bytes,
+                     ms=prep_ms, traffic=read_traffic("chunk_prep_kernel"))
+    scan_flops = scan_flops_per_th(d, C) * units
+    scan_tf = scan_flops / (scan_ms * 1e-3) / 1e12
+    scan_roof = dict(kernel="chunk_scan_rows_kernel", bound="mfma", achieved=scan_tf,
+                     peak=MFMA_PEAK_TFLOPS, unit="TFLOP/s", frac=scan_tf / MFMA_PEAK_TFLOPS,
+                     algorithmic=scan_flops, ms=scan_ms, traffic=read_traffic("chunk_scan_rows_kernel"))
+    roof = dict(prep_roof if prep_ms >= scan_ms else scan_roof)
+    roof["other_kernel"] = scan_roof if prep_ms >= scan_ms else prep_roof
     path_bytes = (prep_bytes_per_th(d) + scan_bytes_per_th(d)) * units + B * H * d * d * 4
     path_gbs = path_bytes / (ms_step * 1e-3) / 1e9
     path = dict(bound="hbm", achieved=path_gbs, peak=HBM_PEAK_GBS, unit="GB/s",

@@ -96,6 +96,12 @@ CASES = [
     ("asym", "f32", 1, 100, 2, 64, 64, 1, 64),
     ("asym", "f32", 1, 100, 2, 64, 64, 1, 16),
     ("asym", "bf16", 1, 256, 2, 128, 128, 1, 64),
+    # bf16, dk 128, chunk 64: fragment-format records and the row-split scan,
+    # every value width and output-row count it handles
+    ("kda", "bf16", 1, 200, 2, 128, 32, 1, 64),
+    ("gdn", "bf16", 2, 150, 2, 128, 16, 1, 64),
+    ("deltaproduct", "bf16", 1, 100, 2, 128, 64, 4, 64),
+    ("asym", "bf16", 1, 190, 3, 128, 64, 1, 64),
 ]
 
 
@@ -112,6 +118,20 @@ def test_chunk_vs_oracle(case, with_s0):
 def test_fg2_plus(dt):
     inp = gdn_inputs.make_inputs("fg2", 1, 211, 2, 64, 128, dtype=dt, seed=12, fg2_plus=True)
     _run_and_check(inp, chunk=64 if dt == "bf16" else 32, what=f"fg2+ {dt}")
+
+
+def test_fg2_plus_fragment_records():
+    """FG2+ (separate value-side beta) with dk 128, dv 64, chunk 64, bf16."""
+    inp = gdn_inputs.make_inputs("fg2", 1, 300, 2, 128, 64, dtype="bf16", seed=14, fg2_plus=True)
+    s0 = gdn_inputs.make_state(1, 2, 128, 64, seed=14)
+    _run_and_check(inp, s0, chunk=64, what="fg2+ dk128 dv64")
+
+
+@pytest.mark.parametrize("T", [1, 63, 65, 130])
+def test_short_and_ragged_fragment_records(T):
+    inp = gdn_inputs.make_inputs("fg2", 1, T, 2, 128, 128, dtype="bf16", seed=40 + T)
+    s0 = gdn_inputs.make_state(1, 2, 128, 128, seed=T)
+    _run_and_check(inp, s0, chunk=64, what=f"T={T} dk128")
 
 
 def test_wide_beta_and_strong_decay():
