@@ -968,10 +968,11 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
         float xcol[16];
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
-          float sacc = (rr == c) ? 1.0f : 0.0f;
+          // four partial sums shorten the dependent chain
+          float s4[4] = {(rr == c) ? 1.0f : 0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int s2 = 0; s2 < rr; ++s2) sacc -= sm.ra.mt.m[16 * bI + rr][16 * bI + s2] * xcol[s2];
-          xcol[rr] = sacc;
+          for (int s2 = 0; s2 < rr; ++s2) s4[s2 & 3] -= sm.ra.mt.m[16 * bI + rr][16 * bI + s2] * xcol[s2];
+          xcol[rr] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
         }
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) sm.ra.mt.t[16 * bI + rr][16 * bI + c] = xcol[rr];
@@ -1003,11 +1004,21 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
     // operand copy of T with a zero upper triangle (fp16 over the dead M; fp32 in place)
     Op* top = F16 ? reinterpret_cast<Op*>(&sm.ra.mt.m[0][0]) : reinterpret_cast<Op*>(&sm.ra.mt.t[0][0]);
     constexpr int LDT = F16 ? 2 * Sm::LDC : Sm::LDC;  // fp16 rows over fp32 rows: twice the elements
-    for (int u = tid; u < C * C; u += kThreads) {
-      const int rr = u / C, s2 = u % C;
-      const float tv = sm.ra.mt.t[rr][s2];
-      if constexpr (F16) top[rr * LDT + s2] = (s2 <= rr) ? (Op)tv : (Op)0.0f;
-      else if (s2 > rr) sm.ra.mt.t[rr][s2] = 0.0f;
+    for (int u = tid; u < C * C / 4; u += kThreads) {  // four values a thread
+      const int rr = u / (C / 4), s0 = 4 * (u % (C / 4));
+      const float4 tv = *reinterpret_cast<const float4*>(&sm.ra.mt.t[rr][s0]);
+      if constexpr (F16) {
+        H8 h8;
+        h8.h[0] = (s0 + 0 <= rr) ? (Op)tv.x : (Op)0.0f;
+        h8.h[1] = (s0 + 1 <= rr) ? (Op)tv.y : (Op)0.0f;
+        h8.h[2] = (s0 + 2 <= rr) ? (Op)tv.z : (Op)0.0f;
+        h8.h[3] = (s0 + 3 <= rr) ? (Op)tv.w : (Op)0.0f;
+        *reinterpret_cast<uint2*>(top + rr * LDT + s0) = h8.u[0];
+      } else {
+        *reinterpret_cast<float4*>(&sm.ra.mt.t[rr][s0]) =
+            make_float4((s0 + 0 <= rr) ? tv.x : 0.0f, (s0 + 1 <= rr) ? tv.y : 0.0f, (s0 + 2 <= rr) ? tv.z : 0.0f,
+                        (s0 + 3 <= rr) ? tv.w : 0.0f);
+      }
     }
     __syncthreads();
 
@@ -1121,10 +1132,516 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
   }
 }
 
+// ---- kernel 1b: chunk preparation, bf16 inputs, dk = 128, chunk 64, eight waves -----
+//
+// Same computation as chunk_prep_kernel (fragment-format record), with the channels
+// of each 16-step tile split over two waves (wave w: tile w % 4, channel half w / 4,
+// i.e. k-blocks 2 (w / 4) and 2 (w / 4) + 1). Half the registers per lane, so two
+// waves share each SIMD and hide each other's latency. The Gram tiles are summed over
+// the two halves through LDS; W and U~ split their column tiles between the halves.
+constexpr bool kUsePrep8 = false;  // (measured slower than chunk_prep_kernel)
+
+struct alignas(16) Prep8Lds {
+  union RA {
+    struct {
+      __bf16 hi[64][136];
+      __bf16 lo[64][136];
+    } am;               // A- (mid reference), Gram phase
+    struct {
+      float m[64][68];  // strictly lower Gram M; T in fp16 after the inverse
+      float t[64][68];  // T = (I + M)^{-1}
+    } mt;
+  } ra;
+  _Float16 bt[128][68];   // B+ transposed
+  _Float16 wvt[128][68];  // written values (scaled), transposed
+  float4 part[4][8][64];  // second-half Gram partials: [tile][M 0..3, P 0..3][lane]
+  float tot[4][128];
+  float gmid_loc[128];
+  float chv[6][128];      // base-2 decay constants: [t] G_mid - prefix, [4] 2^G_mid, [5] 2^(G_C - G_mid)
+  float qpart[2][64];     // per row, per channel half: max |q|
+  float qs[64];
+  float red[8];
+};
+
+template <int V>
+__global__ __launch_bounds__(512, 1) void chunk_prep8_kernel(Problem p, unsigned char* __restrict__ ws,
+                                                             ChunkLayout L, int want_out) {
+  using In = uint16_t;
+  constexpr int DK = 128, C = 64, NT = 4, KB = 4, CK = 2;
+  constexpr bool DP = V == GDN_VARIANT_DELTAPRODUCT;
+  constexpr bool CH_ALPHA = V == GDN_VARIANT_FG2 || V == GDN_VARIANT_KDA || V == GDN_VARIANT_ASYM;
+  constexpr bool CH_BJ = V == GDN_VARIANT_FG2 || V == GDN_VARIANT_ASYM;
+  static_assert(sizeof(Prep8Lds) <= 160 * 1024, "LDS budget");
+  __shared__ Prep8Lds sm;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t = wave & 3, hf = wave >> 2;  // step tile, channel half
+  const int li = lane & 15, lg = lane >> 4;
+  const int r = 16 * t + li;               // step row of this lane
+  const int dv = int(p.dv);
+  const int vnh = dv / 64;                 // value groups of 32 channels per half (1 or 2)
+  const int VT = dv / 16;
+  const int NC = int(p.nchunks);
+  const int H = int(p.H);
+  const int BH = int(p.B) * H;
+  const int total = NC * BH;
+  const In* qg = static_cast<const In*>(p.q);
+  const In* kg = static_cast<const In*>(p.k);
+  const In* vg = static_cast<const In*>(p.v);
+  const In* alg = static_cast<const In*>(p.alpha);
+  const In* beg = static_cast<const In*>(p.beta);
+  const In* bvg = static_cast<const In*>(p.beta_v);
+  const In* jg = static_cast<const In*>(p.j);
+  const In* etg = static_cast<const In*>(p.eta);
+  const bool bv_sep = V == GDN_VARIANT_FG2 && bvg != nullptr;
+  auto ld = [](const In* x) { return IO<In>::ld(x); };
+  // channel of this lane's value x (0..15): k-block 2 hf + x / 8, slot 8 lg + x % 8
+  auto kchan = [&](int x) { return 32 * (2 * hf + x / 8) + 8 * lg + (x & 7); };
+
+  struct Raw8 {
+    uint4 k[2], a[2], bj[2], q[2], v[2], bv[2];
+    float s_alpha, s_beta, s_eta;
+  };
+  struct Where {
+    bool valid;
+    int64_t th, vrow;
+  };
+  auto where = [&](int item) __attribute__((always_inline)) -> Where {
+    Where w;
+    const int n = item / BH, bh = item - n * BH;
+    const int b = bh / H, h = bh - b * H;
+    const int64_t tok = int64_t(n) * C + r;
+    w.valid = tok < p.T;
+    w.th = (int64_t(b) * p.T + tok) * H + h;
+    w.vrow = DP ? w.th * p.n_h : w.th;  // DeltaProduct with one sub-step
+    return w;
+  };
+  auto prefetch = [&](int item, Raw8& raw) __attribute__((always_inline)) {
+    const Where w = where(item);
+    if (!w.valid) return;
+    auto ld_row = [&](const In* row, uint4* dst) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) dst[j] = *reinterpret_cast<const uint4*>(row + 32 * (2 * hf + j) + 8 * lg);
+    };
+    ld_row(kg + w.vrow * DK, raw.k);
+    if constexpr (CH_ALPHA) ld_row(alg + w.th * DK, raw.a);
+    else raw.s_alpha = ld(alg + w.th);
+    if constexpr (V == GDN_VARIANT_FG2) ld_row(beg + w.th * DK, raw.bj);
+    if constexpr (V == GDN_VARIANT_ASYM) {
+      ld_row(jg + w.th * DK, raw.bj);
+      raw.s_eta = ld(etg + w.th);
+    }
+    if constexpr (V == GDN_VARIANT_KDA || V == GDN_VARIANT_GDN) raw.s_beta = ld(beg + w.th);
+    if constexpr (DP) raw.s_beta = ld(beg + w.vrow);
+    if (want_out) ld_row(qg + w.th * DK, raw.q);
+    const In* vrow = vg + w.vrow * dv;
+    const In* bvrow = bvg + w.th * dv;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (j < vnh) {
+        raw.v[j] = *reinterpret_cast<const uint4*>(vrow + 32 * (hf * vnh + j) + 8 * lg);
+        if (bv_sep) raw.bv[j] = *reinterpret_cast<const uint4*>(bvrow + 32 * (hf * vnh + j) + 8 * lg);
+      }
+    }
+  };
+  auto p_frag = [&](int ro, int J) -> size_t {
+    return size_t((((ro >> 4) * CK + (J >> 1)) * 64 + (ro & 15) + 16 * (2 * (J & 1) + (lg >> 1))) * 8 + 4 * (lg & 1));
+  };
+  auto w_frag = [&](int I, int ct) -> size_t {
+    return size_t(((I * KB + (ct >> 1)) * 64 + li + 16 * (2 * (ct & 1) + (lg >> 1))) * 8 + 4 * (lg & 1));
+  };
+  auto u_frag = [&](int I, int ct) -> size_t { return size_t(((I * VT + ct) * 64 + lane) * 4); };
+
+  // 0/1 selection fragments for the MFMA transposes (relative channel 16 h + n)
+  half8 sel[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) sel[hh][s2] = (8 * lg + s2 == li + 16 * hh) ? (_Float16)1.0f : (_Float16)0.0f;
+  auto transpose = [&](half8 x, int hh) __attribute__((always_inline)) -> uint2 {
+    const float4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    const float4v d = mma_pair_f16(x, sel[hh], zero);
+    H8 o8;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o8.h[e] = (_Float16)d[e];
+    return o8.u[0];
+  };
+
+  Raw8 raw;
+  if (int(blockIdx.x) < total) prefetch(blockIdx.x, raw);
+
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    const Where w = where(item);
+    const int item_n = item / BH;
+    unsigned char* rec = ws + (size_t(item - item_n * BH) * size_t(NC) + size_t(item_n)) * L.bytes;
+    _Float16* W_g = reinterpret_cast<_Float16*>(rec + L.off_W);
+    _Float16* AT_g = reinterpret_cast<_Float16*>(rec + L.off_AT);
+    _Float16* Q_g = reinterpret_cast<_Float16*>(rec + L.off_Q);
+    _Float16* P_g = reinterpret_cast<_Float16*>(rec + L.off_P);
+    _Float16* UT_g = reinterpret_cast<_Float16*>(rec + L.off_UT);
+    float* gam_g = reinterpret_cast<float*>(rec + L.off_gamma);
+    float* winv_g = reinterpret_cast<float*>(rec + L.off_winv);
+    float* qinv_g = reinterpret_cast<float*>(rec + L.off_qinv);
+
+    // ---- this lane's half row: keys, log decay (base 2), query, written values ----
+    float a[16], bb[16], G[16], qv[16], wv[16];
+#pragma unroll
+    for (int x = 0; x < 16; ++x) a[x] = bb[x] = G[x] = qv[x] = wv[x] = 0.0f;
+    if (w.valid) {
+      float kf[16], af[16], bf[16], sbk[16];
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        kf[x] = bf16_at(raw.k, x);
+        af[x] = CH_ALPHA ? bf16_at(raw.a, x) : 0.0f;
+        bf[x] = CH_BJ ? bf16_at(raw.bj, x) : 0.0f;
+        if (want_out) qv[x] = bf16_at(raw.q, x);
+      }
+      float wscal = 0.0f;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        if constexpr (V == GDN_VARIANT_FG2) {
+          sbk[x] = __builtin_amdgcn_sqrtf(bf[x]);
+          a[x] = sbk[x] * kf[x];
+          bb[x] = a[x];
+          G[x] = __builtin_amdgcn_logf(af[x]);
+        } else if constexpr (V == GDN_VARIANT_KDA || V == GDN_VARIANT_GDN) {
+          const float sb = __builtin_amdgcn_sqrtf(raw.s_beta);
+          a[x] = sb * kf[x];
+          bb[x] = a[x];
+          G[x] = __builtin_amdgcn_logf(V == GDN_VARIANT_KDA ? af[x] : raw.s_alpha);
+          wscal = sb;
+        } else if constexpr (DP) {
+          a[x] = kf[x];
+          bb[x] = raw.s_beta * kf[x];
+          G[x] = __builtin_amdgcn_logf(raw.s_alpha);
+          wscal = raw.s_beta;
+        } else {  // ASYM
+          a[x] = kf[x];
+          bb[x] = raw.s_eta * bf[x];
+          G[x] = __builtin_amdgcn_logf(af[x]);
+          wscal = raw.s_eta;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (j < vnh) {
+#pragma unroll
+          for (int s2 = 0; s2 < 8; ++s2) {
+            const int y = 8 * j + s2;
+            float f = wscal;
+            if constexpr (V == GDN_VARIANT_FG2) f = bv_sep ? __builtin_amdgcn_sqrtf(bf16_at(raw.bv, y)) : sbk[y];
+            wv[y] = bf16_at(raw.v, y) * f;
+          }
+        }
+      }
+    }
+
+    // inclusive scan of the log decay over the tile's 16 rows; tile totals
+#pragma unroll
+    for (int x = 0; x < 16; ++x) G[x] = scan16(G[x]);
+    if (li == 15) {
+#pragma unroll
+      for (int x = 0; x < 16; ++x) sm.tot[t][kchan(x)] = G[x];
+    }
+    if (t == 1 && li == 15) {  // the middle row, 31
+#pragma unroll
+      for (int x = 0; x < 16; ++x) sm.gmid_loc[kchan(x)] = G[x];
+    }
+    {
+      float mq = 0.0f, mw = 0.0f;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        mq = fmaxf(mq, fabsf(qv[x]));
+        mw = fmaxf(mw, fabsf(wv[x]));
+      }
+      mq = max_over_groups(mq);
+      if (lg == 0) sm.qpart[hf][r] = mq;
+      mw = wave_max(mw);
+      if (lane == 0) sm.red[wave] = mw;
+    }
+    __syncthreads();
+
+    // ---- per-channel decay constants; scales ----
+    if (tid < DK) {
+      const int c = tid;
+      float pre = 0.0f, gm = sm.gmid_loc[c];
+      float pres[NT];
+#pragma unroll
+      for (int I = 0; I < NT; ++I) {
+        pres[I] = pre;
+        if (I < 1) gm += sm.tot[I][c];
+        pre += sm.tot[I][c];
+      }
+#pragma unroll
+      for (int I = 0; I < NT; ++I) sm.chv[I][c] = gm - pres[I];
+      sm.chv[NT][c] = __builtin_amdgcn_exp2f(gm);
+      sm.chv[NT + 1][c] = __builtin_amdgcn_exp2f(pre - gm);
+      gam_g[c] = __builtin_amdgcn_exp2f(pre);
+    }
+    float wsc;
+    {
+      float m = sm.red[0];
+#pragma unroll
+      for (int w2 = 1; w2 < 8; ++w2) m = fmaxf(m, sm.red[w2]);
+      wsc = pow2_scale_for(m);
+    }
+    const float qsc = want_out ? pow2_scale_for(fmaxf(sm.qpart[0][r], sm.qpart[1][r])) : 1.0f;
+    if (tid == 0) winv_g[0] = 1.0f / wsc;
+    __syncthreads();
+
+    // ---- decayed operands ----
+    float bm[16], qm[16];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int u = 2 * hf + j, c0 = 32 * u + 8 * lg;
+      float cof[8], cp[8], cq[8];
+#pragma unroll
+      for (int e = 0; e < 8; e += 4) {
+        const float4 x0 = *reinterpret_cast<const float4*>(&sm.chv[t][c0 + e]);
+        const float4 x1 = *reinterpret_cast<const float4*>(&sm.chv[NT][c0 + e]);
+        const float4 x2 = *reinterpret_cast<const float4*>(&sm.chv[NT + 1][c0 + e]);
+        cof[e] = x0.x, cof[e + 1] = x0.y, cof[e + 2] = x0.z, cof[e + 3] = x0.w;
+        cp[e] = x1.x, cp[e + 1] = x1.y, cp[e + 2] = x1.z, cp[e + 3] = x1.w;
+        cq[e] = x2.x, cq[e + 1] = x2.y, cq[e + 2] = x2.z, cq[e + 3] = x2.w;
+      }
+      half8 xbt, xat;
+      H8 hi, lo, q8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int x = 8 * j + e;
+        const float fup = __builtin_amdgcn_exp2f(G[x] - cof[e]);  // e^{G - G_mid}
+        const float eam = __builtin_amdgcn_rcpf(fup);             // e^{G_mid - G}
+        const float eg = cp[e] * fup;                             // e^{G}
+        const float eat = cq[e] * eam;                            // e^{G_C - G}
+        bm[x] = bb[x] * fup;
+        xbt[e] = (_Float16)(bb[x] * eg);
+        xat[e] = (_Float16)(a[x] * eat);
+        const float am = a[x] * eam;
+        hi.b[e] = (__bf16)am;
+        lo.b[e] = (__bf16)(am - (float)hi.b[e]);
+        qm[x] = qv[x] * fup;
+        q8.h[e] = (_Float16)(qv[x] * eg * qsc);
+      }
+      *reinterpret_cast<uint4*>(&sm.ra.am.hi[r][c0]) = hi.q;
+      *reinterpret_cast<uint4*>(&sm.ra.am.lo[r][c0]) = lo.q;
+      if (want_out) *reinterpret_cast<uint4*>(Q_g + (((t * KB + u) * 64 + li + 16 * lg) * 8)) = q8.q;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int c = 32 * u + 16 * hh + li;
+        *reinterpret_cast<uint2*>(&sm.bt[c][16 * t + 4 * lg]) = transpose(xbt, hh);
+        *reinterpret_cast<uint2*>(AT_g + size_t((((c >> 4) * CK + (t >> 1)) * 64 + li + 16 * (2 * (t & 1) + (lg >> 1))) * 8 +
+                                               4 * (lg & 1))) = transpose(xat, hh);
+      }
+    }
+    if (want_out && hf == 0 && lg == 0) {
+      sm.qs[r] = qsc;
+      qinv_g[r] = 1.0f / qsc;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (j < vnh) {
+        half8 xv;
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2) xv[s2] = (_Float16)(wv[8 * j + s2] * wsc);
+        const int uv = hf * vnh + j;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          *reinterpret_cast<uint2*>(&sm.wvt[32 * uv + 16 * hh + li][16 * t + 4 * lg]) = transpose(xv, hh);
+      }
+    }
+    __syncthreads();
+
+    // ---- Gram tiles over this half's channels (bf16 hi/lo), summed over the halves ----
+    float4v mreg[NT], preg[NT];
+#pragma unroll
+    for (int J = 0; J < NT; ++J) mreg[J] = preg[J] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      H8 bh, bl, qh, ql;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v0 = bm[8 * j + e], v1 = qm[8 * j + e];
+        bh.b[e] = (__bf16)v0;
+        bl.b[e] = (__bf16)(v0 - (float)bh.b[e]);
+        qh.b[e] = (__bf16)v1;
+        ql.b[e] = (__bf16)(v1 - (float)qh.b[e]);
+      }
+      const int c0 = 32 * (2 * hf + j) + 8 * lg;
+      H8 ah[NT], al[NT];
+#pragma unroll
+      for (int J = 0; J < NT; ++J) {
+        ah[J].q = *reinterpret_cast<const uint4*>(&sm.ra.am.hi[16 * J + li][c0]);
+        al[J].q = *reinterpret_cast<const uint4*>(&sm.ra.am.lo[16 * J + li][c0]);
+      }
+#pragma unroll
+      for (int J = 0; J < NT; ++J) mreg[J] = mma_pair_bf16(ah[J].b, bh.b, mreg[J]);
+#pragma unroll
+      for (int J = 0; J < NT; ++J) preg[J] = mma_pair_bf16(ah[J].b, qh.b, preg[J]);
+#pragma unroll
+      for (int J = 0; J < NT; ++J) mreg[J] = mma_pair_bf16(ah[J].b, bl.b, mreg[J]);
+#pragma unroll
+      for (int J = 0; J < NT; ++J) preg[J] = mma_pair_bf16(ah[J].b, ql.b, preg[J]);
+#pragma unroll
+      for (int J = 0; J < NT; ++J) mreg[J] = mma_pair_bf16(al[J].b, bh.b, mreg[J]);
+#pragma unroll
+      for (int J = 0; J < NT; ++J) preg[J] = mma_pair_bf16(al[J].b, qh.b, preg[J]);
+    }
+    if (hf == 1) {
+#pragma unroll
+      for (int J = 0; J < NT; ++J) {
+        sm.part[t][J][lane] = make_float4(mreg[J][0], mreg[J][1], mreg[J][2], mreg[J][3]);
+        sm.part[t][NT + J][lane] = make_float4(preg[J][0], preg[J][1], preg[J][2], preg[J][3]);
+      }
+    }
+    __syncthreads();  // partials complete; A- is dead: its space now holds M and T
+    if (hf == 0) {
+#pragma unroll
+      for (int J = 0; J < NT; ++J) {
+        const float4 pm = sm.part[t][J][lane], pp = sm.part[t][NT + J][lane];
+        const int s0 = 16 * J + 4 * lg;
+        if (J <= t) {
+          float4 m4;
+          m4.x = (s0 + 0 < r) ? mreg[J][0] + pm.x : 0.0f;
+          m4.y = (s0 + 1 < r) ? mreg[J][1] + pm.y : 0.0f;
+          m4.z = (s0 + 2 < r) ? mreg[J][2] + pm.z : 0.0f;
+          m4.w = (s0 + 3 < r) ? mreg[J][3] + pm.w : 0.0f;
+          *reinterpret_cast<float4*>(&sm.ra.mt.m[r][s0]) = m4;
+        }
+        if (want_out) {
+          const float qsl = sm.qs[r];
+          H8 h8;
+          h8.h[0] = (_Float16)((s0 + 0 <= r) ? (preg[J][0] + pp.x) * qsl : 0.0f);
+          h8.h[1] = (_Float16)((s0 + 1 <= r) ? (preg[J][1] + pp.y) * qsl : 0.0f);
+          h8.h[2] = (_Float16)((s0 + 2 <= r) ? (preg[J][2] + pp.z) * qsl : 0.0f);
+          h8.h[3] = (_Float16)((s0 + 3 <= r) ? (preg[J][3] + pp.w) * qsl : 0.0f);
+          *reinterpret_cast<uint2*>(P_g + p_frag(r, J)) = h8.u[0];
+        }
+      }
+    }
+    // every raw value of this item is consumed: load the next item's rows now, so
+    // they arrive while the inverse and W / U~ are computed
+    if (item + int(gridDim.x) < total) prefetch(item + gridDim.x, raw);
+    __syncthreads();
+
+    // ---- T = (I + M)^{-1}: diagonal 16x16 blocks by forward substitution (wave b
+    // does block b, lane c its column c; four partial sums shorten the chain) ----
+    if (wave < NT && lg == 0) {
+      const int bI = wave, c = li;
+      float xcol[16];
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        float s4[4] = {(rr == c) ? 1.0f : 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s2 = 0; s2 < rr; ++s2) s4[s2 & 3] -= sm.ra.mt.m[16 * bI + rr][16 * bI + s2] * xcol[s2];
+        xcol[rr] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+      }
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) sm.ra.mt.t[16 * bI + rr][16 * bI + c] = xcol[rr];
+    }
+    // off-diagonal blocks: T_IJ = -T_II sum_{K=J}^{I-1} M_IK T_KJ, one level per I
+#pragma unroll
+    for (int I = 1; I < NT; ++I) {
+      __syncthreads();
+      if (wave < I) {
+        const int J = wave;
+        float4v xa = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int K = J; K < I; ++K) {
+          float a4[4], b4[4];
+          quad(&sm.ra.mt.m[16 * I + li][16 * K + 4 * lg], a4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) b4[e] = sm.ra.mt.t[16 * K + 4 * lg + e][16 * J + li];
+          xa = mma_slice_f32(a4, b4, xa);
+        }
+        float a4[4], xb[4] = {xa[0], xa[1], xa[2], xa[3]};
+        quad(&sm.ra.mt.t[16 * I + li][16 * I + 4 * lg], a4);
+        const float4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        const float4v y = mma_slice_f32(a4, xb, zero);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.ra.mt.t[16 * I + 4 * lg + e][16 * J + li] = -y[e];
+      }
+    }
+    __syncthreads();
+    // fp16 operand copy of T with a zero upper triangle, over the dead M (4 values a thread)
+    _Float16* top = reinterpret_cast<_Float16*>(&sm.ra.mt.m[0][0]);
+    constexpr int LDT = 2 * 68;
+    for (int u = tid; u < C * C / 4; u += 512) {
+      const int rr = u / (C / 4), s0 = 4 * (u % (C / 4));
+      const float4 tv = *reinterpret_cast<const float4*>(&sm.ra.mt.t[rr][s0]);
+      H8 h8;
+      h8.h[0] = (s0 + 0 <= rr) ? (_Float16)tv.x : (_Float16)0.0f;
+      h8.h[1] = (s0 + 1 <= rr) ? (_Float16)tv.y : (_Float16)0.0f;
+      h8.h[2] = (s0 + 2 <= rr) ? (_Float16)tv.z : (_Float16)0.0f;
+      h8.h[3] = (s0 + 3 <= rr) ? (_Float16)tv.w : (_Float16)0.0f;
+      *reinterpret_cast<uint2*>(top + rr * LDT + s0) = h8.u[0];
+    }
+    __syncthreads();
+
+    // ---- W and U~ of step tile t; this half's column tiles ----
+    {
+      H8 ta[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const _Float16* trow = top + (16 * t + li) * LDT + 32 * u + 4 * lg;
+        ta[u] = pair4(trow, trow + 16);
+      }
+      float4v wacc[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wacc[j] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const _Float16* brow = &sm.bt[16 * (4 * hf + j) + li][32 * u + 4 * lg];
+          wacc[j] = mma_pair_f16(pair4(brow, brow + 16).h, ta[u].h, wacc[j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        H8 h8;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h8.h[e] = (_Float16)wacc[j][e];
+        *reinterpret_cast<uint2*>(W_g + w_frag(t, 4 * hf + j)) = h8.u[0];
+      }
+      const int uct = VT / 2;  // U~ column tiles of this half (2 or 4)
+      float4v uacc[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) uacc[j] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int ct = hf * uct + min(j, uct - 1);
+          const _Float16* brow = &sm.wvt[16 * ct + li][32 * u + 4 * lg];
+          uacc[j] = mma_pair_f16(ta[u].h, pair4(brow, brow + 16).h, uacc[j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j < uct) {
+          H8 h8;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h8.h[e] = (_Float16)uacc[j][e];
+          *reinterpret_cast<uint2*>(UT_g + u_frag(t, hf * uct + j)) = h8.u[0];
+        }
+      }
+    }
+    __syncthreads();  // LDS is reused by the next chunk
+  }
+}
+
 template <typename In, int DK, int C, int V, bool DPV>
 int launch_prep_t(const Problem& p, void* ws, bool want_out, hipStream_t s) {
   const ChunkLayout L = chunk_layout(p);
   const int64_t items = p.nchunks * p.B * p.H;
+  if constexpr (std::is_same<In, uint16_t>::value && DK == 128 && C == 64 && !DPV) {
+    if (kUsePrep8 && (p.dv == 64 || p.dv == 128)) {  // eight-wave kernel (fragment-format record)
+      const int64_t grid = std::min<int64_t>(items, int64_t(device_cus()));
+      chunk_prep8_kernel<V><<<dim3(unsigned(grid)), 512, 0, s>>>(p, static_cast<unsigned char*>(ws), L,
+                                                                   want_out ? 1 : 0);
+      return int(hipGetLastError());
+    }
+  }
   constexpr size_t lds = sizeof(PrepLds<std::is_same<In, uint16_t>::value, DK, C, DPV>);
   const int per_cu = lds <= 40 * 1024 ? 4 : lds <= 80 * 1024 ? 2 : 1;
   const int64_t grid = std::min<int64_t>(items, int64_t(device_cus()) * per_cu);
