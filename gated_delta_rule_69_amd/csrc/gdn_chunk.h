@@ -338,12 +338,14 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
     w.ro = DPV ? r / n_h : r;
     return w;
   };
-  // Issue every load of this lane's row of `item` (bf16 rows only; fp32 rows are
-  // read where they are used).
-  auto prefetch = [&](int item, Raw& raw) __attribute__((always_inline)) {
+  // Issue the loads of this lane's row of the item at `w` (bf16 rows only; fp32 rows
+  // are read where they are used): part 0 key, 1 decay, 2 beta / j, 3 query,
+  // 4 values, -1 all. Spreading the parts over the iteration keeps the memory
+  // pipeline busy without stalling the issuing wave on a burst of requests.
+  auto prefetch = [&](const Where& w, Raw& raw, int part) __attribute__((always_inline)) {
     if constexpr (F16) {
-      const Where w = where(item);
       if (!w.valid) return;
+      const bool all = part < 0;
       auto ld_row = [&](const In* row, uint4* dst) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < Raw::KU; ++u) {
@@ -355,22 +357,26 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
           }
         }
       };
-      ld_row(kg + w.vrow * DK, raw.k);
-      if constexpr (CH_ALPHA) ld_row(alg + w.th * DK, raw.a);
-      else raw.s_alpha = ld(alg + w.th);
-      if constexpr (V == GDN_VARIANT_FG2) ld_row(beg + w.th * DK, raw.bj);
-      if constexpr (V == GDN_VARIANT_ASYM) {
-        ld_row(jg + w.th * DK, raw.bj);
-        raw.s_eta = ld(etg + w.th);
+      if (all || part == 0) ld_row(kg + w.vrow * DK, raw.k);
+      if (all || part == 1) {
+        if constexpr (CH_ALPHA) ld_row(alg + w.th * DK, raw.a);
+        else raw.s_alpha = ld(alg + w.th);
       }
-      if constexpr (V == GDN_VARIANT_KDA || V == GDN_VARIANT_GDN) raw.s_beta = ld(beg + w.th);
-      if constexpr (DP) raw.s_beta = ld(beg + w.vrow);
-      if (w.out_row) ld_row(qg + w.th * DK, raw.q);
+      if (all || part == 2) {
+        if constexpr (V == GDN_VARIANT_FG2) ld_row(beg + w.th * DK, raw.bj);
+        if constexpr (V == GDN_VARIANT_ASYM) {
+          ld_row(jg + w.th * DK, raw.bj);
+          raw.s_eta = ld(etg + w.th);
+        }
+        if constexpr (V == GDN_VARIANT_KDA || V == GDN_VARIANT_GDN) raw.s_beta = ld(beg + w.th);
+        if constexpr (DP) raw.s_beta = ld(beg + w.vrow);
+      }
+      if ((all || part == 3) && w.out_row) ld_row(qg + w.th * DK, raw.q);
       const In* vrow = vg + w.vrow * dv;
       const In* bvrow = bvg + w.th * dv;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        if (u < vnu) {
+        if ((all || part == 4) && u < vnu) {
           if (vuw == 8) {
             raw.v[u] = *reinterpret_cast<const uint4*>(vrow + u * 32 + 8 * lg);
             if (bv_sep) raw.bv[u] = *reinterpret_cast<const uint4*>(bvrow + u * 32 + 8 * lg);
@@ -411,10 +417,12 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
     }
 
   Raw raw;
-  if (int(blockIdx.x) < total) prefetch(blockIdx.x, raw);
+  if (int(blockIdx.x) < total) prefetch(where(blockIdx.x), raw, -1);
 
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     const Where w = where(item);
+    const bool has_next = item + int(gridDim.x) < total;
+    const Where wn = where(has_next ? item + int(gridDim.x) : item);
     const int item_n = item / BH;
     unsigned char* rec = ws + (size_t(item - item_n * BH) * size_t(NC) + size_t(item_n)) * L.bytes;
     Op* W_g = reinterpret_cast<Op*>(rec + L.off_W);
@@ -519,6 +527,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
       }
     }
 
+    // The raw rows are consumed: the next item's loads go out part by part.
+    if (has_next) prefetch(wn, raw, 0);
     // inclusive scan of the log decay over the tile's 16 rows, then tile totals
 #pragma unroll
     for (int x = 0; x < NX; ++x) G[x] = scan16(G[x]);
@@ -761,6 +771,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
       }
     }
     __syncthreads();
+    if (has_next) prefetch(wn, raw, 1);
 
     // A^ transposed (fp32 path): the LDS tile has the record's row pitch (C + 4),
     // so the copy is flat and coalesced (the pad columns are never read as
@@ -941,9 +952,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
       }
     }
     }  // generic Gram path
-    // Every raw value of this item is consumed: load the next item's rows now so
-    // they arrive while the inverse and W / U~ are computed.
-    if (item + int(gridDim.x) < total) prefetch(item + gridDim.x, raw);
+    if (has_next) prefetch(wn, raw, 2);
     __syncthreads();  // A- is dead: its space now holds M and T
     if (owner) {
 #pragma unroll
@@ -1001,6 +1010,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
       }
     }
     __syncthreads();
+    if (has_next) prefetch(wn, raw, 3);
     // operand copy of T with a zero upper triangle (fp16 over the dead M; fp32 in place)
     Op* top = F16 ? reinterpret_cast<Op*>(&sm.ra.mt.m[0][0]) : reinterpret_cast<Op*>(&sm.ra.mt.t[0][0]);
     constexpr int LDT = F16 ? 2 * Sm::LDC : Sm::LDC;  // fp16 rows over fp32 rows: twice the elements
@@ -1128,6 +1138,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
       }
     }
     }  // generic W / U~ path
+    if (has_next) prefetch(wn, raw, 4);
     __syncthreads();  // LDS is reused by the next chunk
   }
 }
