@@ -1143,119 +1143,153 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
   }
 }
 
-// ---- kernel 1b: chunk preparation, bf16 inputs, dk = 128, chunk 64, eight waves -----
+// ---- kernel 1b: chunk preparation with LDS-staged inputs ---------------------------
 //
-// Same computation as chunk_prep_kernel (fragment-format record), with the channels
-// of each 16-step tile split over two waves (wave w: tile w % 4, channel half w / 4,
-// i.e. k-blocks 2 (w / 4) and 2 (w / 4) + 1). Half the registers per lane, so two
-// waves share each SIMD and hide each other's latency. The Gram tiles are summed over
-// the two halves through LDS; W and U~ split their column tiles between the halves.
-constexpr bool kUsePrep8 = false;  // (measured slower than chunk_prep_kernel)
-
-struct alignas(16) Prep8Lds {
+// bf16 inputs, dk = dv = 128, chunk 64, one step per token (every variant but
+// DeltaProduct with n_h >= 2, and FG2 without its own value-side beta). Same
+// computation and record as chunk_prep_kernel; what changes is how the inputs
+// arrive. Each wave copies its own 16 rows of every input tensor of the next chunk
+// global -> LDS with direct-to-LDS loads (no registers are held while they are in
+// flight, and nothing waits for them until the next chunk starts), and decodes the
+// rows where they are used, so the per-lane register set stays small. A row is 256
+// bytes; the 16-byte slot of channel group c of row r sits at slot c ^ (r % 16), so
+// the 16 rows a wave reads at once fall in distinct banks. Rows past the end of
+// the sequence are loaded from its last row (finite values) and then masked.
+struct alignas(16) StagedLds {
   union RA {
     struct {
       __bf16 hi[64][136];
       __bf16 lo[64][136];
-    } am;               // A- (mid reference), Gram phase
+    } am;                   // A- (mid reference), Gram phase
     struct {
-      float m[64][68];  // strictly lower Gram M; T in fp16 after the inverse
-      float t[64][68];  // T = (I + M)^{-1}
+      float m[64][68];      // strictly lower Gram M; T in fp16 after the inverse
+      float t[64][68];      // T = (I + M)^{-1}
     } mt;
   } ra;
-  _Float16 bt[128][68];   // B+ transposed
-  _Float16 wvt[128][68];  // written values (scaled), transposed
-  float4 part[4][8][64];  // second-half Gram partials: [tile][M 0..3, P 0..3][lane]
-  float tot[4][128];
-  float gmid_loc[128];
-  float chv[6][128];      // base-2 decay constants: [t] G_mid - prefix, [4] 2^G_mid, [5] 2^(G_C - G_mid)
-  float qpart[2][64];     // per row, per channel half: max |q|
-  float qs[64];
-  float red[8];
+  _Float16 bt[128][68];     // B+ (chunk-start reference), transposed
+  _Float16 wvt[128][68];    // written values (scaled), transposed
+  float tot[4][128];        // per-tile totals of the log decay (base 2)
+  float gmid_loc[128];      // in-tile prefix at the middle row
+  float chv[6][128];        // [t] G_mid - prefix before tile t, [4] 2^G_mid, [5] 2^(G_C - G_mid)
+  float red[kWaves];
 };
 
+// Whether the staged kernel covers a problem (bf16, dk = dv = 128, chunk 64, one
+// step per token, no separate value-side beta).
+inline bool staged_prep_covers(const Problem& p) {
+  return p.dtype == GDN_DTYPE_BF16 && p.dk == 128 && p.dv == 128 && p.chunk == 64 &&
+         !(p.variant == GDN_VARIANT_DELTAPRODUCT && p.n_h > 1) &&
+         !(p.variant == GDN_VARIANT_FG2 && p.beta_v != nullptr);
+}
+
 template <int V>
-__global__ __launch_bounds__(512, 1) void chunk_prep8_kernel(Problem p, unsigned char* __restrict__ ws,
-                                                             ChunkLayout L, int want_out) {
+__global__ __launch_bounds__(kThreads) void chunk_prep_staged_kernel(Problem p, unsigned char* __restrict__ ws,
+                                                                     ChunkLayout L, int want_out) {
   using In = uint16_t;
-  constexpr int DK = 128, C = 64, NT = 4, KB = 4, CK = 2;
+  constexpr int DK = 128, C = 64, NT = 4, KB = 4, CK = 2, CT = 8, VT = 8;
   constexpr bool DP = V == GDN_VARIANT_DELTAPRODUCT;
   constexpr bool CH_ALPHA = V == GDN_VARIANT_FG2 || V == GDN_VARIANT_KDA || V == GDN_VARIANT_ASYM;
-  constexpr bool CH_BJ = V == GDN_VARIANT_FG2 || V == GDN_VARIANT_ASYM;
-  static_assert(sizeof(Prep8Lds) <= 160 * 1024, "LDS budget");
-  __shared__ Prep8Lds sm;
+  constexpr bool CH_BJ = V == GDN_VARIANT_FG2 || V == GDN_VARIANT_ASYM;  // per-channel beta / j
+  // staged tensors: key, query, values, then the per-channel decay and beta / j
+  constexpr int R_K = 0, R_Q = 1, R_V = 2, R_A = 3, R_B = CH_ALPHA ? 4 : 3;
+  constexpr int NRAW = 3 + (CH_ALPHA ? 1 : 0) + (CH_BJ ? 1 : 0);
+  using Sm = StagedLds;
+  static_assert(sizeof(Sm) + NRAW * 64 * 256 <= 160 * 1024, "LDS budget");
+  constexpr int mid = C / 2 - 1, tile_mid = mid / 16, row_mid = mid % 16;
+  __shared__ Sm sm;
+  // Staged input rows (bf16, swizzled 16-byte slots), one array per tensor: the
+  // compiler orders LDS accesses after pending direct-to-LDS copies only when they
+  // may touch the same array, so separate arrays keep the copies of the next
+  // chunk from stalling the reads of this one.
+  __shared__ uint4 raw_k[64][16], raw_q[64][16], raw_v[64][16];
+  __shared__ uint4 raw_a[CH_ALPHA ? 64 : 1][16], raw_b[CH_BJ ? 64 : 1][16];
+  auto raw_rows = [&](int slot) __attribute__((always_inline)) -> uint4(*)[16] {
+    return slot == R_K ? raw_k : slot == R_Q ? raw_q : slot == R_V ? raw_v : slot == R_A ? raw_a : raw_b;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int t = wave & 3, hf = wave >> 2;  // step tile, channel half
   const int li = lane & 15, lg = lane >> 4;
-  const int r = 16 * t + li;               // step row of this lane
-  const int dv = int(p.dv);
-  const int vnh = dv / 64;                 // value groups of 32 channels per half (1 or 2)
-  const int VT = dv / 16;
+  const int r = 16 * wave + li;  // step row of this lane
   const int NC = int(p.nchunks);
   const int H = int(p.H);
   const int BH = int(p.B) * H;
-  const int total = NC * BH;
+  const int total = NC * BH;  // < 2^31 (checked on the host)
+  const int64_t T = p.T;
   const In* qg = static_cast<const In*>(p.q);
   const In* kg = static_cast<const In*>(p.k);
   const In* vg = static_cast<const In*>(p.v);
   const In* alg = static_cast<const In*>(p.alpha);
   const In* beg = static_cast<const In*>(p.beta);
-  const In* bvg = static_cast<const In*>(p.beta_v);
   const In* jg = static_cast<const In*>(p.j);
   const In* etg = static_cast<const In*>(p.eta);
-  const bool bv_sep = V == GDN_VARIANT_FG2 && bvg != nullptr;
   auto ld = [](const In* x) { return IO<In>::ld(x); };
-  // channel of this lane's value x (0..15): k-block 2 hf + x / 8, slot 8 lg + x % 8
-  auto kchan = [&](int x) { return 32 * (2 * hf + x / 8) + 8 * lg + (x & 7); };
 
-  struct Raw8 {
-    uint4 k[2], a[2], bj[2], q[2], v[2], bv[2];
-    float s_alpha, s_beta, s_eta;
+  // first token-head row (b, token n C, h) of an item, chunk-major order
+  struct Item {
+    int n, bh;
+    int64_t th0;  // (b T + n C) H + h
   };
-  struct Where {
-    bool valid;
-    int64_t th, vrow;
+  auto item_of = [&](int item) __attribute__((always_inline)) -> Item {
+    Item it;
+    it.n = item / BH;
+    it.bh = item - it.n * BH;
+    const int b = it.bh / H, h = it.bh - b * H;
+    it.th0 = (int64_t(b) * T + int64_t(it.n) * C) * H + h;
+    return it;
   };
-  auto where = [&](int item) __attribute__((always_inline)) -> Where {
-    Where w;
-    const int n = item / BH, bh = item - n * BH;
-    const int b = bh / H, h = bh - b * H;
-    const int64_t tok = int64_t(n) * C + r;
-    w.valid = tok < p.T;
-    w.th = (int64_t(b) * p.T + tok) * H + h;
-    w.vrow = DP ? w.th * p.n_h : w.th;  // DeltaProduct with one sub-step
-    return w;
+  // token-head row of step row rr (clamped to the sequence's last token)
+  auto th_of = [&](const Item& it, int rr) __attribute__((always_inline)) -> int64_t {
+    const int64_t last = T - 1 - int64_t(it.n) * C;  // >= 0
+    return it.th0 + min(int64_t(rr), last) * H;
   };
-  auto prefetch = [&](int item, Raw8& raw) __attribute__((always_inline)) {
-    const Where w = where(item);
-    if (!w.valid) return;
-    auto ld_row = [&](const In* row, uint4* dst) __attribute__((always_inline)) {
+
+  // Copy this wave's 16 rows of one tensor of `it` into its LDS slot: four 1 KB
+  // direct-to-LDS loads, lane l moving 16 bytes of row 16 wave + 4 j + l / 16.
+  auto stage = [&](const Item& it, const In* base, int slot) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) dst[j] = *reinterpret_cast<const uint4*>(row + 32 * (2 * hf + j) + 8 * lg);
-    };
-    ld_row(kg + w.vrow * DK, raw.k);
-    if constexpr (CH_ALPHA) ld_row(alg + w.th * DK, raw.a);
-    else raw.s_alpha = ld(alg + w.th);
-    if constexpr (V == GDN_VARIANT_FG2) ld_row(beg + w.th * DK, raw.bj);
-    if constexpr (V == GDN_VARIANT_ASYM) {
-      ld_row(jg + w.th * DK, raw.bj);
-      raw.s_eta = ld(etg + w.th);
-    }
-    if constexpr (V == GDN_VARIANT_KDA || V == GDN_VARIANT_GDN) raw.s_beta = ld(beg + w.th);
-    if constexpr (DP) raw.s_beta = ld(beg + w.vrow);
-    if (want_out) ld_row(qg + w.th * DK, raw.q);
-    const In* vrow = vg + w.vrow * dv;
-    const In* bvrow = bvg + w.th * dv;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (j < vnh) {
-        raw.v[j] = *reinterpret_cast<const uint4*>(vrow + 32 * (hf * vnh + j) + 8 * lg);
-        if (bv_sep) raw.bv[j] = *reinterpret_cast<const uint4*>(bvrow + 32 * (hf * vnh + j) + 8 * lg);
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int rr = 16 * wave + 4 * j + (lane >> 4);
+      const int c = (lane & 15) ^ (rr & 15);  // logical 16-byte group of this lane's slot
+      const In* src = base + th_of(it, rr) * DK + 8 * c;
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
+                                       reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                           reinterpret_cast<uintptr_t>(&raw_rows(slot)[16 * wave + 4 * j][0]) & 0xffffffffu),
+                                       16, 0, 0);
     }
   };
+  // this lane's 8 bf16 values of channel group u (channels 32 u + 8 lg ..) of its row
+  auto raw8 = [&](int slot, int u) __attribute__((always_inline)) -> uint4 {
+    return raw_rows(slot)[r][(4 * u + lg) ^ li];
+  };
+  auto bf = [](const uint4& v, int s) __attribute__((always_inline)) -> float {
+    const uint32_t w = s / 2 == 0 ? v.x : s / 2 == 1 ? v.y : s / 2 == 2 ? v.z : v.w;
+    return __uint_as_float((s & 1) ? (w & 0xffff0000u) : (w << 16));
+  };
+  // per-row scalars (gates of the scalar-gated variants), loaded with the stage
+  struct Scal {
+    float alpha, beta, eta;
+  };
+  auto load_scal = [&](const Item& it) __attribute__((always_inline)) -> Scal {
+    Scal s{1.0f, 0.0f, 0.0f};
+    const int64_t th = th_of(it, r);
+    if constexpr (!CH_ALPHA) s.alpha = ld(alg + th);
+    if constexpr (V == GDN_VARIANT_KDA || V == GDN_VARIANT_GDN || DP) s.beta = ld(beg + th);
+    if constexpr (V == GDN_VARIANT_ASYM) s.eta = ld(etg + th);
+    return s;
+  };
+  // Order a wave's LDS reads of its staged rows before the direct-to-LDS writes
+  // that replace them, and the copies of a chunk before its first read.
+  auto lds_reads_done = []() __attribute__((always_inline)) { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
+  auto copies_landed = []() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  // Workgroup barrier for LDS traffic only. The waves exchange data through LDS
+  // alone (each wave reads back only the rows it staged itself), so the barrier
+  // waits for this wave's LDS operations but not for its outstanding global loads,
+  // stores and direct-to-LDS copies, which a fenced barrier would drain.
+  auto wg_barrier = []() __attribute__((always_inline)) { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+  // fragment-format offsets (elements): P row ro, steps 16 J + 4 lg ..; W row
+  // 16 I + li, channels 16 ct + 4 lg ..; U~ steps 16 I + 4 lg .., column 16 ct + li
   auto p_frag = [&](int ro, int J) -> size_t {
     return size_t((((ro >> 4) * CK + (J >> 1)) * 64 + (ro & 15) + 16 * (2 * (J & 1) + (lg >> 1))) * 8 + 4 * (lg & 1));
   };
@@ -1264,28 +1298,33 @@ __global__ __launch_bounds__(512, 1) void chunk_prep8_kernel(Problem p, unsigned
   };
   auto u_frag = [&](int I, int ct) -> size_t { return size_t(((I * VT + ct) * 64 + lane) * 4); };
 
-  // 0/1 selection fragments for the MFMA transposes (relative channel 16 h + n)
+  // 0/1 selection fragments (B operand of a 16x16x32 MFMA) that move the k-slot of
+  // relative channel 16 h + n to column n (an exact transpose of a row group)
   half8 sel[2];
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
     for (int s2 = 0; s2 < 8; ++s2) sel[hh][s2] = (8 * lg + s2 == li + 16 * hh) ? (_Float16)1.0f : (_Float16)0.0f;
-  auto transpose = [&](half8 x, int hh) __attribute__((always_inline)) -> uint2 {
-    const float4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    const float4v d = mma_pair_f16(x, sel[hh], zero);
-    H8 o8;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o8.h[e] = (_Float16)d[e];
-    return o8.u[0];
-  };
 
-  Raw8 raw;
-  if (int(blockIdx.x) < total) prefetch(blockIdx.x, raw);
+  // stage the first item; later items are staged during the one before
+  Scal scal{1.0f, 0.0f, 0.0f};
+  if (int(blockIdx.x) < total) {
+    const Item it = item_of(blockIdx.x);
+    stage(it, kg, R_K);
+    if (want_out) stage(it, qg, R_Q);
+    stage(it, vg, R_V);
+    if constexpr (CH_ALPHA) stage(it, alg, R_A);
+    if constexpr (V == GDN_VARIANT_FG2) stage(it, beg, R_B);
+    if constexpr (V == GDN_VARIANT_ASYM) stage(it, jg, R_B);
+    scal = load_scal(it);
+  }
 
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    const Where w = where(item);
-    const int item_n = item / BH;
-    unsigned char* rec = ws + (size_t(item - item_n * BH) * size_t(NC) + size_t(item_n)) * L.bytes;
+    const Item it = item_of(item);
+    const bool has_next = item + int(gridDim.x) < total;
+    const Item nx = item_of(has_next ? item + int(gridDim.x) : item);
+    const bool valid = int64_t(it.n) * C + r < p.steps;
+    unsigned char* rec = ws + (size_t(it.bh) * size_t(NC) + size_t(it.n)) * L.bytes;
     _Float16* W_g = reinterpret_cast<_Float16*>(rec + L.off_W);
     _Float16* AT_g = reinterpret_cast<_Float16*>(rec + L.off_AT);
     _Float16* Q_g = reinterpret_cast<_Float16*>(rec + L.off_Q);
@@ -1294,86 +1333,71 @@ __global__ __launch_bounds__(512, 1) void chunk_prep8_kernel(Problem p, unsigned
     float* gam_g = reinterpret_cast<float*>(rec + L.off_gamma);
     float* winv_g = reinterpret_cast<float*>(rec + L.off_winv);
     float* qinv_g = reinterpret_cast<float*>(rec + L.off_qinv);
+    copies_landed();
 
-    // ---- this lane's half row: keys, log decay (base 2), query, written values ----
-    float a[16], bb[16], G[16], qv[16], wv[16];
+    // ---- per-row factors of the variant: key side sqrt(beta) (scalar variants),
+    // written-value scale, scalar log decay; invalid rows get zero weights ----
+    const Scal sc = scal;
+    float kscal = 1.0f, wscal = 0.0f, bscal = 1.0f, glog = 0.0f;
+    if constexpr (V == GDN_VARIANT_KDA || V == GDN_VARIANT_GDN) {
+      kscal = __builtin_amdgcn_sqrtf(sc.beta);
+      wscal = kscal;
+      if constexpr (V == GDN_VARIANT_GDN) glog = __builtin_amdgcn_logf(sc.alpha);
+    } else if constexpr (DP) {
+      bscal = sc.beta;
+      wscal = sc.beta;
+      glog = __builtin_amdgcn_logf(sc.alpha);
+    } else if constexpr (V == GDN_VARIANT_ASYM) {
+      bscal = sc.eta;
+      wscal = sc.eta;
+    }
+    if (!valid) kscal = wscal = bscal = glog = 0.0f;
+
+    // ---- phase 1: log decay, written values, row maxima ----
+    float G[32], wv[32];
+    float qmax = 0.0f, wmax = 0.0f;
 #pragma unroll
-    for (int x = 0; x < 16; ++x) a[x] = bb[x] = G[x] = qv[x] = wv[x] = 0.0f;
-    if (w.valid) {
-      float kf[16], af[16], bf[16], sbk[16];
+    for (int u = 0; u < 4; ++u) {
+      const uint4 vr = raw8(R_V, u);
+      uint4 ar = {}, br = {}, qr = {};
+      if constexpr (CH_ALPHA) ar = raw8(R_A, u);
+      if constexpr (V == GDN_VARIANT_FG2) br = raw8(R_B, u);
+      if (want_out && valid) qr = raw8(R_Q, u);
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        kf[x] = bf16_at(raw.k, x);
-        af[x] = CH_ALPHA ? bf16_at(raw.a, x) : 0.0f;
-        bf[x] = CH_BJ ? bf16_at(raw.bj, x) : 0.0f;
-        if (want_out) qv[x] = bf16_at(raw.q, x);
-      }
-      float wscal = 0.0f;
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        if constexpr (V == GDN_VARIANT_FG2) {
-          sbk[x] = __builtin_amdgcn_sqrtf(bf[x]);
-          a[x] = sbk[x] * kf[x];
-          bb[x] = a[x];
-          G[x] = __builtin_amdgcn_logf(af[x]);
-        } else if constexpr (V == GDN_VARIANT_KDA || V == GDN_VARIANT_GDN) {
-          const float sb = __builtin_amdgcn_sqrtf(raw.s_beta);
-          a[x] = sb * kf[x];
-          bb[x] = a[x];
-          G[x] = __builtin_amdgcn_logf(V == GDN_VARIANT_KDA ? af[x] : raw.s_alpha);
-          wscal = sb;
-        } else if constexpr (DP) {
-          a[x] = kf[x];
-          bb[x] = raw.s_beta * kf[x];
-          G[x] = __builtin_amdgcn_logf(raw.s_alpha);
-          wscal = raw.s_beta;
-        } else {  // ASYM
-          a[x] = kf[x];
-          bb[x] = raw.s_eta * bf[x];
-          G[x] = __builtin_amdgcn_logf(af[x]);
-          wscal = raw.s_eta;
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        if (j < vnh) {
-#pragma unroll
-          for (int s2 = 0; s2 < 8; ++s2) {
-            const int y = 8 * j + s2;
-            float f = wscal;
-            if constexpr (V == GDN_VARIANT_FG2) f = bv_sep ? __builtin_amdgcn_sqrtf(bf16_at(raw.bv, y)) : sbk[y];
-            wv[y] = bf16_at(raw.v, y) * f;
-          }
-        }
+      for (int s2 = 0; s2 < 8; ++s2) {
+        const int x = 8 * u + s2;
+        if constexpr (CH_ALPHA) G[x] = valid ? __builtin_amdgcn_logf(bf(ar, s2)) : 0.0f;
+        else G[x] = glog;
+        float f = wscal;
+        if constexpr (V == GDN_VARIANT_FG2) f = valid ? __builtin_amdgcn_sqrtf(bf(br, s2)) : 0.0f;
+        wv[x] = bf(vr, s2) * f;
+        wmax = fmaxf(wmax, fabsf(wv[x]));
+        qmax = fmaxf(qmax, fabsf(bf(qr, s2)));
       }
     }
-
-    // inclusive scan of the log decay over the tile's 16 rows; tile totals
+    lds_reads_done();
+    if (has_next) {  // the decay and values of this item are read: stage the next item's
+      stage(nx, vg, R_V);
+      if constexpr (CH_ALPHA) stage(nx, alg, R_A);
+    }
+    // inclusive scan of the log decay over the tile's 16 rows, then tile totals
 #pragma unroll
-    for (int x = 0; x < 16; ++x) G[x] = scan16(G[x]);
+    for (int x = 0; x < 32; ++x) G[x] = scan16(G[x]);
     if (li == 15) {
 #pragma unroll
-      for (int x = 0; x < 16; ++x) sm.tot[t][kchan(x)] = G[x];
+      for (int x = 0; x < 32; ++x) sm.tot[wave][32 * (x / 8) + 8 * lg + x % 8] = G[x];
     }
-    if (t == 1 && li == 15) {  // the middle row, 31
+    if (wave == tile_mid && li == row_mid) {
 #pragma unroll
-      for (int x = 0; x < 16; ++x) sm.gmid_loc[kchan(x)] = G[x];
+      for (int x = 0; x < 32; ++x) sm.gmid_loc[32 * (x / 8) + 8 * lg + x % 8] = G[x];
     }
-    {
-      float mq = 0.0f, mw = 0.0f;
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        mq = fmaxf(mq, fabsf(qv[x]));
-        mw = fmaxf(mw, fabsf(wv[x]));
-      }
-      mq = max_over_groups(mq);
-      if (lg == 0) sm.qpart[hf][r] = mq;
-      mw = wave_max(mw);
-      if (lane == 0) sm.red[wave] = mw;
-    }
-    __syncthreads();
+    // power-of-two scales: per output row for q, per chunk for the written values
+    const float qsc = want_out ? pow2_scale_for(max_over_groups(qmax)) : 1.0f;
+    wmax = wave_max(wmax);
+    if (lane == 0) sm.red[wave] = wmax;
+    wg_barrier();
 
-    // ---- per-channel decay constants; scales ----
+    // ---- per-channel decay constants (one thread per key channel) ----
     if (tid < DK) {
       const int c = tid;
       float pre = 0.0f, gm = sm.gmid_loc[c];
@@ -1381,7 +1405,7 @@ __global__ __launch_bounds__(512, 1) void chunk_prep8_kernel(Problem p, unsigned
 #pragma unroll
       for (int I = 0; I < NT; ++I) {
         pres[I] = pre;
-        if (I < 1) gm += sm.tot[I][c];
+        if (I < tile_mid) gm += sm.tot[I][c];
         pre += sm.tot[I][c];
       }
 #pragma unroll
@@ -1394,91 +1418,124 @@ __global__ __launch_bounds__(512, 1) void chunk_prep8_kernel(Problem p, unsigned
     {
       float m = sm.red[0];
 #pragma unroll
-      for (int w2 = 1; w2 < 8; ++w2) m = fmaxf(m, sm.red[w2]);
+      for (int w2 = 1; w2 < kWaves; ++w2) m = fmaxf(m, sm.red[w2]);
       wsc = pow2_scale_for(m);
     }
-    const float qsc = want_out ? pow2_scale_for(fmaxf(sm.qpart[0][r], sm.qpart[1][r])) : 1.0f;
     if (tid == 0) winv_g[0] = 1.0f / wsc;
-    __syncthreads();
+    if (want_out && lg == 0) qinv_g[r] = 1.0f / qsc;
+    wg_barrier();
 
-    // ---- decayed operands ----
-    float bm[16], qm[16];
+    // ---- phase 2a: written values, scaled, transposed into LDS by MFMA ----
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int u = 2 * hf + j, c0 = 32 * u + 8 * lg;
+    for (int u = 0; u < 4; ++u) {
+      half8 xv;
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2) xv[s2] = (_Float16)(wv[8 * u + s2] * wsc);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const float4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        const float4v tv = mma_pair_f16(xv, sel[hh], zero);
+        H8 pv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pv.h[e] = (_Float16)tv[e];
+        *reinterpret_cast<uint2*>(&sm.wvt[32 * u + 16 * hh + li][16 * wave + 4 * lg]) = pv.u[0];
+      }
+    }
+
+    // ---- phase 2b: decayed operands of this wave's rows, one channel group at a time ----
+    H8 bmh[KB], bml[KB], qmh8[KB], qml8[KB];  // B sides of the Grams (bf16 hi / lo)
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int c0 = 32 * u + 8 * lg;  // 8 consecutive channels
       float cof[8], cp[8], cq[8];
 #pragma unroll
       for (int e = 0; e < 8; e += 4) {
-        const float4 x0 = *reinterpret_cast<const float4*>(&sm.chv[t][c0 + e]);
+        const float4 x0 = *reinterpret_cast<const float4*>(&sm.chv[wave][c0 + e]);
         const float4 x1 = *reinterpret_cast<const float4*>(&sm.chv[NT][c0 + e]);
         const float4 x2 = *reinterpret_cast<const float4*>(&sm.chv[NT + 1][c0 + e]);
         cof[e] = x0.x, cof[e + 1] = x0.y, cof[e + 2] = x0.z, cof[e + 3] = x0.w;
         cp[e] = x1.x, cp[e + 1] = x1.y, cp[e + 2] = x1.z, cp[e + 3] = x1.w;
         cq[e] = x2.x, cq[e + 1] = x2.y, cq[e + 2] = x2.z, cq[e + 3] = x2.w;
       }
+      const uint4 kr = raw8(R_K, u);
+      uint4 br = {}, qr = {};
+      if constexpr (CH_BJ) br = raw8(R_B, u);
+      if (want_out && valid) qr = raw8(R_Q, u);
       half8 xbt, xat;
-      H8 hi, lo, q8;
+      H8 hi, lo, qp;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int x = 8 * j + e;
-        const float fup = __builtin_amdgcn_exp2f(G[x] - cof[e]);  // e^{G - G_mid}
-        const float eam = __builtin_amdgcn_rcpf(fup);             // e^{G_mid - G}
-        const float eg = cp[e] * fup;                             // e^{G}
-        const float eat = cq[e] * eam;                            // e^{G_C - G}
-        bm[x] = bb[x] * fup;
-        xbt[e] = (_Float16)(bb[x] * eg);
-        xat[e] = (_Float16)(a[x] * eat);
-        const float am = a[x] * eam;
+        const float kf = bf(kr, e);
+        float a, bb;
+        if constexpr (V == GDN_VARIANT_FG2) {
+          a = (valid ? __builtin_amdgcn_sqrtf(bf(br, e)) : 0.0f) * kf;
+          bb = a;
+        } else if constexpr (V == GDN_VARIANT_ASYM) {
+          a = valid ? kf : 0.0f;
+          bb = bscal * bf(br, e);
+        } else {  // KDA, GDN (kscal = sqrt(beta)); DeltaProduct (bscal = beta)
+          a = kscal * kf;
+          bb = bscal * a;
+        }
+        const float fup = __builtin_amdgcn_exp2f(G[8 * u + e] - cof[e]);  // e^{G - G_mid}
+        const float eam = __builtin_amdgcn_rcpf(fup);                     // e^{G_mid - G}
+        const float eg = cp[e] * fup;                                     // e^{G}
+        const float eat = cq[e] * eam;                                    // e^{G_C - G}
+        xbt[e] = (_Float16)(bb * eg);
+        xat[e] = (_Float16)(a * eat);
+        const float am = a * eam;
         hi.b[e] = (__bf16)am;
         lo.b[e] = (__bf16)(am - (float)hi.b[e]);
-        qm[x] = qv[x] * fup;
-        q8.h[e] = (_Float16)(qv[x] * eg * qsc);
+        const float bm = bb * fup;
+        bmh[u].b[e] = (__bf16)bm;
+        bml[u].b[e] = (__bf16)(bm - (float)bmh[u].b[e]);
+        const float qf = bf(qr, e);
+        const float qm = qf * fup;
+        qmh8[u].b[e] = (__bf16)qm;
+        qml8[u].b[e] = (__bf16)(qm - (float)qmh8[u].b[e]);
+        qp.h[e] = (_Float16)(qf * eg * qsc);
       }
       *reinterpret_cast<uint4*>(&sm.ra.am.hi[r][c0]) = hi.q;
       *reinterpret_cast<uint4*>(&sm.ra.am.lo[r][c0]) = lo.q;
-      if (want_out) *reinterpret_cast<uint4*>(Q_g + (((t * KB + u) * 64 + li + 16 * lg) * 8)) = q8.q;
+      if (want_out)
+        *reinterpret_cast<uint4*>(Q_g + ((((r >> 4) * KB + u) * 64 + (r & 15) + 16 * lg) * 8)) = qp.q;
+      // B+ and A^ of the group transposed by MFMA: lane (li, lg) then holds steps
+      // 16 wave + 4 lg .. of channel 32 u + 16 h + li
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
+        const float4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        const float4v tb = mma_pair_f16(xbt, sel[hh], zero);
+        const float4v ta = mma_pair_f16(xat, sel[hh], zero);
         const int c = 32 * u + 16 * hh + li;
-        *reinterpret_cast<uint2*>(&sm.bt[c][16 * t + 4 * lg]) = transpose(xbt, hh);
-        *reinterpret_cast<uint2*>(AT_g + size_t((((c >> 4) * CK + (t >> 1)) * 64 + li + 16 * (2 * (t & 1) + (lg >> 1))) * 8 +
-                                               4 * (lg & 1))) = transpose(xat, hh);
+        H8 pb, pa;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pb.h[e] = (_Float16)tb[e];
+          pa.h[e] = (_Float16)ta[e];
+        }
+        *reinterpret_cast<uint2*>(&sm.bt[c][16 * wave + 4 * lg]) = pb.u[0];
+        *reinterpret_cast<uint2*>(AT_g + size_t((((c >> 4) * CK + (wave >> 1)) * 64 + li + 16 * (2 * (wave & 1) + (lg >> 1))) * 8 +
+                                                4 * (lg & 1))) = pa.u[0];
       }
     }
-    if (want_out && hf == 0 && lg == 0) {
-      sm.qs[r] = qsc;
-      qinv_g[r] = 1.0f / qsc;
+    lds_reads_done();
+    if (has_next) {  // every staged row of this item is read: stage the rest of the next one
+      stage(nx, kg, R_K);
+      if (want_out) stage(nx, qg, R_Q);
+      if constexpr (V == GDN_VARIANT_FG2) stage(nx, beg, R_B);
+      if constexpr (V == GDN_VARIANT_ASYM) stage(nx, jg, R_B);
+      scal = load_scal(nx);
     }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (j < vnh) {
-        half8 xv;
-#pragma unroll
-        for (int s2 = 0; s2 < 8; ++s2) xv[s2] = (_Float16)(wv[8 * j + s2] * wsc);
-        const int uv = hf * vnh + j;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          *reinterpret_cast<uint2*>(&sm.wvt[32 * uv + 16 * hh + li][16 * t + 4 * lg]) = transpose(xv, hh);
-      }
-    }
-    __syncthreads();
+    wg_barrier();
 
-    // ---- Gram tiles over this half's channels (bf16 hi/lo), summed over the halves ----
+    // ---- Gram tiles: M^T(J, I) = A-(J) B+(I)^T and P^T(J, I) = A-(J) Q+(I)^T, every J
+    // together, k-block outer (tiles above the diagonal are computed and masked) ----
     float4v mreg[NT], preg[NT];
 #pragma unroll
     for (int J = 0; J < NT; ++J) mreg[J] = preg[J] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      H8 bh, bl, qh, ql;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v0 = bm[8 * j + e], v1 = qm[8 * j + e];
-        bh.b[e] = (__bf16)v0;
-        bl.b[e] = (__bf16)(v0 - (float)bh.b[e]);
-        qh.b[e] = (__bf16)v1;
-        ql.b[e] = (__bf16)(v1 - (float)qh.b[e]);
-      }
-      const int c0 = 32 * (2 * hf + j) + 8 * lg;
+    for (int u = 0; u < KB; ++u) {
+      const int c0 = 32 * u + 8 * lg;
       H8 ah[NT], al[NT];
 #pragma unroll
       for (int J = 0; J < NT; ++J) {
@@ -1486,59 +1543,46 @@ __global__ __launch_bounds__(512, 1) void chunk_prep8_kernel(Problem p, unsigned
         al[J].q = *reinterpret_cast<const uint4*>(&sm.ra.am.lo[16 * J + li][c0]);
       }
 #pragma unroll
-      for (int J = 0; J < NT; ++J) mreg[J] = mma_pair_bf16(ah[J].b, bh.b, mreg[J]);
+      for (int J = 0; J < NT; ++J) mreg[J] = mma_pair_bf16(ah[J].b, bmh[u].b, mreg[J]);
 #pragma unroll
-      for (int J = 0; J < NT; ++J) preg[J] = mma_pair_bf16(ah[J].b, qh.b, preg[J]);
+      for (int J = 0; J < NT; ++J) preg[J] = mma_pair_bf16(ah[J].b, qmh8[u].b, preg[J]);
 #pragma unroll
-      for (int J = 0; J < NT; ++J) mreg[J] = mma_pair_bf16(ah[J].b, bl.b, mreg[J]);
+      for (int J = 0; J < NT; ++J) mreg[J] = mma_pair_bf16(ah[J].b, bml[u].b, mreg[J]);
 #pragma unroll
-      for (int J = 0; J < NT; ++J) preg[J] = mma_pair_bf16(ah[J].b, ql.b, preg[J]);
+      for (int J = 0; J < NT; ++J) preg[J] = mma_pair_bf16(ah[J].b, qml8[u].b, preg[J]);
 #pragma unroll
-      for (int J = 0; J < NT; ++J) mreg[J] = mma_pair_bf16(al[J].b, bh.b, mreg[J]);
+      for (int J = 0; J < NT; ++J) mreg[J] = mma_pair_bf16(al[J].b, bmh[u].b, mreg[J]);
 #pragma unroll
-      for (int J = 0; J < NT; ++J) preg[J] = mma_pair_bf16(al[J].b, qh.b, preg[J]);
+      for (int J = 0; J < NT; ++J) preg[J] = mma_pair_bf16(al[J].b, qmh8[u].b, preg[J]);
     }
-    if (hf == 1) {
+    if (want_out) {  // output rows are this wave's own rows (q scale qsc)
 #pragma unroll
       for (int J = 0; J < NT; ++J) {
-        sm.part[t][J][lane] = make_float4(mreg[J][0], mreg[J][1], mreg[J][2], mreg[J][3]);
-        sm.part[t][NT + J][lane] = make_float4(preg[J][0], preg[J][1], preg[J][2], preg[J][3]);
-      }
-    }
-    __syncthreads();  // partials complete; A- is dead: its space now holds M and T
-    if (hf == 0) {
-#pragma unroll
-      for (int J = 0; J < NT; ++J) {
-        const float4 pm = sm.part[t][J][lane], pp = sm.part[t][NT + J][lane];
         const int s0 = 16 * J + 4 * lg;
-        if (J <= t) {
-          float4 m4;
-          m4.x = (s0 + 0 < r) ? mreg[J][0] + pm.x : 0.0f;
-          m4.y = (s0 + 1 < r) ? mreg[J][1] + pm.y : 0.0f;
-          m4.z = (s0 + 2 < r) ? mreg[J][2] + pm.z : 0.0f;
-          m4.w = (s0 + 3 < r) ? mreg[J][3] + pm.w : 0.0f;
-          *reinterpret_cast<float4*>(&sm.ra.mt.m[r][s0]) = m4;
-        }
-        if (want_out) {
-          const float qsl = sm.qs[r];
-          H8 h8;
-          h8.h[0] = (_Float16)((s0 + 0 <= r) ? (preg[J][0] + pp.x) * qsl : 0.0f);
-          h8.h[1] = (_Float16)((s0 + 1 <= r) ? (preg[J][1] + pp.y) * qsl : 0.0f);
-          h8.h[2] = (_Float16)((s0 + 2 <= r) ? (preg[J][2] + pp.z) * qsl : 0.0f);
-          h8.h[3] = (_Float16)((s0 + 3 <= r) ? (preg[J][3] + pp.w) * qsl : 0.0f);
-          *reinterpret_cast<uint2*>(P_g + p_frag(r, J)) = h8.u[0];
-        }
+        H8 h8;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h8.h[e] = (_Float16)((s0 + e <= r) ? preg[J][e] * qsc : 0.0f);
+        *reinterpret_cast<uint2*>(P_g + p_frag(r, J)) = h8.u[0];
       }
     }
-    // every raw value of this item is consumed: load the next item's rows now, so
-    // they arrive while the inverse and W / U~ are computed
-    if (item + int(gridDim.x) < total) prefetch(item + gridDim.x, raw);
-    __syncthreads();
+    wg_barrier();  // A- is dead: its space now holds M and T
+#pragma unroll
+    for (int J = 0; J < NT; ++J) {
+      if (J <= wave) {
+        const int s0 = 16 * J + 4 * lg;
+        float4 m4;
+        m4.x = (s0 + 0 < r) ? mreg[J][0] : 0.0f;
+        m4.y = (s0 + 1 < r) ? mreg[J][1] : 0.0f;
+        m4.z = (s0 + 2 < r) ? mreg[J][2] : 0.0f;
+        m4.w = (s0 + 3 < r) ? mreg[J][3] : 0.0f;
+        *reinterpret_cast<float4*>(&sm.ra.mt.m[r][s0]) = m4;
+      }
+    }
+    wg_barrier();
 
-    // ---- T = (I + M)^{-1}: diagonal 16x16 blocks by forward substitution (wave b
-    // does block b, lane c its column c; four partial sums shorten the chain) ----
-    if (wave < NT && lg == 0) {
-      const int bI = wave, c = li;
+    // ---- T = (I + M)^{-1}: diagonal 16x16 blocks by forward substitution ----
+    if (wave == 0) {
+      const int bI = lane >> 4, c = lane & 15;
       float xcol[16];
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
@@ -1553,7 +1597,7 @@ __global__ __launch_bounds__(512, 1) void chunk_prep8_kernel(Problem p, unsigned
     // off-diagonal blocks: T_IJ = -T_II sum_{K=J}^{I-1} M_IK T_KJ, one level per I
 #pragma unroll
     for (int I = 1; I < NT; ++I) {
-      __syncthreads();
+      wg_barrier();
       if (wave < I) {
         const int J = wave;
         float4v xa = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -1572,11 +1616,11 @@ __global__ __launch_bounds__(512, 1) void chunk_prep8_kernel(Problem p, unsigned
         for (int e = 0; e < 4; ++e) sm.ra.mt.t[16 * I + 4 * lg + e][16 * J + li] = -y[e];
       }
     }
-    __syncthreads();
-    // fp16 operand copy of T with a zero upper triangle, over the dead M (4 values a thread)
+    wg_barrier();
+    // operand copy of T in fp16 with a zero upper triangle, over the dead M
     _Float16* top = reinterpret_cast<_Float16*>(&sm.ra.mt.m[0][0]);
     constexpr int LDT = 2 * 68;
-    for (int u = tid; u < C * C / 4; u += 512) {
+    for (int u = tid; u < C * C / 4; u += kThreads) {
       const int rr = u / (C / 4), s0 = 4 * (u % (C / 4));
       const float4 tv = *reinterpret_cast<const float4*>(&sm.ra.mt.t[rr][s0]);
       H8 h8;
@@ -1586,58 +1630,57 @@ __global__ __launch_bounds__(512, 1) void chunk_prep8_kernel(Problem p, unsigned
       h8.h[3] = (s0 + 3 <= rr) ? (_Float16)tv.w : (_Float16)0.0f;
       *reinterpret_cast<uint2*>(top + rr * LDT + s0) = h8.u[0];
     }
-    __syncthreads();
+    wg_barrier();
 
-    // ---- W and U~ of step tile t; this half's column tiles ----
+    // ---- W^T = B+^T T^T (stored as W rows) and U~ = T Wv (stored transposed): wave w
+    // computes the tiles of step rows 16 w .., independent chains interleaved ----
+    H8 ta[2];  // T rows 16 w + li, steps 32 u + 4 lg .. (+16)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const _Float16* trow = top + (16 * wave + li) * LDT + 32 * u + 4 * lg;
+      ta[u] = pair4(trow, trow + 16);
+    }
     {
-      H8 ta[2];
+      float4v wacc[CT];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const _Float16* trow = top + (16 * t + li) * LDT + 32 * u + 4 * lg;
-        ta[u] = pair4(trow, trow + 16);
-      }
-      float4v wacc[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) wacc[j] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int ct = 0; ct < CT; ++ct) wacc[ct] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const _Float16* brow = &sm.bt[16 * (4 * hf + j) + li][32 * u + 4 * lg];
-          wacc[j] = mma_pair_f16(pair4(brow, brow + 16).h, ta[u].h, wacc[j]);
+        for (int ct = 0; ct < CT; ++ct) {
+          const _Float16* brow = &sm.bt[16 * ct + li][32 * u + 4 * lg];
+          wacc[ct] = mma_pair_f16(pair4(brow, brow + 16).h, ta[u].h, wacc[ct]);
         }
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int ct = 0; ct < CT; ++ct) {
         H8 h8;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) h8.h[e] = (_Float16)wacc[j][e];
-        *reinterpret_cast<uint2*>(W_g + w_frag(t, 4 * hf + j)) = h8.u[0];
+        for (int e = 0; e < 4; ++e) h8.h[e] = (_Float16)wacc[ct][e];
+        *reinterpret_cast<uint2*>(W_g + w_frag(wave, ct)) = h8.u[0];
       }
-      const int uct = VT / 2;  // U~ column tiles of this half (2 or 4)
-      float4v uacc[4];
+    }
+    {
+      float4v uacc[VT];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) uacc[j] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int ct = 0; ct < VT; ++ct) uacc[ct] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int ct = hf * uct + min(j, uct - 1);
+        for (int ct = 0; ct < VT; ++ct) {
           const _Float16* brow = &sm.wvt[16 * ct + li][32 * u + 4 * lg];
-          uacc[j] = mma_pair_f16(ta[u].h, pair4(brow, brow + 16).h, uacc[j]);
+          uacc[ct] = mma_pair_f16(ta[u].h, pair4(brow, brow + 16).h, uacc[ct]);
         }
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (j < uct) {
-          H8 h8;
+      for (int ct = 0; ct < VT; ++ct) {
+        H8 h8;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) h8.h[e] = (_Float16)uacc[j][e];
-          *reinterpret_cast<uint2*>(UT_g + u_frag(t, hf * uct + j)) = h8.u[0];
-        }
+        for (int e = 0; e < 4; ++e) h8.h[e] = (_Float16)uacc[ct][e];
+        *reinterpret_cast<uint2*>(UT_g + u_frag(wave, ct)) = h8.u[0];
       }
     }
-    __syncthreads();  // LDS is reused by the next chunk
+    wg_barrier();  // LDS is reused by the next chunk
   }
 }
 
@@ -1646,10 +1689,10 @@ int launch_prep_t(const Problem& p, void* ws, bool want_out, hipStream_t s) {
   const ChunkLayout L = chunk_layout(p);
   const int64_t items = p.nchunks * p.B * p.H;
   if constexpr (std::is_same<In, uint16_t>::value && DK == 128 && C == 64 && !DPV) {
-    if (kUsePrep8 && (p.dv == 64 || p.dv == 128)) {  // eight-wave kernel (fragment-format record)
+    if (staged_prep_covers(p)) {  // one workgroup per CU (about 150 KB of LDS)
       const int64_t grid = std::min<int64_t>(items, int64_t(device_cus()));
-      chunk_prep8_kernel<V><<<dim3(unsigned(grid)), 512, 0, s>>>(p, static_cast<unsigned char*>(ws), L,
-                                                                   want_out ? 1 : 0);
+      chunk_prep_staged_kernel<V><<<dim3(unsigned(grid)), kThreads, 0, s>>>(p, static_cast<unsigned char*>(ws), L,
+                                                                             want_out ? 1 : 0);
       return int(hipGetLastError());
     }
   }
