@@ -163,10 +163,19 @@ __device__ __forceinline__ H8 pair4(const void* p0, const void* p1) {
   return r;
 }
 
+// DPP lane permutation CTRL of a float (every lane reads a lane of its own row).
+template <int CTRL>
+__device__ __forceinline__ float dpp_perm(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// Maximum over the wave: within each 16-lane row by DPP lane swaps (quads, then
+// half-row and row mirrors), across rows by the lane-swap instructions.
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
-  return x;
+  x = fmaxf(x, dpp_perm<0xb1>(x));   // quad_perm 1,0,3,2
+  x = fmaxf(x, dpp_perm<0x4e>(x));   // quad_perm 2,3,0,1
+  x = fmaxf(x, dpp_perm<0x141>(x));  // row_half_mirror
+  x = fmaxf(x, dpp_perm<0x140>(x));  // row_mirror
+  return max_over_groups(x);
 }
 
 // Inclusive prefix sum over the 16 lanes of each DPP row (lanes 16 g .. 16 g + 15,
@@ -1143,19 +1152,18 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
   }
 }
 
-// ---- kernel 1b: chunk preparation with LDS-staged inputs ---------------------------
+// ---- kernel 1b: chunk preparation, two workgroups per CU ----------------------------
 //
 // bf16 inputs, dk = dv = 128, chunk 64, one step per token (every variant but
-// DeltaProduct with n_h >= 2, and FG2 without its own value-side beta). Same
-// computation and record as chunk_prep_kernel; what changes is how the inputs
-// arrive. Each wave copies its own 16 rows of every input tensor of the next chunk
-// global -> LDS with direct-to-LDS loads (no registers are held while they are in
-// flight, and nothing waits for them until the next chunk starts), and decodes the
-// rows where they are used, so the per-lane register set stays small. A row is 256
-// bytes; the 16-byte slot of channel group c of row r sits at slot c ^ (r % 16), so
-// the 16 rows a wave reads at once fall in distinct banks. Rows past the end of
-// the sequence are loaded from its last row (finite values) and then masked.
-struct alignas(16) StagedLds {
+// DeltaProduct with n_h >= 2, and FG2 with its own value-side beta). Same
+// computation and record as chunk_prep_kernel, arranged so that two workgroups fit
+// on a CU (under 80 KB of LDS, at most 256 registers a lane) and one hides the
+// other's latencies: each lane loads its row of the next chunk into registers
+// while W and U~ of the current one are computed, decodes values where they are
+// used, keeps only the decay logs across the first barriers, and takes the scale
+// maxima on bf16 bit patterns. Barriers wait for LDS traffic only. Rows past the
+// end of the sequence are loaded from its last row (finite values) and masked.
+struct alignas(16) PrepLds2 {
   union RA {
     struct {
       __bf16 hi[64][136];
@@ -1174,43 +1182,43 @@ struct alignas(16) StagedLds {
   float red[kWaves];
 };
 
-// Whether the staged kernel covers a problem (bf16, dk = dv = 128, chunk 64, one
+// Whether chunk_prep2_kernel covers a problem (bf16, dk = dv = 128, chunk 64, one
 // step per token, no separate value-side beta).
-inline bool staged_prep_covers(const Problem& p) {
+inline bool prep2_covers(const Problem& p) {
   return p.dtype == GDN_DTYPE_BF16 && p.dk == 128 && p.dv == 128 && p.chunk == 64 &&
          !(p.variant == GDN_VARIANT_DELTAPRODUCT && p.n_h > 1) &&
          !(p.variant == GDN_VARIANT_FG2 && p.beta_v != nullptr);
 }
 
 template <int V>
-__global__ __launch_bounds__(kThreads) void chunk_prep_staged_kernel(Problem p, unsigned char* __restrict__ ws,
+__global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, unsigned char* __restrict__ ws,
                                                                      ChunkLayout L, int want_out) {
   using In = uint16_t;
   constexpr int DK = 128, C = 64, NT = 4, KB = 4, CK = 2, CT = 8, VT = 8;
   constexpr bool DP = V == GDN_VARIANT_DELTAPRODUCT;
   constexpr bool CH_ALPHA = V == GDN_VARIANT_FG2 || V == GDN_VARIANT_KDA || V == GDN_VARIANT_ASYM;
   constexpr bool CH_BJ = V == GDN_VARIANT_FG2 || V == GDN_VARIANT_ASYM;  // per-channel beta / j
-  // staged tensors: key, query, values, then the per-channel decay and beta / j
-  constexpr int R_K = 0, R_Q = 1, R_V = 2, R_A = 3, R_B = CH_ALPHA ? 4 : 3;
-  constexpr int NRAW = 3 + (CH_ALPHA ? 1 : 0) + (CH_BJ ? 1 : 0);
-  using Sm = StagedLds;
-  static_assert(sizeof(Sm) + NRAW * 64 * 256 <= 160 * 1024, "LDS budget");
+  using Sm = PrepLds2;
+  static_assert(sizeof(Sm) <= 80 * 1024, "two workgroups per CU");
   constexpr int mid = C / 2 - 1, tile_mid = mid / 16, row_mid = mid % 16;
   __shared__ Sm sm;
-  // Staged input rows (bf16, swizzled 16-byte slots), one array per tensor: the
-  // compiler orders LDS accesses after pending direct-to-LDS copies only when they
-  // may touch the same array, so separate arrays keep the copies of the next
-  // chunk from stalling the reads of this one.
-  __shared__ uint4 raw_k[64][16], raw_q[64][16], raw_v[64][16];
-  __shared__ uint4 raw_a[CH_ALPHA ? 64 : 1][16], raw_b[CH_BJ ? 64 : 1][16];
-  auto raw_rows = [&](int slot) __attribute__((always_inline)) -> uint4(*)[16] {
-    return slot == R_K ? raw_k : slot == R_Q ? raw_q : slot == R_V ? raw_v : slot == R_A ? raw_a : raw_b;
-  };
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  // Lane indices are re-derived at the top of every item from an opaque copy of
+  // the thread id: otherwise the compiler keeps every lane-dependent address of
+  // the loop body live across it, more registers than two waves per SIMD allow.
+  int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int li = lane & 15, lg = lane >> 4;
-  const int r = 16 * wave + li;  // step row of this lane
+  int li = lane & 15, lg = lane >> 4;
+  int r = 16 * wave + li;  // step row of this lane
+  auto lane_ids = [&]() __attribute__((always_inline)) {
+    int t = int(threadIdx.x);
+    asm volatile("" : "+v"(t));
+    tid = t;
+    lane = t & 63;
+    li = lane & 15;
+    lg = lane >> 4;
+    r = 16 * wave + li;
+  };
   const int NC = int(p.nchunks);
   const int H = int(p.H);
   const int BH = int(p.B) * H;
@@ -1244,23 +1252,23 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_staged_kernel(Problem p, 
     return it.th0 + min(int64_t(rr), last) * H;
   };
 
-  // Copy this wave's 16 rows of one tensor of `it` into its LDS slot: four 1 KB
-  // direct-to-LDS loads, lane l moving 16 bytes of row 16 wave + 4 j + l / 16.
-  auto stage = [&](const Item& it, const In* base, int slot) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int rr = 16 * wave + 4 * j + (lane >> 4);
-      const int c = (lane & 15) ^ (rr & 15);  // logical 16-byte group of this lane's slot
-      const In* src = base + th_of(it, rr) * DK + 8 * c;
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
-                                       reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                           reinterpret_cast<uintptr_t>(&raw_rows(slot)[16 * wave + 4 * j][0]) & 0xffffffffu),
-                                       16, 0, 0);
-    }
+  // This lane's row of an item's inputs in 16-byte groups (group u: channels
+  // 32 u + 8 lg ..), loaded into registers one item ahead.
+  struct Raw {
+    uint4 k[4], a[4], b[4], q[4], v[4];
   };
-  // this lane's 8 bf16 values of channel group u (channels 32 u + 8 lg ..) of its row
-  auto raw8 = [&](int slot, int u) __attribute__((always_inline)) -> uint4 {
-    return raw_rows(slot)[r][(4 * u + lg) ^ li];
+  auto load_raw = [&](const Item& it, Raw& x) __attribute__((always_inline)) {
+    const int64_t off = th_of(it, r) * DK + 8 * lg;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      auto ld16 = [&](const In* base) { return *reinterpret_cast<const uint4*>(base + off + 32 * u); };
+      x.k[u] = ld16(kg);
+      x.v[u] = ld16(vg);
+      if (want_out) x.q[u] = ld16(qg);
+      if constexpr (CH_ALPHA) x.a[u] = ld16(alg);
+      if constexpr (V == GDN_VARIANT_FG2) x.b[u] = ld16(beg);
+      if constexpr (V == GDN_VARIANT_ASYM) x.b[u] = ld16(jg);
+    }
   };
   auto bf = [](const uint4& v, int s) __attribute__((always_inline)) -> float {
     const uint32_t w = s / 2 == 0 ? v.x : s / 2 == 1 ? v.y : s / 2 == 2 ? v.z : v.w;
@@ -1278,14 +1286,9 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_staged_kernel(Problem p, 
     if constexpr (V == GDN_VARIANT_ASYM) s.eta = ld(etg + th);
     return s;
   };
-  // Order a wave's LDS reads of its staged rows before the direct-to-LDS writes
-  // that replace them, and the copies of a chunk before its first read.
-  auto lds_reads_done = []() __attribute__((always_inline)) { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
-  auto copies_landed = []() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
   // Workgroup barrier for LDS traffic only. The waves exchange data through LDS
-  // alone (each wave reads back only the rows it staged itself), so the barrier
-  // waits for this wave's LDS operations but not for its outstanding global loads,
-  // stores and direct-to-LDS copies, which a fenced barrier would drain.
+  // alone, so the barrier waits for this wave's LDS operations but not for its
+  // outstanding global loads and stores, which a fenced barrier would drain.
   auto wg_barrier = []() __attribute__((always_inline)) { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
   // fragment-format offsets (elements): P row ro, steps 16 J + 4 lg ..; W row
@@ -1306,20 +1309,17 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_staged_kernel(Problem p, 
 #pragma unroll
     for (int s2 = 0; s2 < 8; ++s2) sel[hh][s2] = (8 * lg + s2 == li + 16 * hh) ? (_Float16)1.0f : (_Float16)0.0f;
 
-  // stage the first item; later items are staged during the one before
+  // the first item's inputs; later items load during the one before
   Scal scal{1.0f, 0.0f, 0.0f};
+  Raw raw;
   if (int(blockIdx.x) < total) {
     const Item it = item_of(blockIdx.x);
-    stage(it, kg, R_K);
-    if (want_out) stage(it, qg, R_Q);
-    stage(it, vg, R_V);
-    if constexpr (CH_ALPHA) stage(it, alg, R_A);
-    if constexpr (V == GDN_VARIANT_FG2) stage(it, beg, R_B);
-    if constexpr (V == GDN_VARIANT_ASYM) stage(it, jg, R_B);
+    load_raw(it, raw);
     scal = load_scal(it);
   }
 
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    lane_ids();
     const Item it = item_of(item);
     const bool has_next = item + int(gridDim.x) < total;
     const Item nx = item_of(has_next ? item + int(gridDim.x) : item);
@@ -1333,7 +1333,6 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_staged_kernel(Problem p, 
     float* gam_g = reinterpret_cast<float*>(rec + L.off_gamma);
     float* winv_g = reinterpret_cast<float*>(rec + L.off_winv);
     float* qinv_g = reinterpret_cast<float*>(rec + L.off_qinv);
-    copies_landed();
 
     // ---- per-row factors of the variant: key side sqrt(beta) (scalar variants),
     // written-value scale, scalar log decay; invalid rows get zero weights ----
@@ -1353,33 +1352,37 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_staged_kernel(Problem p, 
     }
     if (!valid) kscal = wscal = bscal = glog = 0.0f;
 
-    // ---- phase 1: log decay, written values, row maxima ----
-    float G[32], wv[32];
-    float qmax = 0.0f, wmax = 0.0f;
+    // ---- phase 1: log decay and row maxima ----
+    // The maxima only set power-of-two scales. They are taken on the bf16 bit
+    // patterns (for non-negative values the order of the patterns is the order of
+    // the values), two at a time; the written values' scale uses the bound
+    // max |v| max sqrt(beta) of the row, which keeps the scaled values below 2^13.
+    float G[32];
+    ushort2v qm2 = {0, 0}, vm2 = {0, 0}, bm2 = {0, 0};
+    auto absmax2 = [](ushort2v m, uint32_t w) __attribute__((always_inline)) {
+      return __builtin_elementwise_max(m, __builtin_bit_cast(ushort2v, w & 0x7fff7fffu));
+    };
+    auto absmax8 = [&](ushort2v m, const uint4& x) __attribute__((always_inline)) {
+      return absmax2(absmax2(absmax2(absmax2(m, x.x), x.y), x.z), x.w);
+    };
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const uint4 vr = raw8(R_V, u);
-      uint4 ar = {}, br = {}, qr = {};
-      if constexpr (CH_ALPHA) ar = raw8(R_A, u);
-      if constexpr (V == GDN_VARIANT_FG2) br = raw8(R_B, u);
-      if (want_out && valid) qr = raw8(R_Q, u);
 #pragma unroll
       for (int s2 = 0; s2 < 8; ++s2) {
         const int x = 8 * u + s2;
-        if constexpr (CH_ALPHA) G[x] = valid ? __builtin_amdgcn_logf(bf(ar, s2)) : 0.0f;
+        if constexpr (CH_ALPHA) G[x] = valid ? __builtin_amdgcn_logf(bf(raw.a[u], s2)) : 0.0f;
         else G[x] = glog;
-        float f = wscal;
-        if constexpr (V == GDN_VARIANT_FG2) f = valid ? __builtin_amdgcn_sqrtf(bf(br, s2)) : 0.0f;
-        wv[x] = bf(vr, s2) * f;
-        wmax = fmaxf(wmax, fabsf(wv[x]));
-        qmax = fmaxf(qmax, fabsf(bf(qr, s2)));
       }
+      vm2 = absmax8(vm2, raw.v[u]);
+      if (want_out) qm2 = absmax8(qm2, raw.q[u]);
+      if constexpr (V == GDN_VARIANT_FG2) bm2 = absmax8(bm2, raw.b[u]);
     }
-    lds_reads_done();
-    if (has_next) {  // the decay and values of this item are read: stage the next item's
-      stage(nx, vg, R_V);
-      if constexpr (CH_ALPHA) stage(nx, alg, R_A);
-    }
+    auto bits_max = [](ushort2v m) __attribute__((always_inline)) {
+      return __uint_as_float(uint32_t(m.x > m.y ? m.x : m.y) << 16);
+    };
+    const float qmax = valid ? bits_max(qm2) : 0.0f;
+    float wmax = bits_max(vm2) * (V == GDN_VARIANT_FG2 ? (valid ? __builtin_amdgcn_sqrtf(bits_max(bm2)) : 0.0f)
+                                                         : fabsf(wscal));
     // inclusive scan of the log decay over the tile's 16 rows, then tile totals
 #pragma unroll
     for (int x = 0; x < 32; ++x) G[x] = scan16(G[x]);
@@ -1425,24 +1428,9 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_staged_kernel(Problem p, 
     if (want_out && lg == 0) qinv_g[r] = 1.0f / qsc;
     wg_barrier();
 
-    // ---- phase 2a: written values, scaled, transposed into LDS by MFMA ----
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      half8 xv;
-#pragma unroll
-      for (int s2 = 0; s2 < 8; ++s2) xv[s2] = (_Float16)(wv[8 * u + s2] * wsc);
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const float4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
-        const float4v tv = mma_pair_f16(xv, sel[hh], zero);
-        H8 pv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pv.h[e] = (_Float16)tv[e];
-        *reinterpret_cast<uint2*>(&sm.wvt[32 * u + 16 * hh + li][16 * wave + 4 * lg]) = pv.u[0];
-      }
-    }
-
-    // ---- phase 2b: decayed operands of this wave's rows, one channel group at a time ----
+    // ---- phase 2: decayed operands and written values of this wave's rows, one
+    // channel group at a time ----
+    const float wrow = (V == GDN_VARIANT_FG2 ? 1.0f : wscal) * wsc;  // written-value factor of the row
     H8 bmh[KB], bml[KB], qmh8[KB], qml8[KB];  // B sides of the Grams (bf16 hi / lo)
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
@@ -1457,19 +1445,21 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_staged_kernel(Problem p, 
         cp[e] = x1.x, cp[e + 1] = x1.y, cp[e + 2] = x1.z, cp[e + 3] = x1.w;
         cq[e] = x2.x, cq[e + 1] = x2.y, cq[e + 2] = x2.z, cq[e + 3] = x2.w;
       }
-      const uint4 kr = raw8(R_K, u);
+      const uint4 kr = raw.k[u], vr = raw.v[u];
       uint4 br = {}, qr = {};
-      if constexpr (CH_BJ) br = raw8(R_B, u);
-      if (want_out && valid) qr = raw8(R_Q, u);
-      half8 xbt, xat;
+      if constexpr (CH_BJ) br = raw.b[u];
+      if (want_out && valid) qr = raw.q[u];
+      half8 xbt, xat, xv;
       H8 hi, lo, qp;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float kf = bf(kr, e);
         float a, bb;
         if constexpr (V == GDN_VARIANT_FG2) {
-          a = (valid ? __builtin_amdgcn_sqrtf(bf(br, e)) : 0.0f) * kf;
+          const float sb = valid ? __builtin_amdgcn_sqrtf(bf(br, e)) : 0.0f;
+          a = sb * kf;
           bb = a;
+          xv[e] = (_Float16)(bf(vr, e) * sb * wsc);
         } else if constexpr (V == GDN_VARIANT_ASYM) {
           a = valid ? kf : 0.0f;
           bb = bscal * bf(br, e);
@@ -1477,6 +1467,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_staged_kernel(Problem p, 
           a = kscal * kf;
           bb = bscal * a;
         }
+        if constexpr (V != GDN_VARIANT_FG2) xv[e] = (_Float16)(bf(vr, e) * wrow);
         const float fup = __builtin_amdgcn_exp2f(G[8 * u + e] - cof[e]);  // e^{G - G_mid}
         const float eam = __builtin_amdgcn_rcpf(fup);                     // e^{G_mid - G}
         const float eg = cp[e] * fup;                                     // e^{G}
@@ -1514,18 +1505,16 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_staged_kernel(Problem p, 
           pa.h[e] = (_Float16)ta[e];
         }
         *reinterpret_cast<uint2*>(&sm.bt[c][16 * wave + 4 * lg]) = pb.u[0];
+        const float4v tv = mma_pair_f16(xv, sel[hh], zero);
+        H8 pv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pv.h[e] = (_Float16)tv[e];
+        *reinterpret_cast<uint2*>(&sm.wvt[c][16 * wave + 4 * lg]) = pv.u[0];
         *reinterpret_cast<uint2*>(AT_g + size_t((((c >> 4) * CK + (wave >> 1)) * 64 + li + 16 * (2 * (wave & 1) + (lg >> 1))) * 8 +
                                                 4 * (lg & 1))) = pa.u[0];
       }
     }
-    lds_reads_done();
-    if (has_next) {  // every staged row of this item is read: stage the rest of the next one
-      stage(nx, kg, R_K);
-      if (want_out) stage(nx, qg, R_Q);
-      if constexpr (V == GDN_VARIANT_FG2) stage(nx, beg, R_B);
-      if constexpr (V == GDN_VARIANT_ASYM) stage(nx, jg, R_B);
-      scal = load_scal(nx);
-    }
+
     wg_barrier();
 
     // ---- Gram tiles: M^T(J, I) = A-(J) B+(I)^T and P^T(J, I) = A-(J) Q+(I)^T, every J
@@ -1632,6 +1621,10 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_staged_kernel(Problem p, 
     }
     wg_barrier();
 
+    if (has_next) {  // the next item's inputs load while W and U~ are computed
+      load_raw(nx, raw);
+      scal = load_scal(nx);
+    }
     // ---- W^T = B+^T T^T (stored as W rows) and U~ = T Wv (stored transposed): wave w
     // computes the tiles of step rows 16 w .., independent chains interleaved ----
     H8 ta[2];  // T rows 16 w + li, steps 32 u + 4 lg .. (+16)
@@ -1689,9 +1682,9 @@ int launch_prep_t(const Problem& p, void* ws, bool want_out, hipStream_t s) {
   const ChunkLayout L = chunk_layout(p);
   const int64_t items = p.nchunks * p.B * p.H;
   if constexpr (std::is_same<In, uint16_t>::value && DK == 128 && C == 64 && !DPV) {
-    if (staged_prep_covers(p)) {  // one workgroup per CU (about 150 KB of LDS)
-      const int64_t grid = std::min<int64_t>(items, int64_t(device_cus()));
-      chunk_prep_staged_kernel<V><<<dim3(unsigned(grid)), kThreads, 0, s>>>(p, static_cast<unsigned char*>(ws), L,
+    if (prep2_covers(p)) {  // two workgroups per CU
+      const int64_t grid = std::min<int64_t>(items, 2 * int64_t(device_cus()));
+      chunk_prep2_kernel<V><<<dim3(unsigned(grid)), kThreads, 0, s>>>(p, static_cast<unsigned char*>(ws), L,
                                                                              want_out ? 1 : 0);
       return int(hipGetLastError());
     }

@@ -12,6 +12,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bhalf8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
 
 // ---- element conversion ------------------------------------------------------
 

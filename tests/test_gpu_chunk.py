@@ -102,7 +102,7 @@ CASES = [
     ("gdn", "bf16", 2, 150, 2, 128, 16, 1, 64),
     ("deltaproduct", "bf16", 1, 100, 2, 128, 64, 4, 64),
     ("asym", "bf16", 1, 190, 3, 128, 64, 1, 64),
-    # bf16, dk = dv = 128, chunk 64, one step per token: LDS-staged prepare kernel
+    # bf16, dk = dv = 128, chunk 64, one step per token: two-workgroup prepare kernel
     ("kda", "bf16", 2, 170, 2, 128, 128, 1, 64),
     ("deltaproduct", "bf16", 1, 200, 2, 128, 128, 1, 64),
 ]
