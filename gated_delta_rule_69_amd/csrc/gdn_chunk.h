@@ -1257,17 +1257,21 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
   struct Raw {
     uint4 k[4], a[4], b[4], q[4], v[4];
   };
-  auto load_raw = [&](const Item& it, Raw& x) __attribute__((always_inline)) {
+  // parts: 1 key, 2 values, 4 query, 8 decay, 16 beta / j
+  auto load_raw = [&](const Item& it, Raw& x, int parts) __attribute__((always_inline)) {
     const int64_t off = th_of(it, r) * DK + 8 * lg;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       auto ld16 = [&](const In* base) { return *reinterpret_cast<const uint4*>(base + off + 32 * u); };
-      x.k[u] = ld16(kg);
-      x.v[u] = ld16(vg);
-      if (want_out) x.q[u] = ld16(qg);
-      if constexpr (CH_ALPHA) x.a[u] = ld16(alg);
-      if constexpr (V == GDN_VARIANT_FG2) x.b[u] = ld16(beg);
-      if constexpr (V == GDN_VARIANT_ASYM) x.b[u] = ld16(jg);
+      if (parts & 1) x.k[u] = ld16(kg);
+      if (parts & 2) x.v[u] = ld16(vg);
+      if ((parts & 4) && want_out) x.q[u] = ld16(qg);
+      if constexpr (CH_ALPHA)
+        if (parts & 8) x.a[u] = ld16(alg);
+      if constexpr (V == GDN_VARIANT_FG2)
+        if (parts & 16) x.b[u] = ld16(beg);
+      if constexpr (V == GDN_VARIANT_ASYM)
+        if (parts & 16) x.b[u] = ld16(jg);
     }
   };
   auto bf = [](const uint4& v, int s) __attribute__((always_inline)) -> float {
@@ -1314,7 +1318,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
   Raw raw;
   if (int(blockIdx.x) < total) {
     const Item it = item_of(blockIdx.x);
-    load_raw(it, raw);
+    load_raw(it, raw, 31);
     scal = load_scal(it);
   }
 
@@ -1515,6 +1519,11 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
       }
     }
 
+    // The next item's inputs load in three groups, each once this item's copy is
+    // consumed, so that the loads of the two workgroups on a CU do not arrive in
+    // one burst: key and values here, query and beta / j after the Grams, the decay
+    // before W and U~.
+    if (has_next) load_raw(nx, raw, 1 | 2);
     wg_barrier();
 
     // ---- Gram tiles: M^T(J, I) = A-(J) B+(I)^T and P^T(J, I) = A-(J) Q+(I)^T, every J
@@ -1554,6 +1563,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
         *reinterpret_cast<uint2*>(P_g + p_frag(r, J)) = h8.u[0];
       }
     }
+    if (has_next) load_raw(nx, raw, 4 | 16);
     wg_barrier();  // A- is dead: its space now holds M and T
 #pragma unroll
     for (int J = 0; J < NT; ++J) {
@@ -1621,8 +1631,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
     }
     wg_barrier();
 
-    if (has_next) {  // the next item's inputs load while W and U~ are computed
-      load_raw(nx, raw);
+    if (has_next) {
+      load_raw(nx, raw, 8);
       scal = load_scal(nx);
     }
     // ---- W^T = B+^T T^T (stored as W rows) and U~ = T Wv (stored transposed): wave w
