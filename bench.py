@@ -225,9 +225,9 @@ def main():
     # HIP events above); `roofline` reports the longer of the two kernels
     prep_bytes = prep_bytes_per_th(d) * units
     prep_gbs = prep_bytes / (prep_ms * 1e-3) / 1e9
-    prep_roof = dict(kernel="chunk_prep_kernel", bound="hbm", achieved=prep_gbs, peak=HBM_PEAK_GBS,
+    prep_roof = dict(kernel="chunk_prep2_kernel", bound="hbm", achieved=prep_gbs, peak=HBM_PEAK_GBS,
                      unit="GB/s", frac=prep_gbs / HBM_PEAK_GBS, algorithmic=prep_bytes,
-                     ms=prep_ms, traffic=read_traffic("chunk_prep_kernel"))
+                     ms=prep_ms, traffic=read_traffic("chunk_prep2_kernel"))
     scan_flops = scan_flops_per_th(d, C) * units
     scan_tf = scan_flops / (scan_ms * 1e-3) / 1e12
     scan_roof = dict(kernel="chunk_scan_rows_kernel", bound="mfma", achieved=scan_tf,

@@ -331,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(Problem p, const u
 // scale per column; a fragment is brought to the column's common (smallest) scale
 // by an exact power-of-two product before its MFMA. Two barriers per chunk.
 // chunks of look-ahead of the scan's L2 prefetch wave
-constexpr int kAhead = 4;
+constexpr int kAhead = 2;
 
 template <int NCT>
 __global__ __launch_bounds__(kThreads + 64) void chunk_scan_rows_kernel(Problem p, const unsigned char* __restrict__ ws,
@@ -646,15 +646,9 @@ int launch_scan_t(const Problem& p, void* ws, bool want_out, hipStream_t s) {
     // fragment-format records: row-split scan, 16 value columns per workgroup
     // (one workgroup per 16 columns keeps the step latency short: the scan is a
     // chain of dependent MFMA / LDS / barrier phases, 512 steps long at 32K)
-    const unsigned nb = 16;
-    const dim3 g(unsigned(p.B * p.H) * unsigned(p.dv / nb));
-    const unsigned char* w = static_cast<const unsigned char*>(ws);
-    const int wo = want_out ? 1 : 0;
-    switch (nb) {
-      case 16: chunk_scan_rows_kernel<1><<<g, kThreads + 64, 0, s>>>(p, w, L, wo); break;
-      case 32: chunk_scan_rows_kernel<2><<<g, kThreads + 64, 0, s>>>(p, w, L, wo); break;
-      default: chunk_scan_rows_kernel<4><<<g, kThreads + 64, 0, s>>>(p, w, L, wo); break;
-    }
+    const dim3 g(unsigned(p.B * p.H) * unsigned(p.dv / 16));
+    chunk_scan_rows_kernel<1><<<g, kThreads + 64, 0, s>>>(p, static_cast<const unsigned char*>(ws), L,
+                                                         want_out ? 1 : 0);
     return int(hipGetLastError());
   } else {
     const unsigned cblocks = unsigned((p.dv + 63) / 64);
