@@ -12,6 +12,7 @@ whole path's HBM roofline, a parity check of sampled heads against the float64
 oracle, and the oracle's own throughput on the host cores (a reported baseline).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+    python bench.py --sweep     # the pages' prefill sweep (fixed 32,768 tokens), FG2 and KDA
 """
 from __future__ import annotations
 
@@ -151,6 +152,69 @@ def profile_driver(args):
     log(f"profile driver: {args.steps} steps and a 1 GiB copy done")
 
 
+# ---- the pages' prefill timing protocol: a fixed 32,768 tokens per step, sequence
+# length x batch from 2K x 16 to 32K x 1, H = 16, d = 128, FG2 and KDA inputs ------
+SWEEP = [(2048, 16), (4096, 8), (8192, 4), (16384, 2), (32768, 1)]
+
+
+def sweep(args):
+    """Tokens/s of one gdn_chunk_fwd step (prepare + scan, final states returned) at
+    each (T, B) of the sweep, for FG2 and KDA inputs. Each variant's inputs are drawn
+    once as one 32,768-token sequence per head and cut into B sequences of T tokens.
+    Parity: the first 1024 tokens of sequence 0, head 0 against the float64 oracle."""
+    import torch
+    import gated_delta_rule_69_amd as gdn
+    import oracle
+    dev = torch.device("cuda:0")
+    H, d, C, total = 16, 128, 64, 32768
+    rows = []
+    for variant in ("fg2", "kda"):
+        log(f"sweep: generating {variant} inputs (32,768 tokens x {H} heads)")
+        inp = gdn_inputs.make_inputs(variant, 1, total, H, d, d, dtype="bf16", seed=20)
+        for T, B in SWEEP:
+            cut = {k: (inp[k].reshape((B, T) + inp[k].shape[2:]) if isinstance(inp[k], np.ndarray) else inp[k])
+                   for k in inp}
+            cut["B"], cut["T"] = B, T
+            tens = {k: torch.from_numpy(np.ascontiguousarray(cut[k])).to(dev).to(torch.bfloat16)
+                    for k in ("q", "k", "v", "alpha", "beta")}
+            o = torch.empty((B, T, H, d), dtype=torch.bfloat16, device=dev)
+            s_final = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+            a = gdn.make_args(variant, tens["q"], tens["k"], tens["v"], tens["alpha"], tens["beta"],
+                              chunk=C, s_final=s_final, o=o)
+            ws = torch.empty(gdn.gdn_workspace_bytes(a), dtype=torch.uint8, device=dev)
+            for _ in range(args.warmup):
+                gdn.gdn_chunk_fwd_args(a, ws)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                gdn.gdn_chunk_fwd_args(a, ws)
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t0) * 1e3 / args.steps
+            Tp = min(T, 1024)
+            sub = {k: (v[0:1, :Tp, 0:1] if isinstance(v, np.ndarray) else v) for k, v in cut.items()}
+            sub["B"], sub["H"], sub["T"] = 1, 1, Tp
+            o_ref, _ = oracle.forward(sub)
+            got = o[0, :Tp, 0].float().cpu().numpy()
+            err = float(np.linalg.norm(got - o_ref[0, :, 0]) / np.linalg.norm(o_ref[0, :, 0]))
+            rows.append(dict(variant=variant, T=T, B=B, ms=ms, tokens_per_s=B * T / (ms * 1e-3),
+                             o_rel_l2_sample=err))
+            log(f"sweep: {variant} T={T} B={B}: {ms:.3f} ms, {B * T / (ms * 1e-3):.3e} tokens/s, "
+                f"parity rel-L2 {err:.2e}")
+            del tens, o, s_final, ws, a
+            torch.cuda.empty_cache()
+    tok = {(r["variant"], r["T"]): r["tokens_per_s"] for r in rows}
+    out = {
+        "metric": "prefill tokens/s at a fixed 32,768 tokens per step (H=16, d=128, chunk 64, bf16)",
+        "unit": "tokens/s",
+        "rows": rows,
+        "long_over_short": {v: tok[(v, 32768)] / tok[(v, 2048)] for v in ("fg2", "kda")},
+        "fg2_over_kda_time": {str(T): tok[("kda", T)] / tok[("fg2", T)] for T, _ in SWEEP},
+        "data": "synthetic",
+        "n_gpus": 1,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -160,6 +224,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=16384)
     ap.add_argument("--profile-driver", action="store_true",
                     help="only run the workload for rocprofv3 counter collection")
+    ap.add_argument("--sweep", action="store_true",
+                    help="the prefill sweep at a fixed 32,768 tokens (2K x 16 .. 32K x 1), FG2 and KDA")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -169,6 +235,9 @@ def main():
 
     if args.profile_driver:
         profile_driver(args)
+        return
+    if args.sweep:
+        sweep(args)
         return
 
     W = WORKLOAD
