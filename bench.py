@@ -13,6 +13,7 @@ oracle, and the oracle's own throughput on the host cores (a reported baseline).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
     python bench.py --sweep     # the pages' prefill sweep (fixed 32,768 tokens), FG2 and KDA
+    python bench.py --decode    # one-token decode step over 512 sequences (state in HBM)
 """
 from __future__ import annotations
 
@@ -215,6 +216,82 @@ def sweep(args):
     print(json.dumps(out), flush=True)
 
 
+def copy_bandwidth_gbs():
+    """Measured device-to-device copy bandwidth (1 GiB, read + write counted), GB/s:
+    what a plain streaming kernel reaches on this GPU, beside the 8 TB/s spec."""
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(5):
+        dst.copy_(src)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / 5
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * (1 << 30) / (ms * 1e-3) / 1e9
+
+
+# ---- decode: one token per sequence through gdn_recurrent_step --------------------
+def decode(args):
+    """Time of one gdn_recurrent_step call with T = 1 over B = 512 sequences, H = 16,
+    dk = dv = 128 (FG2, bf16 inputs, fp32 state resident in HBM: 512 MB, twice the
+    Infinity Cache). The step reads and writes the whole state once: its roofline is
+    HBM traffic of 2 * 4 * dk * dv bytes per (sequence, head) plus the token's inputs.
+    Parity: sequence 0, head 0 (output and updated state) against the float64 oracle."""
+    import torch
+    import gated_delta_rule_69_amd as gdn
+    import oracle
+    dev = torch.device("cuda:0")
+    B, H, d = 512, 16, 128
+    inp = gdn_inputs.make_inputs("fg2", B, 1, H, d, d, dtype="bf16", seed=30)
+    s0 = gdn_inputs.make_state(B, H, d, d, seed=30)
+    tens = {k: torch.from_numpy(inp[k]).to(dev).to(torch.bfloat16).contiguous()
+            for k in ("q", "k", "v", "alpha", "beta")}
+    state = torch.from_numpy(s0).to(dev)
+    o = torch.empty((B, 1, H, d), dtype=torch.bfloat16, device=dev)
+    # parity on a fresh copy of the state (the timed calls update it in place)
+    gdn.gdn_recurrent_step("fg2", tens["q"], tens["k"], tens["v"], tens["alpha"], tens["beta"],
+                           state=state, o=o)
+    torch.cuda.synchronize()
+    sub = {k: (v[0:1, :, 0:1] if isinstance(v, np.ndarray) else v) for k, v in inp.items()}
+    sub["B"], sub["H"] = 1, 1
+    o_ref, s_ref = oracle.forward(sub, s0[0:1, 0:1])
+    o_err = float(np.linalg.norm(o[0, 0, 0].float().cpu().numpy() - o_ref[0, 0, 0]) /
+                  np.linalg.norm(o_ref[0, 0, 0]))
+    s_err = float(np.linalg.norm(state[0, 0].cpu().numpy() - s_ref[0, 0]) / np.linalg.norm(s_ref[0, 0]))
+    for _ in range(args.warmup):
+        gdn.gdn_recurrent_step("fg2", tens["q"], tens["k"], tens["v"], tens["alpha"], tens["beta"],
+                               state=state, o=o)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(args.steps):
+        gdn.gdn_recurrent_step("fg2", tens["q"], tens["k"], tens["v"], tens["alpha"], tens["beta"],
+                               state=state, o=o)
+    ev[1].record()
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / args.steps
+    state_bytes = 2 * 4 * d * d * B * H
+    io_bytes = B * H * (5 * d + d) * 2
+    gbs = (state_bytes + io_bytes) / (us * 1e-6) / 1e9
+    copy_gbs = copy_bandwidth_gbs()
+    log(f"decode: {us:.1f} us per step, {gbs:.0f} GB/s (device copy {copy_gbs:.0f} GB/s), "
+        f"parity o {o_err:.2e} S {s_err:.2e}")
+    print(json.dumps({
+        "metric": "decode step: gdn_recurrent_step, one token for 512 sequences (H=16, d=128)",
+        "us_per_step": us, "tokens_per_s": B / (us * 1e-6),
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "algorithmic": state_bytes + io_bytes,
+                     "device_copy_gbs": copy_gbs},
+        "parity": {"o_rel_l2": o_err, "S_rel_l2": s_err},
+        "data": "synthetic", "n_gpus": 1}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -224,6 +301,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=16384)
     ap.add_argument("--profile-driver", action="store_true",
                     help="only run the workload for rocprofv3 counter collection")
+    ap.add_argument("--decode", action="store_true",
+                    help="one-token decode step (gdn_recurrent_step) over 512 sequences")
     ap.add_argument("--sweep", action="store_true",
                     help="the prefill sweep at a fixed 32,768 tokens (2K x 16 .. 32K x 1), FG2 and KDA")
     args = ap.parse_args()
@@ -238,6 +317,9 @@ def main():
         return
     if args.sweep:
         sweep(args)
+        return
+    if args.decode:
+        decode(args)
         return
 
     W = WORKLOAD
@@ -308,7 +390,7 @@ def main():
     path_gbs = path_bytes / (ms_step * 1e-3) / 1e9
     path = dict(bound="hbm", achieved=path_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=path_gbs / HBM_PEAK_GBS, algorithmic=path_bytes,
-                prepare_ms=prep_ms, scan_ms=scan_ms)
+                prepare_ms=prep_ms, scan_ms=scan_ms, device_copy_gbs=copy_bandwidth_gbs())
 
     parity = None
     if cpu_res:
