@@ -14,6 +14,7 @@ oracle, and the oracle's own throughput on the host cores (a reported baseline).
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
     python bench.py --sweep     # the pages' prefill sweep (fixed 32,768 tokens), FG2 and KDA
     python bench.py --decode    # one-token decode step over 512 sequences (state in HBM)
+    python bench.py --configs   # workloads 0, 1, 3, 4: time per call, both roofline fractions
 """
 from __future__ import annotations
 
@@ -236,6 +237,86 @@ def copy_bandwidth_gbs():
     return 2 * (1 << 30) / (ms * 1e-3) / 1e9
 
 
+# ---- the other workloads: time per gdn_chunk_fwd call and both roofline fractions --
+def alg_per_th(cfg):
+    """Algorithmic bytes and flops per token-head of a workload (inputs + output,
+    never the workspace; the chunkwise method's triangular work)."""
+    es = 2 if cfg["dtype"] == "bf16" else 4
+    d, C, n_h, var = cfg["dk"], cfg["chunk"], cfg["n_h"], cfg["variant"]
+    if var == "deltaproduct":
+        nbytes = (d + n_h * 2 * d + n_h + 1 + d) * es          # q, k_j, v_j, beta_j, gate, o
+        flops = n_h * (4 * d * d + 3 * C * d) + 2 * d * d + 2 * C * d
+    else:
+        per_row = {"fg2": 5 * d, "kda": 4 * d + 1, "gdn": 3 * d + 2, "asym": 5 * d + 1}[var]
+        nbytes = (per_row + d) * es
+        flops = 6 * d * d + 5 * C * d
+    return nbytes, flops
+
+
+def configs(args):
+    """Workloads 0, 1, 3 and 4 (the parity configurations): median time of one
+    gdn_chunk_fwd call over 20 calls (HIP events around each, 5 warm-ups, a 512 MB
+    buffer written between calls so that no input stays in the 256 MB Infinity
+    Cache), both roofline fractions, and o / S_T of sequence 0, head 0 against the
+    float64 oracle."""
+    import torch
+    import gated_delta_rule_69_amd as gdn
+    import oracle
+    dev = torch.device("cuda:0")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    rows = []
+    for idx in (0, 1, 3, 4):
+        cfg = gdn_inputs.CONFIGS[idx]
+        inp = gdn_inputs.config_inputs(idx)
+        io = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
+        names = [n for n in ("q", "k", "v", "alpha", "beta", "j", "eta") if n in inp]
+        t = {n: torch.from_numpy(inp[n]).to(dev).to(io).contiguous() for n in names}
+        B, T, H, dk, dv = cfg["B"], cfg["T"], cfg["H"], cfg["dk"], cfg["dv"]
+        o = torch.empty((B, T, H, dv), dtype=io, device=dev)
+        s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        a = gdn.make_args(cfg["variant"], t["q"], t["k"], t["v"], t["alpha"], t.get("beta"),
+                          chunk=cfg["chunk"], j=t.get("j"), eta=t.get("eta"), s_final=s_final, o=o)
+        ws = torch.empty(gdn.gdn_workspace_bytes(a), dtype=torch.uint8, device=dev)
+        for _ in range(5):
+            gdn.gdn_chunk_fwd_args(a, ws)
+        times = []
+        for _ in range(20):
+            flush.fill_(1)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record()
+            gdn.gdn_chunk_fwd_args(a, ws)
+            ev[1].record()
+            torch.cuda.synchronize()
+            times.append(ev[0].elapsed_time(ev[1]) * 1e3)
+        us = float(np.median(times))
+        sub = {k: (v[0:1, :, 0:1] if isinstance(v, np.ndarray) else v) for k, v in inp.items()}
+        sub["B"], sub["H"] = 1, 1
+        o_ref, s_ref = oracle.forward(sub)
+        o_err = float(np.linalg.norm(o[0, :, 0].float().cpu().numpy() - o_ref[0, :, 0]) /
+                      np.linalg.norm(o_ref[0, :, 0]))
+        s_err = float(np.linalg.norm(s_final[0, 0].cpu().numpy() - s_ref[0, 0]) / np.linalg.norm(s_ref[0, 0]))
+        nb, nf = alg_per_th(cfg)
+        units = B * T * H
+        nbytes = nb * units + B * H * dk * dv * 4
+        peak_tf = MFMA_PEAK_TFLOPS if cfg["dtype"] == "bf16" else 157.3
+        gbs = nbytes / (us * 1e-6) / 1e9
+        tfs = nf * units / (us * 1e-6) / 1e12
+        rows.append(dict(workload=cfg["name"], index=idx, variant=cfg["variant"], dtype=cfg["dtype"],
+                         B=B, T=T, H=H, dk=dk, dv=dv, chunk=cfg["chunk"], n_h=cfg["n_h"], us=us,
+                         tokens_per_s=B * T / (us * 1e-6),
+                         hbm=dict(achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=gbs / HBM_PEAK_GBS,
+                                  algorithmic=nbytes),
+                         mfma=dict(achieved=tfs, peak=peak_tf, unit="TFLOP/s", frac=tfs / peak_tf,
+                                   algorithmic=nf * units),
+                         parity=dict(o_rel_l2=o_err, S_rel_l2=s_err)))
+        log(f"configs: {cfg['name']}: {us:.1f} us, HBM {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%}), "
+            f"MFMA {tfs:.1f} TFLOP/s ({tfs / peak_tf:.1%}), parity o {o_err:.2e} S {s_err:.2e}")
+        del t, o, s_final, ws, a
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "time per gdn_chunk_fwd call and roofline fractions, workloads 0, 1, 3, 4",
+                      "rows": rows, "data": "synthetic", "n_gpus": 1}), flush=True)
+
+
 # ---- decode: one token per sequence through gdn_recurrent_step --------------------
 def decode(args):
     """Time of one gdn_recurrent_step call with T = 1 over B = 512 sequences, H = 16,
@@ -301,6 +382,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=16384)
     ap.add_argument("--profile-driver", action="store_true",
                     help="only run the workload for rocprofv3 counter collection")
+    ap.add_argument("--configs", action="store_true",
+                    help="workloads 0, 1, 3, 4: time per call, roofline fractions, parity")
     ap.add_argument("--decode", action="store_true",
                     help="one-token decode step (gdn_recurrent_step) over 512 sequences")
     ap.add_argument("--sweep", action="store_true",
@@ -320,6 +403,9 @@ def main():
         return
     if args.decode:
         decode(args)
+        return
+    if args.configs:
+        configs(args)
         return
 
     W = WORKLOAD
