@@ -12,6 +12,7 @@ Modules
   dense       explicit transition matrices and the closed forms the pages give
               (spectral norm of I - eta j k^T, the RWKV-7 secular equation),
               used only to pin ``recurrence``
+  stabilize   the GDN2 stabilisers (decay clip, j projection), token-wise
   metrics     rel-L2 and normwise max-rel error
 
 Parity status: every function in ``recurrence`` is pinned by tests that do not
@@ -20,3 +21,4 @@ pages' models, closed forms, hand-derivable cases); see tests/test_oracle_*.py.
 """
 from .recurrence import (deltanet, gdn, kda, fg2, deltaproduct, gdn2, forward)  # noqa: F401
 from .metrics import rel_l2, max_rel  # noqa: F401
+from . import stabilize  # noqa: F401
