@@ -373,6 +373,69 @@ def decode(args):
         "data": "synthetic", "n_gpus": 1}), flush=True)
 
 
+# ---- GDN2 stabilisers: gdn_asym_stabilize on the asymmetric workload ---------------
+def stabilize(args):
+    """Both stabiliser modes on workload 4 (ASYM, fp32, B=8, H=32, T=2048, dk=64):
+    median time of one gdn_asym_stabilize call over 20 calls (512 MB written between
+    calls so that nothing stays in the Infinity Cache), HBM fraction with
+    (4 dk + 1) elements per token-head (k, j, D and eta in, dk out), the cost beside
+    one gdn_chunk_fwd call of the same workload, and the first 4096 token-heads
+    against the float64 oracle."""
+    import torch
+    import gated_delta_rule_69_amd as gdn
+    import oracle
+    dev = torch.device("cuda:0")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cfg = gdn_inputs.CONFIGS[4]
+    inp = gdn_inputs.config_inputs(4)
+    t = {n: torch.from_numpy(inp[n]).to(dev).contiguous() for n in ("q", "k", "v", "alpha", "j", "eta")}
+    B, T, H, dk, dv = cfg["B"], cfg["T"], cfg["H"], cfg["dk"], cfg["dv"]
+    out = torch.empty_like(t["k"])
+
+    def timed(fn):
+        for _ in range(5):
+            fn()
+        times = []
+        for _ in range(20):
+            flush.fill_(1)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record()
+            fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            times.append(ev[0].elapsed_time(ev[1]) * 1e3)
+        return float(np.median(times))
+
+    o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    a = gdn.make_args("asym", t["q"], t["k"], t["v"], t["alpha"], None, chunk=cfg["chunk"],
+                      j=t["j"], eta=t["eta"], s_final=s_final, o=o)
+    ws = torch.empty(gdn.gdn_workspace_bytes(a), dtype=torch.uint8, device=dev)
+    fwd_us = timed(lambda: gdn.gdn_chunk_fwd_args(a, ws))
+    units = B * T * H
+    nbytes = (4 * dk + 1) * 4 * units
+    n = 4096
+    sub = {x: inp[x].reshape(units, -1)[:n].astype(np.float64) for x in ("k", "j", "alpha")}
+    eta = inp["eta"].reshape(units)[:n].astype(np.float64)
+    rows = []
+    for mode in ("clip_decay", "project_j"):
+        us = timed(lambda: gdn.gdn_asym_stabilize(mode, t["k"], t["j"], t["alpha"], t["eta"], out=out))
+        fn = oracle.stabilize.clip_decay if mode == "clip_decay" else oracle.stabilize.project_j
+        ref = fn(sub["k"], sub["j"], eta, sub["alpha"])
+        got = out.reshape(units, dk)[:n].cpu().numpy().astype(np.float64)
+        err = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+        gbs = nbytes / (us * 1e-6) / 1e9
+        rows.append(dict(mode=mode, us=us, vs_chunk_fwd=us / fwd_us,
+                         hbm=dict(achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s",
+                                  frac=gbs / HBM_PEAK_GBS, algorithmic=nbytes),
+                         parity=dict(rel_l2=err, rows=n)))
+        log(f"stabilize {mode}: {us:.1f} us, {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%}), "
+            f"{us / fwd_us:.1%} of gdn_chunk_fwd ({fwd_us:.1f} us), parity {err:.2e}")
+    print(json.dumps({"metric": "time per gdn_asym_stabilize call, workload 4 (B=8, H=32, T=2048, dk=64, fp32)",
+                      "rows": rows, "chunk_fwd_us": fwd_us, "device_copy_gbs": copy_bandwidth_gbs(),
+                      "data": "synthetic", "n_gpus": 1}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -386,6 +449,8 @@ def main():
                     help="workloads 0, 1, 3, 4: time per call, roofline fractions, parity")
     ap.add_argument("--decode", action="store_true",
                     help="one-token decode step (gdn_recurrent_step) over 512 sequences")
+    ap.add_argument("--stabilize", action="store_true",
+                    help="GDN2 stabilisers (gdn_asym_stabilize) on the asymmetric workload")
     ap.add_argument("--sweep", action="store_true",
                     help="the prefill sweep at a fixed 32,768 tokens (2K x 16 .. 32K x 1), FG2 and KDA")
     args = ap.parse_args()
@@ -403,6 +468,9 @@ def main():
         return
     if args.decode:
         decode(args)
+        return
+    if args.stabilize:
+        stabilize(args)
         return
     if args.configs:
         configs(args)

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(PKG, "libgdn.so")
 
 VARIANTS = {"fg2": 0, "kda": 1, "gdn": 2, "deltaproduct": 3, "asym": 4}
 DTYPE_F32, DTYPE_BF16 = 0, 1
+STABILIZE_MODES = {"clip_decay": 1, "project_j": 2}
 STATUS = {0: "GDN_OK", -1: "GDN_ERR_ARG", -2: "GDN_ERR_UNSUPPORTED", -3: "GDN_ERR_WORKSPACE",
           -4: "GDN_ERR_HIP"}
 
@@ -62,6 +63,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             fn.restype = ctypes.c_int
         lib.gdn_recurrent_step.argtypes = [P, ctypes.c_void_p, ctypes.c_void_p]
         lib.gdn_recurrent_step.restype = ctypes.c_int
+        lib.gdn_asym_stabilize.argtypes = [P, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        lib.gdn_asym_stabilize.restype = ctypes.c_int
         lib.gdn_status_str.argtypes = [ctypes.c_int]
         lib.gdn_status_str.restype = ctypes.c_char_p
         lib.gdn_abi_version.argtypes = []
@@ -236,3 +239,36 @@ def gdn_chunk_scan(args: GdnArgs, workspace, stream=None):
 def gdn_chunk_fwd_args(args: GdnArgs, workspace, stream=None):
     """gdn_chunk_fwd on prebuilt args (no per-call marshalling)."""
     _staged("gdn_chunk_fwd", args, workspace, stream)
+
+
+def gdn_asym_stabilize(mode, k, j, alpha, eta, *, out=None, stream=None):
+    """GDN2 stabiliser on ASYM inputs (k, j, alpha = D of shape [B, T, H, dk], eta of
+    shape [B, T, H]). mode "clip_decay" returns D' = min(D, 1/rho); mode "project_j"
+    returns the projected j'. out may be alpha (clip_decay) or j (project_j) to update
+    in place; it is allocated when not given."""
+    import torch
+    if mode not in STABILIZE_MODES:
+        raise ValueError(f"unknown stabilizer mode {mode!r}")
+    if k.dim() != 4 or j.shape != k.shape or alpha.shape != k.shape or eta.shape != k.shape[:3]:
+        raise ValueError("k, j, alpha must be [B, T, H, dk] and eta [B, T, H]")
+    dev, io = k.device, k.dtype
+    if io not in (torch.float32, torch.bfloat16):
+        raise ValueError("inputs must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty_like(k)
+    for name, t in (("k", k), ("j", j), ("alpha", alpha), ("eta", eta), ("out", out)):
+        _check(t, name, dev, io)
+    if out.shape != k.shape:
+        raise ValueError("out must have the shape of k")
+    a = GdnArgs()
+    a.variant = VARIANTS["asym"]
+    a.dtype = DTYPE_BF16 if io == torch.bfloat16 else DTYPE_F32
+    a.B, a.T, a.H = k.shape[0], k.shape[1], k.shape[2]
+    a.dk = a.dv = k.shape[-1]
+    a.chunk, a.n_h = 64, 1
+    a.k, a.j, a.alpha, a.eta = _ptr(k), _ptr(j), _ptr(alpha), _ptr(eta)
+    st = load_library().gdn_asym_stabilize(ctypes.byref(a), STABILIZE_MODES[mode],
+                                           ctypes.c_void_p(out.data_ptr()), _stream(stream))
+    if st != 0:
+        raise GdnError(st, "gdn_asym_stabilize")
+    return out

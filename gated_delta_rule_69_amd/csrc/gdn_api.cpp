@@ -32,7 +32,8 @@ int validate(const gdn_args* a, Entry e, Problem* out) {
   } else if (a->n_h != 1) {
     return GDN_ERR_ARG;
   }
-  if (e != Entry::Recurrent) {
+  const bool chunked = e != Entry::Recurrent && e != Entry::Stabilize;
+  if (chunked) {
     if (a->chunk != 16 && a->chunk != 32 && a->chunk != 64) return GDN_ERR_UNSUPPORTED;
     if (a->chunk % a->n_h != 0) return GDN_ERR_UNSUPPORTED;
     if (a->chunk / a->n_h < 16) return GDN_ERR_UNSUPPORTED;  // one 16-row output tile at least
@@ -43,7 +44,12 @@ int validate(const gdn_args* a, Entry e, Problem* out) {
     return GDN_ERR_ARG;  // one beta vector scales both key and value channels
   if (a->variant != GDN_VARIANT_FG2 && a->beta_v != nullptr) return GDN_ERR_ARG;
 
-  if (e != Entry::Shapes) {
+  if (e == Entry::Stabilize) {
+    // Only k, j, alpha (= D) and eta are read; with T == 0 they may be NULL.
+    if (a->variant != GDN_VARIANT_ASYM) return GDN_ERR_ARG;
+    auto need = [&](const void* p) { return a->T == 0 ? opt_ptr_ok(p) : ptr_ok(p); };
+    if (!need(a->k) || !need(a->j) || !need(a->alpha) || !need(a->eta)) return GDN_ERR_ARG;
+  } else if (e != Entry::Shapes) {
     // With T == 0 the per-token arrays are empty and may be NULL.
     auto need = [&](const void* p) { return a->T == 0 ? opt_ptr_ok(p) : ptr_ok(p); };
     if (!need(a->k) || !need(a->v) || !need(a->alpha)) return GDN_ERR_ARG;
@@ -64,7 +70,7 @@ int validate(const gdn_args* a, Entry e, Problem* out) {
     if (!opt_ptr_ok(a->s0) || !opt_ptr_ok(a->s_final)) return GDN_ERR_ARG;
   }
 
-  if (e != Entry::Recurrent) {
+  if (chunked) {
     const int64_t nchunks = (a->T * a->n_h + a->chunk - 1) / a->chunk;
     if (nchunks * a->B * a->H >= (int64_t(1) << 31)) return GDN_ERR_UNSUPPORTED;  // grid size
   }
@@ -92,7 +98,7 @@ int validate(const gdn_args* a, Entry e, Problem* out) {
     p.s_final = a->s_final;
     p.o = a->o;
     p.steps = a->T * a->n_h;
-    if (e != Entry::Recurrent) {
+    if (chunked) {
       p.nchunks = (p.steps + a->chunk - 1) / a->chunk;
       p.rows_out = a->chunk / a->n_h;
     } else {
@@ -175,6 +181,16 @@ int gdn_recurrent_step(const gdn_args* args, float* state_inout, void* stream) {
     return GDN_ERR_ARG;
   if (p.T == 0) return GDN_OK;
   return gdn::launch_recurrent(p, state_inout, stream) == 0 ? GDN_OK : GDN_ERR_HIP;
+}
+
+int gdn_asym_stabilize(const gdn_args* args, int mode, void* out, void* stream) {
+  Problem p;
+  int st = gdn::validate(args, Entry::Stabilize, &p);
+  if (st != GDN_OK) return st;
+  if (mode != GDN_STABILIZE_CLIP_DECAY && mode != GDN_STABILIZE_PROJECT_J) return GDN_ERR_ARG;
+  if (p.T == 0) return GDN_OK;
+  if (out == nullptr || (reinterpret_cast<uintptr_t>(out) & 15u) != 0) return GDN_ERR_ARG;
+  return gdn::launch_stabilize(p, mode, out, stream) == 0 ? GDN_OK : GDN_ERR_HIP;
 }
 
 const char* gdn_status_str(int status) {

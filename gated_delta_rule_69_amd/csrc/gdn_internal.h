@@ -33,7 +33,7 @@ struct Problem {
 };
 
 // Shapes: the chunked shape checks only (no pointer checks), for workspace sizing.
-enum class Entry { ChunkFwd, FinalState, Recurrent, Shapes };
+enum class Entry { ChunkFwd, FinalState, Recurrent, Stabilize, Shapes };
 
 // Pure argument checks; no HIP call. Returns GDN_OK or a negative status.
 int validate(const gdn_args* a, Entry e, Problem* out);
@@ -119,5 +119,7 @@ int launch_prep_gdn(const Problem& p, void* ws, bool want_output, void* stream);
 int launch_prep_dp(const Problem& p, void* ws, bool want_output, void* stream);
 int launch_prep_asym(const Problem& p, void* ws, bool want_output, void* stream);
 int launch_state_copy(const Problem& p, void* stream);
+// ASYM stabilisers (gdn_stabilize.hip); mode as in gdn_asym_stabilize.
+int launch_stabilize(const Problem& p, int mode, void* out, void* stream);
 
 }  // namespace gdn

@@ -134,6 +134,32 @@ int gdn_chunk_scan(const gdn_args* args, void* ws, size_t ws_bytes, void* stream
  * step). args->s0, args->s_final and args->chunk are ignored. No workspace. */
 int gdn_recurrent_step(const gdn_args* args, float* state_inout, void* stream);
 
+/* Modes of gdn_asym_stabilize. */
+enum gdn_stabilize_mode { GDN_STABILIZE_CLIP_DECAY = 1, GDN_STABILIZE_PROJECT_J = 2 };
+
+/* GDN2 stabilisers: token-wise transforms of the ASYM inputs, run before the forward
+ * pass, that bound the spectral norm of each step's transition D (I - eta j k^T)
+ * (GDN2-stability page: "The Spectral Norm" gives rho = ||I - eta j k^T||_2 in closed
+ * form; "Simple Strategy" clips D; "Modifying Itself" moves j). args is an ASYM
+ * argument set (variant GDN_VARIANT_ASYM, shapes as for the forward pass); only k,
+ * j, alpha (= D) and eta are read, in args->dtype, and out has the same dtype.
+ * The page's unit-norm j and k are not required: their norms are folded into eta.
+ *   GDN_STABILIZE_CLIP_DECAY  out [B, T, H, dk] = min(D, 1/rho) per channel; then
+ *                             ||D' (I - eta j k^T)||_2 <= 1.
+ *   GDN_STABILIZE_PROJECT_J   out [B, T, H, dk] = j' = s k + lam (j - s k) with
+ *                             s = j^T k / ||k||^2: eta j'^T k = eta j^T k (the erase
+ *                             rate c is kept) and, with g = max_i D_i and
+ *                             tau = (c - 1) g + 1/g, ||I - eta j' k^T||_2 <= 1/g
+ *                             whenever tau >= |c|. lam = min(1, sqrt((tau^2 - c^2) /
+ *                             (eta^2 ||k||^2 ||j - s k||^2))); lam = 1 when that
+ *                             denominator is 0; lam = 0 when tau^2 <= c^2 (no j'
+ *                             reaches the bound; only c < 0 gets there).
+ * out must be 16-byte aligned; it may be args->alpha (mode 1) or args->j (mode 2)
+ * for an in-place update, and must not overlap any other input. k = 0 rows give
+ * NaN in mode 2. T = 0 does nothing. Errors: GDN_ERR_ARG for a variant other than
+ * ASYM, a mode outside the enum, or a null or misaligned k, j, alpha, eta or out. */
+int gdn_asym_stabilize(const gdn_args* args, int mode, void* out, void* stream);
+
 /* Static text for a status code. */
 const char* gdn_status_str(int status);
 

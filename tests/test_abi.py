@@ -30,6 +30,7 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) >= {"gdn_chunk_fwd", "gdn_final_state", "gdn_recurrent_step",
+                          "gdn_chunk_prepare", "gdn_chunk_scan", "gdn_asym_stabilize",
                           "gdn_workspace_bytes", "gdn_status_str", "gdn_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -113,6 +114,23 @@ def test_final_state_and_recurrent_checks(lib):
     assert lib.gdn_recurrent_step(ctypes.byref(a), FAKE + 4, None) == -1
     assert lib.gdn_recurrent_step(ctypes.byref(good_args(variant=3, n_h=9)), FAKE, None) == -2
     assert lib.gdn_recurrent_step(None, FAKE, None) == -1
+
+
+def test_stabilize_checks(lib):
+    def stab(mode=1, out=FAKE, **over):
+        a = good_args(**{"variant": 4, "j": FAKE, "eta": FAKE, **over})
+        return lib.gdn_asym_stabilize(ctypes.byref(a), mode, out, None)
+
+    assert stab(mode=0) == -1 and stab(mode=3) == -1
+    assert stab(variant=0) == -1                      # ASYM inputs only
+    for f in ("k", "j", "alpha", "eta"):
+        assert stab(**{f: 0}) == -1, f
+        assert stab(**{f: FAKE + 8}) == -1, f
+    assert stab(out=None) == -1 and stab(out=FAKE + 4) == -1
+    assert stab(dk=48) == -2
+    # T = 0: nothing to do, nothing required, no launch
+    assert stab(T=0, k=0, j=0, alpha=0, eta=0, out=None) == 0
+    assert lib.gdn_asym_stabilize(None, 1, FAKE, None) == -1
 
 
 def test_workspace_bytes_grows_with_tokens(lib):

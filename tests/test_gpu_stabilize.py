@@ -1,0 +1,141 @@
+"""GDN2 stabilisers (gdn_asym_stabilize) against the float64 oracle.
+
+Inputs are the asymmetric workload's recipe with rows reshaped so that every branch
+of both transforms is taken: larger eta (clip active, j moved), j -> -j (erase rate
+c < 0, no bounded j: lam = 0), eta = 0 (nothing to move: lam = 1), j = k (j already
+parallel to k) and D = 1 (g = 1: tau = c, the KDA case). Tolerances as for the
+forward pass (fp32 inputs rel-L2 1e-5 / normwise max-rel 1e-4; bf16 inputs, whose
+outputs are rounded to bf16, 5e-3 / 2e-2).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+ST = oracle.stabilize
+
+
+def mixed_inputs(B, T, H, dk, dtype, seed, dv=None):
+    inp = gdn_inputs.make_inputs("asym", B, T, H, dk, dv or dk, dtype=dtype, seed=seed)
+    k, j, D, eta = (inp[x].astype(np.float64) for x in ("k", "j", "alpha", "eta"))
+    kind = np.arange(B * T * H).reshape(B, T, H) % 6
+    eta = np.where(kind == 1, 4.0 * eta, eta)
+    j = np.where((kind == 2)[..., None], -j, j)
+    eta = np.where(kind == 3, 0.0, eta)
+    j = np.where((kind == 4)[..., None], k, j)
+    D = np.where((kind == 5)[..., None], 1.0, D)
+    fin = gdn_inputs.round_bf16 if dtype == "bf16" else (lambda x: x.astype(np.float32))
+    inp.update(j=fin(j), eta=fin(eta), alpha=fin(D))
+    return inp, kind
+
+
+def _oracle_out(mode, inp):
+    k, j, D, eta = (inp[x].astype(np.float64) for x in ("k", "j", "alpha", "eta"))
+    if mode == "clip_decay":
+        return ST.clip_decay(k, j, eta, D)
+    return ST.project_j(k, j, eta, D)
+
+
+def _run(mode, inp, out=None):
+    import gated_delta_rule_69_amd as gdn
+    from gpu_util import to_dev
+    d = to_dev(inp)
+    return gdn.gdn_asym_stabilize(mode, d["k"], d["j"], d["alpha"], d["eta"], out=out), d
+
+
+def _check(got, ref, dtype, what):
+    from gpu_util import TOL, host
+    tol = TOL[dtype]
+    e2, em = oracle.rel_l2(host(got), ref), oracle.max_rel(host(got), ref)
+    print(what, f"rel_l2={e2:.2e} max_rel={em:.2e}", flush=True)
+    assert e2 <= tol["rel_l2"] and em <= tol["max_rel"], (e2, em)
+
+
+CASES = [  # dtype, B, T, H, dk
+    ("f32", 1, 37, 3, 16),
+    ("f32", 2, 50, 2, 32),
+    ("f32", 1, 70, 4, 64),
+    ("f32", 1, 33, 3, 128),
+    ("bf16", 2, 41, 4, 64),
+    ("bf16", 1, 64, 5, 128),
+]
+
+
+@pytest.mark.parametrize("mode", ["clip_decay", "project_j"])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_stabilize_vs_oracle(mode, case):
+    dt, B, T, H, dk = case
+    inp, kind = mixed_inputs(B, T, H, dk, dt, seed=41)
+    ref = _oracle_out(mode, inp)
+    # every branch is taken by some row of this input
+    k, j, D, eta = (inp[x].astype(np.float64) for x in ("k", "j", "alpha", "eta"))
+    if mode == "clip_decay":
+        assert (ref < D).any() and (ref == D).any()
+    else:
+        c = eta * np.sum(j * k, -1)
+        assert (c < 0).any() and (eta == 0).any() and (D.max(-1) == 1.0).any()
+        moved = np.abs(ref - j).max(-1) > 1e-6
+        assert moved.any() and (~moved).any()
+    got, _ = _run(mode, inp)
+    _check(got, ref, dt, f"{mode} {case}")
+
+
+@pytest.mark.parametrize("mode", ["clip_decay", "project_j"])
+def test_stabilize_in_place_equals_out_of_place(mode):
+    inp, _ = mixed_inputs(2, 30, 3, 64, "f32", seed=5)
+    got, d = _run(mode, inp)
+    target = d["alpha"] if mode == "clip_decay" else d["j"]
+    import gated_delta_rule_69_amd as gdn
+    gdn.gdn_asym_stabilize(mode, d["k"], d["j"], d["alpha"], d["eta"], out=target)
+    torch.cuda.synchronize()
+    assert torch.equal(target, got)
+
+
+def test_stabilize_empty_sequence():
+    import gated_delta_rule_69_amd as gdn
+    from gpu_util import DEV
+    k = torch.empty((2, 0, 3, 64), device=DEV)
+    e = torch.empty((2, 0, 3), device=DEV)
+    out = gdn.gdn_asym_stabilize("project_j", k, k, k, e)
+    assert out.shape == k.shape
+
+
+@pytest.mark.parametrize("mode", ["clip_decay", "project_j"])
+def test_stabilize_full_workload(mode):
+    """The asymmetric workload at full size (B=8, H=32, T=2048, dk=64, fp32), every
+    row against the oracle."""
+    inp = gdn_inputs.config_inputs(4)
+    ref = _oracle_out(mode, inp)
+    got, _ = _run(mode, inp)
+    _check(got, ref, "f32", f"{mode} full workload")
+
+
+@pytest.mark.parametrize("dt,dk,chunk", [("f32", 64, 32), ("bf16", 128, 64)])
+@pytest.mark.parametrize("mode", ["clip_decay", "project_j"])
+def test_stabilized_forward(mode, dt, dk, chunk):
+    """Stabiliser then chunked forward on the device, against the oracle's stabiliser
+    then the oracle's recurrence (the stabilised tensor is stored in the input dtype,
+    so the oracle's is rounded to it too)."""
+    import gated_delta_rule_69_amd as gdn
+    from gpu_util import TOL, host, state_to_dev
+    inp, _ = mixed_inputs(1, 150, 2, dk, dt, seed=12)
+    s0 = gdn_inputs.make_state(1, 2, dk, dk, seed=4)
+    key = "alpha" if mode == "clip_decay" else "j"
+    ref_in = dict(inp)
+    stab = _oracle_out(mode, inp)
+    ref_in[key] = gdn_inputs.round_bf16(stab) if dt == "bf16" else stab
+    o_ref, S_ref = oracle.forward(ref_in, s0)
+
+    new, d = _run(mode, inp)
+    d[key] = new
+    o, S = gdn.gdn_chunk_fwd("asym", d["q"], d["k"], d["v"], d["alpha"], None, chunk=chunk,
+                             j=d["j"], eta=d["eta"], s0=state_to_dev(s0))
+    tol = TOL[dt]
+    for name, x, r in (("o", o, o_ref), ("S", S, S_ref)):
+        e2, em = oracle.rel_l2(host(x), r), oracle.max_rel(host(x), r)
+        print(mode, dt, name, f"rel_l2={e2:.2e} max_rel={em:.2e}", flush=True)
+        assert e2 <= tol["rel_l2"] and em <= tol["max_rel"], (name, e2, em)
