@@ -85,3 +85,21 @@ def test_project_j_special_cases():
     # j parallel to k: nothing to move
     jk = np.array([[0.7, 0.0, 0.0]])
     np.testing.assert_allclose(stabilize.project_j(k, jk, np.array([1.0]), D), jk, rtol=1e-15)
+
+
+def test_gated_key_parametrisation_reaches_the_bound():
+    """'Modifying Itself' closes with j = k (.) b, b in [0, 1]^d: then c = eta j^T k >= 0,
+    and for unit k and eta <= 1 the projected j' always meets ||I - eta j' k^T|| <= 1/g
+    (no row falls in the case without a solution)."""
+    rng = np.random.default_rng(6)
+    n, d = 300, 10
+    k = rng.standard_normal((n, d))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    j = k * rng.random((n, d))
+    eta = rng.random(n)
+    D = 1.0 / (1.0 + np.exp(-(3.0 + rng.standard_normal((n, d)))))
+    assert (eta * np.sum(j * k, -1) >= 0).all()
+    jp = stabilize.project_j(k, j, eta, D)
+    for i in range(n):
+        g = D[i].max()
+        assert np.linalg.norm(_A(k[i], jp[i], eta[i]), 2) <= 1.0 / g + 1e-9
