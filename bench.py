@@ -379,8 +379,9 @@ def stabilize(args):
     median time of one gdn_asym_stabilize call over 20 calls (512 MB written between
     calls so that nothing stays in the Infinity Cache), HBM fraction with
     (4 dk + 1) elements per token-head (k, j, D and eta in, dk out), the cost beside
-    one gdn_chunk_fwd call of the same workload, and the first 4096 token-heads
-    against the float64 oracle."""
+    one gdn_chunk_fwd call of the same workload, the time of gdn_chunk_fwd with the
+    stabiliser inside the pass, and the first 4096 token-heads against the float64
+    oracle."""
     import torch
     import gated_delta_rule_69_amd as gdn
     import oracle
@@ -419,18 +420,22 @@ def stabilize(args):
     eta = inp["eta"].reshape(units)[:n].astype(np.float64)
     rows = []
     for mode in ("clip_decay", "project_j"):
+        fa = gdn.make_args("asym", t["q"], t["k"], t["v"], t["alpha"], None, chunk=cfg["chunk"],
+                           j=t["j"], eta=t["eta"], s_final=s_final, o=o, stabilize=mode)
+        fused_us = timed(lambda: gdn.gdn_chunk_fwd_args(fa, ws))
         us = timed(lambda: gdn.gdn_asym_stabilize(mode, t["k"], t["j"], t["alpha"], t["eta"], out=out))
         fn = oracle.stabilize.clip_decay if mode == "clip_decay" else oracle.stabilize.project_j
         ref = fn(sub["k"], sub["j"], eta, sub["alpha"])
         got = out.reshape(units, dk)[:n].cpu().numpy().astype(np.float64)
         err = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
         gbs = nbytes / (us * 1e-6) / 1e9
-        rows.append(dict(mode=mode, us=us, vs_chunk_fwd=us / fwd_us,
+        rows.append(dict(mode=mode, us=us, vs_chunk_fwd=us / fwd_us, fused_chunk_fwd_us=fused_us,
                          hbm=dict(achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s",
                                   frac=gbs / HBM_PEAK_GBS, algorithmic=nbytes),
                          parity=dict(rel_l2=err, rows=n)))
         log(f"stabilize {mode}: {us:.1f} us, {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%}), "
-            f"{us / fwd_us:.1%} of gdn_chunk_fwd ({fwd_us:.1f} us), parity {err:.2e}")
+            f"{us / fwd_us:.1%} of gdn_chunk_fwd ({fwd_us:.1f} us), parity {err:.2e}; "
+            f"inside gdn_chunk_fwd: {fused_us:.1f} us")
     print(json.dumps({"metric": "time per gdn_asym_stabilize call, workload 4 (B=8, H=32, T=2048, dk=64, fp32)",
                       "rows": rows, "chunk_fwd_us": fwd_us, "device_copy_gbs": copy_bandwidth_gbs(),
                       "data": "synthetic", "n_gpus": 1}), flush=True)

@@ -28,7 +28,8 @@ class GdnArgs(ctypes.Structure):
                 ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("alpha", ctypes.c_void_p), ("beta", ctypes.c_void_p),
                 ("beta_v", ctypes.c_void_p), ("j", ctypes.c_void_p), ("eta", ctypes.c_void_p),
-                ("s0", ctypes.c_void_p), ("s_final", ctypes.c_void_p), ("o", ctypes.c_void_p)]
+                ("s0", ctypes.c_void_p), ("s_final", ctypes.c_void_p), ("o", ctypes.c_void_p),
+                ("stabilize", ctypes.c_int32)]
 
 
 class GdnError(RuntimeError):
@@ -99,7 +100,7 @@ def _check(t, name, device, dtype=None):
 
 
 def make_args(variant, q, k, v, alpha, beta=None, *, chunk=64, n_h=None, beta_v=None, j=None,
-              eta=None, s0=None, s_final=None, o=None) -> GdnArgs:
+              eta=None, s0=None, s_final=None, o=None, stabilize=None) -> GdnArgs:
     import torch
     if variant not in VARIANTS:
         raise ValueError(f"unknown variant {variant!r}")
@@ -130,6 +131,9 @@ def make_args(variant, q, k, v, alpha, beta=None, *, chunk=64, n_h=None, beta_v=
     a.alpha, a.beta, a.beta_v = _ptr(alpha), _ptr(beta), _ptr(beta_v)
     a.j, a.eta = _ptr(j), _ptr(eta)
     a.s0, a.s_final, a.o = _ptr(s0), _ptr(s_final), _ptr(o)
+    if stabilize is not None and stabilize not in STABILIZE_MODES:
+        raise ValueError(f"unknown stabilizer mode {stabilize!r}")
+    a.stabilize = 0 if stabilize is None else STABILIZE_MODES[stabilize]
     a._keep = (q, k, v, alpha, beta, beta_v, j, eta, s0, s_final, o)  # lifetimes
     return a
 
@@ -159,9 +163,11 @@ def _workspace(args, ws, device):
 
 def gdn_chunk_fwd(variant, q, k, v, alpha, beta=None, *, chunk=64, beta_v=None, j=None,
                   eta=None, s0=None, s_final=None, o=None, workspace=None, stream=None,
-                  want_state=True):
+                  want_state=True, stabilize=None):
     """Chunkwise forward. Returns (o, s_final); allocates o / s_final / workspace
-    when not given (torch device memory). s_final may be s0 (updated in place)."""
+    when not given (torch device memory). s_final may be s0 (updated in place).
+    stabilize ("clip_decay" / "project_j", ASYM only) applies that GDN2 stabiliser
+    to every token inside the pass."""
     import torch
     dev = k.device
     B, T, H = k.shape[:3]
@@ -171,7 +177,7 @@ def gdn_chunk_fwd(variant, q, k, v, alpha, beta=None, *, chunk=64, beta_v=None, 
     if s_final is None and want_state:
         s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     a = make_args(variant, q, k, v, alpha, beta, chunk=chunk, beta_v=beta_v, j=j, eta=eta,
-                  s0=s0, s_final=s_final, o=o)
+                  s0=s0, s_final=s_final, o=o, stabilize=stabilize)
     ws = _workspace(a, workspace, dev)
     st = load_library().gdn_chunk_fwd(ctypes.byref(a), ctypes.c_void_p(ws.data_ptr()),
                                       ctypes.c_size_t(ws.numel()), _stream(stream))
@@ -181,7 +187,7 @@ def gdn_chunk_fwd(variant, q, k, v, alpha, beta=None, *, chunk=64, beta_v=None, 
 
 
 def gdn_final_state(variant, k, v, alpha, beta=None, *, chunk=64, beta_v=None, j=None,
-                    eta=None, s0=None, s_final=None, workspace=None, stream=None):
+                    eta=None, s0=None, s_final=None, workspace=None, stream=None, stabilize=None):
     """State-only chunkwise forward. Returns s_final."""
     import torch
     dev = k.device
@@ -190,7 +196,7 @@ def gdn_final_state(variant, k, v, alpha, beta=None, *, chunk=64, beta_v=None, j
     if s_final is None:
         s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     a = make_args(variant, None, k, v, alpha, beta, chunk=chunk, beta_v=beta_v, j=j, eta=eta,
-                  s0=s0, s_final=s_final, o=None)
+                  s0=s0, s_final=s_final, o=None, stabilize=stabilize)
     ws = _workspace(a, workspace, dev)
     st = load_library().gdn_final_state(ctypes.byref(a), ctypes.c_void_p(ws.data_ptr()),
                                         ctypes.c_size_t(ws.numel()), _stream(stream))
@@ -200,7 +206,7 @@ def gdn_final_state(variant, k, v, alpha, beta=None, *, chunk=64, beta_v=None, j
 
 
 def gdn_recurrent_step(variant, q, k, v, alpha, beta=None, *, state, beta_v=None, j=None,
-                       eta=None, o=None, stream=None):
+                       eta=None, o=None, stream=None, stabilize=None):
     """Token-sequential update of ``state`` (in place) over k.shape[1] tokens; returns o."""
     import torch
     B, T, H = k.shape[:3]
@@ -209,7 +215,7 @@ def gdn_recurrent_step(variant, q, k, v, alpha, beta=None, *, state, beta_v=None
         o = torch.empty((B, T, H, dv), dtype=k.dtype, device=k.device)
     _check(state, "state", k.device, torch.float32)
     a = make_args(variant, q, k, v, alpha, beta, chunk=16, beta_v=beta_v, j=j, eta=eta,
-                  s0=None, s_final=None, o=o)
+                  s0=None, s_final=None, o=o, stabilize=stabilize)
     st = load_library().gdn_recurrent_step(ctypes.byref(a), ctypes.c_void_p(state.data_ptr()),
                                            _stream(stream))
     if st != 0:

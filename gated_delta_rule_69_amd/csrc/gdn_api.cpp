@@ -43,6 +43,10 @@ int validate(const gdn_args* a, Entry e, Problem* out) {
   if (a->variant == GDN_VARIANT_FG2 && a->beta_v == nullptr && a->dk != a->dv)
     return GDN_ERR_ARG;  // one beta vector scales both key and value channels
   if (a->variant != GDN_VARIANT_FG2 && a->beta_v != nullptr) return GDN_ERR_ARG;
+  if (e != Entry::Stabilize) {  // the standalone stabiliser takes its mode as an argument
+    if (a->stabilize < 0 || a->stabilize > GDN_STABILIZE_PROJECT_J) return GDN_ERR_ARG;
+    if (a->stabilize != 0 && a->variant != GDN_VARIANT_ASYM) return GDN_ERR_ARG;
+  }
 
   if (e == Entry::Stabilize) {
     // Only k, j, alpha (= D) and eta are read; with T == 0 they may be NULL.
@@ -86,6 +90,7 @@ int validate(const gdn_args* a, Entry e, Problem* out) {
     p.dv = a->dv;
     p.chunk = a->chunk;
     p.n_h = a->n_h;
+    p.stabilize = e == Entry::Stabilize ? 0 : a->stabilize;
     p.q = a->q;
     p.k = a->k;
     p.v = a->v;

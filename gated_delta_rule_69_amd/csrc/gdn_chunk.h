@@ -481,6 +481,18 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigne
         if constexpr (DP) sbt = ld(beg + w.vrow);
         if (w.out_row) load_row<F16, DK>(qg + w.th * DK, lg, qv);
       }
+      if constexpr (V == GDN_VARIANT_ASYM) {
+        if (p.stabilize) {  // GDN2 stabiliser on this row's D or j (row = 4 lane groups)
+          const StabCoef sc = stab_coef<NX>(
+              p.stabilize, seta, [&](int i) { return KJD{kf[i], bf[i], af[i]}; },
+              [](float x) { return sum_over_groups(x); }, [](float x) { return max_over_groups(x); });
+#pragma unroll
+          for (int x = 0; x < NX; ++x) {
+            af[x] = stab_decay(sc, af[x]);
+            bf[x] = stab_j(sc, kf[x], bf[x]);
+          }
+        }
+      }
       float sbk[NX];  // FG2: sqrt(beta) per key channel
 #pragma unroll
       for (int x = 0; x < NX; ++x) {
@@ -1190,7 +1202,9 @@ inline bool prep2_covers(const Problem& p) {
          !(p.variant == GDN_VARIANT_FG2 && p.beta_v != nullptr);
 }
 
-template <int V>
+// STAB: the GDN2 stabiliser mode applied to the rows (ASYM only; a template
+// parameter so that the other instantiations carry none of its registers).
+template <int V, int STAB>
 __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, unsigned char* __restrict__ ws,
                                                                      ChunkLayout L, int want_out) {
   using In = uint16_t;
@@ -1355,6 +1369,23 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
       wscal = sc.eta;
     }
     if (!valid) kscal = wscal = bscal = glog = 0.0f;
+    // GDN2 stabiliser coefficients of this row (identity unless asked for); rows past
+    // the sequence end read the last token and are zeroed below
+    StabCoef stc{__builtin_inff(), 0.0f, 1.0f};
+    if constexpr (STAB != 0) {
+      static_assert(V == GDN_VARIANT_ASYM, "stabilisers act on the asymmetric variant");
+      // Each call unpacks afresh from the packed rows (the empty asm hides that the
+      // two passes read the same words), so the unpacked row is never held whole.
+      auto unpack = [&](const uint4& v, int s2) __attribute__((always_inline)) {
+        uint32_t w = s2 / 2 == 0 ? v.x : s2 / 2 == 1 ? v.y : s2 / 2 == 2 ? v.z : v.w;
+        asm volatile("" : "+v"(w));
+        return __uint_as_float((s2 & 1) ? (w & 0xffff0000u) : (w << 16));
+      };
+      stc = stab_coef<32>(
+          STAB, sc.eta,
+          [&](int i) { return KJD{unpack(raw.k[i / 8], i % 8), unpack(raw.b[i / 8], i % 8), unpack(raw.a[i / 8], i % 8)}; },
+          [](float x) { return sum_over_groups(x); }, [](float x) { return max_over_groups(x); });
+    }
 
     // ---- phase 1: log decay and row maxima ----
     // The maxima only set power-of-two scales. They are taken on the bf16 bit
@@ -1374,7 +1405,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
 #pragma unroll
       for (int s2 = 0; s2 < 8; ++s2) {
         const int x = 8 * u + s2;
-        if constexpr (CH_ALPHA) G[x] = valid ? __builtin_amdgcn_logf(bf(raw.a[u], s2)) : 0.0f;
+        if constexpr (STAB == 1) G[x] = valid ? __builtin_amdgcn_logf(stab_decay(stc, bf(raw.a[u], s2))) : 0.0f;
+        else if constexpr (CH_ALPHA) G[x] = valid ? __builtin_amdgcn_logf(bf(raw.a[u], s2)) : 0.0f;
         else G[x] = glog;
       }
       vm2 = absmax8(vm2, raw.v[u]);
@@ -1466,7 +1498,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
           xv[e] = (_Float16)(bf(vr, e) * sb * wsc);
         } else if constexpr (V == GDN_VARIANT_ASYM) {
           a = valid ? kf : 0.0f;
-          bb = bscal * bf(br, e);
+          bb = bscal * (STAB == 2 ? stab_j(stc, kf, bf(br, e)) : bf(br, e));
         } else {  // KDA, GDN (kscal = sqrt(beta)); DeltaProduct (bscal = beta)
           a = kscal * kf;
           bb = bscal * a;
@@ -1694,8 +1726,18 @@ int launch_prep_t(const Problem& p, void* ws, bool want_out, hipStream_t s) {
   if constexpr (std::is_same<In, uint16_t>::value && DK == 128 && C == 64 && !DPV) {
     if (prep2_covers(p)) {  // two workgroups per CU
       const int64_t grid = std::min<int64_t>(items, 2 * int64_t(device_cus()));
-      chunk_prep2_kernel<V><<<dim3(unsigned(grid)), kThreads, 0, s>>>(p, static_cast<unsigned char*>(ws), L,
-                                                                             want_out ? 1 : 0);
+      unsigned char* w = static_cast<unsigned char*>(ws);
+      const int wo = want_out ? 1 : 0;
+      if constexpr (V == GDN_VARIANT_ASYM) {
+        if (p.stabilize == GDN_STABILIZE_CLIP_DECAY)
+          chunk_prep2_kernel<V, 1><<<dim3(unsigned(grid)), kThreads, 0, s>>>(p, w, L, wo);
+        else if (p.stabilize == GDN_STABILIZE_PROJECT_J)
+          chunk_prep2_kernel<V, 2><<<dim3(unsigned(grid)), kThreads, 0, s>>>(p, w, L, wo);
+        else
+          chunk_prep2_kernel<V, 0><<<dim3(unsigned(grid)), kThreads, 0, s>>>(p, w, L, wo);
+      } else {
+        chunk_prep2_kernel<V, 0><<<dim3(unsigned(grid)), kThreads, 0, s>>>(p, w, L, wo);
+      }
       return int(hipGetLastError());
     }
   }

@@ -82,6 +82,89 @@ __device__ __forceinline__ float max_over_groups(float x) {
   return fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
 }
 
+// Sum and max over the eight lanes l ^ 8m (m = 0..7): DPP row_ror:8 pairs lane l with
+// l ^ 8 inside each 16-lane row, then the four-group exchanges above.
+__device__ __forceinline__ float sum_over_8_groups(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));  // lane ^ 8
+  return sum_over_groups(x);                                                                       // ^ 16, ^ 32
+}
+__device__ __forceinline__ float max_over_8_groups(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false)));
+  return max_over_groups(x);
+}
+
+// ---- GDN2 stabilisers --------------------------------------------------------------
+// Per token and head of the asymmetric variant (GDN2-stability page, "The Spectral
+// Norm", "Simple Strategy", "Modifying Itself"), with the norms of j and k folded
+// into eta so that unit vectors are not required:
+//   clip (mode 1)     D' = min(D, lim),  lim = 1 / rho,  rho = ||I - eta j k^T||_2
+//                     = (e + sqrt(e^2 - 4 eta j^T k + 4)) / 2,  e = eta ||j|| ||k||
+//   project (mode 2)  j' = s k + lam (j - s k),  s = j^T k / ||k||^2,
+//                     c = eta j^T k,  g = max D,  tau = (c - 1) g + 1/g,
+//                     lam = min(1, sqrt((tau^2 - c^2) / (eta^2 ||k||^2 ||j - s k||^2)))
+// lam = 1 for a zero denominator (j parallel to k, or eta = 0); lam = 0 for
+// tau^2 <= c^2 (the page's case without a solution, only reached with c < 0).
+struct StabCoef {
+  float lim, s, lam;  // D' = min(D, lim), j' = s k + lam (j - s k)
+};
+struct KJD {
+  float k, j, d;
+};
+
+// Coefficients of one row whose channels are spread over several lanes: `at(i)`
+// returns this lane's channel i (i < N) of k, j and D; `rsum` / `rmax` reduce over
+// the lanes of the row. mode is uniform across the wave; 0 gives the identity.
+template <int N, typename At, typename Sum, typename Max>
+__device__ __forceinline__ StabCoef stab_coef(int mode, float eta, At at, Sum rsum, Max rmax) {
+  StabCoef c{__builtin_inff(), 0.0f, 1.0f};
+  if (mode == 0) return c;
+  float jk = 0.0f, k2 = 0.0f, j2 = 0.0f, g = 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const KJD x = at(i);
+    jk += x.j * x.k;
+    k2 += x.k * x.k;
+    j2 += x.j * x.j;
+    g = fmaxf(g, x.d);
+  }
+  jk = rsum(jk);
+  k2 = rsum(k2);
+  if (mode == 1) {
+    j2 = rsum(j2);
+    const float en = eta * sqrtf(j2) * sqrtf(k2);
+    // en >= |eta j^T k| makes the radicand >= (en - 2)^2 >= 0; clamp rounding.
+    const float rho = 0.5f * (en + sqrtf(fmaxf(en * en - 4.0f * eta * jk + 4.0f, 0.0f)));
+    c.lim = 1.0f / rho;
+    return c;
+  }
+  g = rmax(g);
+  const float s = jk / k2;
+  float p2 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const KJD x = at(i);
+    const float pe = x.j - s * x.k;
+    p2 += pe * pe;
+  }
+  p2 = rsum(p2);
+  const float cc = eta * jk;
+  const float den = eta * eta * k2 * p2;  // ||eta ||k|| j||^2 - c^2 without cancellation
+  // tau^2 - c^2 = (tau - c)(tau + c) = (1 - g)((1 + g)/g - c) (1 + g)(c + (1 - g)/g):
+  // exactly 0 at g = 1 and no cancellation between tau^2 and c^2, where the square
+  // root below is steepest.
+  const float omg = 1.0f - g;
+  const float num = omg * (1.0f + g) * ((1.0f + g) / g - cc) * (cc + omg / g);
+  // fminf returns 1 for a NaN ratio, as for the zero denominator.
+  c.s = s;
+  c.lam = den <= 0.0f ? 1.0f : (num <= 0.0f ? 0.0f : fminf(1.0f, sqrtf(num / den)));
+  return c;
+}
+
+__device__ __forceinline__ float stab_decay(const StabCoef& c, float d) { return fminf(d, c.lim); }
+__device__ __forceinline__ float stab_j(const StabCoef& c, float k, float j) {
+  return c.s * k + c.lam * (j - c.s * k);
+}
+
 // ---- MFMA wrappers -------------------------------------------------------------
 // Every product below is a 16x16 output tile D += A B with A 16 x K and B K x 16,
 // walked in 16-wide slices of K. Within a slice, lane l = i + 16 g (i = l % 16,

@@ -15,6 +15,7 @@ struct Problem {
   int64_t B, T, H, dk, dv;
   int chunk;
   int n_h;
+  int stabilize;  // ASYM: 0, or the gdn_stabilize_mode applied to each token's inputs
   const void* q;
   const void* k;
   const void* v;

@@ -72,6 +72,16 @@ __global__ __launch_bounds__(64) void recurrent_kernel(Problem p, float* __restr
         load_vec<NR>(jv + th * dk + row0, bb);
         load_vec<NR>(al + th * dk + row0, alpha);
         const float e = IO<In>::ld(et + th);
+        if (p.stabilize) {
+          const StabCoef sc = stab_coef<NR>(
+              p.stabilize, e, [&](int i) { return KJD{a[i], bb[i], alpha[i]}; },
+              [](float x) { return sum_over_groups(x); }, [](float x) { return max_over_groups(x); });
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            alpha[r] = stab_decay(sc, alpha[r]);
+            bb[r] = stab_j(sc, a[r], bb[r]);
+          }
+        }
 #pragma unroll
         for (int r = 0; r < NR; ++r) bb[r] *= e;
         wv = e * IO<In>::ld(v + th * dv + col);
@@ -129,11 +139,6 @@ __global__ __launch_bounds__(64) void recurrent_kernel(Problem p, float* __restr
 // for the DK/8 contiguous key rows starting at g * DK/8, so that each state row of
 // the slice is one 128-byte line read and written by eight lanes. Sums over key
 // rows are a per-lane partial sum and three exchanges across the eight lane groups.
-__device__ __forceinline__ float sum_over_8_groups(float x) {
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));  // lane ^ 8
-  return sum_over_groups(x);                                                                       // ^ 16, ^ 32
-}
-
 template <typename In, int DK>
 __global__ __launch_bounds__(64) void recurrent_wide_kernel(Problem p, float* __restrict__ state) {
   constexpr int NR = DK / 8;  // key rows per lane
@@ -213,6 +218,16 @@ __global__ __launch_bounds__(64) void recurrent_wide_kernel(Problem p, float* __
         load_vec<NR>(jv + th * dk + row0, bb);
         load_vec<NR>(al + th * dk + row0, alpha);
         const float e = IO<In>::ld(et + th);
+        if (p.stabilize) {
+          const StabCoef sc = stab_coef<NR>(
+              p.stabilize, e, [&](int i) { return KJD{a[i], bb[i], alpha[i]}; },
+              [](float x) { return sum_over_8_groups(x); }, [](float x) { return max_over_8_groups(x); });
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            alpha[r] = stab_decay(sc, alpha[r]);
+            bb[r] = stab_j(sc, a[r], bb[r]);
+          }
+        }
 #pragma unroll
         for (int r = 0; r < NR; ++r) bb[r] *= e;
 #pragma unroll

@@ -5,14 +5,9 @@
 //   mode 1 (clip the decay)   D' = min(D, 1/rho),  rho = ||I - eta j k^T||_2
 //   mode 2 (project j)        j' = s k + lam (j - s k),  s = j^T k / ||k||^2
 //
-// The page's closed forms assume unit j and k; here their norms are absorbed into
-// eta, so any nonzero k works:
-//   rho = (e + sqrt(e^2 - 4 eta j^T k + 4)) / 2,  e = eta ||j|| ||k||
-//   c = eta j^T k,  g = max_i D_i,  tau = (c - 1) g + 1/g
-//   lam = min(1, sqrt((tau^2 - c^2) / (eta^2 ||k||^2 ||j - s k||^2)))
-// with lam = 1 when the denominator is 0 (j parallel to k, or eta = 0: nothing to
-// move) and lam = 0 when tau^2 <= c^2 (the page's case without a solution; only
-// c < 0 reaches it, and j' = s k is the closest bounded choice).
+// The formulas (norms folded into eta, the readings where the page gives no value)
+// are in stab_coef; the same coefficients are applied inside the chunked and
+// recurrent passes when gdn_args.stabilize asks for it.
 //
 // Both are HBM-bound streams (three dk-vectors and one scalar in, one dk-vector
 // out per token and head). A row (one token and head) is spread over dk/4 adjacent
@@ -68,56 +63,12 @@ __global__ __launch_bounds__(kThreads) void stabilize_kernel(const In* __restric
     load_vec<4>(k + base, kk);
     load_vec<4>(jv + base, jj);
     load_vec<4>(D + base, dd);
-    const float e = IO<In>::ld(eta + r);
+    const StabCoef sc = stab_coef<4>(
+        MODE, IO<In>::ld(eta + r), [&](int i) { return KJD{kk[i], jj[i], dd[i]}; },
+        [](float x) { return row_sum<LPR>(x); }, [](float x) { return row_max<LPR>(x); });
     float res[4];
-    if constexpr (MODE == 1) {
-      float jk = 0.0f, j2 = 0.0f, k2 = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        jk += jj[i] * kk[i];
-        j2 += jj[i] * jj[i];
-        k2 += kk[i] * kk[i];
-      }
-      jk = row_sum<LPR>(jk);
-      j2 = row_sum<LPR>(j2);
-      k2 = row_sum<LPR>(k2);
-      const float en = e * sqrtf(j2) * sqrtf(k2);
-      // en >= |e j^T k| makes the radicand >= (en - 2)^2 >= 0; clamp rounding.
-      const float rho = 0.5f * (en + sqrtf(fmaxf(en * en - 4.0f * e * jk + 4.0f, 0.0f)));
-      const float lim = 1.0f / rho;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) res[i] = fminf(dd[i], lim);
-    } else {
-      float jk = 0.0f, k2 = 0.0f, g = dd[0];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        jk += jj[i] * kk[i];
-        k2 += kk[i] * kk[i];
-        g = fmaxf(g, dd[i]);
-      }
-      jk = row_sum<LPR>(jk);
-      k2 = row_sum<LPR>(k2);
-      g = row_max<LPR>(g);
-      const float s = jk / k2;
-      float perp[4], p2 = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        perp[i] = jj[i] - s * kk[i];
-        p2 += perp[i] * perp[i];
-      }
-      p2 = row_sum<LPR>(p2);
-      const float c = e * jk;
-      const float den = e * e * k2 * p2;  // ||eta ||k|| j||^2 - c^2, without cancellation
-      // tau^2 - c^2 = (tau - c)(tau + c) = (1 - g)((1 + g)/g - c) (1 + g)(c + (1 - g)/g):
-      // exact 0 at g = 1 and no cancellation between tau^2 and c^2, to which the
-      // square root below is most sensitive.
-      const float omg = 1.0f - g;
-      const float num = omg * (1.0f + g) * ((1.0f + g) / g - c) * (c + omg / g);
-      // fminf returns 1 for a NaN ratio, as for the zero denominator.
-      const float lam = den <= 0.0f ? 1.0f : (num <= 0.0f ? 0.0f : fminf(1.0f, sqrtf(num / den)));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) res[i] = s * kk[i] + lam * perp[i];
-    }
+    for (int i = 0; i < 4; ++i) res[i] = MODE == 1 ? stab_decay(sc, dd[i]) : stab_j(sc, kk[i], jj[i]);
     store4(out + base, res);
   }
 }

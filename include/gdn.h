@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 enum gdn_variant {
   GDN_VARIANT_FG2 = 0,
@@ -81,6 +81,9 @@ enum gdn_status {
   GDN_ERR_HIP = -4          /* a HIP launch reported an error                 */
 };
 
+/* GDN2 stabilisers: gdn_asym_stabilize's mode, and gdn_args.stabilize. */
+enum gdn_stabilize_mode { GDN_STABILIZE_CLIP_DECAY = 1, GDN_STABILIZE_PROJECT_J = 2 };
+
 typedef struct gdn_args {
   int32_t variant;  /* enum gdn_variant */
   int32_t dtype;    /* enum gdn_dtype   */
@@ -99,6 +102,10 @@ typedef struct gdn_args {
   const float* s0;    /* initial state, NULL means zero                        */
   float* s_final;     /* final state, NULL means not written; may alias s0     */
   void* o;            /* outputs; ignored by gdn_final_state                   */
+  int32_t stabilize;  /* ASYM only: 0, or a gdn_stabilize_mode applied to every
+                         token's D or j inside the pass (as gdn_asym_stabilize
+                         would, without its extra pass over the inputs or the
+                         rounding of D' / j' to the input dtype)                */
 } gdn_args;
 
 /* Bytes of device workspace gdn_chunk_fwd / gdn_final_state need for *args
@@ -134,11 +141,7 @@ int gdn_chunk_scan(const gdn_args* args, void* ws, size_t ws_bytes, void* stream
  * step). args->s0, args->s_final and args->chunk are ignored. No workspace. */
 int gdn_recurrent_step(const gdn_args* args, float* state_inout, void* stream);
 
-/* Modes of gdn_asym_stabilize. */
-enum gdn_stabilize_mode { GDN_STABILIZE_CLIP_DECAY = 1, GDN_STABILIZE_PROJECT_J = 2 };
-
-/* GDN2 stabilisers: token-wise transforms of the ASYM inputs, run before the forward
- * pass, that bound the spectral norm of each step's transition D (I - eta j k^T)
+/* GDN2 stabilisers: token-wise transforms of the ASYM inputs that bound the spectral norm of each step's transition D (I - eta j k^T)
  * (GDN2-stability page: "The Spectral Norm" gives rho = ||I - eta j k^T||_2 in closed
  * form; "Simple Strategy" clips D; "Modifying Itself" moves j). args is an ASYM
  * argument set (variant GDN_VARIANT_ASYM, shapes as for the forward pass); only k,
@@ -154,8 +157,10 @@ enum gdn_stabilize_mode { GDN_STABILIZE_CLIP_DECAY = 1, GDN_STABILIZE_PROJECT_J 
  *                             (eta^2 ||k||^2 ||j - s k||^2))); lam = 1 when that
  *                             denominator is 0; lam = 0 when tau^2 <= c^2 (no j'
  *                             reaches the bound; only c < 0 gets there).
- * out must be 16-byte aligned; it may be args->alpha (mode 1) or args->j (mode 2)
- * for an in-place update, and must not overlap any other input. k = 0 rows give
+ * args->stabilize is ignored here; setting it on the forward entry points applies
+ * the same transform inside the pass instead. out must be 16-byte aligned; it may be
+ * args->alpha (mode 1) or args->j (mode 2) for an in-place update, and must not
+ * overlap any other input. k = 0 rows give
  * NaN in mode 2. T = 0 does nothing. Errors: GDN_ERR_ARG for a variant other than
  * ASYM, a mode outside the enum, or a null or misaligned k, j, alpha, eta or out. */
 int gdn_asym_stabilize(const gdn_args* args, int mode, void* out, void* stream);

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
                           "gdn_workspace_bytes", "gdn_status_str", "gdn_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.gdn_abi_version() == 1
+    assert lib.gdn_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -114,6 +114,19 @@ def test_final_state_and_recurrent_checks(lib):
     assert lib.gdn_recurrent_step(ctypes.byref(a), FAKE + 4, None) == -1
     assert lib.gdn_recurrent_step(ctypes.byref(good_args(variant=3, n_h=9)), FAKE, None) == -2
     assert lib.gdn_recurrent_step(None, FAKE, None) == -1
+
+
+def test_fused_stabilizer_field(lib):
+    # ASYM only, modes 0..2; checked before the workspace
+    asym = dict(variant=4, j=FAKE, eta=FAKE)
+    assert call_chunk(lib, good_args(**asym, stabilize=1)) == -3
+    assert call_chunk(lib, good_args(**asym, stabilize=2)) == -3
+    assert call_chunk(lib, good_args(**asym, stabilize=3), FAKE, 1 << 40) == -1
+    assert call_chunk(lib, good_args(**asym, stabilize=-1), FAKE, 1 << 40) == -1
+    assert call_chunk(lib, good_args(stabilize=1), FAKE, 1 << 40) == -1
+    assert lib.gdn_recurrent_step(ctypes.byref(good_args(stabilize=2)), FAKE, None) == -1
+    assert lib.gdn_workspace_bytes(ctypes.byref(good_args(**asym, stabilize=1))) == \
+        lib.gdn_workspace_bytes(ctypes.byref(good_args(**asym)))
 
 
 def test_stabilize_checks(lib):

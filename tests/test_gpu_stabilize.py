@@ -139,3 +139,72 @@ def test_stabilized_forward(mode, dt, dk, chunk):
         e2, em = oracle.rel_l2(host(x), r), oracle.max_rel(host(x), r)
         print(mode, dt, name, f"rel_l2={e2:.2e} max_rel={em:.2e}", flush=True)
         assert e2 <= tol["rel_l2"] and em <= tol["max_rel"], (name, e2, em)
+
+
+# ---- the stabiliser applied inside the forward passes (gdn_args.stabilize) --------
+def _oracle_stabilized(mode, inp):
+    ref_in = dict(inp)
+    ref_in["alpha" if mode == "clip_decay" else "j"] = _oracle_out(mode, inp)
+    return ref_in
+
+
+def _check_pair(o, S, o_ref, S_ref, dt, what):
+    from gpu_util import TOL, host
+    tol = TOL[dt]
+    for name, x, r in (("o", o, o_ref), ("S", S, S_ref)):
+        e2, em = oracle.rel_l2(host(x), r), oracle.max_rel(host(x), r)
+        print(what, name, f"rel_l2={e2:.2e} max_rel={em:.2e}", flush=True)
+        assert e2 <= tol["rel_l2"] and em <= tol["max_rel"], (what, name, e2, em)
+
+
+@pytest.mark.parametrize("dt,dk,chunk", [("f32", 16, 16), ("f32", 64, 32), ("bf16", 32, 32),
+                                         ("bf16", 64, 64), ("bf16", 128, 64)])
+@pytest.mark.parametrize("mode", ["clip_decay", "project_j"])
+def test_fused_chunk_forward(mode, dt, dk, chunk):
+    """gdn_chunk_fwd with the stabiliser inside the pass (the bf16, dk 128, chunk 64
+    case runs the two-workgroup prepare kernel and the row-split scan) against the
+    oracle's stabiliser followed by the oracle's recurrence."""
+    import gated_delta_rule_69_amd as gdn
+    from gpu_util import state_to_dev, to_dev
+    inp, _ = mixed_inputs(2, 150, 3, dk, dt, seed=23)
+    s0 = gdn_inputs.make_state(2, 3, dk, dk, seed=8)
+    o_ref, S_ref = oracle.forward(_oracle_stabilized(mode, inp), s0)
+    d = to_dev(inp)
+    o, S = gdn.gdn_chunk_fwd("asym", d["q"], d["k"], d["v"], d["alpha"], None, chunk=chunk,
+                             j=d["j"], eta=d["eta"], s0=state_to_dev(s0), stabilize=mode)
+    _check_pair(o, S, o_ref, S_ref, dt, f"fused chunk {mode} {dt} dk={dk} C={chunk}")
+
+
+@pytest.mark.parametrize("dt,dk", [("f32", 16), ("f32", 64), ("bf16", 128)])
+@pytest.mark.parametrize("mode", ["clip_decay", "project_j"])
+def test_fused_recurrent(mode, dt, dk):
+    """gdn_recurrent_step with the stabiliser (dk 16 runs the 16-column kernel, the
+    others the 32-column one)."""
+    import gated_delta_rule_69_amd as gdn
+    from gpu_util import state_to_dev, to_dev
+    inp, _ = mixed_inputs(2, 40, 2, dk, dt, seed=31)
+    s0 = gdn_inputs.make_state(2, 2, dk, dk, seed=9)
+    o_ref, S_ref = oracle.forward(_oracle_stabilized(mode, inp), s0)
+    d = to_dev(inp)
+    state = state_to_dev(s0).clone()
+    o = gdn.gdn_recurrent_step("asym", d["q"], d["k"], d["v"], d["alpha"], None, state=state,
+                               j=d["j"], eta=d["eta"], stabilize=mode)
+    _check_pair(o, state, o_ref, S_ref, dt, f"fused recurrent {mode} {dt} dk={dk}")
+
+
+def test_fused_equals_separate_pass_fp32():
+    """fp32: the fused pass and the separate pass followed by the plain forward agree
+    to rounding (the two compute the same coefficients in a different lane layout)."""
+    import gated_delta_rule_69_amd as gdn
+    from gpu_util import host, to_dev
+    inp, _ = mixed_inputs(1, 96, 4, 64, "f32", seed=2)
+    d = to_dev(inp)
+    for mode in ("clip_decay", "project_j"):
+        o1, S1 = gdn.gdn_chunk_fwd("asym", d["q"], d["k"], d["v"], d["alpha"], None, chunk=32,
+                                   j=d["j"], eta=d["eta"], stabilize=mode)
+        new = gdn.gdn_asym_stabilize(mode, d["k"], d["j"], d["alpha"], d["eta"])
+        al, jj = (new, d["j"]) if mode == "clip_decay" else (d["alpha"], new)
+        o2, S2 = gdn.gdn_chunk_fwd("asym", d["q"], d["k"], d["v"], al, None, chunk=32, j=jj,
+                                   eta=d["eta"])
+        assert oracle.rel_l2(host(o1), host(o2)) <= 1e-6
+        assert oracle.rel_l2(host(S1), host(S2)) <= 1e-6
