@@ -72,6 +72,25 @@ def test_config4_asym_cut():
     _run_and_check(inp, chunk=gdn_inputs.CONFIGS[4]["chunk"], what="config4 (B=1, T=512)")
 
 
+@pytest.mark.parametrize("idx,pairs", [(3, ((0, 2), (3, 7))), (4, ((0, 5), (7, 30)))])
+def test_config_full_size_sampled_heads(idx, pairs):
+    """DeltaProduct (B4 H8 T8192, n_h 2) and GDN2 (B8 H32 T2048 fp32) at their full
+    shapes, in the launch configuration of bench.py --configs; the oracle checks two
+    (batch, head) pairs of each."""
+    from gpu_util import host, run_chunk
+    cfg = gdn_inputs.CONFIGS[idx]
+    inp = gdn_inputs.config_inputs(idx)
+    o, S = run_chunk(inp, chunk=cfg["chunk"])
+    torch.cuda.synchronize()
+    for b, h in pairs:
+        sub = {k: (v[b:b + 1, :, h:h + 1] if isinstance(v, np.ndarray) else v) for k, v in inp.items()}
+        sub["B"], sub["H"] = 1, 1
+        o_ref, S_ref = oracle.forward(sub)
+        _check(o[b:b + 1, :, h:h + 1], S[b:b + 1, h:h + 1], o_ref, S_ref, cfg["dtype"],
+               f"config{idx} b{b} h{h}")
+    assert np.isfinite(host(o)).all() and np.isfinite(host(S)).all()
+
+
 # ---- variants, dtypes, shapes, chunk sizes --------------------------------------
 
 CASES = [
