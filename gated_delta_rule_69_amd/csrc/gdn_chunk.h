@@ -1194,22 +1194,28 @@ struct alignas(16) PrepLds2 {
   float red[kWaves];
 };
 
-// Whether chunk_prep2_kernel covers a problem (bf16, dk = dv = 128, chunk 64, one
-// step per token, no separate value-side beta).
+// Whether chunk_prep2_kernel covers a problem (bf16, dk = dv = 128, chunk 64, no
+// separate value-side beta; DeltaProduct with n_h = 1, 2 or 4, the step counts a
+// 64-step chunk with at least 16 output rows allows).
 inline bool prep2_covers(const Problem& p) {
   return p.dtype == GDN_DTYPE_BF16 && p.dk == 128 && p.dv == 128 && p.chunk == 64 &&
-         !(p.variant == GDN_VARIANT_DELTAPRODUCT && p.n_h > 1) &&
+         (p.n_h == 1 || p.n_h == 2 || p.n_h == 4) &&
          !(p.variant == GDN_VARIANT_FG2 && p.beta_v != nullptr);
 }
 
 // STAB: the GDN2 stabiliser mode applied to the rows (ASYM only; a template
 // parameter so that the other instantiations carry none of its registers).
-template <int V, int STAB>
+// NH: steps per token (DeltaProduct's n_h; 1 otherwise). With NH > 1 the rows are
+// Householder sub-steps: k, v and beta come from the step, the gate from the token
+// at its first step, and every NH-th row (the token's last step) is an output row.
+template <int V, int STAB, int NH>
 __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, unsigned char* __restrict__ ws,
                                                                      ChunkLayout L, int want_out) {
   using In = uint16_t;
   constexpr int DK = 128, C = 64, NT = 4, KB = 4, CK = 2, CT = 8, VT = 8;
   constexpr bool DP = V == GDN_VARIANT_DELTAPRODUCT;
+  static_assert(NH == 1 || DP, "several steps per token: DeltaProduct only");
+  constexpr int TPC = C / NH;  // tokens per chunk
   constexpr bool CH_ALPHA = V == GDN_VARIANT_FG2 || V == GDN_VARIANT_KDA || V == GDN_VARIANT_ASYM;
   constexpr bool CH_BJ = V == GDN_VARIANT_FG2 || V == GDN_VARIANT_ASYM;  // per-channel beta / j
   using Sm = PrepLds2;
@@ -1247,23 +1253,32 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
   const In* etg = static_cast<const In*>(p.eta);
   auto ld = [](const In* x) { return IO<In>::ld(x); };
 
-  // first token-head row (b, token n C, h) of an item, chunk-major order
+  // first token-head row (b, token n TPC, h) of an item, chunk-major order
   struct Item {
     int n, bh;
-    int64_t th0;  // (b T + n C) H + h
+    int64_t th0;  // (b T + n TPC) H + h
   };
   auto item_of = [&](int item) __attribute__((always_inline)) -> Item {
     Item it;
     it.n = item / BH;
     it.bh = item - it.n * BH;
     const int b = it.bh / H, h = it.bh - b * H;
-    it.th0 = (int64_t(b) * T + int64_t(it.n) * C) * H + h;
+    it.th0 = (int64_t(b) * T + int64_t(it.n) * TPC) * H + h;
     return it;
   };
   // token-head row of step row rr (clamped to the sequence's last token)
   auto th_of = [&](const Item& it, int rr) __attribute__((always_inline)) -> int64_t {
-    const int64_t last = T - 1 - int64_t(it.n) * C;  // >= 0
-    return it.th0 + min(int64_t(rr), last) * H;
+    const int64_t last = T - 1 - int64_t(it.n) * TPC;  // >= 0
+    return it.th0 + min(int64_t(rr / NH), last) * H;
+  };
+  // row of step rr in the per-step arrays ([B, T, H, NH, ...]; clamped to the last step)
+  auto step_of = [&](const Item& it, int rr) __attribute__((always_inline)) -> int64_t {
+    if constexpr (NH == 1) {
+      return th_of(it, rr);
+    } else {
+      const int64_t rel = min(int64_t(rr), p.steps - 1 - int64_t(it.n) * C);  // >= 0
+      return (it.th0 + (rel / NH) * H) * NH + rel % NH;
+    }
   };
 
   // This lane's row of an item's inputs in 16-byte groups (group u: channels
@@ -1273,13 +1288,15 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
   };
   // parts: 1 key, 2 values, 4 query, 8 decay, 16 beta / j
   auto load_raw = [&](const Item& it, Raw& x, int parts) __attribute__((always_inline)) {
-    const int64_t off = th_of(it, r) * DK + 8 * lg;
+    const int64_t off = th_of(it, r) * DK + 8 * lg;                       // token rows
+    const int64_t offs = NH == 1 ? off : step_of(it, r) * DK + 8 * lg;   // step rows
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       auto ld16 = [&](const In* base) { return *reinterpret_cast<const uint4*>(base + off + 32 * u); };
-      if (parts & 1) x.k[u] = ld16(kg);
-      if (parts & 2) x.v[u] = ld16(vg);
-      if ((parts & 4) && want_out) x.q[u] = ld16(qg);
+      auto ld16s = [&](const In* base) { return *reinterpret_cast<const uint4*>(base + offs + 32 * u); };
+      if (parts & 1) x.k[u] = ld16s(kg);
+      if (parts & 2) x.v[u] = ld16s(vg);
+      if ((parts & 4) && want_out && (NH == 1 || r % NH == NH - 1)) x.q[u] = ld16(qg);  // output rows
       if constexpr (CH_ALPHA)
         if (parts & 8) x.a[u] = ld16(alg);
       if constexpr (V == GDN_VARIANT_FG2)
@@ -1300,7 +1317,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
     Scal s{1.0f, 0.0f, 0.0f};
     const int64_t th = th_of(it, r);
     if constexpr (!CH_ALPHA) s.alpha = ld(alg + th);
-    if constexpr (V == GDN_VARIANT_KDA || V == GDN_VARIANT_GDN || DP) s.beta = ld(beg + th);
+    if constexpr (V == GDN_VARIANT_KDA || V == GDN_VARIANT_GDN) s.beta = ld(beg + th);
+    if constexpr (DP) s.beta = ld(beg + step_of(it, r));
     if constexpr (V == GDN_VARIANT_ASYM) s.eta = ld(etg + th);
     return s;
   };
@@ -1330,6 +1348,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
   // the first item's inputs; later items load during the one before
   Scal scal{1.0f, 0.0f, 0.0f};
   Raw raw;
+  if constexpr (NH > 1) {  // only output rows load q
+#pragma unroll
+    for (int u = 0; u < 4; ++u) raw.q[u] = make_uint4(0u, 0u, 0u, 0u);
+  }
   if (int(blockIdx.x) < total) {
     const Item it = item_of(blockIdx.x);
     load_raw(it, raw, 31);
@@ -1342,6 +1364,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
     const bool has_next = item + int(gridDim.x) < total;
     const Item nx = item_of(has_next ? item + int(gridDim.x) : item);
     const bool valid = int64_t(it.n) * C + r < p.steps;
+    const bool orow = NH == 1 || r % NH == NH - 1;  // the token's last step: an output row
+    const int ro = r / NH;                           // its output row
     unsigned char* rec = ws + (size_t(it.bh) * size_t(NC) + size_t(it.n)) * L.bytes;
     _Float16* W_g = reinterpret_cast<_Float16*>(rec + L.off_W);
     _Float16* AT_g = reinterpret_cast<_Float16*>(rec + L.off_AT);
@@ -1363,7 +1387,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
     } else if constexpr (DP) {
       bscal = sc.beta;
       wscal = sc.beta;
-      glog = __builtin_amdgcn_logf(sc.alpha);
+      glog = (NH == 1 || r % NH == 0) ? __builtin_amdgcn_logf(sc.alpha) : 0.0f;  // gate at the first step
     } else if constexpr (V == GDN_VARIANT_ASYM) {
       bscal = sc.eta;
       wscal = sc.eta;
@@ -1416,7 +1440,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
     auto bits_max = [](ushort2v m) __attribute__((always_inline)) {
       return __uint_as_float(uint32_t(m.x > m.y ? m.x : m.y) << 16);
     };
-    const float qmax = valid ? bits_max(qm2) : 0.0f;
+    const float qmax = (valid && orow) ? bits_max(qm2) : 0.0f;
     float wmax = bits_max(vm2) * (V == GDN_VARIANT_FG2 ? (valid ? __builtin_amdgcn_sqrtf(bits_max(bm2)) : 0.0f)
                                                          : fabsf(wscal));
     // inclusive scan of the log decay over the tile's 16 rows, then tile totals
@@ -1461,7 +1485,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
       wsc = pow2_scale_for(m);
     }
     if (tid == 0) winv_g[0] = 1.0f / wsc;
-    if (want_out && lg == 0) qinv_g[r] = 1.0f / qsc;
+    if (want_out && orow && lg == 0) qinv_g[ro] = 1.0f / qsc;
     wg_barrier();
 
     // ---- phase 2: decayed operands and written values of this wave's rows, one
@@ -1484,7 +1508,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
       const uint4 kr = raw.k[u], vr = raw.v[u];
       uint4 br = {}, qr = {};
       if constexpr (CH_BJ) br = raw.b[u];
-      if (want_out && valid) qr = raw.q[u];
+      if (want_out && valid && orow) qr = raw.q[u];
       half8 xbt, xat, xv;
       H8 hi, lo, qp;
 #pragma unroll
@@ -1524,8 +1548,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
       }
       *reinterpret_cast<uint4*>(&sm.ra.am.hi[r][c0]) = hi.q;
       *reinterpret_cast<uint4*>(&sm.ra.am.lo[r][c0]) = lo.q;
-      if (want_out)
-        *reinterpret_cast<uint4*>(Q_g + ((((r >> 4) * KB + u) * 64 + (r & 15) + 16 * lg) * 8)) = qp.q;
+      if (want_out && orow)
+        *reinterpret_cast<uint4*>(Q_g + ((((ro >> 4) * KB + u) * 64 + (ro & 15) + 16 * lg) * 8)) = qp.q;
       // B+ and A^ of the group transposed by MFMA: lane (li, lg) then holds steps
       // 16 wave + 4 lg .. of channel 32 u + 16 h + li
 #pragma unroll
@@ -1585,14 +1609,14 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
 #pragma unroll
       for (int J = 0; J < NT; ++J) preg[J] = mma_pair_bf16(al[J].b, qmh8[u].b, preg[J]);
     }
-    if (want_out) {  // output rows are this wave's own rows (q scale qsc)
+    if (want_out && orow) {  // output rows are this wave's own rows (q scale qsc)
 #pragma unroll
       for (int J = 0; J < NT; ++J) {
         const int s0 = 16 * J + 4 * lg;
         H8 h8;
 #pragma unroll
         for (int e = 0; e < 4; ++e) h8.h[e] = (_Float16)((s0 + e <= r) ? preg[J][e] * qsc : 0.0f);
-        *reinterpret_cast<uint2*>(P_g + p_frag(r, J)) = h8.u[0];
+        *reinterpret_cast<uint2*>(P_g + p_frag(ro, J)) = h8.u[0];
       }
     }
     if (has_next) load_raw(nx, raw, 4 | 16);
@@ -1723,20 +1747,26 @@ template <typename In, int DK, int C, int V, bool DPV>
 int launch_prep_t(const Problem& p, void* ws, bool want_out, hipStream_t s) {
   const ChunkLayout L = chunk_layout(p);
   const int64_t items = p.nchunks * p.B * p.H;
-  if constexpr (std::is_same<In, uint16_t>::value && DK == 128 && C == 64 && !DPV) {
+  if constexpr (std::is_same<In, uint16_t>::value && DK == 128 && C == 64) {
     if (prep2_covers(p)) {  // two workgroups per CU
       const int64_t grid = std::min<int64_t>(items, 2 * int64_t(device_cus()));
       unsigned char* w = static_cast<unsigned char*>(ws);
       const int wo = want_out ? 1 : 0;
-      if constexpr (V == GDN_VARIANT_ASYM) {
-        if (p.stabilize == GDN_STABILIZE_CLIP_DECAY)
-          chunk_prep2_kernel<V, 1><<<dim3(unsigned(grid)), kThreads, 0, s>>>(p, w, L, wo);
-        else if (p.stabilize == GDN_STABILIZE_PROJECT_J)
-          chunk_prep2_kernel<V, 2><<<dim3(unsigned(grid)), kThreads, 0, s>>>(p, w, L, wo);
+      const dim3 g = dim3(unsigned(grid));
+      if constexpr (DPV) {
+        if (p.n_h == 2)
+          chunk_prep2_kernel<V, 0, 2><<<g, kThreads, 0, s>>>(p, w, L, wo);
         else
-          chunk_prep2_kernel<V, 0><<<dim3(unsigned(grid)), kThreads, 0, s>>>(p, w, L, wo);
+          chunk_prep2_kernel<V, 0, 4><<<g, kThreads, 0, s>>>(p, w, L, wo);
+      } else if constexpr (V == GDN_VARIANT_ASYM) {
+        if (p.stabilize == GDN_STABILIZE_CLIP_DECAY)
+          chunk_prep2_kernel<V, 1, 1><<<g, kThreads, 0, s>>>(p, w, L, wo);
+        else if (p.stabilize == GDN_STABILIZE_PROJECT_J)
+          chunk_prep2_kernel<V, 2, 1><<<g, kThreads, 0, s>>>(p, w, L, wo);
+        else
+          chunk_prep2_kernel<V, 0, 1><<<g, kThreads, 0, s>>>(p, w, L, wo);
       } else {
-        chunk_prep2_kernel<V, 0><<<dim3(unsigned(grid)), kThreads, 0, s>>>(p, w, L, wo);
+        chunk_prep2_kernel<V, 0, 1><<<g, kThreads, 0, s>>>(p, w, L, wo);
       }
       return int(hipGetLastError());
     }

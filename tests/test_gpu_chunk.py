@@ -121,6 +121,10 @@ CASES = [
     ("gdn", "bf16", 2, 150, 2, 128, 16, 1, 64),
     ("deltaproduct", "bf16", 1, 100, 2, 128, 64, 4, 64),
     ("asym", "bf16", 1, 190, 3, 128, 64, 1, 64),
+    # bf16, dk = dv = 128, chunk 64, DeltaProduct with 2 or 4 steps per token (ragged
+    # ends): two-workgroup prepare kernel with multi-step rows
+    ("deltaproduct", "bf16", 2, 77, 2, 128, 128, 4, 64),
+    ("deltaproduct", "bf16", 1, 161, 3, 128, 128, 2, 64),
     # bf16, dk = dv = 128, chunk 64, one step per token: two-workgroup prepare kernel
     ("kda", "bf16", 2, 170, 2, 128, 128, 1, 64),
     ("deltaproduct", "bf16", 1, 200, 2, 128, 128, 1, 64),
