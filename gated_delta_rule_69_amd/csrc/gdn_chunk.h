@@ -268,10 +268,19 @@ struct alignas(16) PrepLds {
   float red[kWaves];
 };
 
+// Waves per SIMD (= workgroups per CU) chunk_prep_kernel is compiled for: three for
+// fp32 rows of 64 channels in chunks of up to 32 steps (at most 168 registers a lane,
+// 48 KB of LDS a workgroup), which hides more of its load latency than two; one
+// (no register cap) otherwise.
+template <typename In, int DK, int C>
+constexpr int prep_occupancy() {
+  return (std::is_same<In, float>::value && DK == 64 && C <= 32) ? 3 : 1;
+}
+
 // V: the variant (gdn_variant); DPV: DeltaProduct with n_h >= 2 (output rows are
 // every n_h-th step row).
 template <typename In, int DK, int C, int V, bool DPV>
-__global__ __launch_bounds__(kThreads) void chunk_prep_kernel(Problem p, unsigned char* __restrict__ ws,
+__global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk_prep_kernel(Problem p, unsigned char* __restrict__ ws,
                                                               ChunkLayout L, int want_out) {
   constexpr bool F16 = std::is_same<In, uint16_t>::value;
   constexpr bool DP = V == GDN_VARIANT_DELTAPRODUCT;
@@ -1772,7 +1781,9 @@ int launch_prep_t(const Problem& p, void* ws, bool want_out, hipStream_t s) {
     }
   }
   constexpr size_t lds = sizeof(PrepLds<std::is_same<In, uint16_t>::value, DK, C, DPV>);
-  const int per_cu = lds <= 40 * 1024 ? 4 : lds <= 80 * 1024 ? 2 : 1;
+  constexpr int occ = prep_occupancy<In, DK, C>();
+  static_assert(occ == 1 || occ * lds <= 160 * 1024, "LDS of the intended occupancy");
+  const int per_cu = occ > 1 ? occ : lds <= 40 * 1024 ? 4 : lds <= 80 * 1024 ? 2 : 1;
   const int64_t grid = std::min<int64_t>(items, int64_t(device_cus()) * per_cu);
   chunk_prep_kernel<In, DK, C, V, DPV><<<dim3(unsigned(grid)), kThreads, 0, s>>>(
       p, static_cast<unsigned char*>(ws), L, want_out ? 1 : 0);
