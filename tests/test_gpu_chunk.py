@@ -241,3 +241,53 @@ def test_bitwise_determinism():
     o2, S2 = run_chunk(inp, chunk=64)
     np.testing.assert_array_equal(host(o1), host(o2))
     np.testing.assert_array_equal(host(S1), host(S2))
+
+
+# ---- degenerate gates and the largest head count ----------------------------------
+
+def test_no_write_keeps_decayed_state():
+    """beta = 0: nothing is written or erased, so S_T = Diag(prod_t alpha_t) S_0 and
+    o_t = S_t^T q_t (closed form, float64)."""
+    from gpu_util import host, run_chunk
+    inp = gdn_inputs.make_inputs("fg2", 1, 130, 2, 64, 64, dtype="f32", seed=71)
+    inp["beta"] = np.zeros_like(inp["beta"])
+    s0 = gdn_inputs.make_state(1, 2, 64, 64, seed=71, scale=1.0)
+    o, S = run_chunk(inp, s0, chunk=32)
+    al = inp["alpha"].astype(np.float64)                   # [1, T, H, dk]
+    cum = np.cumprod(al, axis=1)                           # decay through token t
+    St = cum[0][:, :, :, None] * s0[0][None].astype(np.float64)   # [T, H, dk, dv]
+    o_ref = np.einsum("thkv,thk->thv", St, inp["q"][0].astype(np.float64))[None]
+    assert oracle.rel_l2(host(S), St[-1][None]) <= 1e-5
+    assert oracle.rel_l2(host(o), o_ref) <= 1e-5
+
+
+@pytest.mark.parametrize("variant", ["fg2", "kda"])
+def test_full_write_recalls_the_value(variant):
+    """alpha = 1, beta = 1 and unit keys: each step replaces the value stored along k_t,
+    so reading with q_t = k_t returns v_t exactly (the delta rule's defining case)."""
+    from gpu_util import host, run_chunk
+    inp = gdn_inputs.make_inputs(variant, 1, 100, 2, 32, 32, dtype="f32", seed=72)
+    inp["alpha"] = np.ones_like(inp["alpha"])
+    inp["beta"] = np.ones_like(inp["beta"])
+    inp["q"] = inp["k"].copy()
+    s0 = gdn_inputs.make_state(1, 2, 32, 32, seed=72)
+    o, _ = run_chunk(inp, s0, chunk=32)
+    assert oracle.rel_l2(host(o), inp["v"].astype(np.float64)) <= 1e-5
+
+
+def test_largest_head_count():
+    """B * H = 65536 heads (H at its limit) with a ragged two-chunk sequence: the grids
+    of the prepare and scan kernels run past 65,535 workgroups; sampled heads against
+    the oracle, the recurrent path against the chunked one."""
+    from gpu_util import host, run_chunk, run_recurrent
+    inp = gdn_inputs.make_inputs("fg2", 1, 20, 65536, 16, 16, dtype="f32", seed=73)
+    o, S = run_chunk(inp, chunk=16)
+    o2, S2 = run_recurrent(inp)
+    torch.cuda.synchronize()
+    for h in (0, 40961, 65535):
+        sub = {k: (v[:, :, h:h + 1] if isinstance(v, np.ndarray) else v) for k, v in inp.items()}
+        sub["H"] = 1
+        o_ref, S_ref = oracle.forward(sub)
+        _check(o[:, :, h:h + 1], S[:, h:h + 1], o_ref, S_ref, "f32", f"head {h} of 65536")
+    assert oracle.rel_l2(host(o2), host(o)) <= 1e-5
+    assert oracle.rel_l2(host(S2), host(S)) <= 1e-5

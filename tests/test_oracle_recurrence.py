@@ -236,3 +236,30 @@ def test_split_sequence_state_passing():
     o2, S2 = oracle.forward(gdn_inputs.slice_tokens(inp, 5, 13), S1)
     np.testing.assert_allclose(np.concatenate([o1, o2], axis=1), o, rtol=1e-14, atol=1e-14)
     np.testing.assert_allclose(S2, S, rtol=1e-14, atol=1e-14)
+
+
+def test_no_write_is_pure_decay():
+    """beta = 0: S_t = Diag(prod alpha) S_0 and o_t = S_t^T q_t, channel by channel."""
+    inp = _small("fg2", 15, T=12, d=5, H=2)
+    inp["beta"] = np.zeros_like(inp["beta"])
+    s0 = np.random.default_rng(15).standard_normal((1, 2, 5, 5))
+    o, S = oracle.forward(inp, s0)
+    cum = np.cumprod(np.asarray(inp["alpha"], np.float64), axis=1)[0]      # [T, H, dk]
+    St = cum[:, :, :, None] * s0[0][None]
+    np.testing.assert_allclose(S[0], St[-1], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(o[0], np.einsum("thkv,thk->thv", St, np.asarray(inp["q"], np.float64)[0]),
+                               rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("variant", ["fg2", "kda"])
+def test_full_write_recalls_the_value(variant):
+    """alpha = 1, beta = 1, unit keys and q_t = k_t: o_t = v_t for any earlier state."""
+    inp = _small(variant, 16, T=9, d=6, H=2)
+    inp["alpha"] = np.ones_like(inp["alpha"])
+    inp["beta"] = np.ones_like(inp["beta"])
+    k = np.asarray(inp["k"], np.float64)
+    inp["k"] = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    inp["q"] = inp["k"].copy()
+    s0 = np.random.default_rng(16).standard_normal((1, 2, 6, 6))
+    o, _ = oracle.forward(inp, s0)
+    np.testing.assert_allclose(o, np.asarray(inp["v"], np.float64), rtol=1e-12, atol=1e-12)
