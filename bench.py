@@ -82,6 +82,17 @@ def _oracle_one(args):
         return b, h, o[0, :, 0].astype(np.float32), time.perf_counter() - t0
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, T_sample):
     global _CPU_INP
     _CPU_INP = inp
@@ -97,7 +108,7 @@ def cpu_baseline(inp, T_sample):
         res = pool.map(_oracle_one, [(b, h, T_sample) for b, h in pairs])
     wall = time.perf_counter() - t0
     tokens = len(pairs) * T_sample / inp["H"]     # metric tokens carry all H heads
-    return dict(value=tokens / wall, unit="tokens/s", cores=workers, kind="oracle",
+    return dict(value=tokens / wall, unit="tokens/s", cores=workers, kind="oracle", cpu_model=cpu_model(),
                 sample=f"all {len(pairs)} (batch, head) sequences of the workload, first {T_sample} "
                        f"of {inp['T']} tokens each (B*{T_sample} metric tokens); float64 token "
                        f"loop, {workers} worker processes, one thread each; wall {wall:.1f} s"), res
