@@ -33,12 +33,15 @@ int validate(const gdn_args* a, Entry e, Problem* out) {
     return GDN_ERR_ARG;
   }
   const bool chunked = e != Entry::Recurrent && e != Entry::Stabilize;
+  int chunk = a->chunk;
   if (chunked) {
-    if (a->chunk != 16 && a->chunk != 32 && a->chunk != 64) return GDN_ERR_UNSUPPORTED;
-    if (a->chunk % a->n_h != 0) return GDN_ERR_UNSUPPORTED;
-    if (a->chunk / a->n_h < 16) return GDN_ERR_UNSUPPORTED;  // one 16-row output tile at least
-    // fp32 tiles of a 64-step chunk with 128 key channels exceed the 160 KB LDS
-    if (a->dtype == GDN_DTYPE_F32 && a->dk == 128 && a->chunk == 64) return GDN_ERR_UNSUPPORTED;
+    if (chunk != 16 && chunk != 32 && chunk != 64) return GDN_ERR_UNSUPPORTED;
+    // fp32 tiles of a 64-step chunk with 128 key channels exceed the 160 KB of LDS of
+    // the scan's double-buffered record image: such calls run with 32-step chunks,
+    // the same recurrence up to rounding
+    if (a->dtype == GDN_DTYPE_F32 && a->dk == 128 && chunk == 64) chunk = 32;
+    if (chunk % a->n_h != 0) return GDN_ERR_UNSUPPORTED;
+    if (chunk / a->n_h < 16) return GDN_ERR_UNSUPPORTED;  // one 16-row output tile at least
   }
   if (a->variant == GDN_VARIANT_FG2 && a->beta_v == nullptr && a->dk != a->dv)
     return GDN_ERR_ARG;  // one beta vector scales both key and value channels
@@ -75,7 +78,7 @@ int validate(const gdn_args* a, Entry e, Problem* out) {
   }
 
   if (chunked) {
-    const int64_t nchunks = (a->T * a->n_h + a->chunk - 1) / a->chunk;
+    const int64_t nchunks = (a->T * a->n_h + chunk - 1) / chunk;
     if (nchunks * a->B * a->H >= (int64_t(1) << 31)) return GDN_ERR_UNSUPPORTED;  // grid size
   }
 
@@ -88,7 +91,7 @@ int validate(const gdn_args* a, Entry e, Problem* out) {
     p.H = a->H;
     p.dk = a->dk;
     p.dv = a->dv;
-    p.chunk = a->chunk;
+    p.chunk = chunk;
     p.n_h = a->n_h;
     p.stabilize = e == Entry::Stabilize ? 0 : a->stabilize;
     p.q = a->q;
@@ -104,8 +107,8 @@ int validate(const gdn_args* a, Entry e, Problem* out) {
     p.o = a->o;
     p.steps = a->T * a->n_h;
     if (chunked) {
-      p.nchunks = (p.steps + a->chunk - 1) / a->chunk;
-      p.rows_out = a->chunk / a->n_h;
+      p.nchunks = (p.steps + chunk - 1) / chunk;
+      p.rows_out = chunk / a->n_h;
     } else {
       p.nchunks = 0;
       p.rows_out = 0;

@@ -89,7 +89,9 @@ typedef struct gdn_args {
   int32_t dtype;    /* enum gdn_dtype   */
   int64_t B, T, H;  /* batch, tokens (T >= 0), heads                          */
   int64_t dk, dv;   /* key and value head dims, each in {16, 32, 64, 128}     */
-  int32_t chunk;    /* chunk length C in {16, 32, 64} (chunked entry points) */
+  int32_t chunk;    /* chunk length C in {16, 32, 64} (chunked entry points);
+                       fp32 with dk = 128 runs 64 as 32 (same result up to
+                       rounding, workspace sized for 32)                      */
   int32_t n_h;      /* Householder steps per token (DELTAPRODUCT), else 1     */
   const void* q;
   const void* k;

@@ -146,6 +146,16 @@ def test_stabilize_checks(lib):
     assert lib.gdn_asym_stabilize(None, 1, FAKE, None) == -1
 
 
+def test_fp32_dk128_chunk64_runs_as_chunk32(lib):
+    f32 = dict(dtype=0, dk=128, dv=128)
+    w64 = lib.gdn_workspace_bytes(ctypes.byref(good_args(chunk=64, **f32)))
+    w32 = lib.gdn_workspace_bytes(ctypes.byref(good_args(chunk=32, **f32)))
+    assert w64 == w32 > 0
+    assert call_chunk(lib, good_args(chunk=64, **f32)) == -3     # valid: reaches the workspace check
+    # DeltaProduct with 4 steps a token would have 8 output rows a chunk: unsupported
+    assert call_chunk(lib, good_args(chunk=64, variant=3, n_h=4, **f32), FAKE, 1 << 40) == -2
+
+
 def test_workspace_bytes_grows_with_tokens(lib):
     small = lib.gdn_workspace_bytes(ctypes.byref(good_args(T=64)))
     big = lib.gdn_workspace_bytes(ctypes.byref(good_args(T=6400)))

@@ -99,6 +99,8 @@ CASES = [
     ("fg2", "f32", 2, 100, 2, 32, 32, 1, 32),
     ("fg2", "f32", 1, 90, 2, 16, 16, 1, 16),
     ("fg2", "f32", 1, 150, 2, 128, 128, 1, 32),
+    ("fg2", "f32", 1, 150, 2, 128, 128, 1, 64),          # runs with 32-step chunks
+    ("deltaproduct", "f32", 1, 70, 2, 128, 128, 2, 64),  # likewise
     ("fg2", "bf16", 1, 517, 3, 128, 128, 1, 64),
     ("fg2", "bf16", 2, 333, 2, 64, 64, 1, 32),
     ("fg2", "bf16", 1, 257, 2, 32, 32, 1, 16),
