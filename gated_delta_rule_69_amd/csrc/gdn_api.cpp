@@ -34,14 +34,17 @@ int validate(const gdn_args* a, Entry e, Problem* out) {
   }
   const bool chunked = e != Entry::Recurrent && e != Entry::Stabilize;
   int chunk = a->chunk;
+  // DeltaProduct with three Householder steps a token is laid out in chunks as four,
+  // the fourth an identity step, so that a chunk holds whole tokens
+  const int n_step = (chunked && a->n_h == 3) ? 4 : a->n_h;
   if (chunked) {
     if (chunk != 16 && chunk != 32 && chunk != 64) return GDN_ERR_UNSUPPORTED;
     // fp32 tiles of a 64-step chunk with 128 key channels exceed the 160 KB of LDS of
     // the scan's double-buffered record image: such calls run with 32-step chunks,
     // the same recurrence up to rounding
     if (a->dtype == GDN_DTYPE_F32 && a->dk == 128 && chunk == 64) chunk = 32;
-    if (chunk % a->n_h != 0) return GDN_ERR_UNSUPPORTED;
-    if (chunk / a->n_h < 16) return GDN_ERR_UNSUPPORTED;  // one 16-row output tile at least
+    if (chunk % n_step != 0) return GDN_ERR_UNSUPPORTED;
+    if (chunk / n_step < 16) return GDN_ERR_UNSUPPORTED;  // one 16-row output tile at least
   }
   if (a->variant == GDN_VARIANT_FG2 && a->beta_v == nullptr && a->dk != a->dv)
     return GDN_ERR_ARG;  // one beta vector scales both key and value channels
@@ -78,7 +81,7 @@ int validate(const gdn_args* a, Entry e, Problem* out) {
   }
 
   if (chunked) {
-    const int64_t nchunks = (a->T * a->n_h + chunk - 1) / chunk;
+    const int64_t nchunks = (a->T * n_step + chunk - 1) / chunk;
     if (nchunks * a->B * a->H >= (int64_t(1) << 31)) return GDN_ERR_UNSUPPORTED;  // grid size
   }
 
@@ -93,6 +96,7 @@ int validate(const gdn_args* a, Entry e, Problem* out) {
     p.dv = a->dv;
     p.chunk = chunk;
     p.n_h = a->n_h;
+    p.n_step = n_step;
     p.stabilize = e == Entry::Stabilize ? 0 : a->stabilize;
     p.q = a->q;
     p.k = a->k;
@@ -105,10 +109,10 @@ int validate(const gdn_args* a, Entry e, Problem* out) {
     p.s0 = a->s0;
     p.s_final = a->s_final;
     p.o = a->o;
-    p.steps = a->T * a->n_h;
+    p.steps = a->T * n_step;
     if (chunked) {
       p.nchunks = (p.steps + chunk - 1) / chunk;
-      p.rows_out = chunk / a->n_h;
+      p.rows_out = chunk / n_step;
     } else {
       p.nchunks = 0;
       p.rows_out = 0;

@@ -305,7 +305,7 @@ __global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
-  const int n_h = DPV ? p.n_h : 1;
+  const int n_h = DPV ? p.n_step : 1;  // steps a token takes in the chunk
   const int R = p.rows_out, RT = R / 16;
   const int dv = int(p.dv);
   const int NC = int(p.nchunks);
@@ -335,6 +335,7 @@ __global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk
     bool valid, out_row;
     int64_t th, vrow;
     int sub, ro;
+    bool pad;  // identity step of a padded token (beta = 0)
   };
   auto where = [&](int item) __attribute__((always_inline)) -> Where {
     Where w;
@@ -351,7 +352,8 @@ __global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk
       w.sub = int(vs - tok * n_h);
     }
     w.th = (int64_t(b) * p.T + tok) * H + h;
-    w.vrow = DP ? w.th * p.n_h + w.sub : w.th;
+    w.pad = w.sub >= p.n_h;
+    w.vrow = DP ? w.th * p.n_h + (w.pad ? p.n_h - 1 : w.sub) : w.th;
     w.out_row = want_out && owner && w.sub == n_h - 1;
     w.ro = DPV ? r / n_h : r;
     return w;
@@ -387,7 +389,7 @@ __global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk
           raw.s_eta = ld(etg + w.th);
         }
         if constexpr (V == GDN_VARIANT_KDA || V == GDN_VARIANT_GDN) raw.s_beta = ld(beg + w.th);
-        if constexpr (DP) raw.s_beta = ld(beg + w.vrow);
+        if constexpr (DP) raw.s_beta = w.pad ? 0.0f : ld(beg + w.vrow);
       }
       if ((all || part == 3) && w.out_row) ld_row(qg + w.th * DK, raw.q);
       const In* vrow = vg + w.vrow * dv;
@@ -487,7 +489,7 @@ __global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk
           seta = ld(etg + w.th);
         }
         if constexpr (V == GDN_VARIANT_KDA || V == GDN_VARIANT_GDN) sbt = ld(beg + w.th);
-        if constexpr (DP) sbt = ld(beg + w.vrow);
+        if constexpr (DP) sbt = w.pad ? 0.0f : ld(beg + w.vrow);
         if (w.out_row) load_row<F16, DK>(qg + w.th * DK, lg, qv);
       }
       if constexpr (V == GDN_VARIANT_ASYM) {
@@ -1208,7 +1210,7 @@ struct alignas(16) PrepLds2 {
 // 64-step chunk with at least 16 output rows allows).
 inline bool prep2_covers(const Problem& p) {
   return p.dtype == GDN_DTYPE_BF16 && p.dk == 128 && p.dv == 128 && p.chunk == 64 &&
-         (p.n_h == 1 || p.n_h == 2 || p.n_h == 4) &&
+         (p.n_step == 1 || p.n_step == 2 || p.n_step == 4) &&
          !(p.variant == GDN_VARIANT_FG2 && p.beta_v != nullptr);
 }
 
@@ -1280,13 +1282,14 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
     const int64_t last = T - 1 - int64_t(it.n) * TPC;  // >= 0
     return it.th0 + min(int64_t(rr / NH), last) * H;
   };
-  // row of step rr in the per-step arrays ([B, T, H, NH, ...]; clamped to the last step)
+  // row of step rr in the per-step arrays ([B, T, H, n_h, ...]; clamped to the last
+  // step; the identity step of a padded token reads the token's last real step)
   auto step_of = [&](const Item& it, int rr) __attribute__((always_inline)) -> int64_t {
     if constexpr (NH == 1) {
       return th_of(it, rr);
     } else {
       const int64_t rel = min(int64_t(rr), p.steps - 1 - int64_t(it.n) * C);  // >= 0
-      return (it.th0 + (rel / NH) * H) * NH + rel % NH;
+      return (it.th0 + (rel / NH) * H) * p.n_h + min(int(rel % NH), p.n_h - 1);
     }
   };
 
@@ -1327,7 +1330,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
     const int64_t th = th_of(it, r);
     if constexpr (!CH_ALPHA) s.alpha = ld(alg + th);
     if constexpr (V == GDN_VARIANT_KDA || V == GDN_VARIANT_GDN) s.beta = ld(beg + th);
-    if constexpr (DP) s.beta = ld(beg + step_of(it, r));
+    if constexpr (DP) s.beta = (NH > 1 && r % NH >= p.n_h) ? 0.0f : ld(beg + step_of(it, r));  // padding: identity
     if constexpr (V == GDN_VARIANT_ASYM) s.eta = ld(etg + th);
     return s;
   };
@@ -1763,7 +1766,7 @@ int launch_prep_t(const Problem& p, void* ws, bool want_out, hipStream_t s) {
       const int wo = want_out ? 1 : 0;
       const dim3 g = dim3(unsigned(grid));
       if constexpr (DPV) {
-        if (p.n_h == 2)
+        if (p.n_step == 2)
           chunk_prep2_kernel<V, 0, 2><<<g, kThreads, 0, s>>>(p, w, L, wo);
         else
           chunk_prep2_kernel<V, 0, 4><<<g, kThreads, 0, s>>>(p, w, L, wo);

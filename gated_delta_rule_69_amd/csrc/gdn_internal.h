@@ -15,6 +15,8 @@ struct Problem {
   int64_t B, T, H, dk, dv;
   int chunk;
   int n_h;
+  int n_step;     // steps a token takes in a chunk: n_h, or 4 for n_h = 3 (the fourth
+                  // an identity step: beta = 0 writes and erases nothing)
   int stabilize;  // ASYM: 0, or the gdn_stabilize_mode applied to each token's inputs
   const void* q;
   const void* k;
@@ -28,7 +30,7 @@ struct Problem {
   float* s_final;
   void* o;
   // chunk geometry (chunked entry points)
-  int64_t steps;     // virtual steps: T * n_h
+  int64_t steps;     // virtual steps: T * n_step (chunked), T * n_h (recurrent)
   int64_t nchunks;   // ceil(steps / chunk)
   int rows_out;      // output rows per chunk: chunk / n_h
 };

@@ -92,7 +92,9 @@ typedef struct gdn_args {
   int32_t chunk;    /* chunk length C in {16, 32, 64} (chunked entry points);
                        fp32 with dk = 128 runs 64 as 32 (same result up to
                        rounding, workspace sized for 32)                      */
-  int32_t n_h;      /* Householder steps per token (DELTAPRODUCT), else 1     */
+  int32_t n_h;      /* Householder steps per token (DELTAPRODUCT, 1..8), else 1;
+                       chunked entry points: chunk / n_h >= 16 with n_h = 3
+                       counted as 4 (a chunk holds whole tokens)              */
   const void* q;
   const void* k;
   const void* v;

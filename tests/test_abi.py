@@ -95,9 +95,13 @@ def test_variant_specific_rules(lib):
     assert call_chunk(lib, good_args(variant=1, beta_v=FAKE), FAKE, 1 << 40) == -1
     # ASYM needs j and eta
     assert call_chunk(lib, good_args(variant=4), FAKE, 1 << 40) == -1
-    # DeltaProduct: chunk must be a multiple of n_h with >= 16 output rows
+    # DeltaProduct: chunk must be a multiple of the steps a token takes in a chunk
+    # (n_h, or 4 for n_h = 3) with >= 16 output rows
     dp = dict(variant=3, n_h=3)
-    assert call_chunk(lib, good_args(**dp), FAKE, 1 << 40) == -2
+    assert call_chunk(lib, good_args(**dp)) == -3                        # 64 = 16 tokens x 4
+    assert call_chunk(lib, good_args(chunk=32, **dp), FAKE, 1 << 40) == -2  # 8 output rows
+    assert lib.gdn_workspace_bytes(ctypes.byref(good_args(**dp))) == \
+        lib.gdn_workspace_bytes(ctypes.byref(good_args(variant=3, n_h=4)))
     assert call_chunk(lib, good_args(variant=3, n_h=8), FAKE, 1 << 40) == -2
     assert call_chunk(lib, good_args(variant=3, n_h=9), FAKE, 1 << 40) == -2
     assert call_chunk(lib, good_args(variant=3, n_h=0), FAKE, 1 << 40) == -1

@@ -101,6 +101,8 @@ CASES = [
     ("fg2", "f32", 1, 150, 2, 128, 128, 1, 32),
     ("fg2", "f32", 1, 150, 2, 128, 128, 1, 64),          # runs with 32-step chunks
     ("deltaproduct", "f32", 1, 70, 2, 128, 128, 2, 64),  # likewise
+    ("deltaproduct", "f32", 1, 45, 2, 64, 32, 3, 64),     # 3 steps padded to 4
+    ("deltaproduct", "bf16", 2, 50, 2, 64, 64, 3, 64),
     ("fg2", "bf16", 1, 517, 3, 128, 128, 1, 64),
     ("fg2", "bf16", 2, 333, 2, 64, 64, 1, 32),
     ("fg2", "bf16", 1, 257, 2, 32, 32, 1, 16),
@@ -126,6 +128,7 @@ CASES = [
     # bf16, dk = dv = 128, chunk 64, DeltaProduct with 2 or 4 steps per token (ragged
     # ends): two-workgroup prepare kernel with multi-step rows
     ("deltaproduct", "bf16", 2, 77, 2, 128, 128, 4, 64),
+    ("deltaproduct", "bf16", 1, 90, 2, 128, 128, 3, 64),   # 3 steps padded to 4
     ("deltaproduct", "bf16", 1, 161, 3, 128, 128, 2, 64),
     # bf16, dk = dv = 128, chunk 64, one step per token: two-workgroup prepare kernel
     ("kda", "bf16", 2, 170, 2, 128, 128, 1, 64),
