@@ -323,10 +323,11 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(Problem p, const u
 // ---- kernel 2b: sequential scan, row-split waves (fragment-format records) ---------
 //
 // bf16 inputs, dk = 128, chunk 64. One workgroup per (batch*head, NB value
-// columns). Wave w owns rows 16w..16w+15 of U and O and rows 32w..32w+31 of the
-// workgroup's dk x NB state slice (fp32, MFMA accumulator layout). Its A operands
-// (its rows of W, Q+, A^^T and P, and its U~ tile) are read straight from the
-// record into registers one chunk ahead. The B operands, the state and U in fp16,
+// columns). State wave w owns rows 16w..16w+15 of U and rows 32w..32w+31 of the
+// workgroup's dk x NB state slice (fp32, MFMA accumulator layout); output wave w
+// owns rows 16w..16w+15 of O, computed beside the state chain. A operands (a
+// wave's rows of W, A^^T and its U~ tile; of Q+ and P for output waves) are read
+// straight from the record into registers one chunk ahead. The B operands, the state and U in fp16,
 // cross waves through LDS, transposed, each wave block with its own power-of-two
 // scale per column; a fragment is brought to the column's common (smallest) scale
 // by an exact power-of-two product before its MFMA. Two barriers per chunk.
@@ -334,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(Problem p, const u
 constexpr int kAhead = 2;
 
 template <int NCT>
-__global__ __launch_bounds__(kThreads + 64) void chunk_scan_rows_kernel(Problem p, const unsigned char* __restrict__ ws,
+__global__ __launch_bounds__(2 * kThreads + 64) void chunk_scan_rows_kernel(Problem p, const unsigned char* __restrict__ ws,
                                                                    ChunkLayout L, int want_out) {
   constexpr int DK = 128, C = 64;
   constexpr int NB = 16 * NCT;
@@ -372,35 +373,32 @@ __global__ __launch_bounds__(kThreads + 64) void chunk_scan_rows_kernel(Problem 
   const int b = bh / H, h = bh - b * H;
   const int NC = int(p.nchunks);
   const int R = p.rows_out;
-  const bool orows = want_out && wave < R / 16;
   uint16_t* o = static_cast<uint16_t*>(p.o);
   const int col_base = cb * NB;
 
   // A operands of one chunk, in two halves refilled for the next chunk as soon as
   // the current chunk's half is consumed (mid-step), so that one register set
-  // suffices: FA for U and the state part of O, FB for the state update and P U.
+  // suffices: FA for U, FB for the state update. The output waves hold FO.
   struct FragsA {
-    uint4 w[KU], q[KU];
+    uint4 w[KU];
     uint2 u[NCT];
     float winv;
   };
   struct FragsB {
-    uint4 at[SRT][CU], pp[CU];
+    uint4 at[SRT][CU];
     float4 gam[SRT];
+  };
+  struct FragsO {
+    uint4 q[KU], pp[CU];
     float4 qi;
   };
   auto rec_of = [&](int n) -> const unsigned char* { return ws + (size_t(bh) * size_t(NC) + size_t(n)) * L.bytes; };
   auto load_a = [&](int n, FragsA& f) __attribute__((always_inline)) {
     const unsigned char* rec = rec_of(n);
     const uint4* Wf = reinterpret_cast<const uint4*>(rec + L.off_W);
-    const uint4* Qf = reinterpret_cast<const uint4*>(rec + L.off_Q);
     const uint2* Uf = reinterpret_cast<const uint2*>(rec + L.off_UT);
 #pragma unroll
     for (int u = 0; u < KU; ++u) f.w[u] = Wf[(wave * KU + u) * 64 + lane];
-    // output operands are loaded by every wave (the record holds C rows of them),
-    // so that the number of loads in flight is the same on every path
-#pragma unroll
-    for (int u = 0; u < KU; ++u) f.q[u] = Qf[(wave * KU + u) * 64 + lane];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) f.u[ct] = Uf[(wave * dvt + cb * NCT + ct) * 64 + lane];
     f.winv = *reinterpret_cast<const float*>(rec + L.off_winv);
@@ -408,18 +406,25 @@ __global__ __launch_bounds__(kThreads + 64) void chunk_scan_rows_kernel(Problem 
   auto load_b = [&](int n, FragsB& f) __attribute__((always_inline)) {
     const unsigned char* rec = rec_of(n);
     const uint4* Af = reinterpret_cast<const uint4*>(rec + L.off_AT);
-    const uint4* Pf = reinterpret_cast<const uint4*>(rec + L.off_P);
     const float* gam = reinterpret_cast<const float*>(rec + L.off_gamma);
-    const float* qinv = reinterpret_cast<const float*>(rec + L.off_qinv);
 #pragma unroll
     for (int rt = 0; rt < SRT; ++rt)
 #pragma unroll
       for (int u = 0; u < CU; ++u) f.at[rt][u] = Af[((wave * SRT + rt) * CU + u) * 64 + lane];
 #pragma unroll
-    for (int u = 0; u < CU; ++u) f.pp[u] = Pf[(wave * CU + u) * 64 + lane];
-#pragma unroll
     for (int rt = 0; rt < SRT; ++rt) f.gam[rt] = *reinterpret_cast<const float4*>(gam + 32 * wave + 16 * rt + 4 * lg);
-    f.qi = *reinterpret_cast<const float4*>(qinv + 16 * wave + 4 * lg);
+  };
+  // output wave ow: its 16 output rows of Q+ and P, and their 1/qs
+  auto load_o = [&](int n, int ow, FragsO& f) __attribute__((always_inline)) {
+    const unsigned char* rec = rec_of(n);
+    const uint4* Qf = reinterpret_cast<const uint4*>(rec + L.off_Q);
+    const uint4* Pf = reinterpret_cast<const uint4*>(rec + L.off_P);
+    const float* qinv = reinterpret_cast<const float*>(rec + L.off_qinv);
+#pragma unroll
+    for (int u = 0; u < KU; ++u) f.q[u] = Qf[(ow * KU + u) * 64 + lane];
+#pragma unroll
+    for (int u = 0; u < CU; ++u) f.pp[u] = Pf[(ow * CU + u) * 64 + lane];
+    f.qi = *reinterpret_cast<const float4*>(qinv + 16 * ow + 4 * lg);
   };
 
   // ---- prefetch wave: pulls the records of chunk n + kAhead into L2 while the
@@ -462,6 +467,98 @@ __global__ __launch_bounds__(kThreads + 64) void chunk_scan_rows_kernel(Problem 
     return;
   }
 
+  // 1 / x for a power of two x in [2^-126, 2^126] (exact, one integer op)
+  auto inv_pow2 = [](float x) { return __uint_as_float(0x7f000000u - __float_as_uint(x)); };
+  // B-operand fragments of the state (k-block u) and of U (k-block u), brought to
+  // the column's common (smallest) scale; *inv receives 1 / that scale
+  auto state_frags = [&](half8 (&bv)[KU][NCT], float (&ics)[NCT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const float4 s4 = *reinterpret_cast<const float4*>(&ssc[16 * ct + li][0]);
+      const float cs = fminf(fminf(s4.x, s4.y), fminf(s4.z, s4.w));
+      const float f[4] = {cs * inv_pow2(s4.x), cs * inv_pow2(s4.y), cs * inv_pow2(s4.z), cs * inv_pow2(s4.w)};
+      ics[ct] = inv_pow2(cs);
+#pragma unroll
+      for (int u = 0; u < KU; ++u)
+        bv[u][ct] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&st[16 * ct + li][32 * u + 8 * lg])) *
+                    (_Float16)f[u];
+    }
+  };
+  // fragment u of a column holds U rows 32 u + 8 lg .. +7: wave block 2 u + lg / 2
+  auto u_frags = [&](half8 (&bv)[CU][NCT], float (&icu)[NCT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const float4 s4 = *reinterpret_cast<const float4*>(&usc[16 * ct + li][0]);
+      const float cu = fminf(fminf(s4.x, s4.y), fminf(s4.z, s4.w));
+      icu[ct] = inv_pow2(cu);
+      const float f[2] = {cu * inv_pow2((lg >> 1) ? s4.y : s4.x), cu * inv_pow2((lg >> 1) ? s4.w : s4.z)};
+#pragma unroll
+      for (int u = 0; u < CU; ++u)
+        bv[u][ct] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&ut[16 * ct + li][32 * u + 8 * lg])) *
+                    (_Float16)f[u];
+    }
+  };
+
+  // ---- output waves: O = (Q+ S + P U) / qs for 16 output rows each, off the state
+  // chain: the Q+ S part between the step's two barriers' first half (the state of
+  // the chunk start is in st until the second barrier), P U after the first barrier
+  // (U is in ut until the next step's first barrier). Rows are staged in this
+  // wave's own rows of ost and written with 16-byte stores.
+  if (wave > kWaves) {
+    const int ow = wave - kWaves - 1;
+    const bool act = want_out && ow < R / 16;
+    FragsO fo;
+    if (act && NC > 0) load_o(0, ow, fo);
+    __syncthreads();
+    for (int n = 0; n < NC; ++n) {
+      float4v oa[NCT], pa[NCT];
+      float ics[NCT];
+      if (act) {
+        half8 bv[KU][NCT];
+        state_frags(bv, ics);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) oa[ct] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int u = 0; u < KU; ++u)
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) oa[ct] = mma_pair_f16(__builtin_bit_cast(half8, fo.q[u]), bv[u][ct], oa[ct]);
+      }
+      __syncthreads();
+      if (act) {
+        half8 bu[CU][NCT];
+        float icu[NCT];
+        u_frags(bu, icu);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) pa[ct] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int u = 0; u < CU; ++u)
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) pa[ct] = mma_pair_f16(__builtin_bit_cast(half8, fo.pp[u]), bu[u][ct], pa[ct]);
+        const float qi[4] = {fo.qi.x, fo.qi.y, fo.qi.z, fo.qi.w};
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float ov = (oa[ct][e] * ics[ct] + pa[ct][e] * icu[ct]) * qi[e];
+            ost[16 * ow + 4 * lg + e][16 * ct + li] = __builtin_bit_cast(uint16_t, (__bf16)ov);
+          }
+        if (n + 1 < NC) load_o(n + 1, ow, fo);
+        // this wave's 16 rows: NB / 8 16-byte units each (LDS order within a wave)
+        constexpr int RU = NB / 8;
+        for (int x = lane; x < 16 * RU; x += 64) {
+          const int ro = 16 * ow + x / RU, c8 = x % RU;
+          const int64_t t = int64_t(n) * R + ro;
+          if (t < p.T)
+            *reinterpret_cast<uint4*>(o + ((int64_t(b) * p.T + t) * H + h) * dv + col_base + 8 * c8) =
+                *reinterpret_cast<const uint4*>(&ost[ro][8 * c8]);
+        }
+      }
+      __syncthreads();
+    }
+    return;
+  }
+
+  // ---- state waves ----
   // state: S[rt][ct][e] = S[32 w + 16 rt + 4 lg + e][col_base + 16 ct + li]
   float S[SRT][NCT][4];
   const size_t sbase = size_t(bh) * DK * size_t(dv);
@@ -473,8 +570,6 @@ __global__ __launch_bounds__(kThreads + 64) void chunk_scan_rows_kernel(Problem 
       for (int e = 0; e < 4; ++e)
         S[rt][ct][e] = p.s0 ? p.s0[sbase + size_t(32 * wave + 16 * rt + 4 * lg + e) * dv + col_base + 16 * ct + li]
                             : 0.0f;
-  // 1 / x for a power of two x in [2^-126, 2^126] (exact, one integer op)
-  auto inv_pow2 = [](float x) { return __uint_as_float(0x7f000000u - __float_as_uint(x)); };
   // publish this wave's state rows: fp16 image and the block's column scales
   auto publish_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -498,37 +593,18 @@ __global__ __launch_bounds__(kThreads + 64) void chunk_scan_rows_kernel(Problem 
 
   auto step = [&](int n, FragsA& fa, FragsB& fb) __attribute__((always_inline)) {
     const int nn = min(n + 1, NC - 1);  // next chunk (the last one is read again at the end)
-    // ---- U = U~ / ws - W S and the state part of O (B = state at scale cs) ----
-    // k-block u of the state is wave block u: its fragment is brought from the
-    // block's scale to the column's common (smallest) one by an exact power of two
-    // (k-block outer, column tile inner: 2 NCT independent accumulator chains
-    // interleave, which hides the MFMA latency)
-    float ics[NCT], facs[NCT][KU];
-    float4v ua[NCT], oa[NCT];
+    // ---- U = U~ / ws - W S (B = state at the column's common scale) ----
+    float ics[NCT];
+    float4v ua[NCT];
+    {
+      half8 bv[KU][NCT];
+      state_frags(bv, ics);
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const float4 s4 = *reinterpret_cast<const float4*>(&ssc[16 * ct + li][0]);
-      const float cs = fminf(fminf(s4.x, s4.y), fminf(s4.z, s4.w));
-      facs[ct][0] = cs * inv_pow2(s4.x);
-      facs[ct][1] = cs * inv_pow2(s4.y);
-      facs[ct][2] = cs * inv_pow2(s4.z);
-      facs[ct][3] = cs * inv_pow2(s4.w);
-      ics[ct] = inv_pow2(cs);
-      ua[ct] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-      oa[ct] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-    }
+      for (int ct = 0; ct < NCT; ++ct) ua[ct] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      half8 bv[NCT];
+      for (int u = 0; u < KU; ++u)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-        bv[ct] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&st[16 * ct + li][32 * u + 8 * lg])) *
-                 (_Float16)facs[ct][u];
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        ua[ct] = mma_pair_f16(__builtin_bit_cast(half8, fa.w[u]), bv[ct], ua[ct]);
-        oa[ct] = mma_pair_f16(__builtin_bit_cast(half8, fa.q[u]), bv[ct], oa[ct]);  // (unused without output rows)
-      }
+        for (int ct = 0; ct < NCT; ++ct) ua[ct] = mma_pair_f16(__builtin_bit_cast(half8, fa.w[u]), bv[u][ct], ua[ct]);
     }
     // U rows 16 w + 4 lg + e, column 16 ct + li; fp16 U^T with this block's scale
 #pragma unroll
@@ -550,44 +626,22 @@ __global__ __launch_bounds__(kThreads + 64) void chunk_scan_rows_kernel(Problem 
     load_a(nn, fa);
     __syncthreads();
 
-    // ---- S' = Diag(gamma) S + A^^T U and O = (Q+ S + P U) / qs (B = U at scale cu) ----
-    // fragment u of a column holds U rows 32 u + 8 lg .. +7: wave block 2 u + lg / 2
-    float4v sa[SRT][NCT], pa[NCT];
-    float icu[NCT], facu[NCT][CU];
+    // ---- S' = Diag(gamma) S + A^^T U (B = U at the column's common scale) ----
+    float4v sa[SRT][NCT];
+    float icu[NCT];
+    {
+      half8 bu[CU][NCT];
+      u_frags(bu, icu);
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const float4 s4 = *reinterpret_cast<const float4*>(&usc[16 * ct + li][0]);
-      const float cu = fminf(fminf(s4.x, s4.y), fminf(s4.z, s4.w));
-      icu[ct] = inv_pow2(cu);
-      facu[ct][0] = cu * inv_pow2((lg >> 1) ? s4.y : s4.x);
-      facu[ct][1] = cu * inv_pow2((lg >> 1) ? s4.w : s4.z);
+      for (int rt = 0; rt < SRT; ++rt)
 #pragma unroll
-      for (int rt = 0; rt < SRT; ++rt) sa[rt][ct] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-      pa[ct] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-    }
+        for (int ct = 0; ct < NCT; ++ct) sa[rt][ct] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int u = 0; u < CU; ++u) {
-      half8 bv[NCT];
+      for (int u = 0; u < CU; ++u)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-        bv[ct] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&ut[16 * ct + li][32 * u + 8 * lg])) *
-                 (_Float16)facu[ct][u];
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-        for (int rt = 0; rt < SRT; ++rt) sa[rt][ct] = mma_pair_f16(__builtin_bit_cast(half8, fb.at[rt][u]), bv[ct], sa[rt][ct]);
-        pa[ct] = mma_pair_f16(__builtin_bit_cast(half8, fb.pp[u]), bv[ct], pa[ct]);
-      }
-    }
-    if (orows) {
-      const float qi[4] = {fb.qi.x, fb.qi.y, fb.qi.z, fb.qi.w};
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float ov = (oa[ct][e] * ics[ct] + pa[ct][e] * icu[ct]) * qi[e];
-          ost[16 * wave + 4 * lg + e][16 * ct + li] = __builtin_bit_cast(uint16_t, (__bf16)ov);
-        }
+          for (int rt = 0; rt < SRT; ++rt) sa[rt][ct] = mma_pair_f16(__builtin_bit_cast(half8, fb.at[rt][u]), bu[u][ct], sa[rt][ct]);
     }
     const float gm[SRT][4] = {{fb.gam[0].x, fb.gam[0].y, fb.gam[0].z, fb.gam[0].w},
                               {fb.gam[SRT - 1].x, fb.gam[SRT - 1].y, fb.gam[SRT - 1].z, fb.gam[SRT - 1].w}};
@@ -600,20 +654,6 @@ __global__ __launch_bounds__(kThreads + 64) void chunk_scan_rows_kernel(Problem 
     load_b(nn, fb);
     publish_state();
     __syncthreads();
-    // ---- coalesced copy of the chunk's output rows ----
-    if (want_out) {
-      constexpr int RU = NB / 8;  // 16-byte units per output row
-      constexpr int PER = (C * RU + kThreads - 1) / kThreads;
-#pragma unroll
-      for (int it = 0; it < PER; ++it) {  // fixed trip count: static store count per step
-        const int x = tid + it * kThreads;
-        const int ro = x / RU, c8 = x % RU;
-        const int64_t t = int64_t(n) * R + ro;
-        if (ro < R && t < p.T)
-          *reinterpret_cast<uint4*>(o + ((int64_t(b) * p.T + t) * H + h) * dv + col_base + 8 * c8) =
-              *reinterpret_cast<const uint4*>(&ost[ro][8 * c8]);
-      }
-    }
   };
 
   publish_state();
@@ -647,7 +687,7 @@ int launch_scan_t(const Problem& p, void* ws, bool want_out, hipStream_t s) {
     // (one workgroup per 16 columns keeps the step latency short: the scan is a
     // chain of dependent MFMA / LDS / barrier phases, 512 steps long at 32K)
     const dim3 g(unsigned(p.B * p.H) * unsigned(p.dv / 16));
-    chunk_scan_rows_kernel<1><<<g, kThreads + 64, 0, s>>>(p, static_cast<const unsigned char*>(ws), L,
+    chunk_scan_rows_kernel<1><<<g, 2 * kThreads + 64, 0, s>>>(p, static_cast<const unsigned char*>(ws), L,
                                                          want_out ? 1 : 0);
     return int(hipGetLastError());
   } else {
