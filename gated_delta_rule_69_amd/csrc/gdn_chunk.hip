@@ -56,8 +56,11 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(Problem p, const u
   constexpr int KS = DK / 16;
   constexpr int KP = (KS + 1) / 2;
   constexpr int NP = (NT + 1) / 2;
-  // bf16 outputs are staged in LDS for 16-byte stores; fp32 outputs go out directly
-  constexpr int OSR = F16 ? C : 1;
+  // Outputs are staged in LDS for full-row 16-byte stores whenever the stage fits
+  // beside the double-buffered image (every bf16 case; fp32 but for chunk 64 with
+  // 64 key channels); otherwise they are stored from registers one step later.
+  constexpr bool OSTAGE = F16 || (2 * UNITS * 16 + 2 * C * 64 * 4 <= 160 * 1024);
+  constexpr int OSR = OSTAGE ? C : 1;
   static_assert(2 * UNITS * 16 + 2 * OSR * 64 * sizeof(In) <= 160 * 1024, "LDS budget");
   __shared__ uint4 img[2][UNITS];
   __shared__ In ostage[2][OSR][64];
@@ -128,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(Problem p, const u
   // coalesced copy of a staged output block (rows of chunk n) to o
   const int ounits_row = (min(64, dv - cbase) * int(sizeof(In))) / 16;
   auto flush_out = [&](int buf, int64_t n) __attribute__((always_inline)) {
-    if constexpr (!F16) return;
+    if constexpr (!OSTAGE) return;
     for (int x = tid; x < R * ounits_row; x += kThreads) {
       const int ro = x / ounits_row, cu = x % ounits_row;
       const int64_t t = n * R + ro;
@@ -156,10 +159,32 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(Problem p, const u
   for (int m = 0; m < NT; ++m) ut_cur[m] = ut_next[m];
   __syncthreads();
 
+  // unstaged fp32 outputs of a chunk stay in registers until the next chunk's copies
+  // are issued: stores issued just before the end-of-step wait would hold it up
+  float ohold[NT][4];
+  auto store_hold = [&](int64_t n) __attribute__((always_inline)) {
+    if constexpr (!OSTAGE) {
+      if (!active) return;
+#pragma unroll
+      for (int mo = 0; mo < NT; ++mo) {
+        if (mo < RT) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int64_t t = n * R + 16 * mo + 4 * lg + e;
+            if (t < p.T) o[((b * p.T + t) * p.H + h) * dv + col] = ohold[mo][e];
+          }
+        }
+      }
+    }
+  };
+
   for (int64_t n = 0; n < NC; ++n) {
     const int buf = int(n & 1);
     if (n + 1 < NC) issue_loads(n + 1, buf ^ 1);
-    if (want_out && n > 0) flush_out(buf ^ 1, n - 1);
+    if (want_out && n > 0) {
+      flush_out(buf ^ 1, n - 1);
+      store_hold(n - 1);
+    }
     const unsigned char* base = reinterpret_cast<const unsigned char*>(&img[buf][0]);
     const Op* Wl = reinterpret_cast<const Op*>(base + LC.off_W);
     const Op* ATl = reinterpret_cast<const Op*>(base + LC.off_AT);
@@ -287,9 +312,10 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(Problem p, const u
               const float ov = (a1[e] * iS + a2[e] * iU) * qinvl[ro];
               if constexpr (F16) {
                 ostage[buf][ro][16 * wave + li] = f32_to_bf16(ov);
+              } else if constexpr (OSTAGE) {
+                ostage[buf][ro][16 * wave + li] = ov;
               } else {
-                const int64_t t = n * R + ro;
-                if (t < p.T) o[((b * p.T + t) * p.H + h) * dv + col] = ov;
+                ohold[mo][e] = ov;
               }
             }
           }
@@ -310,7 +336,10 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(Problem p, const u
     }
     __syncthreads();
   }
-  if (want_out) flush_out(int((NC - 1) & 1), NC - 1);
+  if (want_out) {
+    flush_out(int((NC - 1) & 1), NC - 1);
+    store_hold(NC - 1);
+  }
 
   if (active && p.s_final) {
 #pragma unroll
