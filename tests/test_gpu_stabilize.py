@@ -208,3 +208,20 @@ def test_fused_equals_separate_pass_fp32():
                                    eta=d["eta"])
         assert oracle.rel_l2(host(o1), host(o2)) <= 1e-6
         assert oracle.rel_l2(host(S1), host(S2)) <= 1e-6
+
+
+@pytest.mark.parametrize("dt,dk,chunk", [("f32", 64, 32), ("bf16", 128, 64)])
+def test_fused_final_state_entry(dt, dk, chunk):
+    """gdn_final_state with the stabiliser gives the fused forward pass's final state
+    bit for bit (the same prepare and scan kernels, without the outputs)."""
+    import gated_delta_rule_69_amd as gdn
+    from gpu_util import host, state_to_dev, to_dev
+    inp, _ = mixed_inputs(1, 140, 2, dk, dt, seed=44)
+    s0 = gdn_inputs.make_state(1, 2, dk, dk, seed=44)
+    d = to_dev(inp)
+    for mode in ("clip_decay", "project_j"):
+        _, S = gdn.gdn_chunk_fwd("asym", d["q"], d["k"], d["v"], d["alpha"], None, chunk=chunk,
+                                 j=d["j"], eta=d["eta"], s0=state_to_dev(s0), stabilize=mode)
+        S2 = gdn.gdn_final_state("asym", d["k"], d["v"], d["alpha"], None, chunk=chunk, j=d["j"],
+                                 eta=d["eta"], s0=state_to_dev(s0), stabilize=mode)
+        np.testing.assert_array_equal(host(S2), host(S))
