@@ -13,6 +13,8 @@ Modules
               (spectral norm of I - eta j k^T, the RWKV-7 secular equation),
               used only to pin ``recurrence``
   stabilize   the GDN2 stabilisers (decay clip, j projection), token-wise
+  backward    reverse-mode gradients of the token recurrence (all variants but
+              DeltaProduct), pinned by finite differences of ``recurrence``
   metrics     rel-L2 and normwise max-rel error
 
 Parity status: every function in ``recurrence`` is pinned by tests that do not
@@ -21,4 +23,4 @@ pages' models, closed forms, hand-derivable cases); see tests/test_oracle_*.py.
 """
 from .recurrence import (deltanet, gdn, kda, fg2, deltaproduct, gdn2, forward)  # noqa: F401
 from .metrics import rel_l2, max_rel  # noqa: F401
-from . import stabilize  # noqa: F401
+from . import stabilize, backward  # noqa: F401
