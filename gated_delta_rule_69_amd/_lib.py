@@ -32,6 +32,11 @@ class GdnArgs(ctypes.Structure):
                 ("stabilize", ctypes.c_int32)]
 
 
+class GdnGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("dq", "dk", "dv", "dalpha", "dbeta", "dbeta_v", "dj", "deta", "ds0")]
+
+
 class GdnError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -64,6 +69,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             fn.restype = ctypes.c_int
         lib.gdn_recurrent_step.argtypes = [P, ctypes.c_void_p, ctypes.c_void_p]
         lib.gdn_recurrent_step.restype = ctypes.c_int
+        lib.gdn_bwd_workspace_bytes.argtypes = [P]
+        lib.gdn_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.gdn_recurrent_bwd.argtypes = [P, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(GdnGrads),
+                                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        lib.gdn_recurrent_bwd.restype = ctypes.c_int
         lib.gdn_asym_stabilize.argtypes = [P, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
         lib.gdn_asym_stabilize.restype = ctypes.c_int
         lib.gdn_status_str.argtypes = [ctypes.c_int]
@@ -277,4 +287,37 @@ def gdn_asym_stabilize(mode, k, j, alpha, eta, *, out=None, stream=None):
                                            ctypes.c_void_p(out.data_ptr()), _stream(stream))
     if st != 0:
         raise GdnError(st, "gdn_asym_stabilize")
+    return out
+
+
+def gdn_recurrent_bwd(variant, q, k, v, alpha, beta=None, *, d_o, s0=None, ds_final=None,
+                      beta_v=None, j=None, eta=None, workspace=None, stream=None):
+    """Gradients (float32 tensors, named after the inputs: dq, dk, dv, dalpha, dbeta,
+    dbeta_v, dj, deta, ds0) of the token recurrence for upstream d_o (shape of o, input
+    dtype) and ds_final (float32 state shape, optional)."""
+    import torch
+    dev = k.device
+    _check(d_o, "d_o", dev, k.dtype)
+    _check(ds_final, "ds_final", dev, torch.float32)
+    a = make_args(variant, q, k, v, alpha, beta, chunk=16, beta_v=beta_v, j=j, eta=eta, s0=s0,
+                  s_final=None, o=None)
+    out = {}
+    f32 = dict(dtype=torch.float32, device=dev)
+    for name, ref in (("dq", q), ("dk", k), ("dv", v), ("dalpha", alpha), ("dbeta", beta),
+                      ("dbeta_v", beta_v), ("dj", j), ("deta", eta)):
+        if ref is not None:
+            out[name] = torch.empty(ref.shape, **f32)
+    B, H = k.shape[0], k.shape[2]
+    out["ds0"] = torch.empty((B, H, k.shape[-1], v.shape[-1]), **f32)
+    gr = GdnGrads(**{n: (t.data_ptr() if t is not None else None) for n, t in out.items()})
+    need = int(load_library().gdn_bwd_workspace_bytes(ctypes.byref(a)))
+    if need == 0:
+        raise GdnError(-2, "gdn_bwd_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = load_library().gdn_recurrent_bwd(ctypes.byref(a), _ptr(d_o), _ptr(ds_final), ctypes.byref(gr),
+                                          ctypes.c_void_p(workspace.data_ptr()),
+                                          ctypes.c_size_t(workspace.numel()), _stream(stream))
+    if st != 0:
+        raise GdnError(st, "gdn_recurrent_bwd")
     return out

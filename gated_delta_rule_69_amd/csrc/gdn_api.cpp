@@ -195,6 +195,53 @@ int gdn_recurrent_step(const gdn_args* args, float* state_inout, void* stream) {
   return gdn::launch_recurrent(p, state_inout, stream) == 0 ? GDN_OK : GDN_ERR_HIP;
 }
 
+static int bwd_problem(const gdn_args* args, Problem* p) {
+  if (args == nullptr) return GDN_ERR_ARG;
+  gdn_args a = *args;
+  if (a.o == nullptr) a.o = const_cast<void*>(a.q);  // not written by the backward pass
+  int st = gdn::validate(&a, Entry::Recurrent, p);
+  if (st != GDN_OK) return st;
+  if (p->variant == GDN_VARIANT_DELTAPRODUCT || p->stabilize != 0) return GDN_ERR_UNSUPPORTED;
+  return GDN_OK;
+}
+
+size_t gdn_bwd_workspace_bytes(const gdn_args* args) {
+  Problem p;
+  if (args == nullptr) return 0;
+  gdn_args a = *args;  // shapes only: the pointer checks belong to the call itself
+  if (a.T > 0) a.q = a.k = a.v = a.alpha = a.o = reinterpret_cast<void*>(uintptr_t(1) << 20);
+  if (a.T > 0 && a.variant == GDN_VARIANT_ASYM) a.j = a.eta = a.k;
+  if (a.T > 0 && a.variant != GDN_VARIANT_ASYM) a.beta = a.k;
+  if (bwd_problem(&a, &p) != GDN_OK) return 0;
+  return gdn::bwd_workspace_bytes(p);
+}
+
+int gdn_recurrent_bwd(const gdn_args* args, const void* d_o, const float* d_s_final,
+                      const gdn_grads* grads, void* ws, size_t ws_bytes, void* stream) {
+  Problem p;
+  int st = bwd_problem(args, &p);
+  if (st != GDN_OK) return st;
+  if (grads == nullptr) return GDN_ERR_ARG;
+  auto a16 = [](const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) == 0; };
+  auto need = [&](const void* x) { return p.T == 0 ? a16(x) : (x != nullptr && a16(x)); };
+  auto none = [](const void* x) { return x == nullptr; };
+  const bool asym = p.variant == GDN_VARIANT_ASYM;
+  const bool plus = p.variant == GDN_VARIANT_FG2 && p.beta_v != nullptr;
+  if (!need(d_o) || !need(grads->dq) || !need(grads->dk) || !need(grads->dv) || !need(grads->dalpha))
+    return GDN_ERR_ARG;
+  if (asym ? !(need(grads->dj) && need(grads->deta) && none(grads->dbeta))
+           : !(need(grads->dbeta) && none(grads->dj) && none(grads->deta)))
+    return GDN_ERR_ARG;
+  if (plus ? !need(grads->dbeta_v) : !none(grads->dbeta_v)) return GDN_ERR_ARG;
+  if (!a16(grads->ds0) || !a16(d_s_final)) return GDN_ERR_ARG;
+  const size_t need_ws = gdn::bwd_workspace_bytes(p);
+  if (ws == nullptr || ws_bytes < need_ws || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return GDN_ERR_WORKSPACE;
+  const gdn::GradPtrs g{grads->dq, grads->dk, grads->dv, grads->dalpha, grads->dbeta,
+                        grads->dbeta_v, grads->dj, grads->deta, grads->ds0};
+  return gdn::launch_recurrent_bwd(p, d_o, d_s_final, g, ws, stream) == 0 ? GDN_OK : GDN_ERR_HIP;
+}
+
 int gdn_asym_stabilize(const gdn_args* args, int mode, void* out, void* stream) {
   Problem p;
   int st = gdn::validate(args, Entry::Stabilize, &p);

@@ -82,6 +82,13 @@ __device__ __forceinline__ float max_over_groups(float x) {
   return fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
 }
 
+// Sum over all 64 lanes (every lane gets the total).
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
 // Sum and max over the eight lanes l ^ 8m (m = 0..7): DPP row_ror:8 pairs lane l with
 // l ^ 8 inside each 16-lane row, then the four-group exchanges above.
 __device__ __forceinline__ float sum_over_8_groups(float x) {

@@ -122,6 +122,14 @@ int launch_prep_gdn(const Problem& p, void* ws, bool want_output, void* stream);
 int launch_prep_dp(const Problem& p, void* ws, bool want_output, void* stream);
 int launch_prep_asym(const Problem& p, void* ws, bool want_output, void* stream);
 int launch_state_copy(const Problem& p, void* stream);
+// Gradient outputs of the backward pass (float32; see gdn_grads).
+struct GradPtrs {
+  float *dq, *dk, *dv, *dalpha, *dbeta, *dbeta_v, *dj, *deta, *ds0;
+};
+// Backward pass of the token recurrence (gdn_backward.hip).
+size_t bwd_workspace_bytes(const Problem& p);
+int launch_recurrent_bwd(const Problem& p, const void* d_o, const float* dsf, const GradPtrs& g,
+                         void* ws, void* stream);
 // ASYM stabilisers (gdn_stabilize.hip); mode as in gdn_asym_stabilize.
 int launch_stabilize(const Problem& p, int mode, void* out, void* stream);
 

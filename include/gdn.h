@@ -169,6 +169,38 @@ int gdn_recurrent_step(const gdn_args* args, float* state_inout, void* stream);
  * ASYM, a mode outside the enum, or a null or misaligned k, j, alpha, eta or out. */
 int gdn_asym_stabilize(const gdn_args* args, int mode, void* out, void* stream);
 
+/* Gradient outputs of gdn_recurrent_bwd, all float32, laid out like the matching
+ * input (dalpha like alpha, dbeta like beta, ...; ds0 like s0). Pointers for inputs
+ * the variant does not take must be NULL; the others must be non-NULL and 16-byte
+ * aligned, except ds0, which may be NULL (not written). */
+typedef struct gdn_grads {
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dalpha;
+  float* dbeta;    /* FG2, KDA, GDN */
+  float* dbeta_v;  /* FG2 with beta_v */
+  float* dj;       /* ASYM */
+  float* deta;     /* ASYM */
+  float* ds0;
+} gdn_grads;
+
+/* Bytes of device workspace gdn_recurrent_bwd needs (0 for an invalid set). */
+size_t gdn_bwd_workspace_bytes(const gdn_args* args);
+
+/* Backward pass (reverse-mode gradients) of the token recurrence for every variant
+ * with one step a token (FG2, FG2+, KDA, GDN, ASYM; DELTAPRODUCT returns
+ * GDN_ERR_UNSUPPORTED). The pages give the forward pass only; this is the derivative
+ * of the same recurrence (FG2-GDN reading notes, section 2.2 eq. (11), section 2.3
+ * eq. (13); GDN2-stability page, eq. (1)). args as for the forward pass (o, s_final
+ * and chunk are ignored; s0 NULL means zero); d_o [B, T, H, dv] in args->dtype is
+ * dL/do; d_s_final [B, H, dk, dv] float32 is dL/dS_T (NULL: zero). Gradients with
+ * respect to beta and beta_v are singular at 0 (their square roots enter the step).
+ * ws must hold gdn_bwd_workspace_bytes(args) bytes, 256-byte aligned. The forward
+ * states are recomputed from checkpoints every 64 tokens; results are deterministic. */
+int gdn_recurrent_bwd(const gdn_args* args, const void* d_o, const float* d_s_final,
+                      const gdn_grads* grads, void* ws, size_t ws_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* gdn_status_str(int status);
 

@@ -31,6 +31,7 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) >= {"gdn_chunk_fwd", "gdn_final_state", "gdn_recurrent_step",
                           "gdn_chunk_prepare", "gdn_chunk_scan", "gdn_asym_stabilize",
+                          "gdn_recurrent_bwd", "gdn_bwd_workspace_bytes",
                           "gdn_workspace_bytes", "gdn_status_str", "gdn_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -131,6 +132,23 @@ def test_fused_stabilizer_field(lib):
     assert lib.gdn_recurrent_step(ctypes.byref(good_args(stabilize=2)), FAKE, None) == -1
     assert lib.gdn_workspace_bytes(ctypes.byref(good_args(**asym, stabilize=1))) == \
         lib.gdn_workspace_bytes(ctypes.byref(good_args(**asym)))
+
+
+def test_backward_checks(lib):
+    from gated_delta_rule_69_amd._lib import GdnGrads
+    a = good_args()
+    need = lib.gdn_bwd_workspace_bytes(ctypes.byref(a))
+    assert need > 0
+    full = GdnGrads(dq=FAKE, dk=FAKE, dv=FAKE, dalpha=FAKE, dbeta=FAKE)
+    call = lambda args, g, ws=FAKE, n=need: lib.gdn_recurrent_bwd(  # noqa: E731
+        ctypes.byref(args), FAKE, None, ctypes.byref(g) if g is not None else None, ws, n, None)
+    assert call(a, full, None, 0) == -3
+    assert call(a, full, FAKE, need - 1) == -3
+    assert call(a, None) == -1
+    assert call(a, GdnGrads(dq=FAKE, dk=FAKE, dv=FAKE, dalpha=FAKE)) == -1          # dbeta missing
+    assert call(a, GdnGrads(dq=FAKE, dk=FAKE, dv=FAKE, dalpha=FAKE, dbeta=FAKE, dj=FAKE)) == -1
+    assert call(good_args(variant=3, n_h=2), full) == -2                              # DeltaProduct
+    assert lib.gdn_bwd_workspace_bytes(ctypes.byref(good_args(dk=48))) == 0
 
 
 def test_stabilize_checks(lib):

@@ -1,0 +1,67 @@
+"""Backward pass of the token recurrence (gdn_recurrent_bwd) against the float64
+oracle's gradients (oracle.backward, itself pinned by finite differences).
+
+The kernel computes in float32 from the (bf16-rounded, for bf16) inputs, as the oracle
+does in float64 from the same values, so one tolerance covers both input dtypes:
+rel-L2 1e-5 and normwise max-rel 1e-4 for every gradient. Sequences longer than the
+64-token checkpoint interval, with a ragged last interval, exercise the recompute.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs
+import oracle
+from oracle import backward as obwd
+
+pytestmark = pytest.mark.gpu
+
+CASES = [  # variant, fg2_plus, dtype, B, T, H, dk, dv
+    ("fg2", False, "f32", 1, 70, 2, 16, 16),
+    ("fg2", True, "f32", 1, 90, 2, 32, 64),
+    ("kda", False, "bf16", 2, 65, 2, 64, 32),
+    ("gdn", False, "f32", 1, 130, 3, 32, 16),
+    ("asym", False, "f32", 1, 100, 2, 64, 64),
+    ("fg2", False, "bf16", 1, 150, 2, 128, 128),
+    ("asym", False, "bf16", 1, 66, 1, 128, 64),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_backward_vs_oracle(case):
+    import gated_delta_rule_69_amd as gdn
+    from gpu_util import DEV, host, state_to_dev, to_dev
+    var, plus, dt, B, T, H, dk, dv = case
+    inp = gdn_inputs.make_inputs(var, B, T, H, dk, dv, dtype=dt, seed=90, fg2_plus=plus)
+    rng = np.random.default_rng(91)
+    s0 = gdn_inputs.make_state(B, H, dk, dv, seed=92)
+    do = rng.standard_normal((B, T, H, dv)).astype(np.float32)
+    if dt == "bf16":
+        do = gdn_inputs.round_bf16(do)
+    dsf = rng.standard_normal((B, H, dk, dv)).astype(np.float32)
+    ref = obwd.backward(inp, do, s0, dsf)
+    d = to_dev(inp)
+    io = torch.bfloat16 if dt == "bf16" else torch.float32
+    got = gdn.gdn_recurrent_bwd(var, d["q"], d["k"], d["v"], d["alpha"], d.get("beta"),
+                                d_o=torch.from_numpy(do).to(DEV).to(io), s0=state_to_dev(s0),
+                                ds_final=torch.from_numpy(dsf).to(DEV), beta_v=d.get("beta_v"),
+                                j=d.get("j"), eta=d.get("eta"))
+    torch.cuda.synchronize()
+    assert set(ref) <= set(got), (sorted(ref), sorted(got))
+    for name, r in ref.items():
+        x = host(got[name])
+        e2, em = oracle.rel_l2(x, r), oracle.max_rel(x, r)
+        print(case, name, f"rel_l2={e2:.2e} max_rel={em:.2e}", flush=True)
+        assert e2 <= 1e-5 and em <= 1e-4, (name, e2, em)
+
+
+def test_backward_deterministic():
+    import gated_delta_rule_69_amd as gdn
+    from gpu_util import DEV, to_dev
+    inp = gdn_inputs.make_inputs("fg2", 2, 80, 2, 64, 64, dtype="bf16", seed=93)
+    d = to_dev(inp)
+    do = torch.randn((2, 80, 2, 64), device=DEV).bfloat16()
+    r1 = gdn.gdn_recurrent_bwd("fg2", d["q"], d["k"], d["v"], d["alpha"], d["beta"], d_o=do)
+    r2 = gdn.gdn_recurrent_bwd("fg2", d["q"], d["k"], d["v"], d["alpha"], d["beta"], d_o=do)
+    for name in r1:
+        assert torch.equal(r1[name], r2[name]), name
