@@ -452,6 +452,53 @@ def stabilize(args):
                       "data": "synthetic", "n_gpus": 1}), flush=True)
 
 
+# ---- backward: gdn_recurrent_bwd on the 4K prefill workload --------------------------
+def backward(args):
+    """Time of one gdn_recurrent_bwd call on workload 1 (FG2, bf16, B=1, H=16, T=4096,
+    d=128; float32 gradients) and of the forward call it differentiates, HBM fraction
+    with the algorithmic bytes (inputs, d_o and the gradients: 6 d bf16 + 5 d float32
+    per token-head), and sequence 0, head 0 of every gradient against the float64
+    oracle."""
+    import torch
+    import gated_delta_rule_69_amd as gdn
+    import oracle
+    dev = torch.device("cuda:0")
+    cfg = gdn_inputs.CONFIGS[1]
+    B, T, H, d = cfg["B"], cfg["T"], cfg["H"], cfg["dk"]
+    inp = gdn_inputs.config_inputs(1)
+    t = {n: torch.from_numpy(inp[n]).to(dev).to(torch.bfloat16).contiguous()
+         for n in ("q", "k", "v", "alpha", "beta")}
+    rng = np.random.default_rng(7)
+    do_np = gdn_inputs.round_bf16(rng.standard_normal((B, T, H, d)).astype(np.float32))
+    do = torch.from_numpy(do_np).to(dev).to(torch.bfloat16)
+    run = lambda: gdn.gdn_recurrent_bwd("fg2", t["q"], t["k"], t["v"], t["alpha"], t["beta"], d_o=do)  # noqa: E731
+    got = run()
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(args.steps):
+        run()
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / args.steps
+    sub = {k: (v[0:1, :, 0:1] if isinstance(v, np.ndarray) else v) for k, v in inp.items()}
+    sub["B"], sub["H"] = 1, 1
+    ref = oracle.backward.backward(sub, do_np[0:1, :, 0:1])
+    errs = {n: float(np.linalg.norm(got[n][0:1, :, 0:1].cpu().numpy() - r) / np.linalg.norm(r))
+            for n, r in ref.items() if n != "ds0"}
+    nbytes = B * T * H * (6 * d * 2 + 5 * d * 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"backward: {ms:.2f} ms per call ({B * T / (ms * 1e-3):.3e} tokens/s), {gbs:.0f} GB/s "
+        f"({gbs / HBM_PEAK_GBS:.1%}), parity max rel-L2 {max(errs.values()):.2e}")
+    print(json.dumps({"metric": "gdn_recurrent_bwd time, workload 1 (FG2, B=1, H=16, T=4096, d=128, bf16)",
+                      "ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
+                      "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": gbs / HBM_PEAK_GBS, "algorithmic": nbytes},
+                      "parity": errs, "data": "synthetic", "n_gpus": 1}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -465,6 +512,8 @@ def main():
                     help="workloads 0, 1, 3, 4: time per call, roofline fractions, parity")
     ap.add_argument("--decode", action="store_true",
                     help="one-token decode step (gdn_recurrent_step) over 512 sequences")
+    ap.add_argument("--backward", action="store_true",
+                    help="backward pass (gdn_recurrent_bwd) on the 4K prefill workload")
     ap.add_argument("--stabilize", action="store_true",
                     help="GDN2 stabilisers (gdn_asym_stabilize) on the asymmetric workload")
     ap.add_argument("--sweep", action="store_true",
@@ -487,6 +536,9 @@ def main():
         return
     if args.stabilize:
         stabilize(args)
+        return
+    if args.backward:
+        backward(args)
         return
     if args.configs:
         configs(args)

@@ -8,14 +8,15 @@
 // then the chain rule through the variant's (a, b, w, alpha) map (FG2-GDN reading
 // notes, section 2.2 eq. (11) and section 2.3 eq. (13); GDN2-stability page, eq. (1)).
 //
-// One workgroup per (batch, head), one wave per 16-column slice of the state (lane
+// Kernel A: one wave per (batch, head, 16-column slice of the state) (lane
 // l = j + 16 g: column j, key rows g NR .. g NR + NR - 1, as in the forward recurrent
-// kernel). A forward pass stores the slice state every CB tokens; the backward sweep
+// kernel). A forward pass stores the slice state every kCB tokens; the backward sweep
 // takes the chunks in reverse, recomputes the chunk's states from its checkpoint
 // into the workspace, and walks the chunk backwards. Column-complete quantities
 // (dw) come out of the wave directly; row quantities (da, db, dq, dalpha) are partial
 // sums over the wave's 16 columns, reduced across the 16 lanes by a transposing
-// butterfly and across the slices, in a fixed order, after each chunk.
+// butterfly and written per slice. Kernel B sums the slices in a fixed order and
+// applies the variant's chain rule, one wave per token and head.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -24,20 +25,22 @@ namespace {
 
 constexpr int kCB = 64;  // tokens per checkpoint interval
 
+// Workspace (floats): per (batch*head, slice) the checkpoints and the current chunk's
+// states, in lane order ([step][NR/4][64 lanes][4]: one 16-byte vector per lane);
+// then the row partials [slice][B*T*H][4][dk] and dw [B*T*H][dv].
 struct BwdLayout {
-  int64_t ckpt, cs, part, dw, per_head;  // float offsets within a head's area
+  int64_t slice_floats, part, dw, total;
 };
 
-__host__ __device__ inline BwdLayout bwd_layout(int64_t T, int64_t dk, int64_t dv) {
+__host__ __device__ inline BwdLayout bwd_layout(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv) {
   BwdLayout L;
   const int64_t nck = (T + kCB - 1) / kCB;
   const int64_t ns = dv / 16;
-  L.ckpt = 0;
-  L.cs = L.ckpt + nck * dk * dv;
-  L.part = L.cs + int64_t(kCB) * dk * dv;
-  L.dw = L.part + ns * kCB * 4 * dk;
-  L.per_head = L.dw + int64_t(kCB) * dv;
-  L.per_head = (L.per_head + 63) / 64 * 64;
+  const int64_t bth = B * T * H;
+  L.slice_floats = (nck + kCB) * dk * 16;
+  L.part = B * H * ns * L.slice_floats;
+  L.dw = L.part + ns * bth * 4 * dk;
+  L.total = L.dw + bth * dv;
   return L;
 }
 
@@ -86,24 +89,27 @@ struct RowReduce16 {
   }
 };
 
+// Kernel A: one wave per (batch*head, 16-column slice): forward with checkpoints,
+// then the reverse sweep; writes dw (column-complete) and the row partials.
 template <typename In, int DK>
-__global__ __launch_bounds__(512) void recurrent_bwd_kernel(Problem p, const In* __restrict__ d_o,
-                                                            const float* __restrict__ dsf, GradPtrs g,
-                                                            float* __restrict__ ws) {
+__global__ __launch_bounds__(64) void bwd_slice_kernel(Problem p, const In* __restrict__ d_o,
+                                                       const float* __restrict__ dsf, float* __restrict__ ds0,
+                                                       float* __restrict__ ws) {
   constexpr int NR = DK / 4;
   using RR = RowReduce16<NR>;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;  // column slice
+  const int lane = threadIdx.x;
   const int j = lane & 15, gr = lane >> 4;
-  const int64_t bh = blockIdx.x;
-  const int64_t b = bh / p.H, h = bh % p.H;
   const int64_t T = p.T, H = p.H, dv = p.dv;
   const int ns = int(dv / 16);
+  const int64_t bh = blockIdx.x / ns;
+  const int wave = int(blockIdx.x % ns);  // column slice
+  const int64_t b = bh / H, h = bh % H;
   const int col = wave * 16 + j;
   const int row0 = gr * NR;
-  const BwdLayout L = bwd_layout(T, DK, dv);
-  float* wsh = ws + bh * L.per_head;
+  const BwdLayout L = bwd_layout(p.B, T, H, DK, dv);
+  float* wsl = ws + int64_t(blockIdx.x) * L.slice_floats;
   const int64_t nck = (T + kCB - 1) / kCB;
+  const int64_t bth = p.B * T * H;
 
   const In* q = static_cast<const In*>(p.q);
   const In* k = static_cast<const In*>(p.k);
@@ -115,50 +121,110 @@ __global__ __launch_bounds__(512) void recurrent_bwd_kernel(Problem p, const In*
   const In* et = static_cast<const In*>(p.eta);
   auto ld = [](const In* x) { return IO<In>::ld(x); };
 
-  // (a, b, alpha) rows and w of this lane's column for token t
-  auto token = [&](int64_t t, float (&a)[NR], float (&bb)[NR], float (&alpha)[NR], float& w)
-      __attribute__((always_inline)) {
-    const int64_t th = (b * T + t) * H + h;
-    load_vec<NR>(k + th * DK + row0, a);
-    const float vc = ld(v + th * dv + col);
-    if (p.variant == GDN_VARIANT_ASYM) {
-      const float e = ld(et + th);
-      load_vec<NR>(jv + th * DK + row0, bb);
-      load_vec<NR>(al + th * DK + row0, alpha);
+  // A token's inputs as loaded (raw 16- or 8-byte vectors and scalars), so that the
+  // next token's loads can be in flight while the current one is computed; finish()
+  // converts them into (a, b, alpha) rows, w of this lane's column, q rows and do.
+  using V4 = std::conditional_t<std::is_same<In, float>::value, float4, uint2>;
+  struct Raw {
+    V4 k[NR / 4], x[NR / 4], y[NR / 4], qv[NR / 4];
+    In s, vc, vb, dout;
+  };
+  auto rows = [&](const In* base, V4 (&dst)[NR / 4]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int r = 0; r < NR; ++r) bb[r] *= e;
+    for (int i = 0; i < NR / 4; ++i) dst[i] = reinterpret_cast<const V4*>(base)[i];
+  };
+  auto cvt = [](const V4& x, float* o) __attribute__((always_inline)) {
+    if constexpr (std::is_same<In, float>::value) {
+      o[0] = x.x, o[1] = x.y, o[2] = x.z, o[3] = x.w;
+    } else {
+      o[0] = __uint_as_float(x.x << 16), o[1] = __uint_as_float(x.x & 0xffff0000u);
+      o[2] = __uint_as_float(x.y << 16), o[3] = __uint_as_float(x.y & 0xffff0000u);
+    }
+  };
+  auto load_raw = [&](int64_t t, Raw& r, bool with_q) __attribute__((always_inline)) {
+    const int64_t th = (b * T + t) * H + h;
+    rows(k + th * DK + row0, r.k);
+    r.vc = v[th * dv + col];
+    if (p.variant == GDN_VARIANT_ASYM) {
+      r.s = et[th];
+      rows(jv + th * DK + row0, r.y);
+      rows(al + th * DK + row0, r.x);
+    } else if (p.variant == GDN_VARIANT_FG2) {
+      rows(be + th * DK + row0, r.y);
+      rows(al + th * DK + row0, r.x);
+      r.vb = bev ? bev[th * dv + col] : be[th * DK + col];
+    } else {
+      r.s = be[th];
+      if (p.variant == GDN_VARIANT_KDA) rows(al + th * DK + row0, r.x);
+      else r.vb = al[th];
+    }
+    if (with_q) {
+      rows(q + th * DK + row0, r.qv);
+      r.dout = d_o[th * dv + col];
+    }
+  };
+  auto finish = [&](const Raw& r, float (&a)[NR], float (&bb)[NR], float (&alpha)[NR], float& w)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NR / 4; ++i) cvt(r.k[i], a + 4 * i);
+    const float vc = ld(&r.vc);
+    if (p.variant == GDN_VARIANT_ASYM) {
+      const float e = ld(&r.s);
+#pragma unroll
+      for (int i = 0; i < NR / 4; ++i) {
+        cvt(r.y[i], bb + 4 * i);
+        cvt(r.x[i], alpha + 4 * i);
+      }
+#pragma unroll
+      for (int q2 = 0; q2 < NR; ++q2) bb[q2] *= e;
       w = e * vc;
     } else if (p.variant == GDN_VARIANT_FG2) {
       float beta[NR];
-      load_vec<NR>(be + th * DK + row0, beta);
-      load_vec<NR>(al + th * DK + row0, alpha);
 #pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        a[r] *= sqrtf(beta[r]);
-        bb[r] = a[r];
+      for (int i = 0; i < NR / 4; ++i) {
+        cvt(r.y[i], beta + 4 * i);
+        cvt(r.x[i], alpha + 4 * i);
       }
-      w = vc * sqrtf(bev ? ld(bev + th * dv + col) : ld(be + th * DK + col));
-    } else {
-      const float s = sqrtf(ld(be + th));
 #pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        a[r] *= s;
-        bb[r] = a[r];
+      for (int q2 = 0; q2 < NR; ++q2) {
+        a[q2] *= sqrtf(beta[q2]);
+        bb[q2] = a[q2];
+      }
+      w = vc * sqrtf(ld(&r.vb));
+    } else {
+      const float sb = sqrtf(ld(&r.s));
+#pragma unroll
+      for (int q2 = 0; q2 < NR; ++q2) {
+        a[q2] *= sb;
+        bb[q2] = a[q2];
       }
       if (p.variant == GDN_VARIANT_KDA) {
-        load_vec<NR>(al + th * DK + row0, alpha);
-      } else {
-        const float gm = ld(al + th);
 #pragma unroll
-        for (int r = 0; r < NR; ++r) alpha[r] = gm;
+        for (int i = 0; i < NR / 4; ++i) cvt(r.x[i], alpha + 4 * i);
+      } else {
+        const float gm = ld(&r.vb);
+#pragma unroll
+        for (int q2 = 0; q2 < NR; ++q2) alpha[q2] = gm;
       }
-      w = s * vc;
+      w = sb * vc;
     }
   };
-  auto st_addr = [&](float* base, int r) { return base + int64_t(row0 + r) * dv + col; };
-  auto fwd = [&](float (&S)[NR], int64_t t) __attribute__((always_inline)) {
+  // slice state of one step in lane order: 16-byte vectors, coalesced
+  auto save = [&](float* base, const float (&S)[NR]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NR / 4; ++i)
+      reinterpret_cast<float4*>(base)[i * 64 + lane] = make_float4(S[4 * i], S[4 * i + 1], S[4 * i + 2], S[4 * i + 3]);
+  };
+  auto restore = [&](const float* base, float (&S)[NR]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NR / 4; ++i) {
+      const float4 x = reinterpret_cast<const float4*>(base)[i * 64 + lane];
+      S[4 * i] = x.x, S[4 * i + 1] = x.y, S[4 * i + 2] = x.z, S[4 * i + 3] = x.w;
+    }
+  };
+  auto fwd = [&](float (&S)[NR], const Raw& raw) __attribute__((always_inline)) {
     float a[NR], bb[NR], alpha[NR], w;
-    token(t, a, bb, alpha, w);
+    finish(raw, a, bb, alpha, w);
     float bx = 0.0f;
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
@@ -170,53 +236,53 @@ __global__ __launch_bounds__(512) void recurrent_bwd_kernel(Problem p, const In*
     for (int r = 0; r < NR; ++r) S[r] += a[r] * u;
   };
 
-  // ---- forward: checkpoints every kCB tokens ----
+  float* ck = wsl;                  // [nck][DK * 16]
+  float* cs = wsl + nck * DK * 16;  // [kCB][DK * 16]
   float S[NR];
   const size_t sbase = size_t(bh) * DK * size_t(dv);
 #pragma unroll
   for (int r = 0; r < NR; ++r) S[r] = p.s0 ? p.s0[sbase + size_t(row0 + r) * dv + col] : 0.0f;
+  Raw cur, nxt;
+  if (T > 0) load_raw(0, cur, false);
+  nxt = cur;
   for (int64_t t = 0; t < T; ++t) {
-    if (t % kCB == 0) {
-      float* ck = wsh + L.ckpt + (t / kCB) * DK * dv;
-#pragma unroll
-      for (int r = 0; r < NR; ++r) *st_addr(ck, r) = S[r];
-    }
-    fwd(S, t);
+    if (t + 1 < T) load_raw(t + 1, nxt, false);  // in flight during this token
+    if (t % kCB == 0) save(ck + (t / kCB) * DK * 16, S);
+    fwd(S, cur);
+    cur = nxt;
   }
 
-  // ---- backward, chunk by chunk in reverse ----
   float G[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) G[r] = dsf ? dsf[sbase + size_t(row0 + r) * dv + col] : 0.0f;
-  float* cs = wsh + L.cs;
-  float* part = wsh + L.part;
-  float* dwb = wsh + L.dw;
+  float* part = ws + L.part;
+  float* dwg = ws + L.dw;
   for (int64_t c = nck - 1; c >= 0; --c) {
     const int64_t t0 = c * kCB, t1 = min(T, t0 + kCB);
-    {  // recompute the states before each token of the chunk
-      float* ck = wsh + L.ckpt + c * DK * dv;
-#pragma unroll
-      for (int r = 0; r < NR; ++r) S[r] = *st_addr(ck, r);
-      for (int64_t t = t0; t < t1; ++t) {
-        float* dst = cs + (t - t0) * DK * dv;
-#pragma unroll
-        for (int r = 0; r < NR; ++r) *st_addr(dst, r) = S[r];
-        fwd(S, t);
-      }
+    restore(ck + c * DK * 16, S);
+    load_raw(t0, cur, false);
+    nxt = cur;
+    for (int64_t t = t0; t < t1; ++t) {  // the states before each token of the chunk
+      if (t + 1 < t1) load_raw(t + 1, nxt, false);
+      save(cs + (t - t0) * DK * 16, S);
+      fwd(S, cur);
+      cur = nxt;
     }
+    load_raw(t1 - 1, cur, true);
+    nxt = cur;
     for (int64_t t = t1 - 1; t >= t0; --t) {
-      const int tl = int(t - t0);
+      if (t > t0) load_raw(t - 1, nxt, true);  // in flight during this token
       float a[NR], bb[NR], alpha[NR], w, qv[NR];
-      token(t, a, bb, alpha, w);
+      finish(cur, a, bb, alpha, w);
       const int64_t th = (b * T + t) * H + h;
-      load_vec<NR>(q + th * DK + row0, qv);
-      const float doc = IO<In>::ld(d_o + th * dv + col);
+#pragma unroll
+      for (int i = 0; i < NR / 4; ++i) cvt(cur.qv[i], qv + 4 * i);
+      const float doc = ld(&cur.dout);
       float Sp[NR], X[NR];
-      const float* src = cs + int64_t(tl) * DK * dv;
+      restore(cs + (t - t0) * DK * 16, Sp);
       float bx = 0.0f;
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
-        Sp[r] = src[int64_t(row0 + r) * dv + col];
         X[r] = alpha[r] * Sp[r];
         bx += bb[r] * X[r];
       }
@@ -238,8 +304,8 @@ __global__ __launch_bounds__(512) void recurrent_bwd_kernel(Problem p, const In*
         dal[r] = dX * Sp[r];
         G[r] = alpha[r] * dX;
       }
-      if (gr == 0) dwb[int64_t(tl) * dv + col] = dw;
-      float* pw = part + (int64_t(wave) * kCB + tl) * 4 * DK;
+      if (gr == 0) dwg[th * dv + col] = dw;
+      float* pw = part + (int64_t(wave) * bth + th) * 4 * DK;
       float o4[4][RR::M];
       RR::run(dq, j, o4[0]);
       RR::run(da, j, o4[1]);
@@ -251,106 +317,131 @@ __global__ __launch_bounds__(512) void recurrent_bwd_kernel(Problem p, const In*
 #pragma unroll
           for (int i = 0; i < RR::M; ++i) pw[qd * DK + row0 + RR::row_of(j, i)] = o4[qd][i];
       }
+      cur = nxt;
     }
-    __syncthreads();
-    // ---- the chunk's gradients: partials summed over the slices in order, then the
-    // variant's chain rule; wave w takes tokens w, w + ns, ... ----
-    for (int64_t t = t0 + wave; t < t1; t += ns) {
-      const int tl = int(t - t0);
-      const int64_t th = (b * T + t) * H + h;
-      float sk = 0.0f, sv = 0.0f, sj = 0.0f, sal = 0.0f;  // per-token sums
-      const float sbeta = (p.variant == GDN_VARIANT_KDA || p.variant == GDN_VARIANT_GDN) ? sqrtf(ld(be + th)) : 1.0f;
-      const float e = p.variant == GDN_VARIANT_ASYM ? ld(et + th) : 0.0f;
-      for (int r = lane; r < DK; r += 64) {
-        float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int w2 = 0; w2 < ns; ++w2) {
-          const float* pr = part + (int64_t(w2) * kCB + tl) * 4 * DK;
+  }
+  if (ds0) {
 #pragma unroll
-          for (int qd = 0; qd < 4; ++qd) s4[qd] += pr[qd * DK + r];
-        }
-        const float dq = s4[0], dab = s4[1] + s4[2], dal = s4[3];
-        const int64_t ir = th * DK + r;
-        g.dq[ir] = dq;
-        const float kr = ld(k + ir);
-        if (p.variant == GDN_VARIANT_FG2) {
-          const float s = sqrtf(ld(be + ir));
-          g.dk[ir] = s * dab;
-          g.dalpha[ir] = dal;
-          float db = kr * dab;
-          if (!bev) db += ld(v + th * dv + r) * dwb[int64_t(tl) * dv + r];  // shared beta (dk == dv)
-          g.dbeta[ir] = db / (2.0f * s);
-        } else if (p.variant == GDN_VARIANT_ASYM) {
-          g.dk[ir] = s4[1];
-          g.dj[ir] = e * s4[2];
-          g.dalpha[ir] = dal;
-          sj += ld(jv + ir) * s4[2];
-        } else {
-          g.dk[ir] = sbeta * dab;
-          sk += kr * dab;
-          if (p.variant == GDN_VARIANT_KDA) g.dalpha[ir] = dal;
-          else sal += dal;
-        }
+    for (int r = 0; r < NR; ++r) ds0[sbase + size_t(row0 + r) * dv + col] = G[r];
+  }
+}
+
+// Kernel B: one wave per token-head: the partials summed over the slices in order,
+// then the variant's chain rule.
+template <typename In, int DK>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(Problem p, GradPtrs g, const float* __restrict__ ws) {
+  const int lane = threadIdx.x & 63;
+  const int64_t T = p.T, H = p.H, dv = p.dv;
+  const int ns = int(dv / 16);
+  const int64_t bth = p.B * T * H;
+  const BwdLayout L = bwd_layout(p.B, T, H, DK, dv);
+  const float* part = ws + L.part;
+  const float* dwg = ws + L.dw;
+  const In* k = static_cast<const In*>(p.k);
+  const In* v = static_cast<const In*>(p.v);
+  const In* be = static_cast<const In*>(p.beta);
+  const In* bev = static_cast<const In*>(p.beta_v);
+  const In* jv = static_cast<const In*>(p.j);
+  const In* et = static_cast<const In*>(p.eta);
+  auto ld = [](const In* x) { return IO<In>::ld(x); };
+  const int64_t stride = int64_t(gridDim.x) * (blockDim.x / 64);
+  for (int64_t th = int64_t(blockIdx.x) * (blockDim.x / 64) + (threadIdx.x >> 6); th < bth; th += stride) {
+    float sk = 0.0f, sv = 0.0f, sj = 0.0f, sal = 0.0f;  // per-token sums
+    const float sbeta = (p.variant == GDN_VARIANT_KDA || p.variant == GDN_VARIANT_GDN) ? sqrtf(ld(be + th)) : 1.0f;
+    const float e = p.variant == GDN_VARIANT_ASYM ? ld(et + th) : 0.0f;
+    for (int r = lane; r < DK; r += 64) {
+      float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int w2 = 0; w2 < ns; ++w2) {
+        const float* pr = part + (int64_t(w2) * bth + th) * 4 * DK;
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) s4[qd] += pr[qd * DK + r];
       }
-      for (int cc = lane; cc < dv; cc += 64) {
-        const float dw = dwb[int64_t(tl) * dv + cc];
-        const int64_t ic = th * dv + cc;
-        const float vc = ld(v + ic);
-        if (p.variant == GDN_VARIANT_FG2) {
-          if (bev) {
-            const float s = sqrtf(ld(bev + ic));
-            g.dv[ic] = s * dw;
-            g.dbeta_v[ic] = vc * dw / (2.0f * s);
-          } else {
-            g.dv[ic] = sqrtf(ld(be + th * DK + cc)) * dw;
-          }
-        } else if (p.variant == GDN_VARIANT_ASYM) {
-          g.dv[ic] = e * dw;
-          sv += vc * dw;
-        } else {
-          g.dv[ic] = sbeta * dw;
-          sv += vc * dw;
-        }
+      const float dab = s4[1] + s4[2], dal = s4[3];
+      const int64_t ir = th * DK + r;
+      g.dq[ir] = s4[0];
+      const float kr = ld(k + ir);
+      if (p.variant == GDN_VARIANT_FG2) {
+        const float s = sqrtf(ld(be + ir));
+        g.dk[ir] = s * dab;
+        g.dalpha[ir] = dal;
+        float db = kr * dab;
+        if (!bev) db += ld(v + th * dv + r) * dwg[th * dv + r];  // shared beta (dk == dv)
+        g.dbeta[ir] = db / (2.0f * s);
+      } else if (p.variant == GDN_VARIANT_ASYM) {
+        g.dk[ir] = s4[1];
+        g.dj[ir] = e * s4[2];
+        g.dalpha[ir] = dal;
+        sj += ld(jv + ir) * s4[2];
+      } else {
+        g.dk[ir] = sbeta * dab;
+        sk += kr * dab;
+        if (p.variant == GDN_VARIANT_KDA) g.dalpha[ir] = dal;
+        else sal += dal;
       }
-      if (p.variant == GDN_VARIANT_KDA || p.variant == GDN_VARIANT_GDN) {
-        const float tot = wave_sum(sk + sv);
-        if (lane == 0) g.dbeta[th] = tot / (2.0f * sbeta);
-        if (p.variant == GDN_VARIANT_GDN) {
-          const float ta = wave_sum(sal);
-          if (lane == 0) g.dalpha[th] = ta;
+    }
+    for (int cc = lane; cc < dv; cc += 64) {
+      const float dw = dwg[th * dv + cc];
+      const int64_t ic = th * dv + cc;
+      const float vc = ld(v + ic);
+      if (p.variant == GDN_VARIANT_FG2) {
+        if (bev) {
+          const float s = sqrtf(ld(bev + ic));
+          g.dv[ic] = s * dw;
+          g.dbeta_v[ic] = vc * dw / (2.0f * s);
+        } else {
+          g.dv[ic] = sqrtf(ld(be + th * DK + cc)) * dw;
         }
       } else if (p.variant == GDN_VARIANT_ASYM) {
-        const float tot = wave_sum(sj + sv);
-        if (lane == 0) g.deta[th] = tot;
+        g.dv[ic] = e * dw;
+        sv += vc * dw;
+      } else {
+        g.dv[ic] = sbeta * dw;
+        sv += vc * dw;
       }
     }
-    __syncthreads();
+    if (p.variant == GDN_VARIANT_KDA || p.variant == GDN_VARIANT_GDN) {
+      const float tot = wave_sum(sk + sv);
+      if (lane == 0) g.dbeta[th] = tot / (2.0f * sbeta);
+      if (p.variant == GDN_VARIANT_GDN) {
+        const float ta = wave_sum(sal);
+        if (lane == 0) g.dalpha[th] = ta;
+      }
+    } else if (p.variant == GDN_VARIANT_ASYM) {
+      const float tot = wave_sum(sj + sv);
+      if (lane == 0) g.deta[th] = tot;
+    }
   }
-  if (g.ds0) {
-#pragma unroll
-    for (int r = 0; r < NR; ++r) g.ds0[sbase + size_t(row0 + r) * dv + col] = G[r];
-  }
+}
+
+template <typename In, int DK>
+int launch_dk(const Problem& p, const In* dO, const float* dsf, const GradPtrs& g, float* ws, hipStream_t s) {
+  const unsigned slices = unsigned(p.B * p.H * (p.dv / 16));
+  bwd_slice_kernel<In, DK><<<dim3(slices), dim3(64), 0, s>>>(p, dO, dsf, g.ds0, ws);
+  int e = int(hipGetLastError());
+  if (e != 0 || p.T == 0) return e;
+  const int64_t waves = p.B * p.T * p.H;
+  const int64_t blocks = (waves + 3) / 4;
+  bwd_reduce_kernel<In, DK><<<dim3(unsigned(blocks < (int64_t(1) << 20) ? blocks : (int64_t(1) << 20))), dim3(256), 0, s>>>(p, g, ws);
+  return int(hipGetLastError());
 }
 
 template <typename In>
 int launch_in(const Problem& p, const void* d_o, const float* dsf, const GradPtrs& g, float* ws,
               hipStream_t s) {
-  const dim3 grid(unsigned(p.B * p.H));
-  const dim3 block(unsigned(64 * (p.dv / 16)));
   const In* dO = static_cast<const In*>(d_o);
   switch (p.dk) {
-    case 16: recurrent_bwd_kernel<In, 16><<<grid, block, 0, s>>>(p, dO, dsf, g, ws); break;
-    case 32: recurrent_bwd_kernel<In, 32><<<grid, block, 0, s>>>(p, dO, dsf, g, ws); break;
-    case 64: recurrent_bwd_kernel<In, 64><<<grid, block, 0, s>>>(p, dO, dsf, g, ws); break;
-    case 128: recurrent_bwd_kernel<In, 128><<<grid, block, 0, s>>>(p, dO, dsf, g, ws); break;
+    case 16: return launch_dk<In, 16>(p, dO, dsf, g, ws, s);
+    case 32: return launch_dk<In, 32>(p, dO, dsf, g, ws, s);
+    case 64: return launch_dk<In, 64>(p, dO, dsf, g, ws, s);
+    case 128: return launch_dk<In, 128>(p, dO, dsf, g, ws, s);
     default: return int(hipErrorInvalidValue);
   }
-  return int(hipGetLastError());
 }
 
 }  // namespace
 
 size_t bwd_workspace_bytes(const Problem& p) {
-  return size_t(p.B * p.H) * size_t(bwd_layout(p.T, p.dk, p.dv).per_head) * sizeof(float);
+  return size_t(bwd_layout(p.B, p.T, p.H, p.dk, p.dv).total) * sizeof(float);
 }
 
 int launch_recurrent_bwd(const Problem& p, const void* d_o, const float* dsf, const GradPtrs& g,
