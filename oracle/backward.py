@@ -22,7 +22,9 @@ Pinned by central finite differences in tests/test_oracle_backward.py.
 Inputs as for oracle.forward (library layouts, state [B, H, dk, dv]); d_o has the
 shape of o, ds_final (optional) the shape of the state. Returns a dict of float64
 gradients named after the inputs (dq, dk, dv, dalpha, dbeta, dbeta_v, dj, deta, ds0).
-DeltaProduct is not covered.
+DeltaProduct (DeltaProduct summary, "Approach") runs as its sequence of n_h
+Householder sub-steps per token (a = k_i, b = beta_i k_i, w = beta_i v_i, the gate
+as alpha at the first sub-step, q read after the last), through the same loop.
 """
 from __future__ import annotations
 
@@ -54,9 +56,45 @@ def _maps(inp):
     raise ValueError(f"no backward for variant {var!r}")
 
 
+def _deltaproduct(inp, d_o, s0, ds_final):
+    k, v = _f64(inp["k"]), _f64(inp["v"])          # [B, T, H, n_h, d]
+    beta, gate = _f64(inp["beta"]), _f64(inp["alpha"])
+    B, T, H, n, dk = k.shape
+    dv = v.shape[-1]
+    flat = lambda x: np.moveaxis(x, 3, 2).reshape(B, T * n, H, x.shape[-1])  # noqa: E731
+    a = flat(k)
+    bsub = flat(beta[..., None] * k)
+    w = flat(beta[..., None] * v)
+    al = np.ones((B, T, n, H, dk))
+    al[:, :, 0] = gate[..., None]
+    al = al.reshape(B, T * n, H, dk)
+    q = np.zeros((B, T, n, H, dk))
+    q[:, :, n - 1] = _f64(inp["q"])
+    do = np.zeros((B, T, n, H, dv))
+    do[:, :, n - 1] = _f64(d_o)
+    sub = {"variant": "sub", "a": a, "b": bsub, "w": w, "alpha": al,
+           "q": q.reshape(B, T * n, H, dk)}
+    g = _steps(sub, do.reshape(B, T * n, H, dv), s0, ds_final)
+    unflat = lambda x: np.moveaxis(x.reshape(B, T, n, H, x.shape[-1]), 2, 3)  # noqa: E731
+    da, db, dw, dal = unflat(g["da"]), unflat(g["db"]), unflat(g["dw"]), unflat(g["dal"])
+    return {"dq": unflat(g["dq"])[:, :, :, n - 1], "ds0": g["ds0"],
+            "dk": da + beta[..., None] * db, "dv": beta[..., None] * dw,
+            "dbeta": np.sum(k * db, -1) + np.sum(v * dw, -1),
+            "dalpha": np.sum(dal[:, :, :, 0], -1)}
+
+
 def backward(inp: dict, d_o, s0=None, ds_final=None) -> dict:
+    if inp["variant"] == "deltaproduct":
+        return _deltaproduct(inp, d_o, s0, ds_final)
     a, b, w, al = _maps(inp)
-    q = _f64(inp["q"])
+    g = _steps({"a": a, "b": b, "w": w, "alpha": al, "q": _f64(inp["q"])}, d_o, s0, ds_final)
+    da, db, dw, dal, dq = g["da"], g["db"], g["dw"], g["dal"], g["dq"]
+    return _chain(inp, da, db, dw, dal, dq, g["ds0"])
+
+
+def _steps(st: dict, d_o, s0, ds_final) -> dict:
+    """The reverse sweep over steps given per-step (a, b, w, alpha) and q."""
+    a, b, w, al, q = st["a"], st["b"], st["w"], st["alpha"], st["q"]
     do = _f64(d_o)
     B, T, H, dk = a.shape
     dv = w.shape[-1]
@@ -90,7 +128,11 @@ def backward(inp: dict, d_o, s0=None, ds_final=None) -> dict:
         dal[:, t] = np.sum(dX * Sp, axis=-1)
         G = al[:, t][..., None] * dX
 
-    out = {"dq": dq, "ds0": G}
+    return {"da": da, "db": db, "dw": dw, "dal": dal, "dq": dq, "ds0": G}
+
+
+def _chain(inp, da, db, dw, dal, dq, ds0) -> dict:
+    out = {"dq": dq, "ds0": ds0}
     var = inp["variant"]
     k, v = _f64(inp["k"]), _f64(inp["v"])
     if var == "fg2":

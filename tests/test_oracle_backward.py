@@ -8,7 +8,8 @@ import gdn_inputs
 import oracle
 from oracle import backward as bwd
 
-CASES = [("fg2", False), ("fg2", True), ("kda", False), ("gdn", False), ("asym", False)]
+CASES = [("fg2", False), ("fg2", True), ("kda", False), ("gdn", False), ("asym", False),
+         ("deltaproduct", False)]
 
 
 def _loss(inp, s0, do, dsf):
@@ -19,7 +20,8 @@ def _loss(inp, s0, do, dsf):
 @pytest.mark.parametrize("variant,plus", CASES, ids=lambda c: str(c))
 def test_gradients_match_finite_differences(variant, plus):
     B, T, H, d = 1, 5, 2, 3
-    inp = gdn_inputs.make_inputs(variant, B, T, H, d, d, dtype="f32", seed=80, fg2_plus=plus)
+    inp = gdn_inputs.make_inputs(variant, B, T, H, d, d, dtype="f32", seed=80, fg2_plus=plus,
+                                 n_h=3 if variant == "deltaproduct" else 1)
     for key in list(inp):
         if isinstance(inp[key], np.ndarray):
             inp[key] = inp[key].astype(np.float64)
