@@ -201,7 +201,7 @@ static int bwd_problem(const gdn_args* args, Problem* p) {
   if (a.o == nullptr) a.o = const_cast<void*>(a.q);  // not written by the backward pass
   int st = gdn::validate(&a, Entry::Recurrent, p);
   if (st != GDN_OK) return st;
-  if (p->variant == GDN_VARIANT_DELTAPRODUCT || p->stabilize != 0) return GDN_ERR_UNSUPPORTED;
+  if (p->stabilize != 0) return GDN_ERR_UNSUPPORTED;
   return GDN_OK;
 }
 

@@ -1,5 +1,5 @@
-// Backward pass of the token recurrence (reverse mode), every variant with one step a
-// token (FG2, FG2+, KDA, GDN, ASYM).
+// Backward pass of the token recurrence (reverse mode), every variant: FG2, FG2+, KDA,
+// GDN, ASYM, and DeltaProduct as its sequence of Householder sub-steps.
 //
 // Per token, with X = Diag(alpha) S_{t-1}, u = w - X^T b, S_t = X + a u^T,
 // o_t = S_t^T q_t and G = dL/dS_t (the later tokens' gradient plus q_t do_t^T):
@@ -32,6 +32,7 @@ struct BwdLayout {
   int64_t slice_floats, part, dw, total;
 };
 
+// T counts steps here (tokens x n_h for DeltaProduct, whose rows are sub-steps).
 __host__ __device__ inline BwdLayout bwd_layout(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv) {
   BwdLayout L;
   const int64_t nck = (T + kCB - 1) / kCB;
@@ -106,10 +107,12 @@ __global__ __launch_bounds__(64) void bwd_slice_kernel(Problem p, const In* __re
   const int64_t b = bh / H, h = bh % H;
   const int col = wave * 16 + j;
   const int row0 = gr * NR;
-  const BwdLayout L = bwd_layout(p.B, T, H, DK, dv);
+  const int nh = p.n_h;
+  const int64_t NS = p.steps;  // steps: tokens x n_h
+  const BwdLayout L = bwd_layout(p.B, NS, H, DK, dv);
   float* wsl = ws + int64_t(blockIdx.x) * L.slice_floats;
-  const int64_t nck = (T + kCB - 1) / kCB;
-  const int64_t bth = p.B * T * H;
+  const int64_t nck = (NS + kCB - 1) / kCB;
+  const int64_t bth = p.B * T * H * nh;  // step rows
 
   const In* q = static_cast<const In*>(p.q);
   const In* k = static_cast<const In*>(p.k);
@@ -128,6 +131,7 @@ __global__ __launch_bounds__(64) void bwd_slice_kernel(Problem p, const In* __re
   struct Raw {
     V4 k[NR / 4], x[NR / 4], y[NR / 4], qv[NR / 4];
     In s, vc, vb, dout;
+    bool first;  // DeltaProduct: the token's first step (the gate acts)
   };
   auto rows = [&](const In* base, V4 (&dst)[NR / 4]) __attribute__((always_inline)) {
 #pragma unroll
@@ -141,10 +145,29 @@ __global__ __launch_bounds__(64) void bwd_slice_kernel(Problem p, const In* __re
       o[2] = __uint_as_float(x.y << 16), o[3] = __uint_as_float(x.y & 0xffff0000u);
     }
   };
-  auto load_raw = [&](int64_t t, Raw& r, bool with_q) __attribute__((always_inline)) {
+  auto load_raw = [&](int64_t vs, Raw& r, bool with_q) __attribute__((always_inline)) {
+    const int64_t t = vs / nh;
+    const int sub = int(vs - t * nh);
     const int64_t th = (b * T + t) * H + h;
-    rows(k + th * DK + row0, r.k);
-    r.vc = v[th * dv + col];
+    const int64_t sr = th * nh + sub;  // step row ([B, T, H, n_h] for DeltaProduct)
+    rows(k + sr * DK + row0, r.k);
+    r.vc = v[sr * dv + col];
+    r.first = sub == 0;
+    if (p.variant == GDN_VARIANT_DELTAPRODUCT) {
+      r.s = be[sr];
+      r.vb = al[th];
+      if (with_q) {
+        if (sub == nh - 1) {
+          rows(q + th * DK + row0, r.qv);
+          r.dout = d_o[th * dv + col];
+        } else {  // q is read after the last step only
+#pragma unroll
+          for (int i = 0; i < NR / 4; ++i) r.qv[i] = V4{};
+          r.dout = In(0);
+        }
+      }
+      return;
+    }
     if (p.variant == GDN_VARIANT_ASYM) {
       r.s = et[th];
       rows(jv + th * DK + row0, r.y);
@@ -168,7 +191,16 @@ __global__ __launch_bounds__(64) void bwd_slice_kernel(Problem p, const In* __re
 #pragma unroll
     for (int i = 0; i < NR / 4; ++i) cvt(r.k[i], a + 4 * i);
     const float vc = ld(&r.vc);
-    if (p.variant == GDN_VARIANT_ASYM) {
+    if (p.variant == GDN_VARIANT_DELTAPRODUCT) {
+      const float bt = ld(&r.s);
+      const float gm = r.first ? ld(&r.vb) : 1.0f;
+#pragma unroll
+      for (int q2 = 0; q2 < NR; ++q2) {
+        bb[q2] = bt * a[q2];
+        alpha[q2] = gm;
+      }
+      w = bt * vc;
+    } else if (p.variant == GDN_VARIANT_ASYM) {
       const float e = ld(&r.s);
 #pragma unroll
       for (int i = 0; i < NR / 4; ++i) {
@@ -243,10 +275,10 @@ __global__ __launch_bounds__(64) void bwd_slice_kernel(Problem p, const In* __re
 #pragma unroll
   for (int r = 0; r < NR; ++r) S[r] = p.s0 ? p.s0[sbase + size_t(row0 + r) * dv + col] : 0.0f;
   Raw cur, nxt;
-  if (T > 0) load_raw(0, cur, false);
+  if (NS > 0) load_raw(0, cur, false);
   nxt = cur;
-  for (int64_t t = 0; t < T; ++t) {
-    if (t + 1 < T) load_raw(t + 1, nxt, false);  // in flight during this token
+  for (int64_t t = 0; t < NS; ++t) {
+    if (t + 1 < NS) load_raw(t + 1, nxt, false);  // in flight during this step
     if (t % kCB == 0) save(ck + (t / kCB) * DK * 16, S);
     fwd(S, cur);
     cur = nxt;
@@ -258,7 +290,7 @@ __global__ __launch_bounds__(64) void bwd_slice_kernel(Problem p, const In* __re
   float* part = ws + L.part;
   float* dwg = ws + L.dw;
   for (int64_t c = nck - 1; c >= 0; --c) {
-    const int64_t t0 = c * kCB, t1 = min(T, t0 + kCB);
+    const int64_t t0 = c * kCB, t1 = min(NS, t0 + kCB);
     restore(ck + c * DK * 16, S);
     load_raw(t0, cur, false);
     nxt = cur;
@@ -274,7 +306,7 @@ __global__ __launch_bounds__(64) void bwd_slice_kernel(Problem p, const In* __re
       if (t > t0) load_raw(t - 1, nxt, true);  // in flight during this token
       float a[NR], bb[NR], alpha[NR], w, qv[NR];
       finish(cur, a, bb, alpha, w);
-      const int64_t th = (b * T + t) * H + h;
+      const int64_t th = ((b * T + t / nh) * H + h) * nh + t % nh;  // step row
 #pragma unroll
       for (int i = 0; i < NR / 4; ++i) cvt(cur.qv[i], qv + 4 * i);
       const float doc = ld(&cur.dout);
@@ -333,8 +365,9 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(Problem p, GradPtrs g, 
   const int lane = threadIdx.x & 63;
   const int64_t T = p.T, H = p.H, dv = p.dv;
   const int ns = int(dv / 16);
-  const int64_t bth = p.B * T * H;
-  const BwdLayout L = bwd_layout(p.B, T, H, DK, dv);
+  const int nh = p.n_h;
+  const int64_t bth = p.B * T * H * nh;  // step rows
+  const BwdLayout L = bwd_layout(p.B, p.steps, H, DK, dv);
   const float* part = ws + L.part;
   const float* dwg = ws + L.dw;
   const In* k = static_cast<const In*>(p.k);
@@ -346,6 +379,36 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(Problem p, GradPtrs g, 
   auto ld = [](const In* x) { return IO<In>::ld(x); };
   const int64_t stride = int64_t(gridDim.x) * (blockDim.x / 64);
   for (int64_t th = int64_t(blockIdx.x) * (blockDim.x / 64) + (threadIdx.x >> 6); th < bth; th += stride) {
+    if (p.variant == GDN_VARIANT_DELTAPRODUCT) {  // th is a step row (token x n_h + step)
+      const int64_t tok = th / nh;
+      const int sub = int(th - tok * nh);
+      const float bt = ld(be + th);
+      float sb = 0.0f, sal = 0.0f;
+      for (int r = lane; r < DK; r += 64) {
+        float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int w2 = 0; w2 < ns; ++w2) {
+          const float* pr = part + (int64_t(w2) * bth + th) * 4 * DK;
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) s4[qd] += pr[qd * DK + r];
+        }
+        g.dk[th * DK + r] = s4[1] + bt * s4[2];
+        sb += ld(k + th * DK + r) * s4[2];
+        sal += s4[3];
+        if (sub == nh - 1) g.dq[tok * DK + r] = s4[0];
+      }
+      for (int cc = lane; cc < dv; cc += 64) {
+        const float dw = dwg[th * dv + cc];
+        g.dv[th * dv + cc] = bt * dw;
+        sb += ld(v + th * dv + cc) * dw;
+      }
+      const float tb = wave_sum(sb);
+      if (lane == 0) g.dbeta[th] = tb;
+      if (sub == 0) {
+        const float ta = wave_sum(sal);
+        if (lane == 0) g.dalpha[tok] = ta;  // the gate acts at the first step
+      }
+      continue;
+    }
     float sk = 0.0f, sv = 0.0f, sj = 0.0f, sal = 0.0f;  // per-token sums
     const float sbeta = (p.variant == GDN_VARIANT_KDA || p.variant == GDN_VARIANT_GDN) ? sqrtf(ld(be + th)) : 1.0f;
     const float e = p.variant == GDN_VARIANT_ASYM ? ld(et + th) : 0.0f;
@@ -419,7 +482,7 @@ int launch_dk(const Problem& p, const In* dO, const float* dsf, const GradPtrs& 
   bwd_slice_kernel<In, DK><<<dim3(slices), dim3(64), 0, s>>>(p, dO, dsf, g.ds0, ws);
   int e = int(hipGetLastError());
   if (e != 0 || p.T == 0) return e;
-  const int64_t waves = p.B * p.T * p.H;
+  const int64_t waves = p.B * p.T * p.H * p.n_h;
   const int64_t blocks = (waves + 3) / 4;
   bwd_reduce_kernel<In, DK><<<dim3(unsigned(blocks < (int64_t(1) << 20) ? blocks : (int64_t(1) << 20))), dim3(256), 0, s>>>(p, g, ws);
   return int(hipGetLastError());
@@ -441,7 +504,7 @@ int launch_in(const Problem& p, const void* d_o, const float* dsf, const GradPtr
 }  // namespace
 
 size_t bwd_workspace_bytes(const Problem& p) {
-  return size_t(bwd_layout(p.B, p.T, p.H, p.dk, p.dv).total) * sizeof(float);
+  return size_t(bwd_layout(p.B, p.steps, p.H, p.dk, p.dv).total) * sizeof(float);
 }
 
 int launch_recurrent_bwd(const Problem& p, const void* d_o, const float* dsf, const GradPtrs& g,

@@ -189,10 +189,11 @@ typedef struct gdn_grads {
 size_t gdn_bwd_workspace_bytes(const gdn_args* args);
 
 /* Backward pass (reverse-mode gradients) of the token recurrence for every variant
- * with one step a token (FG2, FG2+, KDA, GDN, ASYM; DELTAPRODUCT returns
- * GDN_ERR_UNSUPPORTED). The pages give the forward pass only; this is the derivative
- * of the same recurrence (FG2-GDN reading notes, section 2.2 eq. (11), section 2.3
- * eq. (13); GDN2-stability page, eq. (1)). args as for the forward pass (o, s_final
+ * (FG2, FG2+, KDA, GDN, ASYM, and DELTAPRODUCT through its Householder sub-steps,
+ * DeltaProduct summary, "Approach"; dalpha is then the gate's gradient [B, T, H]).
+ * The pages give the forward pass only; this is the derivative of the same recurrence
+ * (FG2-GDN reading notes, section 2.2 eq. (11), section 2.3 eq. (13); GDN2-stability
+ * page, eq. (1)). gdn_args.stabilize must be 0 (GDN_ERR_UNSUPPORTED otherwise). args as for the forward pass (o, s_final
  * and chunk are ignored; s0 NULL means zero); d_o [B, T, H, dv] in args->dtype is
  * dL/do; d_s_final [B, H, dk, dv] float32 is dL/dS_T (NULL: zero). Gradients with
  * respect to beta and beta_v are singular at 0 (their square roots enter the step).

@@ -147,7 +147,7 @@ def test_backward_checks(lib):
     assert call(a, None) == -1
     assert call(a, GdnGrads(dq=FAKE, dk=FAKE, dv=FAKE, dalpha=FAKE)) == -1          # dbeta missing
     assert call(a, GdnGrads(dq=FAKE, dk=FAKE, dv=FAKE, dalpha=FAKE, dbeta=FAKE, dj=FAKE)) == -1
-    assert call(good_args(variant=3, n_h=2), full) == -2                              # DeltaProduct
+    assert call(good_args(variant=4, j=FAKE, eta=FAKE, stabilize=1), GdnGrads(dq=FAKE, dk=FAKE, dv=FAKE, dalpha=FAKE, dj=FAKE, deta=FAKE)) == -2
     assert lib.gdn_bwd_workspace_bytes(ctypes.byref(good_args(dk=48))) == 0
 
 

@@ -24,6 +24,8 @@ CASES = [  # variant, fg2_plus, dtype, B, T, H, dk, dv
     ("asym", False, "f32", 1, 100, 2, 64, 64),
     ("fg2", False, "bf16", 1, 150, 2, 128, 128),
     ("asym", False, "bf16", 1, 66, 1, 128, 64),
+    ("deltaproduct", False, "f32", 1, 50, 2, 64, 64),     # 2 steps a token
+    ("deltaproduct", False, "bf16", 1, 27, 2, 128, 128),  # 3 steps a token
 ]
 
 
@@ -32,7 +34,8 @@ def test_backward_vs_oracle(case):
     import gated_delta_rule_69_amd as gdn
     from gpu_util import DEV, host, state_to_dev, to_dev
     var, plus, dt, B, T, H, dk, dv = case
-    inp = gdn_inputs.make_inputs(var, B, T, H, dk, dv, dtype=dt, seed=90, fg2_plus=plus)
+    n_h = (2 if T % 2 == 0 else 3) if var == "deltaproduct" else 1
+    inp = gdn_inputs.make_inputs(var, B, T, H, dk, dv, dtype=dt, seed=90, fg2_plus=plus, n_h=n_h)
     rng = np.random.default_rng(91)
     s0 = gdn_inputs.make_state(B, H, dk, dv, seed=92)
     do = rng.standard_normal((B, T, H, dv)).astype(np.float32)
