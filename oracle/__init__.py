@@ -15,7 +15,8 @@ Modules
   stabilize   the GDN2 stabilisers (decay clip, j projection), token-wise
   backward    reverse-mode gradients of the token recurrence (all variants but
               DeltaProduct), pinned by finite differences of ``recurrence``
-  metrics     rel-L2 and normwise max-rel error
+  metrics     rel-L2 and normwise max-rel error (pinned by hand-computed values
+              in tests/test_oracle_metrics.py)
 
 Parity status: every function in ``recurrence`` is pinned by tests that do not
 go through it (explicit matrix products, special-case reductions between the
