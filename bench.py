@@ -78,8 +78,8 @@ def _oracle_one(args):
                for k, v in _CPU_INP.items()}
         sub["B"], sub["H"], sub["T"] = 1, 1, T
         t0 = time.perf_counter()
-        o, _ = oracle.forward(sub)
-        return b, h, o[0, :, 0].astype(np.float32), time.perf_counter() - t0
+        o, S = oracle.forward(sub)
+        return b, h, o[0, :, 0].astype(np.float32), S[0, 0], time.perf_counter() - t0
 
 
 def cpu_model():
@@ -93,14 +93,21 @@ def cpu_model():
     return "unknown"
 
 
+# Worker processes of the CPU leg: every core the process may run on, up to the 16
+# host cores that go with one GPU on the measurement boxes.
+CPU_WORKERS_MAX = 16
+
+
 def cpu_baseline(inp, T_sample):
+    """The oracle over every (batch, head) sequence of the workload, first T_sample
+    tokens each; returns the baseline record and the per-head results (o, S)."""
     global _CPU_INP
     _CPU_INP = inp
     try:
         ncpu = len(os.sched_getaffinity(0))
     except AttributeError:
         ncpu = os.cpu_count() or 1
-    workers = max(1, min(16, ncpu))
+    workers = max(1, min(CPU_WORKERS_MAX, ncpu))
     pairs = [(b, h) for b in range(inp["B"]) for h in range(inp["H"])]
     ctx = mp.get_context("fork")
     t0 = time.perf_counter()
@@ -108,10 +115,33 @@ def cpu_baseline(inp, T_sample):
         res = pool.map(_oracle_one, [(b, h, T_sample) for b, h in pairs])
     wall = time.perf_counter() - t0
     tokens = len(pairs) * T_sample / inp["H"]     # metric tokens carry all H heads
-    return dict(value=tokens / wall, unit="tokens/s", cores=workers, kind="oracle", cpu_model=cpu_model(),
+    return dict(value=tokens / wall, unit="tokens/s", cores=workers, affinity_cores=ncpu, kind="oracle",
+                cpu_model=cpu_model(),
                 sample=f"all {len(pairs)} (batch, head) sequences of the workload, first {T_sample} "
                        f"of {inp['T']} tokens each (B*{T_sample} metric tokens); float64 token "
                        f"loop, {workers} worker processes, one thread each; wall {wall:.1f} s"), res
+
+
+def parity_check(o_dev, s_dev, res, tol):
+    """o and S_T of every sequence the oracle ran, against it: rel-L2 and normwise
+    max-rel over the whole tensors and the worst single sequence."""
+    import oracle
+    o_host = o_dev.float().cpu().numpy()
+    s_host = s_dev.float().cpu().numpy()
+    T = res[0][2].shape[0]
+    got_o = np.stack([o_host[b, :T, h] for b, h, _, _, _ in res])
+    ref_o = np.stack([r[2] for r in res])
+    got_s = np.stack([s_host[b, h] for b, h, _, _, _ in res])
+    ref_s = np.stack([r[3] for r in res])
+    out = dict(sequences=len(res), tokens=int(T), tolerance=dict(tol),
+               o_rel_l2=oracle.rel_l2(got_o, ref_o), o_max_rel=oracle.max_rel(got_o, ref_o),
+               S_rel_l2=oracle.rel_l2(got_s, ref_s), S_max_rel=oracle.max_rel(got_s, ref_s),
+               worst_sequence_o_rel_l2=max(oracle.rel_l2(g, r) for g, r in zip(got_o, ref_o)),
+               worst_sequence_S_rel_l2=max(oracle.rel_l2(g, r) for g, r in zip(got_s, ref_s)))
+    out["pass"] = bool(max(out["o_rel_l2"], out["S_rel_l2"], out["worst_sequence_o_rel_l2"],
+                           out["worst_sequence_S_rel_l2"]) <= tol["rel_l2"]
+                       and max(out["o_max_rel"], out["S_max_rel"]) <= tol["max_rel"])
+    return out
 
 
 def source_sha256():
@@ -505,7 +535,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=16384)
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="tokens per sequence for the oracle leg (default: all)")
     ap.add_argument("--profile-driver", action="store_true",
                     help="only run the workload for rocprofv3 counter collection")
     ap.add_argument("--configs", action="store_true",
@@ -553,7 +584,7 @@ def main():
     cpu_res = []
     if not args.no_cpu_baseline:
         log("bench: oracle CPU baseline")
-        cpu, cpu_res = cpu_baseline(inp, min(args.cpu_tokens, T))
+        cpu, cpu_res = cpu_baseline(inp, min(args.cpu_tokens, T) if args.cpu_tokens > 0 else T)
         log(f"bench: cpu {cpu['value']:.1f} tokens/s on {cpu['cores']} cores")
 
     import torch
@@ -616,14 +647,10 @@ def main():
 
     parity = None
     if cpu_res:
-        o_host = o.float().cpu().numpy()
-        errs = []
-        for b, h, o_ref, _ in cpu_res:
-            got = o_host[b, :o_ref.shape[0], h]
-            errs.append(float(np.linalg.norm(got - o_ref) / np.linalg.norm(o_ref)))
-        parity = dict(o_rel_l2_max=max(errs), heads=len(errs), tokens=int(cpu_res[0][2].shape[0]),
-                      tolerance=5e-3)
-        log(f"bench: parity vs oracle, max rel-L2 {max(errs):.2e} over {len(errs)} heads")
+        parity = parity_check(o, s_final, cpu_res, dict(rel_l2=5e-3, max_rel=2e-2))
+        log(f"bench: parity vs oracle over {parity['sequences']} sequences x {parity['tokens']} tokens: "
+            f"o {parity['o_rel_l2']:.2e} / {parity['o_max_rel']:.2e}, S {parity['S_rel_l2']:.2e} / "
+            f"{parity['S_max_rel']:.2e} -> {'pass' if parity['pass'] else 'FAIL'}")
 
     out = {
         "metric": METRIC,
@@ -647,6 +674,9 @@ def main():
         "parity": parity,
     }
     print(json.dumps(out), flush=True)
+    if parity is not None and not parity["pass"]:
+        log("bench: the results are outside the parity tolerance")
+        sys.exit(1)
 
 
 if __name__ == "__main__":

@@ -13,9 +13,12 @@
 //   O  = Q+ S + P U,  Q+ = Q . e^{G},  P = tril_incl(Q+ A-^T)
 // This is the diagonal-plus-rank-1 chunk recursion that the FG2-GDN reading
 // notes (section 2.4) inherit from KDA's WY/UT algorithm, written out for the
-// unified step. The Gram factors use a reference point in the middle of the
-// chunk (e^{G - G_mid}, e^{G_mid - G}) so that no factor exceeds the decay
-// accumulated over half a chunk.
+// unified step. No factor e^{G_i - G_j} is formed whole: with one decay per step
+// (GDN, DeltaProduct) the Gram products carry no decay and their entries are
+// multiplied by e^{G_i - G_j} <= 1 afterwards; with per-channel decay every factor
+// is split at a reference point inside the chunk's 16-step tiles (the first and
+// last rows of a tile for its off-diagonal blocks, its row 7 for the diagonal
+// block), so that none exceeds the decay of 8 steps.
 //
 // Kernel 1 (chunk_prep): persistent; each workgroup walks chunks. Wave w owns
 // rows 16w..16w+15 of the chunk: it loads them straight into registers (16-byte
@@ -240,14 +243,18 @@ struct alignas(16) PrepLds {
   using Op = std::conditional_t<F16, _Float16, float>;
   using Am = std::conditional_t<F16, __bf16, float>;
   static constexpr int NT = C / 16;
-  static constexpr int LDA = F16 ? DK + 8 : DK + 4;  // rows of A- (16-byte aligned)
+  static constexpr int LDA = F16 ? DK + 8 : DK + 4;  // rows of the A sides (16-byte aligned)
   static constexpr int LDC = C + 4;
   static constexpr int QR = DPV ? C / 2 : 1;         // output rows kept in LDS (n_h >= 2)
   union RA {
     struct {
+      float L[NT][DK];         // tile totals of the log decay, per channel
+      float m[NT][DK];         // in-tile prefix at each tile's row 7
+    } stg;                     // decay staging, read by the per-channel pass
+    struct {
       Am hi[C][LDA];
       Am lo[F16 ? C : 1][LDA];
-    } am;                      // A- (mid reference), Gram phase
+    } am;                      // A sides of the Gram blocks, one 16-row slot per tile
     struct {
       float m[C][LDC];         // strictly lower Gram M; T in fp16 after the inverse
       float t[C][LDC];         // T = (I + M)^{-1}
@@ -256,14 +263,20 @@ struct alignas(16) PrepLds {
   Op bt[DK][LDC];              // B+ (chunk-start reference), transposed
   Op wvt[128][LDC];            // written values (scaled), transposed
   Op at[F16 ? 1 : DK][LDC];    // A^ transposed, staged for a coalesced copy (fp32 path)
-  Am qmh[QR][LDA];             // Q+ (mid reference) of output rows, DeltaProduct only
+  Am qmh[QR][LDA];             // Q of output rows (no decay), DeltaProduct only
   Am qml[(DPV && F16) ? QR : 1][LDA];
-  float tot[NT][DK];           // per-tile totals of the log decay
-  float gmid_loc[DK];          // in-tile prefix at the middle row
-  // per-channel decay constants. bf16 path (base 2): [t] = G_mid - (prefix before
-  // tile t), [NT] = 2^G_mid, [NT+1] = 2^(G_C - G_mid). fp32 path (base e): [t] =
-  // prefix before tile t, [NT] = G_mid, [NT+1] = G_C.
-  float chv[NT + 2][DK];
+  union CU {
+    struct {
+      // per tile t and channel: [0] m_t, [1] e^m_t, [2] e^(L_t - m_t), [3] e^(sum of
+      // L before t), [4] e^(sum of L after t) (base 2 on the bf16 path)
+      float cst[NT][5][DK];
+      float dfac[NT == 4 ? 2 : 1][DK];  // e^L_1 and e^L_2 (chunk 64)
+    } v;                       // per-channel decay
+    struct {
+      float ltot[4];           // tile totals of the scalar log decay
+      float grow[C];           // log decay from the chunk start through each row
+    } s;                       // scalar decay
+  } cu;
   float qs[C];                 // per output row q scale
   float red[kWaves];
 };
@@ -287,6 +300,7 @@ __global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk
   static_assert(!DPV || DP, "multi-step rows are DeltaProduct only");
   constexpr bool CH_ALPHA = V == GDN_VARIANT_FG2 || V == GDN_VARIANT_KDA || V == GDN_VARIANT_ASYM;
   constexpr bool CH_BJ = V == GDN_VARIANT_FG2 || V == GDN_VARIANT_ASYM;  // per-channel beta / j
+  constexpr bool SCALAR = !CH_ALPHA;  // one log decay per row (GDN, DeltaProduct)
   using Sm = PrepLds<F16, DK, C, DPV>;
   using Op = typename Sm::Op;
   using KM = ChanMap<F16, DK>;
@@ -312,7 +326,6 @@ __global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk
   const int H = int(p.H);
   const int BH = int(p.B) * H;
   const int total = NC * BH;  // < 2^31 (checked on the host)
-  const int mid = C / 2 - 1, tile_mid = mid / 16, row_mid = mid % 16;
   const In* qg = static_cast<const In*>(p.q);
   const In* kg = static_cast<const In*>(p.k);
   const In* vg = static_cast<const In*>(p.v);
@@ -561,16 +574,19 @@ __global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk
 
     // The raw rows are consumed: the next item's loads go out part by part.
     if (has_next) prefetch(wn, raw, 0);
-    // inclusive scan of the log decay over the tile's 16 rows, then tile totals
+    // inclusive scan of the log decay over each 16-row tile; the tile totals (row
+    // 15) and the prefixes at row 7 go to LDS
+    if constexpr (SCALAR) {
+      G[0] = scan16(G[0]);
+      if (owner && li == 15 && lg == 0) sm.cu.s.ltot[wave] = G[0];
+    } else {
 #pragma unroll
-    for (int x = 0; x < NX; ++x) G[x] = scan16(G[x]);
-    if (owner && li == 15) {
+      for (int x = 0; x < NX; ++x) G[x] = scan16(G[x]);
+      if (owner && (li == 15 || li == 7)) {
+        float* dst = li == 15 ? &sm.ra.stg.L[wave][0] : &sm.ra.stg.m[wave][0];
 #pragma unroll
-      for (int x = 0; x < NX; ++x) sm.tot[wave][KM::chan(lg, x)] = G[x];
-    }
-    if (owner && wave == tile_mid && li == row_mid) {
-#pragma unroll
-      for (int x = 0; x < NX; ++x) sm.gmid_loc[KM::chan(lg, x)] = G[x];
+        for (int x = 0; x < NX; ++x) dst[KM::chan(lg, x)] = G[x];
+      }
     }
     // power-of-two scales: per output row for q, per chunk for the written values
     float qsc = 1.0f;
@@ -589,30 +605,48 @@ __global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk
     }
     __syncthreads();
 
-    // ---- per-channel decay constants (one thread per key channel) ----
-    if (tid < DK) {
+    // ---- decay constants (the reference points of chunk_prep2_kernel; base e on
+    // the fp32 path): scalar decay per row, per-channel decay per tile ----
+    float gabs = 0.0f, eg_row = 1.0f, eat_row = 1.0f;
+    if constexpr (SCALAR) {
+      float pre = 0.0f, gc = 0.0f;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float lt = sm.cu.s.ltot[t];
+        if (t < wave) pre += lt;
+        gc += lt;
+      }
+      gabs = pre + G[0];                                       // G of this row
+      eg_row = path_exp<F16>(gabs);                            // e^{G}
+      eat_row = path_exp<F16>(fminf(gc - gabs, 0.0f));         // e^{G_C - G}
+      if (owner && lg == 0) sm.cu.s.grow[r] = gabs;
+      if (tid < DK) gam_g[tid] = path_exp<F16>(gc);
+    } else if (tid < DK) {
       const int c = tid;
-      float pre = 0.0f, gm = sm.gmid_loc[c];
-      float pres[NT];
+      float Lt[NT], mt[NT];
 #pragma unroll
-      for (int I = 0; I < NT; ++I) {
-        pres[I] = pre;
-        if (I < tile_mid) gm += sm.tot[I][c];
-        pre += sm.tot[I][c];
+      for (int t = 0; t < NT; ++t) {
+        Lt[t] = sm.ra.stg.L[t][c];
+        mt[t] = sm.ra.stg.m[t][c];
       }
-      const float ge = pre;
-      if constexpr (F16) {
+      float pre = 0.0f;
 #pragma unroll
-        for (int I = 0; I < NT; ++I) sm.chv[I][c] = gm - pres[I];
-        sm.chv[NT][c] = path_exp<F16>(gm);
-        sm.chv[NT + 1][c] = path_exp<F16>(ge - gm);
-      } else {
+      for (int t = 0; t < NT; ++t) {
+        float suf = 0.0f;
 #pragma unroll
-        for (int I = 0; I < NT; ++I) sm.chv[I][c] = pres[I];
-        sm.chv[NT][c] = gm;
-        sm.chv[NT + 1][c] = ge;
+        for (int t2 = t + 1; t2 < NT; ++t2) suf += Lt[t2];
+        sm.cu.v.cst[t][0][c] = mt[t];
+        sm.cu.v.cst[t][1][c] = path_exp<F16>(mt[t]);          // e^{G_7 - G_start}
+        sm.cu.v.cst[t][2][c] = path_exp<F16>(Lt[t] - mt[t]);  // e^{G_end - G_7}
+        sm.cu.v.cst[t][3][c] = path_exp<F16>(pre);            // e^{G_start}
+        sm.cu.v.cst[t][4][c] = path_exp<F16>(suf);            // e^{G_C - G_end}
+        pre += Lt[t];
       }
-      gam_g[c] = path_exp<F16>(ge);
+      if constexpr (NT == 4) {
+        sm.cu.v.dfac[0][c] = path_exp<F16>(Lt[1]);
+        sm.cu.v.dfac[1][c] = path_exp<F16>(Lt[2]);
+      }
+      gam_g[c] = path_exp<F16>(pre);
     }
     float wsc = 1.0f;
     if constexpr (F16) {
@@ -625,53 +659,75 @@ __global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk
     __syncthreads();
 
     // ---- decayed operands of this wave's rows ----
-    float bm[NX];  // B+ with the mid reference: B-side of M
-    float qm[NX];  // Q+ with the mid reference: B-side of P
+    // Per-channel decay (reference points as in chunk_prep2_kernel): B and Q sides of
+    // the off-diagonal Gram blocks at the tile's first row (registers), A side at its
+    // last row (LDS slot = tile; the last tile's A side is never an off-diagonal
+    // operand, and with chunk 64 slot 3 holds tile 0's A side at the reference
+    // between tiles 1 and 2), the diagonal blocks at the tile's row 7, on fp32 MFMA
+    // from registers. Scalar decay: the Gram operands carry no decay.
+    float bm[NX];  // B side of the off-diagonal (scalar decay: every) Gram block
+    float qm[NX];  // Q side likewise
 #pragma unroll
     for (int x = 0; x < NX; ++x) bm[x] = qm[x] = 0.0f;
+    float4v mdg = {0.0f, 0.0f, 0.0f, 0.0f}, pdg = {0.0f, 0.0f, 0.0f, 0.0f};  // diagonal M^T, P^T
     if (owner) {
 #pragma unroll
       for (int u = 0; u < NX / UW; ++u) {
         const int c0 = KM::chan(lg, u * UW);  // UW consecutive channels
-        float cof[UW], cp[UW], cq[UW];
+        float cm[UW], c7[UW], c157[UW], cP[UW], cQ[UW];
+        if constexpr (!SCALAR) {
 #pragma unroll
-        for (int e = 0; e < UW; e += 4) {
-          const float4 x0 = *reinterpret_cast<const float4*>(&sm.chv[wave][c0 + e]);
-          const float4 x1 = *reinterpret_cast<const float4*>(&sm.chv[NT][c0 + e]);
-          const float4 x2 = *reinterpret_cast<const float4*>(&sm.chv[NT + 1][c0 + e]);
-          cof[e] = x0.x, cof[e + 1] = x0.y, cof[e + 2] = x0.z, cof[e + 3] = x0.w;
-          cp[e] = x1.x, cp[e + 1] = x1.y, cp[e + 2] = x1.z, cp[e + 3] = x1.w;
-          cq[e] = x2.x, cq[e + 1] = x2.y, cq[e + 2] = x2.z, cq[e + 3] = x2.w;
+          for (int e = 0; e < UW; e += 4) {
+            float* dsts[5] = {cm, c7, c157, cP, cQ};
+#pragma unroll
+            for (int k5 = 0; k5 < 5; ++k5) {
+              const float4 x = *reinterpret_cast<const float4*>(&sm.cu.v.cst[wave][k5][c0 + e]);
+              dsts[k5][e] = x.x, dsts[k5][e + 1] = x.y, dsts[k5][e + 2] = x.z, dsts[k5][e + 3] = x.w;
+            }
+          }
         }
         float amv[UW];
         half8 xbt = {}, xat = {};  // fp16 B+ and A^ of the group (bf16 path)
 #pragma unroll
         for (int e = 0; e < UW; ++e) {
           const int x = u * UW + e, c = c0 + e;
-          float fup, eg, eat, eam;
-          if constexpr (F16) {
-            fup = path_exp<F16>(G[x] - cof[e]);  // e^{G - G_mid}
-            eam = __builtin_amdgcn_rcpf(fup);    // e^{G_mid - G}
-            eg = cp[e] * fup;                    // e^{G}
-            eat = cq[e] * eam;                   // e^{G_C - G}
+          float bplus, ahat, qplus;
+          if constexpr (SCALAR) {
+            amv[e] = a[x];
+            bm[x] = bb[x];
+            qm[x] = qv[x];
+            bplus = bb[x] * eg_row;
+            ahat = a[x] * eat_row;
+            qplus = qv[x] * eg_row;
           } else {
-            const float g = G[x] + cof[e];
-            fup = expf(g - cp[e]);
-            eg = expf(g);
-            eat = expf(cq[e] - g);
-            eam = expf(cp[e] - g);
+            float fup, eam;  // e^{G - G_7}, e^{G_7 - G}
+            if constexpr (F16) {
+              fup = path_exp<F16>(G[x] - cm[e]);
+              eam = __builtin_amdgcn_rcpf(fup);
+            } else {
+              fup = expf(G[x] - cm[e]);
+              eam = expf(cm[e] - G[x]);
+            }
+            const float st = fup * c7[e];    // e^{G - G_start}
+            const float te = eam * c157[e];  // e^{G_end - G}
+            amv[e] = a[x] * te;
+            bm[x] = bb[x] * st;
+            qm[x] = qv[x] * st;
+            bplus = bm[x] * cP[e];
+            ahat = amv[e] * cQ[e];
+            qplus = qm[x] * cP[e];
+            const float ad = a[x] * eam;
+            mdg = __builtin_amdgcn_mfma_f32_16x16x4f32(ad, bb[x] * fup, mdg, 0, 0, 0);
+            pdg = __builtin_amdgcn_mfma_f32_16x16x4f32(ad, qv[x] * fup, pdg, 0, 0, 0);
           }
-          bm[x] = bb[x] * fup;
           if constexpr (F16) {
-            xbt[e] = (_Float16)(bb[x] * eg);
-            xat[e] = (_Float16)(a[x] * eat);
+            xbt[e] = (_Float16)bplus;
+            xat[e] = (_Float16)ahat;
           } else {
-            sm.bt[c][r] = (Op)(bb[x] * eg);
-            sm.at[c][r] = (Op)(a[x] * eat);
+            sm.bt[c][r] = (Op)bplus;
+            sm.at[c][r] = (Op)ahat;
           }
-          amv[e] = a[x] * eam;
-          qm[x] = qv[x] * fup;
-          qv[x] = qv[x] * eg * qsc;  // Q+ (chunk-start reference), scaled
+          qv[x] = qplus * qsc;  // Q+ (chunk-start reference), scaled
         }
         if constexpr (F16) {
           // B+ and A^ of this row group transposed by MFMA (product with a 0/1
@@ -697,24 +753,35 @@ __global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk
             *reinterpret_cast<uint2*>(adst) = pa.u[0];
           }
         }
-        // A- row group: bf16 hi / lo (or fp32), one vector store each
-        if constexpr (F16) {
-          H8 hi, lo;
+        // A side: bf16 hi / lo (or fp32), one vector store each, to slot `row`
+        auto store_a = [&](int row, const float* v8) __attribute__((always_inline)) {
+          if constexpr (F16) {
+            H8 hi, lo;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float v = e < UW ? amv[e < UW ? e : 0] : 0.0f;
-            hi.b[e] = (__bf16)v;
-            lo.b[e] = (__bf16)(v - (float)hi.b[e]);
-          }
-          if constexpr (UW == 8) {
-            *reinterpret_cast<uint4*>(&sm.ra.am.hi[r][c0]) = hi.q;
-            *reinterpret_cast<uint4*>(&sm.ra.am.lo[r][c0]) = lo.q;
+            for (int e = 0; e < 8; ++e) {
+              const float v = e < UW ? v8[e < UW ? e : 0] : 0.0f;
+              hi.b[e] = (__bf16)v;
+              lo.b[e] = (__bf16)(v - (float)hi.b[e]);
+            }
+            if constexpr (UW == 8) {
+              *reinterpret_cast<uint4*>(&sm.ra.am.hi[row][c0]) = hi.q;
+              *reinterpret_cast<uint4*>(&sm.ra.am.lo[row][c0]) = lo.q;
+            } else {
+              *reinterpret_cast<uint2*>(&sm.ra.am.hi[row][c0]) = hi.u[0];
+              *reinterpret_cast<uint2*>(&sm.ra.am.lo[row][c0]) = lo.u[0];
+            }
           } else {
-            *reinterpret_cast<uint2*>(&sm.ra.am.hi[r][c0]) = hi.u[0];
-            *reinterpret_cast<uint2*>(&sm.ra.am.lo[r][c0]) = lo.u[0];
+            *reinterpret_cast<float4*>(&sm.ra.am.hi[row][c0]) = make_float4(v8[0], v8[1], v8[2], v8[3]);
           }
-        } else {
-          *reinterpret_cast<float4*>(&sm.ra.am.hi[r][c0]) = make_float4(amv[0], amv[1], amv[2], amv[3]);
+        };
+        if (SCALAR || wave < NT - 1) store_a(r, amv);
+        if constexpr (!SCALAR && NT == 4) {
+          if (wave == 0) {  // tile 0's A side at the reference between tiles 1 and 2
+            float mv[UW];
+#pragma unroll
+            for (int e = 0; e < UW; ++e) mv[e] = amv[e] * sm.cu.v.dfac[0][c0 + e];
+            store_a(48 + li, mv);
+          }
         }
         if constexpr (DPV) {
           if (w.out_row) {
@@ -816,27 +883,23 @@ __global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk
       for (int u = tid; u < UNITS; u += kThreads) dst[u] = src[u];
     }
 
-    // ---- Gram tiles: M^T(J, I) = A-(J) B+(I)^T and P^T(J, Io) = A-(J) Q+(Io)^T ----
-    // The B side (own rows) is split into bf16 hi/lo once per item.
-    H8 bmh[F16 ? KB : 1], bml[F16 ? KB : 1], qmh8[F16 ? KB : 1], qml8[F16 ? KB : 1];
-    if constexpr (F16) {
+    // ---- Gram tiles: M^T(J, I) = A(J) B(I)^T and P^T(J, I) = A(J) Q(I)^T ----
+    // Block k of a wave pairs LDS slot slot_of(k) with this wave's B / Q side; with
+    // per-channel decay and chunk 64, tile 3 multiplies its sides by e^{L_2} for
+    // blocks 0 and 1 (the reference between tiles 1 and 2).
+    constexpr bool MOVE = !SCALAR && NT == 4;
+    float fxv[MOVE ? NX : 1];
 #pragma unroll
-      for (int u = 0; u < KB; ++u) {
+    for (int x = 0; x < (MOVE ? NX : 1); ++x) fxv[x] = 1.0f;
+    if constexpr (MOVE) {
+      if (wave == 3) {
 #pragma unroll
-        for (int s2 = 0; s2 < 8; ++s2) {
-          const float v0 = s2 < UW ? bm[u * UW + (s2 < UW ? s2 : 0)] : 0.0f;
-          const float v1 = s2 < UW ? qm[u * UW + (s2 < UW ? s2 : 0)] : 0.0f;
-          const __bf16 h0 = (__bf16)v0, h1 = (__bf16)v1;
-          bmh[u].b[s2] = h0;
-          bml[u].b[s2] = (__bf16)(v0 - (float)h0);
-          qmh8[u].b[s2] = h1;
-          qml8[u].b[s2] = (__bf16)(v1 - (float)h1);
-        }
+        for (int x = 0; x < NX; ++x) fxv[x] = sm.cu.v.dfac[1][KM::chan(lg, x)];
       }
     }
-    // A side from LDS rows of tile J; B side from registers (own rows) or LDS.
-    auto gram = [&](int J, const H8* xh, const H8* xl, const float* xb, int qrow_lds)
-        __attribute__((always_inline)) -> float4v {
+    auto slot_of = [&](int k) -> int { return (MOVE && k == 0 && wave >= 2) ? 3 : k; };
+    // B side from registers (times fxv when `moved`)
+    auto gram = [&](int slot, const float* xb, bool moved) __attribute__((always_inline)) -> float4v {
       float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
       if constexpr (F16) {
 #pragma unroll
@@ -844,25 +907,18 @@ __global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk
           const int c0 = u * 4 * UW + UW * lg;
           H8 ah, al, bh, bl;
           if constexpr (UW == 8) {
-            ah.q = *reinterpret_cast<const uint4*>(&sm.ra.am.hi[16 * J + li][c0]);
-            al.q = *reinterpret_cast<const uint4*>(&sm.ra.am.lo[16 * J + li][c0]);
+            ah.q = *reinterpret_cast<const uint4*>(&sm.ra.am.hi[16 * slot + li][c0]);
+            al.q = *reinterpret_cast<const uint4*>(&sm.ra.am.lo[16 * slot + li][c0]);
           } else {
-            ah = pair4(&sm.ra.am.hi[16 * J + li][c0], nullptr);
-            al = pair4(&sm.ra.am.lo[16 * J + li][c0], nullptr);
+            ah = pair4(&sm.ra.am.hi[16 * slot + li][c0], nullptr);
+            al = pair4(&sm.ra.am.lo[16 * slot + li][c0], nullptr);
           }
-          if (qrow_lds >= 0) {
-            if constexpr (DPV) {
-              if constexpr (UW == 8) {
-                bh.q = *reinterpret_cast<const uint4*>(&sm.qmh[qrow_lds][c0]);
-                bl.q = *reinterpret_cast<const uint4*>(&sm.qml[qrow_lds][c0]);
-              } else {
-                bh = pair4(&sm.qmh[qrow_lds][c0], nullptr);
-                bl = pair4(&sm.qml[qrow_lds][c0], nullptr);
-              }
-            }
-          } else {
-            bh = xh[u];
-            bl = xl[u];
+#pragma unroll
+          for (int s2 = 0; s2 < 8; ++s2) {
+            const int x = u * UW + (s2 < UW ? s2 : 0);
+            const float v = s2 < UW ? xb[x] * (MOVE && moved ? fxv[MOVE ? x : 0] : 1.0f) : 0.0f;
+            bh.b[s2] = (__bf16)v;
+            bl.b[s2] = (__bf16)(v - (float)bh.b[s2]);
           }
           acc = mma_pair_bf16(ah.b, bh.b, acc);
           acc = mma_pair_bf16(ah.b, bl.b, acc);
@@ -872,76 +928,73 @@ __global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk
 #pragma unroll
         for (int t = 0; t < KB; ++t) {
           float a4[4], b4[4];
-          quad(&sm.ra.am.hi[16 * J + li][16 * t + 4 * lg], a4);
-          if (qrow_lds >= 0) {
-            if constexpr (DPV) quad(&sm.qmh[qrow_lds][16 * t + 4 * lg], b4);
-          } else {
+          quad(&sm.ra.am.hi[16 * slot + li][16 * t + 4 * lg], a4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) b4[e] = xb[4 * t + e];
+          for (int e = 0; e < 4; ++e) {
+            const int x = 4 * t + e;
+            b4[e] = xb[x] * (MOVE && moved ? fxv[MOVE ? x : 0] : 1.0f);
           }
           acc = mma_slice_f32(a4, b4, acc);
         }
       }
       return acc;
     };
-
-    float4v mreg[NT];
+    // B side from the LDS copy of output row qrow (DeltaProduct's output rows)
+    auto gram_q = [&](int slot, int qrow) __attribute__((always_inline)) -> float4v {
+      float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (DPV) {
+        if constexpr (F16) {
 #pragma unroll
-    for (int J = 0; J < NT; ++J) mreg[J] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-    if constexpr (F16 && !DPV) {
-      // M and P tiles of every J together, k-block outer: 2 NT independent
-      // accumulator chains interleave (tiles above the diagonal are computed and
-      // masked, which costs no time: the last wave computes all of them anyway).
-      float4v preg[NT];
-#pragma unroll
-      for (int J = 0; J < NT; ++J) preg[J] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-      if (owner) {
-#pragma unroll
-        for (int u = 0; u < KB; ++u) {
-          const int c0 = u * 4 * UW + UW * lg;
-          H8 ah[NT], al[NT];
-#pragma unroll
-          for (int J = 0; J < NT; ++J) {
+          for (int u = 0; u < KB; ++u) {
+            const int c0 = u * 4 * UW + UW * lg;
+            H8 ah, al, bh, bl;
             if constexpr (UW == 8) {
-              ah[J].q = *reinterpret_cast<const uint4*>(&sm.ra.am.hi[16 * J + li][c0]);
-              al[J].q = *reinterpret_cast<const uint4*>(&sm.ra.am.lo[16 * J + li][c0]);
+              ah.q = *reinterpret_cast<const uint4*>(&sm.ra.am.hi[16 * slot + li][c0]);
+              al.q = *reinterpret_cast<const uint4*>(&sm.ra.am.lo[16 * slot + li][c0]);
+              bh.q = *reinterpret_cast<const uint4*>(&sm.qmh[qrow][c0]);
+              bl.q = *reinterpret_cast<const uint4*>(&sm.qml[qrow][c0]);
             } else {
-              ah[J] = pair4(&sm.ra.am.hi[16 * J + li][c0], nullptr);
-              al[J] = pair4(&sm.ra.am.lo[16 * J + li][c0], nullptr);
+              ah = pair4(&sm.ra.am.hi[16 * slot + li][c0], nullptr);
+              al = pair4(&sm.ra.am.lo[16 * slot + li][c0], nullptr);
+              bh = pair4(&sm.qmh[qrow][c0], nullptr);
+              bl = pair4(&sm.qml[qrow][c0], nullptr);
             }
+            acc = mma_pair_bf16(ah.b, bh.b, acc);
+            acc = mma_pair_bf16(ah.b, bl.b, acc);
+            acc = mma_pair_bf16(al.b, bh.b, acc);
           }
+        } else {
 #pragma unroll
-          for (int J = 0; J < NT; ++J) mreg[J] = mma_pair_bf16(ah[J].b, bmh[u].b, mreg[J]);
-#pragma unroll
-          for (int J = 0; J < NT; ++J) preg[J] = mma_pair_bf16(ah[J].b, qmh8[u].b, preg[J]);
-#pragma unroll
-          for (int J = 0; J < NT; ++J) mreg[J] = mma_pair_bf16(ah[J].b, bml[u].b, mreg[J]);
-#pragma unroll
-          for (int J = 0; J < NT; ++J) preg[J] = mma_pair_bf16(ah[J].b, qml8[u].b, preg[J]);
-#pragma unroll
-          for (int J = 0; J < NT; ++J) mreg[J] = mma_pair_bf16(al[J].b, bmh[u].b, mreg[J]);
-#pragma unroll
-          for (int J = 0; J < NT; ++J) preg[J] = mma_pair_bf16(al[J].b, qmh8[u].b, preg[J]);
-        }
-        if (want_out) {  // output rows are this wave's own rows
-          const int ro = 16 * wave + li;
-          const float qsl = sm.qs[ro];
-#pragma unroll
-          for (int J = 0; J < NT; ++J) {
-            const int s0 = 16 * J + 4 * lg;
-            Op* dst = FRAG ? P_g + p_frag(ro, J) : P_g + size_t(ro) * L.ldc + s0;
-            H8 h8;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) h8.h[e] = (_Float16)((s0 + e <= ro) ? preg[J][e] * qsl : 0.0f);
-            *reinterpret_cast<uint2*>(dst) = h8.u[0];
+          for (int t = 0; t < KB; ++t) {
+            float a4[4], b4[4];
+            quad(&sm.ra.am.hi[16 * slot + li][16 * t + 4 * lg], a4);
+            quad(&sm.qmh[qrow][16 * t + 4 * lg], b4);
+            acc = mma_slice_f32(a4, b4, acc);
           }
         }
       }
-    } else {
+      return acc;
+    };
+    // scalar decay: e^{G_i - G_j} of the entries j = 16 J + 4 lg + e of row i (G_i = gi)
+    auto decay4 = [&](int J, float gi, float f[4]) __attribute__((always_inline)) {
+      if constexpr (SCALAR) {
+        const float4 gj = *reinterpret_cast<const float4*>(&sm.cu.s.grow[16 * J + 4 * lg]);
+        f[0] = path_exp<F16>(fminf(gi - gj.x, 0.0f));
+        f[1] = path_exp<F16>(fminf(gi - gj.y, 0.0f));
+        f[2] = path_exp<F16>(fminf(gi - gj.z, 0.0f));
+        f[3] = path_exp<F16>(fminf(gi - gj.w, 0.0f));
+      } else {
+        f[0] = f[1] = f[2] = f[3] = 1.0f;
+      }
+    };
+
+    float4v mreg[NT];  // M^T(J, wave): every J <= wave (scalar decay) or J < wave
+#pragma unroll
+    for (int J = 0; J < NT; ++J) mreg[J] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
     if (owner) {
 #pragma unroll
       for (int J = 0; J < NT; ++J) {
-        if (J <= wave) mreg[J] = gram(J, bmh, bml, bm, -1);
+        if (SCALAR ? J <= wave : J < wave) mreg[J] = gram(slot_of(J), bm, J < 2);
       }
     }
     if (want_out) {
@@ -952,50 +1005,60 @@ __global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk
 #pragma unroll
           for (int J = 0; J < NT; ++J) {
             float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (J <= wave) acc = gram(J, qmh8, qml8, qm, -1);
+            if (SCALAR ? J <= wave : J < wave) acc = gram(slot_of(J), qm, J < 2);
+            if (!SCALAR && J == wave) acc = pdg;
+            float f[4];
+            decay4(J, gabs, f);
             const int s0 = 16 * J + 4 * lg;
             Op* dst = FRAG ? P_g + p_frag(ro, J) : P_g + size_t(ro) * L.ldc + s0;
             if constexpr (F16) {
               H8 h8;
 #pragma unroll
-              for (int e = 0; e < 4; ++e) h8.h[e] = (_Float16)((s0 + e <= ro) ? acc[e] * qsl : 0.0f);
+              for (int e = 0; e < 4; ++e) h8.h[e] = (_Float16)((s0 + e <= ro) ? acc[e] * f[e] * qsl : 0.0f);
               *reinterpret_cast<uint2*>(dst) = h8.u[0];
             } else {
-              *reinterpret_cast<float4*>(dst) = make_float4((s0 + 0 <= ro) ? acc[0] : 0.0f, (s0 + 1 <= ro) ? acc[1] : 0.0f,
-                                                            (s0 + 2 <= ro) ? acc[2] : 0.0f, (s0 + 3 <= ro) ? acc[3] : 0.0f);
+              *reinterpret_cast<float4*>(dst) =
+                  make_float4((s0 + 0 <= ro) ? acc[0] * f[0] : 0.0f, (s0 + 1 <= ro) ? acc[1] * f[1] : 0.0f,
+                              (s0 + 2 <= ro) ? acc[2] * f[2] : 0.0f, (s0 + 3 <= ro) ? acc[3] * f[3] : 0.0f);
             }
           }
         }
       } else {
+        // DeltaProduct (scalar decay): output row ro reads the state after step tau
         if (wave < RT) {
           const int ro = 16 * wave + li;
           const int tau = ro * n_h + n_h - 1;
           const int jmax = min(NT - 1, ((16 * wave + 15) * n_h + n_h - 1) / 16);
           const float qsl = sm.qs[ro];
+          const float gtau = sm.cu.s.grow[tau];
           for (int J = 0; J < NT; ++J) {
             float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (J <= jmax) acc = gram(J, qmh8, qml8, qm, ro);
+            if (J <= jmax) acc = gram_q(J, ro);
+            float f[4];
+            decay4(J, gtau, f);
             const int s0 = 16 * J + 4 * lg;
             Op* dst = FRAG ? P_g + p_frag(ro, J) : P_g + size_t(ro) * L.ldc + s0;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dst[e] = (Op)((s0 + e <= tau) ? acc[e] * qsl : 0.0f);
+            for (int e = 0; e < 4; ++e) dst[e] = (Op)((s0 + e <= tau) ? acc[e] * f[e] * qsl : 0.0f);
           }
         }
       }
     }
-    }  // generic Gram path
     if (has_next) prefetch(wn, raw, 2);
-    __syncthreads();  // A- is dead: its space now holds M and T
+    __syncthreads();  // the A sides are dead: their space now holds M and T
     if (owner) {
 #pragma unroll
       for (int J = 0; J < NT; ++J) {
         if (J <= wave) {
+          const float4v src = (!SCALAR && J == wave) ? mdg : mreg[J];
+          float f[4];
+          decay4(J, gabs, f);
           const int s0 = 16 * J + 4 * lg;
           float4 m4;
-          m4.x = (s0 + 0 < r) ? mreg[J][0] : 0.0f;
-          m4.y = (s0 + 1 < r) ? mreg[J][1] : 0.0f;
-          m4.z = (s0 + 2 < r) ? mreg[J][2] : 0.0f;
-          m4.w = (s0 + 3 < r) ? mreg[J][3] : 0.0f;
+          m4.x = (s0 + 0 < r) ? src[0] * f[0] : 0.0f;
+          m4.y = (s0 + 1 < r) ? src[1] * f[1] : 0.0f;
+          m4.z = (s0 + 2 < r) ? src[2] * f[2] : 0.0f;
+          m4.w = (s0 + 3 < r) ? src[3] * f[3] : 0.0f;
           *reinterpret_cast<float4*>(&sm.ra.mt.m[r][s0]) = m4;
         }
       }
@@ -1189,9 +1252,13 @@ __global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk
 struct alignas(16) PrepLds2 {
   union RA {
     struct {
+      float L[4][128];      // tile totals of the log decay (base 2), per channel
+      float m[4][128];      // in-tile prefix at each tile's row 7
+    } stg;                  // decay staging, read by the per-channel pass
+    struct {
       __bf16 hi[64][136];
       __bf16 lo[64][136];
-    } am;                   // A- (mid reference), Gram phase
+    } am;                   // A side of the off-diagonal Gram blocks, four 16-row slots
     struct {
       float m[64][68];      // strictly lower Gram M; T in fp16 after the inverse
       float t[64][68];      // T = (I + M)^{-1}
@@ -1199,9 +1266,18 @@ struct alignas(16) PrepLds2 {
   } ra;
   _Float16 bt[128][68];     // B+ (chunk-start reference), transposed
   _Float16 wvt[128][68];    // written values (scaled), transposed
-  float tot[4][128];        // per-tile totals of the log decay (base 2)
-  float gmid_loc[128];      // in-tile prefix at the middle row
-  float chv[6][128];        // [t] G_mid - prefix before tile t, [4] 2^G_mid, [5] 2^(G_C - G_mid)
+  union CU {
+    struct {
+      // per tile t and channel: [0] m_t, [1] 2^m_t, [2] 2^(L_t - m_t), [3] 2^(sum of
+      // L before t), [4] 2^(sum of L after t)
+      float cst[4][5][128];
+      float dfac[2][128];   // 2^L_1 and 2^L_2 (decay across tiles 1 and 2)
+    } v;                    // per-channel decay
+    struct {
+      float ltot[4];        // tile totals of the scalar log decay
+      float grow[64];       // log decay from the chunk start through each row
+    } s;                    // scalar decay
+  } cu;
   float red[kWaves];
 };
 
@@ -1229,9 +1305,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
   constexpr int TPC = C / NH;  // tokens per chunk
   constexpr bool CH_ALPHA = V == GDN_VARIANT_FG2 || V == GDN_VARIANT_KDA || V == GDN_VARIANT_ASYM;
   constexpr bool CH_BJ = V == GDN_VARIANT_FG2 || V == GDN_VARIANT_ASYM;  // per-channel beta / j
+  constexpr bool SCALAR = !CH_ALPHA;  // one log decay per row (GDN, DeltaProduct)
   using Sm = PrepLds2;
   static_assert(sizeof(Sm) <= 80 * 1024, "two workgroups per CU");
-  constexpr int mid = C / 2 - 1, tile_mid = mid / 16, row_mid = mid % 16;
   __shared__ Sm sm;
 
   // Lane indices are re-derived at the top of every item from an opaque copy of
@@ -1428,7 +1504,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
     // patterns (for non-negative values the order of the patterns is the order of
     // the values), two at a time; the written values' scale uses the bound
     // max |v| max sqrt(beta) of the row, which keeps the scaled values below 2^13.
-    float G[32];
+    float G[SCALAR ? 1 : 32];
     ushort2v qm2 = {0, 0}, vm2 = {0, 0}, bm2 = {0, 0};
     auto absmax2 = [](ushort2v m, uint32_t w) __attribute__((always_inline)) {
       return __builtin_elementwise_max(m, __builtin_bit_cast(ushort2v, w & 0x7fff7fffu));
@@ -1438,33 +1514,42 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
     };
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
+      if constexpr (!SCALAR) {
 #pragma unroll
-      for (int s2 = 0; s2 < 8; ++s2) {
-        const int x = 8 * u + s2;
-        if constexpr (STAB == 1) G[x] = valid ? __builtin_amdgcn_logf(stab_decay(stc, bf(raw.a[u], s2))) : 0.0f;
-        else if constexpr (CH_ALPHA) G[x] = valid ? __builtin_amdgcn_logf(bf(raw.a[u], s2)) : 0.0f;
-        else G[x] = glog;
+        for (int s2 = 0; s2 < 8; ++s2) {
+          const int x = 8 * u + s2;
+          if constexpr (STAB == 1) G[x] = valid ? __builtin_amdgcn_logf(stab_decay(stc, bf(raw.a[u], s2))) : 0.0f;
+          else G[x] = valid ? __builtin_amdgcn_logf(bf(raw.a[u], s2)) : 0.0f;
+        }
       }
       vm2 = absmax8(vm2, raw.v[u]);
       if (want_out) qm2 = absmax8(qm2, raw.q[u]);
       if constexpr (V == GDN_VARIANT_FG2) bm2 = absmax8(bm2, raw.b[u]);
     }
+    if constexpr (SCALAR) G[0] = glog;
     auto bits_max = [](ushort2v m) __attribute__((always_inline)) {
       return __uint_as_float(uint32_t(m.x > m.y ? m.x : m.y) << 16);
     };
     const float qmax = (valid && orow) ? bits_max(qm2) : 0.0f;
     float wmax = bits_max(vm2) * (V == GDN_VARIANT_FG2 ? (valid ? __builtin_amdgcn_sqrtf(bits_max(bm2)) : 0.0f)
                                                          : fabsf(wscal));
-    // inclusive scan of the log decay over the tile's 16 rows, then tile totals
+    // inclusive scan of the log decay over each 16-row tile; the tile totals (row
+    // 15) and the prefixes at row 7 go to LDS
+    if constexpr (SCALAR) {
+      G[0] = scan16(G[0]);
+      if (li == 15 && lg == 0) sm.cu.s.ltot[wave] = G[0];
+    } else {
 #pragma unroll
-    for (int x = 0; x < 32; ++x) G[x] = scan16(G[x]);
-    if (li == 15) {
+      for (int x = 0; x < 32; ++x) G[x] = scan16(G[x]);
+      if (li == 15 || li == 7) {
+        float* dst = li == 15 ? &sm.ra.stg.L[wave][0] : &sm.ra.stg.m[wave][0];
 #pragma unroll
-      for (int x = 0; x < 32; ++x) sm.tot[wave][32 * (x / 8) + 8 * lg + x % 8] = G[x];
-    }
-    if (wave == tile_mid && li == row_mid) {
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int x = 0; x < 32; ++x) sm.gmid_loc[32 * (x / 8) + 8 * lg + x % 8] = G[x];
+          for (int e = 0; e < 8; e += 4)
+            *reinterpret_cast<float4*>(dst + 32 * u + 8 * lg + e) =
+                make_float4(G[8 * u + e], G[8 * u + e + 1], G[8 * u + e + 2], G[8 * u + e + 3]);
+      }
     }
     // power-of-two scales: per output row for q, per chunk for the written values
     const float qsc = want_out ? pow2_scale_for(max_over_groups(qmax)) : 1.0f;
@@ -1472,21 +1557,50 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
     if (lane == 0) sm.red[wave] = wmax;
     wg_barrier();
 
-    // ---- per-channel decay constants (one thread per key channel) ----
-    if (tid < DK) {
-      const int c = tid;
-      float pre = 0.0f, gm = sm.gmid_loc[c];
-      float pres[NT];
+    // ---- decay constants ----
+    // Scalar decay: every factor is a function of the row alone; the Gram entries
+    // take e^{G_i - G_j} after the product. Per-channel decay: one thread per key
+    // channel writes the constants of every 16-row tile t (reference points: the
+    // tile's first row for the B and Q sides, its last row for the A side, its row
+    // 7 for the diagonal block), so that no factor exceeds the decay of the eight
+    // steps around row 7, and none of the cross-tile factors exceeds 1.
+    float gabs = 0.0f, eg_row = 1.0f, eat_row = 1.0f;
+    if constexpr (SCALAR) {
+      float pre = 0.0f, gc = 0.0f;
 #pragma unroll
-      for (int I = 0; I < NT; ++I) {
-        pres[I] = pre;
-        if (I < tile_mid) gm += sm.tot[I][c];
-        pre += sm.tot[I][c];
+      for (int t = 0; t < NT; ++t) {
+        const float lt = sm.cu.s.ltot[t];
+        if (t < wave) pre += lt;
+        gc += lt;
       }
+      gabs = pre + G[0];                                         // G of this row
+      eg_row = __builtin_amdgcn_exp2f(gabs);                     // e^{G}
+      eat_row = __builtin_amdgcn_exp2f(fminf(gc - gabs, 0.0f));  // e^{G_C - G}
+      if (lg == 0) sm.cu.s.grow[r] = gabs;
+      if (tid < DK) gam_g[tid] = __builtin_amdgcn_exp2f(gc);
+    } else if (tid < DK) {
+      const int c = tid;
+      float Lt[NT], mt[NT];
 #pragma unroll
-      for (int I = 0; I < NT; ++I) sm.chv[I][c] = gm - pres[I];
-      sm.chv[NT][c] = __builtin_amdgcn_exp2f(gm);
-      sm.chv[NT + 1][c] = __builtin_amdgcn_exp2f(pre - gm);
+      for (int t = 0; t < NT; ++t) {
+        Lt[t] = sm.ra.stg.L[t][c];
+        mt[t] = sm.ra.stg.m[t][c];
+      }
+      float pre = 0.0f;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        float suf = 0.0f;
+#pragma unroll
+        for (int t2 = t + 1; t2 < NT; ++t2) suf += Lt[t2];
+        sm.cu.v.cst[t][0][c] = mt[t];
+        sm.cu.v.cst[t][1][c] = __builtin_amdgcn_exp2f(mt[t]);          // e^{G_7 - G_start}
+        sm.cu.v.cst[t][2][c] = __builtin_amdgcn_exp2f(Lt[t] - mt[t]);  // e^{G_end - G_7}
+        sm.cu.v.cst[t][3][c] = __builtin_amdgcn_exp2f(pre);            // e^{G_start}
+        sm.cu.v.cst[t][4][c] = __builtin_amdgcn_exp2f(suf);            // e^{G_C - G_end}
+        pre += Lt[t];
+      }
+      sm.cu.v.dfac[0][c] = __builtin_amdgcn_exp2f(Lt[1]);
+      sm.cu.v.dfac[1][c] = __builtin_amdgcn_exp2f(Lt[2]);
       gam_g[c] = __builtin_amdgcn_exp2f(pre);
     }
     float wsc;
@@ -1502,20 +1616,35 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
 
     // ---- phase 2: decayed operands and written values of this wave's rows, one
     // channel group at a time ----
+    // Off-diagonal Gram blocks M(I, J), P(I, J), J < I, with per-channel decay: B and
+    // Q sides of tile I referenced to its first row (kept in fp32 until the Gram
+    // phase), A side of tile J to its last row (LDS slot J); block (3, 2) pairs
+    // them directly, blocks (I, 0..1) of the lower half pair them through the
+    // reference between tiles 1 and 2: slot 3 holds tile 0's A side moved there
+    // (times e^{L_1}), and tile 3's B and Q sides move back to it (times e^{L_2}) in
+    // the Gram phase. Tile 3's own A side is never an off-diagonal operand. The
+    // diagonal blocks use row 7 of the tile on both sides and run here, on fp32
+    // MFMA straight from registers (the A and B operand layouts of a 16-row tile
+    // are the same).
     const float wrow = (V == GDN_VARIANT_FG2 ? 1.0f : wscal) * wsc;  // written-value factor of the row
-    H8 bmh[KB], bml[KB], qmh8[KB], qml8[KB];  // B sides of the Grams (bf16 hi / lo)
+    float bsv[SCALAR ? 1 : 32], qsv[SCALAR ? 1 : 32];                // B and Q sides (per-channel decay)
+    H8 bmh[SCALAR ? KB : 1], bml[SCALAR ? KB : 1], qmh8[SCALAR ? KB : 1], qml8[SCALAR ? KB : 1];  // (scalar)
+    float4v mdg = {0.0f, 0.0f, 0.0f, 0.0f}, pdg = {0.0f, 0.0f, 0.0f, 0.0f};  // diagonal blocks M^T, P^T
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const int c0 = 32 * u + 8 * lg;  // 8 consecutive channels
-      float cof[8], cp[8], cq[8];
-#pragma unroll
-      for (int e = 0; e < 8; e += 4) {
-        const float4 x0 = *reinterpret_cast<const float4*>(&sm.chv[wave][c0 + e]);
-        const float4 x1 = *reinterpret_cast<const float4*>(&sm.chv[NT][c0 + e]);
-        const float4 x2 = *reinterpret_cast<const float4*>(&sm.chv[NT + 1][c0 + e]);
-        cof[e] = x0.x, cof[e + 1] = x0.y, cof[e + 2] = x0.z, cof[e + 3] = x0.w;
-        cp[e] = x1.x, cp[e + 1] = x1.y, cp[e + 2] = x1.z, cp[e + 3] = x1.w;
-        cq[e] = x2.x, cq[e + 1] = x2.y, cq[e + 2] = x2.z, cq[e + 3] = x2.w;
+      float cm[8], c7[8], c157[8], cP[8], cQ[8];
+      if constexpr (!SCALAR) {
+        auto ld8 = [&](const float* src, float* d) __attribute__((always_inline)) {
+          const float4 x0 = *reinterpret_cast<const float4*>(src);
+          const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+          d[0] = x0.x, d[1] = x0.y, d[2] = x0.z, d[3] = x0.w, d[4] = x1.x, d[5] = x1.y, d[6] = x1.z, d[7] = x1.w;
+        };
+        ld8(&sm.cu.v.cst[wave][0][c0], cm);
+        ld8(&sm.cu.v.cst[wave][1][c0], c7);
+        ld8(&sm.cu.v.cst[wave][2][c0], c157);
+        ld8(&sm.cu.v.cst[wave][3][c0], cP);
+        ld8(&sm.cu.v.cst[wave][4][c0], cQ);
       }
       const uint4 kr = raw.k[u], vr = raw.v[u];
       uint4 br = {}, qr = {};
@@ -1523,6 +1652,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
       if (want_out && valid && orow) qr = raw.q[u];
       half8 xbt, xat, xv;
       H8 hi, lo, qp;
+      float aev[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float kf = bf(kr, e);
@@ -1540,26 +1670,57 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
           bb = bscal * a;
         }
         if constexpr (V != GDN_VARIANT_FG2) xv[e] = (_Float16)(bf(vr, e) * wrow);
-        const float fup = __builtin_amdgcn_exp2f(G[8 * u + e] - cof[e]);  // e^{G - G_mid}
-        const float eam = __builtin_amdgcn_rcpf(fup);                     // e^{G_mid - G}
-        const float eg = cp[e] * fup;                                     // e^{G}
-        const float eat = cq[e] * eam;                                    // e^{G_C - G}
-        xbt[e] = (_Float16)(bb * eg);
-        xat[e] = (_Float16)(a * eat);
-        const float am = a * eam;
-        hi.b[e] = (__bf16)am;
-        lo.b[e] = (__bf16)(am - (float)hi.b[e]);
-        const float bm = bb * fup;
-        bmh[u].b[e] = (__bf16)bm;
-        bml[u].b[e] = (__bf16)(bm - (float)bmh[u].b[e]);
         const float qf = bf(qr, e);
-        const float qm = qf * fup;
-        qmh8[u].b[e] = (__bf16)qm;
-        qml8[u].b[e] = (__bf16)(qm - (float)qmh8[u].b[e]);
-        qp.h[e] = (_Float16)(qf * eg * qsc);
+        if constexpr (SCALAR) {
+          hi.b[e] = (__bf16)a;
+          lo.b[e] = (__bf16)(a - (float)hi.b[e]);
+          bmh[u].b[e] = (__bf16)bb;
+          bml[u].b[e] = (__bf16)(bb - (float)bmh[u].b[e]);
+          qmh8[u].b[e] = (__bf16)qf;
+          qml8[u].b[e] = (__bf16)(qf - (float)qmh8[u].b[e]);
+          xbt[e] = (_Float16)(bb * eg_row);
+          xat[e] = (_Float16)(a * eat_row);
+          qp.h[e] = (_Float16)(qf * eg_row * qsc);
+        } else {
+          const int x = 8 * u + e;
+          const float fup = __builtin_amdgcn_exp2f(G[x] - cm[e]);  // e^{G - G_7}
+          const float eam = __builtin_amdgcn_rcpf(fup);            // e^{G_7 - G}
+          const float st = fup * c7[e];                            // e^{G - G_start}
+          const float te = eam * c157[e];                          // e^{G_end - G}
+          const float ae = a * te;
+          aev[e] = ae;
+          hi.b[e] = (__bf16)ae;
+          lo.b[e] = (__bf16)(ae - (float)hi.b[e]);
+          bsv[x] = bb * st;
+          qsv[x] = qf * st;
+          xbt[e] = (_Float16)(bsv[x] * cP[e]);                     // B e^{G}
+          xat[e] = (_Float16)(ae * cQ[e]);                         // A e^{G_C - G}
+          qp.h[e] = (_Float16)(qsv[x] * cP[e] * qsc);              // Q e^{G}, scaled
+          const float ad = a * eam;
+          mdg = __builtin_amdgcn_mfma_f32_16x16x4f32(ad, bb * fup, mdg, 0, 0, 0);
+          pdg = __builtin_amdgcn_mfma_f32_16x16x4f32(ad, qf * fup, pdg, 0, 0, 0);
+        }
       }
-      *reinterpret_cast<uint4*>(&sm.ra.am.hi[r][c0]) = hi.q;
-      *reinterpret_cast<uint4*>(&sm.ra.am.lo[r][c0]) = lo.q;
+      if (SCALAR || wave < 3) {
+        *reinterpret_cast<uint4*>(&sm.ra.am.hi[r][c0]) = hi.q;
+        *reinterpret_cast<uint4*>(&sm.ra.am.lo[r][c0]) = lo.q;
+      }
+      if constexpr (!SCALAR) {
+        if (wave == 0) {  // tile 0's A side at the reference between tiles 1 and 2 (slot 3)
+          const float4 d0 = *reinterpret_cast<const float4*>(&sm.cu.v.dfac[0][c0]);
+          const float4 d1 = *reinterpret_cast<const float4*>(&sm.cu.v.dfac[0][c0 + 4]);
+          const float df[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+          H8 mh, ml;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float am = aev[e] * df[e];
+            mh.b[e] = (__bf16)am;
+            ml.b[e] = (__bf16)(am - (float)mh.b[e]);
+          }
+          *reinterpret_cast<uint4*>(&sm.ra.am.hi[48 + li][c0]) = mh.q;
+          *reinterpret_cast<uint4*>(&sm.ra.am.lo[48 + li][c0]) = ml.q;
+        }
+      }
       if (want_out && orow)
         *reinterpret_cast<uint4*>(Q_g + ((((ro >> 4) * KB + u) * 64 + (ro & 15) + 16 * lg) * 8)) = qp.q;
       // B+ and A^ of the group transposed by MFMA: lane (li, lg) then holds steps
@@ -1594,54 +1755,141 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
     if (has_next) load_raw(nx, raw, 1 | 2);
     wg_barrier();
 
-    // ---- Gram tiles: M^T(J, I) = A-(J) B+(I)^T and P^T(J, I) = A-(J) Q+(I)^T, every J
-    // together, k-block outer (tiles above the diagonal are computed and masked) ----
-    float4v mreg[NT], preg[NT];
+    // ---- Gram tiles: M^T(J, I) = A(J) B(I)^T and P^T(J, I) = A(J) Q(I)^T, k-block
+    // outer, independent accumulator chains interleaved. Scalar decay: every J
+    // (blocks above the diagonal are computed and masked), the decay applied to the
+    // entries afterwards. Per-channel decay: the three off-diagonal blocks J = 0, 1, 2
+    // (those with J >= I are computed and masked). ----
+    constexpr int NGB = SCALAR ? NT : NT - 1;
+    float4v mreg[NGB], preg[NGB];
 #pragma unroll
-    for (int J = 0; J < NT; ++J) mreg[J] = preg[J] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int J = 0; J < NGB; ++J) mreg[J] = preg[J] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const int c0 = 32 * u + 8 * lg;
-      H8 ah[NT], al[NT];
+      if constexpr (SCALAR) {
+        H8 ah[NT], al[NT];
+#pragma unroll
+        for (int J = 0; J < NT; ++J) {
+          ah[J].q = *reinterpret_cast<const uint4*>(&sm.ra.am.hi[16 * J + li][c0]);
+          al[J].q = *reinterpret_cast<const uint4*>(&sm.ra.am.lo[16 * J + li][c0]);
+        }
+#pragma unroll
+        for (int J = 0; J < NT; ++J) mreg[J] = mma_pair_bf16(ah[J].b, bmh[u].b, mreg[J]);
+#pragma unroll
+        for (int J = 0; J < NT; ++J) preg[J] = mma_pair_bf16(ah[J].b, qmh8[u].b, preg[J]);
+#pragma unroll
+        for (int J = 0; J < NT; ++J) mreg[J] = mma_pair_bf16(ah[J].b, bml[u].b, mreg[J]);
+#pragma unroll
+        for (int J = 0; J < NT; ++J) preg[J] = mma_pair_bf16(ah[J].b, qml8[u].b, preg[J]);
+#pragma unroll
+        for (int J = 0; J < NT; ++J) mreg[J] = mma_pair_bf16(al[J].b, bmh[u].b, mreg[J]);
+#pragma unroll
+        for (int J = 0; J < NT; ++J) preg[J] = mma_pair_bf16(al[J].b, qmh8[u].b, preg[J]);
+      } else {
+        // A sides: block 0 from slot 3 for tiles 2 and 3 (slot 0 for tile 1), blocks
+        // 1 and 2 from slots 1 and 2
+        const int row0 = (wave >= 2 ? 48 : 0) + li;
+        H8 ah[3], al[3];
+        ah[0].q = *reinterpret_cast<const uint4*>(&sm.ra.am.hi[row0][c0]);
+        al[0].q = *reinterpret_cast<const uint4*>(&sm.ra.am.lo[row0][c0]);
+#pragma unroll
+        for (int J = 1; J < 3; ++J) {
+          ah[J].q = *reinterpret_cast<const uint4*>(&sm.ra.am.hi[16 * J + li][c0]);
+          al[J].q = *reinterpret_cast<const uint4*>(&sm.ra.am.lo[16 * J + li][c0]);
+        }
+        H8 bsh, bsl, qsh, qsl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float b0 = bsv[8 * u + e], q0 = qsv[8 * u + e];
+          bsh.b[e] = (__bf16)b0;
+          bsl.b[e] = (__bf16)(b0 - (float)bsh.b[e]);
+          qsh.b[e] = (__bf16)q0;
+          qsl.b[e] = (__bf16)(q0 - (float)qsh.b[e]);
+        }
+        // blocks 0 and 1 of tile 3: its B and Q sides moved to the reference between
+        // tiles 1 and 2 (times e^{L_2}, at most 1)
+        H8 bxh = bsh, bxl = bsl, qxh = qsh, qxl = qsl;
+        if (wave == 3) {
+          const float4 d0 = *reinterpret_cast<const float4*>(&sm.cu.v.dfac[1][c0]);
+          const float4 d1 = *reinterpret_cast<const float4*>(&sm.cu.v.dfac[1][c0 + 4]);
+          const float df[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float b0 = bsv[8 * u + e] * df[e], q0 = qsv[8 * u + e] * df[e];
+            bxh.b[e] = (__bf16)b0;
+            bxl.b[e] = (__bf16)(b0 - (float)bxh.b[e]);
+            qxh.b[e] = (__bf16)q0;
+            qxl.b[e] = (__bf16)(q0 - (float)qxh.b[e]);
+          }
+        }
+        mreg[0] = mma_pair_bf16(ah[0].b, bxh.b, mreg[0]);
+        mreg[1] = mma_pair_bf16(ah[1].b, bxh.b, mreg[1]);
+        mreg[2] = mma_pair_bf16(ah[2].b, bsh.b, mreg[2]);
+        preg[0] = mma_pair_bf16(ah[0].b, qxh.b, preg[0]);
+        preg[1] = mma_pair_bf16(ah[1].b, qxh.b, preg[1]);
+        preg[2] = mma_pair_bf16(ah[2].b, qsh.b, preg[2]);
+        mreg[0] = mma_pair_bf16(ah[0].b, bxl.b, mreg[0]);
+        mreg[1] = mma_pair_bf16(ah[1].b, bxl.b, mreg[1]);
+        mreg[2] = mma_pair_bf16(ah[2].b, bsl.b, mreg[2]);
+        preg[0] = mma_pair_bf16(ah[0].b, qxl.b, preg[0]);
+        preg[1] = mma_pair_bf16(ah[1].b, qxl.b, preg[1]);
+        preg[2] = mma_pair_bf16(ah[2].b, qsl.b, preg[2]);
+        mreg[0] = mma_pair_bf16(al[0].b, bxh.b, mreg[0]);
+        mreg[1] = mma_pair_bf16(al[1].b, bxh.b, mreg[1]);
+        mreg[2] = mma_pair_bf16(al[2].b, bsh.b, mreg[2]);
+        preg[0] = mma_pair_bf16(al[0].b, qxh.b, preg[0]);
+        preg[1] = mma_pair_bf16(al[1].b, qxh.b, preg[1]);
+        preg[2] = mma_pair_bf16(al[2].b, qsh.b, preg[2]);
+      }
+    }
+    // Gram block of tile J as seen by this wave: accumulator and, for scalar decay,
+    // the factors e^{G_i - G_j} of its entries (j = 16 J + 4 lg + e, i = r)
+    float fdec[NT][4];
+#pragma unroll
+    for (int J = 0; J < NT; ++J)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) fdec[J][e] = 1.0f;
+    if constexpr (SCALAR) {
 #pragma unroll
       for (int J = 0; J < NT; ++J) {
-        ah[J].q = *reinterpret_cast<const uint4*>(&sm.ra.am.hi[16 * J + li][c0]);
-        al[J].q = *reinterpret_cast<const uint4*>(&sm.ra.am.lo[16 * J + li][c0]);
+        const float4 gj = *reinterpret_cast<const float4*>(&sm.cu.s.grow[16 * J + 4 * lg]);
+        const float g4[4] = {gj.x, gj.y, gj.z, gj.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fdec[J][e] = __builtin_amdgcn_exp2f(fminf(gabs - g4[e], 0.0f));
       }
-#pragma unroll
-      for (int J = 0; J < NT; ++J) mreg[J] = mma_pair_bf16(ah[J].b, bmh[u].b, mreg[J]);
-#pragma unroll
-      for (int J = 0; J < NT; ++J) preg[J] = mma_pair_bf16(ah[J].b, qmh8[u].b, preg[J]);
-#pragma unroll
-      for (int J = 0; J < NT; ++J) mreg[J] = mma_pair_bf16(ah[J].b, bml[u].b, mreg[J]);
-#pragma unroll
-      for (int J = 0; J < NT; ++J) preg[J] = mma_pair_bf16(ah[J].b, qml8[u].b, preg[J]);
-#pragma unroll
-      for (int J = 0; J < NT; ++J) mreg[J] = mma_pair_bf16(al[J].b, bmh[u].b, mreg[J]);
-#pragma unroll
-      for (int J = 0; J < NT; ++J) preg[J] = mma_pair_bf16(al[J].b, qmh8[u].b, preg[J]);
     }
+    auto mblk = [&](int J) __attribute__((always_inline)) -> float4v {
+      if constexpr (SCALAR) return mreg[J];
+      else return J < wave ? mreg[J < 2 ? J : 2] : mdg;
+    };
+    auto pblk = [&](int J) __attribute__((always_inline)) -> float4v {
+      if constexpr (SCALAR) return preg[J];
+      else return J < wave ? preg[J < 2 ? J : 2] : pdg;
+    };
     if (want_out && orow) {  // output rows are this wave's own rows (q scale qsc)
 #pragma unroll
       for (int J = 0; J < NT; ++J) {
         const int s0 = 16 * J + 4 * lg;
+        const float4v src = pblk(J);
         H8 h8;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) h8.h[e] = (_Float16)((s0 + e <= r) ? preg[J][e] * qsc : 0.0f);
+        for (int e = 0; e < 4; ++e) h8.h[e] = (_Float16)((s0 + e <= r) ? src[e] * fdec[J][e] * qsc : 0.0f);
         *reinterpret_cast<uint2*>(P_g + p_frag(ro, J)) = h8.u[0];
       }
     }
     if (has_next) load_raw(nx, raw, 4 | 16);
-    wg_barrier();  // A- is dead: its space now holds M and T
+    wg_barrier();  // the A sides are dead: their space now holds M and T
 #pragma unroll
     for (int J = 0; J < NT; ++J) {
       if (J <= wave) {
         const int s0 = 16 * J + 4 * lg;
+        const float4v src = mblk(J);
         float4 m4;
-        m4.x = (s0 + 0 < r) ? mreg[J][0] : 0.0f;
-        m4.y = (s0 + 1 < r) ? mreg[J][1] : 0.0f;
-        m4.z = (s0 + 2 < r) ? mreg[J][2] : 0.0f;
-        m4.w = (s0 + 3 < r) ? mreg[J][3] : 0.0f;
+        m4.x = (s0 + 0 < r) ? src[0] * fdec[J][0] : 0.0f;
+        m4.y = (s0 + 1 < r) ? src[1] * fdec[J][1] : 0.0f;
+        m4.z = (s0 + 2 < r) ? src[2] * fdec[J][2] : 0.0f;
+        m4.w = (s0 + 3 < r) ? src[3] * fdec[J][3] : 0.0f;
         *reinterpret_cast<float4*>(&sm.ra.mt.m[r][s0]) = m4;
       }
     }

@@ -45,11 +45,13 @@
  * Errors: 0 is success; negative codes below. Arguments are validated before
  * anything is enqueued: on an error nothing is launched and no output is touched.
  * Out-of-domain values (beta < 0, alpha outside (0, 1]) are not checked on the
- * device; they give NaN or Inf. The chunked path factors the decay through one
- * reference point in the middle of each chunk: it is exact in float32 range when
- * every channel's summed log-decay over half a chunk stays above -80 (for
- * chunk = 64 that is a geometric-mean alpha above 0.08 over 32 steps); use a
- * smaller chunk for stronger decay.
+ * device; they give NaN or Inf. Decay range of the chunked path: GDN and
+ * DELTAPRODUCT (one decay per step) take any alpha in (0, 1]. The per-channel
+ * decays (FG2, KDA, ASYM) are factored through reference points inside each
+ * 16-step tile of a chunk, so the result stays in float32 range as long as no
+ * channel decays by more than e^-87 over 8 consecutive steps (for instance,
+ * alpha >= 1.9e-5 at every step); stronger decay over such a window can give NaN.
+ * The recurrent entry point has no such limit.
  */
 #ifndef GDN_H
 #define GDN_H

@@ -173,6 +173,60 @@ def test_wide_beta_and_strong_decay():
     _run_and_check(inp, chunk=64, what="wide beta, strong decay")
 
 
+# ---- strong decay ------------------------------------------------------------------
+# alpha in (0, 1) is the whole domain (FG2-GDN reading notes, section 2.2 eq. (11);
+# GDN2-stability page, "Problem Description"). Forget-gate logits centred at -2, -3
+# and -6 put the mean alpha near 0.15, 0.07 and 0.0035, so a chunk's decay reaches
+# far below the float32 range; every case runs with a nonzero initial state.
+STRONG = [
+    # variant, dtype, B, T, H, dk, dv, n_h, chunk
+    ("fg2", "bf16", 1, 300, 2, 128, 128, 1, 64),       # two-workgroup prepare kernel
+    ("kda", "bf16", 1, 300, 2, 128, 128, 1, 64),
+    ("gdn", "bf16", 1, 300, 2, 128, 128, 1, 64),
+    ("asym", "bf16", 1, 300, 2, 128, 128, 1, 64),
+    ("deltaproduct", "bf16", 1, 150, 2, 128, 128, 2, 64),
+    ("fg2", "f32", 1, 300, 2, 64, 64, 1, 32),          # generic prepare kernel, fp32
+    ("kda", "f32", 1, 300, 2, 64, 64, 1, 32),
+    ("gdn", "f32", 1, 300, 2, 64, 64, 1, 32),
+    ("asym", "f32", 1, 300, 2, 64, 64, 1, 32),
+    ("fg2", "f32", 1, 200, 2, 32, 32, 1, 64),          # generic, chunk 64 (four tiles)
+    ("kda", "bf16", 1, 300, 2, 64, 64, 1, 64),
+    ("fg2", "bf16", 1, 200, 2, 64, 64, 1, 16),         # one tile per chunk
+    ("deltaproduct", "f32", 1, 100, 2, 64, 64, 2, 64),  # several steps per token, fp32
+    ("deltaproduct", "bf16", 1, 100, 2, 64, 64, 2, 32),
+]
+
+
+@pytest.mark.parametrize("alpha_mean", [-2.0, -3.0, -6.0])
+@pytest.mark.parametrize("case", STRONG, ids=lambda c: "-".join(map(str, c)))
+def test_strong_decay(case, alpha_mean):
+    var, dt, B, T, H, dk, dv, n_h, chunk = case
+    inp = gdn_inputs.make_inputs(var, B, T, H, dk, dv, dtype=dt, seed=81, n_h=n_h, alpha_mean=alpha_mean)
+    s0 = gdn_inputs.make_state(B, H, dk, dv, seed=81, scale=1.0)
+    _run_and_check(inp, s0, chunk=chunk, what=f"strong decay {case} alpha_mean={alpha_mean}")
+
+
+@pytest.mark.parametrize("case", [
+    ("fg2", "bf16", 1, 400, 2, 128, 128, 64),
+    ("kda", "bf16", 1, 400, 2, 128, 128, 64),
+    ("asym", "bf16", 1, 300, 2, 128, 128, 64),
+    ("fg2", "bf16", 1, 300, 2, 64, 64, 64),
+    ("fg2", "f32", 1, 300, 2, 64, 64, 32),
+    ("kda", "f32", 1, 200, 2, 32, 32, 64),
+], ids=lambda c: "-".join(map(str, c)))
+def test_some_channels_forget_at_once(case):
+    """Every seventh key channel has alpha = 1e-4 at every step (ordinary gates on the
+    rest): those channels lose almost all of the state at each step while the others
+    keep it, inside the same chunk."""
+    var, dt, B, T, H, dk, dv, chunk = case
+    inp = gdn_inputs.make_inputs(var, B, T, H, dk, dv, dtype=dt, seed=82)
+    al = inp["alpha"].copy()
+    al[..., ::7] = 1e-4
+    inp["alpha"] = gdn_inputs.round_bf16(al) if dt == "bf16" else al.astype(np.float32)
+    s0 = gdn_inputs.make_state(B, H, dk, dv, seed=82, scale=1.0)
+    _run_and_check(inp, s0, chunk=chunk, what=f"alpha 1e-4 channels {case}")
+
+
 @pytest.mark.parametrize("T", [1, 5, 16, 63, 64, 65])
 def test_short_and_ragged(T):
     inp = gdn_inputs.make_inputs("fg2", 1, T, 2, 64, 64, dtype="bf16", seed=T)
