@@ -67,6 +67,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.argtypes = [P, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
             fn.restype = ctypes.c_int
+        lib.gdn_chunk_fwd_static.argtypes = [P, ctypes.c_void_p]
+        lib.gdn_chunk_fwd_static.restype = ctypes.c_int
         lib.gdn_recurrent_step.argtypes = [P, ctypes.c_void_p, ctypes.c_void_p]
         lib.gdn_recurrent_step.restype = ctypes.c_int
         lib.gdn_bwd_workspace_bytes.argtypes = [P]
@@ -255,6 +257,14 @@ def gdn_chunk_scan(args: GdnArgs, workspace, stream=None):
 def gdn_chunk_fwd_args(args: GdnArgs, workspace, stream=None):
     """gdn_chunk_fwd on prebuilt args (no per-call marshalling)."""
     _staged("gdn_chunk_fwd", args, workspace, stream)
+
+
+def gdn_chunk_fwd_static(args: GdnArgs, stream=None):
+    """gdn_chunk_fwd on prebuilt args (o and, optionally, s_final given) with the
+    library's own record buffer instead of a workspace: nothing is allocated."""
+    st = load_library().gdn_chunk_fwd_static(ctypes.byref(args), _stream(stream))
+    if st != 0:
+        raise GdnError(st, "gdn_chunk_fwd_static")
 
 
 def gdn_asym_stabilize(mode, k, j, alpha, eta, *, out=None, stream=None):

@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 
 SOURCES = ["gdn_api.cpp", "gdn_recurrent.hip", "gdn_chunk.hip", "gdn_prep_fg2.hip", "gdn_prep_kda.hip",
            "gdn_prep_gdn.hip", "gdn_prep_dp.hip", "gdn_prep_asym.hip", "gdn_stabilize.hip",
-           "gdn_backward.hip"]
+           "gdn_backward.hip", "gdn_static.hip"]
 ARCH = "gfx950"
 # Packed fp32 instructions are disabled for every device compile.
 # MFMA accumulators are kept in VGPRs (VALU reads them without AGPR copies).

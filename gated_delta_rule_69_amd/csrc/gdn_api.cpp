@@ -110,6 +110,7 @@ int validate(const gdn_args* a, Entry e, Problem* out) {
     p.s_final = a->s_final;
     p.o = a->o;
     p.steps = a->T * n_step;
+    p.c0 = 0;
     if (chunked) {
       p.nchunks = (p.steps + chunk - 1) / chunk;
       p.rows_out = chunk / n_step;

@@ -354,9 +354,9 @@ __global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk
     Where w;
     // chunk-major order: the workgroups in flight read the same tokens of every
     // head, i.e. contiguous memory ([B, T, H, d] rows of one token are adjacent)
-    const int n = item / BH, bh = item - n * BH;
+    const int n = item / BH, bh = item - n * BH;  // chunk n of the launch
     const int b = bh / H, h = bh - b * H;
-    const int64_t vs = int64_t(n) * C + r;
+    const int64_t vs = (p.c0 + n) * C + r;
     w.valid = owner && vs < p.steps;
     int64_t tok = vs;
     w.sub = 0;
@@ -1342,20 +1342,22 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
 
   // first token-head row (b, token n TPC, h) of an item, chunk-major order
   struct Item {
-    int n, bh;
+    int nl, bh;   // chunk of the launch, (batch, head)
+    int64_t n;    // chunk of the sequence
     int64_t th0;  // (b T + n TPC) H + h
   };
   auto item_of = [&](int item) __attribute__((always_inline)) -> Item {
     Item it;
-    it.n = item / BH;
-    it.bh = item - it.n * BH;
+    it.nl = item / BH;
+    it.bh = item - it.nl * BH;
+    it.n = p.c0 + it.nl;
     const int b = it.bh / H, h = it.bh - b * H;
-    it.th0 = (int64_t(b) * T + int64_t(it.n) * TPC) * H + h;
+    it.th0 = (int64_t(b) * T + it.n * TPC) * H + h;
     return it;
   };
   // token-head row of step row rr (clamped to the sequence's last token)
   auto th_of = [&](const Item& it, int rr) __attribute__((always_inline)) -> int64_t {
-    const int64_t last = T - 1 - int64_t(it.n) * TPC;  // >= 0
+    const int64_t last = T - 1 - it.n * TPC;  // >= 0
     return it.th0 + min(int64_t(rr / NH), last) * H;
   };
   // row of step rr in the per-step arrays ([B, T, H, n_h, ...]; clamped to the last
@@ -1364,7 +1366,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
     if constexpr (NH == 1) {
       return th_of(it, rr);
     } else {
-      const int64_t rel = min(int64_t(rr), p.steps - 1 - int64_t(it.n) * C);  // >= 0
+      const int64_t rel = min(int64_t(rr), p.steps - 1 - it.n * C);  // >= 0
       return (it.th0 + (rel / NH) * H) * p.n_h + min(int(rel % NH), p.n_h - 1);
     }
   };
@@ -1451,10 +1453,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
     const Item it = item_of(item);
     const bool has_next = item + int(gridDim.x) < total;
     const Item nx = item_of(has_next ? item + int(gridDim.x) : item);
-    const bool valid = int64_t(it.n) * C + r < p.steps;
+    const bool valid = it.n * C + r < p.steps;
     const bool orow = NH == 1 || r % NH == NH - 1;  // the token's last step: an output row
     const int ro = r / NH;                           // its output row
-    unsigned char* rec = ws + (size_t(it.bh) * size_t(NC) + size_t(it.n)) * L.bytes;
+    unsigned char* rec = ws + (size_t(it.bh) * size_t(NC) + size_t(it.nl)) * L.bytes;
     _Float16* W_g = reinterpret_cast<_Float16*>(rec + L.off_W);
     _Float16* AT_g = reinterpret_cast<_Float16*>(rec + L.off_AT);
     _Float16* Q_g = reinterpret_cast<_Float16*>(rec + L.off_Q);

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(Problem p, const u
     if constexpr (!OSTAGE) return;
     for (int x = tid; x < R * ounits_row; x += kThreads) {
       const int ro = x / ounits_row, cu = x % ounits_row;
-      const int64_t t = n * R + ro;
+      const int64_t t = (p.c0 + n) * R + ro;
       if (t < p.T) {
         const int c = cu * 16 / int(sizeof(In));
         const uint4 val = *reinterpret_cast<const uint4*>(&ostage[buf][ro][c]);
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(Problem p, const u
         if (mo < RT) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int64_t t = n * R + 16 * mo + 4 * lg + e;
+            const int64_t t = (p.c0 + n) * R + 16 * mo + 4 * lg + e;
             if (t < p.T) o[((b * p.T + t) * p.H + h) * dv + col] = ohold[mo][e];
           }
         }
@@ -576,7 +576,7 @@ __global__ __launch_bounds__(2 * kThreads + 64) void chunk_scan_rows_kernel(Prob
         constexpr int RU = NB / 8;
         for (int x = lane; x < 16 * RU; x += 64) {
           const int ro = 16 * ow + x / RU, c8 = x % RU;
-          const int64_t t = int64_t(n) * R + ro;
+          const int64_t t = (p.c0 + n) * R + ro;
           if (t < p.T)
             *reinterpret_cast<uint4*>(o + ((int64_t(b) * p.T + t) * H + h) * dv + col_base + 8 * c8) =
                 *reinterpret_cast<const uint4*>(&ost[ro][8 * c8]);

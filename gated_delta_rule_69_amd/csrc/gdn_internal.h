@@ -31,7 +31,11 @@ struct Problem {
   void* o;
   // chunk geometry (chunked entry points)
   int64_t steps;     // virtual steps: T * n_step (chunked), T * n_h (recurrent)
-  int64_t nchunks;   // ceil(steps / chunk)
+  int64_t nchunks;   // chunks of one launch: ceil(steps / chunk) for the whole sequence
+  int64_t c0;        // first chunk of the launch (0 for the whole sequence); the
+                     // workspace holds the records of chunks c0 .. c0 + nchunks - 1,
+                     // s0 is the state before chunk c0 and s_final the state after
+                     // the launch's last chunk
   int rows_out;      // output rows per chunk: chunk / n_h
 };
 

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 enum gdn_variant {
   GDN_VARIANT_FG2 = 0,
@@ -141,6 +141,29 @@ int gdn_final_state(const gdn_args* args, void* ws, size_t ws_bytes, void* strea
  * modified between the two calls. */
 int gdn_chunk_prepare(const gdn_args* args, void* ws, size_t ws_bytes, void* stream);
 int gdn_chunk_scan(const gdn_args* args, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of the device buffer gdn_chunk_fwd_static keeps on each device. */
+#define GDN_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* gdn_chunk_fwd without a workspace, for callers that cannot allocate device
+ * memory: code under stream capture, serving loops that must not allocate, and
+ * harnesses that forbid hipMalloc. The call itself allocates nothing. The chunk
+ * records live in a buffer of GDN_STATIC_SCRATCH_BYTES inside the library, one per
+ * device, created when the library's code is loaded on that device and held until
+ * the process ends; its device address is looked up once per device, on the first
+ * call made with that device current. The sequence runs in blocks of as many
+ * chunks as the buffer holds for all B*H sequences (one prepare and one scan
+ * launch per block, each block starting from the state the previous one left), so
+ * o and s_final are bitwise equal to gdn_chunk_fwd's for the same args.
+ * Arguments, layouts and errors are those of gdn_chunk_fwd, plus
+ * GDN_ERR_UNSUPPORTED when one chunk's records for all B*H sequences, plus
+ * B*H*dk*dv*4 bytes for the carried state when s_final is NULL, exceed the buffer
+ * (bf16, dk = dv = 128, chunk 64: 72 KiB of records per sequence, so B*H <= 910
+ * with s_final given, B*H <= 481 without).
+ * All calls on one device share its buffer, and the buffer keeps the last call's
+ * contents: calls that may overlap on one device (several streams or host threads)
+ * race and must be serialised by the caller. */
+int gdn_chunk_fwd_static(const gdn_args* args, void* stream);
 
 /* Token-sequential recurrence: advances state_inout ([B, H, dk, dv] float32,
  * updated in place) by args->T tokens, writing o for each (T = 1 is one decode

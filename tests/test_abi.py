@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
                           "gdn_workspace_bytes", "gdn_status_str", "gdn_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.gdn_abi_version() == 2
+    assert lib.gdn_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -184,3 +184,15 @@ def test_workspace_bytes_grows_with_tokens(lib):
     assert big == 100 * small
     assert lib.gdn_workspace_bytes(ctypes.byref(good_args(dk=48))) == 0
     assert lib.gdn_workspace_bytes(None) == 0
+
+
+def test_static_entry_rejects_what_its_buffer_cannot_hold(lib):
+    """gdn_chunk_fwd_static checks its size limit before any HIP call: 1024 sequences
+    of bf16 records (dk = dv = 128, chunk 64) exceed its buffer in a single chunk."""
+    a = good_args(B=2, H=512, dk=128, dv=128)
+    assert lib.gdn_chunk_fwd_static(ctypes.byref(a), None) == -2
+    # without s_final the carried state counts too: 482 sequences no longer fit
+    a = good_args(B=2, H=241, dk=128, dv=128)
+    assert lib.gdn_chunk_fwd_static(ctypes.byref(a), None) == -2
+    # and the ordinary argument checks come first
+    assert lib.gdn_chunk_fwd_static(ctypes.byref(good_args(B=0)), None) == -1
