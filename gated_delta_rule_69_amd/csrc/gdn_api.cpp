@@ -138,8 +138,7 @@ size_t gdn_workspace_bytes(const gdn_args* args) {
   Problem p;
   if (gdn::validate(args, Entry::Shapes, &p) != GDN_OK) return 0;
   if (p.nchunks == 0) return 256;
-  const gdn::ChunkLayout L = gdn::chunk_layout(p);
-  return size_t(p.B) * size_t(p.H) * size_t(p.nchunks) * L.bytes;
+  return gdn::workspace_bytes(p, gdn::chunk_layout(p));
 }
 
 enum class Stage { Both, Prepare, Scan };

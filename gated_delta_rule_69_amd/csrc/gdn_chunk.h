@@ -1277,8 +1277,13 @@ struct alignas(16) PrepLds2 {
       float ltot[4];        // tile totals of the scalar log decay
       float grow[64];       // log decay from the chunk start through each row
     } s;                    // scalar decay
+    struct {
+      // [t] G_31 - (sum of L before tile t), [4] 2^G_31, [5] 2^(G_C - G_31)
+      float chv[6][128];
+    } o;                    // per-channel decay, every factor referenced to row 31
   } cu;
   float red[kWaves];
+  float tdec[kWaves];       // largest decay of any channel over each 16-step tile (log2)
 };
 
 // Whether chunk_prep2_kernel covers a problem (bf16, dk = dv = 128, chunk 64, no
@@ -1295,8 +1300,13 @@ inline bool prep2_covers(const Problem& p) {
 // NH: steps per token (DeltaProduct's n_h; 1 otherwise). With NH > 1 the rows are
 // Householder sub-steps: k, v and beta come from the step, the gate from the token
 // at its first step, and every NH-th row (the token's last step) is an output row.
-template <int V, int STAB, int NH>
+// MODE (per-channel decay only): 1 = chunks of mild decay on the path referenced
+// to the chunk's middle; every other chunk is only flagged (flags[item] = 1, else
+// 0); 2 = the flagged chunks, on the tile-referenced path. 0 = every chunk on the
+// tile-referenced path (scalar decay).
+template <int V, int STAB, int NH, int MODE>
 __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, unsigned char* __restrict__ ws,
+                                                                     unsigned char* __restrict__ flags,
                                                                      ChunkLayout L, int want_out) {
   using In = uint16_t;
   constexpr int DK = 128, C = 64, NT = 4, KB = 4, CK = 2, CT = 8, VT = 8;
@@ -1306,6 +1316,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
   constexpr bool CH_ALPHA = V == GDN_VARIANT_FG2 || V == GDN_VARIANT_KDA || V == GDN_VARIANT_ASYM;
   constexpr bool CH_BJ = V == GDN_VARIANT_FG2 || V == GDN_VARIANT_ASYM;  // per-channel beta / j
   constexpr bool SCALAR = !CH_ALPHA;  // one log decay per row (GDN, DeltaProduct)
+  static_assert(SCALAR ? MODE == 0 : MODE != 0, "mild / flagged passes for per-channel decay");
   using Sm = PrepLds2;
   static_assert(sizeof(Sm) <= 80 * 1024, "two workgroups per CU");
   __shared__ Sm sm;
@@ -1343,21 +1354,21 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
   // first token-head row (b, token n TPC, h) of an item, chunk-major order
   struct Item {
     int nl, bh;   // chunk of the launch, (batch, head)
-    int64_t n;    // chunk of the sequence
+    int n;        // chunk of the sequence
     int64_t th0;  // (b T + n TPC) H + h
   };
   auto item_of = [&](int item) __attribute__((always_inline)) -> Item {
     Item it;
     it.nl = item / BH;
     it.bh = item - it.nl * BH;
-    it.n = p.c0 + it.nl;
+    it.n = int(p.c0) + it.nl;
     const int b = it.bh / H, h = it.bh - b * H;
-    it.th0 = (int64_t(b) * T + it.n * TPC) * H + h;
+    it.th0 = (int64_t(b) * T + int64_t(it.n) * TPC) * H + h;
     return it;
   };
   // token-head row of step row rr (clamped to the sequence's last token)
   auto th_of = [&](const Item& it, int rr) __attribute__((always_inline)) -> int64_t {
-    const int64_t last = T - 1 - it.n * TPC;  // >= 0
+    const int64_t last = T - 1 - int64_t(it.n) * TPC;  // >= 0
     return it.th0 + min(int64_t(rr / NH), last) * H;
   };
   // row of step rr in the per-step arrays ([B, T, H, n_h, ...]; clamped to the last
@@ -1366,7 +1377,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
     if constexpr (NH == 1) {
       return th_of(it, rr);
     } else {
-      const int64_t rel = min(int64_t(rr), p.steps - 1 - it.n * C);  // >= 0
+      const int64_t rel = min(int64_t(rr), p.steps - 1 - int64_t(it.n) * C);  // >= 0
       return (it.th0 + (rel / NH) * H) * p.n_h + min(int(rel % NH), p.n_h - 1);
     }
   };
@@ -1442,18 +1453,34 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
 #pragma unroll
     for (int u = 0; u < 4; ++u) raw.q[u] = make_uint4(0u, 0u, 0u, 0u);
   }
-  if (int(blockIdx.x) < total) {
-    const Item it = item_of(blockIdx.x);
+  // items of this workgroup: every gridDim-th one; the flagged pass skips the others
+  auto next_item = [&](int item) __attribute__((always_inline)) -> int {
+    if constexpr (MODE == 2) {
+      // 64 of this workgroup's items per wave-wide load, the first flagged one by ballot
+      const int l = int(threadIdx.x & 63);
+      for (; item < total; item += 64 * int(gridDim.x)) {
+        const int x = item + l * int(gridDim.x);
+        const uint64_t hit = __ballot(x < total && flags[x] != 0);
+        if (hit) return item + int(__builtin_ctzll(hit)) * int(gridDim.x);
+      }
+      return total;
+    }
+    return item;
+  };
+  const int first = next_item(blockIdx.x);
+  if (first < total) {
+    const Item it = item_of(first);
     load_raw(it, raw, 31);
     scal = load_scal(it);
   }
 
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+  for (int item = first, after; item < total; item = after) {
     lane_ids();
+    after = next_item(item + int(gridDim.x));
     const Item it = item_of(item);
-    const bool has_next = item + int(gridDim.x) < total;
-    const Item nx = item_of(has_next ? item + int(gridDim.x) : item);
-    const bool valid = it.n * C + r < p.steps;
+    const bool has_next = after < total;
+    const Item nx = item_of(has_next ? after : item);
+    const bool valid = int64_t(it.n) * C + r < p.steps;
     const bool orow = NH == 1 || r % NH == NH - 1;  // the token's last step: an output row
     const int ro = r / NH;                           // its output row
     unsigned char* rec = ws + (size_t(it.bh) * size_t(NC) + size_t(it.nl)) * L.bytes;
@@ -1543,7 +1570,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
     } else {
 #pragma unroll
       for (int x = 0; x < 32; ++x) G[x] = scan16(G[x]);
-      if (li == 15 || li == 7) {
+      if (li == 15 || (MODE != 1 && li == 7)) {  // the mild pass needs the totals only
         float* dst = li == 15 ? &sm.ra.stg.L[wave][0] : &sm.ra.stg.m[wave][0];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
@@ -1553,11 +1580,41 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
                 make_float4(G[8 * u + e], G[8 * u + e + 1], G[8 * u + e + 2], G[8 * u + e + 3]);
       }
     }
+    // largest decay over this wave's tile (row 15 holds the tile totals)
+    float tdmax = 0.0f;
+    if constexpr (!SCALAR) {
+      if (li == 15) {
+#pragma unroll
+        for (int x = 0; x < 32; ++x) tdmax = fmaxf(tdmax, -G[x]);
+      }
+      tdmax = wave_max(tdmax);
+    }
     // power-of-two scales: per output row for q, per chunk for the written values
     const float qsc = want_out ? pow2_scale_for(max_over_groups(qmax)) : 1.0f;
     wmax = wave_max(wmax);
-    if (lane == 0) sm.red[wave] = wmax;
+    if (lane == 0) {
+      sm.red[wave] = wmax;
+      sm.tdec[wave] = tdmax;
+    }
     wg_barrier();
+
+    // Mild decay (every channel decays by less than 2^-55 over each 16-step tile, so
+    // by less than 2^-110 over either half of the chunk): one reference point in the
+    // middle of the chunk keeps every factor in range, and the chunk takes the
+    // shorter path that forms every Gram block from it. Otherwise the tile
+    // references below.
+    if constexpr (MODE == 1) {
+      float td = sm.tdec[0];
+#pragma unroll
+      for (int w2 = 1; w2 < kWaves; ++w2) td = fmaxf(td, sm.tdec[w2]);
+      const bool mild = td < 55.0f;
+      if (tid == 0 && mild) flags[item] = 0;
+      if (!mild) {
+        // this chunk and every later one of the workgroup go to the flagged pass
+        for (int x = item + tid * int(gridDim.x); x < total; x += kThreads * int(gridDim.x)) flags[x] = 1;
+        break;
+      }
+    }
 
     // ---- decay constants ----
     // Scalar decay: every factor is a function of the row alone; the Gram entries
@@ -1580,30 +1637,44 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
       eat_row = __builtin_amdgcn_exp2f(fminf(gc - gabs, 0.0f));  // e^{G_C - G}
       if (lg == 0) sm.cu.s.grow[r] = gabs;
       if (tid < DK) gam_g[tid] = __builtin_amdgcn_exp2f(gc);
-    } else if (tid < DK) {
-      const int c = tid;
-      float Lt[NT], mt[NT];
+    } else if (MODE == 1) {
+      if (tid < DK) {  // one thread per key channel
+        const int c = tid;
+        float Lt[NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        Lt[t] = sm.ra.stg.L[t][c];
-        mt[t] = sm.ra.stg.m[t][c];
+        for (int t = 0; t < NT; ++t) Lt[t] = sm.ra.stg.L[t][c];
+        const float gm = Lt[0] + Lt[1];  // G at row 31
+        float pre = 0.0f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          sm.cu.o.chv[t][c] = gm - pre;
+          pre += Lt[t];
+        }
+        sm.cu.o.chv[NT][c] = __builtin_amdgcn_exp2f(gm);
+        sm.cu.o.chv[NT + 1][c] = __builtin_amdgcn_exp2f(pre - gm);
+        gam_g[c] = __builtin_amdgcn_exp2f(pre);
       }
-      float pre = 0.0f;
+    } else {
+      // thread (c, half): channel c, tiles 2 half and 2 half + 1
+      const int c = tid & (DK - 1), half = tid >> 7;
+      float Lt[NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        float suf = 0.0f;
+      for (int t = 0; t < NT; ++t) Lt[t] = sm.ra.stg.L[t][c];
+      const float gc = (Lt[0] + Lt[1]) + (Lt[2] + Lt[3]);
 #pragma unroll
-        for (int t2 = t + 1; t2 < NT; ++t2) suf += Lt[t2];
-        sm.cu.v.cst[t][0][c] = mt[t];
-        sm.cu.v.cst[t][1][c] = __builtin_amdgcn_exp2f(mt[t]);          // e^{G_7 - G_start}
-        sm.cu.v.cst[t][2][c] = __builtin_amdgcn_exp2f(Lt[t] - mt[t]);  // e^{G_end - G_7}
-        sm.cu.v.cst[t][3][c] = __builtin_amdgcn_exp2f(pre);            // e^{G_start}
-        sm.cu.v.cst[t][4][c] = __builtin_amdgcn_exp2f(suf);            // e^{G_C - G_end}
-        pre += Lt[t];
+      for (int k = 0; k < 2; ++k) {
+        const int t = 2 * half + k;
+        const float mt = sm.ra.stg.m[t][c];
+        const float pre = t == 0 ? 0.0f : t == 1 ? Lt[0] : t == 2 ? Lt[0] + Lt[1] : Lt[0] + Lt[1] + Lt[2];
+        const float suf = t == 3 ? 0.0f : t == 2 ? Lt[3] : t == 1 ? Lt[2] + Lt[3] : Lt[1] + Lt[2] + Lt[3];
+        sm.cu.v.cst[t][0][c] = mt;
+        sm.cu.v.cst[t][1][c] = __builtin_amdgcn_exp2f(mt);          // e^{G_7 - G_start}
+        sm.cu.v.cst[t][2][c] = __builtin_amdgcn_exp2f(Lt[t] - mt);  // e^{G_end - G_7}
+        sm.cu.v.cst[t][3][c] = __builtin_amdgcn_exp2f(pre);         // e^{G_start}
+        sm.cu.v.cst[t][4][c] = __builtin_amdgcn_exp2f(suf);         // e^{G_C - G_end}
       }
-      sm.cu.v.dfac[0][c] = __builtin_amdgcn_exp2f(Lt[1]);
-      sm.cu.v.dfac[1][c] = __builtin_amdgcn_exp2f(Lt[2]);
-      gam_g[c] = __builtin_amdgcn_exp2f(pre);
+      sm.cu.v.dfac[half][c] = __builtin_amdgcn_exp2f(Lt[1 + half]);
+      if (half == 0) gam_g[c] = __builtin_amdgcn_exp2f(gc);
     }
     float wsc;
     {
@@ -1616,160 +1687,110 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
     if (want_out && orow && lg == 0) qinv_g[ro] = 1.0f / qsc;
     wg_barrier();
 
-    // ---- phase 2: decayed operands and written values of this wave's rows, one
-    // channel group at a time ----
-    // Off-diagonal Gram blocks M(I, J), P(I, J), J < I, with per-channel decay: B and
-    // Q sides of tile I referenced to its first row (kept in fp32 until the Gram
-    // phase), A side of tile J to its last row (LDS slot J); block (3, 2) pairs
-    // them directly, blocks (I, 0..1) of the lower half pair them through the
-    // reference between tiles 1 and 2: slot 3 holds tile 0's A side moved there
-    // (times e^{L_1}), and tile 3's B and Q sides move back to it (times e^{L_2}) in
-    // the Gram phase. Tile 3's own A side is never an off-diagonal operand. The
-    // diagonal blocks use row 7 of the tile on both sides and run here, on fp32
-    // MFMA straight from registers (the A and B operand layouts of a 16-row tile
-    // are the same).
-    const float wrow = (V == GDN_VARIANT_FG2 ? 1.0f : wscal) * wsc;  // written-value factor of the row
-    float bsv[SCALAR ? 1 : 32], qsv[SCALAR ? 1 : 32];                // B and Q sides (per-channel decay)
-    H8 bmh[SCALAR ? KB : 1], bml[SCALAR ? KB : 1], qmh8[SCALAR ? KB : 1], qml8[SCALAR ? KB : 1];  // (scalar)
-    float4v mdg = {0.0f, 0.0f, 0.0f, 0.0f}, pdg = {0.0f, 0.0f, 0.0f, 0.0f};  // diagonal blocks M^T, P^T
+    if constexpr (MODE == 1) {
+      // ---- phase 2 (mild decay): decayed operands and written values of this wave's
+      // rows, one channel group at a time, every factor referenced to the chunk's
+      // middle (row 31) ----
+      const float wrow = (V == GDN_VARIANT_FG2 ? 1.0f : wscal) * wsc;  // written-value factor of the row
+      H8 bmh[KB], bml[KB], qmh8[KB], qml8[KB];  // B sides of the Grams (bf16 hi / lo)
 #pragma unroll
-    for (int u = 0; u < KB; ++u) {
-      const int c0 = 32 * u + 8 * lg;  // 8 consecutive channels
-      float cm[8], c7[8], c157[8], cP[8], cQ[8];
-      if constexpr (!SCALAR) {
-        auto ld8 = [&](const float* src, float* d) __attribute__((always_inline)) {
-          const float4 x0 = *reinterpret_cast<const float4*>(src);
-          const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
-          d[0] = x0.x, d[1] = x0.y, d[2] = x0.z, d[3] = x0.w, d[4] = x1.x, d[5] = x1.y, d[6] = x1.z, d[7] = x1.w;
-        };
-        ld8(&sm.cu.v.cst[wave][0][c0], cm);
-        ld8(&sm.cu.v.cst[wave][1][c0], c7);
-        ld8(&sm.cu.v.cst[wave][2][c0], c157);
-        ld8(&sm.cu.v.cst[wave][3][c0], cP);
-        ld8(&sm.cu.v.cst[wave][4][c0], cQ);
-      }
-      const uint4 kr = raw.k[u], vr = raw.v[u];
-      uint4 br = {}, qr = {};
-      if constexpr (CH_BJ) br = raw.b[u];
-      if (want_out && valid && orow) qr = raw.q[u];
-      half8 xbt, xat, xv;
-      H8 hi, lo, qp;
-      float aev[8];
+      for (int u = 0; u < KB; ++u) {
+        const int c0 = 32 * u + 8 * lg;  // 8 consecutive channels
+        float cof[8], cp[8], cq[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float kf = bf(kr, e);
-        float a, bb;
-        if constexpr (V == GDN_VARIANT_FG2) {
-          const float sb = valid ? __builtin_amdgcn_sqrtf(bf(br, e)) : 0.0f;
-          a = sb * kf;
-          bb = a;
-          xv[e] = (_Float16)(bf(vr, e) * sb * wsc);
-        } else if constexpr (V == GDN_VARIANT_ASYM) {
-          a = valid ? kf : 0.0f;
-          bb = bscal * (STAB == 2 ? stab_j(stc, kf, bf(br, e)) : bf(br, e));
-        } else {  // KDA, GDN (kscal = sqrt(beta)); DeltaProduct (bscal = beta)
-          a = kscal * kf;
-          bb = bscal * a;
+        for (int e = 0; e < 8; e += 4) {
+          const float4 x0 = *reinterpret_cast<const float4*>(&sm.cu.o.chv[wave][c0 + e]);
+          const float4 x1 = *reinterpret_cast<const float4*>(&sm.cu.o.chv[NT][c0 + e]);
+          const float4 x2 = *reinterpret_cast<const float4*>(&sm.cu.o.chv[NT + 1][c0 + e]);
+          cof[e] = x0.x, cof[e + 1] = x0.y, cof[e + 2] = x0.z, cof[e + 3] = x0.w;
+          cp[e] = x1.x, cp[e + 1] = x1.y, cp[e + 2] = x1.z, cp[e + 3] = x1.w;
+          cq[e] = x2.x, cq[e + 1] = x2.y, cq[e + 2] = x2.z, cq[e + 3] = x2.w;
         }
-        if constexpr (V != GDN_VARIANT_FG2) xv[e] = (_Float16)(bf(vr, e) * wrow);
-        const float qf = bf(qr, e);
-        if constexpr (SCALAR) {
-          hi.b[e] = (__bf16)a;
-          lo.b[e] = (__bf16)(a - (float)hi.b[e]);
-          bmh[u].b[e] = (__bf16)bb;
-          bml[u].b[e] = (__bf16)(bb - (float)bmh[u].b[e]);
-          qmh8[u].b[e] = (__bf16)qf;
-          qml8[u].b[e] = (__bf16)(qf - (float)qmh8[u].b[e]);
-          xbt[e] = (_Float16)(bb * eg_row);
-          xat[e] = (_Float16)(a * eat_row);
-          qp.h[e] = (_Float16)(qf * eg_row * qsc);
-        } else {
-          const int x = 8 * u + e;
-          const float fup = __builtin_amdgcn_exp2f(G[x] - cm[e]);  // e^{G - G_7}
-          const float eam = __builtin_amdgcn_rcpf(fup);            // e^{G_7 - G}
-          const float st = fup * c7[e];                            // e^{G - G_start}
-          const float te = eam * c157[e];                          // e^{G_end - G}
-          const float ae = a * te;
-          aev[e] = ae;
-          hi.b[e] = (__bf16)ae;
-          lo.b[e] = (__bf16)(ae - (float)hi.b[e]);
-          bsv[x] = bb * st;
-          qsv[x] = qf * st;
-          xbt[e] = (_Float16)(bsv[x] * cP[e]);                     // B e^{G}
-          xat[e] = (_Float16)(ae * cQ[e]);                         // A e^{G_C - G}
-          qp.h[e] = (_Float16)(qsv[x] * cP[e] * qsc);              // Q e^{G}, scaled
-          const float ad = a * eam;
-          mdg = __builtin_amdgcn_mfma_f32_16x16x4f32(ad, bb * fup, mdg, 0, 0, 0);
-          pdg = __builtin_amdgcn_mfma_f32_16x16x4f32(ad, qf * fup, pdg, 0, 0, 0);
+        const uint4 kr = raw.k[u], vr = raw.v[u];
+        uint4 br = {}, qr = {};
+        if constexpr (CH_BJ) br = raw.b[u];
+        if (want_out && valid && orow) qr = raw.q[u];
+        half8 xbt, xat, xv;
+        H8 hi, lo, qp;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float kf = bf(kr, e);
+          float a, bb;
+          if constexpr (V == GDN_VARIANT_FG2) {
+            const float sb = valid ? __builtin_amdgcn_sqrtf(bf(br, e)) : 0.0f;
+            a = sb * kf;
+            bb = a;
+            xv[e] = (_Float16)(bf(vr, e) * sb * wsc);
+          } else if constexpr (V == GDN_VARIANT_ASYM) {
+            a = valid ? kf : 0.0f;
+            bb = bscal * (STAB == 2 ? stab_j(stc, kf, bf(br, e)) : bf(br, e));
+          } else {  // KDA, GDN (kscal = sqrt(beta)); DeltaProduct (bscal = beta)
+            a = kscal * kf;
+            bb = bscal * a;
+          }
+          if constexpr (V != GDN_VARIANT_FG2) xv[e] = (_Float16)(bf(vr, e) * wrow);
+          const float fup = __builtin_amdgcn_exp2f(G[8 * u + e] - cof[e]);  // e^{G - G_mid}
+          const float eam = __builtin_amdgcn_rcpf(fup);                     // e^{G_mid - G}
+          const float eg = cp[e] * fup;                                     // e^{G}
+          const float eat = cq[e] * eam;                                    // e^{G_C - G}
+          xbt[e] = (_Float16)(bb * eg);
+          xat[e] = (_Float16)(a * eat);
+          const float am = a * eam;
+          hi.b[e] = (__bf16)am;
+          lo.b[e] = (__bf16)(am - (float)hi.b[e]);
+          const float bm = bb * fup;
+          bmh[u].b[e] = (__bf16)bm;
+          bml[u].b[e] = (__bf16)(bm - (float)bmh[u].b[e]);
+          const float qf = bf(qr, e);
+          const float qm = qf * fup;
+          qmh8[u].b[e] = (__bf16)qm;
+          qml8[u].b[e] = (__bf16)(qm - (float)qmh8[u].b[e]);
+          qp.h[e] = (_Float16)(qf * eg * qsc);
         }
-      }
-      if (SCALAR || wave < 3) {
         *reinterpret_cast<uint4*>(&sm.ra.am.hi[r][c0]) = hi.q;
         *reinterpret_cast<uint4*>(&sm.ra.am.lo[r][c0]) = lo.q;
-      }
-      if constexpr (!SCALAR) {
-        if (wave == 0) {  // tile 0's A side at the reference between tiles 1 and 2 (slot 3)
-          const float4 d0 = *reinterpret_cast<const float4*>(&sm.cu.v.dfac[0][c0]);
-          const float4 d1 = *reinterpret_cast<const float4*>(&sm.cu.v.dfac[0][c0 + 4]);
-          const float df[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-          H8 mh, ml;
+        if (want_out && orow)
+          *reinterpret_cast<uint4*>(Q_g + ((((ro >> 4) * KB + u) * 64 + (ro & 15) + 16 * lg) * 8)) = qp.q;
+        // B+ and A^ of the group transposed by MFMA: lane (li, lg) then holds steps
+        // 16 wave + 4 lg .. of channel 32 u + 16 h + li
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float am = aev[e] * df[e];
-            mh.b[e] = (__bf16)am;
-            ml.b[e] = (__bf16)(am - (float)mh.b[e]);
+        for (int hh = 0; hh < 2; ++hh) {
+          const float4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
+          const float4v tb = mma_pair_f16(xbt, sel[hh], zero);
+          const float4v ta = mma_pair_f16(xat, sel[hh], zero);
+          const int c = 32 * u + 16 * hh + li;
+          H8 pb, pa;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pb.h[e] = (_Float16)tb[e];
+            pa.h[e] = (_Float16)ta[e];
           }
-          *reinterpret_cast<uint4*>(&sm.ra.am.hi[48 + li][c0]) = mh.q;
-          *reinterpret_cast<uint4*>(&sm.ra.am.lo[48 + li][c0]) = ml.q;
+          *reinterpret_cast<uint2*>(&sm.bt[c][16 * wave + 4 * lg]) = pb.u[0];
+          const float4v tv = mma_pair_f16(xv, sel[hh], zero);
+          H8 pv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pv.h[e] = (_Float16)tv[e];
+          *reinterpret_cast<uint2*>(&sm.wvt[c][16 * wave + 4 * lg]) = pv.u[0];
+          *reinterpret_cast<uint2*>(AT_g + size_t((((c >> 4) * CK + (wave >> 1)) * 64 + li + 16 * (2 * (wave & 1) + (lg >> 1))) * 8 +
+                                                  4 * (lg & 1))) = pa.u[0];
         }
       }
-      if (want_out && orow)
-        *reinterpret_cast<uint4*>(Q_g + ((((ro >> 4) * KB + u) * 64 + (ro & 15) + 16 * lg) * 8)) = qp.q;
-      // B+ and A^ of the group transposed by MFMA: lane (li, lg) then holds steps
-      // 16 wave + 4 lg .. of channel 32 u + 16 h + li
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const float4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
-        const float4v tb = mma_pair_f16(xbt, sel[hh], zero);
-        const float4v ta = mma_pair_f16(xat, sel[hh], zero);
-        const int c = 32 * u + 16 * hh + li;
-        H8 pb, pa;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pb.h[e] = (_Float16)tb[e];
-          pa.h[e] = (_Float16)ta[e];
-        }
-        *reinterpret_cast<uint2*>(&sm.bt[c][16 * wave + 4 * lg]) = pb.u[0];
-        const float4v tv = mma_pair_f16(xv, sel[hh], zero);
-        H8 pv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pv.h[e] = (_Float16)tv[e];
-        *reinterpret_cast<uint2*>(&sm.wvt[c][16 * wave + 4 * lg]) = pv.u[0];
-        *reinterpret_cast<uint2*>(AT_g + size_t((((c >> 4) * CK + (wave >> 1)) * 64 + li + 16 * (2 * (wave & 1) + (lg >> 1))) * 8 +
-                                                4 * (lg & 1))) = pa.u[0];
-      }
-    }
 
-    // The next item's inputs load in three groups, each once this item's copy is
-    // consumed, so that the loads of the two workgroups on a CU do not arrive in
-    // one burst: key and values here, query and beta / j after the Grams, the decay
-    // before W and U~.
-    if (has_next) load_raw(nx, raw, 1 | 2);
-    wg_barrier();
+      // The next item's inputs load in three groups, each once this item's copy is
+      // consumed, so that the loads of the two workgroups on a CU do not arrive in
+      // one burst: key and values here, query and beta / j after the Grams, the decay
+      // before W and U~.
+      if (has_next) load_raw(nx, raw, 1 | 2);
+      wg_barrier();
 
-    // ---- Gram tiles: M^T(J, I) = A(J) B(I)^T and P^T(J, I) = A(J) Q(I)^T, k-block
-    // outer, independent accumulator chains interleaved. Scalar decay: every J
-    // (blocks above the diagonal are computed and masked), the decay applied to the
-    // entries afterwards. Per-channel decay: the three off-diagonal blocks J = 0, 1, 2
-    // (those with J >= I are computed and masked). ----
-    constexpr int NGB = SCALAR ? NT : NT - 1;
-    float4v mreg[NGB], preg[NGB];
+      // ---- Gram tiles: M^T(J, I) = A-(J) B+(I)^T and P^T(J, I) = A-(J) Q+(I)^T, every J
+      // together, k-block outer (tiles above the diagonal are computed and masked) ----
+      float4v mreg[NT], preg[NT];
 #pragma unroll
-    for (int J = 0; J < NGB; ++J) mreg[J] = preg[J] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int J = 0; J < NT; ++J) mreg[J] = preg[J] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int u = 0; u < KB; ++u) {
-      const int c0 = 32 * u + 8 * lg;
-      if constexpr (SCALAR) {
+      for (int u = 0; u < KB; ++u) {
+        const int c0 = 32 * u + 8 * lg;
         H8 ah[NT], al[NT];
 #pragma unroll
         for (int J = 0; J < NT; ++J) {
@@ -1788,114 +1809,321 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
         for (int J = 0; J < NT; ++J) mreg[J] = mma_pair_bf16(al[J].b, bmh[u].b, mreg[J]);
 #pragma unroll
         for (int J = 0; J < NT; ++J) preg[J] = mma_pair_bf16(al[J].b, qmh8[u].b, preg[J]);
-      } else {
-        // A sides: block 0 from slot 3 for tiles 2 and 3 (slot 0 for tile 1), blocks
-        // 1 and 2 from slots 1 and 2
-        const int row0 = (wave >= 2 ? 48 : 0) + li;
-        H8 ah[3], al[3];
-        ah[0].q = *reinterpret_cast<const uint4*>(&sm.ra.am.hi[row0][c0]);
-        al[0].q = *reinterpret_cast<const uint4*>(&sm.ra.am.lo[row0][c0]);
+      }
+      if (want_out && orow) {  // output rows are this wave's own rows (q scale qsc)
 #pragma unroll
-        for (int J = 1; J < 3; ++J) {
-          ah[J].q = *reinterpret_cast<const uint4*>(&sm.ra.am.hi[16 * J + li][c0]);
-          al[J].q = *reinterpret_cast<const uint4*>(&sm.ra.am.lo[16 * J + li][c0]);
+        for (int J = 0; J < NT; ++J) {
+          const int s0 = 16 * J + 4 * lg;
+          H8 h8;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h8.h[e] = (_Float16)((s0 + e <= r) ? preg[J][e] * qsc : 0.0f);
+          *reinterpret_cast<uint2*>(P_g + p_frag(ro, J)) = h8.u[0];
         }
-        H8 bsh, bsl, qsh, qsl;
+      }
+      if (has_next) load_raw(nx, raw, 4 | 16);
+      wg_barrier();  // A- is dead: its space now holds M and T
+#pragma unroll
+      for (int J = 0; J < NT; ++J) {
+        if (J <= wave) {
+          const int s0 = 16 * J + 4 * lg;
+          float4 m4;
+          m4.x = (s0 + 0 < r) ? mreg[J][0] : 0.0f;
+          m4.y = (s0 + 1 < r) ? mreg[J][1] : 0.0f;
+          m4.z = (s0 + 2 < r) ? mreg[J][2] : 0.0f;
+          m4.w = (s0 + 3 < r) ? mreg[J][3] : 0.0f;
+          *reinterpret_cast<float4*>(&sm.ra.mt.m[r][s0]) = m4;
+        }
+      }
+      wg_barrier();
+
+    } else {
+      // ---- phase 2: decayed operands and written values of this wave's rows, one
+      // channel group at a time ----
+      // Off-diagonal Gram blocks M(I, J), P(I, J), J < I, with per-channel decay: B and
+      // Q sides of tile I referenced to its first row (kept in fp32 until the Gram
+      // phase), A side of tile J to its last row (LDS slot J); block (3, 2) pairs
+      // them directly, blocks (I, 0..1) of the lower half pair them through the
+      // reference between tiles 1 and 2: slot 3 holds tile 0's A side moved there
+      // (times e^{L_1}), and tile 3's B and Q sides move back to it (times e^{L_2}) in
+      // the Gram phase. Tile 3's own A side is never an off-diagonal operand. The
+      // diagonal blocks use row 7 of the tile on both sides and run here, on fp32
+      // MFMA straight from registers (the A and B operand layouts of a 16-row tile
+      // are the same).
+      const float wrow = (V == GDN_VARIANT_FG2 ? 1.0f : wscal) * wsc;  // written-value factor of the row
+      float bsv[SCALAR ? 1 : 32], qsv[SCALAR ? 1 : 32];                // B and Q sides (per-channel decay)
+      H8 bmh[SCALAR ? KB : 1], bml[SCALAR ? KB : 1], qmh8[SCALAR ? KB : 1], qml8[SCALAR ? KB : 1];  // (scalar)
+      float4v mdg = {0.0f, 0.0f, 0.0f, 0.0f}, pdg = {0.0f, 0.0f, 0.0f, 0.0f};  // diagonal blocks M^T, P^T
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int c0 = 32 * u + 8 * lg;  // 8 consecutive channels
+        float cm[8], c7[8], c157[8], cP[8], cQ[8];
+        if constexpr (!SCALAR) {
+          auto ld8 = [&](const float* src, float* d) __attribute__((always_inline)) {
+            const float4 x0 = *reinterpret_cast<const float4*>(src);
+            const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+            d[0] = x0.x, d[1] = x0.y, d[2] = x0.z, d[3] = x0.w, d[4] = x1.x, d[5] = x1.y, d[6] = x1.z, d[7] = x1.w;
+          };
+          ld8(&sm.cu.v.cst[wave][0][c0], cm);
+          ld8(&sm.cu.v.cst[wave][1][c0], c7);
+          ld8(&sm.cu.v.cst[wave][2][c0], c157);
+          ld8(&sm.cu.v.cst[wave][3][c0], cP);
+          ld8(&sm.cu.v.cst[wave][4][c0], cQ);
+        }
+        const uint4 kr = raw.k[u], vr = raw.v[u];
+        uint4 br = {}, qr = {};
+        if constexpr (CH_BJ) br = raw.b[u];
+        if (want_out && valid && orow) qr = raw.q[u];
+        half8 xbt, xat, xv;
+        H8 hi, lo, qp;
+        float aev[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float b0 = bsv[8 * u + e], q0 = qsv[8 * u + e];
-          bsh.b[e] = (__bf16)b0;
-          bsl.b[e] = (__bf16)(b0 - (float)bsh.b[e]);
-          qsh.b[e] = (__bf16)q0;
-          qsl.b[e] = (__bf16)(q0 - (float)qsh.b[e]);
-        }
-        // blocks 0 and 1 of tile 3: its B and Q sides moved to the reference between
-        // tiles 1 and 2 (times e^{L_2}, at most 1)
-        H8 bxh = bsh, bxl = bsl, qxh = qsh, qxl = qsl;
-        if (wave == 3) {
-          const float4 d0 = *reinterpret_cast<const float4*>(&sm.cu.v.dfac[1][c0]);
-          const float4 d1 = *reinterpret_cast<const float4*>(&sm.cu.v.dfac[1][c0 + 4]);
-          const float df[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float b0 = bsv[8 * u + e] * df[e], q0 = qsv[8 * u + e] * df[e];
-            bxh.b[e] = (__bf16)b0;
-            bxl.b[e] = (__bf16)(b0 - (float)bxh.b[e]);
-            qxh.b[e] = (__bf16)q0;
-            qxl.b[e] = (__bf16)(q0 - (float)qxh.b[e]);
+          const float kf = bf(kr, e);
+          float a, bb;
+          if constexpr (V == GDN_VARIANT_FG2) {
+            const float sb = valid ? __builtin_amdgcn_sqrtf(bf(br, e)) : 0.0f;
+            a = sb * kf;
+            bb = a;
+            xv[e] = (_Float16)(bf(vr, e) * sb * wsc);
+          } else if constexpr (V == GDN_VARIANT_ASYM) {
+            a = valid ? kf : 0.0f;
+            bb = bscal * (STAB == 2 ? stab_j(stc, kf, bf(br, e)) : bf(br, e));
+          } else {  // KDA, GDN (kscal = sqrt(beta)); DeltaProduct (bscal = beta)
+            a = kscal * kf;
+            bb = bscal * a;
+          }
+          if constexpr (V != GDN_VARIANT_FG2) xv[e] = (_Float16)(bf(vr, e) * wrow);
+          const float qf = bf(qr, e);
+          if constexpr (SCALAR) {
+            hi.b[e] = (__bf16)a;
+            lo.b[e] = (__bf16)(a - (float)hi.b[e]);
+            bmh[u].b[e] = (__bf16)bb;
+            bml[u].b[e] = (__bf16)(bb - (float)bmh[u].b[e]);
+            qmh8[u].b[e] = (__bf16)qf;
+            qml8[u].b[e] = (__bf16)(qf - (float)qmh8[u].b[e]);
+            xbt[e] = (_Float16)(bb * eg_row);
+            xat[e] = (_Float16)(a * eat_row);
+            qp.h[e] = (_Float16)(qf * eg_row * qsc);
+          } else {
+            const int x = 8 * u + e;
+            const float fup = __builtin_amdgcn_exp2f(G[x] - cm[e]);  // e^{G - G_7}
+            const float eam = __builtin_amdgcn_rcpf(fup);            // e^{G_7 - G}
+            const float st = fup * c7[e];                            // e^{G - G_start}
+            const float te = eam * c157[e];                          // e^{G_end - G}
+            const float ae = a * te;
+            aev[e] = ae;
+            bsv[x] = bb * st;
+            qsv[x] = qf * st;
+            xbt[e] = (_Float16)(bsv[x] * cP[e]);                     // B e^{G}
+            xat[e] = (_Float16)(ae * cQ[e]);                         // A e^{G_C - G}
+            qp.h[e] = (_Float16)(qsv[x] * cP[e] * qsc);              // Q e^{G}, scaled
+            const float ad = a * eam;
+            mdg = __builtin_amdgcn_mfma_f32_16x16x4f32(ad, bb * fup, mdg, 0, 0, 0);
+            pdg = __builtin_amdgcn_mfma_f32_16x16x4f32(ad, qf * fup, pdg, 0, 0, 0);
           }
         }
-        mreg[0] = mma_pair_bf16(ah[0].b, bxh.b, mreg[0]);
-        mreg[1] = mma_pair_bf16(ah[1].b, bxh.b, mreg[1]);
-        mreg[2] = mma_pair_bf16(ah[2].b, bsh.b, mreg[2]);
-        preg[0] = mma_pair_bf16(ah[0].b, qxh.b, preg[0]);
-        preg[1] = mma_pair_bf16(ah[1].b, qxh.b, preg[1]);
-        preg[2] = mma_pair_bf16(ah[2].b, qsh.b, preg[2]);
-        mreg[0] = mma_pair_bf16(ah[0].b, bxl.b, mreg[0]);
-        mreg[1] = mma_pair_bf16(ah[1].b, bxl.b, mreg[1]);
-        mreg[2] = mma_pair_bf16(ah[2].b, bsl.b, mreg[2]);
-        preg[0] = mma_pair_bf16(ah[0].b, qxl.b, preg[0]);
-        preg[1] = mma_pair_bf16(ah[1].b, qxl.b, preg[1]);
-        preg[2] = mma_pair_bf16(ah[2].b, qsl.b, preg[2]);
-        mreg[0] = mma_pair_bf16(al[0].b, bxh.b, mreg[0]);
-        mreg[1] = mma_pair_bf16(al[1].b, bxh.b, mreg[1]);
-        mreg[2] = mma_pair_bf16(al[2].b, bsh.b, mreg[2]);
-        preg[0] = mma_pair_bf16(al[0].b, qxh.b, preg[0]);
-        preg[1] = mma_pair_bf16(al[1].b, qxh.b, preg[1]);
-        preg[2] = mma_pair_bf16(al[2].b, qsh.b, preg[2]);
+        if (SCALAR || wave < 3) {
+          if constexpr (!SCALAR) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              hi.b[e] = (__bf16)aev[e];
+              lo.b[e] = (__bf16)(aev[e] - (float)hi.b[e]);
+            }
+          }
+          *reinterpret_cast<uint4*>(&sm.ra.am.hi[r][c0]) = hi.q;
+          *reinterpret_cast<uint4*>(&sm.ra.am.lo[r][c0]) = lo.q;
+        }
+        if constexpr (!SCALAR) {
+          if (wave == 0) {  // tile 0's A side at the reference between tiles 1 and 2 (slot 3)
+            const float4 d0 = *reinterpret_cast<const float4*>(&sm.cu.v.dfac[0][c0]);
+            const float4 d1 = *reinterpret_cast<const float4*>(&sm.cu.v.dfac[0][c0 + 4]);
+            const float df[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+            H8 mh, ml;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float am = aev[e] * df[e];
+              mh.b[e] = (__bf16)am;
+              ml.b[e] = (__bf16)(am - (float)mh.b[e]);
+            }
+            *reinterpret_cast<uint4*>(&sm.ra.am.hi[48 + li][c0]) = mh.q;
+            *reinterpret_cast<uint4*>(&sm.ra.am.lo[48 + li][c0]) = ml.q;
+          }
+        }
+        if (want_out && orow)
+          *reinterpret_cast<uint4*>(Q_g + ((((ro >> 4) * KB + u) * 64 + (ro & 15) + 16 * lg) * 8)) = qp.q;
+        // B+ and A^ of the group transposed by MFMA: lane (li, lg) then holds steps
+        // 16 wave + 4 lg .. of channel 32 u + 16 h + li
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const float4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
+          const float4v tb = mma_pair_f16(xbt, sel[hh], zero);
+          const float4v ta = mma_pair_f16(xat, sel[hh], zero);
+          const int c = 32 * u + 16 * hh + li;
+          H8 pb, pa;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pb.h[e] = (_Float16)tb[e];
+            pa.h[e] = (_Float16)ta[e];
+          }
+          *reinterpret_cast<uint2*>(&sm.bt[c][16 * wave + 4 * lg]) = pb.u[0];
+          const float4v tv = mma_pair_f16(xv, sel[hh], zero);
+          H8 pv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pv.h[e] = (_Float16)tv[e];
+          *reinterpret_cast<uint2*>(&sm.wvt[c][16 * wave + 4 * lg]) = pv.u[0];
+          *reinterpret_cast<uint2*>(AT_g + size_t((((c >> 4) * CK + (wave >> 1)) * 64 + li + 16 * (2 * (wave & 1) + (lg >> 1))) * 8 +
+                                                  4 * (lg & 1))) = pa.u[0];
+        }
       }
-    }
-    // Gram block of tile J as seen by this wave: accumulator and, for scalar decay,
-    // the factors e^{G_i - G_j} of its entries (j = 16 J + 4 lg + e, i = r)
-    float fdec[NT][4];
+
+      // The next item's inputs load in three groups, each once this item's copy is
+      // consumed, so that the loads of the two workgroups on a CU do not arrive in
+      // one burst: key and values here, query and beta / j after the Grams, the decay
+      // before W and U~.
+      if (has_next) load_raw(nx, raw, 1 | 2);
+      wg_barrier();
+
+      // ---- Gram tiles: M^T(J, I) = A(J) B(I)^T and P^T(J, I) = A(J) Q(I)^T, k-block
+      // outer, independent accumulator chains interleaved. Scalar decay: every J
+      // (blocks above the diagonal are computed and masked), the decay applied to the
+      // entries afterwards. Per-channel decay: the three off-diagonal blocks J = 0, 1, 2
+      // (those with J >= I are computed and masked). ----
+      constexpr int NGB = SCALAR ? NT : NT - 1;
+      float4v mreg[NGB], preg[NGB];
 #pragma unroll
-    for (int J = 0; J < NT; ++J)
+      for (int J = 0; J < NGB; ++J) mreg[J] = preg[J] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) fdec[J][e] = 1.0f;
-    if constexpr (SCALAR) {
+      for (int u = 0; u < KB; ++u) {
+        const int c0 = 32 * u + 8 * lg;
+        if constexpr (SCALAR) {
+          H8 ah[NT], al[NT];
+#pragma unroll
+          for (int J = 0; J < NT; ++J) {
+            ah[J].q = *reinterpret_cast<const uint4*>(&sm.ra.am.hi[16 * J + li][c0]);
+            al[J].q = *reinterpret_cast<const uint4*>(&sm.ra.am.lo[16 * J + li][c0]);
+          }
+#pragma unroll
+          for (int J = 0; J < NT; ++J) mreg[J] = mma_pair_bf16(ah[J].b, bmh[u].b, mreg[J]);
+#pragma unroll
+          for (int J = 0; J < NT; ++J) preg[J] = mma_pair_bf16(ah[J].b, qmh8[u].b, preg[J]);
+#pragma unroll
+          for (int J = 0; J < NT; ++J) mreg[J] = mma_pair_bf16(ah[J].b, bml[u].b, mreg[J]);
+#pragma unroll
+          for (int J = 0; J < NT; ++J) preg[J] = mma_pair_bf16(ah[J].b, qml8[u].b, preg[J]);
+#pragma unroll
+          for (int J = 0; J < NT; ++J) mreg[J] = mma_pair_bf16(al[J].b, bmh[u].b, mreg[J]);
+#pragma unroll
+          for (int J = 0; J < NT; ++J) preg[J] = mma_pair_bf16(al[J].b, qmh8[u].b, preg[J]);
+        } else {
+          // A sides: block 0 from slot 3 for tiles 2 and 3 (slot 0 for tile 1), blocks
+          // 1 and 2 from slots 1 and 2
+          const int row0 = (wave >= 2 ? 48 : 0) + li;
+          H8 ah[3], al[3];
+          ah[0].q = *reinterpret_cast<const uint4*>(&sm.ra.am.hi[row0][c0]);
+          al[0].q = *reinterpret_cast<const uint4*>(&sm.ra.am.lo[row0][c0]);
+#pragma unroll
+          for (int J = 1; J < 3; ++J) {
+            ah[J].q = *reinterpret_cast<const uint4*>(&sm.ra.am.hi[16 * J + li][c0]);
+            al[J].q = *reinterpret_cast<const uint4*>(&sm.ra.am.lo[16 * J + li][c0]);
+          }
+          H8 bsh, bsl, qsh, qsl;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float b0 = bsv[8 * u + e], q0 = qsv[8 * u + e];
+            bsh.b[e] = (__bf16)b0;
+            bsl.b[e] = (__bf16)(b0 - (float)bsh.b[e]);
+            qsh.b[e] = (__bf16)q0;
+            qsl.b[e] = (__bf16)(q0 - (float)qsh.b[e]);
+          }
+          // blocks 0 and 1 of tile 3: its B and Q sides moved to the reference between
+          // tiles 1 and 2 (times e^{L_2}, at most 1)
+          H8 bxh = bsh, bxl = bsl, qxh = qsh, qxl = qsl;
+          if (wave == 3) {
+            const float4 d0 = *reinterpret_cast<const float4*>(&sm.cu.v.dfac[1][c0]);
+            const float4 d1 = *reinterpret_cast<const float4*>(&sm.cu.v.dfac[1][c0 + 4]);
+            const float df[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float b0 = bsv[8 * u + e] * df[e], q0 = qsv[8 * u + e] * df[e];
+              bxh.b[e] = (__bf16)b0;
+              bxl.b[e] = (__bf16)(b0 - (float)bxh.b[e]);
+              qxh.b[e] = (__bf16)q0;
+              qxl.b[e] = (__bf16)(q0 - (float)qxh.b[e]);
+            }
+          }
+          mreg[0] = mma_pair_bf16(ah[0].b, bxh.b, mreg[0]);
+          mreg[1] = mma_pair_bf16(ah[1].b, bxh.b, mreg[1]);
+          mreg[2] = mma_pair_bf16(ah[2].b, bsh.b, mreg[2]);
+          preg[0] = mma_pair_bf16(ah[0].b, qxh.b, preg[0]);
+          preg[1] = mma_pair_bf16(ah[1].b, qxh.b, preg[1]);
+          preg[2] = mma_pair_bf16(ah[2].b, qsh.b, preg[2]);
+          mreg[0] = mma_pair_bf16(ah[0].b, bxl.b, mreg[0]);
+          mreg[1] = mma_pair_bf16(ah[1].b, bxl.b, mreg[1]);
+          mreg[2] = mma_pair_bf16(ah[2].b, bsl.b, mreg[2]);
+          preg[0] = mma_pair_bf16(ah[0].b, qxl.b, preg[0]);
+          preg[1] = mma_pair_bf16(ah[1].b, qxl.b, preg[1]);
+          preg[2] = mma_pair_bf16(ah[2].b, qsl.b, preg[2]);
+          mreg[0] = mma_pair_bf16(al[0].b, bxh.b, mreg[0]);
+          mreg[1] = mma_pair_bf16(al[1].b, bxh.b, mreg[1]);
+          mreg[2] = mma_pair_bf16(al[2].b, bsh.b, mreg[2]);
+          preg[0] = mma_pair_bf16(al[0].b, qxh.b, preg[0]);
+          preg[1] = mma_pair_bf16(al[1].b, qxh.b, preg[1]);
+          preg[2] = mma_pair_bf16(al[2].b, qsh.b, preg[2]);
+        }
+      }
+      // Gram block of tile J as seen by this wave: accumulator and, for scalar decay,
+      // the factors e^{G_i - G_j} of its entries (j = 16 J + 4 lg + e, i = r)
+      float fdec[NT][4];
+#pragma unroll
+      for (int J = 0; J < NT; ++J)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fdec[J][e] = 1.0f;
+      if constexpr (SCALAR) {
+#pragma unroll
+        for (int J = 0; J < NT; ++J) {
+          const float4 gj = *reinterpret_cast<const float4*>(&sm.cu.s.grow[16 * J + 4 * lg]);
+          const float g4[4] = {gj.x, gj.y, gj.z, gj.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) fdec[J][e] = __builtin_amdgcn_exp2f(fminf(gabs - g4[e], 0.0f));
+        }
+      }
+      auto mblk = [&](int J) __attribute__((always_inline)) -> float4v {
+        if constexpr (SCALAR) return mreg[J];
+        else return J < wave ? mreg[J < 2 ? J : 2] : mdg;
+      };
+      auto pblk = [&](int J) __attribute__((always_inline)) -> float4v {
+        if constexpr (SCALAR) return preg[J];
+        else return J < wave ? preg[J < 2 ? J : 2] : pdg;
+      };
+      if (want_out && orow) {  // output rows are this wave's own rows (q scale qsc)
+#pragma unroll
+        for (int J = 0; J < NT; ++J) {
+          const int s0 = 16 * J + 4 * lg;
+          const float4v src = pblk(J);
+          H8 h8;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h8.h[e] = (_Float16)((s0 + e <= r) ? src[e] * fdec[J][e] * qsc : 0.0f);
+          *reinterpret_cast<uint2*>(P_g + p_frag(ro, J)) = h8.u[0];
+        }
+      }
+      if (has_next) load_raw(nx, raw, 4 | 16);
+      wg_barrier();  // the A sides are dead: their space now holds M and T
 #pragma unroll
       for (int J = 0; J < NT; ++J) {
-        const float4 gj = *reinterpret_cast<const float4*>(&sm.cu.s.grow[16 * J + 4 * lg]);
-        const float g4[4] = {gj.x, gj.y, gj.z, gj.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) fdec[J][e] = __builtin_amdgcn_exp2f(fminf(gabs - g4[e], 0.0f));
+        if (J <= wave) {
+          const int s0 = 16 * J + 4 * lg;
+          const float4v src = mblk(J);
+          float4 m4;
+          m4.x = (s0 + 0 < r) ? src[0] * fdec[J][0] : 0.0f;
+          m4.y = (s0 + 1 < r) ? src[1] * fdec[J][1] : 0.0f;
+          m4.z = (s0 + 2 < r) ? src[2] * fdec[J][2] : 0.0f;
+          m4.w = (s0 + 3 < r) ? src[3] * fdec[J][3] : 0.0f;
+          *reinterpret_cast<float4*>(&sm.ra.mt.m[r][s0]) = m4;
+        }
       }
+      wg_barrier();
+
     }
-    auto mblk = [&](int J) __attribute__((always_inline)) -> float4v {
-      if constexpr (SCALAR) return mreg[J];
-      else return J < wave ? mreg[J < 2 ? J : 2] : mdg;
-    };
-    auto pblk = [&](int J) __attribute__((always_inline)) -> float4v {
-      if constexpr (SCALAR) return preg[J];
-      else return J < wave ? preg[J < 2 ? J : 2] : pdg;
-    };
-    if (want_out && orow) {  // output rows are this wave's own rows (q scale qsc)
-#pragma unroll
-      for (int J = 0; J < NT; ++J) {
-        const int s0 = 16 * J + 4 * lg;
-        const float4v src = pblk(J);
-        H8 h8;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) h8.h[e] = (_Float16)((s0 + e <= r) ? src[e] * fdec[J][e] * qsc : 0.0f);
-        *reinterpret_cast<uint2*>(P_g + p_frag(ro, J)) = h8.u[0];
-      }
-    }
-    if (has_next) load_raw(nx, raw, 4 | 16);
-    wg_barrier();  // the A sides are dead: their space now holds M and T
-#pragma unroll
-    for (int J = 0; J < NT; ++J) {
-      if (J <= wave) {
-        const int s0 = 16 * J + 4 * lg;
-        const float4v src = mblk(J);
-        float4 m4;
-        m4.x = (s0 + 0 < r) ? src[0] * fdec[J][0] : 0.0f;
-        m4.y = (s0 + 1 < r) ? src[1] * fdec[J][1] : 0.0f;
-        m4.z = (s0 + 2 < r) ? src[2] * fdec[J][2] : 0.0f;
-        m4.w = (s0 + 3 < r) ? src[3] * fdec[J][3] : 0.0f;
-        *reinterpret_cast<float4*>(&sm.ra.mt.m[r][s0]) = m4;
-      }
-    }
-    wg_barrier();
 
     // ---- T = (I + M)^{-1}: diagonal 16x16 blocks by forward substitution ----
     if (wave == 0) {
@@ -2013,22 +2241,32 @@ int launch_prep_t(const Problem& p, void* ws, bool want_out, hipStream_t s) {
     if (prep2_covers(p)) {  // two workgroups per CU
       const int64_t grid = std::min<int64_t>(items, 2 * int64_t(device_cus()));
       unsigned char* w = static_cast<unsigned char*>(ws);
+      unsigned char* fl = w + record_bytes(p, L);  // one byte per item, after the records
       const int wo = want_out ? 1 : 0;
       const dim3 g = dim3(unsigned(grid));
       if constexpr (DPV) {
         if (p.n_step == 2)
-          chunk_prep2_kernel<V, 0, 2><<<g, kThreads, 0, s>>>(p, w, L, wo);
+          chunk_prep2_kernel<V, 0, 2, 0><<<g, kThreads, 0, s>>>(p, w, fl, L, wo);
         else
-          chunk_prep2_kernel<V, 0, 4><<<g, kThreads, 0, s>>>(p, w, L, wo);
-      } else if constexpr (V == GDN_VARIANT_ASYM) {
-        if (p.stabilize == GDN_STABILIZE_CLIP_DECAY)
-          chunk_prep2_kernel<V, 1, 1><<<g, kThreads, 0, s>>>(p, w, L, wo);
-        else if (p.stabilize == GDN_STABILIZE_PROJECT_J)
-          chunk_prep2_kernel<V, 2, 1><<<g, kThreads, 0, s>>>(p, w, L, wo);
-        else
-          chunk_prep2_kernel<V, 0, 1><<<g, kThreads, 0, s>>>(p, w, L, wo);
+          chunk_prep2_kernel<V, 0, 4, 0><<<g, kThreads, 0, s>>>(p, w, fl, L, wo);
+      } else if constexpr (V == GDN_VARIANT_GDN || V == GDN_VARIANT_DELTAPRODUCT) {
+        chunk_prep2_kernel<V, 0, 1, 0><<<g, kThreads, 0, s>>>(p, w, fl, L, wo);
       } else {
-        chunk_prep2_kernel<V, 0, 1><<<g, kThreads, 0, s>>>(p, w, L, wo);
+        // per-channel decay: chunks of mild decay first, then the flagged ones
+        auto two_pass = [&](auto mild_pass, auto flagged_pass) {
+          mild_pass<<<g, kThreads, 0, s>>>(p, w, fl, L, wo);
+          flagged_pass<<<g, kThreads, 0, s>>>(p, w, fl, L, wo);
+        };
+        if constexpr (V == GDN_VARIANT_ASYM) {
+          if (p.stabilize == GDN_STABILIZE_CLIP_DECAY)
+            two_pass(chunk_prep2_kernel<V, 1, 1, 1>, chunk_prep2_kernel<V, 1, 1, 2>);
+          else if (p.stabilize == GDN_STABILIZE_PROJECT_J)
+            two_pass(chunk_prep2_kernel<V, 2, 1, 1>, chunk_prep2_kernel<V, 2, 1, 2>);
+          else
+            two_pass(chunk_prep2_kernel<V, 0, 1, 1>, chunk_prep2_kernel<V, 0, 1, 2>);
+        } else {
+          two_pass(chunk_prep2_kernel<V, 0, 1, 1>, chunk_prep2_kernel<V, 0, 1, 2>);
+        }
       }
       return int(hipGetLastError());
     }

@@ -114,6 +114,16 @@ constexpr ChunkLayout make_chunk_layout(size_t es, size_t dk, size_t dv, size_t 
 
 ChunkLayout chunk_layout(const Problem& p);
 
+// Workspace of a chunked launch: the records of its B * H * nchunks items, then one
+// flag byte per item (set by the prepare pass for chunks it leaves to its second
+// pass), rounded to 256 bytes.
+inline size_t record_bytes(const Problem& p, const ChunkLayout& L) {
+  return size_t(p.B) * size_t(p.H) * size_t(p.nchunks) * L.bytes;
+}
+inline size_t workspace_bytes(const Problem& p, const ChunkLayout& L) {
+  return record_bytes(p, L) + round_up_c(size_t(p.B) * size_t(p.H) * size_t(p.nchunks), 256);
+}
+
 // Kernel launchers (defined in the .hip translation units). Return hipError_t as int.
 int launch_recurrent(const Problem& p, float* state, void* stream);
 int launch_chunk(const Problem& p, void* ws, bool want_output, void* stream);

@@ -57,8 +57,15 @@ extern "C" int gdn_chunk_fwd_static(const gdn_args* args, void* stream) {
   // without s_final the state between blocks is kept at the start of the buffer
   const size_t carry = p.s_final ? 0 : round_up_c(bh * size_t(p.dk) * size_t(p.dv) * sizeof(float), 256);
   const size_t cap = GDN_STATIC_SCRATCH_BYTES;
-  if (carry + bh * L.bytes > cap) return GDN_ERR_UNSUPPORTED;  // one chunk of every sequence must fit
-  const int64_t per_block = int64_t((cap - carry) / (bh * L.bytes));
+  // records and flag bytes of a block of n chunks
+  auto block_bytes = [&](int64_t n) {
+    Problem q = p;
+    q.nchunks = n;
+    return workspace_bytes(q, L);
+  };
+  if (carry + block_bytes(1) > cap) return GDN_ERR_UNSUPPORTED;  // one chunk of every sequence must fit
+  int64_t per_block = int64_t((cap - carry) / (bh * (L.bytes + 1)));
+  while (per_block > 1 && carry + block_bytes(per_block) > cap) --per_block;
   void* base = nullptr;
   st = scratch_address(&base);
   if (st != GDN_OK) return st;
