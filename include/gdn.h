@@ -96,7 +96,12 @@ typedef struct gdn_args {
                        rounding, workspace sized for 32)                      */
   int32_t n_h;      /* Householder steps per token (DELTAPRODUCT, 1..8), else 1;
                        chunked entry points: chunk / n_h >= 16 with n_h = 3
-                       counted as 4 (a chunk holds whole tokens)              */
+                       counted as 4 (a chunk holds whole tokens and one 16-row
+                       output tile), so they take n_h = 1..4 (n_h 3 and 4 only
+                       with chunk 64, n_h 2 with chunk 32 or 64) and return
+                       GDN_ERR_UNSUPPORTED for n_h 5..8 and for fp32 with
+                       dk = 128 and n_h 3 or 4 (run as 32-step chunks);
+                       gdn_recurrent_step takes every n_h                     */
   const void* q;
   const void* k;
   const void* v;
@@ -128,7 +133,9 @@ size_t gdn_workspace_bytes(const gdn_args* args);
 int gdn_chunk_fwd(const gdn_args* args, void* ws, size_t ws_bytes, void* stream);
 
 /* Same pass computing the final state only (o is not read or written;
- * s_final must be non-NULL). */
+ * s_final must be non-NULL): the state S_T the recurrence above reaches after T
+ * tokens (FG2-GDN reading notes, section 2.2 eq. (11), the state a chunked
+ * prefill hands to decoding). */
 int gdn_final_state(const gdn_args* args, void* ws, size_t ws_bytes, void* stream);
 
 /* The two stages of gdn_chunk_fwd, for callers that schedule them separately
@@ -167,7 +174,11 @@ int gdn_chunk_fwd_static(const gdn_args* args, void* stream);
 
 /* Token-sequential recurrence: advances state_inout ([B, H, dk, dv] float32,
  * updated in place) by args->T tokens, writing o for each (T = 1 is one decode
- * step). args->s0, args->s_final and args->chunk are ignored. No workspace. */
+ * step): the step above applied token by token, exactly as the FG2-GDN reading
+ * notes write it (section 2.2 eq. (11); section 2.1 eq. (6) for the delta rule it
+ * extends; GDN2-stability page eq. (1) for ASYM; DeltaProduct summary, "Approach",
+ * for the n_h sub-steps). args->s0, args->s_final and args->chunk are ignored. No
+ * workspace. */
 int gdn_recurrent_step(const gdn_args* args, float* state_inout, void* stream);
 
 /* GDN2 stabilisers: token-wise transforms of the ASYM inputs that bound the spectral norm of each step's transition D (I - eta j k^T)
@@ -210,7 +221,10 @@ typedef struct gdn_grads {
   float* ds0;
 } gdn_grads;
 
-/* Bytes of device workspace gdn_recurrent_bwd needs (0 for an invalid set). */
+/* Bytes of device workspace gdn_recurrent_bwd needs (0 for an invalid set):
+ * about dk * dv bytes per token (or sub-step) and head for the per-column-slice
+ * partial row gradients, plus the 64-token state checkpoints; 16 KiB per token and
+ * head at dk = dv = 128 (1.24 GB for 4,096 tokens x 16 heads). */
 size_t gdn_bwd_workspace_bytes(const gdn_args* args);
 
 /* Backward pass (reverse-mode gradients) of the token recurrence for every variant
