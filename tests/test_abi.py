@@ -179,9 +179,13 @@ def test_fp32_dk128_chunk64_runs_as_chunk32(lib):
 
 
 def test_workspace_bytes_grows_with_tokens(lib):
-    small = lib.gdn_workspace_bytes(ctypes.byref(good_args(T=64)))
-    big = lib.gdn_workspace_bytes(ctypes.byref(good_args(T=6400)))
-    assert big == 100 * small
+    # records of B * H * chunks items, then one flag byte per item rounded to 256
+    def flags(items):
+        return (items + 255) // 256 * 256
+    small = lib.gdn_workspace_bytes(ctypes.byref(good_args(T=64)))       # 2 * 4 items
+    big = lib.gdn_workspace_bytes(ctypes.byref(good_args(T=6400)))       # 2 * 4 * 100 items
+    assert big - flags(800) == 100 * (small - flags(8))
+    assert (small - flags(8)) % 256 == 0
     assert lib.gdn_workspace_bytes(ctypes.byref(good_args(dk=48))) == 0
     assert lib.gdn_workspace_bytes(None) == 0
 
