@@ -1,119 +1,184 @@
 // Backward pass of the token recurrence (reverse mode), every variant: FG2, FG2+, KDA,
 // GDN, ASYM, and DeltaProduct as its sequence of Householder sub-steps.
 //
-// Per token, with X = Diag(alpha) S_{t-1}, u = w - X^T b, S_t = X + a u^T,
-// o_t = S_t^T q_t and G = dL/dS_t (the later tokens' gradient plus q_t do_t^T):
+// Per step, with X = Diag(alpha) S_{t-1}, u = w - X^T b, S_t = X + a u^T,
+// o_t = S_t^T q_t and G = dL/dS_t (the later steps' gradient plus q_t do_t^T):
 //   dq = S_t do,  dw = G^T a,  da = G u,  db = -X dw,  dX = G - b dw^T,
 //   dalpha = rowsum(dX . S_{t-1}),  dL/dS_{t-1} = Diag(alpha) dX,
 // then the chain rule through the variant's (a, b, w, alpha) map (FG2-GDN reading
 // notes, section 2.2 eq. (11) and section 2.3 eq. (13); GDN2-stability page, eq. (1)).
 //
-// Kernel A: one wave per (batch, head, 16-column slice of the state) (lane
-// l = j + 16 g: column j, key rows g NR .. g NR + NR - 1, as in the forward recurrent
-// kernel). A forward pass stores the slice state every kCB tokens; the backward sweep
-// takes the chunks in reverse, recomputes the chunk's states from its checkpoint
-// into the workspace, and walks the chunk backwards. Column-complete quantities
-// (dw) come out of the wave directly; row quantities (da, db, dq, dalpha) are partial
-// sums over the wave's 16 columns, reduced across the 16 lanes by a transposing
-// butterfly and written per slice. Kernel B sums the slices in a fixed order and
-// applies the variant's chain rule, one wave per token and head.
+// Only two things are sequential: the state S runs forward, and the state gradient
+// runs backward as G <- Diag(alpha) (I - b a^T) G + q do^T, which does not involve S.
+// So the pass is split into:
+//  1. the operand kernel: every step's a, b, alpha, q rows and w, do columns, once,
+//     in float32 (the later kernels do not branch on the variant);
+//  2. the chain kernel: the S and G recursions side by side, in separate waves, each
+//     over narrow column slices; S is stored at the start and G at the end of every
+//     64-step interval;
+//  3. the interval kernel: every (batch*head, 16-column slice, interval) on its own.
+//     It recomputes the interval's states from the stored S (keeping one state in
+//     four in a per-workgroup scratch slot, and four states at a time in registers)
+//     and walks the interval backwards from the stored G, writing the slice's row
+//     partials and the column-complete dw;
+//  4. the reduce kernel: slices summed in a fixed order, then the variant's chain rule.
+// Every sum runs in a fixed order: the results are deterministic.
+//
+// Lane layout of the chain and interval kernels (rows on lanes): lane l owns state
+// rows l*NR .. l*NR+NR-1 (NR = max(dk / 64, 1); lanes past dk hold zeros) and all CW
+// columns of its slice in registers. Sums over a slice's columns stay inside a lane;
+// sums over rows are wave reductions: a transposing butterfly over the lane bits
+// below CW (each exchange halves the values a lane carries, DPP within 16-lane rows)
+// and then plain pair sums over the remaining lane bits, which leaves the total of
+// column bitrev(l mod CW) in lane l; v_readlane then broadcasts them as scalars.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 namespace {
 
-constexpr int kCB = 64;  // tokens per checkpoint interval
+constexpr int kCB = 64;        // steps per checkpoint interval
+constexpr int kSub = 4;        // steps whose states the interval kernel holds in registers
+constexpr int kCW = 16;        // columns of an interval-kernel wave (a row-partial slice)
+constexpr int kChainCW = 4;    // columns of a chain-kernel wave
+constexpr int kChainRing = 16; // steps of operands a chain wave keeps in flight
+constexpr int kSlots = 1024;   // interval-kernel workgroups, each with a scratch slot
 
-// Workspace (floats): per (batch*head, slice) the checkpoints and the current chunk's
-// states, in lane order ([step][NR/4][64 lanes][4]: one 16-byte vector per lane);
-// then the row partials [slice][B*T*H][4][dk] and dw [B*T*H][dv].
+__host__ __device__ constexpr int rows_per_lane(int64_t dk) { return dk >= 64 ? int(dk / 64) : 1; }
+
+// Workspace (float offsets). T counts steps here (tokens x n_h for DeltaProduct).
+//   rows [B*H][steps][4][dk]   a, b, alpha, q        cols [B*H][steps][2][dv]   w, do
+//   ck   [B*H][intervals][dk][dv]   S before the interval's first step
+//   gk   [B*H][intervals][dk][dv]   dL/dS after the interval's last step
+//   sub  [slots][kCB / kSub][NR * kCW / 4][64 lanes] float4   interval-kernel states
+//   part [slices][B*H][steps][4][dk]   dq, da, db, dalpha partials per slice
+//   dw   [B*H][steps][dv]
 struct BwdLayout {
-  int64_t slice_floats, part, dw, total;
+  int64_t rows, cols, ck, gk, sub, part, dw, total;
+  int64_t nck, items, slots;
 };
 
-// T counts steps here (tokens x n_h for DeltaProduct, whose rows are sub-steps).
 __host__ __device__ inline BwdLayout bwd_layout(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv) {
   BwdLayout L;
-  const int64_t nck = (T + kCB - 1) / kCB;
-  const int64_t ns = dv / 16;
+  const int64_t bh = B * H;
   const int64_t bth = B * T * H;
-  L.slice_floats = (nck + kCB) * dk * 16;
-  L.part = B * H * ns * L.slice_floats;
-  L.dw = L.part + ns * bth * 4 * dk;
+  L.nck = (T + kCB - 1) / kCB;
+  L.items = bh * (dv / kCW) * L.nck;
+  L.slots = L.items < kSlots ? L.items : kSlots;
+  L.rows = 0;
+  L.cols = L.rows + bth * 4 * dk;
+  L.ck = L.cols + bth * 2 * dv;
+  L.gk = L.ck + bh * L.nck * dk * dv;
+  L.sub = L.gk + bh * L.nck * dk * dv;
+  L.part = L.sub + L.slots * (kCB / kSub) * 64 * rows_per_lane(dk) * kCW;
+  L.dw = L.part + (dv / kCW) * bth * 4 * dk;
   L.total = L.dw + bth * dv;
+  if (L.total < 64) L.total = 64;  // a valid empty problem still reports a nonzero size
   return L;
 }
 
-// Sum over the 16 lanes of a row group (lanes j = 0..15 at fixed g) of NR values per
-// lane, by a butterfly that halves the value count at each exchange (transpose-
-// reduce). On return lane j holds sums for M = max(NR / 16, 1) rows, out[i] for
-// row i + M * (j * M * 16 / NR) ... expressed by row_of(j, i).
-template <int NR>
-struct RowReduce16 {
-  static constexpr int M = NR >= 16 ? NR / 16 : 1;
-  __device__ static __forceinline__ void run(float (&v)[NR], int j, float (&out)[M]) {
-    int n = NR;
-#pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) {
-      if (n >= 2) {
-        const bool hi = (j & m) != 0;
-#pragma unroll
-        for (int i = 0; i < NR / 2; ++i) {
-          if (i < n / 2) {
-            const float lo_v = v[i], hi_v = v[i + n / 2];
-            const float send = hi ? lo_v : hi_v;
-            const float keep = hi ? hi_v : lo_v;
-            v[i] = keep + __shfl_xor(send, m, 64);
-          }
-        }
-        n /= 2;
-      } else {
-        v[0] += __shfl_xor(v[0], m, 64);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < M; ++i) out[i] = v[i];
-  }
-  // row (within the group's NR rows) of out[i] in lane j
-  __device__ static __forceinline__ int row_of(int j, int i) {
-    if constexpr (NR >= 16) {
-      return j * M + i;
-    } else {
-      return j / (16 / NR);  // NR < 16: lanes j .. share the row j / (16 / NR)
-    }
-  }
-  // whether lane j writes its rows (one writer per row)
-  __device__ static __forceinline__ bool writer(int j) {
-    if constexpr (NR >= 16) return true;
-    else return j % (16 / NR) == 0;
-  }
-};
+// ---- wave reductions in the rows-on-lanes layout ------------------------------------
 
-// Kernel A: one wave per (batch*head, 16-column slice): forward with checkpoints,
-// then the reverse sweep; writes dw (column-complete) and the row partials.
-template <typename In, int DK>
-__global__ __launch_bounds__(64) void bwd_slice_kernel(Problem p, const In* __restrict__ d_o,
-                                                       const float* __restrict__ dsf, float* __restrict__ ds0,
-                                                       float* __restrict__ ws) {
-  constexpr int NR = DK / 4;
-  using RR = RowReduce16<NR>;
-  const int lane = threadIdx.x;
-  const int j = lane & 15, gr = lane >> 4;
-  const int64_t T = p.T, H = p.H, dv = p.dv;
-  const int ns = int(dv / 16);
-  const int64_t bh = blockIdx.x / ns;
-  const int wave = int(blockIdx.x % ns);  // column slice
-  const int64_t b = bh / H, h = bh % H;
-  const int col = wave * 16 + j;
-  const int row0 = gr * NR;
+// The value lane l ^ M holds (M < 16: DPP inside 16-lane rows).
+template <int M>
+__device__ __forceinline__ float lane_xor(float x) {
+  const int v = __float_as_int(x);
+  if constexpr (M == 1) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xb1, 0xf, 0xf, false));  // quad_perm 1,0,3,2
+  } else if constexpr (M == 2) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x4e, 0xf, 0xf, false));  // quad_perm 2,3,0,1
+  } else if constexpr (M == 4) {
+    // lanes 0-3 and 8-11 of a row (banks 0, 2) read lane + 4 (row_shl:4), lanes
+    // 4-7 and 12-15 (banks 1, 3) read lane - 4 (row_shr:4)
+    int r = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xf, 0x5, false);
+    r = __builtin_amdgcn_update_dpp(r, v, 0x114, 0xf, 0xa, false);
+    return __int_as_float(r);
+  } else {
+    static_assert(M == 8, "lane_xor: M is 1, 2, 4 or 8");
+    return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x128, 0xf, 0xf, false));  // row_ror:8
+  }
+}
+
+// x + (x of lane l ^ M), the same bits in both lanes of the pair.
+template <int M>
+__device__ __forceinline__ float pair_sum(float x) {
+  if constexpr (M == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  } else if constexpr (M == 32) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  } else {
+    return x + lane_xor<M>(x);
+  }
+}
+
+// One transposing level: a lane with bit M clear keeps the lower half of its n = CW / M
+// values and adds the partner's lower half; a lane with bit M set keeps the upper half.
+template <int M, int CW>
+__device__ __forceinline__ void transpose_level(float (&v)[CW], int lane) {
+  constexpr int n = CW / M;
+  const bool hi = (lane & M) != 0;
+#pragma unroll
+  for (int i = 0; i < n / 2; ++i) {
+    const float lo = v[i], up = v[i + n / 2];
+    const float keep = hi ? up : lo;
+    const float send = hi ? lo : up;
+    v[i] = keep + lane_xor<M>(send);
+  }
+}
+
+// Column sums over the 64 lanes of v[CW] (each lane's partials of CW columns).
+// Returns in lane l the total of column col_lane<CW>(l mod CW); v is consumed.
+template <int CW>
+__device__ __forceinline__ float col_sum(float (&v)[CW], int lane) {
+  static_assert(CW == 2 || CW == 4 || CW == 8 || CW == 16, "col_sum: CW is 2, 4, 8 or 16");
+  transpose_level<1, CW>(v, lane);
+  if constexpr (CW > 2) transpose_level<2, CW>(v, lane);
+  if constexpr (CW > 4) transpose_level<4, CW>(v, lane);
+  if constexpr (CW > 8) transpose_level<8, CW>(v, lane);
+  float x = v[0];
+  if constexpr (CW <= 2) x = pair_sum<2>(x);
+  if constexpr (CW <= 4) x = pair_sum<4>(x);
+  if constexpr (CW <= 8) x = pair_sum<8>(x);
+  x = pair_sum<16>(x);
+  return pair_sum<32>(x);
+}
+
+// Bit reversal over log2(CW) bits: the column whose total col_sum leaves in lane
+// l (l < CW), and, being an involution, the lane that holds column c.
+template <int CW>
+__host__ __device__ constexpr int col_lane(int c) {
+  int r = 0;
+  for (int b = 1, rb = CW / 2; b < CW; b <<= 1, rb >>= 1)
+    if (c & b) r |= rb;
+  return r;
+}
+
+__device__ __forceinline__ float bcast(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+// ---- 1. operand kernel -------------------------------------------------------------
+// One wave per (batch*head, step): rows a, b, alpha, q and columns w, do in float32.
+// q and do act after a token's last step (DeltaProduct: zero for the earlier steps),
+// the gate at its first.
+template <typename In>
+__global__ __launch_bounds__(256) void bwd_ops_kernel(Problem p, const In* __restrict__ d_o,
+                                                      float* __restrict__ ws) {
+  const int lane = threadIdx.x & 63;
+  const int64_t NS = p.steps, T = p.T, H = p.H, DK = p.dk, dv = p.dv;
   const int nh = p.n_h;
-  const int64_t NS = p.steps;  // steps: tokens x n_h
   const BwdLayout L = bwd_layout(p.B, NS, H, DK, dv);
-  float* wsl = ws + int64_t(blockIdx.x) * L.slice_floats;
-  const int64_t nck = (NS + kCB - 1) / kCB;
-  const int64_t bth = p.B * T * H * nh;  // step rows
-
+  const int64_t x = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);  // bh * NS + s
+  if (x >= p.B * H * NS) return;
+  const int64_t bh = x / NS, s = x % NS;
+  const int64_t b = bh / H, h = bh % H;
+  const int64_t t = s / nh;
+  const int sub = int(s - t * nh);
+  const int64_t th = (b * T + t) * H + h;  // token-head
+  const int64_t sr = th * nh + sub;        // step row ([B, T, H, n_h] for DeltaProduct)
+  const bool last = sub == nh - 1;
   const In* q = static_cast<const In*>(p.q);
   const In* k = static_cast<const In*>(p.k);
   const In* v = static_cast<const In*>(p.v);
@@ -122,249 +187,444 @@ __global__ __launch_bounds__(64) void bwd_slice_kernel(Problem p, const In* __re
   const In* bev = static_cast<const In*>(p.beta_v);
   const In* jv = static_cast<const In*>(p.j);
   const In* et = static_cast<const In*>(p.eta);
-  auto ld = [](const In* x) { return IO<In>::ld(x); };
-
-  // A token's inputs as loaded (raw 16- or 8-byte vectors and scalars), so that the
-  // next token's loads can be in flight while the current one is computed; finish()
-  // converts them into (a, b, alpha) rows, w of this lane's column, q rows and do.
-  using V4 = std::conditional_t<std::is_same<In, float>::value, float4, uint2>;
-  struct Raw {
-    V4 k[NR / 4], x[NR / 4], y[NR / 4], qv[NR / 4];
-    In s, vc, vb, dout;
-    bool first;  // DeltaProduct: the token's first step (the gate acts)
-  };
-  auto rows = [&](const In* base, V4 (&dst)[NR / 4]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < NR / 4; ++i) dst[i] = reinterpret_cast<const V4*>(base)[i];
-  };
-  auto cvt = [](const V4& x, float* o) __attribute__((always_inline)) {
-    if constexpr (std::is_same<In, float>::value) {
-      o[0] = x.x, o[1] = x.y, o[2] = x.z, o[3] = x.w;
-    } else {
-      o[0] = __uint_as_float(x.x << 16), o[1] = __uint_as_float(x.x & 0xffff0000u);
-      o[2] = __uint_as_float(x.y << 16), o[3] = __uint_as_float(x.y & 0xffff0000u);
-    }
-  };
-  auto load_raw = [&](int64_t vs, Raw& r, bool with_q) __attribute__((always_inline)) {
-    const int64_t t = vs / nh;
-    const int sub = int(vs - t * nh);
-    const int64_t th = (b * T + t) * H + h;
-    const int64_t sr = th * nh + sub;  // step row ([B, T, H, n_h] for DeltaProduct)
-    rows(k + sr * DK + row0, r.k);
-    r.vc = v[sr * dv + col];
-    r.first = sub == 0;
-    if (p.variant == GDN_VARIANT_DELTAPRODUCT) {
-      r.s = be[sr];
-      r.vb = al[th];
-      if (with_q) {
-        if (sub == nh - 1) {
-          rows(q + th * DK + row0, r.qv);
-          r.dout = d_o[th * dv + col];
-        } else {  // q is read after the last step only
-#pragma unroll
-          for (int i = 0; i < NR / 4; ++i) r.qv[i] = V4{};
-          r.dout = In(0);
-        }
-      }
-      return;
-    }
-    if (p.variant == GDN_VARIANT_ASYM) {
-      r.s = et[th];
-      rows(jv + th * DK + row0, r.y);
-      rows(al + th * DK + row0, r.x);
-    } else if (p.variant == GDN_VARIANT_FG2) {
-      rows(be + th * DK + row0, r.y);
-      rows(al + th * DK + row0, r.x);
-      r.vb = bev ? bev[th * dv + col] : be[th * DK + col];
-    } else {
-      r.s = be[th];
-      if (p.variant == GDN_VARIANT_KDA) rows(al + th * DK + row0, r.x);
-      else r.vb = al[th];
-    }
-    if (with_q) {
-      rows(q + th * DK + row0, r.qv);
-      r.dout = d_o[th * dv + col];
-    }
-  };
-  auto finish = [&](const Raw& r, float (&a)[NR], float (&bb)[NR], float (&alpha)[NR], float& w)
-      __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < NR / 4; ++i) cvt(r.k[i], a + 4 * i);
-    const float vc = ld(&r.vc);
-    if (p.variant == GDN_VARIANT_DELTAPRODUCT) {
-      const float bt = ld(&r.s);
-      const float gm = r.first ? ld(&r.vb) : 1.0f;
-#pragma unroll
-      for (int q2 = 0; q2 < NR; ++q2) {
-        bb[q2] = bt * a[q2];
-        alpha[q2] = gm;
-      }
-      w = bt * vc;
-    } else if (p.variant == GDN_VARIANT_ASYM) {
-      const float e = ld(&r.s);
-#pragma unroll
-      for (int i = 0; i < NR / 4; ++i) {
-        cvt(r.y[i], bb + 4 * i);
-        cvt(r.x[i], alpha + 4 * i);
-      }
-#pragma unroll
-      for (int q2 = 0; q2 < NR; ++q2) bb[q2] *= e;
-      w = e * vc;
-    } else if (p.variant == GDN_VARIANT_FG2) {
-      float beta[NR];
-#pragma unroll
-      for (int i = 0; i < NR / 4; ++i) {
-        cvt(r.y[i], beta + 4 * i);
-        cvt(r.x[i], alpha + 4 * i);
-      }
-#pragma unroll
-      for (int q2 = 0; q2 < NR; ++q2) {
-        a[q2] *= sqrtf(beta[q2]);
-        bb[q2] = a[q2];
-      }
-      w = vc * sqrtf(ld(&r.vb));
-    } else {
-      const float sb = sqrtf(ld(&r.s));
-#pragma unroll
-      for (int q2 = 0; q2 < NR; ++q2) {
-        a[q2] *= sb;
-        bb[q2] = a[q2];
-      }
-      if (p.variant == GDN_VARIANT_KDA) {
-#pragma unroll
-        for (int i = 0; i < NR / 4; ++i) cvt(r.x[i], alpha + 4 * i);
-      } else {
-        const float gm = ld(&r.vb);
-#pragma unroll
-        for (int q2 = 0; q2 < NR; ++q2) alpha[q2] = gm;
-      }
-      w = sb * vc;
-    }
-  };
-  // slice state of one step in lane order: 16-byte vectors, coalesced
-  auto save = [&](float* base, const float (&S)[NR]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < NR / 4; ++i)
-      reinterpret_cast<float4*>(base)[i * 64 + lane] = make_float4(S[4 * i], S[4 * i + 1], S[4 * i + 2], S[4 * i + 3]);
-  };
-  auto restore = [&](const float* base, float (&S)[NR]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < NR / 4; ++i) {
-      const float4 x = reinterpret_cast<const float4*>(base)[i * 64 + lane];
-      S[4 * i] = x.x, S[4 * i + 1] = x.y, S[4 * i + 2] = x.z, S[4 * i + 3] = x.w;
-    }
-  };
-  auto fwd = [&](float (&S)[NR], const Raw& raw) __attribute__((always_inline)) {
-    float a[NR], bb[NR], alpha[NR], w;
-    finish(raw, a, bb, alpha, w);
-    float bx = 0.0f;
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      S[r] *= alpha[r];
-      bx += bb[r] * S[r];
-    }
-    const float u = w - sum_over_groups(bx);
-#pragma unroll
-    for (int r = 0; r < NR; ++r) S[r] += a[r] * u;
-  };
-
-  float* ck = wsl;                  // [nck][DK * 16]
-  float* cs = wsl + nck * DK * 16;  // [kCB][DK * 16]
-  float S[NR];
-  const size_t sbase = size_t(bh) * DK * size_t(dv);
-#pragma unroll
-  for (int r = 0; r < NR; ++r) S[r] = p.s0 ? p.s0[sbase + size_t(row0 + r) * dv + col] : 0.0f;
-  Raw cur, nxt;
-  if (NS > 0) load_raw(0, cur, false);
-  nxt = cur;
-  for (int64_t t = 0; t < NS; ++t) {
-    if (t + 1 < NS) load_raw(t + 1, nxt, false);  // in flight during this step
-    if (t % kCB == 0) save(ck + (t / kCB) * DK * 16, S);
-    fwd(S, cur);
-    cur = nxt;
+  auto ld = [](const In* y) { return IO<In>::ld(y); };
+  float* rw = ws + L.rows + x * 4 * DK;
+  float* cl = ws + L.cols + x * 2 * dv;
+  const int var = p.variant;
+  // per-step scalars
+  float sc = 0.0f, gate = 1.0f;
+  if (var == GDN_VARIANT_DELTAPRODUCT) {
+    sc = ld(be + sr);
+    gate = sub == 0 ? ld(al + th) : 1.0f;
+  } else if (var == GDN_VARIANT_ASYM) {
+    sc = ld(et + th);
+  } else if (var == GDN_VARIANT_KDA || var == GDN_VARIANT_GDN) {
+    sc = sqrtf(ld(be + th));
+    if (var == GDN_VARIANT_GDN) gate = ld(al + th);
   }
-
-  float G[NR];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) G[r] = dsf ? dsf[sbase + size_t(row0 + r) * dv + col] : 0.0f;
-  float* part = ws + L.part;
-  float* dwg = ws + L.dw;
-  for (int64_t c = nck - 1; c >= 0; --c) {
-    const int64_t t0 = c * kCB, t1 = min(NS, t0 + kCB);
-    restore(ck + c * DK * 16, S);
-    load_raw(t0, cur, false);
-    nxt = cur;
-    for (int64_t t = t0; t < t1; ++t) {  // the states before each token of the chunk
-      if (t + 1 < t1) load_raw(t + 1, nxt, false);
-      save(cs + (t - t0) * DK * 16, S);
-      fwd(S, cur);
-      cur = nxt;
+  for (int64_t e = lane; e < DK; e += 64) {
+    const float kr = ld(k + sr * DK + e);
+    float a, bb, alpha;
+    if (var == GDN_VARIANT_DELTAPRODUCT) {
+      a = kr, bb = sc * kr, alpha = gate;
+    } else if (var == GDN_VARIANT_ASYM) {
+      a = kr, bb = ld(jv + th * DK + e) * sc, alpha = ld(al + th * DK + e);
+    } else if (var == GDN_VARIANT_FG2) {
+      a = kr * sqrtf(ld(be + th * DK + e)), bb = a, alpha = ld(al + th * DK + e);
+    } else {
+      a = kr * sc, bb = a, alpha = var == GDN_VARIANT_KDA ? ld(al + th * DK + e) : gate;
     }
-    load_raw(t1 - 1, cur, true);
-    nxt = cur;
-    for (int64_t t = t1 - 1; t >= t0; --t) {
-      if (t > t0) load_raw(t - 1, nxt, true);  // in flight during this token
-      float a[NR], bb[NR], alpha[NR], w, qv[NR];
-      finish(cur, a, bb, alpha, w);
-      const int64_t th = ((b * T + t / nh) * H + h) * nh + t % nh;  // step row
-#pragma unroll
-      for (int i = 0; i < NR / 4; ++i) cvt(cur.qv[i], qv + 4 * i);
-      const float doc = ld(&cur.dout);
-      float Sp[NR], X[NR];
-      restore(cs + (t - t0) * DK * 16, Sp);
-      float bx = 0.0f;
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        X[r] = alpha[r] * Sp[r];
-        bx += bb[r] * X[r];
-      }
-      const float u = w - sum_over_groups(bx);
-      float dq[NR], da[NR], db[NR], dal[NR];
-      float gw = 0.0f;
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        dq[r] = (X[r] + a[r] * u) * doc;  // S_t do, this column's term
-        G[r] += qv[r] * doc;
-        gw += G[r] * a[r];
-      }
-      const float dw = sum_over_groups(gw);
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        da[r] = G[r] * u;
-        db[r] = -X[r] * dw;
-        const float dX = G[r] - bb[r] * dw;
-        dal[r] = dX * Sp[r];
-        G[r] = alpha[r] * dX;
-      }
-      if (gr == 0) dwg[th * dv + col] = dw;
-      float* pw = part + (int64_t(wave) * bth + th) * 4 * DK;
-      float o4[4][RR::M];
-      RR::run(dq, j, o4[0]);
-      RR::run(da, j, o4[1]);
-      RR::run(db, j, o4[2]);
-      RR::run(dal, j, o4[3]);
-      if (RR::writer(j)) {
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd)
-#pragma unroll
-          for (int i = 0; i < RR::M; ++i) pw[qd * DK + row0 + RR::row_of(j, i)] = o4[qd][i];
-      }
-      cur = nxt;
-    }
+    rw[e] = a;
+    rw[DK + e] = bb;
+    rw[2 * DK + e] = alpha;
+    rw[3 * DK + e] = last ? ld(q + th * DK + e) : 0.0f;
   }
-  if (ds0) {
-#pragma unroll
-    for (int r = 0; r < NR; ++r) ds0[sbase + size_t(row0 + r) * dv + col] = G[r];
+  for (int64_t c = lane; c < dv; c += 64) {
+    const float vc = ld(v + sr * dv + c);
+    float w;
+    if (var == GDN_VARIANT_FG2) w = vc * sqrtf(ld(bev ? bev + th * dv + c : be + th * DK + c));
+    else w = sc * vc;
+    cl[c] = w;
+    cl[dv + c] = last ? ld(d_o + th * dv + c) : 0.0f;
   }
 }
 
-// Kernel B: one wave per token-head: the partials summed over the slices in order,
-// then the variant's chain rule.
+// One step's operands in the rows-on-lanes layout: this lane's rows of a, b, alpha
+// (and q), and one column value (w or do of column col_lane(l mod CW)).
+template <int NR>
+struct Op {
+  float a[NR], b[NR], al[NR], q[NR];
+  float w, d;
+};
+
+// Inactive lanes (rows past dk) read row 0 and keep zeros.
+template <int NR, bool WQ, bool WW, bool WD>
+__device__ __forceinline__ void load_op(const float* rows, const float* cols, int64_t s, int64_t DK,
+                                        int64_t dv, int r0, bool act, int col, Op<NR>& o) {
+  const float* rw = rows + s * 4 * DK + (act ? r0 : 0);
+  float a[NR], b[NR], al[NR], q[NR];
+  if constexpr (NR == 2) {
+    const float2 x = *reinterpret_cast<const float2*>(rw);
+    const float2 y = *reinterpret_cast<const float2*>(rw + DK);
+    const float2 z = *reinterpret_cast<const float2*>(rw + 2 * DK);
+    a[0] = x.x, a[1] = x.y, b[0] = y.x, b[1] = y.y, al[0] = z.x, al[1] = z.y;
+    if constexpr (WQ) {
+      const float2 w = *reinterpret_cast<const float2*>(rw + 3 * DK);
+      q[0] = w.x, q[1] = w.y;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      a[r] = rw[r], b[r] = rw[DK + r], al[r] = rw[2 * DK + r];
+      if constexpr (WQ) q[r] = rw[3 * DK + r];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    o.a[r] = act ? a[r] : 0.0f;
+    o.b[r] = act ? b[r] : 0.0f;
+    o.al[r] = act ? al[r] : 0.0f;
+    o.q[r] = WQ && act ? q[r] : 0.0f;
+  }
+  const float* cl = cols + s * 2 * dv + col;
+  o.w = WW ? cl[0] : 0.0f;
+  o.d = WD ? cl[dv] : 0.0f;
+}
+
+// S <- X + a u^T with X = Diag(alpha) S, u = w - X^T b (a forward step). Returns u of
+// column col_lane(l mod CW).
+template <int NR, int CW>
+__device__ __forceinline__ float fwd_step(float (&S)[NR][CW], const Op<NR>& o, int lane) {
+  float part[CW];
+#pragma unroll
+  for (int c = 0; c < CW; ++c) part[c] = 0.0f;
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int c = 0; c < CW; ++c) {
+      S[r][c] *= o.al[r];
+      part[c] += o.b[r] * S[r][c];
+    }
+  const float u = o.w - col_sum<CW>(part, lane);
+#pragma unroll
+  for (int c = 0; c < CW; ++c) {
+    const float uc = bcast(u, col_lane<CW>(c));
+#pragma unroll
+    for (int r = 0; r < NR; ++r) S[r][c] += o.a[r] * uc;
+  }
+  return u;
+}
+
+// G <- Diag(alpha) (G' - b dw^T), G' = G + q do^T, dw = G'^T a (a backward step of the
+// state gradient alone).
+template <int NR, int CW>
+__device__ __forceinline__ void grad_step(float (&G)[NR][CW], const Op<NR>& o, int lane) {
+  float part[CW];
+#pragma unroll
+  for (int c = 0; c < CW; ++c) {
+    const float dc = bcast(o.d, col_lane<CW>(c));
+    part[c] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      G[r][c] += o.q[r] * dc;
+      part[c] += G[r][c] * o.a[r];
+    }
+  }
+  const float dw = col_sum<CW>(part, lane);
+#pragma unroll
+  for (int c = 0; c < CW; ++c) {
+    const float dwc = bcast(dw, col_lane<CW>(c));
+#pragma unroll
+    for (int r = 0; r < NR; ++r) G[r][c] = o.al[r] * (G[r][c] - o.b[r] * dwc);
+  }
+}
+
+// ---- 2. chain kernel ----------------------------------------------------------------
+// Four waves per workgroup, one per CW-column slice; the first B*H*dv/CW waves run S
+// forward from s0, the rest run the state gradient backward from dL/dS_T.
+template <int DK, int CW>
+__global__ __launch_bounds__(256) void bwd_chain_kernel(Problem p, const float* __restrict__ dsf,
+                                                        float* __restrict__ ds0, float* __restrict__ ws) {
+  constexpr int NR = rows_per_lane(DK);
+  constexpr int D = kChainRing;
+  const int lane = threadIdx.x & 63;
+  const int64_t NS = p.steps, H = p.H, dv = p.dv;
+  const BwdLayout L = bwd_layout(p.B, NS, H, DK, dv);
+  const int ncs = int(dv / CW);
+  const int64_t nw = p.B * H * ncs;  // waves per chain
+  const int64_t wid = int64_t(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool grad = wid >= nw;
+  const int64_t w2 = grad ? wid - nw : wid;
+  const int64_t bh = w2 / ncs;
+  const int cbase = int(w2 % ncs) * CW;
+  const int r0 = lane * NR;
+  const bool act = DK >= 64 || r0 < DK;
+  const int col = cbase + col_lane<CW>(lane & (CW - 1));
+  const float* rows = ws + L.rows + bh * NS * 4 * DK;
+  const float* cols = ws + L.cols + bh * NS * 2 * dv;
+  const size_t sbase = size_t(bh) * DK * size_t(dv);
+  float* ckp = ws + (grad ? L.gk : L.ck) + bh * L.nck * DK * dv;
+  const float* init = grad ? dsf : p.s0;
+
+  float X[NR][CW];
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int c = 0; c < CW; ++c)
+      X[r][c] = (act && init) ? init[sbase + size_t(r0 + r) * dv + cbase + c] : 0.0f;
+  auto store = [&](float* dst) __attribute__((always_inline)) {
+    if (!act) return;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      float* d = dst + size_t(r0 + r) * dv + cbase;
+      if constexpr (CW % 4 == 0) {
+#pragma unroll
+        for (int c = 0; c < CW; c += 4)
+          *reinterpret_cast<float4*>(d + c) = make_float4(X[r][c], X[r][c + 1], X[r][c + 2], X[r][c + 3]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < CW; ++c) d[c] = X[r][c];
+      }
+    }
+  };
+
+  // Operands of the next D steps stay in flight in a register ring. The steady state
+  // runs whole groups of D steps aligned to multiples of D (kCB is one), so its loads
+  // are unconditional and each step waits only for its own slot; the ragged end
+  // (fewer than D steps) runs separately.
+  static_assert(kCB % D == 0, "checkpoint interval is a multiple of the ring depth");
+  if (NS == 0) {  // nothing to run: dL/dS_0 is dL/dS_T
+    if (grad && ds0) store(ds0 + sbase);
+    return;
+  }
+  Op<NR> ring[D];
+  const int64_t nfull = NS / D;  // whole groups [D g, D g + D)
+  const int64_t tail0 = nfull * D;
+  if (!grad) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {  // in slot order, as the loop refills them
+      load_op<NR, false, true, false>(rows, cols, min<int64_t>(i, NS - 1), DK, dv, r0, act, col, ring[i]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int64_t g = 0; g < nfull; ++g) {
+      const int64_t s0 = g * D;
+      if (s0 % kCB == 0) store(ckp + (s0 / kCB) * DK * dv);
+#pragma unroll
+      for (int i = 0; i < D; ++i) {
+        fwd_step<NR, CW>(X, ring[i], lane);
+        load_op<NR, false, true, false>(rows, cols, min<int64_t>(s0 + D + i, NS - 1), DK, dv, r0, act, col, ring[i]);
+        __builtin_amdgcn_sched_barrier(0);  // keep the refill here, D steps ahead of its use
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < D; ++i) {  // the ring holds steps tail0 .. tail0 + D - 1
+      const int64_t s = tail0 + i;
+      if (s < NS) {
+        if (s % kCB == 0) store(ckp + (s / kCB) * DK * dv);
+        fwd_step<NR, CW>(X, ring[i], lane);
+      }
+    }
+    return;
+  }
+  // the ragged end first (steps NS - 1 down to tail0), loading as it goes
+  for (int64_t s = NS - 1; s >= tail0; --s) {
+    Op<NR> o;
+    load_op<NR, true, false, true>(rows, cols, s, DK, dv, r0, act, col, o);
+    if (s == NS - 1 || (s + 1) % kCB == 0) store(ckp + (s / kCB) * DK * dv);
+    grad_step<NR, CW>(X, o, lane);
+  }
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    load_op<NR, true, false, true>(rows, cols, max<int64_t>(tail0 - 1 - i, 0), DK, dv, r0, act, col, ring[i]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int64_t g = nfull - 1; g >= 0; --g) {
+    const int64_t s0 = g * D + D - 1;  // an interval's last step can only be a group's first
+    if (s0 == NS - 1 || (s0 + 1) % kCB == 0) store(ckp + (s0 / kCB) * DK * dv);
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      grad_step<NR, CW>(X, ring[i], lane);
+      load_op<NR, true, false, true>(rows, cols, max<int64_t>(s0 - D - i, 0), DK, dv, r0, act, col, ring[i]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if (ds0) store(ds0 + sbase);
+}
+
+// ---- 3. interval kernel -------------------------------------------------------------
+// One wave per workgroup, persistent over the items (batch*head, interval, 16-column
+// slice). Pass A runs the interval forward from its stored S and keeps the state
+// before every kSub-step block in this workgroup's slot; pass B takes the blocks in
+// reverse: it recomputes the block's kSub states into registers and walks them back.
+template <int DK>
+__global__ __launch_bounds__(64) void bwd_interval_kernel(Problem p, float* __restrict__ ws) {
+  constexpr int NR = rows_per_lane(DK);
+  constexpr int CW = kCW;
+  constexpr int NV = NR * CW / 4;  // float4 per lane of a state
+  const int lane = threadIdx.x;
+  const int64_t NS = p.steps, H = p.H, dv = p.dv;
+  const int ns = int(dv / CW);
+  const BwdLayout L = bwd_layout(p.B, NS, H, DK, dv);
+  const int64_t bth = p.B * NS * H;  // step rows
+  const int r0 = lane * NR;
+  const bool act = DK >= 64 || r0 < DK;
+  const int lc = col_lane<CW>(lane & (CW - 1));
+  float4* slot = reinterpret_cast<float4*>(ws + L.sub) + int64_t(blockIdx.x) * (kCB / kSub) * NV * 64;
+  __shared__ float4 sts[kSub * NV * 64];  // states of the current block, lane order
+  float* part = ws + L.part;
+  float* dwg = ws + L.dw;
+
+  using St = float[NR][CW];
+  auto save = [&](float4* dst, const St& S) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int r = (4 * i) / CW, c = (4 * i) % CW;
+      dst[i * 64 + lane] = make_float4(S[r][c], S[r][c + 1], S[r][c + 2], S[r][c + 3]);
+    }
+  };
+  auto restore = [&](const float4* src, St& S) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int r = (4 * i) / CW, c = (4 * i) % CW;
+      const float4 x = src[i * 64 + lane];
+      S[r][c] = x.x, S[r][c + 1] = x.y, S[r][c + 2] = x.z, S[r][c + 3] = x.w;
+    }
+  };
+
+  for (int64_t item = blockIdx.x; item < L.items; item += gridDim.x) {
+    const int slice = int(item % ns);
+    const int64_t rest = item / ns;
+    const int64_t ci = rest % L.nck, bh = rest / L.nck;
+    const int cbase = slice * CW;
+    const int64_t t0 = ci * kCB, t1 = min(NS, t0 + kCB);
+    const int nb = int((t1 - t0 + kSub - 1) / kSub);
+    const float* rows = ws + L.rows + bh * NS * 4 * DK;
+    const float* cols = ws + L.cols + bh * NS * 2 * dv;
+    auto load_blk = [&](int m, Op<NR> (&o)[kSub]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < kSub; ++i) {
+        // past the interval's end: a valid step's operands, never used
+        const int64_t s = min(t0 + int64_t(m) * kSub + i, t1 - 1);
+        load_op<NR, true, true, true>(rows, cols, s, DK, dv, r0, act, cbase + lc, o[i]);
+      }
+    };
+
+    float S[NR][CW], G[NR][CW];
+    {
+      const float* sck = ws + L.ck + (bh * L.nck + ci) * DK * dv + cbase;
+      const float* gck = ws + L.gk + (bh * L.nck + ci) * DK * dv + cbase;
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int c = 0; c < CW; c += 4) {
+          const float4 x = act ? *reinterpret_cast<const float4*>(sck + size_t(r0 + r) * dv + c) : float4{};
+          const float4 y = act ? *reinterpret_cast<const float4*>(gck + size_t(r0 + r) * dv + c) : float4{};
+          S[r][c] = x.x, S[r][c + 1] = x.y, S[r][c + 2] = x.z, S[r][c + 3] = x.w;
+          G[r][c] = y.x, G[r][c + 1] = y.y, G[r][c + 2] = y.z, G[r][c + 3] = y.w;
+        }
+    }
+
+    // pass A: blocks 0 .. nb-2 forward, the state before each kept in the slot; S
+    // ends as the state before block nb-1, and cur holds that block's operands
+    Op<NR> cur[kSub], nxt[kSub];
+    load_blk(0, cur);
+    for (int m = 0; m + 1 < nb; ++m) {
+      load_blk(m + 1, nxt);
+      save(slot + int64_t(m) * NV * 64, S);
+#pragma unroll
+      for (int i = 0; i < kSub; ++i) fwd_step<NR, CW>(S, cur[i], lane);  // full block (m < nb - 1)
+#pragma unroll
+      for (int i = 0; i < kSub; ++i) cur[i] = nxt[i];
+    }
+
+    // pass B: blocks in reverse; the last one (possibly short) first, so that the
+    // loop over whole blocks has no conditional memory operation (each block waits
+    // only for its own prefetched operands)
+    auto run_block = [&](const int m, auto whole) __attribute__((always_inline)) {
+      constexpr bool W = decltype(whole)::value;
+      const int mp = m > 0 ? m - 1 : 0;  // prefetch (block 0 again at the end: unused)
+      load_blk(mp, nxt);
+      float Sn[NR][CW];
+      restore(slot + int64_t(mp) * NV * 64, Sn);
+      const int64_t sb = t0 + int64_t(m) * kSub;
+      const int n = W ? kSub : int(min<int64_t>(kSub, t1 - sb));
+      // the state before each step of the block, in this wave's LDS, and each step's u
+      // (this lane's column); the block's last step runs too, for its u
+      float ul[kSub];
+#pragma unroll
+      for (int i = 0; i < kSub; ++i) {
+        save(sts + i * NV * 64, S);
+        ul[i] = (W || i < n) ? fwd_step<NR, CW>(S, cur[i], lane) : 0.0f;
+      }
+      auto back = [&](const int i) __attribute__((always_inline)) {
+        const Op<NR>& o = cur[i];
+        float Sp[NR][CW];
+        restore(sts + i * NV * 64, Sp);
+        const int64_t s = sb + i;
+        float X[NR][CW];
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+          for (int c = 0; c < CW; ++c) X[r][c] = o.al[r] * Sp[r][c];
+        float u = ul[i];
+        // u^T do over the slice's columns (lanes 0..15 of every row hold distinct ones)
+        float udo = u * o.d;
+        udo = pair_sum<1>(udo);
+        udo = pair_sum<2>(udo);
+        udo = pair_sum<4>(udo);
+        udo = pair_sum<8>(udo);
+        // dq = S_t do = X do + a (u^T do); G += q do^T; dw = G^T a
+        float dq[NR], gw[CW];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) dq[r] = o.a[r] * udo;
+#pragma unroll
+        for (int c = 0; c < CW; ++c) {
+          const float dc = bcast(o.d, col_lane<CW>(c));
+          gw[c] = 0.0f;
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            dq[r] += X[r][c] * dc;
+            G[r][c] += o.q[r] * dc;
+            gw[c] += G[r][c] * o.a[r];
+          }
+        }
+        const float dw = col_sum<CW>(gw, lane);
+        asm volatile("" : "+v"(u));  // broadcast u here, after the reduction
+        // da = G u; db = -X dw; dX = G - b dw^T; dalpha = rowsum(dX . S_{t-1}); G = Diag(alpha) dX
+        float da[NR], db[NR], dal[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) da[r] = db[r] = dal[r] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CW; ++c) {
+          const float uc = bcast(u, col_lane<CW>(c));
+          const float dwc = bcast(dw, col_lane<CW>(c));
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            da[r] += G[r][c] * uc;
+            db[r] -= X[r][c] * dwc;
+            const float dX = G[r][c] - o.b[r] * dwc;
+            dal[r] += dX * Sp[r][c];
+            G[r][c] = o.al[r] * dX;
+          }
+        }
+        const int64_t pr = bh * NS + s;  // this head's step s
+        if (lane < CW) dwg[pr * dv + cbase + lc] = dw;
+        if (act) {
+          float* pw = part + (int64_t(slice) * bth + pr) * 4 * DK + r0;
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            pw[r] = dq[r];
+            pw[DK + r] = da[r];
+            pw[2 * DK + r] = db[r];
+            pw[3 * DK + r] = dal[r];
+          }
+        }
+      };
+      static_assert(kSub == 4, "the reverse walk below is written out for four steps");
+      if (W || n > 3) back(3);
+      if (W || n > 2) back(2);
+      if (W || n > 1) back(1);
+      back(0);
+#pragma unroll
+      for (int i = 0; i < kSub; ++i) cur[i] = nxt[i];
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int c = 0; c < CW; ++c) S[r][c] = Sn[r][c];
+    };
+    run_block(nb - 1, std::false_type{});
+    for (int m = nb - 2; m >= 0; --m) run_block(m, std::true_type{});
+  }
+}
+
+// ---- 4. reduce kernel -------------------------------------------------------------
+// One wave per step row: the partials summed over the slices in order, then the
+// variant's chain rule.
 template <typename In, int DK>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(Problem p, GradPtrs g, const float* __restrict__ ws) {
   const int lane = threadIdx.x & 63;
   const int64_t T = p.T, H = p.H, dv = p.dv;
-  const int ns = int(dv / 16);
+  const int ns = int(dv / kCW);
   const int nh = p.n_h;
   const int64_t bth = p.B * T * H * nh;  // step rows
   const BwdLayout L = bwd_layout(p.B, p.steps, H, DK, dv);
@@ -379,15 +639,18 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(Problem p, GradPtrs g, 
   auto ld = [](const In* x) { return IO<In>::ld(x); };
   const int64_t stride = int64_t(gridDim.x) * (blockDim.x / 64);
   for (int64_t th = int64_t(blockIdx.x) * (blockDim.x / 64) + (threadIdx.x >> 6); th < bth; th += stride) {
+    // the partials of step row th = ((b T + t) H + h) n_h + sub sit at head b H + h, step t n_h + sub
+    const int64_t tok = th / nh;
+    const int64_t bt = tok / H;
+    const int64_t prow = ((bt / T) * H + tok % H) * p.steps + (bt % T) * nh + (th - tok * nh);
     if (p.variant == GDN_VARIANT_DELTAPRODUCT) {  // th is a step row (token x n_h + step)
-      const int64_t tok = th / nh;
       const int sub = int(th - tok * nh);
       const float bt = ld(be + th);
       float sb = 0.0f, sal = 0.0f;
       for (int r = lane; r < DK; r += 64) {
         float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int w2 = 0; w2 < ns; ++w2) {
-          const float* pr = part + (int64_t(w2) * bth + th) * 4 * DK;
+          const float* pr = part + (int64_t(w2) * bth + prow) * 4 * DK;
 #pragma unroll
           for (int qd = 0; qd < 4; ++qd) s4[qd] += pr[qd * DK + r];
         }
@@ -397,7 +660,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(Problem p, GradPtrs g, 
         if (sub == nh - 1) g.dq[tok * DK + r] = s4[0];
       }
       for (int cc = lane; cc < dv; cc += 64) {
-        const float dw = dwg[th * dv + cc];
+        const float dw = dwg[prow * dv + cc];
         g.dv[th * dv + cc] = bt * dw;
         sb += ld(v + th * dv + cc) * dw;
       }
@@ -415,7 +678,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(Problem p, GradPtrs g, 
     for (int r = lane; r < DK; r += 64) {
       float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       for (int w2 = 0; w2 < ns; ++w2) {
-        const float* pr = part + (int64_t(w2) * bth + th) * 4 * DK;
+        const float* pr = part + (int64_t(w2) * bth + prow) * 4 * DK;
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) s4[qd] += pr[qd * DK + r];
       }
@@ -428,7 +691,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(Problem p, GradPtrs g, 
         g.dk[ir] = s * dab;
         g.dalpha[ir] = dal;
         float db = kr * dab;
-        if (!bev) db += ld(v + th * dv + r) * dwg[th * dv + r];  // shared beta (dk == dv)
+        if (!bev) db += ld(v + th * dv + r) * dwg[prow * dv + r];  // shared beta (dk == dv)
         g.dbeta[ir] = db / (2.0f * s);
       } else if (p.variant == GDN_VARIANT_ASYM) {
         g.dk[ir] = s4[1];
@@ -443,7 +706,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(Problem p, GradPtrs g, 
       }
     }
     for (int cc = lane; cc < dv; cc += 64) {
-      const float dw = dwg[th * dv + cc];
+      const float dw = dwg[prow * dv + cc];
       const int64_t ic = th * dv + cc;
       const float vc = ld(v + ic);
       if (p.variant == GDN_VARIANT_FG2) {
@@ -478,10 +741,22 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(Problem p, GradPtrs g, 
 
 template <typename In, int DK>
 int launch_dk(const Problem& p, const In* dO, const float* dsf, const GradPtrs& g, float* ws, hipStream_t s) {
-  const unsigned slices = unsigned(p.B * p.H * (p.dv / 16));
-  bwd_slice_kernel<In, DK><<<dim3(slices), dim3(64), 0, s>>>(p, dO, dsf, g.ds0, ws);
+  const BwdLayout L = bwd_layout(p.B, p.steps, p.H, DK, p.dv);
+  const int64_t nsteps = p.B * p.H * p.steps;
+  if (nsteps > 0) {
+    bwd_ops_kernel<In><<<dim3(unsigned((nsteps + 3) / 4)), dim3(256), 0, s>>>(p, dO, ws);
+    int e = int(hipGetLastError());
+    if (e != 0) return e;
+  }
+  // dv / kChainCW is a multiple of 4: whole workgroups, and the S and G halves split
+  // between workgroups
+  const int64_t chain_waves = 2 * p.B * p.H * (p.dv / kChainCW);
+  bwd_chain_kernel<DK, kChainCW><<<dim3(unsigned(chain_waves / 4)), dim3(256), 0, s>>>(p, dsf, g.ds0, ws);
   int e = int(hipGetLastError());
-  if (e != 0 || p.T == 0) return e;
+  if (e != 0 || nsteps == 0) return e;
+  bwd_interval_kernel<DK><<<dim3(unsigned(L.slots)), dim3(64), 0, s>>>(p, ws);
+  e = int(hipGetLastError());
+  if (e != 0) return e;
   const int64_t waves = p.B * p.T * p.H * p.n_h;
   const int64_t blocks = (waves + 3) / 4;
   bwd_reduce_kernel<In, DK><<<dim3(unsigned(blocks < (int64_t(1) << 20) ? blocks : (int64_t(1) << 20))), dim3(256), 0, s>>>(p, g, ws);

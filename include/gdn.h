@@ -221,10 +221,13 @@ typedef struct gdn_grads {
   float* ds0;
 } gdn_grads;
 
-/* Bytes of device workspace gdn_recurrent_bwd needs (0 for an invalid set):
- * about dk * dv bytes per token (or sub-step) and head for the per-column-slice
- * partial row gradients, plus the 64-token state checkpoints; 16 KiB per token and
- * head at dk = dv = 128 (1.24 GB for 4,096 tokens x 16 heads). */
+/* Bytes of device workspace gdn_recurrent_bwd needs (0 for an invalid set). Per
+ * token (or sub-step) and head: the float32 step operands (4 dk + 2 dv floats), the
+ * per-16-column-slice partial row gradients (dv / 16 x 4 dk floats), dw (dv floats)
+ * and the state and state-gradient checkpoints (2 dk dv floats every 64 steps); plus
+ * a fixed part of at most 1,024 x 16 x dk x 16 floats (128 MiB at dk = 128) for the
+ * per-workgroup state slots. 21.5 KiB per token and head at dk = dv = 128: 1.58 GB
+ * for 4,096 tokens x 16 heads. */
 size_t gdn_bwd_workspace_bytes(const gdn_args* args);
 
 /* Backward pass (reverse-mode gradients) of the token recurrence for every variant
@@ -237,7 +240,9 @@ size_t gdn_bwd_workspace_bytes(const gdn_args* args);
  * dL/do; d_s_final [B, H, dk, dv] float32 is dL/dS_T (NULL: zero). Gradients with
  * respect to beta and beta_v are singular at 0 (their square roots enter the step).
  * ws must hold gdn_bwd_workspace_bytes(args) bytes, 256-byte aligned. The forward
- * states are recomputed from checkpoints every 64 tokens; results are deterministic. */
+ * states are recomputed from checkpoints every 64 steps, the state gradient starts
+ * from checkpoints taken on its own backward sweep, so the 64-step intervals run in
+ * parallel; every sum has a fixed order and results are deterministic. */
 int gdn_recurrent_bwd(const gdn_args* args, const void* d_o, const float* d_s_final,
                       const gdn_grads* grads, void* ws, size_t ws_bytes, void* stream);
 
