@@ -43,11 +43,14 @@ constexpr int kCW = 16;        // columns of an interval-kernel wave (a row-part
 constexpr int kChainCW = 4;    // columns of a chain-kernel wave
 constexpr int kChainRing = 16; // steps of operands a chain wave keeps in flight
 constexpr int kSlots = 1024;   // interval-kernel workgroups, each with a scratch slot
+constexpr int kPad = kChainRing;  // operand padding (steps) before and after a sequence
+static_assert(kSub <= kPad, "an interval block reads at most kSub - 1 steps past the end");
 
 __host__ __device__ constexpr int rows_per_lane(int64_t dk) { return dk >= 64 ? int(dk / 64) : 1; }
 
 // Workspace (float offsets). T counts steps here (tokens x n_h for DeltaProduct).
-//   rows [B*H][steps][4][dk]   a, b, alpha, q        cols [B*H][steps][2][dv]   w, do
+//   rows [B*H][kPad + steps + kPad][4][dk]   a, b, alpha, q      (kPad steps of padding on
+//   cols [B*H][kPad + steps + kPad][2][dv]   w, do                both sides, never used)
 //   ck   [B*H][intervals][dk][dv]   S before the interval's first step
 //   gk   [B*H][intervals][dk][dv]   dL/dS after the interval's last step
 //   sub  [slots][kCB / kSub][NR * kCW / 4][64 lanes] float4   interval-kernel states
@@ -65,9 +68,10 @@ __host__ __device__ inline BwdLayout bwd_layout(int64_t B, int64_t T, int64_t H,
   L.nck = (T + kCB - 1) / kCB;
   L.items = bh * (dv / kCW) * L.nck;
   L.slots = L.items < kSlots ? L.items : kSlots;
+  const int64_t bsp = bh * (T + 2 * kPad);  // padded steps
   L.rows = 0;
-  L.cols = L.rows + bth * 4 * dk;
-  L.ck = L.cols + bth * 2 * dv;
+  L.cols = L.rows + bsp * 4 * dk;
+  L.ck = L.cols + bsp * 2 * dv;
   L.gk = L.ck + bh * L.nck * dk * dv;
   L.sub = L.gk + bh * L.nck * dk * dv;
   L.part = L.sub + L.slots * (kCB / kSub) * 64 * rows_per_lane(dk) * kCW;
@@ -83,10 +87,11 @@ __host__ __device__ inline BwdLayout bwd_layout(int64_t B, int64_t T, int64_t H,
 template <int M>
 __device__ __forceinline__ float lane_xor(float x) {
   const int v = __float_as_int(x);
+  // (bound_ctrl set where every lane has a source: lets the move fuse into its add)
   if constexpr (M == 1) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xb1, 0xf, 0xf, false));  // quad_perm 1,0,3,2
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0xb1, 0xf, 0xf, true));  // quad_perm 1,0,3,2
   } else if constexpr (M == 2) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x4e, 0xf, 0xf, false));  // quad_perm 2,3,0,1
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x4e, 0xf, 0xf, true));  // quad_perm 2,3,0,1
   } else if constexpr (M == 4) {
     // lanes 0-3 and 8-11 of a row (banks 0, 2) read lane + 4 (row_shl:4), lanes
     // 4-7 and 12-15 (banks 1, 3) read lane - 4 (row_shr:4)
@@ -95,7 +100,7 @@ __device__ __forceinline__ float lane_xor(float x) {
     return __int_as_float(r);
   } else {
     static_assert(M == 8, "lane_xor: M is 1, 2, 4 or 8");
-    return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x128, 0xf, 0xf, false));  // row_ror:8
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x128, 0xf, 0xf, true));  // row_ror:8
   }
 }
 
@@ -188,8 +193,9 @@ __global__ __launch_bounds__(256) void bwd_ops_kernel(Problem p, const In* __res
   const In* jv = static_cast<const In*>(p.j);
   const In* et = static_cast<const In*>(p.eta);
   auto ld = [](const In* y) { return IO<In>::ld(y); };
-  float* rw = ws + L.rows + x * 4 * DK;
-  float* cl = ws + L.cols + x * 2 * dv;
+  const int64_t xp = bh * (NS + 2 * kPad) + kPad + s;
+  float* rw = ws + L.rows + xp * 4 * DK;
+  float* cl = ws + L.cols + xp * 2 * dv;
   const int var = p.variant;
   // per-step scalars
   float sc = 0.0f, gate = 1.0f;
@@ -340,8 +346,9 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(Problem p, const float* 
   const int r0 = lane * NR;
   const bool act = DK >= 64 || r0 < DK;
   const int col = cbase + col_lane<CW>(lane & (CW - 1));
-  const float* rows = ws + L.rows + bh * NS * 4 * DK;
-  const float* cols = ws + L.cols + bh * NS * 2 * dv;
+  // step s of this head at rows + s * 4 dk (s in [-kPad, NS + kPad))
+  const float* rows = ws + L.rows + (bh * (NS + 2 * kPad) + kPad) * 4 * DK;
+  const float* cols = ws + L.cols + (bh * (NS + 2 * kPad) + kPad) * 2 * dv;
   const size_t sbase = size_t(bh) * DK * size_t(dv);
   float* ckp = ws + (grad ? L.gk : L.ck) + bh * L.nck * DK * dv;
   const float* init = grad ? dsf : p.s0;
@@ -383,16 +390,20 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(Problem p, const float* 
   if (!grad) {
 #pragma unroll
     for (int i = 0; i < D; ++i) {  // in slot order, as the loop refills them
-      load_op<NR, false, true, false>(rows, cols, min<int64_t>(i, NS - 1), DK, dv, r0, act, col, ring[i]);
-      __builtin_amdgcn_sched_barrier(0);
+      load_op<NR, false, true, false>(rows, cols, i, DK, dv, r0, act, col, ring[i]);
+      asm volatile("" ::: "memory");
     }
     for (int64_t g = 0; g < nfull; ++g) {
       const int64_t s0 = g * D;
       if (s0 % kCB == 0) store(ckp + (s0 / kCB) * DK * dv);
+      // opaque to the optimizer, which would otherwise turn the refills back into
+      // loads at the point of use (the next group's addresses are the same)
+      int64_t nb = s0 + D;
+      asm volatile("" : "+s"(nb));
 #pragma unroll
       for (int i = 0; i < D; ++i) {
         fwd_step<NR, CW>(X, ring[i], lane);
-        load_op<NR, false, true, false>(rows, cols, min<int64_t>(s0 + D + i, NS - 1), DK, dv, r0, act, col, ring[i]);
+        load_op<NR, false, true, false>(rows, cols, nb + i, DK, dv, r0, act, col, ring[i]);
         __builtin_amdgcn_sched_barrier(0);  // keep the refill here, D steps ahead of its use
       }
     }
@@ -415,16 +426,18 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(Problem p, const float* 
   }
 #pragma unroll
   for (int i = 0; i < D; ++i) {
-    load_op<NR, true, false, true>(rows, cols, max<int64_t>(tail0 - 1 - i, 0), DK, dv, r0, act, col, ring[i]);
-    __builtin_amdgcn_sched_barrier(0);
+    load_op<NR, true, false, true>(rows, cols, tail0 - 1 - i, DK, dv, r0, act, col, ring[i]);
+    asm volatile("" ::: "memory");
   }
   for (int64_t g = nfull - 1; g >= 0; --g) {
     const int64_t s0 = g * D + D - 1;  // an interval's last step can only be a group's first
     if (s0 == NS - 1 || (s0 + 1) % kCB == 0) store(ckp + (s0 / kCB) * DK * dv);
+    int64_t nb = s0 - D;
+    asm volatile("" : "+s"(nb));
 #pragma unroll
     for (int i = 0; i < D; ++i) {
       grad_step<NR, CW>(X, ring[i], lane);
-      load_op<NR, true, false, true>(rows, cols, max<int64_t>(s0 - D - i, 0), DK, dv, r0, act, col, ring[i]);
+      load_op<NR, true, false, true>(rows, cols, nb - i, DK, dv, r0, act, col, ring[i]);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -478,13 +491,13 @@ __global__ __launch_bounds__(64) void bwd_interval_kernel(Problem p, float* __re
     const int cbase = slice * CW;
     const int64_t t0 = ci * kCB, t1 = min(NS, t0 + kCB);
     const int nb = int((t1 - t0 + kSub - 1) / kSub);
-    const float* rows = ws + L.rows + bh * NS * 4 * DK;
-    const float* cols = ws + L.cols + bh * NS * 2 * dv;
+    const float* rows = ws + L.rows + (bh * (NS + 2 * kPad) + kPad) * 4 * DK;
+    const float* cols = ws + L.cols + (bh * (NS + 2 * kPad) + kPad) * 2 * dv;
     auto load_blk = [&](int m, Op<NR> (&o)[kSub]) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < kSub; ++i) {
-        // past the interval's end: a valid step's operands, never used
-        const int64_t s = min(t0 + int64_t(m) * kSub + i, t1 - 1);
+        // past the interval's end: the next steps or padding, never used
+        const int64_t s = t0 + int64_t(m) * kSub + i;
         load_op<NR, true, true, true>(rows, cols, s, DK, dv, r0, act, cbase + lc, o[i]);
       }
     };
