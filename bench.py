@@ -144,16 +144,60 @@ def parity_check(o_dev, s_dev, res, tol):
     return out
 
 
+# Sources the two measured kernels (chunk_prep2_kernel for FG2, chunk_scan_rows_kernel)
+# are built from, with the launch and argument code around them.
+TRAFFIC_SOURCES = ("gdn_chunk.h", "gdn_chunk.hip", "gdn_prep_fg2.hip", "gdn_device.h", "gdn_internal.h",
+                   "gdn_api.cpp", os.path.join("..", "..", "include", "gdn.h"))
+
+
 def source_sha256():
-    """Hash of every kernel source file (the PMC traffic figures are only valid for
+    """Hash of the measured kernels' sources (the PMC traffic figures are only valid for
     the sources they were measured on)."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            h.update(name.encode())
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(f.read())
+    for name in TRAFFIC_SOURCES:
+        h.update(os.path.basename(name).encode())
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
+
+
+def write_traffic(pmc_dir):
+    """Write profiles/chunk_traffic_fg2_32k.json from two rocprofv3 runs of
+    `bench.py --profile-driver`, one with --pmc FETCH_SIZE (output under
+    pmc_dir/fetch, prefix fetch) and one with --pmc WRITE_SIZE (pmc_dir/write, prefix
+    write). The driver's 1 GiB device copy calibrates both counters."""
+    import collections
+    import csv
+    import re
+    # per dispatch, averaged over the steps for each instantiation; a stage's launches
+    # (the prepare stage's mild and flagged passes) are summed
+    vals = collections.defaultdict(list)
+    for name in ("fetch", "write"):
+        with open(os.path.join(pmc_dir, name, f"{name}_counter_collection.csv")) as f:
+            for row in csv.DictReader(f):
+                nm = row["Kernel_Name"]
+                m = re.search(r"::(\w+)(<[^(]*>)?\(", nm)
+                key = m.group(1) if m else ("copy" if "copyBuffer" in nm else nm[:30])
+                inst = m.group(2) if m else ""
+                vals[(key, inst, row["Counter_Name"])].append(float(row["Counter_Value"]))
+    avg = collections.defaultdict(float)
+    for (key, _, counter), v in vals.items():
+        avg[(key, counter)] += sum(v) / len(v)
+    cf, cw = avg[("copy", "FETCH_SIZE")], avg[("copy", "WRITE_SIZE")]
+    ff, wf = 1048576.0 / cf, 1048576.0 / cw  # KiB the copy moves each way / KiB counted
+    rec = {"source_sha256": source_sha256(),
+           "workload": "fg2_prefill_32k_bf16 (B=2, T=32768, H=16, dk=dv=128, chunk 64)",
+           "calibration": {"copy_bytes": 1 << 30, "FETCH_SIZE_KiB": cf, "WRITE_SIZE_KiB": cw,
+                           "fetch_factor": ff, "write_factor": wf},
+           "kernels": {}}
+    for k in ("chunk_prep2_kernel", "chunk_scan_rows_kernel"):
+        fk, wk = avg[(k, "FETCH_SIZE")], avg[(k, "WRITE_SIZE")]
+        rb, wb = fk * 1024 * ff, wk * 1024 * wf
+        rec["kernels"][k] = {"FETCH_SIZE_KiB": fk, "WRITE_SIZE_KiB": wk, "read_bytes": rb,
+                             "write_bytes": wb, "traffic_bytes_per_launch": rb + wb}
+    with open(PROFILE_TRAFFIC, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
 
 
 def read_traffic(kernel):
@@ -537,6 +581,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens per sequence for the oracle leg (default: all)")
+    ap.add_argument("--write-traffic", metavar="PMC_DIR",
+                    help="write the traffic summary from FETCH_SIZE / WRITE_SIZE runs under PMC_DIR")
     ap.add_argument("--profile-driver", action="store_true",
                     help="only run the workload for rocprofv3 counter collection")
     ap.add_argument("--configs", action="store_true",
@@ -556,6 +602,9 @@ def main():
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
 
+    if args.write_traffic:
+        write_traffic(args.write_traffic)
+        return
     if args.profile_driver:
         profile_driver(args)
         return
