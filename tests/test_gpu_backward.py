@@ -26,6 +26,12 @@ CASES = [  # variant, fg2_plus, dtype, B, T, H, dk, dv
     ("asym", False, "bf16", 1, 66, 1, 128, 64),
     ("deltaproduct", False, "f32", 1, 50, 2, 64, 64),     # 2 steps a token
     ("deltaproduct", False, "bf16", 1, 27, 2, 128, 128),  # 3 steps a token
+    # edges of the chain kernel's 16-step operand ring and the 64-step intervals
+    ("fg2", False, "bf16", 1, 1, 2, 128, 128),    # one token
+    ("kda", False, "f32", 2, 17, 3, 32, 16),      # one whole ring group and one step
+    ("gdn", False, "bf16", 1, 64, 2, 64, 64),     # exactly one interval
+    ("fg2", True, "bf16", 1, 129, 1, 128, 32),    # FG2+, a third interval of one step
+    ("asym", False, "f32", 1, 48, 2, 16, 128),    # dk 16: lanes past dk idle
 ]
 
 
@@ -68,3 +74,41 @@ def test_backward_deterministic():
     r2 = gdn.gdn_recurrent_bwd("fg2", d["q"], d["k"], d["v"], d["alpha"], d["beta"], d_o=do)
     for name in r1:
         assert torch.equal(r1[name], r2[name]), name
+
+
+def test_backward_deltaproduct_eight_steps():
+    """DeltaProduct with n_h = 8 (72 sub-steps for 9 tokens): q and do act after the
+    eighth sub-step of each token, the gate at the first."""
+    import gated_delta_rule_69_amd as gdn
+    from gpu_util import DEV, host, state_to_dev, to_dev
+    inp = gdn_inputs.make_inputs("deltaproduct", 1, 9, 2, 64, 32, dtype="f32", seed=94, n_h=8)
+    rng = np.random.default_rng(95)
+    s0 = gdn_inputs.make_state(1, 2, 64, 32, seed=96)
+    do = rng.standard_normal((1, 9, 2, 32)).astype(np.float32)
+    ref = obwd.backward(inp, do, s0, None)
+    d = to_dev(inp)
+    got = gdn.gdn_recurrent_bwd("deltaproduct", d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                d_o=torch.from_numpy(do).to(DEV), s0=state_to_dev(s0))
+    torch.cuda.synchronize()
+    for name, r in ref.items():
+        x = host(got[name])
+        e2, em = oracle.rel_l2(x, r), oracle.max_rel(x, r)
+        print("dp n_h 8", name, f"rel_l2={e2:.2e} max_rel={em:.2e}", flush=True)
+        assert e2 <= 1e-5 and em <= 1e-4, (name, e2, em)
+
+
+def test_backward_empty_sequence():
+    """T = 0: no step to differentiate; dL/dS_0 is dL/dS_T (zero without it)."""
+    import gated_delta_rule_69_amd as gdn
+    from gpu_util import DEV
+    B, H, d = 2, 3, 64
+    z = lambda *sh: torch.zeros(sh, device=DEV, dtype=torch.bfloat16)  # noqa: E731
+    q, k, v, al, be = z(B, 0, H, d), z(B, 0, H, d), z(B, 0, H, d), z(B, 0, H, d), z(B, 0, H, d)
+    dsf = torch.randn((B, H, d, d), device=DEV)
+    got = gdn.gdn_recurrent_bwd("fg2", q, k, v, al, be, d_o=z(B, 0, H, d), ds_final=dsf)
+    torch.cuda.synchronize()
+    assert torch.equal(got["ds0"], dsf)
+    assert all(got[n].numel() == 0 for n in ("dq", "dk", "dv", "dalpha", "dbeta"))
+    got = gdn.gdn_recurrent_bwd("fg2", q, k, v, al, be, d_o=z(B, 0, H, d))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(got["ds0"]) == 0
