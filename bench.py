@@ -573,6 +573,61 @@ def backward(args):
                       "parity": errs, "data": "synthetic", "n_gpus": 1}), flush=True)
 
 
+def fg2_plus(args):
+    """FG2-GDN+ (a value-side beta of its own) on the headline workload's shape (B=2,
+    T=32768, H=16, d=128, chunk 64, bf16): prepare and scan times (HIP events around
+    each stage, mean over --steps steps after --warmup), the prepare stage's HBM
+    fraction on its 6 d bf16 input bytes per token-head, and o / S_T of sequence 0,
+    head 0 against the float64 oracle."""
+    import torch
+    import gated_delta_rule_69_amd as gdn
+    import oracle
+    dev = torch.device("cuda:0")
+    W = gdn_inputs.CONFIGS[2]
+    B, T, H, d, C = W["B"], W["T"], W["H"], W["dk"], W["chunk"]
+    log("fg2+: generating inputs")
+    inp = gdn_inputs.make_inputs("fg2", B, T, H, d, d, dtype="bf16", seed=2, fg2_plus=True)
+    t = {n: torch.from_numpy(inp[n]).to(dev).to(torch.bfloat16).contiguous()
+         for n in ("q", "k", "v", "alpha", "beta", "beta_v")}
+    o = torch.empty((B, T, H, d), dtype=torch.bfloat16, device=dev)
+    s_final = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    a = gdn.make_args("fg2", t["q"], t["k"], t["v"], t["alpha"], t["beta"], chunk=C, beta_v=t["beta_v"],
+                      s_final=s_final, o=o)
+    ws = torch.empty(gdn.gdn_workspace_bytes(a), dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        gdn.gdn_chunk_prepare(a, ws)
+        gdn.gdn_chunk_scan(a, ws)
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(args.steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        gdn.gdn_chunk_prepare(a, ws)
+        e[1].record()
+        gdn.gdn_chunk_scan(a, ws)
+        e[2].record()
+        evs.append(e)
+    torch.cuda.synchronize()
+    prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    nbytes = B * T * H * 6 * d * 2  # q, k, v, alpha, beta, beta_v
+    gbs = nbytes / (prep_ms * 1e-3) / 1e9
+    sub = {k: (v[0:1, :, 0:1] if isinstance(v, np.ndarray) else v) for k, v in inp.items()}
+    sub["B"], sub["H"] = 1, 1
+    o_ref, s_ref = oracle.forward(sub)
+    o_err = oracle.rel_l2(o[0, :, 0].float().cpu().numpy(), o_ref[0, :, 0])
+    s_err = oracle.rel_l2(s_final[0, 0].cpu().numpy(), s_ref[0, 0])
+    log(f"fg2+: prepare {prep_ms:.3f} ms ({gbs:.0f} GB/s, {gbs / HBM_PEAK_GBS:.1%}), scan {scan_ms:.3f} ms, "
+        f"parity o {o_err:.2e} S {s_err:.2e}")
+    print(json.dumps({"metric": "FG2-GDN+ chunked prefill at 32K (B=2, H=16, d=128): stage times",
+                      "prepare_ms": prep_ms, "scan_ms": scan_ms, "ms_per_step": prep_ms + scan_ms,
+                      "tokens_per_s": B * T / ((prep_ms + scan_ms) * 1e-3),
+                      "prepare_roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                           "frac": gbs / HBM_PEAK_GBS, "algorithmic": nbytes},
+                      "parity": {"o_rel_l2": o_err, "S_rel_l2": s_err}, "data": "synthetic", "n_gpus": 1}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -593,6 +648,8 @@ def main():
                     help="backward pass (gdn_recurrent_bwd) on the 4K prefill workload")
     ap.add_argument("--stabilize", action="store_true",
                     help="GDN2 stabilisers (gdn_asym_stabilize) on the asymmetric workload")
+    ap.add_argument("--fg2-plus", action="store_true",
+                    help="FG2-GDN+ (value-side beta) stage times on the 32K workload's shape")
     ap.add_argument("--sweep", action="store_true",
                     help="the prefill sweep at a fixed 32,768 tokens (2K x 16 .. 32K x 1), FG2 and KDA")
     args = ap.parse_args()
@@ -616,6 +673,9 @@ def main():
         return
     if args.stabilize:
         stabilize(args)
+        return
+    if args.fg2_plus:
+        fg2_plus(args)
         return
     if args.backward:
         backward(args)

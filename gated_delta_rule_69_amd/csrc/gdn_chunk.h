@@ -1286,13 +1286,12 @@ struct alignas(16) PrepLds2 {
   float tdec[kWaves];       // largest decay of any channel over each 16-step tile (log2)
 };
 
-// Whether chunk_prep2_kernel covers a problem (bf16, dk = dv = 128, chunk 64, no
-// separate value-side beta; DeltaProduct with n_h = 1, 2 or 4, the step counts a
-// 64-step chunk with at least 16 output rows allows).
+// Whether chunk_prep2_kernel covers a problem (bf16, dk = dv = 128, chunk 64;
+// DeltaProduct with n_h = 1, 2 or 4, the step counts a 64-step chunk with at least
+// 16 output rows allows).
 inline bool prep2_covers(const Problem& p) {
   return p.dtype == GDN_DTYPE_BF16 && p.dk == 128 && p.dv == 128 && p.chunk == 64 &&
-         (p.n_step == 1 || p.n_step == 2 || p.n_step == 4) &&
-         !(p.variant == GDN_VARIANT_FG2 && p.beta_v != nullptr);
+         (p.n_step == 1 || p.n_step == 2 || p.n_step == 4);
 }
 
 // STAB: the GDN2 stabiliser mode applied to the rows (ASYM only; a template
@@ -1304,7 +1303,7 @@ inline bool prep2_covers(const Problem& p) {
 // to the chunk's middle; every other chunk is only flagged (flags[item] = 1, else
 // 0); 2 = the flagged chunks, on the tile-referenced path. 0 = every chunk on the
 // tile-referenced path (scalar decay).
-template <int V, int STAB, int NH, int MODE>
+template <int V, int STAB, int NH, int MODE, bool PLUS = false>
 __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, unsigned char* __restrict__ ws,
                                                                      unsigned char* __restrict__ flags,
                                                                      ChunkLayout L, int want_out) {
@@ -1317,6 +1316,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
   constexpr bool CH_BJ = V == GDN_VARIANT_FG2 || V == GDN_VARIANT_ASYM;  // per-channel beta / j
   constexpr bool SCALAR = !CH_ALPHA;  // one log decay per row (GDN, DeltaProduct)
   static_assert(SCALAR ? MODE == 0 : MODE != 0, "mild / flagged passes for per-channel decay");
+  static_assert(!PLUS || V == GDN_VARIANT_FG2, "a value-side beta is FG2-GDN+ only");
   using Sm = PrepLds2;
   static_assert(sizeof(Sm) <= 80 * 1024, "two workgroups per CU");
   __shared__ Sm sm;
@@ -1535,6 +1535,20 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
     // max |v| max sqrt(beta) of the row, which keeps the scaled values below 2^13.
     float G[SCALAR ? 1 : 32];
     ushort2v qm2 = {0, 0}, vm2 = {0, 0}, bm2 = {0, 0};
+    // FG2-GDN+: this row's value-side beta (dv = dk channels, the lane's 32), read
+    // here for the written values' bound and kept for phase 2
+    // (the flagged pass, short of registers, reads it again there)
+    uint4 bvr[PLUS ? 4 : 1];
+    const In* bvg = static_cast<const In*>(p.beta_v);
+    const int64_t offv = th_of(it, r) * DK + 8 * lg;
+    if constexpr (PLUS) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) bvr[u] = *reinterpret_cast<const uint4*>(bvg + offv + 32 * u);
+    }
+    auto bv_at = [&](int u) __attribute__((always_inline)) -> uint4 {
+      if constexpr (MODE == 2) return *reinterpret_cast<const uint4*>(bvg + offv + 32 * u);
+      else return bvr[PLUS ? u : 0];
+    };
     auto absmax2 = [](ushort2v m, uint32_t w) __attribute__((always_inline)) {
       return __builtin_elementwise_max(m, __builtin_bit_cast(ushort2v, w & 0x7fff7fffu));
     };
@@ -1553,7 +1567,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
       }
       vm2 = absmax8(vm2, raw.v[u]);
       if (want_out) qm2 = absmax8(qm2, raw.q[u]);
-      if constexpr (V == GDN_VARIANT_FG2) bm2 = absmax8(bm2, raw.b[u]);
+      if constexpr (V == GDN_VARIANT_FG2) {
+        if constexpr (PLUS) bm2 = absmax8(bm2, bvr[u]);  // the written values' beta
+        else bm2 = absmax8(bm2, raw.b[u]);
+      }
     }
     if constexpr (SCALAR) G[0] = glog;
     auto bits_max = [](ushort2v m) __attribute__((always_inline)) {
@@ -1709,6 +1726,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
         const uint4 kr = raw.k[u], vr = raw.v[u];
         uint4 br = {}, qr = {};
         if constexpr (CH_BJ) br = raw.b[u];
+        uint4 bvu = {};
+        if constexpr (PLUS) bvu = bv_at(u);
         if (want_out && valid && orow) qr = raw.q[u];
         half8 xbt, xat, xv;
         H8 hi, lo, qp;
@@ -1720,7 +1739,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
             const float sb = valid ? __builtin_amdgcn_sqrtf(bf(br, e)) : 0.0f;
             a = sb * kf;
             bb = a;
-            xv[e] = (_Float16)(bf(vr, e) * sb * wsc);
+            const float sbv = PLUS ? (valid ? __builtin_amdgcn_sqrtf(bf(bvu, e)) : 0.0f) : sb;
+            xv[e] = (_Float16)(bf(vr, e) * sbv * wsc);
           } else if constexpr (V == GDN_VARIANT_ASYM) {
             a = valid ? kf : 0.0f;
             bb = bscal * (STAB == 2 ? stab_j(stc, kf, bf(br, e)) : bf(br, e));
@@ -1872,6 +1892,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
         const uint4 kr = raw.k[u], vr = raw.v[u];
         uint4 br = {}, qr = {};
         if constexpr (CH_BJ) br = raw.b[u];
+        uint4 bvu = {};
+        if constexpr (PLUS) bvu = bv_at(u);
         if (want_out && valid && orow) qr = raw.q[u];
         half8 xbt, xat, xv;
         H8 hi, lo, qp;
@@ -1884,7 +1906,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
             const float sb = valid ? __builtin_amdgcn_sqrtf(bf(br, e)) : 0.0f;
             a = sb * kf;
             bb = a;
-            xv[e] = (_Float16)(bf(vr, e) * sb * wsc);
+            const float sbv = PLUS ? (valid ? __builtin_amdgcn_sqrtf(bf(bvu, e)) : 0.0f) : sb;
+            xv[e] = (_Float16)(bf(vr, e) * sbv * wsc);
           } else if constexpr (V == GDN_VARIANT_ASYM) {
             a = valid ? kf : 0.0f;
             bb = bscal * (STAB == 2 ? stab_j(stc, kf, bf(br, e)) : bf(br, e));
@@ -2262,6 +2285,11 @@ int launch_prep_t(const Problem& p, void* ws, bool want_out, hipStream_t s) {
             two_pass(chunk_prep2_kernel<V, 1, 1, 1>, chunk_prep2_kernel<V, 1, 1, 2>);
           else if (p.stabilize == GDN_STABILIZE_PROJECT_J)
             two_pass(chunk_prep2_kernel<V, 2, 1, 1>, chunk_prep2_kernel<V, 2, 1, 2>);
+          else
+            two_pass(chunk_prep2_kernel<V, 0, 1, 1>, chunk_prep2_kernel<V, 0, 1, 2>);
+        } else if constexpr (V == GDN_VARIANT_FG2) {
+          if (p.beta_v != nullptr)  // FG2-GDN+
+            two_pass(chunk_prep2_kernel<V, 0, 1, 1, true>, chunk_prep2_kernel<V, 0, 1, 2, true>);
           else
             two_pass(chunk_prep2_kernel<V, 0, 1, 1>, chunk_prep2_kernel<V, 0, 1, 2>);
         } else {

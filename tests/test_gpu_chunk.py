@@ -158,6 +158,17 @@ def test_fg2_plus_fragment_records():
     _run_and_check(inp, s0, chunk=64, what="fg2+ dk128 dv64")
 
 
+@pytest.mark.parametrize("T,alpha_mean", [(1, 3.0), (130, 3.0), (300, 3.0), (300, -3.0)])
+def test_fg2_plus_two_workgroup_prepare(T, alpha_mean):
+    """FG2+ with dk = dv = 128, chunk 64, bf16: the two-workgroup prepare kernel with a
+    value-side beta row, on mild decay (the mid-chunk pass) and on strong decay (the
+    flagged chunks' tile-referenced pass), ragged ends and a nonzero initial state."""
+    inp = gdn_inputs.make_inputs("fg2", 1, T, 2, 128, 128, dtype="bf16", seed=15 + T, fg2_plus=True,
+                                 alpha_mean=alpha_mean)
+    s0 = gdn_inputs.make_state(1, 2, 128, 128, seed=16)
+    _run_and_check(inp, s0, chunk=64, what=f"fg2+ dk128 dv128 T={T} alpha_mean={alpha_mean}")
+
+
 @pytest.mark.parametrize("T", [1, 63, 65, 130])
 def test_short_and_ragged_fragment_records(T):
     inp = gdn_inputs.make_inputs("fg2", 1, T, 2, 128, 128, dtype="bf16", seed=40 + T)
