@@ -34,9 +34,10 @@ int validate(const gdn_args* a, Entry e, Problem* out) {
   }
   const bool chunked = e != Entry::Recurrent && e != Entry::Stabilize;
   int chunk = a->chunk;
-  // DeltaProduct with three Householder steps a token is laid out in chunks as four,
-  // the fourth an identity step, so that a chunk holds whole tokens
-  const int n_step = (chunked && a->n_h == 3) ? 4 : a->n_h;
+  // DeltaProduct is laid out in chunks with a power-of-two number of steps a token
+  // (three Householder steps as four, five to seven as eight), the extra ones
+  // identity steps, so that a chunk holds whole tokens
+  const int n_step = !chunked ? a->n_h : a->n_h == 3 ? 4 : a->n_h >= 5 ? 8 : a->n_h;
   if (chunked) {
     if (chunk != 16 && chunk != 32 && chunk != 64) return GDN_ERR_UNSUPPORTED;
     // fp32 tiles of a 64-step chunk with 128 key channels exceed the 160 KB of LDS of
@@ -44,7 +45,8 @@ int validate(const gdn_args* a, Entry e, Problem* out) {
     // the same recurrence up to rounding
     if (a->dtype == GDN_DTYPE_F32 && a->dk == 128 && chunk == 64) chunk = 32;
     if (chunk % n_step != 0) return GDN_ERR_UNSUPPORTED;
-    if (chunk / n_step < 16) return GDN_ERR_UNSUPPORTED;  // one 16-row output tile at least
+    // output rows a chunk: 8 (one half-filled 16-row tile) or a multiple of 16
+    if (chunk / n_step < 8) return GDN_ERR_UNSUPPORTED;
   }
   if (a->variant == GDN_VARIANT_FG2 && a->beta_v == nullptr && a->dk != a->dv)
     return GDN_ERR_ARG;  // one beta vector scales both key and value channels

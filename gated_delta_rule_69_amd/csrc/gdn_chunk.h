@@ -320,7 +320,7 @@ __global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
   const int n_h = DPV ? p.n_step : 1;  // steps a token takes in the chunk
-  const int R = p.rows_out, RT = R / 16;
+  const int R = p.rows_out, RT = (R + 15) / 16;  // output rows, 16-row tiles (R = 8: one)
   const int dv = int(p.dv);
   const int NC = int(p.nchunks);
   const int H = int(p.H);
@@ -1026,20 +1026,26 @@ __global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk
       } else {
         // DeltaProduct (scalar decay): output row ro reads the state after step tau
         if (wave < RT) {
+          // With 8 output rows (R = 8) lanes 8..15 of the tile have no row: they run
+          // the products on row R - 1 (the MFMAs take every lane) and store nothing.
           const int ro = 16 * wave + li;
-          const int tau = ro * n_h + n_h - 1;
+          const bool live = ro < R;
+          const int rq = live ? ro : R - 1;
+          const int tau = rq * n_h + n_h - 1;
           const int jmax = min(NT - 1, ((16 * wave + 15) * n_h + n_h - 1) / 16);
-          const float qsl = sm.qs[ro];
+          const float qsl = sm.qs[rq];
           const float gtau = sm.cu.s.grow[tau];
           for (int J = 0; J < NT; ++J) {
             float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (J <= jmax) acc = gram_q(J, ro);
+            if (J <= jmax) acc = gram_q(J, rq);
             float f[4];
             decay4(J, gtau, f);
             const int s0 = 16 * J + 4 * lg;
             Op* dst = FRAG ? P_g + p_frag(ro, J) : P_g + size_t(ro) * L.ldc + s0;
+            if (live) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dst[e] = (Op)((s0 + e <= tau) ? acc[e] * f[e] * qsl : 0.0f);
+              for (int e = 0; e < 4; ++e) dst[e] = (Op)((s0 + e <= tau) ? acc[e] * f[e] * qsl : 0.0f);
+            }
           }
         }
       }

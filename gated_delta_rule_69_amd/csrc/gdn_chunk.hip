@@ -90,7 +90,9 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(Problem p, const u
   const int col0 = cbase + 16 * wave;
   const bool active = col0 < dv;
   const int col = col0 + li;
-  const int R = p.rows_out, RT = R / 16;
+  // output rows a chunk: R = 8 fills half of one 16-row tile, whose other rows are
+  // computed from unwritten record rows and never stored
+  const int R = p.rows_out, RT = (R + 15) / 16;
   const int64_t NC = p.nchunks;
   const int64_t b = bh / p.H, h = bh % p.H;
   In* o = static_cast<In*>(p.o);
@@ -170,8 +172,9 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(Problem p, const u
         if (mo < RT) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int64_t t = (p.c0 + n) * R + 16 * mo + 4 * lg + e;
-            if (t < p.T) o[((b * p.T + t) * p.H + h) * dv + col] = ohold[mo][e];
+            const int ro = 16 * mo + 4 * lg + e;
+            const int64_t t = (p.c0 + n) * R + ro;
+            if (ro < R && t < p.T) o[((b * p.T + t) * p.H + h) * dv + col] = ohold[mo][e];
           }
         }
       }
@@ -535,7 +538,7 @@ __global__ __launch_bounds__(2 * kThreads + 64) void chunk_scan_rows_kernel(Prob
   // wave's own rows of ost and written with 16-byte stores.
   if (wave > kWaves) {
     const int ow = wave - kWaves - 1;
-    const bool act = want_out && ow < R / 16;
+    const bool act = want_out && ow < (R + 15) / 16;  // R = 8: half of one wave's rows
     FragsO fo;
     if (act && NC > 0) load_o(0, ow, fo);
     __syncthreads();
@@ -577,7 +580,7 @@ __global__ __launch_bounds__(2 * kThreads + 64) void chunk_scan_rows_kernel(Prob
         for (int x = lane; x < 16 * RU; x += 64) {
           const int ro = 16 * ow + x / RU, c8 = x % RU;
           const int64_t t = (p.c0 + n) * R + ro;
-          if (t < p.T)
+          if (ro < R && t < p.T)
             *reinterpret_cast<uint4*>(o + ((int64_t(b) * p.T + t) * H + h) * dv + col_base + 8 * c8) =
                 *reinterpret_cast<const uint4*>(&ost[ro][8 * c8]);
         }

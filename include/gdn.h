@@ -95,12 +95,12 @@ typedef struct gdn_args {
                        fp32 with dk = 128 runs 64 as 32 (same result up to
                        rounding, workspace sized for 32)                      */
   int32_t n_h;      /* Householder steps per token (DELTAPRODUCT, 1..8), else 1;
-                       chunked entry points: chunk / n_h >= 16 with n_h = 3
-                       counted as 4 (a chunk holds whole tokens and one 16-row
-                       output tile), so they take n_h = 1..4 (n_h 3 and 4 only
-                       with chunk 64, n_h 2 with chunk 32 or 64) and return
-                       GDN_ERR_UNSUPPORTED for n_h 5..8 and for fp32 with
-                       dk = 128 and n_h 3 or 4 (run as 32-step chunks);
+                       chunked entry points lay a token out as n_h steps, 4 for
+                       n_h = 3 and 8 for n_h = 5..7 (the extra ones identity
+                       steps) and need chunk / steps >= 8 output rows a chunk:
+                       n_h 1..8 with chunk 64 (fp32 with dk = 128 runs 32-step
+                       chunks: n_h 1..4), n_h 1..4 with chunk 32, n_h 1..2 with
+                       chunk 16; GDN_ERR_UNSUPPORTED otherwise;
                        gdn_recurrent_step takes every n_h                     */
   const void* q;
   const void* k;

@@ -96,14 +96,18 @@ def test_variant_specific_rules(lib):
     assert call_chunk(lib, good_args(variant=1, beta_v=FAKE), FAKE, 1 << 40) == -1
     # ASYM needs j and eta
     assert call_chunk(lib, good_args(variant=4), FAKE, 1 << 40) == -1
-    # DeltaProduct: chunk must be a multiple of the steps a token takes in a chunk
-    # (n_h, or 4 for n_h = 3) with >= 16 output rows
+    # DeltaProduct: a chunk holds whole tokens of n_step steps (n_h; 4 for n_h = 3; 8
+    # for n_h = 5..7) and at least 8 output rows (valid calls stop at the workspace)
     dp = dict(variant=3, n_h=3)
+    ws_of = lambda **kw: lib.gdn_workspace_bytes(ctypes.byref(good_args(**kw)))  # noqa: E731
     assert call_chunk(lib, good_args(**dp)) == -3                        # 64 = 16 tokens x 4
-    assert call_chunk(lib, good_args(chunk=32, **dp), FAKE, 1 << 40) == -2  # 8 output rows
-    assert lib.gdn_workspace_bytes(ctypes.byref(good_args(**dp))) == \
-        lib.gdn_workspace_bytes(ctypes.byref(good_args(variant=3, n_h=4)))
-    assert call_chunk(lib, good_args(variant=3, n_h=8), FAKE, 1 << 40) == -2
+    assert call_chunk(lib, good_args(chunk=32, **dp)) == -3              # 8 output rows
+    assert call_chunk(lib, good_args(chunk=16, **dp), FAKE, 1 << 40) == -2  # 4 output rows
+    assert ws_of(**dp) == ws_of(variant=3, n_h=4)
+    for n_h in (5, 6, 7, 8):                                             # 8 tokens x 8 steps
+        assert call_chunk(lib, good_args(variant=3, n_h=n_h)) == -3, n_h
+        assert ws_of(variant=3, n_h=n_h) == ws_of(variant=3, n_h=8) > 0, n_h
+    assert call_chunk(lib, good_args(variant=3, n_h=8, chunk=32), FAKE, 1 << 40) == -2
     assert call_chunk(lib, good_args(variant=3, n_h=9), FAKE, 1 << 40) == -2
     assert call_chunk(lib, good_args(variant=3, n_h=0), FAKE, 1 << 40) == -1
     assert call_chunk(lib, good_args(variant=3, n_h=2), FAKE, 0) == -3
@@ -174,8 +178,9 @@ def test_fp32_dk128_chunk64_runs_as_chunk32(lib):
     w32 = lib.gdn_workspace_bytes(ctypes.byref(good_args(chunk=32, **f32)))
     assert w64 == w32 > 0
     assert call_chunk(lib, good_args(chunk=64, **f32)) == -3     # valid: reaches the workspace check
-    # DeltaProduct with 4 steps a token would have 8 output rows a chunk: unsupported
-    assert call_chunk(lib, good_args(chunk=64, variant=3, n_h=4, **f32), FAKE, 1 << 40) == -2
+    # DeltaProduct in the 32-step chunks: 8 output rows with 4 steps a token, 4 with 8
+    assert call_chunk(lib, good_args(chunk=64, variant=3, n_h=4, **f32)) == -3
+    assert call_chunk(lib, good_args(chunk=64, variant=3, n_h=8, **f32), FAKE, 1 << 40) == -2
 
 
 def test_workspace_bytes_grows_with_tokens(lib):

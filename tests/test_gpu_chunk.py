@@ -145,6 +145,37 @@ def test_chunk_vs_oracle(case, with_s0):
     _run_and_check(inp, s0, chunk=chunk, what=f"{case} s0={with_s0}")
 
 
+# DeltaProduct chunks with 8 output rows (half of one 16-row tile): 8 steps a token
+# (n_h 5..7 padded with identity steps), or 4 (n_h 3, 4) in 32-step chunks, or 2 in
+# 16-step chunks; both scans (fragment records at bf16 dk 128, image records else)
+EIGHT_ROWS = [
+    # variant, dtype, B, T, H, dk, dv, n_h, chunk
+    ("deltaproduct", "bf16", 1, 50, 2, 128, 128, 8, 64),
+    ("deltaproduct", "bf16", 2, 37, 2, 128, 128, 5, 64),
+    ("deltaproduct", "f32", 1, 41, 2, 64, 64, 6, 64),
+    ("deltaproduct", "f32", 1, 20, 1, 16, 16, 7, 64),
+    ("deltaproduct", "f32", 1, 40, 2, 128, 128, 4, 64),   # fp32 dk 128: 32-step chunks
+    ("deltaproduct", "bf16", 1, 45, 2, 64, 64, 3, 32),
+    ("deltaproduct", "bf16", 1, 33, 2, 32, 32, 2, 16),
+]
+
+
+@pytest.mark.parametrize("case", EIGHT_ROWS, ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("with_s0", [False, True])
+def test_deltaproduct_eight_output_rows(case, with_s0):
+    var, dt, B, T, H, dk, dv, n_h, chunk = case
+    inp = gdn_inputs.make_inputs(var, B, T, H, dk, dv, dtype=dt, seed=60 + n_h, n_h=n_h)
+    s0 = gdn_inputs.make_state(B, H, dk, dv, seed=61) if with_s0 else None
+    _run_and_check(inp, s0, chunk=chunk, what=f"{case} s0={with_s0}")
+
+
+def test_deltaproduct_eight_steps_strong_decay():
+    inp = gdn_inputs.make_inputs("deltaproduct", 1, 60, 2, 128, 128, dtype="bf16", seed=62, n_h=8,
+                                 alpha_mean=-3.0)
+    s0 = gdn_inputs.make_state(1, 2, 128, 128, seed=63)
+    _run_and_check(inp, s0, chunk=64, what="dp n_h 8 strong decay")
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_fg2_plus(dt):
     inp = gdn_inputs.make_inputs("fg2", 1, 211, 2, 64, 128, dtype=dt, seed=12, fg2_plus=True)
