@@ -42,19 +42,22 @@ constexpr int kSub = 4;        // steps whose states the interval kernel holds i
 constexpr int kCW = 16;        // columns of an interval-kernel wave (a row-partial slice)
 constexpr int kChainCW = 4;    // columns of a chain-kernel wave
 constexpr int kChainRing = 16; // steps of operands a chain wave keeps in flight
-constexpr int kSlots = 1024;   // interval-kernel workgroups, each with a scratch slot
+constexpr int kSlots = 1024;   // interval-kernel waves, each with a scratch slot
 constexpr int kPad = kChainRing;  // operand padding (steps) before and after a sequence
 static_assert(kSub <= kPad, "an interval block reads at most kSub - 1 steps past the end");
 
 __host__ __device__ constexpr int rows_per_lane(int64_t dk) { return dk >= 64 ? int(dk / 64) : 1; }
+// Column slices an interval-kernel workgroup takes (one wave each): their row partials
+// are summed in LDS, so the workspace holds one partial set per group of slices.
+__host__ __device__ constexpr int slices_per_group(int64_t dv) { return dv >= 64 ? 4 : int(dv / kCW); }
 
 // Workspace (float offsets). T counts steps here (tokens x n_h for DeltaProduct).
 //   rows [B*H][kPad + steps + kPad][4][dk]   a, b, alpha, q      (kPad steps of padding on
 //   cols [B*H][kPad + steps + kPad][2][dv]   w, do                both sides, never used)
 //   ck   [B*H][intervals][dk][dv]   S before the interval's first step
 //   gk   [B*H][intervals][dk][dv]   dL/dS after the interval's last step
-//   sub  [slots][kCB / kSub][NR * kCW / 4][64 lanes] float4   interval-kernel states
-//   part [slices][B*H][steps][4][dk]   dq, da, db, dalpha partials per slice
+//   sub  [waves][kCB / kSub][NR * kCW / 4][64 lanes] float4   interval-kernel states
+//   part [slice groups][B*H][steps][4][dk]   dq, da, db, dalpha partials per group
 //   dw   [B*H][steps][dv]
 struct BwdLayout {
   int64_t rows, cols, ck, gk, sub, part, dw, total;
@@ -66,16 +69,17 @@ __host__ __device__ inline BwdLayout bwd_layout(int64_t B, int64_t T, int64_t H,
   const int64_t bh = B * H;
   const int64_t bth = B * T * H;
   L.nck = (T + kCB - 1) / kCB;
-  L.items = bh * (dv / kCW) * L.nck;
-  L.slots = L.items < kSlots ? L.items : kSlots;
+  const int64_t wpg = slices_per_group(dv), groups = dv / kCW / wpg;
+  L.items = bh * groups * L.nck;  // interval-kernel workgroup items
+  L.slots = L.items < kSlots / wpg ? L.items : kSlots / wpg;  // its workgroups
   const int64_t bsp = bh * (T + 2 * kPad);  // padded steps
   L.rows = 0;
   L.cols = L.rows + bsp * 4 * dk;
   L.ck = L.cols + bsp * 2 * dv;
   L.gk = L.ck + bh * L.nck * dk * dv;
   L.sub = L.gk + bh * L.nck * dk * dv;
-  L.part = L.sub + L.slots * (kCB / kSub) * 64 * rows_per_lane(dk) * kCW;
-  L.dw = L.part + (dv / kCW) * bth * 4 * dk;
+  L.part = L.sub + L.slots * wpg * (kCB / kSub) * 64 * rows_per_lane(dk) * kCW;
+  L.dw = L.part + groups * bth * 4 * dk;
   L.total = L.dw + bth * dv;
   if (L.total < 64) L.total = 64;  // a valid empty problem still reports a nonzero size
   return L;
@@ -445,25 +449,31 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(Problem p, const float* 
 }
 
 // ---- 3. interval kernel -------------------------------------------------------------
-// One wave per workgroup, persistent over the items (batch*head, interval, 16-column
-// slice). Pass A runs the interval forward from its stored S and keeps the state
-// before every kSub-step block in this workgroup's slot; pass B takes the blocks in
-// reverse: it recomputes the block's kSub states into registers and walks them back.
-template <int DK>
-__global__ __launch_bounds__(64) void bwd_interval_kernel(Problem p, float* __restrict__ ws) {
+// WPG waves per workgroup, one per 16-column slice of a group of slices, persistent
+// over the items (batch*head, interval, slice group). Pass A runs the interval forward
+// from its stored S and keeps the state before every kSub-step block in the wave's
+// slot; pass B takes the blocks in reverse: it recomputes the block's kSub states into
+// the wave's LDS and walks them back. The waves' row partials of a step are summed in
+// LDS in wave order (one barrier a step) and written once per group.
+template <int DK, int WPG>
+__global__ __launch_bounds__(64 * WPG) void bwd_interval_kernel(Problem p, float* __restrict__ ws) {
   constexpr int NR = rows_per_lane(DK);
   constexpr int CW = kCW;
   constexpr int NV = NR * CW / 4;  // float4 per lane of a state
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t NS = p.steps, H = p.H, dv = p.dv;
-  const int ns = int(dv / CW);
+  const int ngroups = int(dv / CW) / WPG;
   const BwdLayout L = bwd_layout(p.B, NS, H, DK, dv);
   const int64_t bth = p.B * NS * H;  // step rows
   const int r0 = lane * NR;
   const bool act = DK >= 64 || r0 < DK;
   const int lc = col_lane<CW>(lane & (CW - 1));
-  float4* slot = reinterpret_cast<float4*>(ws + L.sub) + int64_t(blockIdx.x) * (kCB / kSub) * NV * 64;
-  __shared__ float4 sts[kSub * NV * 64];  // states of the current block, lane order
+  float4* slot = reinterpret_cast<float4*>(ws + L.sub) + (int64_t(blockIdx.x) * WPG + wave) * (kCB / kSub) * NV * 64;
+  __shared__ float4 sts_all[WPG][kSub * NV * 64];  // each wave's block states, lane order
+  __shared__ float xch[WPG > 1 ? 2 : 1][WPG][4][DK];  // row partials of a step, by parity
+  float4* sts = sts_all[wave];
+  int par = 0;  // exchange buffer of the next step (the same sequence in every wave)
   float* part = ws + L.part;
   float* dwg = ws + L.dw;
 
@@ -485,8 +495,9 @@ __global__ __launch_bounds__(64) void bwd_interval_kernel(Problem p, float* __re
   };
 
   for (int64_t item = blockIdx.x; item < L.items; item += gridDim.x) {
-    const int slice = int(item % ns);
-    const int64_t rest = item / ns;
+    const int grp = int(item % ngroups);
+    const int slice = grp * WPG + wave;
+    const int64_t rest = item / ngroups;
     const int64_t ci = rest % L.nck, bh = rest / L.nck;
     const int cbase = slice * CW;
     const int64_t t0 = ci * kCB, t1 = min(NS, t0 + kCB);
@@ -602,15 +613,41 @@ __global__ __launch_bounds__(64) void bwd_interval_kernel(Problem p, float* __re
         }
         const int64_t pr = bh * NS + s;  // this head's step s
         if (lane < CW) dwg[pr * dv + cbase + lc] = dw;
-        if (act) {
-          float* pw = part + (int64_t(slice) * bth + pr) * 4 * DK + r0;
+        float* pw = part + (int64_t(grp) * bth + pr) * 4 * DK;
+        if constexpr (WPG == 1) {
+          if (act) {
 #pragma unroll
-          for (int r = 0; r < NR; ++r) {
-            pw[r] = dq[r];
-            pw[DK + r] = da[r];
-            pw[2 * DK + r] = db[r];
-            pw[3 * DK + r] = dal[r];
+            for (int r = 0; r < NR; ++r) {
+              pw[r0 + r] = dq[r];
+              pw[DK + r0 + r] = da[r];
+              pw[2 * DK + r0 + r] = db[r];
+              pw[3 * DK + r0 + r] = dal[r];
+            }
           }
+        } else {
+          float(*xb)[4][DK] = xch[par];
+          if (act) {
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+              xb[wave][0][r0 + r] = dq[r];
+              xb[wave][1][r0 + r] = da[r];
+              xb[wave][2][r0 + r] = db[r];
+              xb[wave][3][r0 + r] = dal[r];
+            }
+          }
+          __syncthreads();
+          // the sum over the group's slices, one quantity per wave (two for WPG = 2)
+#pragma unroll
+          for (int q = wave; q < 4; q += WPG) {
+#pragma unroll
+            for (int row = lane; row < DK; row += 64) {
+              float sum = xb[0][q][row];
+#pragma unroll
+              for (int w = 1; w < WPG; ++w) sum += xb[w][q][row];
+              pw[q * DK + row] = sum;
+            }
+          }
+          par ^= 1;
         }
       };
       static_assert(kSub == 4, "the reverse walk below is written out for four steps");
@@ -637,7 +674,7 @@ template <typename In, int DK>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(Problem p, GradPtrs g, const float* __restrict__ ws) {
   const int lane = threadIdx.x & 63;
   const int64_t T = p.T, H = p.H, dv = p.dv;
-  const int ns = int(dv / kCW);
+  const int ns = int(dv / kCW) / slices_per_group(dv);  // partial sets (slice groups)
   const int nh = p.n_h;
   const int64_t bth = p.B * T * H * nh;  // step rows
   const BwdLayout L = bwd_layout(p.B, p.steps, H, DK, dv);
@@ -767,7 +804,11 @@ int launch_dk(const Problem& p, const In* dO, const float* dsf, const GradPtrs& 
   bwd_chain_kernel<DK, kChainCW><<<dim3(unsigned(chain_waves / 4)), dim3(256), 0, s>>>(p, dsf, g.ds0, ws);
   int e = int(hipGetLastError());
   if (e != 0 || nsteps == 0) return e;
-  bwd_interval_kernel<DK><<<dim3(unsigned(L.slots)), dim3(64), 0, s>>>(p, ws);
+  switch (slices_per_group(p.dv)) {
+    case 1: bwd_interval_kernel<DK, 1><<<dim3(unsigned(L.slots)), dim3(64), 0, s>>>(p, ws); break;
+    case 2: bwd_interval_kernel<DK, 2><<<dim3(unsigned(L.slots)), dim3(128), 0, s>>>(p, ws); break;
+    default: bwd_interval_kernel<DK, 4><<<dim3(unsigned(L.slots)), dim3(256), 0, s>>>(p, ws); break;
+  }
   e = int(hipGetLastError());
   if (e != 0) return e;
   const int64_t waves = p.B * p.T * p.H * p.n_h;

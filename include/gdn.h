@@ -223,11 +223,11 @@ typedef struct gdn_grads {
 
 /* Bytes of device workspace gdn_recurrent_bwd needs (0 for an invalid set). Per
  * token (or sub-step) and head: the float32 step operands (4 dk + 2 dv floats), the
- * per-16-column-slice partial row gradients (dv / 16 x 4 dk floats), dw (dv floats)
- * and the state and state-gradient checkpoints (2 dk dv floats every 64 steps); plus
- * a fixed part of at most 1,024 x 16 x dk x 16 floats (128 MiB at dk = 128) for the
- * per-workgroup state slots. 21.5 KiB per token and head at dk = dv = 128: 1.58 GB
- * for 4,096 tokens x 16 heads. */
+ * partial row gradients of each group of up to four 16-column slices
+ * (max(dv / 64, 1) x 4 dk floats), dw (dv floats) and the state and state-gradient
+ * checkpoints (2 dk dv floats every 64 steps); plus a fixed part of at most
+ * 1,024 x 16 x dk x 16 floats (128 MiB at dk = 128) for the per-wave state slots.
+ * 9.5 KiB per token and head at dk = dv = 128: 0.77 GB for 4,096 tokens x 16 heads. */
 size_t gdn_bwd_workspace_bytes(const gdn_args* args);
 
 /* Backward pass (reverse-mode gradients) of the token recurrence for every variant
