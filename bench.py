@@ -246,28 +246,31 @@ SWEEP = [(2048, 16), (4096, 8), (8192, 4), (16384, 2), (32768, 1)]
 
 def sweep(args):
     """Tokens/s of one gdn_chunk_fwd step (prepare + scan, final states returned) at
-    each (T, B) of the sweep, for FG2 and KDA inputs. Each variant's inputs are drawn
-    once as one 32,768-token sequence per head and cut into B sequences of T tokens.
-    Parity: the first 1024 tokens of sequence 0, head 0 against the float64 oracle."""
+    each (T, B) of the sweep, for FG2, FG2+ (a value-side beta of its own) and KDA
+    inputs. Each variant's inputs are drawn once as one 32,768-token sequence per head
+    and cut into B sequences of T tokens. Parity: the first 1024 tokens of sequence 0,
+    head 0 against the float64 oracle."""
     import torch
     import gated_delta_rule_69_amd as gdn
     import oracle
     dev = torch.device("cuda:0")
     H, d, C, total = 16, 128, 64, 32768
     rows = []
-    for variant in ("fg2", "kda"):
+    for variant in ("fg2", "fg2_plus", "kda"):
         log(f"sweep: generating {variant} inputs (32,768 tokens x {H} heads)")
-        inp = gdn_inputs.make_inputs(variant, 1, total, H, d, d, dtype="bf16", seed=20)
+        base = "fg2" if variant == "fg2_plus" else variant
+        inp = gdn_inputs.make_inputs(base, 1, total, H, d, d, dtype="bf16", seed=20,
+                                     fg2_plus=variant == "fg2_plus")
         for T, B in SWEEP:
             cut = {k: (inp[k].reshape((B, T) + inp[k].shape[2:]) if isinstance(inp[k], np.ndarray) else inp[k])
                    for k in inp}
             cut["B"], cut["T"] = B, T
             tens = {k: torch.from_numpy(np.ascontiguousarray(cut[k])).to(dev).to(torch.bfloat16)
-                    for k in ("q", "k", "v", "alpha", "beta")}
+                    for k in ("q", "k", "v", "alpha", "beta", "beta_v") if k in cut}
             o = torch.empty((B, T, H, d), dtype=torch.bfloat16, device=dev)
             s_final = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
-            a = gdn.make_args(variant, tens["q"], tens["k"], tens["v"], tens["alpha"], tens["beta"],
-                              chunk=C, s_final=s_final, o=o)
+            a = gdn.make_args(base, tens["q"], tens["k"], tens["v"], tens["alpha"], tens["beta"],
+                              chunk=C, beta_v=tens.get("beta_v"), s_final=s_final, o=o)
             ws = torch.empty(gdn.gdn_workspace_bytes(a), dtype=torch.uint8, device=dev)
             for _ in range(args.warmup):
                 gdn.gdn_chunk_fwd_args(a, ws)
@@ -294,8 +297,9 @@ def sweep(args):
         "metric": "prefill tokens/s at a fixed 32,768 tokens per step (H=16, d=128, chunk 64, bf16)",
         "unit": "tokens/s",
         "rows": rows,
-        "long_over_short": {v: tok[(v, 32768)] / tok[(v, 2048)] for v in ("fg2", "kda")},
+        "long_over_short": {v: tok[(v, 32768)] / tok[(v, 2048)] for v in ("fg2", "fg2_plus", "kda")},
         "fg2_over_kda_time": {str(T): tok[("kda", T)] / tok[("fg2", T)] for T, _ in SWEEP},
+        "fg2_plus_over_kda_time": {str(T): tok[("kda", T)] / tok[("fg2_plus", T)] for T, _ in SWEEP},
         "data": "synthetic",
         "n_gpus": 1,
     }
