@@ -30,7 +30,8 @@
 // sums over rows are wave reductions: a transposing butterfly over the lane bits
 // below CW (each exchange halves the values a lane carries, DPP within 16-lane rows)
 // and then plain pair sums over the remaining lane bits, which leaves the total of
-// column bitrev(l mod CW) in lane l; v_readlane then broadcasts them as scalars.
+// column bitrev(l mod CW) in lane l; a DPP move (quad_perm or row_newbcast) then gives
+// every lane any column's total.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -164,9 +165,30 @@ __host__ __device__ constexpr int col_lane(int c) {
   return r;
 }
 
-__device__ __forceinline__ float bcast(float x, int lane) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+// The total of column c in every lane, after col_sum: DPP from the lane holding it in
+// the lane's own quad (CW <= 4, quad_perm) or 16-lane row (row_newbcast). c must fold
+// to a constant (unrolled loops), so that the switch leaves one DPP move.
+#define GDN_BCAST_CASE(n, ctrl) \
+  case n:                      \
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, v, ctrl, 0xf, 0xf, true));
+template <int CW>
+__device__ __forceinline__ float col_bcast(float x, int c) {
+  const int v = __float_as_int(x);
+  if constexpr (CW <= 4) {
+    switch (col_lane<CW>(c)) {
+      GDN_BCAST_CASE(0, 0x00) GDN_BCAST_CASE(1, 0x55) GDN_BCAST_CASE(2, 0xaa) GDN_BCAST_CASE(3, 0xff)
+    }
+  } else {
+    switch (col_lane<CW>(c)) {
+      GDN_BCAST_CASE(0, 0x150) GDN_BCAST_CASE(1, 0x151) GDN_BCAST_CASE(2, 0x152) GDN_BCAST_CASE(3, 0x153)
+      GDN_BCAST_CASE(4, 0x154) GDN_BCAST_CASE(5, 0x155) GDN_BCAST_CASE(6, 0x156) GDN_BCAST_CASE(7, 0x157)
+      GDN_BCAST_CASE(8, 0x158) GDN_BCAST_CASE(9, 0x159) GDN_BCAST_CASE(10, 0x15a) GDN_BCAST_CASE(11, 0x15b)
+      GDN_BCAST_CASE(12, 0x15c) GDN_BCAST_CASE(13, 0x15d) GDN_BCAST_CASE(14, 0x15e) GDN_BCAST_CASE(15, 0x15f)
+    }
+  }
+  return 0.0f;
 }
+#undef GDN_BCAST_CASE
 
 // ---- 1. operand kernel -------------------------------------------------------------
 // One wave per (batch*head, step): rows a, b, alpha, q and columns w, do in float32.
@@ -298,7 +320,7 @@ __device__ __forceinline__ float fwd_step(float (&S)[NR][CW], const Op<NR>& o, i
   const float u = o.w - col_sum<CW>(part, lane);
 #pragma unroll
   for (int c = 0; c < CW; ++c) {
-    const float uc = bcast(u, col_lane<CW>(c));
+    const float uc = col_bcast<CW>(u, c);
 #pragma unroll
     for (int r = 0; r < NR; ++r) S[r][c] += o.a[r] * uc;
   }
@@ -312,7 +334,7 @@ __device__ __forceinline__ void grad_step(float (&G)[NR][CW], const Op<NR>& o, i
   float part[CW];
 #pragma unroll
   for (int c = 0; c < CW; ++c) {
-    const float dc = bcast(o.d, col_lane<CW>(c));
+    const float dc = col_bcast<CW>(o.d, c);
     part[c] = 0.0f;
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
@@ -323,7 +345,7 @@ __device__ __forceinline__ void grad_step(float (&G)[NR][CW], const Op<NR>& o, i
   const float dw = col_sum<CW>(part, lane);
 #pragma unroll
   for (int c = 0; c < CW; ++c) {
-    const float dwc = bcast(dw, col_lane<CW>(c));
+    const float dwc = col_bcast<CW>(dw, c);
 #pragma unroll
     for (int r = 0; r < NR; ++r) G[r][c] = o.al[r] * (G[r][c] - o.b[r] * dwc);
   }
@@ -583,7 +605,7 @@ __global__ __launch_bounds__(64 * WPG) void bwd_interval_kernel(Problem p, float
         for (int r = 0; r < NR; ++r) dq[r] = o.a[r] * udo;
 #pragma unroll
         for (int c = 0; c < CW; ++c) {
-          const float dc = bcast(o.d, col_lane<CW>(c));
+          const float dc = col_bcast<CW>(o.d, c);
           gw[c] = 0.0f;
 #pragma unroll
           for (int r = 0; r < NR; ++r) {
@@ -600,8 +622,8 @@ __global__ __launch_bounds__(64 * WPG) void bwd_interval_kernel(Problem p, float
         for (int r = 0; r < NR; ++r) da[r] = db[r] = dal[r] = 0.0f;
 #pragma unroll
         for (int c = 0; c < CW; ++c) {
-          const float uc = bcast(u, col_lane<CW>(c));
-          const float dwc = bcast(dw, col_lane<CW>(c));
+          const float uc = col_bcast<CW>(u, c);
+          const float dwc = col_bcast<CW>(dw, c);
 #pragma unroll
           for (int r = 0; r < NR; ++r) {
             da[r] += G[r][c] * uc;
