@@ -816,6 +816,8 @@ int launch_dk(const Problem& p, const In* dO, const float* dsf, const GradPtrs& 
   const BwdLayout L = bwd_layout(p.B, p.steps, p.H, DK, p.dv);
   const int64_t nsteps = p.B * p.H * p.steps;
   if (nsteps > 0) {
+    // one wave a step: the grid fits 32 bits for any workspace that can exist (at least
+    // 16 dk + 8 dv bytes a step, so 2^34 steps would need hundreds of terabytes)
     bwd_ops_kernel<In><<<dim3(unsigned((nsteps + 3) / 4)), dim3(256), 0, s>>>(p, dO, ws);
     int e = int(hipGetLastError());
     if (e != 0) return e;
