@@ -204,6 +204,7 @@ static int bwd_problem(const gdn_args* args, Problem* p) {
   int st = gdn::validate(&a, Entry::Recurrent, p);
   if (st != GDN_OK) return st;
   if (p->stabilize != 0) return GDN_ERR_UNSUPPORTED;
+  if (p->B * p->H * p->steps > (int64_t(1) << 33)) return GDN_ERR_UNSUPPORTED;  // keeps every grid in 32 bits
   return GDN_OK;
 }
 

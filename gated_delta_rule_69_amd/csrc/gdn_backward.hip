@@ -1,199 +1,152 @@
 // Backward pass of the token recurrence (reverse mode), every variant: FG2, FG2+, KDA,
 // GDN, ASYM, and DeltaProduct as its sequence of Householder sub-steps.
 //
-// Per step, with X = Diag(alpha) S_{t-1}, u = w - X^T b, S_t = X + a u^T,
-// o_t = S_t^T q_t and G = dL/dS_t (the later steps' gradient plus q_t do_t^T):
-//   dq = S_t do,  dw = G^T a,  da = G u,  db = -X dw,  dX = G - b dw^T,
-//   dalpha = rowsum(dX . S_{t-1}),  dL/dS_{t-1} = Diag(alpha) dX,
-// then the chain rule through the variant's (a, b, w, alpha) map (FG2-GDN reading
-// notes, section 2.2 eq. (11) and section 2.3 eq. (13); GDN2-stability page, eq. (1)).
+// Per step S_t = (I - a b^T) Diag(alpha) S_{t-1} + a w^T and o_t = S_t^T q_t (FG2-GDN
+// reading notes, section 2.2 eq. (11) and section 2.3 eq. (13); GDN2-stability page,
+// eq. (1)); each variant is a map onto the per-step rows a, b, alpha, q and columns w.
+// The pass runs on chunks of 16 steps in the WY / UT form the forward pass uses
+// (reading notes, section 2.4). For a chunk with start state S and in-chunk inclusive
+// cumulative log decay G (per key channel, G_C at its last step):
+//   B+ = b e^G,  A- = a e^-G,  Q+ = q e^G,  A^ = a e^(G_C - G),  Gamma = e^(G_C)
+//   M = strict_tril(B+ A-^T),  P = tril(Q+ A-^T),  T = (I + M)^-1
+//   W = T B+,  U~ = T W_v,  U = U~ - W S,  O = Q+ S + P U,  S' = Gamma S + A^^T U.
+// With D = dL/dS' and dO, reverse mode through these products gives
+//   dU = P^T dO + A^ D,  dR = T^T dU (the gradient of W_v, i.e. of w),
+//   dP = tril(dO U^T),   dM = -strict_tril(dR U^T),
+//   dS = Gamma D + Q+^T dO - W^T dU = Gamma D - W^T (A^ D) + (Q+ - P W)^T dO,
+//   dQ+ = dO S^T + dP A-,  dB+ = -dR S^T + dM A-,  dA- = dP^T Q+ + dM^T B+,  dA^ = U D^T,
+// and the decay through dG = q.dq + b.db - a.da (at the last step also the A^ and Gamma
+// terms), d log alpha being the suffix sum of dG over the chunk.
 //
-// Only two things are sequential: the state S runs forward, and the state gradient
-// runs backward as G <- Diag(alpha) (I - b a^T) G + q do^T, which does not involve S.
-// So the pass is split into:
-//  1. the operand kernel: every step's a, b, alpha, q rows and w, do columns, once,
-//     in float32 (the later kernels do not branch on the variant);
-//  2. the chain kernel: the S and G recursions side by side, in separate waves, each
-//     over narrow column slices; S is stored at the start and G at the end of every
-//     64-step interval;
-//  3. the interval kernel: every (batch*head, 16-column slice, interval) on its own.
-//     It recomputes the interval's states from the stored S (keeping one state in
-//     four in a per-workgroup scratch slot, and four states at a time in registers)
-//     and walks the interval backwards from the stored G, writing the slice's row
-//     partials and the column-complete dw;
-//  4. the reduce kernel: slices summed in a fixed order, then the variant's chain rule.
+// e^-G is never formed: the Grams and the products with A- take factors split at the
+// chunk's step 8, e^(G - G_8) on the B+ / Q+ side and e^(G_8 - G) on the A- side, so no
+// factor spans more than 8 steps of decay; e^G, e^(G_C - G) and Gamma are at most 1.
+//
+// Kernels (all arithmetic in float32, products on fp32 MFMA):
+//  1. operands: every step's a, b, alpha, q rows and w, do columns (the variant's map),
+//     then identity steps up to a whole chunk;
+//  2. records: per chunk, the Grams, T by forward substitution, W, U~, A^, Q+ - P W and
+//     Gamma, each stored in the lane order of the products that read it;
+//  3. recursions: the state forward and its gradient backward over the chunks, one wave
+//     per (batch*head, 16 value columns) and direction; the state before and the
+//     gradient after every chunk are stored;
+//  4. intra-chunk gradients: every chunk on its own, from the two stored matrices;
+//  5. reduce: the variant's chain rule.
 // Every sum runs in a fixed order: the results are deterministic.
 //
-// Lane layout of the chain and interval kernels (rows on lanes): lane l owns state
-// rows l*NR .. l*NR+NR-1 (NR = max(dk / 64, 1); lanes past dk hold zeros) and all CW
-// columns of its slice in registers. Sums over a slice's columns stay inside a lane;
-// sums over rows are wave reductions: a transposing butterfly over the lane bits
-// below CW (each exchange halves the values a lane carries, DPP within 16-lane rows)
-// and then plain pair sums over the remaining lane bits, which leaves the total of
-// column bitrev(l mod CW) in lane l; a DPP move (quad_perm or row_newbcast) then gives
-// every lane any column's total.
+// MFMA layout (16x16x4 fp32, one wave): in a 16 x 16 tile, lane l = i + 16 g supplies
+// A[i][4g + e] and B[4g + e][i] for e = 0..3, and receives D[4g + e][i]. So an output
+// tile can be fed back as a B operand, or as the A operand of the transposed matrix,
+// and swapping the operands of a product yields its transpose. Two storage orders of
+// a 16-row matrix X follow: the fragment order (lane i + 16g holds X[4g + e][16t + i])
+// and the row order (lane i + 16g holds X[i][16t + 4g + e]), both one float4 per lane
+// and tile.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 namespace {
 
-constexpr int kCB = 64;        // steps per checkpoint interval
-constexpr int kSub = 4;        // steps whose states the interval kernel holds in registers
-constexpr int kCW = 16;        // columns of an interval-kernel wave (a row-partial slice)
-constexpr int kChainCW = 4;    // columns of a chain-kernel wave
-constexpr int kChainRing = 16; // steps of operands a chain wave keeps in flight
-constexpr int kSlots = 1024;   // interval-kernel waves, each with a scratch slot
-constexpr int kPad = kChainRing;  // operand padding (steps) before and after a sequence
-static_assert(kSub <= kPad, "an interval block reads at most kSub - 1 steps past the end");
+constexpr int kC = 16;    // steps a chunk
+constexpr int kRef = 8;   // reference step of the split decay factors
+constexpr int kPad = kC;  // operand rows after a sequence (identity steps fill its last chunk)
 
-__host__ __device__ constexpr int rows_per_lane(int64_t dk) { return dk >= 64 ? int(dk / 64) : 1; }
-// Column slices an interval-kernel workgroup takes (one wave each): their row partials
-// are summed in LDS, so the workspace holds one partial set per group of slices.
-__host__ __device__ constexpr int slices_per_group(int64_t dv) { return dv >= 64 ? 4 : int(dv / kCW); }
-
-// Workspace (float offsets). T counts steps here (tokens x n_h for DeltaProduct).
-//   rows [B*H][kPad + steps + kPad][4][dk]   a, b, alpha, q      (kPad steps of padding on
-//   cols [B*H][kPad + steps + kPad][2][dv]   w, do                both sides, never used)
-//   ck   [B*H][intervals][dk][dv]   S before the interval's first step
-//   gk   [B*H][intervals][dk][dv]   dL/dS after the interval's last step
-//   sub  [waves][kCB / kSub][NR * kCW / 4][64 lanes] float4   interval-kernel states
-//   part [slice groups][B*H][steps][4][dk]   dq, da, db, dalpha partials per group
-//   dw   [B*H][steps][dv]
-struct BwdLayout {
-  int64_t rows, cols, ck, gk, sub, part, dw, total;
-  int64_t nck, items, slots;
+// Record of one chunk (float offsets): W (fragment, row order), A^ (fragment, row
+// order), Q+ - P W (fragment), U~ (fragment, row order), Gamma, T and P (row-major 16 x 16).
+__host__ __device__ constexpr int64_t rec_floats(int64_t dk, int64_t dv) { return 80 * dk + 32 * dv + dk + 512; }
+template <int DK, int DV>
+struct Rec {
+  static constexpr int Wf = 0, Wr = 16 * DK, Af = 32 * DK, Ar = 48 * DK, Cf = 64 * DK;
+  static constexpr int Uf = 80 * DK, Ur = 80 * DK + 16 * DV, Gm = 80 * DK + 32 * DV;
+  static constexpr int Tm = Gm + DK, Pm = Tm + 256, size = Pm + 256;
+  static_assert(size == rec_floats(DK, DV), "record size");
 };
 
-__host__ __device__ inline BwdLayout bwd_layout(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv) {
+// Workspace (float offsets); NS steps a head (tokens x n_h for DeltaProduct):
+//   rows [B*H][NS + kPad][4][dk]   a, b, alpha, q
+//   cols [B*H][NS + kPad][2][dv]   w, do
+//   rec  [B*H][chunks][rec_floats]
+//   sst  [B*H][chunks][dk/16][dv/16][64 lanes][4]   state before the chunk (fragment order)
+//   dst  [B*H][chunks][dk/16][dv/16][64 lanes][4]   dL/dS after the chunk
+//   part [B*H][NS][4][dk]   dq, da, db, dalpha of each step
+//   dw   [B*H][NS][dv]
+struct BwdLayout {
+  int64_t rows, cols, rec, sst, dst, part, dw, total;
+  int64_t nc, rs;  // chunks and operand rows a head
+};
+
+__host__ __device__ inline BwdLayout bwd_layout(int64_t B, int64_t NS, int64_t H, int64_t dk, int64_t dv) {
   BwdLayout L;
   const int64_t bh = B * H;
-  const int64_t bth = B * T * H;
-  L.nck = (T + kCB - 1) / kCB;
-  const int64_t wpg = slices_per_group(dv), groups = dv / kCW / wpg;
-  L.items = bh * groups * L.nck;  // interval-kernel workgroup items
-  L.slots = L.items < kSlots / wpg ? L.items : kSlots / wpg;  // its workgroups
-  const int64_t bsp = bh * (T + 2 * kPad);  // padded steps
+  L.nc = (NS + kC - 1) / kC;
+  L.rs = NS + kPad;
   L.rows = 0;
-  L.cols = L.rows + bsp * 4 * dk;
-  L.ck = L.cols + bsp * 2 * dv;
-  L.gk = L.ck + bh * L.nck * dk * dv;
-  L.sub = L.gk + bh * L.nck * dk * dv;
-  L.part = L.sub + L.slots * wpg * (kCB / kSub) * 64 * rows_per_lane(dk) * kCW;
-  L.dw = L.part + groups * bth * 4 * dk;
-  L.total = L.dw + bth * dv;
+  L.cols = L.rows + bh * L.rs * 4 * dk;
+  L.rec = L.cols + bh * L.rs * 2 * dv;
+  L.sst = L.rec + bh * L.nc * rec_floats(dk, dv);
+  L.dst = L.sst + bh * L.nc * dk * dv;
+  L.part = L.dst + bh * L.nc * dk * dv;
+  L.dw = L.part + bh * NS * 4 * dk;
+  L.total = L.dw + bh * NS * dv;
   if (L.total < 64) L.total = 64;  // a valid empty problem still reports a nonzero size
   return L;
 }
 
-// ---- wave reductions in the rows-on-lanes layout ------------------------------------
+__device__ __forceinline__ float4v ld4(const float* p) { return *reinterpret_cast<const float4v*>(p); }
+__device__ __forceinline__ void st4(float* p, float4v v) { *reinterpret_cast<float4v*>(p) = v; }
+__device__ __forceinline__ float4v zero4() { return float4v{0.0f, 0.0f, 0.0f, 0.0f}; }
 
-// The value lane l ^ M holds (M < 16: DPP inside 16-lane rows).
-template <int M>
-__device__ __forceinline__ float lane_xor(float x) {
-  const int v = __float_as_int(x);
-  // (bound_ctrl set where every lane has a source: lets the move fuse into its add)
-  if constexpr (M == 1) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0xb1, 0xf, 0xf, true));  // quad_perm 1,0,3,2
-  } else if constexpr (M == 2) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x4e, 0xf, 0xf, true));  // quad_perm 2,3,0,1
-  } else if constexpr (M == 4) {
-    // lanes 0-3 and 8-11 of a row (banks 0, 2) read lane + 4 (row_shl:4), lanes
-    // 4-7 and 12-15 (banks 1, 3) read lane - 4 (row_shr:4)
-    int r = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xf, 0x5, false);
-    r = __builtin_amdgcn_update_dpp(r, v, 0x114, 0xf, 0xa, false);
-    return __int_as_float(r);
-  } else {
-    static_assert(M == 8, "lane_xor: M is 1, 2, 4 or 8");
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x128, 0xf, 0xf, true));  // row_ror:8
-  }
-}
-
-// x + (x of lane l ^ M), the same bits in both lanes of the pair.
-template <int M>
-__device__ __forceinline__ float pair_sum(float x) {
-  if constexpr (M == 16) {
-    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-  } else if constexpr (M == 32) {
-    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-  } else {
-    return x + lane_xor<M>(x);
-  }
-}
-
-// One transposing level: a lane with bit M clear keeps the lower half of its n = CW / M
-// values and adds the partner's lower half; a lane with bit M set keeps the upper half.
-template <int M, int CW>
-__device__ __forceinline__ void transpose_level(float (&v)[CW], int lane) {
-  constexpr int n = CW / M;
-  const bool hi = (lane & M) != 0;
+// D += A B over one 16-wide slice of the summed index (four MFMA 16x16x4).
+__device__ __forceinline__ float4v mma4(float4v a, float4v b, float4v acc) {
 #pragma unroll
-  for (int i = 0; i < n / 2; ++i) {
-    const float lo = v[i], up = v[i + n / 2];
-    const float keep = hi ? up : lo;
-    const float send = hi ? lo : up;
-    v[i] = keep + lane_xor<M>(send);
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
+  return acc;
+}
+
+// Sum of x over the lane groups below this lane's (lanes l - 16, l - 32, l - 48).
+__device__ __forceinline__ float group_prefix(float x, int l) {
+  const int g = l >> 4;
+  const float x1 = __shfl(x, (l + 48) & 63, 64);
+  const float x2 = __shfl(x, (l + 32) & 63, 64);
+  const float x3 = __shfl(x, (l + 16) & 63, 64);
+  return (g >= 1 ? x1 : 0.0f) + (g >= 2 ? x2 : 0.0f) + (g >= 3 ? x3 : 0.0f);
+}
+// Sum of x over the lane groups above this lane's.
+__device__ __forceinline__ float group_suffix(float x, int l) {
+  const int g = l >> 4;
+  const float x1 = __shfl(x, (l + 16) & 63, 64);
+  const float x2 = __shfl(x, (l + 32) & 63, 64);
+  const float x3 = __shfl(x, (l + 48) & 63, 64);
+  return (g <= 2 ? x1 : 0.0f) + (g <= 1 ? x2 : 0.0f) + (g == 0 ? x3 : 0.0f);
+}
+
+// In-chunk cumulative log decay of channel ch at steps 4g .. 4g+3 (fragment order),
+// from the operand rows of the chunk's first step. Every kernel forms G this way, so
+// all of them see the same values.
+template <int DK>
+__device__ __forceinline__ void chunk_logdecay(const float* rb, int ch, int l, float (&gv)[4]) {
+  const int g = l >> 4;
+  float run = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    run += logf(rb[(4 * g + e) * 4 * DK + 2 * DK + ch]);
+    gv[e] = run;
   }
+  const float pre = group_prefix(run, l);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) gv[e] += pre;
 }
 
-// Column sums over the 64 lanes of v[CW] (each lane's partials of CW columns).
-// Returns in lane l the total of column col_lane<CW>(l mod CW); v is consumed.
-template <int CW>
-__device__ __forceinline__ float col_sum(float (&v)[CW], int lane) {
-  static_assert(CW == 2 || CW == 4 || CW == 8 || CW == 16, "col_sum: CW is 2, 4, 8 or 16");
-  transpose_level<1, CW>(v, lane);
-  if constexpr (CW > 2) transpose_level<2, CW>(v, lane);
-  if constexpr (CW > 4) transpose_level<4, CW>(v, lane);
-  if constexpr (CW > 8) transpose_level<8, CW>(v, lane);
-  float x = v[0];
-  if constexpr (CW <= 2) x = pair_sum<2>(x);
-  if constexpr (CW <= 4) x = pair_sum<4>(x);
-  if constexpr (CW <= 8) x = pair_sum<8>(x);
-  x = pair_sum<16>(x);
-  return pair_sum<32>(x);
-}
-
-// Bit reversal over log2(CW) bits: the column whose total col_sum leaves in lane
-// l (l < CW), and, being an involution, the lane that holds column c.
-template <int CW>
-__host__ __device__ constexpr int col_lane(int c) {
-  int r = 0;
-  for (int b = 1, rb = CW / 2; b < CW; b <<= 1, rb >>= 1)
-    if (c & b) r |= rb;
-  return r;
-}
-
-// The total of column c in every lane, after col_sum: DPP from the lane holding it in
-// the lane's own quad (CW <= 4, quad_perm) or 16-lane row (row_newbcast). c must fold
-// to a constant (unrolled loops), so that the switch leaves one DPP move.
-#define GDN_BCAST_CASE(n, ctrl) \
-  case n:                      \
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, v, ctrl, 0xf, 0xf, true));
-template <int CW>
-__device__ __forceinline__ float col_bcast(float x, int c) {
-  const int v = __float_as_int(x);
-  if constexpr (CW <= 4) {
-    switch (col_lane<CW>(c)) {
-      GDN_BCAST_CASE(0, 0x00) GDN_BCAST_CASE(1, 0x55) GDN_BCAST_CASE(2, 0xaa) GDN_BCAST_CASE(3, 0xff)
-    }
-  } else {
-    switch (col_lane<CW>(c)) {
-      GDN_BCAST_CASE(0, 0x150) GDN_BCAST_CASE(1, 0x151) GDN_BCAST_CASE(2, 0x152) GDN_BCAST_CASE(3, 0x153)
-      GDN_BCAST_CASE(4, 0x154) GDN_BCAST_CASE(5, 0x155) GDN_BCAST_CASE(6, 0x156) GDN_BCAST_CASE(7, 0x157)
-      GDN_BCAST_CASE(8, 0x158) GDN_BCAST_CASE(9, 0x159) GDN_BCAST_CASE(10, 0x15a) GDN_BCAST_CASE(11, 0x15b)
-      GDN_BCAST_CASE(12, 0x15c) GDN_BCAST_CASE(13, 0x15d) GDN_BCAST_CASE(14, 0x15e) GDN_BCAST_CASE(15, 0x15f)
-    }
-  }
-  return 0.0f;
-}
-#undef GDN_BCAST_CASE
-
-// ---- 1. operand kernel -------------------------------------------------------------
-// One wave per (batch*head, step): rows a, b, alpha, q and columns w, do in float32.
+// ---- 1. operand kernel ------------------------------------------------------------
+// One wave per step: a, b, alpha, q rows and w, do columns in float32:
+//   FG2:   a = b = sqrt(beta) k, w = sqrt(beta) v (sqrt(beta_v) v for FG2+), alpha per channel
+//   KDA:   a = b = sqrt(beta) k, w = sqrt(beta) v, alpha per channel
+//   GDN:   the same with a scalar alpha
+//   DeltaProduct sub-step i: a = k_i, b = beta_i k_i, w = beta_i v_i
+//   ASYM:  a = k, b = eta j, w = eta v, alpha = D
 // q and do act after a token's last step (DeltaProduct: zero for the earlier steps),
-// the gate at its first.
+// the gate at its first. Steps from the end of the sequence to the end of its last
+// chunk are identity steps (nothing erased, written or read; no decay).
 template <typename In>
 __global__ __launch_bounds__(256) void bwd_ops_kernel(Problem p, const In* __restrict__ d_o,
                                                       float* __restrict__ ws) {
@@ -201,9 +154,25 @@ __global__ __launch_bounds__(256) void bwd_ops_kernel(Problem p, const In* __res
   const int64_t NS = p.steps, T = p.T, H = p.H, DK = p.dk, dv = p.dv;
   const int nh = p.n_h;
   const BwdLayout L = bwd_layout(p.B, NS, H, DK, dv);
-  const int64_t x = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);  // bh * NS + s
-  if (x >= p.B * H * NS) return;
-  const int64_t bh = x / NS, s = x % NS;
+  const int64_t NP = L.nc * kC;
+  const int64_t x = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);  // bh * NP + s
+  if (x >= p.B * H * NP) return;
+  const int64_t bh = x / NP, s = x % NP;
+  float* rw = ws + L.rows + (bh * L.rs + s) * 4 * DK;
+  float* cl = ws + L.cols + (bh * L.rs + s) * 2 * dv;
+  if (s >= NS) {
+    for (int64_t e = lane; e < DK; e += 64) {
+      rw[e] = 0.0f;
+      rw[DK + e] = 0.0f;
+      rw[2 * DK + e] = 1.0f;
+      rw[3 * DK + e] = 0.0f;
+    }
+    for (int64_t c = lane; c < dv; c += 64) {
+      cl[c] = 0.0f;
+      cl[dv + c] = 0.0f;
+    }
+    return;
+  }
   const int64_t b = bh / H, h = bh % H;
   const int64_t t = s / nh;
   const int sub = int(s - t * nh);
@@ -219,9 +188,6 @@ __global__ __launch_bounds__(256) void bwd_ops_kernel(Problem p, const In* __res
   const In* jv = static_cast<const In*>(p.j);
   const In* et = static_cast<const In*>(p.eta);
   auto ld = [](const In* y) { return IO<In>::ld(y); };
-  const int64_t xp = bh * (NS + 2 * kPad) + kPad + s;
-  float* rw = ws + L.rows + xp * 4 * DK;
-  float* cl = ws + L.cols + xp * 2 * dv;
   const int var = p.variant;
   // per-step scalars
   float sc = 0.0f, gate = 1.0f;
@@ -261,442 +227,404 @@ __global__ __launch_bounds__(256) void bwd_ops_kernel(Problem p, const In* __res
   }
 }
 
-// One step's operands in the rows-on-lanes layout: this lane's rows of a, b, alpha
-// (and q), and one column value (w or do of column col_lane(l mod CW)).
-template <int NR>
-struct Op {
-  float a[NR], b[NR], al[NR], q[NR];
-  float w, d;
+// ---- 2. record kernel -------------------------------------------------------------
+// One wave per (batch*head, chunk).
+template <int DK, int DV>
+__global__ __launch_bounds__(64) void bwd_rec_kernel(Problem p, float* __restrict__ ws) {
+  constexpr int KT = DK / 16, VT = DV / 16;
+  using R = Rec<DK, DV>;
+  __shared__ __align__(16) float Gs[kC * DK];  // G [step][channel]
+  __shared__ __align__(16) float Ms[256];
+  __shared__ __align__(16) float Ps[256];
+  __shared__ __align__(16) float Ts[256];
+  const int l = threadIdx.x, i = l & 15, g = l >> 4;
+  const BwdLayout L = bwd_layout(p.B, p.steps, p.H, DK, DV);
+  const int64_t item = blockIdx.x;  // bh * chunks + c
+  const int64_t bh = item / L.nc, c = item % L.nc;
+  const float* rb = ws + L.rows + (bh * L.rs + c * kC) * 4 * DK;  // step s of the chunk at rb + s 4 DK
+  const float* cb = ws + L.cols + (bh * L.rs + c * kC) * 2 * DV;
+  float* rec = ws + L.rec + item * R::size;
+
+  float gc[KT];  // G at the chunk's last step, channel 16t + i
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    float gv[4];
+    chunk_logdecay<DK>(rb, 16 * t + i, l, gv);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Gs[(4 * g + e) * DK + 16 * t + i] = gv[e];
+    gc[t] = __shfl(gv[3], 48 + i, 64);
+  }
+  __syncthreads();
+
+  // Grams in the row order: B~ = b e^(G - G_8), Q~ = q e^(G - G_8), A~ = a e^(G_8 - G)
+  float4v m = zero4(), pp = zero4();
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    const int ch = 16 * t + 4 * g;
+    const float4v av = ld4(rb + i * 4 * DK + ch);
+    const float4v bv = ld4(rb + i * 4 * DK + DK + ch);
+    const float4v qv = ld4(rb + i * 4 * DK + 3 * DK + ch);
+    const float4v gv = ld4(Gs + i * DK + ch);
+    const float4v gr = ld4(Gs + kRef * DK + ch);
+    float4v bt, qt, at;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float up = expf(gv[e] - gr[e]), dn = expf(gr[e] - gv[e]);
+      bt[e] = bv[e] * up;
+      qt[e] = qv[e] * up;
+      at[e] = av[e] * dn;
+    }
+    m = mma4(bt, at, m);   // M[4g+e][i] = B~[4g+e] . A~[i]
+    pp = mma4(qt, at, pp);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = 4 * g + e;
+    Ms[r * 16 + i] = r > i ? m[e] : 0.0f;
+    Ps[r * 16 + i] = r >= i ? pp[e] : 0.0f;
+  }
+  __syncthreads();
+
+  // T = (I + M)^-1 by forward substitution, column i in lane i (every lane group alike)
+  float tc[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float x = r == i ? 1.0f : 0.0f;
+#pragma unroll
+    for (int s = 0; s < r; ++s) x -= Ms[r * 16 + s] * tc[s];
+    tc[r] = x;
+  }
+  if (g == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Ts[r * 16 + i] = tc[r];
+  }
+  __syncthreads();
+  st4(rec + R::Tm + 4 * l, ld4(Ts + 4 * l));
+  st4(rec + R::Pm + 4 * l, ld4(Ps + 4 * l));
+  const float4v tA = ld4(Ts + i * 16 + 4 * g);  // T[i][4g+e]
+  const float4v pA = ld4(Ps + i * 16 + 4 * g);  // P[i][4g+e]
+
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    const int ch = 16 * t + i;
+    float4v bF, qF, aF;  // B+, Q+, A^ at (step 4g+e, channel ch)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int s = 4 * g + e;
+      const float gv = Gs[s * DK + ch];
+      const float eg = expf(gv), eh = expf(gc[t] - gv);
+      bF[e] = rb[s * 4 * DK + DK + ch] * eg;
+      qF[e] = rb[s * 4 * DK + 3 * DK + ch] * eg;
+      aF[e] = rb[s * 4 * DK + ch] * eh;
+    }
+    const float4v w = mma4(tA, bF, zero4());   // W = T B+ (fragment order)
+    const float4v wr = mma4(bF, tA, zero4());  // W^T: W in the row order
+    const float4v pw = mma4(pA, w, zero4());   // P W (fragment order)
+    float4v cm, ar;
+    const float4v av = ld4(rb + i * 4 * DK + 16 * t + 4 * g);
+    const float4v gv = ld4(Gs + i * DK + 16 * t + 4 * g);
+    const float4v ge = ld4(Gs + (kC - 1) * DK + 16 * t + 4 * g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      cm[e] = qF[e] - pw[e];
+      ar[e] = av[e] * expf(ge[e] - gv[e]);
+    }
+    st4(rec + R::Wf + t * 256 + 4 * l, w);
+    st4(rec + R::Wr + t * 256 + 4 * l, wr);
+    st4(rec + R::Af + t * 256 + 4 * l, aF);
+    st4(rec + R::Ar + t * 256 + 4 * l, ar);
+    st4(rec + R::Cf + t * 256 + 4 * l, cm);
+    if (g == 0) rec[R::Gm + ch] = expf(gc[t]);
+  }
+#pragma unroll
+  for (int vt = 0; vt < VT; ++vt) {
+    float4v wF;  // w at (step 4g+e, column 16vt+i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) wF[e] = cb[(4 * g + e) * 2 * DV + 16 * vt + i];
+    st4(rec + R::Uf + vt * 256 + 4 * l, mma4(tA, wF, zero4()));  // U~ = T W_v
+    st4(rec + R::Ur + vt * 256 + 4 * l, mma4(wF, tA, zero4()));  // U~ in the row order
+  }
+}
+
+// ---- 3. recursions ----------------------------------------------------------------
+// Blocks [0, B*H*dv/16): the state S_{c+1} = Gamma S_c + A^^T (U~ - W S_c), storing S_c.
+// Blocks [B*H*dv/16, 2 B*H*dv/16): its gradient D_{c-1} = Gamma D_c - W^T (A^ D_c) +
+// (Q+ - P W)^T dO_c from D = dL/dS_final, storing D_c; D_{-1} is dL/dS_0.
+// A block holds one 16-column slice (dk x 16) in accumulator tiles, its key tiles split
+// over up to four waves; the 16 x 16 products summed over the key channels (W S, A^ D)
+// are added up through LDS in wave order, one barrier a chunk. Each wave loads the next
+// chunk's record while it applies the current one.
+__host__ __device__ constexpr int chain_waves(int dk) { return dk / 16 < 4 ? dk / 16 : 4; }
+
+template <int TW>
+struct SOps {
+  float4v wr[TW], af[TW], gm[TW], uf;
+};
+template <int TW>
+struct GOps {
+  float4v ar[TW], wf[TW], cf[TW], gm[TW], dof;
 };
 
-// Inactive lanes (rows past dk) read row 0 and keep zeros.
-template <int NR, bool WQ, bool WW, bool WD>
-__device__ __forceinline__ void load_op(const float* rows, const float* cols, int64_t s, int64_t DK,
-                                        int64_t dv, int r0, bool act, int col, Op<NR>& o) {
-  const float* rw = rows + s * 4 * DK + (act ? r0 : 0);
-  float a[NR], b[NR], al[NR], q[NR];
-  if constexpr (NR == 2) {
-    const float2 x = *reinterpret_cast<const float2*>(rw);
-    const float2 y = *reinterpret_cast<const float2*>(rw + DK);
-    const float2 z = *reinterpret_cast<const float2*>(rw + 2 * DK);
-    a[0] = x.x, a[1] = x.y, b[0] = y.x, b[1] = y.y, al[0] = z.x, al[1] = z.y;
-    if constexpr (WQ) {
-      const float2 w = *reinterpret_cast<const float2*>(rw + 3 * DK);
-      q[0] = w.x, q[1] = w.y;
+template <int DK, int DV>
+__global__ __launch_bounds__(64 * chain_waves(DK)) void bwd_chain_kernel(Problem p, const float* __restrict__ dsf,
+                                                                         float* __restrict__ ds0, float* __restrict__ ws) {
+  constexpr int KT = DK / 16, VT = DV / 16, NW = chain_waves(DK), TW = KT / NW;
+  using R = Rec<DK, DV>;
+  __shared__ float4v xch[2][NW][64];
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6, g = l >> 4, i = l & 15;
+  const BwdLayout L = bwd_layout(p.B, p.steps, p.H, DK, DV);
+  const int64_t nbv = p.B * p.H * VT;
+  const bool grad = blockIdx.x >= nbv;
+  const int64_t y = grad ? blockIdx.x - nbv : blockIdx.x;
+  const int64_t bh = y / VT;
+  const int vt = int(y % VT);
+  const int64_t NC = L.nc;
+  const float* recs = ws + L.rec + bh * NC * R::size;
+  // barrier for the LDS exchange only: loads in flight stay in flight
+  auto lds_barrier = []() __attribute__((always_inline)) { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+  float4v X[TW];  // key tiles t = w TW + j of the slice
+  // element (row 16t + 4g + e, column 16vt + i) of a [dk][dv] state
+  const int64_t sbase = bh * DK * DV + (4 * g) * DV + 16 * vt + i;
+  if (!grad) {
+    const float* s0 = p.s0;
+#pragma unroll
+    for (int j = 0; j < TW; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) X[j][e] = s0 ? s0[sbase + (16 * (w * TW + j) + e) * DV] : 0.0f;
+    if (NC == 0) return;
+    auto load = [&](int64_t c, SOps<TW>& o) {
+      const float* r = recs + c * R::size;
+#pragma unroll
+      for (int j = 0; j < TW; ++j) {
+        const int t = w * TW + j;
+        o.wr[j] = ld4(r + R::Wr + t * 256 + 4 * l);
+        o.af[j] = ld4(r + R::Af + t * 256 + 4 * l);
+        o.gm[j] = ld4(r + R::Gm + 16 * t + 4 * g);
+      }
+      o.uf = ld4(r + R::Uf + vt * 256 + 4 * l);
+    };
+    SOps<TW> cur, nxt;
+    load(0, cur);
+    for (int64_t c = 0; c < NC; ++c) {
+      load(c + 1 < NC ? c + 1 : c, nxt);
+      float* so = ws + L.sst + (bh * NC + c) * KT * VT * 256;
+#pragma unroll
+      for (int j = 0; j < TW; ++j) st4(so + ((w * TW + j) * VT + vt) * 256 + 4 * l, X[j]);
+      float4v pu = zero4();
+#pragma unroll
+      for (int j = 0; j < TW; ++j) pu = mma4(cur.wr[j], X[j], pu);  // this wave's share of W S
+      xch[c & 1][w][l] = pu;
+      lds_barrier();
+      float4v u = cur.uf;  // U = U~ - W S
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) u -= xch[c & 1][w2][l];
+#pragma unroll
+      for (int j = 0; j < TW; ++j) X[j] = mma4(cur.af[j], u, X[j] * cur.gm[j]);
+      cur = nxt;
     }
   } else {
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      a[r] = rw[r], b[r] = rw[DK + r], al[r] = rw[2 * DK + r];
-      if constexpr (WQ) q[r] = rw[3 * DK + r];
-    }
-  }
+    for (int j = 0; j < TW; ++j)
 #pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    o.a[r] = act ? a[r] : 0.0f;
-    o.b[r] = act ? b[r] : 0.0f;
-    o.al[r] = act ? al[r] : 0.0f;
-    o.q[r] = WQ && act ? q[r] : 0.0f;
-  }
-  const float* cl = cols + s * 2 * dv + col;
-  o.w = WW ? cl[0] : 0.0f;
-  o.d = WD ? cl[dv] : 0.0f;
-}
-
-// S <- X + a u^T with X = Diag(alpha) S, u = w - X^T b (a forward step). Returns u of
-// column col_lane(l mod CW).
-template <int NR, int CW>
-__device__ __forceinline__ float fwd_step(float (&S)[NR][CW], const Op<NR>& o, int lane) {
-  float part[CW];
+      for (int e = 0; e < 4; ++e) X[j][e] = dsf ? dsf[sbase + (16 * (w * TW + j) + e) * DV] : 0.0f;
+    const float* cols = ws + L.cols + bh * L.rs * 2 * DV + DV + 16 * vt + i;  // do, column 16vt + i
+    auto load = [&](int64_t c, GOps<TW>& o) {
+      const float* r = recs + c * R::size;
 #pragma unroll
-  for (int c = 0; c < CW; ++c) part[c] = 0.0f;
+      for (int j = 0; j < TW; ++j) {
+        const int t = w * TW + j;
+        o.ar[j] = ld4(r + R::Ar + t * 256 + 4 * l);
+        o.wf[j] = ld4(r + R::Wf + t * 256 + 4 * l);
+        o.cf[j] = ld4(r + R::Cf + t * 256 + 4 * l);
+        o.gm[j] = ld4(r + R::Gm + 16 * t + 4 * g);
+      }
 #pragma unroll
-  for (int r = 0; r < NR; ++r)
+      for (int e = 0; e < 4; ++e) o.dof[e] = cols[(c * kC + 4 * g + e) * 2 * DV];
+    };
+    if (NC > 0) {
+      GOps<TW> cur, nxt;
+      load(NC - 1, cur);
+      for (int64_t c = NC - 1; c >= 0; --c) {
+        load(c > 0 ? c - 1 : c, nxt);
+        float* dO_ = ws + L.dst + (bh * NC + c) * KT * VT * 256;
 #pragma unroll
-    for (int c = 0; c < CW; ++c) {
-      S[r][c] *= o.al[r];
-      part[c] += o.b[r] * S[r][c];
-    }
-  const float u = o.w - col_sum<CW>(part, lane);
+        for (int j = 0; j < TW; ++j) st4(dO_ + ((w * TW + j) * VT + vt) * 256 + 4 * l, X[j]);
+        float4v px = zero4();
 #pragma unroll
-  for (int c = 0; c < CW; ++c) {
-    const float uc = col_bcast<CW>(u, c);
+        for (int j = 0; j < TW; ++j) px = mma4(cur.ar[j], X[j], px);  // this wave's share of A^ D
+        xch[c & 1][w][l] = px;
+        lds_barrier();
+        float4v nx = -xch[c & 1][0][l];  // -A^ D
 #pragma unroll
-    for (int r = 0; r < NR; ++r) S[r][c] += o.a[r] * uc;
-  }
-  return u;
-}
-
-// G <- Diag(alpha) (G' - b dw^T), G' = G + q do^T, dw = G'^T a (a backward step of the
-// state gradient alone).
-template <int NR, int CW>
-__device__ __forceinline__ void grad_step(float (&G)[NR][CW], const Op<NR>& o, int lane) {
-  float part[CW];
+        for (int w2 = 1; w2 < NW; ++w2) nx -= xch[c & 1][w2][l];
 #pragma unroll
-  for (int c = 0; c < CW; ++c) {
-    const float dc = col_bcast<CW>(o.d, c);
-    part[c] = 0.0f;
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      G[r][c] += o.q[r] * dc;
-      part[c] += G[r][c] * o.a[r];
-    }
-  }
-  const float dw = col_sum<CW>(part, lane);
-#pragma unroll
-  for (int c = 0; c < CW; ++c) {
-    const float dwc = col_bcast<CW>(dw, c);
-#pragma unroll
-    for (int r = 0; r < NR; ++r) G[r][c] = o.al[r] * (G[r][c] - o.b[r] * dwc);
-  }
-}
-
-// ---- 2. chain kernel ----------------------------------------------------------------
-// Four waves per workgroup, one per CW-column slice; the first B*H*dv/CW waves run S
-// forward from s0, the rest run the state gradient backward from dL/dS_T.
-template <int DK, int CW>
-__global__ __launch_bounds__(256) void bwd_chain_kernel(Problem p, const float* __restrict__ dsf,
-                                                        float* __restrict__ ds0, float* __restrict__ ws) {
-  constexpr int NR = rows_per_lane(DK);
-  constexpr int D = kChainRing;
-  const int lane = threadIdx.x & 63;
-  const int64_t NS = p.steps, H = p.H, dv = p.dv;
-  const BwdLayout L = bwd_layout(p.B, NS, H, DK, dv);
-  const int ncs = int(dv / CW);
-  const int64_t nw = p.B * H * ncs;  // waves per chain
-  const int64_t wid = int64_t(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const bool grad = wid >= nw;
-  const int64_t w2 = grad ? wid - nw : wid;
-  const int64_t bh = w2 / ncs;
-  const int cbase = int(w2 % ncs) * CW;
-  const int r0 = lane * NR;
-  const bool act = DK >= 64 || r0 < DK;
-  const int col = cbase + col_lane<CW>(lane & (CW - 1));
-  // step s of this head at rows + s * 4 dk (s in [-kPad, NS + kPad))
-  const float* rows = ws + L.rows + (bh * (NS + 2 * kPad) + kPad) * 4 * DK;
-  const float* cols = ws + L.cols + (bh * (NS + 2 * kPad) + kPad) * 2 * dv;
-  const size_t sbase = size_t(bh) * DK * size_t(dv);
-  float* ckp = ws + (grad ? L.gk : L.ck) + bh * L.nck * DK * dv;
-  const float* init = grad ? dsf : p.s0;
-
-  float X[NR][CW];
-#pragma unroll
-  for (int r = 0; r < NR; ++r)
-#pragma unroll
-    for (int c = 0; c < CW; ++c)
-      X[r][c] = (act && init) ? init[sbase + size_t(r0 + r) * dv + cbase + c] : 0.0f;
-  auto store = [&](float* dst) __attribute__((always_inline)) {
-    if (!act) return;
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      float* d = dst + size_t(r0 + r) * dv + cbase;
-      if constexpr (CW % 4 == 0) {
-#pragma unroll
-        for (int c = 0; c < CW; c += 4)
-          *reinterpret_cast<float4*>(d + c) = make_float4(X[r][c], X[r][c + 1], X[r][c + 2], X[r][c + 3]);
-      } else {
-#pragma unroll
-        for (int c = 0; c < CW; ++c) d[c] = X[r][c];
+        for (int j = 0; j < TW; ++j) X[j] = mma4(cur.wf[j], nx, mma4(cur.cf[j], cur.dof, X[j] * cur.gm[j]));
+        cur = nxt;
       }
     }
-  };
-
-  // Operands of the next D steps stay in flight in a register ring. The steady state
-  // runs whole groups of D steps aligned to multiples of D (kCB is one), so its loads
-  // are unconditional and each step waits only for its own slot; the ragged end
-  // (fewer than D steps) runs separately.
-  static_assert(kCB % D == 0, "checkpoint interval is a multiple of the ring depth");
-  if (NS == 0) {  // nothing to run: dL/dS_0 is dL/dS_T
-    if (grad && ds0) store(ds0 + sbase);
-    return;
-  }
-  Op<NR> ring[D];
-  const int64_t nfull = NS / D;  // whole groups [D g, D g + D)
-  const int64_t tail0 = nfull * D;
-  if (!grad) {
+    if (ds0) {
 #pragma unroll
-    for (int i = 0; i < D; ++i) {  // in slot order, as the loop refills them
-      load_op<NR, false, true, false>(rows, cols, i, DK, dv, r0, act, col, ring[i]);
-      asm volatile("" ::: "memory");
-    }
-    for (int64_t g = 0; g < nfull; ++g) {
-      const int64_t s0 = g * D;
-      if (s0 % kCB == 0) store(ckp + (s0 / kCB) * DK * dv);
-      // opaque to the optimizer, which would otherwise turn the refills back into
-      // loads at the point of use (the next group's addresses are the same)
-      int64_t nb = s0 + D;
-      asm volatile("" : "+s"(nb));
+      for (int j = 0; j < TW; ++j)
 #pragma unroll
-      for (int i = 0; i < D; ++i) {
-        fwd_step<NR, CW>(X, ring[i], lane);
-        load_op<NR, false, true, false>(rows, cols, nb + i, DK, dv, r0, act, col, ring[i]);
-        __builtin_amdgcn_sched_barrier(0);  // keep the refill here, D steps ahead of its use
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < D; ++i) {  // the ring holds steps tail0 .. tail0 + D - 1
-      const int64_t s = tail0 + i;
-      if (s < NS) {
-        if (s % kCB == 0) store(ckp + (s / kCB) * DK * dv);
-        fwd_step<NR, CW>(X, ring[i], lane);
-      }
-    }
-    return;
-  }
-  // the ragged end first (steps NS - 1 down to tail0), loading as it goes
-  for (int64_t s = NS - 1; s >= tail0; --s) {
-    Op<NR> o;
-    load_op<NR, true, false, true>(rows, cols, s, DK, dv, r0, act, col, o);
-    if (s == NS - 1 || (s + 1) % kCB == 0) store(ckp + (s / kCB) * DK * dv);
-    grad_step<NR, CW>(X, o, lane);
-  }
-#pragma unroll
-  for (int i = 0; i < D; ++i) {
-    load_op<NR, true, false, true>(rows, cols, tail0 - 1 - i, DK, dv, r0, act, col, ring[i]);
-    asm volatile("" ::: "memory");
-  }
-  for (int64_t g = nfull - 1; g >= 0; --g) {
-    const int64_t s0 = g * D + D - 1;  // an interval's last step can only be a group's first
-    if (s0 == NS - 1 || (s0 + 1) % kCB == 0) store(ckp + (s0 / kCB) * DK * dv);
-    int64_t nb = s0 - D;
-    asm volatile("" : "+s"(nb));
-#pragma unroll
-    for (int i = 0; i < D; ++i) {
-      grad_step<NR, CW>(X, ring[i], lane);
-      load_op<NR, true, false, true>(rows, cols, nb - i, DK, dv, r0, act, col, ring[i]);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int e = 0; e < 4; ++e) ds0[sbase + (16 * (w * TW + j) + e) * DV] = X[j][e];
     }
   }
-  if (ds0) store(ds0 + sbase);
 }
 
-// ---- 3. interval kernel -------------------------------------------------------------
-// WPG waves per workgroup, one per 16-column slice of a group of slices, persistent
-// over the items (batch*head, interval, slice group). Pass A runs the interval forward
-// from its stored S and keeps the state before every kSub-step block in the wave's
-// slot; pass B takes the blocks in reverse: it recomputes the block's kSub states into
-// the wave's LDS and walks them back. The waves' row partials of a step are summed in
-// LDS in wave order (one barrier a step) and written once per group.
-template <int DK, int WPG>
-__global__ __launch_bounds__(64 * WPG) void bwd_interval_kernel(Problem p, float* __restrict__ ws) {
-  constexpr int NR = rows_per_lane(DK);
-  constexpr int CW = kCW;
-  constexpr int NV = NR * CW / 4;  // float4 per lane of a state
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t NS = p.steps, H = p.H, dv = p.dv;
-  const int ngroups = int(dv / CW) / WPG;
-  const BwdLayout L = bwd_layout(p.B, NS, H, DK, dv);
-  const int64_t bth = p.B * NS * H;  // step rows
-  const int r0 = lane * NR;
-  const bool act = DK >= 64 || r0 < DK;
-  const int lc = col_lane<CW>(lane & (CW - 1));
-  float4* slot = reinterpret_cast<float4*>(ws + L.sub) + (int64_t(blockIdx.x) * WPG + wave) * (kCB / kSub) * NV * 64;
-  __shared__ float4 sts_all[WPG][kSub * NV * 64];  // each wave's block states, lane order
-  __shared__ float xch[WPG > 1 ? 2 : 1][WPG][4][DK];  // row partials of a step, by parity
-  float4* sts = sts_all[wave];
-  int par = 0;  // exchange buffer of the next step (the same sequence in every wave)
+// ---- 4. intra-chunk gradients -------------------------------------------------------
+// One wave per (batch*head, chunk): S (state before the chunk) and D (dL/dS after it)
+// from the recursions, the chunk's record and operands; writes every step's dq, da,
+// db, dalpha and dw.
+template <int DK, int DV>
+__global__ __launch_bounds__(64) void bwd_intra_kernel(Problem p, float* __restrict__ ws) {
+  constexpr int KT = DK / 16, VT = DV / 16;
+  using R = Rec<DK, DV>;
+  const int l = threadIdx.x, i = l & 15, g = l >> 4;
+  const BwdLayout L = bwd_layout(p.B, p.steps, p.H, DK, DV);
+  const int64_t NS = p.steps;
+  const int64_t item = blockIdx.x;
+  const int64_t bh = item / L.nc, c = item % L.nc;
+  const float* rb = ws + L.rows + (bh * L.rs + c * kC) * 4 * DK;
+  const float* cb = ws + L.cols + (bh * L.rs + c * kC) * 2 * DV;
+  const float* rec = ws + L.rec + item * R::size;
+  const float* sS = ws + L.sst + item * KT * VT * 256;
+  const float* sD = ws + L.dst + item * KT * VT * 256;
+
+  // U in the row order, tile vt: U[i][16vt + 4g + e]  (U^T = U~^T - S^T W^T)
+  float4v ut[VT];
+#pragma unroll
+  for (int vt = 0; vt < VT; ++vt) {
+    float4v a = -ld4(rec + R::Ur + vt * 256 + 4 * l);
+#pragma unroll
+    for (int t = 0; t < KT; ++t) a = mma4(ld4(sS + (t * VT + vt) * 256 + 4 * l), ld4(rec + R::Wr + t * 256 + 4 * l), a);
+    ut[vt] = -a;
+  }
+  // dU = A^ D + P^T dO (fragment order), then dR^T = dU^T T: dR[i][16vt + 4g + e]
+  float4v pF, tF;  // P[4g+e][i], T[4g+e][i]
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    pF[e] = rec[R::Pm + (4 * g + e) * 16 + i];
+    tF[e] = rec[R::Tm + (4 * g + e) * 16 + i];
+  }
+  float4v rt[VT], doA[VT];  // dR and dO in the row order
+  const bool row_live = c * kC + i < NS;
+#pragma unroll
+  for (int vt = 0; vt < VT; ++vt) {
+    float4v x = zero4();
+#pragma unroll
+    for (int t = 0; t < KT; ++t) x = mma4(ld4(rec + R::Ar + t * 256 + 4 * l), ld4(sD + (t * VT + vt) * 256 + 4 * l), x);
+    float4v dF;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dF[e] = cb[(4 * g + e) * 2 * DV + DV + 16 * vt + i];
+    x = mma4(pF, dF, x);
+    rt[vt] = mma4(x, tF, zero4());
+    doA[vt] = ld4(cb + i * 2 * DV + DV + 16 * vt + 4 * g);
+    if (row_live) st4(ws + L.dw + (bh * NS + c * kC + i) * DV + 16 * vt + 4 * g, rt[vt]);
+  }
+  // dP = tril(dO U^T), dM = -strict_tril(dR U^T), each in both orientations:
+  // dp[e] = dP[4g+e][i], dpt[e] = dP[i][4g+e]; likewise dm, dmt
+  float4v dp = zero4(), dpt = zero4(), dm = zero4(), dmt = zero4();
+#pragma unroll
+  for (int vt = 0; vt < VT; ++vt) {
+    dp = mma4(doA[vt], ut[vt], dp);
+    dpt = mma4(ut[vt], doA[vt], dpt);
+    dm = mma4(rt[vt], ut[vt], dm);
+    dmt = mma4(ut[vt], rt[vt], dmt);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = 4 * g + e;
+    dp[e] = r >= i ? dp[e] : 0.0f;
+    dpt[e] = i >= r ? dpt[e] : 0.0f;
+    dm[e] = r > i ? -dm[e] : 0.0f;
+    dmt[e] = i > r ? -dmt[e] : 0.0f;
+  }
+
   float* part = ws + L.part;
-  float* dwg = ws + L.dw;
-
-  using St = float[NR][CW];
-  auto save = [&](float4* dst, const St& S) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int r = (4 * i) / CW, c = (4 * i) % CW;
-      dst[i * 64 + lane] = make_float4(S[r][c], S[r][c + 1], S[r][c + 2], S[r][c + 3]);
-    }
-  };
-  auto restore = [&](const float4* src, St& S) __attribute__((always_inline)) {
+  for (int t = 0; t < KT; ++t) {
+    const int ch = 16 * t + i;
+    // dO S^T, dR S^T, U D^T at (step 4g+e, channel ch); sum over v of D . S for channel ch
+    float4v qs = zero4(), rs = zero4(), ud = zero4();
+    float rsum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int r = (4 * i) / CW, c = (4 * i) % CW;
-      const float4 x = src[i * 64 + lane];
-      S[r][c] = x.x, S[r][c + 1] = x.y, S[r][c + 2] = x.z, S[r][c + 3] = x.w;
-    }
-  };
-
-  for (int64_t item = blockIdx.x; item < L.items; item += gridDim.x) {
-    const int grp = int(item % ngroups);
-    const int slice = grp * WPG + wave;
-    const int64_t rest = item / ngroups;
-    const int64_t ci = rest % L.nck, bh = rest / L.nck;
-    const int cbase = slice * CW;
-    const int64_t t0 = ci * kCB, t1 = min(NS, t0 + kCB);
-    const int nb = int((t1 - t0 + kSub - 1) / kSub);
-    const float* rows = ws + L.rows + (bh * (NS + 2 * kPad) + kPad) * 4 * DK;
-    const float* cols = ws + L.cols + (bh * (NS + 2 * kPad) + kPad) * 2 * dv;
-    auto load_blk = [&](int m, Op<NR> (&o)[kSub]) __attribute__((always_inline)) {
+    for (int vt = 0; vt < VT; ++vt) {
+      // element (row 16t + i, column 16vt + 4g + e) of a fragment-order tile
+      const float* ts = sS + (t * VT + vt) * 256 + (i >> 2) * 64 + 16 * g + (i & 3);
+      const float* td = sD + (t * VT + vt) * 256 + (i >> 2) * 64 + 16 * g + (i & 3);
+      float4v sT, dT;
 #pragma unroll
-      for (int i = 0; i < kSub; ++i) {
-        // past the interval's end: the next steps or padding, never used
-        const int64_t s = t0 + int64_t(m) * kSub + i;
-        load_op<NR, true, true, true>(rows, cols, s, DK, dv, r0, act, cbase + lc, o[i]);
+      for (int e = 0; e < 4; ++e) {
+        sT[e] = ts[4 * e];
+        dT[e] = td[4 * e];
+        rsum += sT[e] * dT[e];
       }
-    };
-
-    float S[NR][CW], G[NR][CW];
-    {
-      const float* sck = ws + L.ck + (bh * L.nck + ci) * DK * dv + cbase;
-      const float* gck = ws + L.gk + (bh * L.nck + ci) * DK * dv + cbase;
-#pragma unroll
-      for (int r = 0; r < NR; ++r)
-#pragma unroll
-        for (int c = 0; c < CW; c += 4) {
-          const float4 x = act ? *reinterpret_cast<const float4*>(sck + size_t(r0 + r) * dv + c) : float4{};
-          const float4 y = act ? *reinterpret_cast<const float4*>(gck + size_t(r0 + r) * dv + c) : float4{};
-          S[r][c] = x.x, S[r][c + 1] = x.y, S[r][c + 2] = x.z, S[r][c + 3] = x.w;
-          G[r][c] = y.x, G[r][c + 1] = y.y, G[r][c + 2] = y.z, G[r][c + 3] = y.w;
-        }
+      qs = mma4(doA[vt], sT, qs);
+      rs = mma4(rt[vt], sT, rs);
+      ud = mma4(ut[vt], dT, ud);
     }
-
-    // pass A: blocks 0 .. nb-2 forward, the state before each kept in the slot; S
-    // ends as the state before block nb-1, and cur holds that block's operands
-    Op<NR> cur[kSub], nxt[kSub];
-    load_blk(0, cur);
-    for (int m = 0; m + 1 < nb; ++m) {
-      load_blk(m + 1, nxt);
-      save(slot + int64_t(m) * NV * 64, S);
+    rsum = sum_over_groups(rsum);
+    float gv[4];
+    chunk_logdecay<DK>(rb, ch, l, gv);
+    const float gr = __shfl(gv[0], 32 + i, 64);  // step 8
+    const float ge = __shfl(gv[3], 48 + i, 64);  // step 15
+    float4v av, bv, qv, alv, eg, eu, ed, eh, at, bt, qt;
 #pragma unroll
-      for (int i = 0; i < kSub; ++i) fwd_step<NR, CW>(S, cur[i], lane);  // full block (m < nb - 1)
-#pragma unroll
-      for (int i = 0; i < kSub; ++i) cur[i] = nxt[i];
+    for (int e = 0; e < 4; ++e) {
+      const float* rr = rb + (4 * g + e) * 4 * DK + ch;
+      av[e] = rr[0];
+      bv[e] = rr[DK];
+      alv[e] = rr[2 * DK];
+      qv[e] = rr[3 * DK];
+      eg[e] = expf(gv[e]);
+      eu[e] = expf(gv[e] - gr);
+      ed[e] = expf(gr - gv[e]);
+      eh[e] = expf(ge - gv[e]);
+      at[e] = av[e] * ed[e];
+      bt[e] = bv[e] * eu[e];
+      qt[e] = qv[e] * eu[e];
     }
-
-    // pass B: blocks in reverse; the last one (possibly short) first, so that the
-    // loop over whole blocks has no conditional memory operation (each block waits
-    // only for its own prefetched operands)
-    auto run_block = [&](const int m, auto whole) __attribute__((always_inline)) {
-      constexpr bool W = decltype(whole)::value;
-      const int mp = m > 0 ? m - 1 : 0;  // prefetch (block 0 again at the end: unused)
-      load_blk(mp, nxt);
-      float Sn[NR][CW];
-      restore(slot + int64_t(mp) * NV * 64, Sn);
-      const int64_t sb = t0 + int64_t(m) * kSub;
-      const int n = W ? kSub : int(min<int64_t>(kSub, t1 - sb));
-      // the state before each step of the block, in this wave's LDS, and each step's u
-      // (this lane's column); the block's last step runs too, for its u
-      float ul[kSub];
+    const float4v pa = mma4(dpt, at, zero4());        // dP A~
+    const float4v ma = mma4(dmt, at, zero4());        // dM A~
+    const float4v aa = mma4(dm, bt, mma4(dp, qt, zero4()));  // dP^T Q~ + dM^T B~
+    float4v dq, da, db, dG;
+    float hs = 0.0f;
 #pragma unroll
-      for (int i = 0; i < kSub; ++i) {
-        save(sts + i * NV * 64, S);
-        ul[i] = (W || i < n) ? fwd_step<NR, CW>(S, cur[i], lane) : 0.0f;
+    for (int e = 0; e < 4; ++e) {
+      dq[e] = qs[e] * eg[e] + pa[e] * eu[e];
+      db[e] = ma[e] * eu[e] - rs[e] * eg[e];
+      const float dh = ud[e] * eh[e];
+      da[e] = aa[e] * ed[e] + dh;
+      hs += av[e] * dh;
+      dG[e] = qv[e] * dq[e] + bv[e] * db[e] - av[e] * da[e];
+    }
+    hs = sum_over_groups(hs);
+    dG[3] += g == 3 ? hs + expf(ge) * rsum : 0.0f;  // G_C: the A^ and Gamma terms
+    float suf[4];
+    suf[3] = dG[3];
+#pragma unroll
+    for (int e = 2; e >= 0; --e) suf[e] = dG[e] + suf[e + 1];
+    const float later = group_suffix(suf[0], l);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t s = c * kC + 4 * g + e;
+      if (s < NS) {
+        float* pr = part + (bh * NS + s) * 4 * DK + ch;
+        pr[0] = dq[e];
+        pr[DK] = da[e];
+        pr[2 * DK] = db[e];
+        pr[3 * DK] = (suf[e] + later) / alv[e];
       }
-      auto back = [&](const int i) __attribute__((always_inline)) {
-        const Op<NR>& o = cur[i];
-        float Sp[NR][CW];
-        restore(sts + i * NV * 64, Sp);
-        const int64_t s = sb + i;
-        float X[NR][CW];
-#pragma unroll
-        for (int r = 0; r < NR; ++r)
-#pragma unroll
-          for (int c = 0; c < CW; ++c) X[r][c] = o.al[r] * Sp[r][c];
-        float u = ul[i];
-        // u^T do over the slice's columns (lanes 0..15 of every row hold distinct ones)
-        float udo = u * o.d;
-        udo = pair_sum<1>(udo);
-        udo = pair_sum<2>(udo);
-        udo = pair_sum<4>(udo);
-        udo = pair_sum<8>(udo);
-        // dq = S_t do = X do + a (u^T do); G += q do^T; dw = G^T a
-        float dq[NR], gw[CW];
-#pragma unroll
-        for (int r = 0; r < NR; ++r) dq[r] = o.a[r] * udo;
-#pragma unroll
-        for (int c = 0; c < CW; ++c) {
-          const float dc = col_bcast<CW>(o.d, c);
-          gw[c] = 0.0f;
-#pragma unroll
-          for (int r = 0; r < NR; ++r) {
-            dq[r] += X[r][c] * dc;
-            G[r][c] += o.q[r] * dc;
-            gw[c] += G[r][c] * o.a[r];
-          }
-        }
-        const float dw = col_sum<CW>(gw, lane);
-        asm volatile("" : "+v"(u));  // broadcast u here, after the reduction
-        // da = G u; db = -X dw; dX = G - b dw^T; dalpha = rowsum(dX . S_{t-1}); G = Diag(alpha) dX
-        float da[NR], db[NR], dal[NR];
-#pragma unroll
-        for (int r = 0; r < NR; ++r) da[r] = db[r] = dal[r] = 0.0f;
-#pragma unroll
-        for (int c = 0; c < CW; ++c) {
-          const float uc = col_bcast<CW>(u, c);
-          const float dwc = col_bcast<CW>(dw, c);
-#pragma unroll
-          for (int r = 0; r < NR; ++r) {
-            da[r] += G[r][c] * uc;
-            db[r] -= X[r][c] * dwc;
-            const float dX = G[r][c] - o.b[r] * dwc;
-            dal[r] += dX * Sp[r][c];
-            G[r][c] = o.al[r] * dX;
-          }
-        }
-        const int64_t pr = bh * NS + s;  // this head's step s
-        if (lane < CW) dwg[pr * dv + cbase + lc] = dw;
-        float* pw = part + (int64_t(grp) * bth + pr) * 4 * DK;
-        if constexpr (WPG == 1) {
-          if (act) {
-#pragma unroll
-            for (int r = 0; r < NR; ++r) {
-              pw[r0 + r] = dq[r];
-              pw[DK + r0 + r] = da[r];
-              pw[2 * DK + r0 + r] = db[r];
-              pw[3 * DK + r0 + r] = dal[r];
-            }
-          }
-        } else {
-          float(*xb)[4][DK] = xch[par];
-          if (act) {
-#pragma unroll
-            for (int r = 0; r < NR; ++r) {
-              xb[wave][0][r0 + r] = dq[r];
-              xb[wave][1][r0 + r] = da[r];
-              xb[wave][2][r0 + r] = db[r];
-              xb[wave][3][r0 + r] = dal[r];
-            }
-          }
-          __syncthreads();
-          // the sum over the group's slices, one quantity per wave (two for WPG = 2)
-#pragma unroll
-          for (int q = wave; q < 4; q += WPG) {
-#pragma unroll
-            for (int row = lane; row < DK; row += 64) {
-              float sum = xb[0][q][row];
-#pragma unroll
-              for (int w = 1; w < WPG; ++w) sum += xb[w][q][row];
-              pw[q * DK + row] = sum;
-            }
-          }
-          par ^= 1;
-        }
-      };
-      static_assert(kSub == 4, "the reverse walk below is written out for four steps");
-      if (W || n > 3) back(3);
-      if (W || n > 2) back(2);
-      if (W || n > 1) back(1);
-      back(0);
-#pragma unroll
-      for (int i = 0; i < kSub; ++i) cur[i] = nxt[i];
-#pragma unroll
-      for (int r = 0; r < NR; ++r)
-#pragma unroll
-        for (int c = 0; c < CW; ++c) S[r][c] = Sn[r][c];
-    };
-    run_block(nb - 1, std::false_type{});
-    for (int m = nb - 2; m >= 0; --m) run_block(m, std::true_type{});
+    }
   }
 }
 
-// ---- 4. reduce kernel -------------------------------------------------------------
-// One wave per step row: the partials summed over the slices in order, then the
-// variant's chain rule.
+// ---- 5. reduce kernel -------------------------------------------------------------
+// One wave per step row: the variant's chain rule.
 template <typename In, int DK>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(Problem p, GradPtrs g, const float* __restrict__ ws) {
   const int lane = threadIdx.x & 63;
   const int64_t T = p.T, H = p.H, dv = p.dv;
-  const int ns = int(dv / kCW) / slices_per_group(dv);  // partial sets (slice groups)
   const int nh = p.n_h;
   const int64_t bth = p.B * T * H * nh;  // step rows
   const BwdLayout L = bwd_layout(p.B, p.steps, H, DK, dv);
@@ -711,25 +639,20 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(Problem p, GradPtrs g, 
   auto ld = [](const In* x) { return IO<In>::ld(x); };
   const int64_t stride = int64_t(gridDim.x) * (blockDim.x / 64);
   for (int64_t th = int64_t(blockIdx.x) * (blockDim.x / 64) + (threadIdx.x >> 6); th < bth; th += stride) {
-    // the partials of step row th = ((b T + t) H + h) n_h + sub sit at head b H + h, step t n_h + sub
+    // the gradients of step row th = ((b T + t) H + h) n_h + sub sit at head b H + h, step t n_h + sub
     const int64_t tok = th / nh;
     const int64_t bt = tok / H;
     const int64_t prow = ((bt / T) * H + tok % H) * p.steps + (bt % T) * nh + (th - tok * nh);
+    const float* pr = part + prow * 4 * DK;
     if (p.variant == GDN_VARIANT_DELTAPRODUCT) {  // th is a step row (token x n_h + step)
       const int sub = int(th - tok * nh);
       const float bt = ld(be + th);
       float sb = 0.0f, sal = 0.0f;
       for (int r = lane; r < DK; r += 64) {
-        float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int w2 = 0; w2 < ns; ++w2) {
-          const float* pr = part + (int64_t(w2) * bth + prow) * 4 * DK;
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd) s4[qd] += pr[qd * DK + r];
-        }
-        g.dk[th * DK + r] = s4[1] + bt * s4[2];
-        sb += ld(k + th * DK + r) * s4[2];
-        sal += s4[3];
-        if (sub == nh - 1) g.dq[tok * DK + r] = s4[0];
+        g.dk[th * DK + r] = pr[DK + r] + bt * pr[2 * DK + r];
+        sb += ld(k + th * DK + r) * pr[2 * DK + r];
+        sal += pr[3 * DK + r];
+        if (sub == nh - 1) g.dq[tok * DK + r] = pr[r];
       }
       for (int cc = lane; cc < dv; cc += 64) {
         const float dw = dwg[prow * dv + cc];
@@ -748,15 +671,9 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(Problem p, GradPtrs g, 
     const float sbeta = (p.variant == GDN_VARIANT_KDA || p.variant == GDN_VARIANT_GDN) ? sqrtf(ld(be + th)) : 1.0f;
     const float e = p.variant == GDN_VARIANT_ASYM ? ld(et + th) : 0.0f;
     for (int r = lane; r < DK; r += 64) {
-      float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      for (int w2 = 0; w2 < ns; ++w2) {
-        const float* pr = part + (int64_t(w2) * bth + prow) * 4 * DK;
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd) s4[qd] += pr[qd * DK + r];
-      }
-      const float dab = s4[1] + s4[2], dal = s4[3];
+      const float dab = pr[DK + r] + pr[2 * DK + r], dal = pr[3 * DK + r];
       const int64_t ir = th * DK + r;
-      g.dq[ir] = s4[0];
+      g.dq[ir] = pr[r];
       const float kr = ld(k + ir);
       if (p.variant == GDN_VARIANT_FG2) {
         const float s = sqrtf(ld(be + ir));
@@ -766,10 +683,10 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(Problem p, GradPtrs g, 
         if (!bev) db += ld(v + th * dv + r) * dwg[prow * dv + r];  // shared beta (dk == dv)
         g.dbeta[ir] = db / (2.0f * s);
       } else if (p.variant == GDN_VARIANT_ASYM) {
-        g.dk[ir] = s4[1];
-        g.dj[ir] = e * s4[2];
+        g.dk[ir] = pr[DK + r];
+        g.dj[ir] = e * pr[2 * DK + r];
         g.dalpha[ir] = dal;
-        sj += ld(jv + ir) * s4[2];
+        sj += ld(jv + ir) * pr[2 * DK + r];
       } else {
         g.dk[ir] = sbeta * dab;
         sk += kr * dab;
@@ -811,34 +728,34 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(Problem p, GradPtrs g, 
   }
 }
 
-template <typename In, int DK>
-int launch_dk(const Problem& p, const In* dO, const float* dsf, const GradPtrs& g, float* ws, hipStream_t s) {
-  const BwdLayout L = bwd_layout(p.B, p.steps, p.H, DK, p.dv);
-  const int64_t nsteps = p.B * p.H * p.steps;
-  if (nsteps > 0) {
-    // one wave a step: the grid fits 32 bits for any workspace that can exist (at least
-    // 16 dk + 8 dv bytes a step, so 2^34 steps would need hundreds of terabytes)
-    bwd_ops_kernel<In><<<dim3(unsigned((nsteps + 3) / 4)), dim3(256), 0, s>>>(p, dO, ws);
-    int e = int(hipGetLastError());
-    if (e != 0) return e;
+template <typename In, int DK, int DV>
+int launch_shape(const Problem& p, const In* dO, const float* dsf, const GradPtrs& g, float* ws, hipStream_t s) {
+  const BwdLayout L = bwd_layout(p.B, p.steps, p.H, DK, DV);
+  const int64_t bh = p.B * p.H;
+  const int64_t items = bh * L.nc;  // (batch*head, chunk) pairs
+  // grids: B*H*steps <= 2^33 (checked by the caller), so every one fits 32 bits
+  if (items > 0) {
+    bwd_ops_kernel<In><<<dim3(unsigned((items * kC + 3) / 4)), dim3(256), 0, s>>>(p, dO, ws);
+    bwd_rec_kernel<DK, DV><<<dim3(unsigned(items)), dim3(64), 0, s>>>(p, ws);
   }
-  // dv / kChainCW is a multiple of 4: whole workgroups, and the S and G halves split
-  // between workgroups
-  const int64_t chain_waves = 2 * p.B * p.H * (p.dv / kChainCW);
-  bwd_chain_kernel<DK, kChainCW><<<dim3(unsigned(chain_waves / 4)), dim3(256), 0, s>>>(p, dsf, g.ds0, ws);
-  int e = int(hipGetLastError());
-  if (e != 0 || nsteps == 0) return e;
-  switch (slices_per_group(p.dv)) {
-    case 1: bwd_interval_kernel<DK, 1><<<dim3(unsigned(L.slots)), dim3(64), 0, s>>>(p, ws); break;
-    case 2: bwd_interval_kernel<DK, 2><<<dim3(unsigned(L.slots)), dim3(128), 0, s>>>(p, ws); break;
-    default: bwd_interval_kernel<DK, 4><<<dim3(unsigned(L.slots)), dim3(256), 0, s>>>(p, ws); break;
-  }
-  e = int(hipGetLastError());
-  if (e != 0) return e;
+  bwd_chain_kernel<DK, DV><<<dim3(unsigned(2 * bh * (DV / 16))), dim3(64 * chain_waves(DK)), 0, s>>>(p, dsf, g.ds0, ws);
+  if (items == 0) return int(hipGetLastError());
+  bwd_intra_kernel<DK, DV><<<dim3(unsigned(items)), dim3(64), 0, s>>>(p, ws);
   const int64_t waves = p.B * p.T * p.H * p.n_h;
   const int64_t blocks = (waves + 3) / 4;
   bwd_reduce_kernel<In, DK><<<dim3(unsigned(blocks < (int64_t(1) << 20) ? blocks : (int64_t(1) << 20))), dim3(256), 0, s>>>(p, g, ws);
   return int(hipGetLastError());
+}
+
+template <typename In, int DK>
+int launch_dk(const Problem& p, const In* dO, const float* dsf, const GradPtrs& g, float* ws, hipStream_t s) {
+  switch (p.dv) {
+    case 16: return launch_shape<In, DK, 16>(p, dO, dsf, g, ws, s);
+    case 32: return launch_shape<In, DK, 32>(p, dO, dsf, g, ws, s);
+    case 64: return launch_shape<In, DK, 64>(p, dO, dsf, g, ws, s);
+    case 128: return launch_shape<In, DK, 128>(p, dO, dsf, g, ws, s);
+    default: return int(hipErrorInvalidValue);
+  }
 }
 
 template <typename In>
