@@ -365,6 +365,13 @@ struct GOps {
   float4v ar[TW], wf[TW], cf[TW], gm[TW], dof;
 };
 
+// Records in flight a wave (a register ring). Refills sit right after the step that
+// frees their slot: a scheduling barrier keeps the compiler from moving them, and
+// the refill index is hidden from the optimizer, which would otherwise turn a refill
+// back into a load at the point of use. Whole ring groups run with unconditional
+// refills (clamped to the last chunk), the remainder without any.
+constexpr int kRing = 4;
+
 template <int DK, int DV>
 __global__ __launch_bounds__(64 * chain_waves(DK)) void bwd_chain_kernel(Problem p, const float* __restrict__ dsf,
                                                                          float* __restrict__ ds0, float* __restrict__ ws) {
@@ -374,11 +381,17 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void bwd_chain_kernel(Problem
   const int l = threadIdx.x & 63, w = threadIdx.x >> 6, g = l >> 4, i = l & 15;
   const BwdLayout L = bwd_layout(p.B, p.steps, p.H, DK, DV);
   const int64_t nbv = p.B * p.H * VT;
-  const bool grad = blockIdx.x >= nbv;
-  const int64_t y = grad ? blockIdx.x - nbv : blockIdx.x;
+  // Blocks go to the 8 XCDs in turn (block b to XCD b mod 8): with a multiple of 8
+  // blocks, block b takes logical index (b mod 8) N/8 + b/8, so the slices of one
+  // head, which read the same records, run on one XCD and share its L2.
+  const int64_t nblk = gridDim.x, blk = blockIdx.x;
+  const int64_t x = nblk % 8 == 0 ? (blk % 8) * (nblk / 8) + blk / 8 : blk;
+  const bool grad = x >= nbv;
+  const int64_t y = grad ? x - nbv : x;
   const int64_t bh = y / VT;
   const int vt = int(y % VT);
   const int64_t NC = L.nc;
+  const int64_t full = NC - NC % kRing;  // chunks in whole ring groups
   const float* recs = ws + L.rec + bh * NC * R::size;
   // barrier for the LDS exchange only: loads in flight stay in flight
   auto lds_barrier = []() __attribute__((always_inline)) { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
@@ -392,7 +405,7 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void bwd_chain_kernel(Problem
 #pragma unroll
       for (int e = 0; e < 4; ++e) X[j][e] = s0 ? s0[sbase + (16 * (w * TW + j) + e) * DV] : 0.0f;
     if (NC == 0) return;
-    auto load = [&](int64_t c, SOps<TW>& o) {
+    auto load = [&](int64_t c, SOps<TW>& o) __attribute__((always_inline)) {
       const float* r = recs + c * R::size;
 #pragma unroll
       for (int j = 0; j < TW; ++j) {
@@ -403,32 +416,46 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void bwd_chain_kernel(Problem
       }
       o.uf = ld4(r + R::Uf + vt * 256 + 4 * l);
     };
-    SOps<TW> cur, nxt;
-    load(0, cur);
-    for (int64_t c = 0; c < NC; ++c) {
-      load(c + 1 < NC ? c + 1 : c, nxt);
+    auto step = [&](int64_t c, const SOps<TW>& o) __attribute__((always_inline)) {
       float* so = ws + L.sst + (bh * NC + c) * KT * VT * 256;
 #pragma unroll
       for (int j = 0; j < TW; ++j) st4(so + ((w * TW + j) * VT + vt) * 256 + 4 * l, X[j]);
       float4v pu = zero4();
 #pragma unroll
-      for (int j = 0; j < TW; ++j) pu = mma4(cur.wr[j], X[j], pu);  // this wave's share of W S
+      for (int j = 0; j < TW; ++j) pu = mma4(o.wr[j], X[j], pu);  // this wave's share of W S
       xch[c & 1][w][l] = pu;
       lds_barrier();
-      float4v u = cur.uf;  // U = U~ - W S
+      float4v u = o.uf;  // U = U~ - W S
 #pragma unroll
       for (int w2 = 0; w2 < NW; ++w2) u -= xch[c & 1][w2][l];
 #pragma unroll
-      for (int j = 0; j < TW; ++j) X[j] = mma4(cur.af[j], u, X[j] * cur.gm[j]);
-      cur = nxt;
+      for (int j = 0; j < TW; ++j) X[j] = mma4(o.af[j], u, X[j] * o.gm[j]);
+    };
+    SOps<TW> ring[kRing];
+#pragma unroll
+    for (int k = 0; k < kRing; ++k) load(k < NC ? k : NC - 1, ring[k]);
+    asm volatile("" ::: "memory");
+    for (int64_t c0 = 0; c0 < full; c0 += kRing) {
+#pragma unroll
+      for (int k = 0; k < kRing; ++k) {
+        step(c0 + k, ring[k]);
+        int64_t nb = c0 + k + kRing;
+        nb = nb < NC ? nb : NC - 1;
+        asm volatile("" : "+s"(nb));
+        load(nb, ring[k]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
+#pragma unroll
+    for (int k = 0; k < kRing; ++k)
+      if (full + k < NC) step(full + k, ring[k]);
   } else {
 #pragma unroll
     for (int j = 0; j < TW; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) X[j][e] = dsf ? dsf[sbase + (16 * (w * TW + j) + e) * DV] : 0.0f;
     const float* cols = ws + L.cols + bh * L.rs * 2 * DV + DV + 16 * vt + i;  // do, column 16vt + i
-    auto load = [&](int64_t c, GOps<TW>& o) {
+    auto load = [&](int64_t c, GOps<TW>& o) __attribute__((always_inline)) {
       const float* r = recs + c * R::size;
 #pragma unroll
       for (int j = 0; j < TW; ++j) {
@@ -441,26 +468,41 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void bwd_chain_kernel(Problem
 #pragma unroll
       for (int e = 0; e < 4; ++e) o.dof[e] = cols[(c * kC + 4 * g + e) * 2 * DV];
     };
+    auto step = [&](int64_t c, const GOps<TW>& o) __attribute__((always_inline)) {
+      float* so = ws + L.dst + (bh * NC + c) * KT * VT * 256;
+#pragma unroll
+      for (int j = 0; j < TW; ++j) st4(so + ((w * TW + j) * VT + vt) * 256 + 4 * l, X[j]);
+      float4v px = zero4();
+#pragma unroll
+      for (int j = 0; j < TW; ++j) px = mma4(o.ar[j], X[j], px);  // this wave's share of A^ D
+      xch[c & 1][w][l] = px;
+      lds_barrier();
+      float4v nx = -xch[c & 1][0][l];  // -A^ D
+#pragma unroll
+      for (int w2 = 1; w2 < NW; ++w2) nx -= xch[c & 1][w2][l];
+#pragma unroll
+      for (int j = 0; j < TW; ++j) X[j] = mma4(o.wf[j], nx, mma4(o.cf[j], o.dof, X[j] * o.gm[j]));
+    };
     if (NC > 0) {
-      GOps<TW> cur, nxt;
-      load(NC - 1, cur);
-      for (int64_t c = NC - 1; c >= 0; --c) {
-        load(c > 0 ? c - 1 : c, nxt);
-        float* dO_ = ws + L.dst + (bh * NC + c) * KT * VT * 256;
+      // chunks from the last: the k-th of a ring group is chunk NC - 1 - (c0 + k)
+      GOps<TW> ring[kRing];
 #pragma unroll
-        for (int j = 0; j < TW; ++j) st4(dO_ + ((w * TW + j) * VT + vt) * 256 + 4 * l, X[j]);
-        float4v px = zero4();
+      for (int k = 0; k < kRing; ++k) load(k < NC ? NC - 1 - k : 0, ring[k]);
+      asm volatile("" ::: "memory");
+      for (int64_t c0 = 0; c0 < full; c0 += kRing) {
 #pragma unroll
-        for (int j = 0; j < TW; ++j) px = mma4(cur.ar[j], X[j], px);  // this wave's share of A^ D
-        xch[c & 1][w][l] = px;
-        lds_barrier();
-        float4v nx = -xch[c & 1][0][l];  // -A^ D
-#pragma unroll
-        for (int w2 = 1; w2 < NW; ++w2) nx -= xch[c & 1][w2][l];
-#pragma unroll
-        for (int j = 0; j < TW; ++j) X[j] = mma4(cur.wf[j], nx, mma4(cur.cf[j], cur.dof, X[j] * cur.gm[j]));
-        cur = nxt;
+        for (int k = 0; k < kRing; ++k) {
+          step(NC - 1 - (c0 + k), ring[k]);
+          int64_t nb = NC - 1 - (c0 + k + kRing);
+          nb = nb > 0 ? nb : 0;
+          asm volatile("" : "+s"(nb));
+          load(nb, ring[k]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
+#pragma unroll
+      for (int k = 0; k < kRing; ++k)
+        if (full + k < NC) step(NC - 1 - (full + k), ring[k]);
     }
     if (ds0) {
 #pragma unroll
@@ -474,7 +516,10 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void bwd_chain_kernel(Problem
 // ---- 4. intra-chunk gradients -------------------------------------------------------
 // One wave per (batch*head, chunk): S (state before the chunk) and D (dL/dS after it)
 // from the recursions, the chunk's record and operands; writes every step's dq, da,
-// db, dalpha and dw.
+// db, dalpha and dw. The value columns are taken 16 at a time: each S and D tile is
+// read once, used in the fragment order for U and A^ D (sums over key channels), and
+// transposed in registers (an MFMA against the identity, exact) for dO S^T, dR S^T and
+// U D^T (sums over value channels).
 template <int DK, int DV>
 __global__ __launch_bounds__(64) void bwd_intra_kernel(Problem p, float* __restrict__ ws) {
   constexpr int KT = DK / 16, VT = DV / 16;
@@ -490,46 +535,60 @@ __global__ __launch_bounds__(64) void bwd_intra_kernel(Problem p, float* __restr
   const float* sS = ws + L.sst + item * KT * VT * 256;
   const float* sD = ws + L.dst + item * KT * VT * 256;
 
-  // U in the row order, tile vt: U[i][16vt + 4g + e]  (U^T = U~^T - S^T W^T)
-  float4v ut[VT];
-#pragma unroll
-  for (int vt = 0; vt < VT; ++vt) {
-    float4v a = -ld4(rec + R::Ur + vt * 256 + 4 * l);
-#pragma unroll
-    for (int t = 0; t < KT; ++t) a = mma4(ld4(sS + (t * VT + vt) * 256 + 4 * l), ld4(rec + R::Wr + t * 256 + 4 * l), a);
-    ut[vt] = -a;
-  }
-  // dU = A^ D + P^T dO (fragment order), then dR^T = dU^T T: dR[i][16vt + 4g + e]
-  float4v pF, tF;  // P[4g+e][i], T[4g+e][i]
+  float4v pF, tF, id;  // P[4g+e][i], T[4g+e][i], the identity
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     pF[e] = rec[R::Pm + (4 * g + e) * 16 + i];
     tF[e] = rec[R::Tm + (4 * g + e) * 16 + i];
+    id[e] = 4 * g + e == i ? 1.0f : 0.0f;
   }
-  float4v rt[VT], doA[VT];  // dR and dO in the row order
   const bool row_live = c * kC + i < NS;
+  // over the value tiles: dP, dM (both orientations: dp[e] = dP[4g+e][i], dpt[e] =
+  // dP[i][4g+e], likewise dm, dmt) and, per key tile, dO S^T, dR S^T, U D^T at
+  // (step 4g+e, channel 16t+i) and the sum over v of D . S for channel 16t+i
+  float4v dp = zero4(), dpt = zero4(), dm = zero4(), dmt = zero4();
+  float4v qs[KT], rs[KT], ud[KT];
+  float rsum[KT];
 #pragma unroll
+  for (int t = 0; t < KT; ++t) qs[t] = rs[t] = ud[t] = zero4(), rsum[t] = 0.0f;
+#pragma unroll 1
   for (int vt = 0; vt < VT; ++vt) {
+    float4v sf[KT], df[KT];  // S[16t+4g+e][16vt+i], D likewise
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      sf[t] = ld4(sS + (t * VT + vt) * 256 + 4 * l);
+      df[t] = ld4(sD + (t * VT + vt) * 256 + 4 * l);
+    }
+    // U in the row order: ut[e] = U[i][16vt+4g+e]  (U^T = U~^T - S^T W^T)
+    float4v ut = -ld4(rec + R::Ur + vt * 256 + 4 * l);
+#pragma unroll
+    for (int t = 0; t < KT; ++t) ut = mma4(sf[t], ld4(rec + R::Wr + t * 256 + 4 * l), ut);
+    ut = -ut;
+    // dU = A^ D + P^T dO (fragment order), then dR^T = dU^T T: rt[e] = dR[i][16vt+4g+e]
     float4v x = zero4();
 #pragma unroll
-    for (int t = 0; t < KT; ++t) x = mma4(ld4(rec + R::Ar + t * 256 + 4 * l), ld4(sD + (t * VT + vt) * 256 + 4 * l), x);
+    for (int t = 0; t < KT; ++t) x = mma4(ld4(rec + R::Ar + t * 256 + 4 * l), df[t], x);
     float4v dF;
 #pragma unroll
     for (int e = 0; e < 4; ++e) dF[e] = cb[(4 * g + e) * 2 * DV + DV + 16 * vt + i];
     x = mma4(pF, dF, x);
-    rt[vt] = mma4(x, tF, zero4());
-    doA[vt] = ld4(cb + i * 2 * DV + DV + 16 * vt + 4 * g);
-    if (row_live) st4(ws + L.dw + (bh * NS + c * kC + i) * DV + 16 * vt + 4 * g, rt[vt]);
-  }
-  // dP = tril(dO U^T), dM = -strict_tril(dR U^T), each in both orientations:
-  // dp[e] = dP[4g+e][i], dpt[e] = dP[i][4g+e]; likewise dm, dmt
-  float4v dp = zero4(), dpt = zero4(), dm = zero4(), dmt = zero4();
+    const float4v rt = mma4(x, tF, zero4());
+    if (row_live) st4(ws + L.dw + (bh * NS + c * kC + i) * DV + 16 * vt + 4 * g, rt);
+    const float4v doA = ld4(cb + i * 2 * DV + DV + 16 * vt + 4 * g);  // dO[i][16vt+4g+e]
+    dp = mma4(doA, ut, dp);
+    dpt = mma4(ut, doA, dpt);
+    dm = mma4(rt, ut, dm);
+    dmt = mma4(ut, rt, dmt);
 #pragma unroll
-  for (int vt = 0; vt < VT; ++vt) {
-    dp = mma4(doA[vt], ut[vt], dp);
-    dpt = mma4(ut[vt], doA[vt], dpt);
-    dm = mma4(rt[vt], ut[vt], dm);
-    dmt = mma4(ut[vt], rt[vt], dmt);
+    for (int t = 0; t < KT; ++t) {
+      const float4v sT = mma4(sf[t], id, zero4());  // S[16t+i][16vt+4g+e]
+      const float4v dT = mma4(df[t], id, zero4());
+      qs[t] = mma4(doA, sT, qs[t]);
+      rs[t] = mma4(rt, sT, rs[t]);
+      ud[t] = mma4(ut, dT, ud[t]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rsum[t] += sT[e] * dT[e];
+    }
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -544,26 +603,7 @@ __global__ __launch_bounds__(64) void bwd_intra_kernel(Problem p, float* __restr
 #pragma unroll
   for (int t = 0; t < KT; ++t) {
     const int ch = 16 * t + i;
-    // dO S^T, dR S^T, U D^T at (step 4g+e, channel ch); sum over v of D . S for channel ch
-    float4v qs = zero4(), rs = zero4(), ud = zero4();
-    float rsum = 0.0f;
-#pragma unroll
-    for (int vt = 0; vt < VT; ++vt) {
-      // element (row 16t + i, column 16vt + 4g + e) of a fragment-order tile
-      const float* ts = sS + (t * VT + vt) * 256 + (i >> 2) * 64 + 16 * g + (i & 3);
-      const float* td = sD + (t * VT + vt) * 256 + (i >> 2) * 64 + 16 * g + (i & 3);
-      float4v sT, dT;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sT[e] = ts[4 * e];
-        dT[e] = td[4 * e];
-        rsum += sT[e] * dT[e];
-      }
-      qs = mma4(doA[vt], sT, qs);
-      rs = mma4(rt[vt], sT, rs);
-      ud = mma4(ut[vt], dT, ud);
-    }
-    rsum = sum_over_groups(rsum);
+    const float rs_t = sum_over_groups(rsum[t]);
     float gv[4];
     chunk_logdecay<DK>(rb, ch, l, gv);
     const float gr = __shfl(gv[0], 32 + i, 64);  // step 8
@@ -584,22 +624,22 @@ __global__ __launch_bounds__(64) void bwd_intra_kernel(Problem p, float* __restr
       bt[e] = bv[e] * eu[e];
       qt[e] = qv[e] * eu[e];
     }
-    const float4v pa = mma4(dpt, at, zero4());        // dP A~
-    const float4v ma = mma4(dmt, at, zero4());        // dM A~
+    const float4v pa = mma4(dpt, at, zero4());               // dP A~
+    const float4v ma = mma4(dmt, at, zero4());               // dM A~
     const float4v aa = mma4(dm, bt, mma4(dp, qt, zero4()));  // dP^T Q~ + dM^T B~
     float4v dq, da, db, dG;
     float hs = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      dq[e] = qs[e] * eg[e] + pa[e] * eu[e];
-      db[e] = ma[e] * eu[e] - rs[e] * eg[e];
-      const float dh = ud[e] * eh[e];
+      dq[e] = qs[t][e] * eg[e] + pa[e] * eu[e];
+      db[e] = ma[e] * eu[e] - rs[t][e] * eg[e];
+      const float dh = ud[t][e] * eh[e];
       da[e] = aa[e] * ed[e] + dh;
       hs += av[e] * dh;
       dG[e] = qv[e] * dq[e] + bv[e] * db[e] - av[e] * da[e];
     }
     hs = sum_over_groups(hs);
-    dG[3] += g == 3 ? hs + expf(ge) * rsum : 0.0f;  // G_C: the A^ and Gamma terms
+    dG[3] += g == 3 ? hs + expf(ge) * rs_t : 0.0f;  // G_C: the A^ and Gamma terms
     float suf[4];
     suf[3] = dG[3];
 #pragma unroll
