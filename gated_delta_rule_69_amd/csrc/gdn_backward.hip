@@ -48,7 +48,6 @@ namespace gdn {
 namespace {
 
 constexpr int kC = 16;    // steps a chunk
-constexpr int kRef = 8;   // reference step of the split decay factors
 constexpr int kPad = kC;  // operand rows after a sequence (identity steps fill its last chunk)
 
 // Record of one chunk (float offsets): W (fragment, row order), A^ (fragment, row
@@ -120,21 +119,47 @@ __device__ __forceinline__ float group_suffix(float x, int l) {
   return (g <= 2 ? x1 : 0.0f) + (g <= 1 ? x2 : 0.0f) + (g == 0 ? x3 : 0.0f);
 }
 
-// In-chunk cumulative log decay of channel ch at steps 4g .. 4g+3 (fragment order),
-// from the operand rows of the chunk's first step. Every kernel forms G this way, so
-// all of them see the same values.
-template <int DK>
-__device__ __forceinline__ void chunk_logdecay(const float* rb, int ch, int l, float (&gv)[4]) {
-  const int g = l >> 4;
-  float run = 0.0f;
+// Decay factors of one channel at steps s = 4g .. 4g+3 of a chunk (fragment order),
+// from its decays alpha at those steps: eg = e^(G_s), eh = e^(G_C - G_s), up =
+// e^(G_s - G_8), dn = e^(G_8 - G_s) and gam = e^(G_C). Each is a product of the
+// alphas over just the steps it spans (up and dn at most 8 of them), never an
+// exponential of a difference of cumulative log decays, which would carry the
+// rounding of sums as large as 16 |log alpha| into every factor. Every kernel forms
+// the factors here, in the same order, so all of them see the same values.
+struct Decay {
+  float eg[4], eh[4], up[4], dn[4], gam;
+};
+__device__ __forceinline__ Decay chunk_decay(const float (&al)[4], int l) {
+  const int g = l >> 4, i = l & 15;
+  float ip[4], es[4], ipx[4];  // in-group inclusive prefix, exclusive suffix, prefix after the first
+  ip[0] = al[0];
+  ipx[0] = 1.0f;
+  ipx[1] = al[1];
+#pragma unroll
+  for (int e = 1; e < 4; ++e) ip[e] = ip[e - 1] * al[e];
+  ipx[2] = ipx[1] * al[2];
+  ipx[3] = ipx[2] * al[3];
+  es[3] = 1.0f;
+#pragma unroll
+  for (int e = 2; e >= 0; --e) es[e] = al[e + 1] * es[e + 1];
+  const float t0 = __shfl(ip[3], i, 64), t1 = __shfl(ip[3], 16 + i, 64);  // group products
+  const float t2 = __shfl(ip[3], 32 + i, 64), t3 = __shfl(ip[3], 48 + i, 64);
+  const float a8 = __shfl(al[0], 32 + i, 64);     // alpha at step 8
+  const float p911 = __shfl(ipx[3], 32 + i, 64);  // alphas of steps 9 .. 11
+  const float before = g == 0 ? 1.0f : g == 1 ? t0 : g == 2 ? t0 * t1 : (t0 * t1) * t2;
+  const float after = g == 3 ? 1.0f : g == 2 ? t3 : g == 1 ? t2 * t3 : t1 * (t2 * t3);
+  Decay d;
+  d.gam = ((t0 * t1) * t2) * t3;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    run += logf(rb[(4 * g + e) * 4 * DK + 2 * DK + ch]);
-    gv[e] = run;
+    d.eg[e] = before * ip[e];
+    d.eh[e] = es[e] * after;
+    const float u = g == 2 ? ipx[e] : p911 * ip[e];        // steps 8 .. 15: alphas of steps 9 .. s
+    const float w = g == 1 ? es[e] * a8 : (es[e] * t1) * a8;  // steps 0 .. 7: alphas of steps s+1 .. 8
+    d.up[e] = g >= 2 ? u : 1.0f / w;
+    d.dn[e] = g >= 2 ? 1.0f / u : w;
   }
-  const float pre = group_prefix(run, l);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) gv[e] += pre;
+  return d;
 }
 
 // ---- 1. operand kernel ------------------------------------------------------------
@@ -228,12 +253,13 @@ __global__ __launch_bounds__(256) void bwd_ops_kernel(Problem p, const In* __res
 }
 
 // ---- 2. record kernel -------------------------------------------------------------
-// One wave per (batch*head, chunk).
+// One wave per (batch*head, chunk). The operands are formed in the fragment order
+// (step 4g+e, channel 16t+i) and turned into the row order the Grams need by an MFMA
+// against the identity (exact).
 template <int DK, int DV>
 __global__ __launch_bounds__(64) void bwd_rec_kernel(Problem p, float* __restrict__ ws) {
   constexpr int KT = DK / 16, VT = DV / 16;
   using R = Rec<DK, DV>;
-  __shared__ __align__(16) float Gs[kC * DK];  // G [step][channel]
   __shared__ __align__(16) float Ms[256];
   __shared__ __align__(16) float Ps[256];
   __shared__ __align__(16) float Ts[256];
@@ -244,38 +270,45 @@ __global__ __launch_bounds__(64) void bwd_rec_kernel(Problem p, float* __restric
   const float* rb = ws + L.rows + (bh * L.rs + c * kC) * 4 * DK;  // step s of the chunk at rb + s 4 DK
   const float* cb = ws + L.cols + (bh * L.rs + c * kC) * 2 * DV;
   float* rec = ws + L.rec + item * R::size;
-
-  float gc[KT];  // G at the chunk's last step, channel 16t + i
+  float4v id;
 #pragma unroll
-  for (int t = 0; t < KT; ++t) {
-    float gv[4];
-    chunk_logdecay<DK>(rb, 16 * t + i, l, gv);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) Gs[(4 * g + e) * DK + 16 * t + i] = gv[e];
-    gc[t] = __shfl(gv[3], 48 + i, 64);
-  }
-  __syncthreads();
+  for (int e = 0; e < 4; ++e) id[e] = 4 * g + e == i ? 1.0f : 0.0f;
 
-  // Grams in the row order: B~ = b e^(G - G_8), Q~ = q e^(G - G_8), A~ = a e^(G_8 - G)
+  // per key tile: B+, Q+, A^ (fragment order) kept for W and Q+ - P W; the Grams
+  // M = strict_tril(B~ A~^T), P = tril(Q~ A~^T) with B~ = b e^(G - G_8), Q~ = q e^(G - G_8),
+  // A~ = a e^(G_8 - G) from the transposed operands
+  float4v bF[KT], qF[KT];
   float4v m = zero4(), pp = zero4();
 #pragma unroll
   for (int t = 0; t < KT; ++t) {
-    const int ch = 16 * t + 4 * g;
-    const float4v av = ld4(rb + i * 4 * DK + ch);
-    const float4v bv = ld4(rb + i * 4 * DK + DK + ch);
-    const float4v qv = ld4(rb + i * 4 * DK + 3 * DK + ch);
-    const float4v gv = ld4(Gs + i * DK + ch);
-    const float4v gr = ld4(Gs + kRef * DK + ch);
-    float4v bt, qt, at;
+    const int ch = 16 * t + i;
+    float al[4];
+    float4v av, bv, qv;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float up = expf(gv[e] - gr[e]), dn = expf(gr[e] - gv[e]);
-      bt[e] = bv[e] * up;
-      qt[e] = qv[e] * up;
-      at[e] = av[e] * dn;
+      const float* rr = rb + (4 * g + e) * 4 * DK + ch;
+      av[e] = rr[0];
+      bv[e] = rr[DK];
+      al[e] = rr[2 * DK];
+      qv[e] = rr[3 * DK];
     }
-    m = mma4(bt, at, m);   // M[4g+e][i] = B~[4g+e] . A~[i]
-    pp = mma4(qt, at, pp);
+    const Decay d = chunk_decay(al, l);
+    float4v bt, qt, at, aF;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bF[t][e] = bv[e] * d.eg[e];
+      qF[t][e] = qv[e] * d.eg[e];
+      aF[e] = av[e] * d.eh[e];
+      bt[e] = bv[e] * d.up[e];
+      qt[e] = qv[e] * d.up[e];
+      at[e] = av[e] * d.dn[e];
+    }
+    const float4v btr = mma4(bt, id, zero4()), qtr = mma4(qt, id, zero4()), atr = mma4(at, id, zero4());
+    m = mma4(btr, atr, m);  // M[4g+e][i] = B~[4g+e] . A~[i]
+    pp = mma4(qtr, atr, pp);
+    st4(rec + R::Af + t * 256 + 4 * l, aF);
+    st4(rec + R::Ar + t * 256 + 4 * l, mma4(aF, id, zero4()));  // A^ in the row order
+    if (g == 0) rec[R::Gm + ch] = d.gam;
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -291,7 +324,7 @@ __global__ __launch_bounds__(64) void bwd_rec_kernel(Problem p, float* __restric
   for (int r = 0; r < 16; ++r) {
     float x = r == i ? 1.0f : 0.0f;
 #pragma unroll
-    for (int s = 0; s < r; ++s) x -= Ms[r * 16 + s] * tc[s];
+    for (int s2 = 0; s2 < r; ++s2) x -= Ms[r * 16 + s2] * tc[s2];
     tc[r] = x;
   }
   if (g == 0) {
@@ -306,35 +339,12 @@ __global__ __launch_bounds__(64) void bwd_rec_kernel(Problem p, float* __restric
 
 #pragma unroll
   for (int t = 0; t < KT; ++t) {
-    const int ch = 16 * t + i;
-    float4v bF, qF, aF;  // B+, Q+, A^ at (step 4g+e, channel ch)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int s = 4 * g + e;
-      const float gv = Gs[s * DK + ch];
-      const float eg = expf(gv), eh = expf(gc[t] - gv);
-      bF[e] = rb[s * 4 * DK + DK + ch] * eg;
-      qF[e] = rb[s * 4 * DK + 3 * DK + ch] * eg;
-      aF[e] = rb[s * 4 * DK + ch] * eh;
-    }
-    const float4v w = mma4(tA, bF, zero4());   // W = T B+ (fragment order)
-    const float4v wr = mma4(bF, tA, zero4());  // W^T: W in the row order
-    const float4v pw = mma4(pA, w, zero4());   // P W (fragment order)
-    float4v cm, ar;
-    const float4v av = ld4(rb + i * 4 * DK + 16 * t + 4 * g);
-    const float4v gv = ld4(Gs + i * DK + 16 * t + 4 * g);
-    const float4v ge = ld4(Gs + (kC - 1) * DK + 16 * t + 4 * g);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      cm[e] = qF[e] - pw[e];
-      ar[e] = av[e] * expf(ge[e] - gv[e]);
-    }
+    const float4v w = mma4(tA, bF[t], zero4());   // W = T B+ (fragment order)
+    const float4v wr = mma4(bF[t], tA, zero4());  // W^T: W in the row order
+    const float4v pw = mma4(pA, w, zero4());      // P W (fragment order)
     st4(rec + R::Wf + t * 256 + 4 * l, w);
     st4(rec + R::Wr + t * 256 + 4 * l, wr);
-    st4(rec + R::Af + t * 256 + 4 * l, aF);
-    st4(rec + R::Ar + t * 256 + 4 * l, ar);
-    st4(rec + R::Cf + t * 256 + 4 * l, cm);
-    if (g == 0) rec[R::Gm + ch] = expf(gc[t]);
+    st4(rec + R::Cf + t * 256 + 4 * l, qF[t] - pw);
   }
 #pragma unroll
   for (int vt = 0; vt < VT; ++vt) {
@@ -535,6 +545,14 @@ __global__ __launch_bounds__(64) void bwd_intra_kernel(Problem p, float* __restr
   const float* sS = ws + L.sst + item * KT * VT * 256;
   const float* sD = ws + L.dst + item * KT * VT * 256;
 
+  // W and A^ in the row order, the same for every value tile: parked in LDS (each
+  // lane reads back only its own slots, so no barrier is needed)
+  __shared__ float4v lw[KT][64], la[KT][64];
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    lw[t][l] = ld4(rec + R::Wr + t * 256 + 4 * l);
+    la[t][l] = ld4(rec + R::Ar + t * 256 + 4 * l);
+  }
   float4v pF, tF, id;  // P[4g+e][i], T[4g+e][i], the identity
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -562,12 +580,12 @@ __global__ __launch_bounds__(64) void bwd_intra_kernel(Problem p, float* __restr
     // U in the row order: ut[e] = U[i][16vt+4g+e]  (U^T = U~^T - S^T W^T)
     float4v ut = -ld4(rec + R::Ur + vt * 256 + 4 * l);
 #pragma unroll
-    for (int t = 0; t < KT; ++t) ut = mma4(sf[t], ld4(rec + R::Wr + t * 256 + 4 * l), ut);
+    for (int t = 0; t < KT; ++t) ut = mma4(sf[t], lw[t][l], ut);
     ut = -ut;
     // dU = A^ D + P^T dO (fragment order), then dR^T = dU^T T: rt[e] = dR[i][16vt+4g+e]
     float4v x = zero4();
 #pragma unroll
-    for (int t = 0; t < KT; ++t) x = mma4(ld4(rec + R::Ar + t * 256 + 4 * l), df[t], x);
+    for (int t = 0; t < KT; ++t) x = mma4(la[t][l], df[t], x);
     float4v dF;
 #pragma unroll
     for (int e = 0; e < 4; ++e) dF[e] = cb[(4 * g + e) * 2 * DV + DV + 16 * vt + i];
@@ -590,61 +608,102 @@ __global__ __launch_bounds__(64) void bwd_intra_kernel(Problem p, float* __restr
       for (int e = 0; e < 4; ++e) rsum[t] += sT[e] * dT[e];
     }
   }
+  // Pairs of steps of one token (one step, or a DeltaProduct token's sub-steps) have no
+  // decay between them: their terms reach dq, db and da but add exactly nothing to dG
+  // (each enters it twice with opposite signs). They are kept apart (the *w products),
+  // since under strong decay such an exact zero, summed from its two halves, would be
+  // far larger than dG itself.
+  int64_t tk[4];  // tokens of steps 4g+e
+#pragma unroll
+  for (int e = 0; e < 4; ++e) tk[e] = (c * kC + 4 * g + e) / p.n_h;
+  const int64_t tki = (c * kC + i) / p.n_h, tkl = (c * kC + kC - 1) / p.n_h;
+  float4v dpw, dptw, dmw, dmtw;  // the within-token parts (dP with its diagonal)
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int r = 4 * g + e;
-    dp[e] = r >= i ? dp[e] : 0.0f;
-    dpt[e] = i >= r ? dpt[e] : 0.0f;
-    dm[e] = r > i ? -dm[e] : 0.0f;
-    dmt[e] = i > r ? -dmt[e] : 0.0f;
+    const bool same = tk[e] == tki;
+    dpw[e] = r >= i && same ? dp[e] : 0.0f;
+    dptw[e] = i >= r && same ? dpt[e] : 0.0f;
+    dmw[e] = r > i && same ? -dm[e] : 0.0f;
+    dmtw[e] = i > r && same ? -dmt[e] : 0.0f;
+    dp[e] = r > i && !same ? dp[e] : 0.0f;
+    dpt[e] = i > r && !same ? dpt[e] : 0.0f;
+    dm[e] = r > i && !same ? -dm[e] : 0.0f;
+    dmt[e] = i > r && !same ? -dmt[e] : 0.0f;
   }
 
+  // per key tile: the operands at (step 4g+e, channel 16t+i), the next tile's loaded
+  // while this one is assembled
+  struct EOps {
+    float av[4], bv[4], alv[4], qv[4];
+  };
+  auto eload = [&](int t, EOps& o) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float* rr = rb + (4 * g + e) * 4 * DK + 16 * t + i;
+      o.av[e] = rr[0];
+      o.bv[e] = rr[DK];
+      o.alv[e] = rr[2 * DK];
+      o.qv[e] = rr[3 * DK];
+    }
+  };
   float* part = ws + L.part;
+  EOps cur, nxt;
+  eload(0, cur);
 #pragma unroll
   for (int t = 0; t < KT; ++t) {
+    if (t + 1 < KT) {
+      eload(t + 1, nxt);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     const int ch = 16 * t + i;
     const float rs_t = sum_over_groups(rsum[t]);
-    float gv[4];
-    chunk_logdecay<DK>(rb, ch, l, gv);
-    const float gr = __shfl(gv[0], 32 + i, 64);  // step 8
-    const float ge = __shfl(gv[3], 48 + i, 64);  // step 15
-    float4v av, bv, qv, alv, eg, eu, ed, eh, at, bt, qt;
+    const Decay dc = chunk_decay(cur.alv, l);
+    float4v eg, eu, ed, eh, at, bt, qt;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float* rr = rb + (4 * g + e) * 4 * DK + ch;
-      av[e] = rr[0];
-      bv[e] = rr[DK];
-      alv[e] = rr[2 * DK];
-      qv[e] = rr[3 * DK];
-      eg[e] = expf(gv[e]);
-      eu[e] = expf(gv[e] - gr);
-      ed[e] = expf(gr - gv[e]);
-      eh[e] = expf(ge - gv[e]);
-      at[e] = av[e] * ed[e];
-      bt[e] = bv[e] * eu[e];
-      qt[e] = qv[e] * eu[e];
+      eg[e] = dc.eg[e];
+      eu[e] = dc.up[e];
+      ed[e] = dc.dn[e];
+      eh[e] = dc.eh[e];
+      at[e] = cur.av[e] * ed[e];
+      bt[e] = cur.bv[e] * eu[e];
+      qt[e] = cur.qv[e] * eu[e];
     }
-    const float4v pa = mma4(dpt, at, zero4());               // dP A~
-    const float4v ma = mma4(dmt, at, zero4());               // dM A~
-    const float4v aa = mma4(dm, bt, mma4(dp, qt, zero4()));  // dP^T Q~ + dM^T B~
-    float4v dq, da, db, dG;
-    float hs = 0.0f;
+    const float4v pa = mma4(dpt, at, zero4());                  // dP A~
+    const float4v ma = mma4(dmt, at, zero4());                  // dM A~
+    const float4v aa = mma4(dm, bt, mma4(dp, qt, zero4()));     // dP^T Q~ + dM^T B~
+    const float4v paw = mma4(dptw, at, zero4());                // the same within tokens
+    const float4v maw = mma4(dmtw, at, zero4());
+    const float4v aaw = mma4(dmw, bt, mma4(dpw, qt, zero4()));
+    // d log alpha_s = (suffix sum over s' >= s of dG_s') + (prefix sum over j < s of
+    // a_j . dh_j): the A^ terms enter dG_j with a minus and G_C with a plus, so their net
+    // share is that prefix sum, formed directly; the Gamma term enters at G_C.
+    float4v dq, da, db, dG, ah;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      dq[e] = qs[t][e] * eg[e] + pa[e] * eu[e];
-      db[e] = ma[e] * eu[e] - rs[t][e] * eg[e];
+      const float dqo = qs[t][e] * eg[e] + pa[e] * eu[e];
+      const float dbo = ma[e] * eu[e] - rs[t][e] * eg[e];
+      const float dao = aa[e] * ed[e];
       const float dh = ud[t][e] * eh[e];
-      da[e] = aa[e] * ed[e] + dh;
-      hs += av[e] * dh;
-      dG[e] = qv[e] * dq[e] + bv[e] * db[e] - av[e] * da[e];
+      dq[e] = dqo + paw[e] * eu[e];
+      db[e] = dbo + maw[e] * eu[e];
+      da[e] = dao + aaw[e] * ed[e] + dh;
+      // an A^ term of a step in the chunk's last token has no decay up to the chunk's
+      // end and adds nothing: left out
+      ah[e] = tk[e] == tkl ? 0.0f : cur.av[e] * dh;
+      dG[e] = cur.qv[e] * dqo + cur.bv[e] * dbo - cur.av[e] * dao;
     }
-    hs = sum_over_groups(hs);
-    dG[3] += g == 3 ? hs + expf(ge) * rs_t : 0.0f;  // G_C: the A^ and Gamma terms
-    float suf[4];
+    dG[3] += g == 3 ? dc.gam * rs_t : 0.0f;  // G_C: the Gamma term
+    float suf[4], pre[4];
     suf[3] = dG[3];
 #pragma unroll
     for (int e = 2; e >= 0; --e) suf[e] = dG[e] + suf[e + 1];
+    pre[0] = 0.0f;
+#pragma unroll
+    for (int e = 1; e < 4; ++e) pre[e] = pre[e - 1] + ah[e - 1];
     const float later = group_suffix(suf[0], l);
+    const float earlier = group_prefix(pre[3] + ah[3], l);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int64_t s = c * kC + 4 * g + e;
@@ -653,9 +712,10 @@ __global__ __launch_bounds__(64) void bwd_intra_kernel(Problem p, float* __restr
         pr[0] = dq[e];
         pr[DK] = da[e];
         pr[2 * DK] = db[e];
-        pr[3 * DK] = (suf[e] + later) / alv[e];
+        pr[3 * DK] = ((suf[e] + later) + (pre[e] + earlier)) / cur.alv[e];
       }
     }
+    if (t + 1 < KT) cur = nxt;
   }
 }
 

@@ -3,8 +3,9 @@ oracle's gradients (oracle.backward, itself pinned by finite differences).
 
 The kernel computes in float32 from the (bf16-rounded, for bf16) inputs, as the oracle
 does in float64 from the same values, so one tolerance covers both input dtypes:
-rel-L2 1e-5 and normwise max-rel 1e-4 for every gradient. Sequences longer than the
-64-token checkpoint interval, with a ragged last interval, exercise the recompute.
+rel-L2 1e-5 and normwise max-rel 1e-4 for every gradient. The pass runs on 16-step
+chunks; the cases span one to several chunks, ragged last chunks and several sub-steps
+per token.
 """
 import numpy as np
 import pytest
@@ -26,22 +27,28 @@ CASES = [  # variant, fg2_plus, dtype, B, T, H, dk, dv
     ("asym", False, "bf16", 1, 66, 1, 128, 64),
     ("deltaproduct", False, "f32", 1, 50, 2, 64, 64),     # 2 steps a token
     ("deltaproduct", False, "bf16", 1, 27, 2, 128, 128),  # 3 steps a token
-    # edges of the chain kernel's 16-step operand ring and the 64-step intervals
+    # one step, one chunk and a step, exactly four chunks (one operand-ring group of the
+    # recursions), several groups and a ragged chunk
     ("fg2", False, "bf16", 1, 1, 2, 128, 128),    # one token
-    ("kda", False, "f32", 2, 17, 3, 32, 16),      # one whole ring group and one step
-    ("gdn", False, "bf16", 1, 64, 2, 64, 64),     # exactly one interval
-    ("fg2", True, "bf16", 1, 129, 1, 128, 32),    # FG2+, a third interval of one step
+    ("kda", False, "f32", 2, 17, 3, 32, 16),      # one chunk and one step
+    ("gdn", False, "bf16", 1, 64, 2, 64, 64),     # four chunks: one ring group
+    ("fg2", True, "bf16", 1, 129, 1, 128, 32),    # FG2+, two groups and one step
     ("asym", False, "f32", 1, 48, 2, 16, 128),    # dk 16: lanes past dk idle
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
 def test_backward_vs_oracle(case):
-    import gated_delta_rule_69_amd as gdn
-    from gpu_util import DEV, host, state_to_dev, to_dev
     var, plus, dt, B, T, H, dk, dv = case
     n_h = (2 if T % 2 == 0 else 3) if var == "deltaproduct" else 1
     inp = gdn_inputs.make_inputs(var, B, T, H, dk, dv, dtype=dt, seed=90, fg2_plus=plus, n_h=n_h)
+    _check_backward(inp, case)
+
+
+def _check_backward(inp, case):
+    import gated_delta_rule_69_amd as gdn
+    from gpu_util import DEV, host, state_to_dev, to_dev
+    var, dt, B, T, H, dk, dv = (inp[k] for k in ("variant", "dtype", "B", "T", "H", "dk", "dv"))
     rng = np.random.default_rng(91)
     s0 = gdn_inputs.make_state(B, H, dk, dv, seed=92)
     do = rng.standard_normal((B, T, H, dv)).astype(np.float32)
@@ -62,6 +69,41 @@ def test_backward_vs_oracle(case):
         e2, em = oracle.rel_l2(x, r), oracle.max_rel(x, r)
         print(case, name, f"rel_l2={e2:.2e} max_rel={em:.2e}", flush=True)
         assert e2 <= 1e-5 and em <= 1e-4, (name, e2, em)
+
+
+# Strong decay: the backward pass runs in 16-step chunks whose decay factors are split
+# at the chunk's step 8, so none spans more than 8 steps (the same window as the
+# chunked forward pass). Forget-gate logits centred at -2, -3 and -6 (mean alpha 0.15,
+# 0.07, 0.0035) for every variant.
+STRONG = [  # variant, dtype, B, T, H, dk, dv
+    ("fg2", "bf16", 1, 100, 2, 128, 128),
+    ("kda", "f32", 1, 70, 2, 64, 64),
+    ("gdn", "f32", 1, 70, 2, 32, 32),
+    ("asym", "f32", 1, 70, 2, 64, 64),
+    ("deltaproduct", "f32", 1, 40, 2, 64, 64),
+]
+
+
+@pytest.mark.parametrize("alpha_mean", [-2.0, -3.0, -6.0])
+@pytest.mark.parametrize("case", STRONG, ids=lambda c: "-".join(map(str, c)))
+def test_backward_strong_decay(case, alpha_mean):
+    var, dt, B, T, H, dk, dv = case
+    n_h = 2 if var == "deltaproduct" else 1
+    inp = gdn_inputs.make_inputs(var, B, T, H, dk, dv, dtype=dt, seed=97, n_h=n_h, alpha_mean=alpha_mean)
+    _check_backward(inp, (case, alpha_mean))
+
+
+@pytest.mark.parametrize("case", [("fg2", "bf16", 1, 100, 2, 128, 128), ("kda", "f32", 1, 70, 2, 64, 32)],
+                         ids=lambda c: "-".join(map(str, c)))
+def test_backward_some_channels_forget_at_once(case):
+    """Every seventh key channel has alpha = 1e-4 at every step, the others ordinary
+    gates, inside the same chunk."""
+    var, dt, B, T, H, dk, dv = case
+    inp = gdn_inputs.make_inputs(var, B, T, H, dk, dv, dtype=dt, seed=98)
+    al = inp["alpha"].copy()
+    al[..., ::7] = 1e-4
+    inp["alpha"] = gdn_inputs.round_bf16(al) if dt == "bf16" else al.astype(np.float32)
+    _check_backward(inp, case)
 
 
 def test_backward_deterministic():
