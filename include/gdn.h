@@ -223,11 +223,10 @@ typedef struct gdn_grads {
 
 /* Bytes of device workspace gdn_recurrent_bwd needs (0 for an invalid set). Per
  * token (or sub-step) and head: the float32 step operands (4 dk + 2 dv floats), the
- * partial row gradients of each group of up to four 16-column slices
- * (max(dv / 64, 1) x 4 dk floats), dw (dv floats) and the state and state-gradient
- * checkpoints (2 dk dv floats every 64 steps); plus a fixed part of at most
- * 1,024 x 16 x dk x 16 floats (128 MiB at dk = 128) for the per-wave state slots.
- * 9.5 KiB per token and head at dk = dv = 128: 0.77 GB for 4,096 tokens x 16 heads. */
+ * records of the 16-step chunks ((80 dk + 32 dv + dk + 512) / 16 floats), the state
+ * before and the state gradient after every chunk (2 dk dv / 16 floats) and the row
+ * gradients (4 dk + dv floats). 17.2 KiB per token and head at dk = dv = 128:
+ * 1.15 GB for 4,096 tokens x 16 heads. */
 size_t gdn_bwd_workspace_bytes(const gdn_args* args);
 
 /* Backward pass (reverse-mode gradients) of the token recurrence for every variant
@@ -235,14 +234,17 @@ size_t gdn_bwd_workspace_bytes(const gdn_args* args);
  * DeltaProduct summary, "Approach"; dalpha is then the gate's gradient [B, T, H]).
  * The pages give the forward pass only; this is the derivative of the same recurrence
  * (FG2-GDN reading notes, section 2.2 eq. (11), section 2.3 eq. (13); GDN2-stability
- * page, eq. (1)). gdn_args.stabilize must be 0 (GDN_ERR_UNSUPPORTED otherwise). args as for the forward pass (o, s_final
- * and chunk are ignored; s0 NULL means zero); d_o [B, T, H, dv] in args->dtype is
- * dL/do; d_s_final [B, H, dk, dv] float32 is dL/dS_T (NULL: zero). Gradients with
- * respect to beta and beta_v are singular at 0 (their square roots enter the step).
- * ws must hold gdn_bwd_workspace_bytes(args) bytes, 256-byte aligned. The forward
- * states are recomputed from checkpoints every 64 steps, the state gradient starts
- * from checkpoints taken on its own backward sweep, so the 64-step intervals run in
- * parallel; every sum has a fixed order and results are deterministic. */
+ * page, eq. (1)), taken through the chunkwise WY / UT form of section 2.4 on 16-step
+ * chunks. gdn_args.stabilize must be 0 (GDN_ERR_UNSUPPORTED otherwise), and
+ * B * H * T * n_h may not exceed 2^33 (GDN_ERR_UNSUPPORTED). args as for the forward
+ * pass (o, s_final and chunk are ignored; s0 NULL means zero); d_o [B, T, H, dv] in
+ * args->dtype is dL/do; d_s_final [B, H, dk, dv] float32 is dL/dS_T (NULL: zero).
+ * Gradients with respect to beta and beta_v are singular at 0 (their square roots
+ * enter the step). ws must hold gdn_bwd_workspace_bytes(args) bytes, 256-byte
+ * aligned. Decay factors span at most 8 steps of a chunk, so, as in the chunked
+ * forward pass, results stay in float32 range while no channel decays by more than
+ * e^-87 over 8 consecutive steps (alpha >= 1.9e-5 at every step suffices); beyond
+ * that they can overflow. Every sum has a fixed order: results are deterministic. */
 int gdn_recurrent_bwd(const gdn_args* args, const void* d_o, const float* d_s_final,
                       const gdn_grads* grads, void* ws, size_t ws_bytes, void* stream);
 
