@@ -15,21 +15,22 @@
 //   dP = tril(dO U^T),   dM = -strict_tril(dR U^T),
 //   dS = Gamma D + Q+^T dO - W^T dU = Gamma D - W^T (A^ D) + (Q+ - P W)^T dO,
 //   dQ+ = dO S^T + dP A-,  dB+ = -dR S^T + dM A-,  dA- = dP^T Q+ + dM^T B+,  dA^ = U D^T,
-// and the decay through dG = q.dq + b.db - a.da (at the last step also the A^ and Gamma
-// terms), d log alpha being the suffix sum of dG over the chunk.
+// and the decay through dG = q.dq + b.db - a.da: d log alpha_l is the sum of dG over the
+// steps from l on, plus the Gamma term, plus the A^ terms of the steps before l.
 //
 // e^-G is never formed: the Grams and the products with A- take factors split at the
 // chunk's step 8, e^(G - G_8) on the B+ / Q+ side and e^(G_8 - G) on the A- side, so no
 // factor spans more than 8 steps of decay; e^G, e^(G_C - G) and Gamma are at most 1.
+// Every factor is a product of the alphas it spans.
 //
 // Kernels (all arithmetic in float32, products on fp32 MFMA):
 //  1. operands: every step's a, b, alpha, q rows and w, do columns (the variant's map),
 //     then identity steps up to a whole chunk;
 //  2. records: per chunk, the Grams, T by forward substitution, W, U~, A^, Q+ - P W and
 //     Gamma, each stored in the lane order of the products that read it;
-//  3. recursions: the state forward and its gradient backward over the chunks, one wave
-//     per (batch*head, 16 value columns) and direction; the state before and the
-//     gradient after every chunk are stored;
+//  3. recursions: the state forward and its gradient backward over the chunks, one
+//     four-wave workgroup per (batch*head, 16 value columns) and direction; the state
+//     before and the gradient after every chunk are stored;
 //  4. intra-chunk gradients: every chunk on its own, from the two stored matrices;
 //  5. reduce: the variant's chain rule.
 // Every sum runs in a fixed order: the results are deterministic.
