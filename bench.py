@@ -37,6 +37,7 @@ METRIC = "FG²-GDN chunked prefill tokens/s at 32K (H=16,d=128); % of MFMA/HBM r
 WORKLOAD = gdn_inputs.CONFIGS[2]
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA
+MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 MFMA
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "chunk_traffic_fg2_32k.json")
 CSRC = os.path.join(ROOT, "gated_delta_rule_69_amd", "csrc")
 
@@ -387,7 +388,7 @@ def configs(args):
         nb, nf = alg_per_th(cfg)
         units = B * T * H
         nbytes = nb * units + B * H * dk * dv * 4
-        peak_tf = MFMA_PEAK_TFLOPS if cfg["dtype"] == "bf16" else 157.3
+        peak_tf = MFMA_PEAK_TFLOPS if cfg["dtype"] == "bf16" else MFMA_F32_PEAK_TFLOPS
         gbs = nbytes / (us * 1e-6) / 1e9
         tfs = nf * units / (us * 1e-6) / 1e12
         rows.append(dict(workload=cfg["name"], index=idx, variant=cfg["variant"], dtype=cfg["dtype"],
@@ -531,50 +532,79 @@ def stabilize(args):
 
 
 # ---- backward: gdn_recurrent_bwd on the 4K prefill workload --------------------------
-def backward(args):
-    """Time of one gdn_recurrent_bwd call on workload 1 (FG2, bf16, B=1, H=16, T=4096,
-    d=128; float32 gradients) and of the forward call it differentiates, HBM fraction
-    with the algorithmic bytes (inputs, d_o and the gradients: 6 d bf16 + 5 d float32
-    per token-head), and sequence 0, head 0 of every gradient against the float64
-    oracle."""
+def bwd_flops_per_step(dk, dv, C=16):
+    """Algorithmic flops of the chunkwise backward pass per step (token, or DeltaProduct
+    sub-step) and head: the state and state-gradient recursions (W S, A^^T U; A^ D,
+    W^T X, (Q+ - P W)^T dO) and the intra-chunk products U, A^ D, dO S^T, dR S^T, U D^T,
+    10 dk dv multiply-adds, plus the C x C x d ones of the chunk (Grams, W, U~, Q+ - P W,
+    P^T dO, dR, dP, dM and the four per key tile), about 11 C d."""
+    return 2 * (10 * dk * dv + 11 * C * max(dk, dv))
+
+
+def backward_one(index, steps):
+    """One gdn_recurrent_bwd workload: time per call (HIP events over `steps` calls
+    after 3 warm-ups), HBM fraction of the algorithmic bytes (inputs, d_o and float32
+    gradients) and fp32 MFMA fraction of the algorithmic flops, and every gradient of
+    sequence 0, head 0 against the float64 oracle (rel-L2)."""
     import torch
     import gated_delta_rule_69_amd as gdn
     import oracle
     dev = torch.device("cuda:0")
-    cfg = gdn_inputs.CONFIGS[1]
-    B, T, H, d = cfg["B"], cfg["T"], cfg["H"], cfg["dk"]
-    inp = gdn_inputs.config_inputs(1)
-    t = {n: torch.from_numpy(inp[n]).to(dev).to(torch.bfloat16).contiguous()
-         for n in ("q", "k", "v", "alpha", "beta")}
+    cfg = gdn_inputs.CONFIGS[index]
+    var, B, T, H, dk, dv, nh = (cfg[k] for k in ("variant", "B", "T", "H", "dk", "dv", "n_h"))
+    io = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
+    es = 2 if cfg["dtype"] == "bf16" else 4
+    inp = gdn_inputs.config_inputs(index)
+    t = {n: torch.from_numpy(inp[n]).to(dev).to(io).contiguous()
+         for n in ("q", "k", "v", "alpha", "beta", "beta_v", "j", "eta") if inp.get(n) is not None}
     rng = np.random.default_rng(7)
-    do_np = gdn_inputs.round_bf16(rng.standard_normal((B, T, H, d)).astype(np.float32))
-    do = torch.from_numpy(do_np).to(dev).to(torch.bfloat16)
-    run = lambda: gdn.gdn_recurrent_bwd("fg2", t["q"], t["k"], t["v"], t["alpha"], t["beta"], d_o=do)  # noqa: E731
+    do_np = rng.standard_normal((B, T, H, dv)).astype(np.float32)
+    if cfg["dtype"] == "bf16":
+        do_np = gdn_inputs.round_bf16(do_np)
+    do = torch.from_numpy(do_np).to(dev).to(io)
+    run = lambda: gdn.gdn_recurrent_bwd(var, t["q"], t["k"], t["v"], t["alpha"], t.get("beta"), d_o=do,  # noqa: E731
+                                        beta_v=t.get("beta_v"), j=t.get("j"), eta=t.get("eta"))
     got = run()
     for _ in range(2):
         run()
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         run()
     ev[1].record()
     torch.cuda.synchronize()
-    ms = ev[0].elapsed_time(ev[1]) / args.steps
+    ms = ev[0].elapsed_time(ev[1]) / steps
     sub = {k: (v[0:1, :, 0:1] if isinstance(v, np.ndarray) else v) for k, v in inp.items()}
     sub["B"], sub["H"] = 1, 1
     ref = oracle.backward.backward(sub, do_np[0:1, :, 0:1])
     errs = {n: float(np.linalg.norm(got[n][0:1, :, 0:1].cpu().numpy() - r) / np.linalg.norm(r))
             for n, r in ref.items() if n != "ds0"}
-    nbytes = B * T * H * (6 * d * 2 + 5 * d * 4)
+    steps_th = B * T * H * nh
+    in_bytes = sum(x.numel() * es for x in t.values()) + do.numel() * es
+    out_bytes = sum(x.numel() * 4 for n, x in got.items() if n != "ds0" and x is not None)
+    nbytes = in_bytes + out_bytes
     gbs = nbytes / (ms * 1e-3) / 1e9
-    log(f"backward: {ms:.2f} ms per call ({B * T / (ms * 1e-3):.3e} tokens/s), {gbs:.0f} GB/s "
-        f"({gbs / HBM_PEAK_GBS:.1%}), parity max rel-L2 {max(errs.values()):.2e}")
-    print(json.dumps({"metric": "gdn_recurrent_bwd time, workload 1 (FG2, B=1, H=16, T=4096, d=128, bf16)",
-                      "ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
-                      "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                   "frac": gbs / HBM_PEAK_GBS, "algorithmic": nbytes},
-                      "parity": errs, "data": "synthetic", "n_gpus": 1}), flush=True)
+    flops = bwd_flops_per_step(dk, dv) * steps_th
+    tfs = flops / (ms * 1e-3) / 1e12
+    return dict(workload=cfg["name"], ms=ms, tokens_per_s=B * T / (ms * 1e-3),
+                roofline={"bound": "mfma", "achieved": tfs, "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": tfs / MFMA_F32_PEAK_TFLOPS, "algorithmic": flops},
+                hbm={"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "algorithmic": nbytes},
+                parity=errs)
+
+
+def backward(args):
+    """gdn_recurrent_bwd on workload 1 (FG2, bf16, B=1, H=16, T=4096, d=128), or with
+    --all on workloads 1, 3 and 4: one JSON line each (see backward_one)."""
+    for index in ((1, 3, 4) if args.all else (1,)):
+        r = backward_one(index, args.steps)
+        log(f"backward {r['workload']}: {r['ms']:.3f} ms per call ({r['tokens_per_s']:.3e} tokens/s), "
+            f"{r['roofline']['achieved']:.1f} TFLOP/s fp32 ({r['roofline']['frac']:.1%}), "
+            f"{r['hbm']['achieved']:.0f} GB/s ({r['hbm']['frac']:.1%}), parity max rel-L2 {max(r['parity'].values()):.2e}")
+        print(json.dumps({"metric": f"gdn_recurrent_bwd time, {r['workload']}", **r,
+                          "data": "synthetic", "n_gpus": 1}), flush=True)
 
 
 def fg2_plus(args):
@@ -650,6 +680,8 @@ def main():
                     help="one-token decode step (gdn_recurrent_step) over 512 sequences")
     ap.add_argument("--backward", action="store_true",
                     help="backward pass (gdn_recurrent_bwd) on the 4K prefill workload")
+    ap.add_argument("--all", action="store_true",
+                    help="with --backward: workloads 1, 3 and 4")
     ap.add_argument("--stabilize", action="store_true",
                     help="GDN2 stabilisers (gdn_asym_stabilize) on the asymmetric workload")
     ap.add_argument("--fg2-plus", action="store_true",
