@@ -173,29 +173,65 @@ __device__ __forceinline__ Decay chunk_decay(const float (&al)[4], int l) {
 // q and do act after a token's last step (DeltaProduct: zero for the earlier steps),
 // the gate at its first. Steps from the end of the sequence to the end of its last
 // chunk are identity steps (nothing erased, written or read; no decay).
-template <typename In>
+// R consecutive elements (R = 1 or 2; the address aligned to R elements) as floats.
+template <int R>
+__device__ __forceinline__ void ldr(const float* p, float (&o)[R]) {
+  if constexpr (R == 2) {
+    const float2 x = *reinterpret_cast<const float2*>(p);
+    o[0] = x.x, o[1] = x.y;
+  } else {
+    o[0] = *p;
+  }
+}
+template <int R>
+__device__ __forceinline__ void ldr(const uint16_t* p, float (&o)[R]) {
+  if constexpr (R == 2) {
+    const uint32_t x = *reinterpret_cast<const uint32_t*>(p);
+    o[0] = __uint_as_float(x << 16), o[1] = __uint_as_float(x & 0xffff0000u);
+  } else {
+    o[0] = bf16_to_f32(*p);
+  }
+}
+template <int R>
+__device__ __forceinline__ void str(float* p, const float (&x)[R]) {
+  if constexpr (R == 2) *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
+  else *p = x[0];
+}
+// channels a lane takes in a row of d: d / 64 consecutive ones (lanes past d idle below 64)
+__host__ __device__ constexpr int lane_run(int d) { return d >= 64 ? d / 64 : 1; }
+
+template <typename In, int DK, int DV>
 __global__ __launch_bounds__(256) void bwd_ops_kernel(Problem p, const In* __restrict__ d_o,
                                                       float* __restrict__ ws) {
+  constexpr int RK = lane_run(DK), RV = lane_run(DV);
   const int lane = threadIdx.x & 63;
-  const int64_t NS = p.steps, T = p.T, H = p.H, DK = p.dk, dv = p.dv;
+  const int64_t NS = p.steps, T = p.T, H = p.H;
   const int nh = p.n_h;
-  const BwdLayout L = bwd_layout(p.B, NS, H, DK, dv);
+  const BwdLayout L = bwd_layout(p.B, NS, H, DK, DV);
   const int64_t NP = L.nc * kC;
   const int64_t x = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);  // bh * NP + s
   if (x >= p.B * H * NP) return;
   const int64_t bh = x / NP, s = x % NP;
   float* rw = ws + L.rows + (bh * L.rs + s) * 4 * DK;
-  float* cl = ws + L.cols + (bh * L.rs + s) * 2 * dv;
+  float* cl = ws + L.cols + (bh * L.rs + s) * 2 * DV;
+  const int ek = lane * RK, ev = lane * RV;  // this lane's first channel and column
+  const bool kl = ek < DK, vl = ev < DV;
   if (s >= NS) {
-    for (int64_t e = lane; e < DK; e += 64) {
-      rw[e] = 0.0f;
-      rw[DK + e] = 0.0f;
-      rw[2 * DK + e] = 1.0f;
-      rw[3 * DK + e] = 0.0f;
+    float z[RK], one[RK];
+#pragma unroll
+    for (int r = 0; r < RK; ++r) z[r] = 0.0f, one[r] = 1.0f;
+    if (kl) {
+      str<RK>(rw + ek, z);
+      str<RK>(rw + DK + ek, z);
+      str<RK>(rw + 2 * DK + ek, one);
+      str<RK>(rw + 3 * DK + ek, z);
     }
-    for (int64_t c = lane; c < dv; c += 64) {
-      cl[c] = 0.0f;
-      cl[dv + c] = 0.0f;
+    float zv[RV];
+#pragma unroll
+    for (int r = 0; r < RV; ++r) zv[r] = 0.0f;
+    if (vl) {
+      str<RV>(cl + ev, zv);
+      str<RV>(cl + DV + ev, zv);
     }
     return;
   }
@@ -226,30 +262,43 @@ __global__ __launch_bounds__(256) void bwd_ops_kernel(Problem p, const In* __res
     sc = sqrtf(ld(be + th));
     if (var == GDN_VARIANT_GDN) gate = ld(al + th);
   }
-  for (int64_t e = lane; e < DK; e += 64) {
-    const float kr = ld(k + sr * DK + e);
-    float a, bb, alpha;
-    if (var == GDN_VARIANT_DELTAPRODUCT) {
-      a = kr, bb = sc * kr, alpha = gate;
-    } else if (var == GDN_VARIANT_ASYM) {
-      a = kr, bb = ld(jv + th * DK + e) * sc, alpha = ld(al + th * DK + e);
-    } else if (var == GDN_VARIANT_FG2) {
-      a = kr * sqrtf(ld(be + th * DK + e)), bb = a, alpha = ld(al + th * DK + e);
-    } else {
-      a = kr * sc, bb = a, alpha = var == GDN_VARIANT_KDA ? ld(al + th * DK + e) : gate;
+  if (kl) {
+    float kr[RK], a[RK], bb[RK], alpha[RK], qq[RK], x1[RK], x2[RK];
+    ldr<RK>(k + sr * DK + ek, kr);
+    if (var == GDN_VARIANT_ASYM || var == GDN_VARIANT_FG2 || var == GDN_VARIANT_KDA) ldr<RK>(al + th * DK + ek, x1);
+    if (var == GDN_VARIANT_ASYM) ldr<RK>(jv + th * DK + ek, x2);
+    if (var == GDN_VARIANT_FG2) ldr<RK>(be + th * DK + ek, x2);
+    if (last) ldr<RK>(q + th * DK + ek, qq);
+#pragma unroll
+    for (int r = 0; r < RK; ++r) {
+      if (var == GDN_VARIANT_DELTAPRODUCT) {
+        a[r] = kr[r], bb[r] = sc * kr[r], alpha[r] = gate;
+      } else if (var == GDN_VARIANT_ASYM) {
+        a[r] = kr[r], bb[r] = x2[r] * sc, alpha[r] = x1[r];
+      } else if (var == GDN_VARIANT_FG2) {
+        a[r] = kr[r] * sqrtf(x2[r]), bb[r] = a[r], alpha[r] = x1[r];
+      } else {
+        a[r] = kr[r] * sc, bb[r] = a[r], alpha[r] = var == GDN_VARIANT_KDA ? x1[r] : gate;
+      }
+      if (!last) qq[r] = 0.0f;
     }
-    rw[e] = a;
-    rw[DK + e] = bb;
-    rw[2 * DK + e] = alpha;
-    rw[3 * DK + e] = last ? ld(q + th * DK + e) : 0.0f;
+    str<RK>(rw + ek, a);
+    str<RK>(rw + DK + ek, bb);
+    str<RK>(rw + 2 * DK + ek, alpha);
+    str<RK>(rw + 3 * DK + ek, qq);
   }
-  for (int64_t c = lane; c < dv; c += 64) {
-    const float vc = ld(v + sr * dv + c);
-    float w;
-    if (var == GDN_VARIANT_FG2) w = vc * sqrtf(ld(bev ? bev + th * dv + c : be + th * DK + c));
-    else w = sc * vc;
-    cl[c] = w;
-    cl[dv + c] = last ? ld(d_o + th * dv + c) : 0.0f;
+  if (vl) {
+    float vc[RV], w[RV], dd[RV], bs[RV];
+    ldr<RV>(v + sr * DV + ev, vc);
+    if (var == GDN_VARIANT_FG2) ldr<RV>(bev ? bev + th * DV + ev : be + th * DK + ev, bs);
+    if (last) ldr<RV>(d_o + th * DV + ev, dd);
+#pragma unroll
+    for (int r = 0; r < RV; ++r) {
+      w[r] = var == GDN_VARIANT_FG2 ? vc[r] * sqrtf(bs[r]) : sc * vc[r];
+      if (!last) dd[r] = 0.0f;
+    }
+    str<RV>(cl + ev, w);
+    str<RV>(cl + DV + ev, dd);
   }
 }
 
@@ -721,14 +770,16 @@ __global__ __launch_bounds__(64) void bwd_intra_kernel(Problem p, float* __restr
 }
 
 // ---- 5. reduce kernel -------------------------------------------------------------
-// One wave per step row: the variant's chain rule.
-template <typename In, int DK>
+// One wave per step row: the variant's chain rule (a lane takes dk / 64 consecutive
+// channels and dv / 64 consecutive columns).
+template <typename In, int DK, int DV>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(Problem p, GradPtrs g, const float* __restrict__ ws) {
+  constexpr int RK = lane_run(DK), RV = lane_run(DV);
   const int lane = threadIdx.x & 63;
-  const int64_t T = p.T, H = p.H, dv = p.dv;
+  const int64_t T = p.T, H = p.H;
   const int nh = p.n_h;
   const int64_t bth = p.B * T * H * nh;  // step rows
-  const BwdLayout L = bwd_layout(p.B, p.steps, H, DK, dv);
+  const BwdLayout L = bwd_layout(p.B, p.steps, H, DK, DV);
   const float* part = ws + L.part;
   const float* dwg = ws + L.dw;
   const In* k = static_cast<const In*>(p.k);
@@ -738,6 +789,9 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(Problem p, GradPtrs g, 
   const In* jv = static_cast<const In*>(p.j);
   const In* et = static_cast<const In*>(p.eta);
   auto ld = [](const In* x) { return IO<In>::ld(x); };
+  const int ek = lane * RK, ev = lane * RV;
+  const bool kl = ek < DK, vl = ev < DV;
+  const int var = p.variant;
   const int64_t stride = int64_t(gridDim.x) * (blockDim.x / 64);
   for (int64_t th = int64_t(blockIdx.x) * (blockDim.x / 64) + (threadIdx.x >> 6); th < bth; th += stride) {
     // the gradients of step row th = ((b T + t) H + h) n_h + sub sit at head b H + h, step t n_h + sub
@@ -745,20 +799,39 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(Problem p, GradPtrs g, 
     const int64_t bt = tok / H;
     const int64_t prow = ((bt / T) * H + tok % H) * p.steps + (bt % T) * nh + (th - tok * nh);
     const float* pr = part + prow * 4 * DK;
-    if (p.variant == GDN_VARIANT_DELTAPRODUCT) {  // th is a step row (token x n_h + step)
+    float dq[RK], da[RK], db[RK], dal[RK], dw[RV];
+    if (kl) {
+      ldr<RK>(pr + ek, dq);
+      ldr<RK>(pr + DK + ek, da);
+      ldr<RK>(pr + 2 * DK + ek, db);
+      ldr<RK>(pr + 3 * DK + ek, dal);
+    }
+    if (vl) ldr<RV>(dwg + prow * DV + ev, dw);
+    if (var == GDN_VARIANT_DELTAPRODUCT) {  // th is a step row (token x n_h + step)
       const int sub = int(th - tok * nh);
-      const float bt = ld(be + th);
+      const float bt2 = ld(be + th);
       float sb = 0.0f, sal = 0.0f;
-      for (int r = lane; r < DK; r += 64) {
-        g.dk[th * DK + r] = pr[DK + r] + bt * pr[2 * DK + r];
-        sb += ld(k + th * DK + r) * pr[2 * DK + r];
-        sal += pr[3 * DK + r];
-        if (sub == nh - 1) g.dq[tok * DK + r] = pr[r];
+      if (kl) {
+        float kr[RK], dk[RK];
+        ldr<RK>(k + th * DK + ek, kr);
+#pragma unroll
+        for (int r = 0; r < RK; ++r) {
+          dk[r] = da[r] + bt2 * db[r];
+          sb += kr[r] * db[r];
+          sal += dal[r];
+        }
+        str<RK>(g.dk + th * DK + ek, dk);
+        if (sub == nh - 1) str<RK>(g.dq + tok * DK + ek, dq);
       }
-      for (int cc = lane; cc < dv; cc += 64) {
-        const float dw = dwg[prow * dv + cc];
-        g.dv[th * dv + cc] = bt * dw;
-        sb += ld(v + th * dv + cc) * dw;
+      if (vl) {
+        float vc[RV], dvo[RV];
+        ldr<RV>(v + th * DV + ev, vc);
+#pragma unroll
+        for (int r = 0; r < RV; ++r) {
+          dvo[r] = bt2 * dw[r];
+          sb += vc[r] * dw[r];
+        }
+        str<RV>(g.dv + th * DV + ev, dvo);
       }
       const float tb = wave_sum(sb);
       if (lane == 0) g.dbeta[th] = tb;
@@ -769,60 +842,85 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(Problem p, GradPtrs g, 
       continue;
     }
     float sk = 0.0f, sv = 0.0f, sj = 0.0f, sal = 0.0f;  // per-token sums
-    const float sbeta = (p.variant == GDN_VARIANT_KDA || p.variant == GDN_VARIANT_GDN) ? sqrtf(ld(be + th)) : 1.0f;
-    const float e = p.variant == GDN_VARIANT_ASYM ? ld(et + th) : 0.0f;
-    for (int r = lane; r < DK; r += 64) {
-      const float dab = pr[DK + r] + pr[2 * DK + r], dal = pr[3 * DK + r];
-      const int64_t ir = th * DK + r;
-      g.dq[ir] = pr[r];
-      const float kr = ld(k + ir);
-      if (p.variant == GDN_VARIANT_FG2) {
-        const float s = sqrtf(ld(be + ir));
-        g.dk[ir] = s * dab;
-        g.dalpha[ir] = dal;
-        float db = kr * dab;
-        if (!bev) db += ld(v + th * dv + r) * dwg[prow * dv + r];  // shared beta (dk == dv)
-        g.dbeta[ir] = db / (2.0f * s);
-      } else if (p.variant == GDN_VARIANT_ASYM) {
-        g.dk[ir] = pr[DK + r];
-        g.dj[ir] = e * pr[2 * DK + r];
-        g.dalpha[ir] = dal;
-        sj += ld(jv + ir) * pr[2 * DK + r];
-      } else {
-        g.dk[ir] = sbeta * dab;
-        sk += kr * dab;
-        if (p.variant == GDN_VARIANT_KDA) g.dalpha[ir] = dal;
-        else sal += dal;
-      }
-    }
-    for (int cc = lane; cc < dv; cc += 64) {
-      const float dw = dwg[prow * dv + cc];
-      const int64_t ic = th * dv + cc;
-      const float vc = ld(v + ic);
-      if (p.variant == GDN_VARIANT_FG2) {
-        if (bev) {
-          const float s = sqrtf(ld(bev + ic));
-          g.dv[ic] = s * dw;
-          g.dbeta_v[ic] = vc * dw / (2.0f * s);
-        } else {
-          g.dv[ic] = sqrtf(ld(be + th * DK + cc)) * dw;
+    const float sbeta = (var == GDN_VARIANT_KDA || var == GDN_VARIANT_GDN) ? sqrtf(ld(be + th)) : 1.0f;
+    const float e = var == GDN_VARIANT_ASYM ? ld(et + th) : 0.0f;
+    if (kl) {
+      const int64_t ir = th * DK + ek;
+      float kr[RK], x[RK], dk[RK], o1[RK], o2[RK];
+      ldr<RK>(k + ir, kr);
+      str<RK>(g.dq + ir, dq);
+      if (var == GDN_VARIANT_FG2) {
+        ldr<RK>(be + ir, x);
+        float vc[RK], dwk[RK];
+        if (!bev) {  // shared beta (dk == dv): the value side of channel c as well
+          ldr<RK>(v + th * DV + ek, vc);
+          ldr<RK>(dwg + prow * DV + ek, dwk);
         }
-      } else if (p.variant == GDN_VARIANT_ASYM) {
-        g.dv[ic] = e * dw;
-        sv += vc * dw;
+#pragma unroll
+        for (int r = 0; r < RK; ++r) {
+          const float sq = sqrtf(x[r]), dab = da[r] + db[r];
+          dk[r] = sq * dab;
+          float d2 = kr[r] * dab;
+          if (!bev) d2 += vc[r] * dwk[r];
+          o1[r] = d2 / (2.0f * sq);
+        }
+        str<RK>(g.dk + ir, dk);
+        str<RK>(g.dalpha + ir, dal);
+        str<RK>(g.dbeta + ir, o1);
+      } else if (var == GDN_VARIANT_ASYM) {
+        ldr<RK>(jv + ir, x);
+#pragma unroll
+        for (int r = 0; r < RK; ++r) {
+          o2[r] = e * db[r];
+          sj += x[r] * db[r];
+        }
+        str<RK>(g.dk + ir, da);
+        str<RK>(g.dj + ir, o2);
+        str<RK>(g.dalpha + ir, dal);
       } else {
-        g.dv[ic] = sbeta * dw;
-        sv += vc * dw;
+#pragma unroll
+        for (int r = 0; r < RK; ++r) {
+          const float dab = da[r] + db[r];
+          dk[r] = sbeta * dab;
+          sk += kr[r] * dab;
+          sal += dal[r];
+        }
+        str<RK>(g.dk + ir, dk);
+        if (var == GDN_VARIANT_KDA) str<RK>(g.dalpha + ir, dal);
       }
     }
-    if (p.variant == GDN_VARIANT_KDA || p.variant == GDN_VARIANT_GDN) {
+    if (vl) {
+      const int64_t ic = th * DV + ev;
+      float vc[RV], dvo[RV], o3[RV];
+      ldr<RV>(v + ic, vc);
+      if (var == GDN_VARIANT_FG2) {
+        float bs[RV];
+        ldr<RV>(bev ? bev + ic : be + th * DK + ev, bs);
+#pragma unroll
+        for (int r = 0; r < RV; ++r) {
+          const float sq = sqrtf(bs[r]);
+          dvo[r] = sq * dw[r];
+          o3[r] = vc[r] * dw[r] / (2.0f * sq);
+        }
+        if (bev) str<RV>(g.dbeta_v + ic, o3);
+      } else {
+        const float sc = var == GDN_VARIANT_ASYM ? e : sbeta;
+#pragma unroll
+        for (int r = 0; r < RV; ++r) {
+          dvo[r] = sc * dw[r];
+          sv += vc[r] * dw[r];
+        }
+      }
+      str<RV>(g.dv + ic, dvo);
+    }
+    if (var == GDN_VARIANT_KDA || var == GDN_VARIANT_GDN) {
       const float tot = wave_sum(sk + sv);
       if (lane == 0) g.dbeta[th] = tot / (2.0f * sbeta);
-      if (p.variant == GDN_VARIANT_GDN) {
+      if (var == GDN_VARIANT_GDN) {
         const float ta = wave_sum(sal);
         if (lane == 0) g.dalpha[th] = ta;
       }
-    } else if (p.variant == GDN_VARIANT_ASYM) {
+    } else if (var == GDN_VARIANT_ASYM) {
       const float tot = wave_sum(sj + sv);
       if (lane == 0) g.deta[th] = tot;
     }
@@ -836,7 +934,7 @@ int launch_shape(const Problem& p, const In* dO, const float* dsf, const GradPtr
   const int64_t items = bh * L.nc;  // (batch*head, chunk) pairs
   // grids: B*H*steps <= 2^33 (checked by the caller), so every one fits 32 bits
   if (items > 0) {
-    bwd_ops_kernel<In><<<dim3(unsigned((items * kC + 3) / 4)), dim3(256), 0, s>>>(p, dO, ws);
+    bwd_ops_kernel<In, DK, DV><<<dim3(unsigned((items * kC + 3) / 4)), dim3(256), 0, s>>>(p, dO, ws);
     bwd_rec_kernel<DK, DV><<<dim3(unsigned(items)), dim3(64), 0, s>>>(p, ws);
   }
   bwd_chain_kernel<DK, DV><<<dim3(unsigned(2 * bh * (DV / 16))), dim3(64 * chain_waves(DK)), 0, s>>>(p, dsf, g.ds0, ws);
@@ -844,7 +942,7 @@ int launch_shape(const Problem& p, const In* dO, const float* dsf, const GradPtr
   bwd_intra_kernel<DK, DV><<<dim3(unsigned(items)), dim3(64), 0, s>>>(p, ws);
   const int64_t waves = p.B * p.T * p.H * p.n_h;
   const int64_t blocks = (waves + 3) / 4;
-  bwd_reduce_kernel<In, DK><<<dim3(unsigned(blocks < (int64_t(1) << 20) ? blocks : (int64_t(1) << 20))), dim3(256), 0, s>>>(p, g, ws);
+  bwd_reduce_kernel<In, DK, DV><<<dim3(unsigned(blocks < (int64_t(1) << 20) ? blocks : (int64_t(1) << 20))), dim3(256), 0, s>>>(p, g, ws);
   return int(hipGetLastError());
 }
 
