@@ -304,7 +304,9 @@ def gdn_recurrent_bwd(variant, q, k, v, alpha, beta=None, *, d_o, s0=None, ds_fi
                       beta_v=None, j=None, eta=None, workspace=None, stream=None):
     """Gradients (float32 tensors, named after the inputs: dq, dk, dv, dalpha, dbeta,
     dbeta_v, dj, deta, ds0) of the token recurrence for upstream d_o (shape of o, input
-    dtype) and ds_final (float32 state shape, optional)."""
+    dtype) and ds_final (float32 state shape, optional); the library computes them in
+    the chunkwise form on 16-step chunks. A workspace of gdn_bwd_workspace_bytes is
+    allocated when none is given."""
     import torch
     dev = k.device
     _check(d_o, "d_o", dev, k.dtype)

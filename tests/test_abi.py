@@ -153,6 +153,12 @@ def test_backward_checks(lib):
     assert call(a, GdnGrads(dq=FAKE, dk=FAKE, dv=FAKE, dalpha=FAKE, dbeta=FAKE, dj=FAKE)) == -1
     assert call(good_args(variant=4, j=FAKE, eta=FAKE, stabilize=1), GdnGrads(dq=FAKE, dk=FAKE, dv=FAKE, dalpha=FAKE, dj=FAKE, deta=FAKE)) == -2
     assert lib.gdn_bwd_workspace_bytes(ctypes.byref(good_args(dk=48))) == 0
+    # at most 2^33 steps over all heads (every launch grid stays in 32 bits)
+    big = dict(B=1, H=1 << 10, T=1 << 23)
+    assert lib.gdn_bwd_workspace_bytes(ctypes.byref(good_args(**big))) > 0          # 2^33 steps
+    assert lib.gdn_bwd_workspace_bytes(ctypes.byref(good_args(B=2, H=1 << 10, T=1 << 23))) == 0
+    assert call(good_args(B=2, H=1 << 10, T=1 << 23), full, FAKE, 1 << 62) == -2
+    assert lib.gdn_bwd_workspace_bytes(ctypes.byref(good_args(variant=3, n_h=2, **big))) == 0
 
 
 def test_stabilize_checks(lib):
