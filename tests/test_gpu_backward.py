@@ -154,3 +154,37 @@ def test_backward_empty_sequence():
     got = gdn.gdn_recurrent_bwd("fg2", q, k, v, al, be, d_o=z(B, 0, H, d))
     torch.cuda.synchronize()
     assert torch.count_nonzero(got["ds0"]) == 0
+
+
+@pytest.mark.parametrize("index,pairs", [(1, [(0, 0), (0, 15)]), (3, [(3, 7)]), (4, [(0, 5), (7, 31)])],
+                         ids=["workload1", "workload3", "workload4"])
+def test_backward_full_size_sampled_heads(index, pairs):
+    """Workloads 1 (FG2, bf16, T 4096, H 16, d 128), 3 (DeltaProduct n_h 2, T 8192) and 4
+    (ASYM, fp32, d 64, B 8, H 32) at full size: every gradient of the sampled
+    (sequence, head) pairs against the oracle, run on that pair alone."""
+    import gated_delta_rule_69_amd as gdn
+    from gpu_util import DEV, host
+    cfg = gdn_inputs.CONFIGS[index]
+    inp = gdn_inputs.config_inputs(index)
+    B, T, H, dv = cfg["B"], cfg["T"], cfg["H"], cfg["dv"]
+    io = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
+    rng = np.random.default_rng(100 + index)
+    do = rng.standard_normal((B, T, H, dv)).astype(np.float32)
+    if cfg["dtype"] == "bf16":
+        do = gdn_inputs.round_bf16(do)
+    t = {n: torch.from_numpy(inp[n]).to(DEV).to(io) for n in ("q", "k", "v", "alpha", "beta", "beta_v", "j", "eta")
+         if inp.get(n) is not None}
+    got = gdn.gdn_recurrent_bwd(cfg["variant"], t["q"], t["k"], t["v"], t["alpha"], t.get("beta"),
+                                d_o=torch.from_numpy(do).to(DEV).to(io), beta_v=t.get("beta_v"),
+                                j=t.get("j"), eta=t.get("eta"))
+    torch.cuda.synchronize()
+    for b, h in pairs:
+        sub = {k: (v[b:b + 1, :, h:h + 1] if isinstance(v, np.ndarray) else v) for k, v in inp.items()}
+        sub["B"], sub["H"] = 1, 1
+        ref = obwd.backward(sub, do[b:b + 1, :, h:h + 1])
+        for name, r in ref.items():
+            x = host(got[name])
+            x = x[b:b + 1, :, h:h + 1] if name != "ds0" else x[b:b + 1, h:h + 1]
+            e2, em = oracle.rel_l2(x, r), oracle.max_rel(x, r)
+            print(cfg["name"], (b, h), name, f"rel_l2={e2:.2e} max_rel={em:.2e}", flush=True)
+            assert e2 <= 1e-5 and em <= 1e-4, (cfg["name"], b, h, name, e2, em)
