@@ -603,12 +603,24 @@ __global__ __launch_bounds__(64) void bwd_intra_kernel(Problem p, float* __restr
     lw[t][l] = ld4(rec + R::Wr + t * 256 + 4 * l);
     la[t][l] = ld4(rec + R::Ar + t * 256 + 4 * l);
   }
-  float4v pF, tF, id;  // P[4g+e][i], T[4g+e][i], the identity
+  // a 16 x 16 tile transposed through LDS: lane (g, i) writes its column i (rows
+  // 4g..4g+3) as a row of tr, then reads row i (columns 4g..4g+3) back; rows 20
+  // floats apart keep the four lane groups on different banks
+  __shared__ __align__(16) float tr[2][16 * 20];
+  auto transpose = [&](float4v x, int k) __attribute__((always_inline)) {
+    *reinterpret_cast<float4v*>(&tr[k][i * 20 + 4 * g]) = x;
+    asm volatile("" ::: "memory");  // a wave's LDS accesses complete in order: keep this order
+    float4v y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = tr[k][(4 * g + e) * 20 + i];
+    asm volatile("" ::: "memory");
+    return y;
+  };
+  float4v pF, tF;  // P[4g+e][i], T[4g+e][i]
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     pF[e] = rec[R::Pm + (4 * g + e) * 16 + i];
     tF[e] = rec[R::Tm + (4 * g + e) * 16 + i];
-    id[e] = 4 * g + e == i ? 1.0f : 0.0f;
   }
   const bool row_live = c * kC + i < NS;
   // over the value tiles: dP, dM (both orientations: dp[e] = dP[4g+e][i], dpt[e] =
@@ -649,8 +661,8 @@ __global__ __launch_bounds__(64) void bwd_intra_kernel(Problem p, float* __restr
     dmt = mma4(ut, rt, dmt);
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
-      const float4v sT = mma4(sf[t], id, zero4());  // S[16t+i][16vt+4g+e]
-      const float4v dT = mma4(df[t], id, zero4());
+      const float4v sT = transpose(sf[t], 0);  // S[16t+i][16vt+4g+e]
+      const float4v dT = transpose(df[t], 1);
       qs[t] = mma4(doA, sT, qs[t]);
       rs[t] = mma4(rt, sT, rs[t]);
       ud[t] = mma4(ut, dT, ud[t]);
