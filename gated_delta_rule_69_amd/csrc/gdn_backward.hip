@@ -103,6 +103,22 @@ __device__ __forceinline__ float4v mma4(float4v a, float4v b, float4v acc) {
   return acc;
 }
 
+// A 16 x 16 tile in the fragment order (lane i + 16g holds X[4g+e][i]) returned in the
+// row order (X[i][4g+e]) through a 16 x 20 float LDS tile of the calling wave: one
+// 16-byte write of the lane's column, four reads of its row (rows 20 floats apart put
+// the four lane groups on different banks). A wave's LDS accesses complete in order;
+// the empty asm statements keep the compiler from reordering them.
+__device__ __forceinline__ float4v lds_transpose(float* tr, float4v x, int l) {
+  const int i = l & 15, g = l >> 4;
+  *reinterpret_cast<float4v*>(tr + i * 20 + 4 * g) = x;
+  asm volatile("" ::: "memory");
+  float4v y;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) y[e] = tr[(4 * g + e) * 20 + i];
+  asm volatile("" ::: "memory");
+  return y;
+}
+
 // Sum of x over the lane groups below this lane's (lanes l - 16, l - 32, l - 48).
 __device__ __forceinline__ float group_prefix(float x, int l) {
   const int g = l >> 4;
@@ -304,8 +320,7 @@ __global__ __launch_bounds__(256) void bwd_ops_kernel(Problem p, const In* __res
 
 // ---- 2. record kernel -------------------------------------------------------------
 // One wave per (batch*head, chunk). The operands are formed in the fragment order
-// (step 4g+e, channel 16t+i) and turned into the row order the Grams need by an MFMA
-// against the identity (exact).
+// (step 4g+e, channel 16t+i) and turned into the row order the Grams need through LDS.
 template <int DK, int DV>
 __global__ __launch_bounds__(64) void bwd_rec_kernel(Problem p, float* __restrict__ ws) {
   constexpr int KT = DK / 16, VT = DV / 16;
@@ -320,9 +335,7 @@ __global__ __launch_bounds__(64) void bwd_rec_kernel(Problem p, float* __restric
   const float* rb = ws + L.rows + (bh * L.rs + c * kC) * 4 * DK;  // step s of the chunk at rb + s 4 DK
   const float* cb = ws + L.cols + (bh * L.rs + c * kC) * 2 * DV;
   float* rec = ws + L.rec + item * R::size;
-  float4v id;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) id[e] = 4 * g + e == i ? 1.0f : 0.0f;
+  __shared__ __align__(16) float tr[16 * 20];  // tile transposes
 
   // per key tile: B+, Q+, A^ (fragment order) kept for W and Q+ - P W; the Grams
   // M = strict_tril(B~ A~^T), P = tril(Q~ A~^T) with B~ = b e^(G - G_8), Q~ = q e^(G - G_8),
@@ -353,11 +366,11 @@ __global__ __launch_bounds__(64) void bwd_rec_kernel(Problem p, float* __restric
       qt[e] = qv[e] * d.up[e];
       at[e] = av[e] * d.dn[e];
     }
-    const float4v btr = mma4(bt, id, zero4()), qtr = mma4(qt, id, zero4()), atr = mma4(at, id, zero4());
+    const float4v btr = lds_transpose(tr, bt, l), qtr = lds_transpose(tr, qt, l), atr = lds_transpose(tr, at, l);
     m = mma4(btr, atr, m);  // M[4g+e][i] = B~[4g+e] . A~[i]
     pp = mma4(qtr, atr, pp);
     st4(rec + R::Af + t * 256 + 4 * l, aF);
-    st4(rec + R::Ar + t * 256 + 4 * l, mma4(aF, id, zero4()));  // A^ in the row order
+    st4(rec + R::Ar + t * 256 + 4 * l, lds_transpose(tr, aF, l));  // A^ in the row order
     if (g == 0) rec[R::Gm + ch] = d.gam;
   }
 #pragma unroll
@@ -578,8 +591,7 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void bwd_chain_kernel(Problem
 // from the recursions, the chunk's record and operands; writes every step's dq, da,
 // db, dalpha and dw. The value columns are taken 16 at a time: each S and D tile is
 // read once, used in the fragment order for U and A^ D (sums over key channels), and
-// transposed in registers (an MFMA against the identity, exact) for dO S^T, dR S^T and
-// U D^T (sums over value channels).
+// transposed through LDS for dO S^T, dR S^T and U D^T (sums over value channels).
 template <int DK, int DV>
 __global__ __launch_bounds__(64) void bwd_intra_kernel(Problem p, float* __restrict__ ws) {
   constexpr int KT = DK / 16, VT = DV / 16;
@@ -603,19 +615,7 @@ __global__ __launch_bounds__(64) void bwd_intra_kernel(Problem p, float* __restr
     lw[t][l] = ld4(rec + R::Wr + t * 256 + 4 * l);
     la[t][l] = ld4(rec + R::Ar + t * 256 + 4 * l);
   }
-  // a 16 x 16 tile transposed through LDS: lane (g, i) writes its column i (rows
-  // 4g..4g+3) as a row of tr, then reads row i (columns 4g..4g+3) back; rows 20
-  // floats apart keep the four lane groups on different banks
-  __shared__ __align__(16) float tr[2][16 * 20];
-  auto transpose = [&](float4v x, int k) __attribute__((always_inline)) {
-    *reinterpret_cast<float4v*>(&tr[k][i * 20 + 4 * g]) = x;
-    asm volatile("" ::: "memory");  // a wave's LDS accesses complete in order: keep this order
-    float4v y;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) y[e] = tr[k][(4 * g + e) * 20 + i];
-    asm volatile("" ::: "memory");
-    return y;
-  };
+  __shared__ __align__(16) float tr[2][16 * 20];  // transposes of the S and D tiles
   float4v pF, tF;  // P[4g+e][i], T[4g+e][i]
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -661,8 +661,8 @@ __global__ __launch_bounds__(64) void bwd_intra_kernel(Problem p, float* __restr
     dmt = mma4(ut, rt, dmt);
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
-      const float4v sT = transpose(sf[t], 0);  // S[16t+i][16vt+4g+e]
-      const float4v dT = transpose(df[t], 1);
+      const float4v sT = lds_transpose(tr[0], sf[t], l);  // S[16t+i][16vt+4g+e]
+      const float4v dT = lds_transpose(tr[1], df[t], l);
       qs[t] = mma4(doA, sT, qs[t]);
       rs[t] = mma4(rt, sT, rs[t]);
       ud[t] = mma4(ut, dT, ud[t]);
