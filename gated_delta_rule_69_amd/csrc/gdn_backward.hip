@@ -30,8 +30,9 @@
 //     Gamma, each stored in the lane order of the products that read it;
 //  3. recursions: the state forward and its gradient backward over the chunks, one
 //     four-wave workgroup per (batch*head, 16 value columns) and direction; the state
-//     before and the gradient after every chunk are stored;
-//  4. intra-chunk gradients: every chunk on its own, from the two stored matrices;
+//     before every even chunk and the gradient after every odd one are stored;
+//  4. intra-chunk gradients: the chunks in pairs, one wave each; each wave rebuilds
+//     the matrix its partner lacks from its own chunk's record;
 //  5. reduce: the variant's chain rule.
 // Every sum runs in a fixed order: the results are deterministic.
 //
@@ -48,8 +49,8 @@
 namespace gdn {
 namespace {
 
-constexpr int kC = 16;    // steps a chunk
-constexpr int kPad = kC;  // operand rows after a sequence (identity steps fill its last chunk)
+constexpr int kC = 16;        // steps a chunk
+constexpr int kPad = 2 * kC;  // operand rows after a sequence (identity steps fill its last chunk pair)
 
 // Record of one chunk (float offsets): W (fragment, row order), A^ (fragment, row
 // order), Q+ - P W (fragment), U~ (fragment, row order), Gamma, T and P (row-major 16 x 16).
@@ -66,8 +67,8 @@ struct Rec {
 //   rows [B*H][NS + kPad][4][dk]   a, b, alpha, q
 //   cols [B*H][NS + kPad][2][dv]   w, do
 //   rec  [B*H][chunks][rec_floats]
-//   sst  [B*H][chunks][dk/16][dv/16][64 lanes][4]   state before the chunk (fragment order)
-//   dst  [B*H][chunks][dk/16][dv/16][64 lanes][4]   dL/dS after the chunk
+//   sst  [B*H][chunks/2][dk/16][dv/16][64 lanes][4]   state before chunk 2m (fragment order)
+//   dst  [B*H][chunks/2][dk/16][dv/16][64 lanes][4]   dL/dS after chunk 2m + 1
 //   part [B*H][NS][4][dk]   dq, da, db, dalpha of each step
 //   dw   [B*H][NS][dv]
 struct BwdLayout {
@@ -78,14 +79,14 @@ struct BwdLayout {
 __host__ __device__ inline BwdLayout bwd_layout(int64_t B, int64_t NS, int64_t H, int64_t dk, int64_t dv) {
   BwdLayout L;
   const int64_t bh = B * H;
-  L.nc = (NS + kC - 1) / kC;
+  L.nc = ((NS + kC - 1) / kC + 1) & ~int64_t(1);  // an even number: chunks go in pairs
   L.rs = NS + kPad;
   L.rows = 0;
   L.cols = L.rows + bh * L.rs * 4 * dk;
   L.rec = L.cols + bh * L.rs * 2 * dv;
   L.sst = L.rec + bh * L.nc * rec_floats(dk, dv);
-  L.dst = L.sst + bh * L.nc * dk * dv;
-  L.part = L.dst + bh * L.nc * dk * dv;
+  L.dst = L.sst + bh * (L.nc / 2) * dk * dv;
+  L.part = L.dst + bh * (L.nc / 2) * dk * dv;
   L.dw = L.part + bh * NS * 4 * dk;
   L.total = L.dw + bh * NS * dv;
   if (L.total < 64) L.total = 64;  // a valid empty problem still reports a nonzero size
@@ -420,9 +421,11 @@ __global__ __launch_bounds__(64) void bwd_rec_kernel(Problem p, float* __restric
 }
 
 // ---- 3. recursions ----------------------------------------------------------------
-// Blocks [0, B*H*dv/16): the state S_{c+1} = Gamma S_c + A^^T (U~ - W S_c), storing S_c.
-// Blocks [B*H*dv/16, 2 B*H*dv/16): its gradient D_{c-1} = Gamma D_c - W^T (A^ D_c) +
-// (Q+ - P W)^T dO_c from D = dL/dS_final, storing D_c; D_{-1} is dL/dS_0.
+// Blocks [0, B*H*dv/16): the state S_{c+1} = Gamma S_c + A^^T (U~ - W S_c), storing S_c
+// for even c. Blocks [B*H*dv/16, 2 B*H*dv/16): its gradient D_{c-1} = Gamma D_c -
+// W^T (A^ D_c) + (Q+ - P W)^T dO_c from D = dL/dS_final, storing D_c for odd c; D_{-1}
+// is dL/dS_0. (The intra-chunk kernel rebuilds the other halves; the stores are what
+// the recursions' time depends on most.)
 // A block holds one 16-column slice (dk x 16) in accumulator tiles, its key tiles split
 // over up to four waves; the 16 x 16 products summed over the key channels (W S, A^ D)
 // are added up through LDS in wave order, one barrier a chunk. Each wave loads the next
@@ -444,6 +447,13 @@ struct GOps {
 // back into a load at the point of use. Whole ring groups run with unconditional
 // refills (clamped to the last chunk), the remainder without any.
 constexpr int kRing = 4;
+static_assert(kRing % 2 == 0, "a ring group starts on an even chunk");
+
+// compile-time flag: whether a recursion step stores its tile
+template <bool B>
+struct Keep {
+  static constexpr bool value = B;
+};
 
 template <int DK, int DV>
 __global__ __launch_bounds__(64 * chain_waves(DK)) void bwd_chain_kernel(Problem p, const float* __restrict__ dsf,
@@ -489,10 +499,12 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void bwd_chain_kernel(Problem
       }
       o.uf = ld4(r + R::Uf + vt * 256 + 4 * l);
     };
-    auto step = [&](int64_t c, const SOps<TW>& o) __attribute__((always_inline)) {
-      float* so = ws + L.sst + (bh * NC + c) * KT * VT * 256;
+    auto step = [&](int64_t c, const SOps<TW>& o, auto keep) __attribute__((always_inline)) {
+      if constexpr (decltype(keep)::value) {  // c even
+        float* so = ws + L.sst + (bh * NC / 2 + c / 2) * KT * VT * 256;
 #pragma unroll
-      for (int j = 0; j < TW; ++j) st4(so + ((w * TW + j) * VT + vt) * 256 + 4 * l, X[j]);
+        for (int j = 0; j < TW; ++j) st4(so + ((w * TW + j) * VT + vt) * 256 + 4 * l, X[j]);
+      }
       float4v pu = zero4();
 #pragma unroll
       for (int j = 0; j < TW; ++j) pu = mma4(o.wr[j], X[j], pu);  // this wave's share of W S
@@ -511,7 +523,9 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void bwd_chain_kernel(Problem
     for (int64_t c0 = 0; c0 < full; c0 += kRing) {
 #pragma unroll
       for (int k = 0; k < kRing; ++k) {
-        step(c0 + k, ring[k]);
+        // c0 and full are multiples of kRing: chunk c0 + k is even exactly when k is
+        if (k % 2 == 0) step(c0 + k, ring[k], Keep<true>());
+        else step(c0 + k, ring[k], Keep<false>());
         int64_t nb = c0 + k + kRing;
         nb = nb < NC ? nb : NC - 1;
         asm volatile("" : "+s"(nb));
@@ -520,8 +534,12 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void bwd_chain_kernel(Problem
       }
     }
 #pragma unroll
-    for (int k = 0; k < kRing; ++k)
-      if (full + k < NC) step(full + k, ring[k]);
+    for (int k = 0; k < kRing; ++k) {
+      if (full + k < NC) {
+        if (k % 2 == 0) step(full + k, ring[k], Keep<true>());
+        else step(full + k, ring[k], Keep<false>());
+      }
+    }
   } else {
 #pragma unroll
     for (int j = 0; j < TW; ++j)
@@ -541,10 +559,12 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void bwd_chain_kernel(Problem
 #pragma unroll
       for (int e = 0; e < 4; ++e) o.dof[e] = cols[(c * kC + 4 * g + e) * 2 * DV];
     };
-    auto step = [&](int64_t c, const GOps<TW>& o) __attribute__((always_inline)) {
-      float* so = ws + L.dst + (bh * NC + c) * KT * VT * 256;
+    auto step = [&](int64_t c, const GOps<TW>& o, auto keep) __attribute__((always_inline)) {
+      if constexpr (decltype(keep)::value) {  // c odd
+        float* so = ws + L.dst + (bh * NC / 2 + c / 2) * KT * VT * 256;
 #pragma unroll
-      for (int j = 0; j < TW; ++j) st4(so + ((w * TW + j) * VT + vt) * 256 + 4 * l, X[j]);
+        for (int j = 0; j < TW; ++j) st4(so + ((w * TW + j) * VT + vt) * 256 + 4 * l, X[j]);
+      }
       float4v px = zero4();
 #pragma unroll
       for (int j = 0; j < TW; ++j) px = mma4(o.ar[j], X[j], px);  // this wave's share of A^ D
@@ -557,7 +577,8 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void bwd_chain_kernel(Problem
       for (int j = 0; j < TW; ++j) X[j] = mma4(o.wf[j], nx, mma4(o.cf[j], o.dof, X[j] * o.gm[j]));
     };
     if (NC > 0) {
-      // chunks from the last: the k-th of a ring group is chunk NC - 1 - (c0 + k)
+      // chunks from the last: the k-th of a ring group is chunk NC - 1 - (c0 + k), odd
+      // exactly when k is even (NC is even, c0 and full multiples of kRing)
       GOps<TW> ring[kRing];
 #pragma unroll
       for (int k = 0; k < kRing; ++k) load(k < NC ? NC - 1 - k : 0, ring[k]);
@@ -565,7 +586,8 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void bwd_chain_kernel(Problem
       for (int64_t c0 = 0; c0 < full; c0 += kRing) {
 #pragma unroll
         for (int k = 0; k < kRing; ++k) {
-          step(NC - 1 - (c0 + k), ring[k]);
+          if (k % 2 == 0) step(NC - 1 - (c0 + k), ring[k], Keep<true>());
+          else step(NC - 1 - (c0 + k), ring[k], Keep<false>());
           int64_t nb = NC - 1 - (c0 + k + kRing);
           nb = nb > 0 ? nb : 0;
           asm volatile("" : "+s"(nb));
@@ -574,8 +596,12 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void bwd_chain_kernel(Problem
         }
       }
 #pragma unroll
-      for (int k = 0; k < kRing; ++k)
-        if (full + k < NC) step(NC - 1 - (full + k), ring[k]);
+      for (int k = 0; k < kRing; ++k) {
+        if (full + k < NC) {
+          if (k % 2 == 0) step(NC - 1 - (full + k), ring[k], Keep<true>());
+          else step(NC - 1 - (full + k), ring[k], Keep<false>());
+        }
+      }
     }
     if (ds0) {
 #pragma unroll
@@ -587,35 +613,51 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void bwd_chain_kernel(Problem
 }
 
 // ---- 4. intra-chunk gradients -------------------------------------------------------
-// One wave per (batch*head, chunk): S (state before the chunk) and D (dL/dS after it)
-// from the recursions, the chunk's record and operands; writes every step's dq, da,
-// db, dalpha and dw. The value columns are taken 16 at a time: each S and D tile is
-// read once, used in the fragment order for U and A^ D (sums over key channels), and
-// transposed through LDS for dO S^T, dR S^T and U D^T (sums over value channels).
+// One two-wave workgroup per (batch*head, chunk pair): wave w takes chunk c = 2m + w,
+// with S (state before it) and D (dL/dS after it), its record and operands, and writes
+// every step's dq, da, db, dalpha and dw. The value columns are taken 16 at a time.
+// The recursions stored S before chunk 2m and D after chunk 2m + 1 only; per value
+// tile, wave 0 forms S before chunk 2m + 1 = Gamma S + A^^T U from the U of its chunk,
+// wave 1 forms D after chunk 2m = Gamma D - W^T (A^ D) + (Q+ - P W)^T dO from the A^ D of
+// its chunk (both products it needs anyway), and the two tiles cross through LDS. Each
+// S and D tile is used in the fragment order for U and A^ D (sums over key channels)
+// and transposed through LDS for dO S^T, dR S^T and U D^T (sums over value channels).
 template <int DK, int DV>
-__global__ __launch_bounds__(64) void bwd_intra_kernel(Problem p, float* __restrict__ ws) {
+__global__ __launch_bounds__(128) void bwd_intra_kernel(Problem p, float* __restrict__ ws) {
   constexpr int KT = DK / 16, VT = DV / 16;
   using R = Rec<DK, DV>;
-  const int l = threadIdx.x, i = l & 15, g = l >> 4;
+  const int l = threadIdx.x & 63, i = l & 15, g = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: the branches on it are too
   const BwdLayout L = bwd_layout(p.B, p.steps, p.H, DK, DV);
   const int64_t NS = p.steps;
-  const int64_t item = blockIdx.x;
-  const int64_t bh = item / L.nc, c = item % L.nc;
+  const int64_t np = L.nc / 2, pair = blockIdx.x;
+  const int64_t bh = pair / np, c = 2 * (pair % np) + w;
+  const int64_t item = bh * L.nc + c;
   const float* rb = ws + L.rows + (bh * L.rs + c * kC) * 4 * DK;
   const float* cb = ws + L.cols + (bh * L.rs + c * kC) * 2 * DV;
   const float* rec = ws + L.rec + item * R::size;
-  const float* sS = ws + L.sst + item * KT * VT * 256;
-  const float* sD = ws + L.dst + item * KT * VT * 256;
+  // the stored tiles this wave reads: S before chunk 2m (wave 0), D after chunk 2m + 1 (wave 1)
+  const float* sX = ws + (w == 0 ? L.sst : L.dst) + pair * KT * VT * 256;
+  // LDS-only barrier of the two waves: global loads in flight stay in flight
+  auto lds_barrier = []() __attribute__((always_inline)) { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
-  // W and A^ in the row order, the same for every value tile: parked in LDS (each
-  // lane reads back only its own slots, so no barrier is needed)
-  __shared__ float4v lw[KT][64], la[KT][64];
+  // Operands that are the same for every value tile: W and A^ in the row order and Gamma,
+  // parked in LDS; those of the rebuilt tiles in registers, A^ (fragment order) for
+  // wave 0, W and Q+ - P W (fragment order) for wave 1.
+  __shared__ float4v lw[2][KT][64], la[2][KT][64];
+  __shared__ float4v xs[2][KT][64], xd[2][KT][64];  // the rebuilt S and D tiles, two value tiles deep
+  __shared__ __align__(16) float lg[2][DK];
+  __shared__ __align__(16) float tr[2][2][16 * 20];  // transposes of the S and D tiles
+  float4v x1[KT], x2[KT];
 #pragma unroll
   for (int t = 0; t < KT; ++t) {
-    lw[t][l] = ld4(rec + R::Wr + t * 256 + 4 * l);
-    la[t][l] = ld4(rec + R::Ar + t * 256 + 4 * l);
+    lw[w][t][l] = ld4(rec + R::Wr + t * 256 + 4 * l);
+    la[w][t][l] = ld4(rec + R::Ar + t * 256 + 4 * l);
+    x1[t] = ld4(rec + (w == 0 ? R::Af : R::Wf) + t * 256 + 4 * l);
+    x2[t] = w == 0 ? zero4() : ld4(rec + R::Cf + t * 256 + 4 * l);
   }
-  __shared__ __align__(16) float tr[2][16 * 20];  // transposes of the S and D tiles
+  for (int k = l; k < DK; k += 64) lg[w][k] = rec[R::Gm + k];
+  __syncthreads();
   float4v pF, tF;  // P[4g+e][i], T[4g+e][i]
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -631,38 +673,76 @@ __global__ __launch_bounds__(64) void bwd_intra_kernel(Problem p, float* __restr
   float rsum[KT];
 #pragma unroll
   for (int t = 0; t < KT; ++t) qs[t] = rs[t] = ud[t] = zero4(), rsum[t] = 0.0f;
+  // a value tile's loads, issued one tile ahead: the stored tiles, dO in both orders, U~
+  struct VOps {
+    float4v st[KT], dF, doA, ur;
+  };
+  auto vload = [&](int vt, VOps& o) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < KT; ++t) o.st[t] = ld4(sX + (t * VT + vt) * 256 + 4 * l);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o.dF[e] = cb[(4 * g + e) * 2 * DV + DV + 16 * vt + i];  // dO[4g+e][16vt+i]
+    o.doA = ld4(cb + i * 2 * DV + DV + 16 * vt + 4 * g);                                // dO[i][16vt+4g+e]
+    o.ur = ld4(rec + R::Ur + vt * 256 + 4 * l);
+  };
+  VOps vn;
+  vload(0, vn);
 #pragma unroll 1
   for (int vt = 0; vt < VT; ++vt) {
+    const VOps vc = vn;
+    if (vt + 1 < VT) vload(vt + 1, vn);
     float4v sf[KT], df[KT];  // S[16t+4g+e][16vt+i], D likewise
-#pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      sf[t] = ld4(sS + (t * VT + vt) * 256 + 4 * l);
-      df[t] = ld4(sD + (t * VT + vt) * 256 + 4 * l);
-    }
     // U in the row order: ut[e] = U[i][16vt+4g+e]  (U^T = U~^T - S^T W^T)
-    float4v ut = -ld4(rec + R::Ur + vt * 256 + 4 * l);
+    auto u_rows = [&]() __attribute__((always_inline)) {
+      float4v ut = -vc.ur;
 #pragma unroll
-    for (int t = 0; t < KT; ++t) ut = mma4(sf[t], lw[t][l], ut);
-    ut = -ut;
-    // dU = A^ D + P^T dO (fragment order), then dR^T = dU^T T: rt[e] = dR[i][16vt+4g+e]
-    float4v x = zero4();
+      for (int t = 0; t < KT; ++t) ut = mma4(sf[t], lw[w][t][l], ut);
+      return -ut;
+    };
+    float4v ut, x = zero4();  // x: A^ D, then dU = A^ D + P^T dO (fragment order)
+    const float4v dF = vc.dF, doA = vc.doA;
+    if (w == 0) {
 #pragma unroll
-    for (int t = 0; t < KT; ++t) x = mma4(la[t][l], df[t], x);
-    float4v dF;
+      for (int t = 0; t < KT; ++t) sf[t] = vc.st[t];
+      ut = u_rows();
+      const float4v uF = lds_transpose(tr[w][0], ut, l);  // U[4g+e][16vt+i]
 #pragma unroll
-    for (int e = 0; e < 4; ++e) dF[e] = cb[(4 * g + e) * 2 * DV + DV + 16 * vt + i];
+      for (int t = 0; t < KT; ++t)
+        xs[vt & 1][t][l] = mma4(x1[t], uF, sf[t] * *reinterpret_cast<const float4v*>(&lg[0][16 * t + 4 * g]));
+    } else {
+#pragma unroll
+      for (int t = 0; t < KT; ++t) df[t] = vc.st[t];
+#pragma unroll
+      for (int t = 0; t < KT; ++t) x = mma4(la[w][t][l], df[t], x);
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+        xd[vt & 1][t][l] = mma4(x1[t], -x, mma4(x2[t], dF, df[t] * *reinterpret_cast<const float4v*>(&lg[1][16 * t + 4 * g])));
+    }
+    // one barrier a value tile: a buffer is written again two tiles later, after both
+    // waves have passed the next tile's barrier and so have read it
+    lds_barrier();
+    if (w == 0) {
+#pragma unroll
+      for (int t = 0; t < KT; ++t) df[t] = xd[vt & 1][t][l];
+#pragma unroll
+      for (int t = 0; t < KT; ++t) x = mma4(la[w][t][l], df[t], x);
+    } else {
+#pragma unroll
+      for (int t = 0; t < KT; ++t) sf[t] = xs[vt & 1][t][l];
+      ut = u_rows();
+    }
+    // dR^T = dU^T T: rt[e] = dR[i][16vt+4g+e]
     x = mma4(pF, dF, x);
     const float4v rt = mma4(x, tF, zero4());
     if (row_live) st4(ws + L.dw + (bh * NS + c * kC + i) * DV + 16 * vt + 4 * g, rt);
-    const float4v doA = ld4(cb + i * 2 * DV + DV + 16 * vt + 4 * g);  // dO[i][16vt+4g+e]
     dp = mma4(doA, ut, dp);
     dpt = mma4(ut, doA, dpt);
     dm = mma4(rt, ut, dm);
     dmt = mma4(ut, rt, dmt);
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
-      const float4v sT = lds_transpose(tr[0], sf[t], l);  // S[16t+i][16vt+4g+e]
-      const float4v dT = lds_transpose(tr[1], df[t], l);
+      const float4v sT = lds_transpose(tr[w][0], sf[t], l);  // S[16t+i][16vt+4g+e]
+      const float4v dT = lds_transpose(tr[w][1], df[t], l);
       qs[t] = mma4(doA, sT, qs[t]);
       rs[t] = mma4(rt, sT, rs[t]);
       ud[t] = mma4(ut, dT, ud[t]);
@@ -951,7 +1031,7 @@ int launch_shape(const Problem& p, const In* dO, const float* dsf, const GradPtr
   }
   bwd_chain_kernel<DK, DV><<<dim3(unsigned(2 * bh * (DV / 16))), dim3(64 * chain_waves(DK)), 0, s>>>(p, dsf, g.ds0, ws);
   if (items == 0) return int(hipGetLastError());
-  bwd_intra_kernel<DK, DV><<<dim3(unsigned(items)), dim3(64), 0, s>>>(p, ws);
+  bwd_intra_kernel<DK, DV><<<dim3(unsigned(items / 2)), dim3(128), 0, s>>>(p, ws);  // chunk pairs
   const int64_t waves = p.B * p.T * p.H * p.n_h;
   const int64_t blocks = (waves + 3) / 4;
   bwd_reduce_kernel<In, DK, DV><<<dim3(unsigned(blocks < (int64_t(1) << 20) ? blocks : (int64_t(1) << 20))), dim3(256), 0, s>>>(p, g, ws);

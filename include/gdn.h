@@ -224,9 +224,9 @@ typedef struct gdn_grads {
 /* Bytes of device workspace gdn_recurrent_bwd needs (0 for an invalid set). Per
  * token (or sub-step) and head: the float32 step operands (4 dk + 2 dv floats), the
  * records of the 16-step chunks ((80 dk + 32 dv + dk + 512) / 16 floats), the state
- * before and the state gradient after every chunk (2 dk dv / 16 floats) and the row
- * gradients (4 dk + dv floats). 17.2 KiB per token and head at dk = dv = 128:
- * 1.15 GB for 4,096 tokens x 16 heads. */
+ * before every even chunk and the state gradient after every odd one (dk dv / 16
+ * floats) and the row gradients (4 dk + dv floats); chunks are counted in pairs. 13.2
+ * KiB per token and head at dk = dv = 128: 0.88 GB for 4,096 tokens x 16 heads. */
 size_t gdn_bwd_workspace_bytes(const gdn_args* args);
 
 /* Backward pass (reverse-mode gradients) of the token recurrence for every variant
