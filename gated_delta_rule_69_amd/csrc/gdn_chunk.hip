@@ -591,6 +591,9 @@ __global__ __launch_bounds__(2 * kThreads + 64) void chunk_scan_rows_kernel(Prob
   }
 
   // ---- state waves ----
+  // They carry the dependent chain, so their instructions issue ahead of the output
+  // and prefetch waves' on the same SIMD (wave priority only; no memory effect).
+  __builtin_amdgcn_s_setprio(3);
   // state: S[rt][ct][e] = S[32 w + 16 rt + 4 lg + e][col_base + 16 ct + li]
   float S[SRT][NCT][4];
   const size_t sbase = size_t(bh) * DK * size_t(dv);
