@@ -269,6 +269,69 @@ def test_some_channels_forget_at_once(case):
     _run_and_check(inp, s0, chunk=chunk, what=f"alpha 1e-4 channels {case}")
 
 
+# ---- magnitudes of the caller's values -----------------------------------------------
+# The bf16 path feeds v, q, the state and U to fp16 MFMAs with exact power-of-two
+# scales (per chunk for the written values, per output row for q, per wave block and
+# column for the state and U), so its relative accuracy must not depend on how large
+# or small the caller's values are, nor on a change of magnitude between chunks.
+# Powers of two keep the bf16 inputs exact; the oracle sees the same values.
+MAG_SHAPES = [
+    # variant, dtype, dk, dv, chunk
+    ("fg2", "bf16", 128, 128, 64),    # two-workgroup prepare, row-split scan
+    ("kda", "bf16", 128, 32, 64),     # general prepare, row-split scan
+    ("fg2", "bf16", 64, 64, 64),      # image records, image scan
+    ("gdn", "bf16", 32, 64, 32),
+]
+MAGNITUDES = [
+    # scale of v, of q, of the initial state (0: none)
+    (2.0 ** 14, 1.0, 0.0),
+    (2.0 ** -14, 1.0, 0.0),
+    (1.0, 2.0 ** 14, 0.0),
+    (1.0, 2.0 ** -14, 1.0),
+    (2.0 ** -12, 1.0, 2.0 ** 10),        # the state dominates every write
+    (2.0 ** 12, 2.0 ** -12, 2.0 ** -12),  # the writes dominate the state
+]
+
+
+@pytest.mark.parametrize("mag", MAGNITUDES, ids=lambda m: "v%g-q%g-s%g" % m)
+@pytest.mark.parametrize("shape", MAG_SHAPES, ids=lambda c: "-".join(map(str, c)))
+def test_value_magnitudes(shape, mag):
+    var, dt, dk, dv, chunk = shape
+    vs, qs, ss = mag
+    inp = gdn_inputs.make_inputs(var, 1, 200, 2, dk, dv, dtype=dt, seed=91)
+    inp["v"] = (inp["v"] * np.float32(vs)).astype(np.float32)
+    inp["q"] = (inp["q"] * np.float32(qs)).astype(np.float32)
+    s0 = gdn_inputs.make_state(1, 2, dk, dv, seed=91, scale=1.0) * np.float32(ss) if ss else None
+    _run_and_check(inp, s0, chunk=chunk, what=f"magnitudes {shape} v {vs:g} q {qs:g} s0 {ss:g}")
+
+
+@pytest.mark.parametrize("shape", MAG_SHAPES, ids=lambda c: "-".join(map(str, c)))
+def test_value_magnitude_changes_between_chunks(shape):
+    """The written values jump by 2^12 for one chunk, then fall to 2^-12 of their
+    size: every chunk's outputs are checked on their own (a whole-tensor norm would
+    be dominated by the loud chunk)."""
+    from gpu_util import TOL, host, run_chunk
+    var, dt, dk, dv, chunk = shape
+    T = 6 * chunk
+    inp = gdn_inputs.make_inputs(var, 1, T, 2, dk, dv, dtype=dt, seed=92)
+    v = inp["v"].copy()
+    v[:, 2 * chunk:3 * chunk] *= np.float32(2.0 ** 12)
+    v[:, 4 * chunk:] *= np.float32(2.0 ** -12)
+    inp["v"] = v
+    s0 = gdn_inputs.make_state(1, 2, dk, dv, seed=92, scale=1.0)
+    print(f"chunk_fwd magnitude jumps {shape}", flush=True)
+    o, S = run_chunk(inp, s0, chunk=chunk)
+    o_ref, S_ref = oracle.forward(inp, s0)
+    got, tol = host(o), TOL[dt]
+    for c in range(T // chunk):
+        seg = slice(c * chunk, (c + 1) * chunk)
+        e = oracle.rel_l2(got[:, seg], o_ref[:, seg])
+        m = oracle.max_rel(got[:, seg], o_ref[:, seg])
+        assert e <= tol["rel_l2"] and m <= tol["max_rel"], (c, e, m)
+    assert oracle.rel_l2(host(S), S_ref) <= tol["rel_l2"]
+    assert oracle.max_rel(host(S), S_ref) <= tol["max_rel"]
+
+
 @pytest.mark.parametrize("T", [1, 5, 16, 63, 64, 65])
 def test_short_and_ragged(T):
     inp = gdn_inputs.make_inputs("fg2", 1, T, 2, 64, 64, dtype="bf16", seed=T)
