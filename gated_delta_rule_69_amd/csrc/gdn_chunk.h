@@ -1072,7 +1072,11 @@ __global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk
     __syncthreads();
 
     // ---- T = (I + M)^{-1}: diagonal 16x16 blocks by forward substitution ----
+    // The waves of the inverse raise their priority while the rest of the workgroup
+    // waits at its barriers, so that the other workgroup on the CU does not hold
+    // this serial phase back; they drop it again before the parallel phases.
     if (wave == 0) {
+      __builtin_amdgcn_s_setprio(2);
       const int bI = lane >> 4, c = lane & 15;
       if (bI < NT) {
         float xcol[16];
@@ -1093,6 +1097,7 @@ __global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk
     for (int I = 1; I < NT; ++I) {
       __syncthreads();
       if (wave < I) {
+        __builtin_amdgcn_s_setprio(2);
         const int J = wave;
         float4v xa = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int K = J; K < I; ++K) {
@@ -1110,6 +1115,7 @@ __global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk
         for (int e = 0; e < 4; ++e) sm.ra.mt.t[16 * I + 4 * lg + e][16 * J + li] = -y[e];
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();
     if (has_next) prefetch(wn, raw, 3);
     // operand copy of T with a zero upper triangle (fp16 over the dead M; fp32 in place)
@@ -2155,7 +2161,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
     }
 
     // ---- T = (I + M)^{-1}: diagonal 16x16 blocks by forward substitution ----
+    // (at raised wave priority, as in chunk_prep_kernel)
     if (wave == 0) {
+      __builtin_amdgcn_s_setprio(2);
       const int bI = lane >> 4, c = lane & 15;
       float xcol[16];
 #pragma unroll
@@ -2173,6 +2181,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
     for (int I = 1; I < NT; ++I) {
       wg_barrier();
       if (wave < I) {
+        __builtin_amdgcn_s_setprio(2);
         const int J = wave;
         float4v xa = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int K = J; K < I; ++K) {
@@ -2190,6 +2199,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
         for (int e = 0; e < 4; ++e) sm.ra.mt.t[16 * I + 4 * lg + e][16 * J + li] = -y[e];
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     wg_barrier();
     // operand copy of T in fp16 with a zero upper triangle, over the dead M
     _Float16* top = reinterpret_cast<_Float16*>(&sm.ra.mt.m[0][0]);
