@@ -19,8 +19,8 @@ pytestmark = pytest.mark.gpu
 ST = oracle.stabilize
 
 
-def mixed_inputs(B, T, H, dk, dtype, seed, dv=None):
-    inp = gdn_inputs.make_inputs("asym", B, T, H, dk, dv or dk, dtype=dtype, seed=seed)
+def mixed_inputs(B, T, H, dk, dtype, seed, dv=None, alpha_mean=3.0):
+    inp = gdn_inputs.make_inputs("asym", B, T, H, dk, dv or dk, dtype=dtype, seed=seed, alpha_mean=alpha_mean)
     k, j, D, eta = (inp[x].astype(np.float64) for x in ("k", "j", "alpha", "eta"))
     kind = np.arange(B * T * H).reshape(B, T, H) % 6
     eta = np.where(kind == 1, 4.0 * eta, eta)
@@ -173,6 +173,24 @@ def test_fused_chunk_forward(mode, dt, dk, chunk):
     o, S = gdn.gdn_chunk_fwd("asym", d["q"], d["k"], d["v"], d["alpha"], None, chunk=chunk,
                              j=d["j"], eta=d["eta"], s0=state_to_dev(s0), stabilize=mode)
     _check_pair(o, S, o_ref, S_ref, dt, f"fused chunk {mode} {dt} dk={dk} C={chunk}")
+
+
+@pytest.mark.parametrize("dt,dk,chunk", [("f32", 64, 32), ("bf16", 64, 64), ("bf16", 128, 64)])
+@pytest.mark.parametrize("mode", ["clip_decay", "project_j"])
+def test_fused_chunk_forward_strong_decay(mode, dt, dk, chunk):
+    """The stabiliser inside the forward pass on chunks of strong decay (decay logits
+    centred at -3, mean D near 0.07; every sixth row keeps D = 1): at bf16, dk 128,
+    chunk 64 the chunks go to the two-workgroup kernel's flagged pass (per-tile decay
+    references) with the stabiliser in its prologue."""
+    import gated_delta_rule_69_amd as gdn
+    from gpu_util import state_to_dev, to_dev
+    inp, _ = mixed_inputs(2, 200, 2, dk, dt, seed=27, alpha_mean=-3.0)
+    s0 = gdn_inputs.make_state(2, 2, dk, dk, seed=12, scale=1.0)
+    o_ref, S_ref = oracle.forward(_oracle_stabilized(mode, inp), s0)
+    d = to_dev(inp)
+    o, S = gdn.gdn_chunk_fwd("asym", d["q"], d["k"], d["v"], d["alpha"], None, chunk=chunk,
+                             j=d["j"], eta=d["eta"], s0=state_to_dev(s0), stabilize=mode)
+    _check_pair(o, S, o_ref, S_ref, dt, f"fused chunk, strong decay, {mode} {dt} dk={dk} C={chunk}")
 
 
 @pytest.mark.parametrize("dt,dk", [("f32", 16), ("f32", 64), ("bf16", 128)])
