@@ -227,6 +227,7 @@ STRONG = [
     ("gdn", "bf16", 1, 300, 2, 128, 128, 1, 64),
     ("asym", "bf16", 1, 300, 2, 128, 128, 1, 64),
     ("deltaproduct", "bf16", 1, 150, 2, 128, 128, 2, 64),
+    ("deltaproduct", "bf16", 1, 90, 2, 128, 128, 3, 64),  # 3 steps padded to 4 a token
     ("fg2", "f32", 1, 300, 2, 64, 64, 1, 32),          # generic prepare kernel, fp32
     ("kda", "f32", 1, 300, 2, 64, 64, 1, 32),
     ("gdn", "f32", 1, 300, 2, 64, 64, 1, 32),
