@@ -884,6 +884,8 @@ __global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk
     }
 
     // ---- Gram tiles: M^T(J, I) = A(J) B(I)^T and P^T(J, I) = A(J) Q(I)^T ----
+    // (MFMA phases run at raised wave priority, as in chunk_prep2_kernel.)
+    __builtin_amdgcn_s_setprio(1);
     // Block k of a wave pairs LDS slot slot_of(k) with this wave's B / Q side; with
     // per-channel decay and chunk 64, tile 3 multiplies its sides by e^{L_2} for
     // blocks 0 and 1 (the reference between tiles 1 and 2).
@@ -1050,6 +1052,7 @@ __global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     if (has_next) prefetch(wn, raw, 2);
     __syncthreads();  // the A sides are dead: their space now holds M and T
     if (owner) {
@@ -1140,6 +1143,7 @@ __global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk
     __syncthreads();
 
     // ---- W^T = B+^T T^T (stored as W rows) and U~ = T Wv (stored transposed) ----
+    __builtin_amdgcn_s_setprio(1);
     auto tprod = [&](const Op* arow, const Op* brow, int I) __attribute__((always_inline)) -> float4v {
       float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
       if constexpr (F16) {
@@ -1245,6 +1249,7 @@ __global__ __launch_bounds__(kThreads, (prep_occupancy<In, DK, C>())) void chunk
       }
     }
     }  // generic W / U~ path
+    __builtin_amdgcn_s_setprio(0);
     if (has_next) prefetch(wn, raw, 4);
     __syncthreads();  // LDS is reused by the next chunk
   }
@@ -1816,7 +1821,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
       wg_barrier();
 
       // ---- Gram tiles: M^T(J, I) = A-(J) B+(I)^T and P^T(J, I) = A-(J) Q+(I)^T, every J
-      // together, k-block outer (tiles above the diagonal are computed and masked) ----
+      // together, k-block outer (tiles above the diagonal are computed and masked).
+      // The MFMA phases run at raised wave priority: their MFMAs issue first and the
+      // other workgroup's VALU work fills the cycles while they execute. ----
+      __builtin_amdgcn_s_setprio(1);
       float4v mreg[NT], preg[NT];
 #pragma unroll
       for (int J = 0; J < NT; ++J) mreg[J] = preg[J] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
@@ -1852,6 +1860,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
           *reinterpret_cast<uint2*>(P_g + p_frag(ro, J)) = h8.u[0];
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       if (has_next) load_raw(nx, raw, 4 | 16);
       wg_barrier();  // A- is dead: its space now holds M and T
 #pragma unroll
@@ -2024,6 +2033,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
       // entries afterwards. Per-channel decay: the three off-diagonal blocks J = 0, 1, 2
       // (those with J >= I are computed and masked). ----
       constexpr int NGB = SCALAR ? NT : NT - 1;
+      __builtin_amdgcn_s_setprio(1);  // MFMA phase (as in the mild pass)
       float4v mreg[NGB], preg[NGB];
 #pragma unroll
       for (int J = 0; J < NGB; ++J) mreg[J] = preg[J] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
@@ -2141,6 +2151,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
           *reinterpret_cast<uint2*>(P_g + p_frag(ro, J)) = h8.u[0];
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       if (has_next) load_raw(nx, raw, 4 | 16);
       wg_barrier();  // the A sides are dead: their space now holds M and T
 #pragma unroll
@@ -2221,7 +2232,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
       scal = load_scal(nx);
     }
     // ---- W^T = B+^T T^T (stored as W rows) and U~ = T Wv (stored transposed): wave w
-    // computes the tiles of step rows 16 w .., independent chains interleaved ----
+    // computes the tiles of step rows 16 w .., independent chains interleaved (an
+    // MFMA phase: raised wave priority) ----
+    __builtin_amdgcn_s_setprio(1);
     H8 ta[2];  // T rows 16 w + li, steps 32 u + 4 lg .. (+16)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -2268,6 +2281,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep2_kernel(Problem p, uns
         *reinterpret_cast<uint2*>(UT_g + u_frag(wave, ct)) = h8.u[0];
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     wg_barrier();  // LDS is reused by the next chunk
   }
 }
